@@ -1,0 +1,9 @@
+"""CPU oracle for the delta-rule recurrence (fp64, token by token).
+
+TEST INFRASTRUCTURE ONLY: imported by the test suite, the smoke check and the
+CPU-baseline leg of the benchmark, never by the GPU library.
+"""
+
+from .recurrence import forward, gate_kind, recurrent_step, rel_l2
+
+__all__ = ["forward", "gate_kind", "recurrent_step", "rel_l2"]

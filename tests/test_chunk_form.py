@@ -1,0 +1,32 @@
+"""The chunk equations (as read) reproduce the token-by-token oracle in fp64."""
+
+import numpy as np
+import pytest
+
+from oracle import forward
+from tests.chunk_form import chunk_forward
+
+
+def _inputs(seed, B, T, H, dk, dv, gate):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, T, H, dk))
+    k = rng.standard_normal((B, T, H, dk))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    v = rng.standard_normal((B, T, H, dv))
+    beta = 1 / (1 + np.exp(-rng.standard_normal((B, T, H))))
+    x = rng.standard_normal((B, T, H) if gate == "scalar" else (B, T, H, dk))
+    log_a = None if gate == "none" else -np.logaddexp(0, x)
+    S0 = 0.1 * rng.standard_normal((B, H, dk, dv))
+    return q, k, v, beta, log_a, S0
+
+
+@pytest.mark.parametrize("gate", ["none", "scalar", "channel"])
+@pytest.mark.parametrize("form", ["page", "literal"])
+@pytest.mark.parametrize("C", [1, 2, 8, 16, 64])
+def test_chunk_form_equals_oracle(gate, form, C):
+    q, k, v, beta, log_a, S0 = _inputs(C, 1, 131, 2, 12, 7, gate)
+    o_ref, S_ref = forward(q, k, v, beta, log_a, S0, form=form)
+    o, S = chunk_forward(q, k, v, beta, log_a, S0, C, form=form)
+    assert np.max(np.abs(o - o_ref)) <= 1e-12 * max(1, np.max(np.abs(o_ref)))
+    assert np.max(np.abs(S - S_ref)) <= 1e-12 * max(1, np.max(np.abs(S_ref)))

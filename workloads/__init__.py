@@ -1,0 +1,7 @@
+"""Seeded synthetic workloads (random draws and dtype rounding only)."""
+
+from .inputs import (CONFIGS, DECODE_CONFIG, DecodeWorkload, Workload, bf16_round, chunk_inputs,
+                     decode_inputs, decode_slice, round_to_io, slice_inputs)
+
+__all__ = ["CONFIGS", "DECODE_CONFIG", "DecodeWorkload", "Workload", "bf16_round", "chunk_inputs",
+           "decode_inputs", "decode_slice", "round_to_io", "slice_inputs"]
