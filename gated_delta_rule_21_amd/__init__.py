@@ -1,0 +1,10 @@
+"""Gated delta-rule linear attention for AMD Instinct MI355X (gfx950).
+
+Public calls (thin wrappers over the C ABI in include/gdr.h):
+    chunk_fwd(q, k, v, beta, log_a=None, S0=None, form="page")  -> (o, S_T)
+    recurrent_step(q, k, v, beta, log_a, S, form="page")         -> (o, S_new)
+"""
+
+from ._lib import EXPORTED, GdrError, LIB_PATH, chunk_fwd, load, recurrent_step
+
+__all__ = ["EXPORTED", "GdrError", "LIB_PATH", "chunk_fwd", "load", "recurrent_step"]

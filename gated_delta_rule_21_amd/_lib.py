@@ -1,0 +1,175 @@
+"""ctypes binding of libgdr.so (argument marshalling only).
+
+Every computation runs in the HIP kernels behind the C ABI declared in
+include/gdr.h.  PyTorch supplies device memory and the current stream.  There
+is no fallback: if the library is missing or the GPU is unavailable, calls
+raise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional, Tuple
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdr.so")
+
+GDR_OK, GDR_ERR_INVALID_ARG, GDR_ERR_UNSUPPORTED, GDR_ERR_ALIGNMENT, GDR_ERR_HIP = range(5)
+GDR_F32, GDR_BF16 = 0, 1
+GATES = {"none": 0, "scalar": 1, "channel": 2}
+FORMS = {"page": 0, "literal": 1}
+
+EXPORTED = ("gdr_chunk_fwd", "gdr_recurrent_step", "gdr_status_string", "gdr_last_error", "gdr_version")
+
+
+class GdrDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("H", ctypes.c_int64),
+                ("d_k", ctypes.c_int64), ("d_v", ctypes.c_int64), ("chunk", ctypes.c_int32),
+                ("io", ctypes.c_int32), ("gate", ctypes.c_int32), ("form", ctypes.c_int32)]
+
+
+class GdrError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"status {status}: {message}")
+        self.status = status
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libgdr.so (once) and declare the C signatures."""
+    global _lib
+    with _lock:
+        if _lib is not None and path is None:
+            return _lib
+        p = path or LIB_PATH
+        if not os.path.exists(p):
+            raise RuntimeError(f"{p} is missing: build it with `python -m gated_delta_rule_21_amd.build`")
+        lib = ctypes.CDLL(p)
+        vp = ctypes.c_void_p
+        lib.gdr_chunk_fwd.restype = ctypes.c_int
+        lib.gdr_chunk_fwd.argtypes = [ctypes.POINTER(GdrDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.gdr_recurrent_step.restype = ctypes.c_int
+        lib.gdr_recurrent_step.argtypes = [ctypes.POINTER(GdrDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.gdr_status_string.restype = ctypes.c_char_p
+        lib.gdr_status_string.argtypes = [ctypes.c_int]
+        lib.gdr_last_error.restype = ctypes.c_char_p
+        lib.gdr_last_error.argtypes = []
+        lib.gdr_version.restype = ctypes.c_int
+        lib.gdr_version.argtypes = []
+        if path is None:
+            _lib = lib
+        return lib
+
+
+def _check(lib, status: int) -> None:
+    if status != GDR_OK:
+        msg = lib.gdr_last_error().decode() or lib.gdr_status_string(status).decode()
+        raise GdrError(status, msg)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _io_of(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return GDR_BF16
+    if t.dtype == torch.float32:
+        return GDR_F32
+    raise TypeError(f"unsupported I/O dtype {t.dtype}; use bfloat16 or float32")
+
+
+def _require(t: torch.Tensor, name: str, dtype: torch.dtype, shape: Tuple[int, ...]) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _gate_of(log_a, beta_shape, k_shape) -> int:
+    if log_a is None:
+        return GATES["none"]
+    if tuple(log_a.shape) == tuple(beta_shape):
+        return GATES["scalar"]
+    if tuple(log_a.shape) == tuple(k_shape):
+        return GATES["channel"]
+    raise ValueError(f"log_a shape {tuple(log_a.shape)} fits neither {tuple(beta_shape)} nor {tuple(k_shape)}")
+
+
+def _stream_handle(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def chunk_fwd(q, k, v, beta, log_a=None, S0=None, *, form: str = "page", o=None, S_T=None,
+              want_state: bool = True, stream=None):
+    """gdr_chunk_fwd on torch tensors.  q, k [B, T, H, d_k]; v [B, T, H, d_v];
+    beta [B, T, H]; log_a None, [B, T, H] or [B, T, H, d_k] (all one I/O dtype);
+    S0 None or [B, H, d_k, d_v] float32.  Returns (o, S_T) (S_T None when
+    want_state is False).  Asynchronous on the current (or given) stream."""
+    lib = load()
+    B, T, H, dk = k.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    _require(q, "q", dt, (B, T, H, dk))
+    _require(k, "k", dt, (B, T, H, dk))
+    _require(v, "v", dt, (B, T, H, dv))
+    _require(beta, "beta", dt, (B, T, H))
+    gate = _gate_of(log_a, beta.shape, k.shape)
+    if log_a is not None:
+        _require(log_a, "log_a", dt, tuple(log_a.shape))
+    if S0 is not None:
+        _require(S0, "S0", torch.float32, (B, H, dk, dv))
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=dt, device=q.device)
+    _require(o, "o", dt, (B, T, H, dv))
+    if want_state and S_T is None:
+        S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    if S_T is not None:
+        _require(S_T, "S_T", torch.float32, (B, H, dk, dv))
+    desc = GdrDesc(B, T, H, dk, dv, 64, _io_of(q), gate, FORMS[form])
+    st = lib.gdr_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_a), _ptr(S0),
+                           _ptr(o), _ptr(S_T), _stream_handle(stream))
+    _check(lib, st)
+    return o, S_T
+
+
+def recurrent_step(q, k, v, beta, log_a, S, *, S_new=None, o=None, form: str = "page", stream=None):
+    """gdr_recurrent_step on torch tensors.  q, k [B, H, d_k]; v [B, H, d_v];
+    beta [B, H]; log_a None, [B, H] or [B, H, d_k]; S [B, H, d_k, d_v] float32.
+    S_new defaults to S (update in place).  Returns (o, S_new)."""
+    lib = load()
+    B, H, dk = k.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    _require(q, "q", dt, (B, H, dk))
+    _require(k, "k", dt, (B, H, dk))
+    _require(v, "v", dt, (B, H, dv))
+    _require(beta, "beta", dt, (B, H))
+    gate = _gate_of(log_a, beta.shape, k.shape)
+    if log_a is not None:
+        _require(log_a, "log_a", dt, tuple(log_a.shape))
+    _require(S, "S", torch.float32, (B, H, dk, dv))
+    if S_new is None:
+        S_new = S
+    _require(S_new, "S_new", torch.float32, (B, H, dk, dv))
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=dt, device=q.device)
+    _require(o, "o", dt, (B, H, dv))
+    desc = GdrDesc(B, 1, H, dk, dv, 0, _io_of(q), gate, FORMS[form])
+    st = lib.gdr_recurrent_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_a), _ptr(S),
+                                _ptr(S_new), _ptr(o), _stream_handle(stream))
+    _check(lib, st)
+    return o, S_new

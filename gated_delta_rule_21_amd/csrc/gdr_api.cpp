@@ -1,0 +1,198 @@
+// C ABI of the gated delta-rule library: argument checks, then dispatch to the
+// gfx950 kernels.  Every check runs before anything is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "../../include/gdr.h"
+#include "launchers.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+gdr_status fail(gdr_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+struct Span {
+  const char* name;
+  uintptr_t lo, hi;   // [lo, hi); empty when lo == hi
+};
+
+bool overlaps(const Span& a, const Span& b) {
+  if (a.lo == a.hi || b.lo == b.hi) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+
+Span span(const char* name, const void* p, int64_t bytes) {
+  uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Span{name, lo, p ? lo + static_cast<uintptr_t>(bytes) : lo};
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > INT64_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+// Checks shared by both entry points.  Fills element counts per token-row.
+gdr_status check_desc(const gdr_desc* d, bool decode) {
+  if (!d) return fail(GDR_ERR_INVALID_ARG, "desc is NULL");
+  if (d->io != GDR_F32 && d->io != GDR_BF16) return fail(GDR_ERR_INVALID_ARG, "io dtype %d is not GDR_F32/GDR_BF16", d->io);
+  if (d->gate < GDR_GATE_NONE || d->gate > GDR_GATE_CHANNEL) return fail(GDR_ERR_INVALID_ARG, "gate %d is not a gdr_gate", d->gate);
+  if (d->form != GDR_FORM_PAGE && d->form != GDR_FORM_LITERAL) return fail(GDR_ERR_INVALID_ARG, "form %d is not a gdr_form", d->form);
+  if (d->B < 1) return fail(GDR_ERR_INVALID_ARG, "B = %lld must be >= 1", (long long)d->B);
+  if (d->H < 1) return fail(GDR_ERR_INVALID_ARG, "H = %lld must be >= 1", (long long)d->H);
+  if (decode) {
+    if (d->T != 1) return fail(GDR_ERR_INVALID_ARG, "T = %lld: a decode step takes exactly one token", (long long)d->T);
+  } else {
+    if (d->T < 0) return fail(GDR_ERR_INVALID_ARG, "T = %lld must be >= 0", (long long)d->T);
+    if (d->chunk != 0 && d->chunk != 64) return fail(GDR_ERR_UNSUPPORTED, "chunk = %d: only 64 is implemented", d->chunk);
+  }
+  if (d->d_k != 64 && d->d_k != 128) return fail(GDR_ERR_UNSUPPORTED, "d_k = %lld: supported 64, 128", (long long)d->d_k);
+  if (d->d_v != 64 && d->d_v != 128) return fail(GDR_ERR_UNSUPPORTED, "d_v = %lld: supported 64, 128", (long long)d->d_v);
+  if (!decode && d->io == GDR_F32 && d->d_k != 64)
+    return fail(GDR_ERR_UNSUPPORTED, "fp32 I/O chunk forward supports d_k = 64 only");
+  int64_t bh, bth, x;
+  if (!mul_ok(d->B, d->H, &bh) || !mul_ok(bh, d->T, &bth) || !mul_ok(bth, 128, &x) || !mul_ok(bh, 128 * 128 * 4, &x))
+    return fail(GDR_ERR_INVALID_ARG, "sizes overflow");
+  if (bh * 8 > INT32_MAX) return fail(GDR_ERR_UNSUPPORTED, "B*H = %lld exceeds the grid limit", (long long)bh);
+  return GDR_OK;
+}
+
+gdr_status check_align(const char* name, const void* p, uintptr_t a) {
+  if (p && (reinterpret_cast<uintptr_t>(p) % a) != 0)
+    return fail(GDR_ERR_ALIGNMENT, "%s = %p is not %u-byte aligned", name, p, (unsigned)a);
+  return GDR_OK;
+}
+
+gdr_status check_no_overlap(const Span* outs, int n_out, const Span* all, int n_all) {
+  for (int i = 0; i < n_out; ++i)
+    for (int j = 0; j < n_all; ++j) {
+      if (outs[i].name == all[j].name) continue;
+      if (overlaps(outs[i], all[j]))
+        return fail(GDR_ERR_INVALID_ARG, "%s overlaps %s", outs[i].name, all[j].name);
+    }
+  return GDR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gdr_status_string(gdr_status s) {
+  switch (s) {
+    case GDR_OK: return "GDR_OK";
+    case GDR_ERR_INVALID_ARG: return "GDR_ERR_INVALID_ARG: invalid argument";
+    case GDR_ERR_UNSUPPORTED: return "GDR_ERR_UNSUPPORTED: configuration not implemented";
+    case GDR_ERR_ALIGNMENT: return "GDR_ERR_ALIGNMENT: pointer misaligned";
+    case GDR_ERR_HIP: return "GDR_ERR_HIP: HIP runtime error";
+  }
+  return "unknown gdr_status";
+}
+
+const char* gdr_last_error(void) { return g_last_error.c_str(); }
+
+int gdr_version(void) { return 100; }
+
+gdr_status gdr_chunk_fwd(const gdr_desc* d, const void* q, const void* k, const void* v, const void* beta,
+                         const void* log_a, const float* S0, void* o, float* S_T, void* stream) {
+  try {
+    g_last_error.clear();
+    gdr_status st = check_desc(d, false);
+    if (st != GDR_OK) return st;
+    const int64_t esz = d->io == GDR_BF16 ? 2 : 4;
+    const int64_t ntok = d->B * d->T * d->H;
+    const bool any = d->T > 0;
+    if (any) {
+      if (!q) return fail(GDR_ERR_INVALID_ARG, "q is NULL");
+      if (!k) return fail(GDR_ERR_INVALID_ARG, "k is NULL");
+      if (!v) return fail(GDR_ERR_INVALID_ARG, "v is NULL");
+      if (!beta) return fail(GDR_ERR_INVALID_ARG, "beta is NULL");
+      if (!o) return fail(GDR_ERR_INVALID_ARG, "o is NULL");
+      if (d->gate != GDR_GATE_NONE && !log_a) return fail(GDR_ERR_INVALID_ARG, "log_a is NULL but a gate is requested");
+    }
+    if (d->gate == GDR_GATE_NONE && log_a) return fail(GDR_ERR_INVALID_ARG, "log_a must be NULL for GDR_GATE_NONE");
+    if ((st = check_align("q", q, 16)) || (st = check_align("k", k, 16)) || (st = check_align("v", v, 16)) ||
+        (st = check_align("o", o, 16)) || (st = check_align("S0", S0, 16)) || (st = check_align("S_T", S_T, 16)) ||
+        (st = check_align("beta", beta, esz)) || (st = check_align("log_a", log_a, esz)))
+      return st;
+    const int64_t gate_w = d->gate == GDR_GATE_NONE ? 0 : d->gate == GDR_GATE_SCALAR ? 1 : d->d_k;
+    const int64_t state_bytes = d->B * d->H * d->d_k * d->d_v * 4;
+    Span all[] = {span("q", q, ntok * d->d_k * esz), span("k", k, ntok * d->d_k * esz),
+                  span("v", v, ntok * d->d_v * esz), span("beta", beta, ntok * esz),
+                  span("log_a", log_a, ntok * gate_w * esz), span("S0", S0, state_bytes),
+                  span("o", o, ntok * d->d_v * esz), span("S_T", S_T, state_bytes)};
+    Span outs[] = {all[6], all[7]};
+    if (S_T && S0 == S_T) all[5].hi = all[5].lo;   // exact in-place update of the state is allowed
+    if ((st = check_no_overlap(outs, 2, all, 8))) return st;
+
+    gdr::ChunkParams p;
+    p.q = q; p.k = k; p.v = v; p.beta = beta; p.log_a = log_a; p.S0 = S0; p.o = o; p.S_T = S_T;
+    p.B = d->B; p.T = d->T; p.H = d->H;
+    p.d_k = static_cast<int>(d->d_k); p.d_v = static_cast<int>(d->d_v);
+    p.io = d->io; p.gate = d->gate; p.literal = d->form == GDR_FORM_LITERAL;
+    if (d->T == 0 && !S_T) return GDR_OK;
+    hipError_t e = gdr::launch_chunk_fwd(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(GDR_ERR_HIP, "chunk forward launch failed: %s", hipGetErrorString(e));
+    return GDR_OK;
+  } catch (...) {
+    return fail(GDR_ERR_INVALID_ARG, "internal error");
+  }
+}
+
+gdr_status gdr_recurrent_step(const gdr_desc* d, const void* q, const void* k, const void* v, const void* beta,
+                              const void* log_a, const float* S, float* S_new, void* o, void* stream) {
+  try {
+    g_last_error.clear();
+    gdr_status st = check_desc(d, true);
+    if (st != GDR_OK) return st;
+    const int64_t esz = d->io == GDR_BF16 ? 2 : 4;
+    const int64_t n = d->B * d->H;
+    if (!q) return fail(GDR_ERR_INVALID_ARG, "q is NULL");
+    if (!k) return fail(GDR_ERR_INVALID_ARG, "k is NULL");
+    if (!v) return fail(GDR_ERR_INVALID_ARG, "v is NULL");
+    if (!beta) return fail(GDR_ERR_INVALID_ARG, "beta is NULL");
+    if (!S) return fail(GDR_ERR_INVALID_ARG, "S is NULL");
+    if (!S_new) return fail(GDR_ERR_INVALID_ARG, "S_new is NULL");
+    if (!o) return fail(GDR_ERR_INVALID_ARG, "o is NULL");
+    if (d->gate != GDR_GATE_NONE && !log_a) return fail(GDR_ERR_INVALID_ARG, "log_a is NULL but a gate is requested");
+    if (d->gate == GDR_GATE_NONE && log_a) return fail(GDR_ERR_INVALID_ARG, "log_a must be NULL for GDR_GATE_NONE");
+    if ((st = check_align("q", q, 16)) || (st = check_align("k", k, 16)) || (st = check_align("v", v, 16)) ||
+        (st = check_align("o", o, 16)) || (st = check_align("S", S, 16)) || (st = check_align("S_new", S_new, 16)) ||
+        (st = check_align("beta", beta, esz)) || (st = check_align("log_a", log_a, esz)))
+      return st;
+    const int64_t gate_w = d->gate == GDR_GATE_NONE ? 0 : d->gate == GDR_GATE_SCALAR ? 1 : d->d_k;
+    const int64_t state_bytes = n * d->d_k * d->d_v * 4;
+    Span all[] = {span("q", q, n * d->d_k * esz), span("k", k, n * d->d_k * esz), span("v", v, n * d->d_v * esz),
+                  span("beta", beta, n * esz), span("log_a", log_a, n * gate_w * esz), span("S", S, state_bytes),
+                  span("o", o, n * d->d_v * esz), span("S_new", S_new, state_bytes)};
+    Span outs[] = {all[6], all[7]};
+    if (S == S_new) all[5].hi = all[5].lo;   // exact in-place update is allowed
+    if ((st = check_no_overlap(outs, 2, all, 8))) return st;
+
+    gdr::DecodeParams p;
+    p.q = q; p.k = k; p.v = v; p.beta = beta; p.log_a = log_a; p.S = S; p.S_new = S_new; p.o = o;
+    p.n_states = n;
+    p.d_k = static_cast<int>(d->d_k); p.d_v = static_cast<int>(d->d_v);
+    p.io = d->io; p.gate = d->gate; p.literal = d->form == GDR_FORM_LITERAL;
+    hipError_t e = gdr::launch_decode_step(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(GDR_ERR_HIP, "decode step launch failed: %s", hipGetErrorString(e));
+    return GDR_OK;
+  } catch (...) {
+    return fail(GDR_ERR_INVALID_ARG, "internal error");
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,40 @@
+// Internal interface between the C-ABI layer (argument checks) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdr {
+
+struct DecodeParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* beta;
+  const void* log_a;
+  const float* S;
+  float* S_new;
+  void* o;
+  int64_t n_states;   // B * H
+  int d_k, d_v;
+  int io, gate, literal;
+};
+
+struct ChunkParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* beta;
+  const void* log_a;
+  const float* S0;    // may be null (zero initial state)
+  void* o;
+  float* S_T;         // may be null (not written)
+  int64_t B, T, H;
+  int d_k, d_v;
+  int io, gate, literal;
+};
+
+hipError_t launch_decode_step(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_chunk_fwd(const ChunkParams& p, hipStream_t stream);
+
+}  // namespace gdr

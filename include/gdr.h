@@ -1,0 +1,146 @@
+/*
+ * gdr.h -- C ABI of the gated delta-rule library for AMD Instinct MI355X (gfx950).
+ *
+ * The library computes the delta-rule linear-attention recurrence, written
+ * key-major (the state S has d_k rows and d_v columns):
+ *
+ *     S_t = (I - beta_t k_t k_t^T) diag(a_t) S_{t-1} + beta_t k_t v_t^T,
+ *     o_t = S_t^T q_t,                       a_t = exp(log_a_t).
+ *
+ * Sources: "Moonshot AI's New Attention Architecture: Key Innovations
+ * Explained", §2 Core Operator (DeltaNet update; scalar-gated update; per-channel
+ * gated update) and §3 Hardware-Friendly Algorithm (chunkwise form: state passed
+ * between chunks, correction terms W and U, causally masked intra-chunk
+ * product); "OSDN: Improving Delta Rule with Provable Online Preconditioning in
+ * Linear Attention", Technical Summary §1 (the delta rule as one gradient step
+ * on 0.5*||S k - v||^2).  Without a gate (a_t = 1) this is DeltaNet; a scalar
+ * a_t gives Gated DeltaNet; a vector a_t over key channels gives the per-channel
+ * (KDA-style) gate.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every pointer argument is a DEVICE pointer except `desc`, which is a host
+ *    pointer read during the call only.  The caller owns every buffer; the
+ *    library allocates no device memory, keeps no mutable global state and
+ *    is safe to call from several host threads.
+ *  - Work is enqueued asynchronously on `stream` (0 = the null stream).  The
+ *    library never synchronises; the caller synchronises before reading results.
+ *  - All tensors are dense, contiguous and row-major in the layouts given
+ *    below.  Pointers to q, k, v, o and to the fp32 states must be 16-byte
+ *    aligned; beta and log_a must be aligned to their element size.
+ *  - q, k, v, beta, log_a and o share the I/O dtype (`io`): GDR_F32 or GDR_BF16.
+ *    Recurrent states (S0, S_T, S, S_new) are always fp32.  bf16 outputs are
+ *    rounded to nearest even.
+ *  - Every argument check runs before anything is enqueued; on error nothing
+ *    is enqueued, the status is returned and a message is available from
+ *    gdr_last_error() on the calling thread.  No C++ exception crosses the ABI
+ *    and the library never aborts.
+ */
+#ifndef GDR_H_
+#define GDR_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GDR_OK = 0,
+  GDR_ERR_INVALID_ARG = 1,   /* null pointer, bad size, bad enum, forbidden alias */
+  GDR_ERR_UNSUPPORTED = 2,   /* valid but not implemented (d_k, d_v, chunk) */
+  GDR_ERR_ALIGNMENT = 3,     /* pointer not aligned as required */
+  GDR_ERR_HIP = 4            /* the HIP runtime reported an error at launch */
+} gdr_status;
+
+typedef enum { GDR_F32 = 0, GDR_BF16 = 1 } gdr_dtype;
+
+typedef enum {
+  GDR_GATE_NONE = 0,     /* a_t = 1; log_a must be NULL                        */
+  GDR_GATE_SCALAR = 1,   /* one log-gate per (token, head): log_a [B, T, H]    */
+  GDR_GATE_CHANNEL = 2   /* one per key channel: log_a [B, T, H, d_k]          */
+} gdr_gate;
+
+/* Where the decay sits relative to the erase.  GDR_FORM_PAGE (default) decays
+ * first and erases from the decayed state, S_t = (I - b k k^T) D S + b k v^T, as
+ * both gated updates of "Moonshot AI's New Attention Architecture", §2 print it.
+ * GDR_FORM_LITERAL erases from the undecayed state, S_t = (D - b k k^T) S + b k v^T.
+ * The two coincide without a gate. */
+typedef enum { GDR_FORM_PAGE = 0, GDR_FORM_LITERAL = 1 } gdr_form;
+
+/* Problem descriptor.  All fields are read by value during the call. */
+typedef struct {
+  int64_t B;       /* sequences (batch); for a decode step: independent sequences */
+  int64_t T;       /* tokens per sequence (>= 0); must be 1 for a decode step     */
+  int64_t H;       /* heads                                                       */
+  int64_t d_k;     /* key / query width: 64 or 128                                 */
+  int64_t d_v;     /* value width: 64 or 128                                       */
+  int32_t chunk;   /* chunk length of the chunkwise form: 64 (0 selects 64).  The
+                      result does not depend on it beyond rounding.               */
+  int32_t io;      /* gdr_dtype */
+  int32_t gate;    /* gdr_gate  */
+  int32_t form;    /* gdr_form  */
+} gdr_desc;
+
+/*
+ * gdr_chunk_fwd -- forward over whole sequences with the chunkwise-parallel form.
+ *
+ * Defined by the recurrence above, run token by token from S0 for each (b, h)
+ * independently; computed chunk by chunk as in "Moonshot AI's New Attention
+ * Architecture", §3 (per-chunk cumulative log-gate, intra-chunk WY correction
+ * terms from a unit-lower-triangular solve, sequential state pass between
+ * chunks, output as a state read plus a causally masked intra-chunk product).
+ *
+ *   q      [B, T, H, d_k]  io dtype
+ *   k      [B, T, H, d_k]  io dtype
+ *   v      [B, T, H, d_v]  io dtype
+ *   beta   [B, T, H]       io dtype (any finite value; workloads use (0, 1))
+ *   log_a  NULL for GDR_GATE_NONE; [B, T, H] (scalar) or [B, T, H, d_k]
+ *          (channel), io dtype, finite (log of a decay in (0, 1] for workloads)
+ *   S0     [B, H, d_k, d_v] fp32, or NULL for a zero initial state
+ *   o      [B, T, H, d_v]  io dtype, written (may be NULL only when T == 0)
+ *   S_T    [B, H, d_k, d_v] fp32 final state, or NULL to skip it.  S_T may be
+ *          the same pointer as S0 (updated in place) but must not otherwise
+ *          overlap any argument.
+ *   o must not overlap any input or S_T.
+ *
+ * T == 0 writes S_T = S0 (or zeros).  T need not be a multiple of the chunk.
+ */
+gdr_status gdr_chunk_fwd(const gdr_desc* desc, const void* q, const void* k, const void* v,
+                         const void* beta, const void* log_a, const float* S0, void* o,
+                         float* S_T, void* stream /* hipStream_t */);
+
+/*
+ * gdr_recurrent_step -- one decode token for B independent sequences.
+ *
+ * One step of the recurrence above with a constant-size state ("Moonshot AI's
+ * New Attention Architecture", §1: linear layers decode with a fixed-size state
+ * instead of a growing key-value cache).  desc->T must be 1; desc->chunk is
+ * ignored.
+ *
+ *   q, k   [B, H, d_k]  io dtype        v, o  [B, H, d_v]  io dtype
+ *   beta   [B, H]       io dtype        log_a NULL / [B, H] / [B, H, d_k]
+ *   S      [B, H, d_k, d_v] fp32 state before the token
+ *   S_new  [B, H, d_k, d_v] fp32 state after the token; may equal S (in place)
+ *          but must not otherwise overlap S.
+ *   o must not overlap any other argument.
+ */
+gdr_status gdr_recurrent_step(const gdr_desc* desc, const void* q, const void* k, const void* v,
+                              const void* beta, const void* log_a, const float* S, float* S_new,
+                              void* o, void* stream /* hipStream_t */);
+
+/* Static description of a status code. */
+const char* gdr_status_string(gdr_status status);
+
+/* Message describing the last error returned on the calling thread ("" if none). */
+const char* gdr_last_error(void);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int gdr_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDR_H_ */

@@ -1,0 +1,129 @@
+"""The C-ABI library loads, exports every symbol the header declares, and rejects
+bad arguments before anything is launched (CPU only: every call below fails
+validation, so no kernel is ever enqueued and no pointer is dereferenced)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_21_amd as gdr
+from gated_delta_rule_21_amd._lib import GdrDesc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdr.h")
+
+OK, INVALID, UNSUPPORTED, ALIGN, HIP = range(5)
+FAKE = 0x10000          # a 16-byte aligned address that is never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gdr.LIB_PATH):
+        from gated_delta_rule_21_amd.build import build
+        build()
+    return gdr.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(gdr_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_expected_entry_points():
+    assert set(declared_functions()) == set(gdr.EXPORTED)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in gdr.h but not exported"
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert lib.gdr_status_string(s).startswith(b"GDR_")
+    assert lib.gdr_version() >= 100
+
+
+def _desc(**kw):
+    d = dict(B=1, T=8, H=2, d_k=128, d_v=128, chunk=64, io=1, gate=1, form=0)
+    d.update(kw)
+    return GdrDesc(**d)
+
+
+def _ptrs(n=8, start=FAKE, stride=1 << 24):
+    return [start + i * stride for i in range(n)]
+
+
+def _chunk(lib, d, ptrs):
+    q, k, v, beta, log_a, S0, o, S_T = ptrs
+    return lib.gdr_chunk_fwd(None if d is None else ctypes.byref(d), q, k, v, beta, log_a, S0, o, S_T, None)
+
+
+def test_null_desc(lib):
+    assert _chunk(lib, None, _ptrs()) == INVALID
+    assert b"desc" in lib.gdr_last_error()
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("d_k", 96, UNSUPPORTED), ("d_v", 256, UNSUPPORTED), ("chunk", 32, UNSUPPORTED),
+    ("io", 7, INVALID), ("gate", 3, INVALID), ("form", 2, INVALID),
+    ("B", 0, INVALID), ("H", -1, INVALID), ("T", -5, INVALID),
+])
+def test_bad_descriptor_fields(lib, field, value, code):
+    assert _chunk(lib, _desc(**{field: value}), _ptrs()) == code
+
+
+def test_fp32_io_with_dk128_is_unsupported(lib):
+    assert _chunk(lib, _desc(io=0), _ptrs()) == UNSUPPORTED
+
+
+@pytest.mark.parametrize("which", range(5))
+def test_null_required_pointer(lib, which):
+    p = _ptrs()
+    p[[0, 1, 2, 3, 6][which]] = None
+    assert _chunk(lib, _desc(), p) == INVALID
+
+
+def test_gate_pointer_consistency(lib):
+    p = _ptrs()
+    p[4] = None
+    assert _chunk(lib, _desc(gate=1), p) == INVALID          # gate requested, no log_a
+    assert _chunk(lib, _desc(gate=0), _ptrs()) == INVALID    # log_a given without a gate
+
+
+def test_misaligned_pointers(lib):
+    for idx in (0, 1, 2, 6, 5, 7):
+        p = _ptrs()
+        p[idx] += 8
+        assert _chunk(lib, _desc(), p) == ALIGN, idx
+    p = _ptrs()
+    p[3] += 1                                                  # beta (bf16) must be 2-byte aligned
+    assert _chunk(lib, _desc(), p) == ALIGN
+
+
+def test_output_overlapping_input_is_rejected(lib):
+    p = _ptrs()
+    p[6] = p[0] + 64                                           # o inside q
+    assert _chunk(lib, _desc(), p) == INVALID
+    assert b"overlaps" in lib.gdr_last_error()
+    p = _ptrs()
+    p[7] = p[5] + 256                                          # S_T partially over S0
+    assert _chunk(lib, _desc(), p) == INVALID
+
+
+def _step(lib, d, ptrs):
+    q, k, v, beta, log_a, S, S_new, o = ptrs
+    return lib.gdr_recurrent_step(ctypes.byref(d), q, k, v, beta, log_a, S, S_new, o, None)
+
+
+def test_decode_checks(lib):
+    assert _step(lib, _desc(T=4), _ptrs()) == INVALID           # one token per step
+    p = _ptrs()
+    p[6] = p[5] + 1024                                          # S_new partially over S
+    assert _step(lib, _desc(T=1), p) == INVALID
+    p = _ptrs()
+    p[5] = None
+    assert _step(lib, _desc(T=1), p) == INVALID
+    assert _step(lib, _desc(T=1, d_k=32), _ptrs()) == UNSUPPORTED
