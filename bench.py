@@ -1,0 +1,265 @@
+#!/usr/bin/env python3
+"""Benchmark of the gated delta-rule hot path on one MI355X.
+
+One step = one gdr_chunk_fwd call over the Gated DeltaNet workload (scalar gate,
+B=8, H=16, T=8192, d_k=d_v=128, chunk 64, bf16 I/O, fp32 state), which runs every
+stage of the chunkwise forward (log-gate scan, intra-chunk WY terms, state pass,
+output, final state).  The headline value is tokens/s (B*T per step) with the
+inputs already resident in HBM.  The decode step (256 sequences x 32 heads,
+fp32 128x128 states, bf16 tokens) is timed in the same run and reported as GB/s.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Prints one JSON line.  `roofline` is for the chunk-forward kernel: algorithmic
+bytes per launch (inputs read once, outputs written once) over the average
+launch time measured with HIP events on the launch stream.  `cpu_baseline` is the
+fp64 oracle timed on one host core over a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = [os.path.join(ROOT, "gated_delta_rule_21_amd", "csrc", n)
+                  for n in ("chunk_fwd.hip", "device_common.h")]
+
+
+def chunk_algorithmic(wl, with_S0: bool):
+    """Bytes and useful flops of one chunk-forward call.
+
+    Bytes: q, k, v, beta, log_a (and S0 when given) read once; o and S_T written once.
+    Flops per (chunk, head) with C = chunk, for the intra-chunk Gram and score
+    matrices (lower triangles), the triangular solve, W and U, and the three
+    state products:  C(C-1)d_k + C^3/3 + C(C+1)(2d_k+2d_v) + 6 C d_k d_v.
+    """
+    esz = 2 if wl.io == "bf16" else 4
+    ntok = wl.B * wl.T * wl.H
+    gate_w = {"none": 0, "scalar": 1, "channel": wl.d_k}[wl.gate]
+    state = wl.B * wl.H * wl.d_k * wl.d_v * 4
+    rd = ntok * (2 * wl.d_k + wl.d_v + 1 + gate_w) * esz + (state if with_S0 else 0)
+    wr = ntok * wl.d_v * esz + state
+    C, dk, dv = wl.chunk, wl.d_k, wl.d_v
+    per_chunk = C * (C - 1) * dk + C ** 3 / 3 + C * (C + 1) * (2 * dk + 2 * dv) + 6 * C * dk * dv
+    nchunks = -(-wl.T // C)
+    return rd + wr, per_chunk * nchunks * wl.B * wl.H
+
+
+def decode_bytes(wl):
+    """Bytes of one decode step: each fp32 state read and written once, plus q, k,
+    v, beta, log_a read and o written (bf16)."""
+    esz = 2 if wl.io == "bf16" else 4
+    gate_w = {"none": 0, "scalar": 1, "channel": wl.d_k}[wl.gate]
+    per = 2 * 4 * wl.d_k * wl.d_v + esz * (2 * wl.d_k + 2 * wl.d_v + 1 + gate_w)
+    return wl.N * wl.H * per
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def profiled_traffic(name: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it was
+    taken on the current kernel source (None otherwise)."""
+    path = os.path.join(PROFILE_DIR, name)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    m_s = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    if not m_b or not m_s or m_s.group(1) != kernel_source_digest():
+        return None
+    return float(m_b.group(1))
+
+
+# ------------------------------------------------------------------ CPU baseline
+def cpu_baseline_child(T: int, heads: int) -> None:
+    """Run the oracle on batch 0, `heads` heads, T tokens of the gated workload."""
+    import numpy as np
+    from oracle import forward
+    from workloads import CONFIGS, slice_inputs
+    wl = CONFIGS[3]
+    sl = [slice_inputs(wl, 0, h, T) for h in range(heads)]
+    st = lambda n: np.stack([s[n] for s in sl], axis=1)[None]
+    args = [st(n) for n in ("q", "k", "v", "beta", "log_a")]
+    t0 = time.perf_counter()
+    forward(*args, None)
+    dt = time.perf_counter() - t0
+    print(json.dumps({"seconds": dt, "T": T, "heads": heads}))
+
+
+def cpu_baseline(T: int, heads: int, H_total: int):
+    env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1")
+    out = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-baseline-child",
+                          "--cpu-T", str(T), "--cpu-heads", str(heads)],
+                         capture_output=True, text=True, env=env, check=True)
+    r = json.loads(out.stdout.strip().splitlines()[-1])
+    head_tok_s = r["heads"] * r["T"] / r["seconds"]
+    return {"value": head_tok_s / H_total, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": (f"fp64 token-by-token oracle (NumPy, one thread) on batch 0, {heads} of {H_total} heads, "
+                       f"{T} tokens of the gated workload; {r['seconds']:.1f} s; tokens/s = head-tokens/s / H"),
+            "seconds": round(r["seconds"], 2)}
+
+
+# ------------------------------------------------------------------ GPU legs
+def bench_chunk(args, log):
+    import torch
+    import gated_delta_rule_21_amd as gdr
+    from workloads import CONFIGS, chunk_inputs
+    wl = CONFIGS[3]
+    log(f"generating {wl.name}")
+    inp = chunk_inputs(wl)
+    dev = lambda x: None if x is None else torch.from_numpy(x).to(torch.bfloat16).cuda()
+    q, k, v, beta, log_a = (dev(inp[n]) for n in ("q", "k", "v", "beta", "log_a"))
+    del inp
+    o = torch.empty((wl.B, wl.T, wl.H, wl.d_v), dtype=torch.bfloat16, device="cuda")
+    S_T = torch.empty((wl.B, wl.H, wl.d_k, wl.d_v), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        gdr.chunk_fwd(q, k, v, beta, log_a, None, o=o, S_T=S_T)     # S0 = 0 for this workload
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    log(f"chunk forward: {ms:.3f} ms/step (wall {1e3 * wall / args.steps:.3f} ms/step)")
+    nbytes, flops = chunk_algorithmic(wl, with_S0=False)
+    return wl, ms, nbytes, flops
+
+
+def bench_decode(args, log):
+    import torch
+    import gated_delta_rule_21_amd as gdr
+    from workloads import DECODE_CONFIG, decode_inputs
+    wl = DECODE_CONFIG
+    n_sets = 16
+    log(f"generating {wl.name} ({n_sets} token sets, reused cyclically)")
+    inp = decode_inputs(wl, steps=n_sets)
+    dev = lambda x: torch.from_numpy(x).to(torch.bfloat16).cuda()
+    q, k, v, beta, log_a = (dev(inp[n]) for n in ("q", "k", "v", "beta", "log_a"))
+    S = torch.from_numpy(inp["S0"]).cuda()
+    o = torch.empty((wl.N, wl.H, wl.d_v), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(s):
+        j = s % n_sets
+        gdr.recurrent_step(q[j], k[j], v[j], beta[j], log_a[j], S, o=o)
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for s in range(args.decode_steps):
+        step(s)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.decode_steps
+    nbytes = decode_bytes(wl)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"decode: {ms * 1e3:.1f} us/step, {gbs:.0f} GB/s")
+    return {"value": round(gbs, 1), "unit": "GB/s", "us_per_step": round(ms * 1e3, 2),
+            "tokens_per_s": round(wl.N / (ms * 1e-3), 1), "steps": args.decode_steps,
+            "workload": wl.name, "bytes_per_step": nbytes,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": profiled_traffic("decode_step_n256h32d128_counters.md")}}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-T", type=int, default=8192)
+    ap.add_argument("--cpu-heads", type=int, default=16)
+    ap.add_argument("--cpu-baseline-child", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--quiet", action="store_true")
+    args = ap.parse_args()
+
+    if args.cpu_baseline_child:
+        cpu_baseline_child(args.cpu_T, args.cpu_heads)
+        return
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "the hot path has no multi-GPU leg in this build.", file=sys.stderr)
+        sys.exit(2)
+
+    log = (lambda *a: None) if args.quiet else (lambda *a: print("[bench]", *a, file=sys.stderr, flush=True))
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import gated_delta_rule_21_amd as gdr
+    gdr.load()
+
+    wl, ms, nbytes, flops = bench_chunk(args, log)
+    tok_s = wl.B * wl.T / (ms * 1e-3)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    tflops = flops / (ms * 1e-3) / 1e12
+    decode = None if args.no_decode else bench_decode(args, log)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle sample")
+        cpu = cpu_baseline(args.cpu_T, args.cpu_heads, wl.H)
+
+    line = {
+        "metric": "tokens/s + % MFMA peak, gated delta-rule chunk fwd T=8192 d=128; decode GB/s",
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "H": wl.H, "d_k": wl.d_k, "d_v": wl.d_v,
+                   "chunk": wl.chunk, "gate": wl.gate, "io": wl.io, "state": "fp32", "S0": "zero",
+                   "global_batch": wl.B, "seq_len": wl.T, "parallelism": "none (1 GPU)"},
+        "tflops_useful": round(tflops, 2),
+        "mfma_frac_useful": round(tflops / BF16_PEAK_TFLOPS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": profiled_traffic("chunk_fwd_gated_b8h16t8192d128_counters.md")},
+        "algorithmic_bytes_per_launch": nbytes,
+        "useful_flops_per_launch": flops,
+        "decode": decode,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

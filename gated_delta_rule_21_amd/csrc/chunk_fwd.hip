@@ -18,26 +18,33 @@
 //   O     = (Q*e^{g}) S + lower_incl( (Q*e^{g}) (K*e^{-g})^T ) Delta
 //   S'    = diag(e^{g_63}) S + (K*e^{g_63 - g})^T Delta
 // (the correction terms W, U and the two state/output equations of §3; the
-// query/key decay factors as derived from the §2 update, see the design notes).
+// query/key decay factors as derived from the §2 update).
 //
 // Work decomposition.  One workgroup of NW waves owns one (batch, head, d_v tile
 // of 16*NW columns) and walks the chunks in order.  Wave w owns 16 state
 // columns: its slice of S (d_k x 16, fp32) lives in MFMA accumulators for the
 // whole sequence.  An accumulator tile (lane l: column l%16, rows 4(l/16)+s) is
-// exactly the B-operand layout of the next product, so W*S, Q*S and the state
-// update chain through registers without touching LDS.  The d_v-independent
-// per-chunk work (log-gate scan, decayed operands, the 16x16 blocks of A and of
-// the masked score matrix P, the four diagonal 16x16 inverses) is shared by the
-// waves through LDS.  (I + A)^{-1} is never formed: each wave solves for its own
-// columns of W and U by forward substitution over the four 16-row blocks
-// (inverse diagonal block times right-hand side minus the blocks already solved).
+// the operand layout of the next product, so W*S, the output and the state
+// update chain through registers.  The d_v-independent per-chunk work (log-gate
+// scan, the 16x16 blocks of A and of the masked score matrix P, the four
+// diagonal 16x16 inverses) is shared by the waves through LDS.  (I + A)^{-1} is
+// never formed: each wave solves for its own columns of W and U by forward
+// substitution over the four 16-row blocks.  The next chunk's q, k, v, beta and
+// log-gate are loaded into registers (16-byte loads) while the current chunk
+// computes.
 //
-// Numerics.  Decay factors are computed in the log domain.  For the score
+// Gates.  With no gate or a scalar gate the decay factors are per row and per
+// column of the 64x64 intra-chunk matrices, so the products run on the raw
+// q, k, v tiles and the factors are applied to the results (A and P element by
+// element, the output and Delta row by row).  A per-channel gate sits inside
+// the d_k contraction, so decayed operands are built first; for the score
 // matrices the factor e^{g_r - g_j} is split at the first row of each 16-row
-// block (e^{g_r - g_16R} on rows, e^{g_16J - g_j} on columns, and e^{g_16R - g_16J}
-// on the column operand of blocks below the diagonal), so no operand exceeds the
-// decay accumulated over 15 tokens.  Products run on bf16 MFMA with fp32
-// accumulation for bf16 I/O and on fp32 MFMA for fp32 I/O; the state stays fp32.
+// block (e^{g_r - g_16R} on rows, e^{g_16J - g_j} on columns, e^{g_16R - g_16J} on
+// the column operand of blocks below the diagonal), so no operand exceeds the
+// decay accumulated over 15 tokens.
+//
+// Products run on bf16 MFMA with fp32 accumulation for bf16 I/O and on fp32
+// MFMA for fp32 I/O; the state stays fp32.
 #include "device_common.h"
 #include "launchers.h"
 
@@ -51,7 +58,6 @@ template <> struct Op<IO_BF16> {
   typedef bf16x4 frag;
   static constexpr int PAD = 8;
   static __device__ __forceinline__ frag ld(const T* p) { return *reinterpret_cast<const frag*>(p); }
-  static __device__ __forceinline__ void st(T* p, frag x) { *reinterpret_cast<frag*>(p) = x; }
   static __device__ __forceinline__ frag cvt(f32x4 x) { return to_bf16x4(x); }
   static __device__ __forceinline__ f32x4 f32(frag x) {
     f32x4 r;
@@ -60,6 +66,7 @@ template <> struct Op<IO_BF16> {
     return r;
   }
   static __device__ __forceinline__ T from(float x) { return static_cast<__bf16>(x); }
+  static __device__ __forceinline__ float to(T x) { return static_cast<float>(x); }
   static __device__ __forceinline__ f32x4 mma2(f32x4 acc, frag a0, frag a1, frag b0, frag b1) {
     return mma_k32_bf16(acc, a0, a1, b0, b1);
   }
@@ -70,10 +77,10 @@ template <> struct Op<IO_F32> {
   typedef f32x4 frag;
   static constexpr int PAD = 4;
   static __device__ __forceinline__ frag ld(const T* p) { return *reinterpret_cast<const frag*>(p); }
-  static __device__ __forceinline__ void st(T* p, frag x) { *reinterpret_cast<frag*>(p) = x; }
   static __device__ __forceinline__ frag cvt(f32x4 x) { return x; }
   static __device__ __forceinline__ f32x4 f32(frag x) { return x; }
   static __device__ __forceinline__ T from(float x) { return x; }
+  static __device__ __forceinline__ float to(T x) { return x; }
   static __device__ __forceinline__ f32x4 mma2(f32x4 acc, frag a0, frag a1, frag b0, frag b1) {
     return mma_k16_f32(mma_k16_f32(acc, a0, b0), a1, b1);
   }
@@ -82,48 +89,73 @@ template <> struct Op<IO_F32> {
 
 constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
 
-// LDS layout (bytes).  Regions that are dead by the time a later phase writes
-// share storage: W over the row operand of A, the diagonal inverses over the
-// column operand, and A and P over the log-gate scan buffer.
+// LDS layout (bytes).  Row-major [64][DK] tiles use stride LDK, transposed
+// [*][64] tiles stride LCH; both carry padding against bank conflicts.
 template <int IO, int GATE, int DK, int NW>
 struct Layout {
   typedef typename Op<IO>::T T;
+  static constexpr bool RAW = GATE != GATE_CHANNEL;   // products on raw q, k, v
   static constexpr int PAD = Op<IO>::PAD;
-  static constexpr int LDK = DK + PAD;    // row stride of [64][DK] tiles
-  static constexpr int LCH = CH + PAD;    // row stride of [*][64] tiles
-  static constexpr int LA = CH + 4;       // row stride of the fp32 A matrix
-  static constexpr int LXI = 16 + PAD;    // row stride of the 16x16 inverses
+  static constexpr int LDK = DK + PAD;
+  static constexpr int LCH = CH + PAD;
+  static constexpr int LA = CH + 4;
+  static constexpr int LXI = 16 + PAD;
   static constexpr int DVT = 16 * NW;
+  static constexpr int LVT = DVT + PAD;
   static constexpr int NSEG = (64 * NW) / DK > 0 ? (64 * NW) / DK : 1;
-  static constexpr size_t TILE_RM = size_t(CH) * LDK * sizeof(T);
-  static constexpr size_t TILE_T = size_t(DK) * LCH * sizeof(T);
-  static constexpr size_t XINV = size_t(4) * 16 * LXI * sizeof(T);
-  static constexpr size_t A_BYTES = size_t(CH) * LA * 4;
-  static constexpr size_t P_BYTES = size_t(CH) * LCH * sizeof(T);
-  static constexpr size_t G_BYTES = GATE == GATE_CHANNEL ? size_t(CH) * DK * 4 : size_t(CH) * 4;
-  static constexpr size_t OFF_XK = 0;                                   // X_K, then W
-  static constexpr size_t OFF_Y = OFF_XK + TILE_RM;                     // Y, then inverses
-  static constexpr size_t OFF_XQ = OFF_Y + cmax(TILE_RM, XINV);
-  static constexpr size_t OFF_QH = OFF_XQ + TILE_RM;
-  static constexpr size_t OFF_KRT = OFF_QH + TILE_RM;
-  static constexpr size_t OFF_KDT = OFF_KRT + TILE_T;
-  static constexpr size_t OFF_VT = OFF_KDT + TILE_T;
-  static constexpr size_t OFF_G = OFF_VT + size_t(DVT) * LCH * sizeof(T);   // g, then A and P
-  static constexpr size_t OFF_P = OFF_G + A_BYTES;
-  static constexpr size_t OFF_BETA = OFF_G + cmax(G_BYTES, A_BYTES + P_BYTES);
-  static constexpr size_t OFF_GAM = OFF_BETA + CH * 4;
-  static constexpr size_t OFF_M = OFF_GAM + DK * 4;
-  static constexpr size_t OFF_TOT = OFF_M + 6 * DK * 4;
-  static constexpr size_t TOTAL = OFF_TOT + NSEG * DK * 4;
+  static constexpr size_t RM = size_t(CH) * LDK * sizeof(T);      // [64][DK]
+  static constexpr size_t TR = size_t(DK) * LCH * sizeof(T);      // [DK][64]
+  static constexpr size_t A_B = size_t(CH) * LA * 4;
+  static constexpr size_t P_B = size_t(CH) * LCH * sizeof(T);
+  static constexpr size_t XI_B = size_t(CH) * LXI * sizeof(T);
+  static constexpr size_t V_B = size_t(CH) * LVT * sizeof(T);
+  static constexpr size_t VT_B = size_t(DVT) * LCH * sizeof(T);
+  // common regions
+  static constexpr size_t OFF_K = 0;                     // raw k (channel: X_K in place, then W)
+  static constexpr size_t OFF_Q = OFF_K + RM;            // raw q (channel: X_Q in place)
+  static constexpr size_t OFF_V = OFF_Q + RM;            // raw v tile, then the inverses
+  static constexpr size_t OFF_VT = OFF_V + V_B;          // beta * v, transposed
+  static constexpr size_t OFF_X = OFF_VT + VT_B;         // gate-dependent regions start here
+  // raw gates
+  static constexpr size_t R_KT = OFF_X;                  // k transposed
+  static constexpr size_t R_W = R_KT + TR;
+  static constexpr size_t R_A = R_W + RM;
+  static constexpr size_t R_P = R_A + A_B;
+  static constexpr size_t R_SMALL = R_P + P_B;           // beta, g, g_read, e_w, e_o, e_d, gamma
+  static constexpr size_t R_TOTAL = R_SMALL + 7 * CH * 4;
+  // per-channel gate
+  static constexpr size_t C_Y = OFF_X;                   // column operand of the score blocks
+  static constexpr size_t C_QH = C_Y + RM;
+  static constexpr size_t C_KRT = C_QH + RM;
+  static constexpr size_t C_KDT = C_KRT + TR;
+  static constexpr size_t C_G = C_KDT + TR;              // g [64][DK] fp32, then A and P
+  static constexpr size_t C_G_B = cmax(size_t(CH) * DK * 4, A_B + P_B);
+  static constexpr size_t C_BETA = C_G + C_G_B;
+  static constexpr size_t C_GAM = C_BETA + CH * 4;
+  static constexpr size_t C_M = C_GAM + DK * 4;
+  static constexpr size_t C_TOT = C_M + 6 * DK * 4;
+  static constexpr size_t C_TOTAL = C_TOT + NSEG * DK * 4;
+  static constexpr size_t TOTAL = RAW ? R_TOTAL : C_TOTAL;
+  static_assert(V_B >= XI_B, "the inverses reuse the raw v tile");
 };
 
-// (R, J) block pairs of the lower triangle (incl. diagonal) of a 4x4 block grid.
-__device__ __forceinline__ void lower_pair(int t, int& R, int& J) {
-  R = (t >= 1) + (t >= 3) + (t >= 6);
-  J = t - R * (R + 1) / 2;
+// Off-diagonal 16x16 tasks of the A/P phase: 6 strictly-lower blocks of A, then
+// the 10 lower blocks (incl. diagonal) of P.
+__device__ __forceinline__ void other_task(int t, bool& isP, int& R, int& J) {
+  if (t < 6) {
+    isP = false;
+    R = 1 + (t >= 1) + (t >= 3);
+    J = t - R * (R - 1) / 2;
+  } else {
+    isP = true;
+    const int u = t - 6;
+    R = (u >= 1) + (u >= 3) + (u >= 6);
+    J = u - R * (R + 1) / 2;
+  }
 }
-// Index of a strictly-lower pair (R > J) in 0..5.
 __device__ __forceinline__ int strict_pair(int R, int J) { return R * (R - 1) / 2 + J; }
+
+__device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
 template <int IO, int GATE, int DK, int NW>
 __global__ __launch_bounds__(NW * 64) void chunk_fwd_kernel(ChunkParams p, int n_tiles) {
@@ -132,30 +164,50 @@ __global__ __launch_bounds__(NW * 64) void chunk_fwd_kernel(ChunkParams p, int n
   typedef typename O::frag frag;
   typedef typename Io<IO>::elem elem;
   typedef Layout<IO, GATE, DK, NW> L;
+  constexpr bool RAW = L::RAW;
   constexpr int NT = NW * 64;
   constexpr int DVT = 16 * NW;
   constexpr int DKT = DK / 16;
   constexpr int CBW = DKT / NW;          // 16-channel blocks of W solved per wave
-  constexpr int LDK = L::LDK, LCH = L::LCH, LA = L::LA, LXI = L::LXI;
+  constexpr int LDK = L::LDK, LCH = L::LCH, LA = L::LA, LXI = L::LXI, LVT = L::LVT;
+  constexpr int EPV = 16 / int(sizeof(elem));   // elements per 16-byte load
+  constexpr int KROW = DK / EPV, VROW = DVT / EPV;
+  constexpr int KV = CH * KROW / NT, VV = CH * VROW / NT;
   static_assert(CBW >= 1 && CBW * NW == DKT, "channel blocks must split over waves");
+  static_assert(KV * NT == CH * KROW && VV * NT == CH * VROW && VV >= 1, "tile loads must split evenly");
+  static_assert(L::TOTAL <= 163840, "LDS budget");
 
   __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
-  T* sXK = reinterpret_cast<T*>(smem + L::OFF_XK);
-  T* sW = sXK;
-  T* sY = reinterpret_cast<T*>(smem + L::OFF_Y);
-  T* sXi = sY;
-  T* sXQ = reinterpret_cast<T*>(smem + L::OFF_XQ);
-  T* sQh = reinterpret_cast<T*>(smem + L::OFF_QH);
-  T* sKrT = reinterpret_cast<T*>(smem + L::OFF_KRT);
-  T* sKdT = reinterpret_cast<T*>(smem + L::OFF_KDT);
+  T* sK = reinterpret_cast<T*>(smem + L::OFF_K);
+  T* sQ = reinterpret_cast<T*>(smem + L::OFF_Q);
+  T* sV = reinterpret_cast<T*>(smem + L::OFF_V);
   T* sVT = reinterpret_cast<T*>(smem + L::OFF_VT);
-  float* sG = reinterpret_cast<float*>(smem + L::OFF_G);
-  float* sA = sG;
-  T* sP = reinterpret_cast<T*>(smem + L::OFF_P);
-  float* sBeta = reinterpret_cast<float*>(smem + L::OFF_BETA);
-  float* sGam = reinterpret_cast<float*>(smem + L::OFF_GAM);
-  float* sM = reinterpret_cast<float*>(smem + L::OFF_M);
-  float* sTot = reinterpret_cast<float*>(smem + L::OFF_TOT);
+  // raw-gate regions
+  T* sKT = reinterpret_cast<T*>(smem + L::R_KT);
+  float* sSmall = reinterpret_cast<float*>(smem + L::R_SMALL);
+  float* sBr = sSmall;              // beta
+  float* sGr = sSmall + CH;         // g
+  float* sGrd = sSmall + 2 * CH;    // g_read
+  float* sEw = sSmall + 3 * CH;     // beta e^{g_read}   (right-hand side of W)
+  float* sEo = sSmall + 4 * CH;     // e^{g}             (output rows)
+  float* sEd = sSmall + 5 * CH;     // e^{g_63 - g}      (Delta rows in the state update)
+  float* sGamR = sSmall + 6 * CH;   // e^{g_63}
+  // per-channel regions
+  T* sY = reinterpret_cast<T*>(smem + L::C_Y);
+  T* sQh = reinterpret_cast<T*>(smem + L::C_QH);
+  T* sKrT = reinterpret_cast<T*>(smem + L::C_KRT);
+  T* sKdT = reinterpret_cast<T*>(smem + L::C_KDT);
+  float* sG = reinterpret_cast<float*>(smem + L::C_G);
+  float* sBc = reinterpret_cast<float*>(smem + L::C_BETA);
+  float* sGamC = reinterpret_cast<float*>(smem + L::C_GAM);
+  float* sM = reinterpret_cast<float*>(smem + L::C_M);
+  float* sTot = reinterpret_cast<float*>(smem + L::C_TOT);
+  // shared names
+  T* sW = RAW ? reinterpret_cast<T*>(smem + L::R_W) : sK;
+  float* sA = RAW ? reinterpret_cast<float*>(smem + L::R_A) : sG;
+  T* sP = RAW ? reinterpret_cast<T*>(smem + L::R_P) : reinterpret_cast<T*>(smem + L::C_G + L::A_B);
+  T* sXi = sV;   // the raw v tile is dead once its transpose is built
+  float* sBeta = RAW ? sBr : sBc;
 
   const elem* gq = static_cast<const elem*>(p.q);
   const elem* gk = static_cast<const elem*>(p.k);
@@ -181,14 +233,9 @@ __global__ __launch_bounds__(NW * 64) void chunk_fwd_kernel(ChunkParams p, int n
   const int lane = tid & 63;
   const int lr = lane & 15;
   const int lg = lane >> 4;
-  const int scol = col0 + 16 * wave + lr;   // this lane's state / output column
+  const int scol = col0 + 16 * wave + lr;   // this lane's state column
 
   auto tok = [&](int64_t t) -> int64_t { return (bb * p.T + t) * p.H + hh; };
-  auto G = [&](int r, int i) -> float {
-    if (GATE == GATE_CHANNEL) return sG[r * DK + i];
-    if (GATE == GATE_SCALAR) return sG[r];
-    return 0.f;
-  };
 
   // State slice: S[t][s] = S[16t + 4lg + s][scol].
   f32x4 S[DKT];
@@ -198,220 +245,317 @@ __global__ __launch_bounds__(NW * 64) void chunk_fwd_kernel(ChunkParams p, int n
     for (int s = 0; s < 4; ++s)
       S[t][s] = p.S0 ? p.S0[(bh * DK + 16 * t + 4 * lg + s) * dv + scol] : 0.f;
 
+  // ---- register prefetch of one chunk's inputs ----------------------------------
+  uint4 pk[KV], pq[KV], pl[GATE == GATE_CHANNEL ? KV : 1], pv[VV];
+  float pb = 0.f, pls = 0.f;
+  auto prefetch = [&](int64_t m) {
+    const int64_t t0m = m * CH;
+    const int nr = static_cast<int>(p.T - t0m < CH ? p.T - t0m : CH);
+    const uint4 z = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int v = 0; v < KV; ++v) {
+      const int seg = tid + v * NT, row = seg / KROW, c = (seg % KROW) * EPV;
+      const bool live = row < nr;
+      const int64_t off = tok(t0m + row) * DK + c;
+      pk[v] = live ? ldg16(gk + off) : z;
+      pq[v] = live ? ldg16(gq + off) : z;
+      if constexpr (GATE == GATE_CHANNEL) pl[v] = live ? ldg16(gla + off) : z;
+    }
+#pragma unroll
+    for (int v = 0; v < VV; ++v) {
+      const int seg = tid + v * NT, row = seg / VROW, c = (seg % VROW) * EPV;
+      pv[v] = row < nr ? ldg16(gv + tok(t0m + row) * dv + col0 + c) : z;
+    }
+    if (tid < CH) {
+      pb = tid < nr ? Io<IO>::load(gbeta, tok(t0m + tid)) : 0.f;
+      if constexpr (GATE == GATE_SCALAR) pls = tid < nr ? Io<IO>::load(gla, tok(t0m + tid)) : 0.f;
+    }
+  };
+
   const int64_t nchunks = (p.T + CH - 1) / CH;
+  if (nchunks > 0) prefetch(0);
+
   for (int64_t n = 0; n < nchunks; ++n) {
     const int64_t t0 = n * CH;
     const int nrows = static_cast<int>(p.T - t0 < CH ? p.T - t0 : CH);
 
-    // ---- (1) beta and the per-chunk cumulative log-gate -------------------------
-    if (tid < CH) sBeta[tid] = tid < nrows ? Io<IO>::load(gbeta, tok(t0 + tid)) : 0.f;
-    if (GATE == GATE_SCALAR) {
-      if (wave == 0) {
-        float x = lane < nrows ? Io<IO>::load(gla, tok(t0 + lane)) : 0.f;
+    // ---- (0) raw chunk from registers into LDS; start loading the next chunk ---
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const float y = __shfl_up(x, off);
-          if (lane >= off) x += y;
+    for (int v = 0; v < KV; ++v) {
+      const int seg = tid + v * NT, row = seg / KROW, c = (seg % KROW) * EPV;
+      *reinterpret_cast<uint4*>(sK + row * LDK + c) = pk[v];
+      *reinterpret_cast<uint4*>(sQ + row * LDK + c) = pq[v];
+      if constexpr (GATE == GATE_CHANNEL) {
+        const elem* e = reinterpret_cast<const elem*>(&pl[v]);
+#pragma unroll
+        for (int j = 0; j < EPV; ++j) {
+          float x;
+          if constexpr (IO == IO_BF16) x = bf16_bits_to_f32(e[j]); else x = e[j];
+          sG[row * DK + c + j] = x;
         }
-        sG[lane] = x;
       }
-      __syncthreads();
-      if (tid == 0) {
-        sGam[0] = __expf(sG[CH - 1]);
+    }
 #pragma unroll
-        for (int R = 1; R < 4; ++R)
-          for (int J = 0; J < R; ++J) sM[strict_pair(R, J)] = __expf(sG[16 * R] - sG[16 * J]);
+    for (int v = 0; v < VV; ++v) {
+      const int seg = tid + v * NT, row = seg / VROW, c = (seg % VROW) * EPV;
+      *reinterpret_cast<uint4*>(sV + row * LVT + c) = pv[v];
+    }
+    if (tid < CH) {
+      sBeta[tid] = pb;
+      if constexpr (GATE == GATE_SCALAR) sGr[tid] = pls;   // raw log-gate; scanned below
+    }
+    if (n + 1 < nchunks) prefetch(n + 1);
+    __syncthreads();
+
+    // ---- (1) log-gate scan and, for raw gates, the transposed operands ------------
+    if constexpr (RAW) {
+      if (wave == 0) {
+        float g = 0.f, gread = 0.f;
+        if constexpr (GATE == GATE_SCALAR) {
+          g = sGr[lane];
+#pragma unroll
+          for (int off = 1; off < 64; off <<= 1) {
+            const float y = __shfl_up(g, off);
+            if (lane >= off) g += y;
+          }
+          const float gprev = __shfl_up(g, 1);
+          gread = p.literal ? (lane == 0 ? 0.f : gprev) : g;
+        }
+        const float gC = __shfl(g, 63);
+        const float be = sBr[lane];
+        sGr[lane] = g;
+        sGrd[lane] = gread;
+        sEw[lane] = be * __expf(gread);
+        sEo[lane] = __expf(g);
+        sEd[lane] = __expf(gC - g);
+        if (lane == 0) sGamR[0] = __expf(gC);
       }
-    } else if (GATE == GATE_CHANNEL) {
-      for (int idx = tid; idx < CH * DK; idx += NT) {
-        const int r = idx / DK, i = idx % DK;
-        sG[idx] = r < nrows ? Io<IO>::load(gla, tok(t0 + r) * DK + i) : 0.f;
+      // k transposed: column i, rows 8rg..8rg+7 -> one contiguous run of KT
+      for (int task = tid; task < DK * 8; task += NT) {
+        const int i = task % DK, rg = task / DK;
+        T buf[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) buf[j] = sK[(8 * rg + j) * LDK + i];
+#pragma unroll
+        for (int j = 0; j < 8; j += 4) {
+          frag f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) f[e] = buf[j + e];
+          *reinterpret_cast<frag*>(sKT + i * LCH + 8 * rg + j) = f;
+        }
       }
-      __syncthreads();
-      constexpr int NSEG = L::NSEG;
-      constexpr int SEGL = CH / NSEG;
+    } else {
+      // per-channel scan over the rows of each channel
+      constexpr int NSEG = L::NSEG, SEGL = CH / NSEG;
       if (tid < NSEG * DK) {
         const int i = tid % DK, seg = tid / DK;
         float acc = 0.f;
+#pragma unroll 8
         for (int r = seg * SEGL; r < (seg + 1) * SEGL; ++r) {
           acc += sG[r * DK + i];
           sG[r * DK + i] = acc;
         }
         sTot[seg * DK + i] = acc;
       }
-      __syncthreads();
-      if (NSEG > 1 && tid < NSEG * DK) {
-        const int i = tid % DK, seg = tid / DK;
-        float pre = 0.f;
-        for (int s2 = 0; s2 < seg; ++s2) pre += sTot[s2 * DK + i];
-        if (seg > 0)
-          for (int r = seg * SEGL; r < (seg + 1) * SEGL; ++r) sG[r * DK + i] += pre;
-      }
-      __syncthreads();
-      for (int i = tid; i < DK; i += NT) {
-        sGam[i] = __expf(sG[(CH - 1) * DK + i]);
-#pragma unroll
-        for (int R = 1; R < 4; ++R)
-          for (int J = 0; J < R; ++J) sM[strict_pair(R, J) * DK + i] = __expf(sG[16 * R * DK + i] - sG[16 * J * DK + i]);
-      }
-    } else {
-      __syncthreads();
-    }
-
-    // ---- (2) decayed operands in LDS --------------------------------------------
-    for (int idx = tid; idx < CH * (DK / 4); idx += NT) {
-      const int r = idx / (DK / 4);
-      const int i0 = (idx % (DK / 4)) * 4;
-      const int R = r >> 4;
-      float kk[4], qq[4];
-      const bool live = r < nrows;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        kk[j] = live ? Io<IO>::load(gk, tok(t0 + r) * DK + i0 + j) : 0.f;
-        qq[j] = live ? Io<IO>::load(gq, tok(t0 + r) * DK + i0 + j) : 0.f;
-      }
-      const float be = sBeta[r];
-      f32x4 xk, y, xq, qh;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = i0 + j;
-        float e_xk = 1.f, e_y = 1.f, e_xq = 1.f, e_q = 1.f, e_kr = 1.f, e_kd = 1.f;
-        if (GATE != GATE_NONE) {
-          const float g = G(r, i), gR = G(16 * R, i), gC = G(CH - 1, i);
-          const float gread = p.literal ? (r > 0 ? G(r - 1, i) : 0.f) : g;
-          e_xk = __expf(gread - gR);
-          e_y = __expf(gR - g);
-          e_xq = __expf(g - gR);
-          e_q = __expf(g);
-          e_kr = __expf(gread);
-          e_kd = __expf(gC - g);
+      if constexpr (NSEG > 1) {
+        __syncthreads();
+        if (tid < NSEG * DK) {
+          const int i = tid % DK, seg = tid / DK;
+          float pre = 0.f;
+          for (int s2 = 0; s2 < seg; ++s2) pre += sTot[s2 * DK + i];
+          if (seg > 0)
+            for (int r = seg * SEGL; r < (seg + 1) * SEGL; ++r) sG[r * DK + i] += pre;
         }
-        xk[j] = be * kk[j] * e_xk;
-        y[j] = kk[j] * e_y;
-        xq[j] = qq[j] * e_xq;
-        qh[j] = qq[j] * e_q;
-        sKrT[i * LCH + r] = O::from(be * kk[j] * e_kr);
-        sKdT[i * LCH + r] = O::from(kk[j] * e_kd);
       }
-      O::st(sXK + r * LDK + i0, O::cvt(xk));
-      O::st(sY + r * LDK + i0, O::cvt(y));
-      O::st(sXQ + r * LDK + i0, O::cvt(xq));
-      O::st(sQh + r * LDK + i0, O::cvt(qh));
     }
-    for (int idx = tid; idx < CH * (DVT / 4); idx += NT) {
-      const int r = idx / (DVT / 4);
-      const int c0 = (idx % (DVT / 4)) * 4;
-      const bool live = r < nrows;
-      const float be = sBeta[r];
+    // beta * v, transposed
+    for (int task = tid; task < DVT * 8; task += NT) {
+      const int c = task % DVT, rg = task / DVT;
+      frag f0, f1;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float vv = live ? Io<IO>::load(gv, tok(t0 + r) * dv + col0 + c0 + j) : 0.f;
-        sVT[(c0 + j) * LCH + r] = O::from(be * vv);
+      for (int e = 0; e < 4; ++e) {
+        f0[e] = O::from(sBeta[8 * rg + e] * O::to(sV[(8 * rg + e) * LVT + c]));
+        f1[e] = O::from(sBeta[8 * rg + 4 + e] * O::to(sV[(8 * rg + 4 + e) * LVT + c]));
       }
+      *reinterpret_cast<frag*>(sVT + c * LCH + 8 * rg) = f0;
+      *reinterpret_cast<frag*>(sVT + c * LCH + 8 * rg + 4) = f1;
     }
     __syncthreads();
 
-    // ---- (3) 16x16 blocks of A (strictly lower) and P (lower incl. diagonal) ----
-    for (int task = wave; task < 20; task += NW) {
-      const bool isP = task >= 10;
-      int R, J;
-      lower_pair(task % 10, R, J);
-      const T* rows = isP ? sXQ : sXK;
+    if constexpr (!RAW) {
+      // decayed operands; X_K and X_Q overwrite the raw tiles in place
+      for (int i = tid; i < DK; i += NT) {
+        sGamC[i] = __expf(sG[(CH - 1) * DK + i]);
+#pragma unroll
+        for (int R = 1; R < 4; ++R)
+#pragma unroll
+          for (int J = 0; J < R; ++J)
+            sM[strict_pair(R, J) * DK + i] = __expf(sG[16 * R * DK + i] - sG[16 * J * DK + i]);
+      }
+      for (int task = tid; task < CH * (DK / 4); task += NT) {
+        const int r = task / (DK / 4), i0 = (task % (DK / 4)) * 4, R = r >> 4;
+        const f32x4 kk = O::f32(O::ld(sK + r * LDK + i0));
+        const f32x4 qq = O::f32(O::ld(sQ + r * LDK + i0));
+        const float be = sBeta[r];
+        f32x4 xk, y, xq, qh;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = i0 + j;
+          const float g = sG[r * DK + i], gR = sG[16 * R * DK + i], gC = sG[(CH - 1) * DK + i];
+          const float gread = p.literal ? (r > 0 ? sG[(r - 1) * DK + i] : 0.f) : g;
+          xk[j] = be * kk[j] * __expf(gread - gR);
+          y[j] = kk[j] * __expf(gR - g);
+          xq[j] = qq[j] * __expf(g - gR);
+          qh[j] = qq[j] * __expf(g);
+          sKrT[i * LCH + r] = O::from(be * kk[j] * __expf(gread));
+          sKdT[i * LCH + r] = O::from(kk[j] * __expf(gC - g));
+        }
+        *reinterpret_cast<frag*>(sK + r * LDK + i0) = O::cvt(xk);
+        *reinterpret_cast<frag*>(sY + r * LDK + i0) = O::cvt(y);
+        *reinterpret_cast<frag*>(sQ + r * LDK + i0) = O::cvt(xq);
+        *reinterpret_cast<frag*>(sQh + r * LDK + i0) = O::cvt(qh);
+      }
+      __syncthreads();
+    }
+
+    // ---- (2) 16x16 blocks of A (strictly lower) and P (lower incl. diagonal) ------
+    // Wave 0 computes the four diagonal blocks of A and inverts them while the
+    // other waves compute the off-diagonal blocks of A and all blocks of P.
+    auto block_product = [&](bool isP, int R, int J) -> f32x4 {
+      const T* rows = isP ? sQ : sK;
+      const T* cols = RAW ? sK : sY;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < DK / 32; ++kb) {
         const int c = 32 * kb + 4 * lg;
         frag a0 = O::ld(rows + (16 * R + lr) * LDK + c);
         frag a1 = O::ld(rows + (16 * R + lr) * LDK + c + 16);
-        frag b0 = O::ld(sY + (16 * J + lr) * LDK + c);
-        frag b1 = O::ld(sY + (16 * J + lr) * LDK + c + 16);
-        if (GATE != GATE_NONE && R > J) {
-          const int pr = strict_pair(R, J);
-          f32x4 m0, m1;
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            m0[s] = GATE == GATE_CHANNEL ? sM[pr * DK + c + s] : sM[pr];
-            m1[s] = GATE == GATE_CHANNEL ? sM[pr * DK + c + 16 + s] : sM[pr];
+        frag b0 = O::ld(cols + (16 * J + lr) * LDK + c);
+        frag b1 = O::ld(cols + (16 * J + lr) * LDK + c + 16);
+        if constexpr (GATE == GATE_CHANNEL) {
+          if (R > J) {
+            const float* m = sM + strict_pair(R, J) * DK + c;
+            b0 = O::cvt(O::f32(b0) * *reinterpret_cast<const f32x4*>(m));
+            b1 = O::cvt(O::f32(b1) * *reinterpret_cast<const f32x4*>(m + 16));
           }
-          b0 = O::cvt(O::f32(b0) * m0);
-          b1 = O::cvt(O::f32(b1) * m1);
         }
         acc = O::mma2(acc, a0, a1, b0, b1);
       }
+      return acc;
+    };
+    auto store_block = [&](bool isP, int R, int J, f32x4 acc) {
+      const int j = 16 * J + lr;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const int rr = 4 * lg + s;
+        const int rr = 4 * lg + s, r = 16 * R + rr;
+        float val = acc[s];
+        if constexpr (GATE == GATE_SCALAR) val *= __expf((isP ? sGr[r] : sGrd[r]) - sGr[j]);
         if (!isP) {
-          sA[(16 * R + rr) * LA + 16 * J + lr] = (R == J && rr <= lr) ? 0.f : acc[s];
+          if constexpr (RAW) val *= sBr[r];
+          sA[r * LA + j] = (R == J && rr <= lr) ? 0.f : val;
         } else {
-          sP[(16 * R + rr) * LCH + 16 * J + lr] = O::from((R == J && rr < lr) ? 0.f : acc[s]);
+          sP[r * LCH + j] = O::from((R == J && rr < lr) ? 0.f : val);
         }
       }
-    }
-    __syncthreads();
-
-    // ---- (4) inverses of the four unit-lower diagonal blocks of I + A -----------
+    };
+    constexpr int W0 = NW == 2 ? 4 : 0;             // off-diagonal tasks taken by wave 0
+    constexpr int PER = NW > 1 ? (16 - W0 + NW - 2) / (NW - 1) : 16;
     if (wave == 0) {
+#pragma unroll
+      for (int R = 0; R < 4; ++R) store_block(false, R, R, block_product(false, R, R));
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // unit-lower inverse of each diagonal block, one column per lane
       const int R = lane >> 4, j = lane & 15;
       float x[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float acc = (i == j) ? 1.f : 0.f;
+        const float* arow = sA + (16 * R + i) * LA + 16 * R;
+        float s0 = (i == j) ? 1.f : 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
 #pragma unroll
-        for (int kk = 0; kk < i; ++kk) acc -= sA[(16 * R + i) * LA + 16 * R + kk] * x[kk];
-        x[i] = acc;
+        for (int kk = 0; kk + 3 < i; kk += 4) {
+          s0 -= arow[kk] * x[kk];
+          s1 -= arow[kk + 1] * x[kk + 1];
+          s2 -= arow[kk + 2] * x[kk + 2];
+          s3 -= arow[kk + 3] * x[kk + 3];
+        }
+#pragma unroll
+        for (int kk = i & ~3; kk < i; ++kk) s0 -= arow[kk] * x[kk];
+        x[i] = (s0 + s1) + (s2 + s3);
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) sXi[(16 * R + i) * LXI + j] = O::from(x[i]);
+#pragma unroll
+      for (int t = 16 - W0; t < 16; ++t) {
+        bool isP; int R2, J2;
+        other_task(t, isP, R2, J2);
+        store_block(isP, R2, J2, block_product(isP, R2, J2));
+      }
+    } else {
+      const int lo = (wave - 1) * PER;
+      const int hi = lo + PER < 16 - W0 ? lo + PER : 16 - W0;
+      for (int t = lo; t < hi; ++t) {
+        bool isP; int R2, J2;
+        other_task(t, isP, R2, J2);
+        store_block(isP, R2, J2, block_product(isP, R2, J2));
+      }
     }
     __syncthreads();
 
-    // ---- (5) W and U by block forward substitution (per wave, own columns) ------
-    // out_R = X_RR (rhs_R - sum_{J<R} A_RJ out_J), rhs taken from a transposed
-    // [column][row] buffer.
-    auto solve = [&](const T* rhsT, int colrow, f32x4* out) {
-      frag outb[4];
+    // ---- (3) W and U by block forward substitution (per wave, own columns) --------
+    // out_R = X_RR (rhs_R - sum_{J<R} A_RJ out_J); the CBW channel blocks of W and
+    // the wave's block of U advance together.
+    constexpr int NB = CBW + 1;
+    f32x4 outf[NB][4];
+    frag outb[NB][4];
 #pragma unroll
-      for (int R = 0; R < 4; ++R) {
-        f32x4 acc = O::f32(O::ld(rhsT + colrow * LCH + 16 * R + 4 * lg));
+    for (int R = 0; R < 4; ++R) {
+      frag aR[3];
+#pragma unroll
+      for (int J = 0; J < R; ++J)
+        aR[J] = O::cvt(-*reinterpret_cast<const f32x4*>(sA + (16 * R + lr) * LA + 16 * J + 4 * lg));
+      const frag xi = O::ld(sXi + (16 * R + lr) * LXI + 4 * lg);
+#pragma unroll
+      for (int c = 0; c < NB; ++c) {
+        f32x4 acc;
+        if (c < CBW) {
+          const int ch = (wave * CBW + c) * 16 + lr;
+          if constexpr (RAW) {
+            acc = O::f32(O::ld(sKT + ch * LCH + 16 * R + 4 * lg));
+#pragma unroll
+            for (int s = 0; s < 4; ++s) acc[s] *= sEw[16 * R + 4 * lg + s];
+          } else {
+            acc = O::f32(O::ld(sKrT + ch * LCH + 16 * R + 4 * lg));
+          }
+        } else {
+          acc = O::f32(O::ld(sVT + (16 * wave + lr) * LCH + 16 * R + 4 * lg));
+        }
         int J = 0;
 #pragma unroll
-        for (; J + 1 < R; J += 2) {
-          const float* ar = sA + (16 * R + lr) * LA;
-          f32x4 a0 = *reinterpret_cast<const f32x4*>(ar + 16 * J + 4 * lg);
-          f32x4 a1 = *reinterpret_cast<const f32x4*>(ar + 16 * (J + 1) + 4 * lg);
-          acc = O::mma2(acc, O::cvt(-a0), O::cvt(-a1), outb[J], outb[J + 1]);
-        }
-        if (J < R) {
-          f32x4 a0 = *reinterpret_cast<const f32x4*>(sA + (16 * R + lr) * LA + 16 * J + 4 * lg);
-          acc = O::mma1(acc, O::cvt(-a0), outb[J]);
-        }
+        for (; J + 1 < R; J += 2) acc = O::mma2(acc, aR[J], aR[J + 1], outb[c][J], outb[c][J + 1]);
+        if (J < R) acc = O::mma1(acc, aR[J], outb[c][J]);
         f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        z = O::mma1(z, O::ld(sXi + (16 * R + lr) * LXI + 4 * lg), O::cvt(acc));
-        out[R] = z;
-        outb[R] = O::cvt(z);
+        z = O::mma1(z, xi, O::cvt(acc));
+        outf[c][R] = z;
+        outb[c][R] = O::cvt(z);
       }
-    };
+    }
 #pragma unroll
-    for (int cb = 0; cb < CBW; ++cb) {
-      const int ch = (wave * CBW + cb) * 16;
-      f32x4 w[4];
-      solve(sKrT, ch + lr, w);
-      // sW shares storage with the row operand of A, which is dead after (3).
+    for (int c = 0; c < CBW; ++c) {
+      const int ch = (wave * CBW + c) * 16 + lr;
 #pragma unroll
       for (int R = 0; R < 4; ++R)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) sW[(16 * R + 4 * lg + s) * LDK + ch + lr] = O::from(w[R][s]);
+        for (int s = 0; s < 4; ++s) sW[(16 * R + 4 * lg + s) * LDK + ch] = O::from(outf[c][R][s]);
     }
-    f32x4 U[4];
-    solve(sVT, 16 * wave + lr, U);
     __syncthreads();
 
-    // ---- (6) state pass and output for this wave's 16 columns ------------------
+    // ---- (4) state pass and output for this wave's 16 columns ---------------------
     frag Sb[DKT];
 #pragma unroll
     for (int t = 0; t < DKT; ++t) Sb[t] = O::cvt(S[t]);
-    frag Db[4];
+    frag Db[4], Ds[4];
 #pragma unroll
     for (int R = 0; R < 4; ++R) {            // Delta = U - W S
       f32x4 ws = {0.f, 0.f, 0.f, 0.f};
@@ -420,39 +564,61 @@ __global__ __launch_bounds__(NW * 64) void chunk_fwd_kernel(ChunkParams p, int n
         const T* wr = sW + (16 * R + lr) * LDK + 32 * kb + 4 * lg;
         ws = O::mma2(ws, O::ld(wr), O::ld(wr + 16), Sb[2 * kb], Sb[2 * kb + 1]);
       }
-      Db[R] = O::cvt(U[R] - ws);
-    }
+      const f32x4 d = outf[CBW][R] - ws;
+      Db[R] = O::cvt(d);
+      if constexpr (GATE == GATE_SCALAR) {
+        f32x4 ds;
 #pragma unroll
-    for (int R = 0; R < 4; ++R) {            // O = (Q e^g) S + P Delta
-      f32x4 oacc = {0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < 4; ++s) ds[s] = d[s] * sEd[16 * R + 4 * lg + s];
+        Ds[R] = O::cvt(ds);
+      } else {
+        Ds[R] = Db[R];
+      }
+    }
+    // O^T tile (rows = this wave's 16 columns, columns = 16 tokens):
+    //   S^T (Q e^g)^T + Delta^T P^T; a lane ends up with 4 adjacent output columns.
+    const T* qsrc = RAW ? sQ : sQh;
+#pragma unroll
+    for (int R = 0; R < 4; ++R) {
+      f32x4 oq = {0.f, 0.f, 0.f, 0.f}, op = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < DK / 32; ++kb) {
-        const T* qr = sQh + (16 * R + lr) * LDK + 32 * kb + 4 * lg;
-        oacc = O::mma2(oacc, O::ld(qr), O::ld(qr + 16), Sb[2 * kb], Sb[2 * kb + 1]);
+        const T* qr = qsrc + (16 * R + lr) * LDK + 32 * kb + 4 * lg;
+        oq = O::mma2(oq, Sb[2 * kb], Sb[2 * kb + 1], O::ld(qr), O::ld(qr + 16));
       }
       const T* pr = sP + (16 * R + lr) * LCH + 4 * lg;
       int J = 0;
 #pragma unroll
-      for (; J + 1 <= R; J += 2) oacc = O::mma2(oacc, O::ld(pr + 16 * J), O::ld(pr + 16 * (J + 1)), Db[J], Db[J + 1]);
-      if (J <= R) oacc = O::mma1(oacc, O::ld(pr + 16 * J), Db[J]);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int r = 16 * R + 4 * lg + s;
-        if (r < nrows) Io<IO>::store(go, tok(t0 + r) * dv + scol, oacc[s]);
+      for (; J + 1 <= R; J += 2) op = O::mma2(op, Db[J], Db[J + 1], O::ld(pr + 16 * J), O::ld(pr + 16 * (J + 1)));
+      if (J <= R) op = O::mma1(op, Db[J], O::ld(pr + 16 * J));
+      const int r = 16 * R + lr;
+      f32x4 ov;
+      if constexpr (GATE == GATE_SCALAR) ov = oq * sEo[r] + op; else ov = oq + op;
+      if (r < nrows) {
+        elem* dst = go + tok(t0 + r) * dv + col0 + 16 * wave + 4 * lg;
+        if constexpr (IO == IO_BF16) {
+          const uint32_t lo = uint32_t(f32_to_bf16_bits(ov[0])) | (uint32_t(f32_to_bf16_bits(ov[1])) << 16);
+          const uint32_t hi = uint32_t(f32_to_bf16_bits(ov[2])) | (uint32_t(f32_to_bf16_bits(ov[3])) << 16);
+          *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+        } else {
+          *reinterpret_cast<float4*>(dst) = make_float4(ov[0], ov[1], ov[2], ov[3]);
+        }
       }
     }
+    // S' = diag(e^{g_63}) S + (K e^{g_63 - g})^T Delta
+    const T* kdt = RAW ? sKT : sKdT;
 #pragma unroll
-    for (int t = 0; t < DKT; ++t) {          // S' = diag(e^{g_63}) S + Kd^T Delta
+    for (int t = 0; t < DKT; ++t) {
       f32x4 acc = S[t];
-      if (GATE == GATE_CHANNEL) {
+      if constexpr (GATE == GATE_CHANNEL) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) acc[s] *= sGam[16 * t + 4 * lg + s];
-      } else if (GATE == GATE_SCALAR) {
-        acc = acc * sGam[0];
+        for (int s = 0; s < 4; ++s) acc[s] *= sGamC[16 * t + 4 * lg + s];
+      } else if constexpr (GATE == GATE_SCALAR) {
+        acc = acc * sGamR[0];
       }
-      const T* kr = sKdT + (16 * t + lr) * LCH + 4 * lg;
-      acc = O::mma2(acc, O::ld(kr), O::ld(kr + 16), Db[0], Db[1]);
-      acc = O::mma2(acc, O::ld(kr + 32), O::ld(kr + 48), Db[2], Db[3]);
+      const T* kr = kdt + (16 * t + lr) * LCH + 4 * lg;
+      acc = O::mma2(acc, O::ld(kr), O::ld(kr + 16), Ds[0], Ds[1]);
+      acc = O::mma2(acc, O::ld(kr + 32), O::ld(kr + 48), Ds[2], Ds[3]);
       S[t] = acc;
     }
     __syncthreads();                          // LDS is rewritten by the next chunk
@@ -477,8 +643,8 @@ static hipError_t launch_chunk_t(const ChunkParams& p, hipStream_t stream) {
 
 template <int IO, int GATE, int DK>
 static hipError_t launch_chunk_dk(const ChunkParams& p, hipStream_t stream) {
-  if constexpr (IO == IO_F32) {
-    return launch_chunk_t<IO, GATE, DK, 2>(p, stream);
+  if constexpr (IO == IO_F32 || GATE == GATE_CHANNEL) {
+    return launch_chunk_t<IO, GATE, DK, 2>(p, stream);   // LDS budget: 32-column tiles
   } else {
     // Four waves (64 columns per workgroup) when that still gives at least one
     // workgroup per CU, otherwise two waves (32 columns) to fill the 256 CUs.
