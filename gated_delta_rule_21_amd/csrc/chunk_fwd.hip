@@ -45,6 +45,8 @@
 //
 // Products run on bf16 MFMA with fp32 accumulation for bf16 I/O and on fp32
 // MFMA for fp32 I/O; the state stays fp32.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launchers.h"
 
@@ -100,26 +102,26 @@ struct Layout {
   static constexpr int LCH = CH + PAD;
   static constexpr int LA = CH + 4;
   static constexpr int LXI = 16 + PAD;
+  static constexpr int LSC = 20;                       // per-wave 16x16 fp32 scratch stride
   static constexpr int DVT = 16 * NW;
-  static constexpr int LVT = DVT + PAD;
   static constexpr int NSEG = (64 * NW) / DK > 0 ? (64 * NW) / DK : 1;
   static constexpr size_t RM = size_t(CH) * LDK * sizeof(T);      // [64][DK]
   static constexpr size_t TR = size_t(DK) * LCH * sizeof(T);      // [DK][64]
   static constexpr size_t A_B = size_t(CH) * LA * 4;
   static constexpr size_t P_B = size_t(CH) * LCH * sizeof(T);
   static constexpr size_t XI_B = size_t(CH) * LXI * sizeof(T);
-  static constexpr size_t V_B = size_t(CH) * LVT * sizeof(T);
   static constexpr size_t VT_B = size_t(DVT) * LCH * sizeof(T);
+  static constexpr size_t SC_B = size_t(NW) * 16 * LSC * 4;
   // common regions
-  static constexpr size_t OFF_K = 0;                     // raw k (channel: X_K in place, then W)
+  static constexpr size_t OFF_K = 0;                     // raw k (channel: X_K in place), then W
   static constexpr size_t OFF_Q = OFF_K + RM;            // raw q (channel: X_Q in place)
-  static constexpr size_t OFF_V = OFF_Q + RM;            // raw v tile, then the inverses
-  static constexpr size_t OFF_VT = OFF_V + V_B;          // beta * v, transposed
-  static constexpr size_t OFF_X = OFF_VT + VT_B;         // gate-dependent regions start here
+  static constexpr size_t OFF_VT = OFF_Q + RM;           // raw v tile, transposed
+  static constexpr size_t OFF_XI = OFF_VT + VT_B;        // inverses of the diagonal blocks
+  static constexpr size_t OFF_SC = OFF_XI + XI_B;        // per-wave scratch of the inversion
+  static constexpr size_t OFF_X = OFF_SC + SC_B;         // gate-dependent regions start here
   // raw gates
   static constexpr size_t R_KT = OFF_X;                  // k transposed
-  static constexpr size_t R_W = R_KT + TR;
-  static constexpr size_t R_A = R_W + RM;
+  static constexpr size_t R_A = R_KT + TR;
   static constexpr size_t R_P = R_A + A_B;
   static constexpr size_t R_SMALL = R_P + P_B;           // beta, g, g_read, e_w, e_o, e_d, gamma
   static constexpr size_t R_TOTAL = R_SMALL + 7 * CH * 4;
@@ -136,26 +138,63 @@ struct Layout {
   static constexpr size_t C_TOT = C_M + 6 * DK * 4;
   static constexpr size_t C_TOTAL = C_TOT + NSEG * DK * 4;
   static constexpr size_t TOTAL = RAW ? R_TOTAL : C_TOTAL;
-  static_assert(V_B >= XI_B, "the inverses reuse the raw v tile");
 };
 
-// Off-diagonal 16x16 tasks of the A/P phase: 6 strictly-lower blocks of A, then
-// the 10 lower blocks (incl. diagonal) of P.
-__device__ __forceinline__ void other_task(int t, bool& isP, int& R, int& J) {
-  if (t < 6) {
-    isP = false;
-    R = 1 + (t >= 1) + (t >= 3);
-    J = t - R * (R - 1) / 2;
-  } else {
-    isP = true;
-    const int u = t - 6;
-    R = (u >= 1) + (u >= 3) + (u >= 6);
-    J = u - R * (R + 1) / 2;
-  }
-}
 __device__ __forceinline__ int strict_pair(int R, int J) { return R * (R - 1) / 2 + J; }
 
 __device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+// x if keep else 0, component by component (a whole-vector select can be lowered
+// through private memory)
+__device__ __forceinline__ uint4 keep_or_zero(bool keep, uint4 x) {
+  const uint32_t m = keep ? 0xffffffffu : 0u;
+  return make_uint4(x.x & m, x.y & m, x.z & m, x.w & m);
+}
+
+// Ordering point for LDS traffic between the lanes of one wave.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// (I + N)^{-1} of a strictly lower 16x16 block N held as an accumulator tile, by
+// the finite Neumann product (I - N)(I + N^2)(I + N^4)(I + N^8) (N^16 = 0), on
+// fp32 MFMA.  `scr` is this wave's 16x16 fp32 scratch, used to turn an
+// accumulator tile into a row-major A operand.
+__device__ __forceinline__ f32x4 unit_lower_inverse(f32x4 N, float* scr, int lr, int lg) {
+  constexpr int LSC = 20;
+  auto put = [&](f32x4 M) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) scr[(4 * lg + s) * LSC + lr] = M[s];
+  };
+  auto rows = [&]() -> f32x4 { return *reinterpret_cast<const f32x4*>(scr + lr * LSC + 4 * lg); };
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  f32x4 Y;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) Y[s] = (4 * lg + s == lr ? 1.f : 0.f) - N[s];
+  put(N);
+  wave_sync();
+  f32x4 a = rows();
+  wave_sync();
+  f32x4 P = mma_k16_f32(zero, a, N);          // N^2
+  put(P);
+  wave_sync();
+  a = rows();
+  wave_sync();
+  Y = mma_k16_f32(Y, a, Y);                   // (I + N^2)(I - N)
+  P = mma_k16_f32(zero, a, P);                // N^4
+  put(P);
+  wave_sync();
+  a = rows();
+  wave_sync();
+  Y = mma_k16_f32(Y, a, Y);
+  P = mma_k16_f32(zero, a, P);                // N^8
+  put(P);
+  wave_sync();
+  a = rows();
+  wave_sync();
+  return mma_k16_f32(Y, a, Y);
+}
 
 template <int IO, int GATE, int DK, int NW>
 __global__ __launch_bounds__(NW * 64) void chunk_fwd_kernel(ChunkParams p, int n_tiles) {
@@ -169,19 +208,23 @@ __global__ __launch_bounds__(NW * 64) void chunk_fwd_kernel(ChunkParams p, int n
   constexpr int DVT = 16 * NW;
   constexpr int DKT = DK / 16;
   constexpr int CBW = DKT / NW;          // 16-channel blocks of W solved per wave
-  constexpr int LDK = L::LDK, LCH = L::LCH, LA = L::LA, LXI = L::LXI, LVT = L::LVT;
+  constexpr int LDK = L::LDK, LCH = L::LCH, LA = L::LA, LXI = L::LXI;
   constexpr int EPV = 16 / int(sizeof(elem));   // elements per 16-byte load
-  constexpr int KROW = DK / EPV, VROW = DVT / EPV;
-  constexpr int KV = CH * KROW / NT, VV = CH * VROW / NT;
+  constexpr int KROW = DK / EPV;
+  constexpr int KV = CH * KROW / NT;            // row-major 16-byte pieces of a k (q) tile per thread
+  constexpr int KTT = RAW ? DK * 8 / NT : 1;    // 8-row column runs of k^T per thread
+  constexpr int VTT = DVT * 8 / NT;             // 8-row column runs of v^T per thread
   static_assert(CBW >= 1 && CBW * NW == DKT, "channel blocks must split over waves");
-  static_assert(KV * NT == CH * KROW && VV * NT == CH * VROW && VV >= 1, "tile loads must split evenly");
+  static_assert(KV * NT == CH * KROW && VTT * NT == DVT * 8 && (!RAW || KTT * NT == DK * 8), "even split");
   static_assert(L::TOTAL <= 163840, "LDS budget");
 
   __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
   T* sK = reinterpret_cast<T*>(smem + L::OFF_K);
   T* sQ = reinterpret_cast<T*>(smem + L::OFF_Q);
-  T* sV = reinterpret_cast<T*>(smem + L::OFF_V);
   T* sVT = reinterpret_cast<T*>(smem + L::OFF_VT);
+  T* sXi = reinterpret_cast<T*>(smem + L::OFF_XI);
+  float* sScr = reinterpret_cast<float*>(smem + L::OFF_SC);
+  T* sW = sK;                       // k is dead once A and P are formed
   // raw-gate regions
   T* sKT = reinterpret_cast<T*>(smem + L::R_KT);
   float* sSmall = reinterpret_cast<float*>(smem + L::R_SMALL);
@@ -202,11 +245,8 @@ __global__ __launch_bounds__(NW * 64) void chunk_fwd_kernel(ChunkParams p, int n
   float* sGamC = reinterpret_cast<float*>(smem + L::C_GAM);
   float* sM = reinterpret_cast<float*>(smem + L::C_M);
   float* sTot = reinterpret_cast<float*>(smem + L::C_TOT);
-  // shared names
-  T* sW = RAW ? reinterpret_cast<T*>(smem + L::R_W) : sK;
   float* sA = RAW ? reinterpret_cast<float*>(smem + L::R_A) : sG;
   T* sP = RAW ? reinterpret_cast<T*>(smem + L::R_P) : reinterpret_cast<T*>(smem + L::C_G + L::A_B);
-  T* sXi = sV;   // the raw v tile is dead once its transpose is built
   float* sBeta = RAW ? sBr : sBc;
 
   const elem* gq = static_cast<const elem*>(p.q);
@@ -246,30 +286,69 @@ __global__ __launch_bounds__(NW * 64) void chunk_fwd_kernel(ChunkParams p, int n
       S[t][s] = p.S0 ? p.S0[(bh * DK + 16 * t + 4 * lg + s) * dv + scol] : 0.f;
 
   // ---- register prefetch of one chunk's inputs ----------------------------------
-  uint4 pk[KV], pq[KV], pl[GATE == GATE_CHANNEL ? KV : 1], pv[VV];
+  // Rows past the end of the sequence are read from the last valid row (so no
+  // load needs a guard and none stalls the issuing wave) and zeroed when the
+  // registers are written to LDS.
+  constexpr int RW = 8 * int(sizeof(elem)) / 4;         // 32-bit words in an 8-element run
+  uint4 pk[KV], pq[KV], pl[GATE == GATE_CHANNEL ? KV : 1];
+  uint32_t pkt[KTT][RW], pvt[VTT][RW];
+  // element e of a 16-byte piece / of an 8-element run, as float
+  auto elem_of = [&](const uint32_t* w, int e) -> float {
+    if constexpr (IO == IO_BF16) return bf16_bits_to_f32(static_cast<uint16_t>(w[e >> 1] >> (16 * (e & 1))));
+    else return __uint_as_float(w[e]);
+  };
+  auto load_run = [&](uint32_t* w, const elem* base, int64_t t0m, int row0, int last, int64_t stride)
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int row = row0 + e;
+      const elem x = base[tok(t0m + (row < last ? row : last)) * stride];
+      if constexpr (IO == IO_BF16) {
+        if (e & 1) w[e >> 1] |= uint32_t(x) << 16; else w[e >> 1] = uint32_t(x);
+      } else {
+        w[e] = __float_as_uint(x);
+      }
+    }
+  };
   float pb = 0.f, pls = 0.f;
-  auto prefetch = [&](int64_t m) {
+  auto prefetch = [&](int64_t m) __attribute__((always_inline)) {
     const int64_t t0m = m * CH;
-    const int nr = static_cast<int>(p.T - t0m < CH ? p.T - t0m : CH);
-    const uint4 z = make_uint4(0, 0, 0, 0);
+    const int last = static_cast<int>(p.T - t0m < CH ? p.T - t0m : CH) - 1;
 #pragma unroll
     for (int v = 0; v < KV; ++v) {
       const int seg = tid + v * NT, row = seg / KROW, c = (seg % KROW) * EPV;
-      const bool live = row < nr;
-      const int64_t off = tok(t0m + row) * DK + c;
-      pk[v] = live ? ldg16(gk + off) : z;
-      pq[v] = live ? ldg16(gq + off) : z;
-      if constexpr (GATE == GATE_CHANNEL) pl[v] = live ? ldg16(gla + off) : z;
+      const int64_t off = tok(t0m + (row < last ? row : last)) * DK + c;
+      pk[v] = ldg16(gk + off);
+      pq[v] = ldg16(gq + off);
+      if constexpr (GATE == GATE_CHANNEL) pl[v] = ldg16(gla + off);
+    }
+    if constexpr (RAW) {
+#pragma unroll
+      for (int j = 0; j < KTT; ++j) {
+        const int task = tid + j * NT, i = task % DK, rg = task / DK;
+        load_run(pkt[j], gk + i, t0m, 8 * rg, last, DK);
+      }
     }
 #pragma unroll
-    for (int v = 0; v < VV; ++v) {
-      const int seg = tid + v * NT, row = seg / VROW, c = (seg % VROW) * EPV;
-      pv[v] = row < nr ? ldg16(gv + tok(t0m + row) * dv + col0 + c) : z;
+    for (int j = 0; j < VTT; ++j) {
+      const int task = tid + j * NT, c = task % DVT, rg = task / DVT;
+      load_run(pvt[j], gv + col0 + c, t0m, 8 * rg, last, dv);
     }
     if (tid < CH) {
-      pb = tid < nr ? Io<IO>::load(gbeta, tok(t0m + tid)) : 0.f;
-      if constexpr (GATE == GATE_SCALAR) pls = tid < nr ? Io<IO>::load(gla, tok(t0m + tid)) : 0.f;
+      const int row = tid < last ? tid : last;
+      pb = Io<IO>::load(gbeta, tok(t0m + row));
+      if constexpr (GATE == GATE_SCALAR) pls = Io<IO>::load(gla, tok(t0m + row));
     }
+  };
+  auto put_run = [&](T* dst, const uint32_t* w, int row0, int nrows) __attribute__((always_inline)) {   // 8 rows of one column
+    frag f0, f1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f0[e] = O::from(row0 + e < nrows ? elem_of(w, e) : 0.f);
+      f1[e] = O::from(row0 + 4 + e < nrows ? elem_of(w, e + 4) : 0.f);
+    }
+    *reinterpret_cast<frag*>(dst) = f0;
+    *reinterpret_cast<frag*>(dst + 4) = f1;
   };
 
   const int64_t nchunks = (p.T + CH - 1) / CH;
@@ -279,72 +358,64 @@ __global__ __launch_bounds__(NW * 64) void chunk_fwd_kernel(ChunkParams p, int n
     const int64_t t0 = n * CH;
     const int nrows = static_cast<int>(p.T - t0 < CH ? p.T - t0 : CH);
 
-    // ---- (0) raw chunk from registers into LDS; start loading the next chunk ---
+    // ---- (0) chunk from registers into LDS, per-chunk log-gate; next chunk's loads
+    {
 #pragma unroll
-    for (int v = 0; v < KV; ++v) {
-      const int seg = tid + v * NT, row = seg / KROW, c = (seg % KROW) * EPV;
-      *reinterpret_cast<uint4*>(sK + row * LDK + c) = pk[v];
-      *reinterpret_cast<uint4*>(sQ + row * LDK + c) = pq[v];
-      if constexpr (GATE == GATE_CHANNEL) {
-        const elem* e = reinterpret_cast<const elem*>(&pl[v]);
+      for (int v = 0; v < KV; ++v) {
+        const int seg = tid + v * NT, row = seg / KROW, c = (seg % KROW) * EPV;
+        const bool live = row < nrows;
+        *reinterpret_cast<uint4*>(sK + row * LDK + c) = keep_or_zero(live, pk[v]);
+        *reinterpret_cast<uint4*>(sQ + row * LDK + c) = keep_or_zero(live, pq[v]);
+        if constexpr (GATE == GATE_CHANNEL) {
+          const uint32_t w[4] = {pl[v].x, pl[v].y, pl[v].z, pl[v].w};
 #pragma unroll
-        for (int j = 0; j < EPV; ++j) {
-          float x;
-          if constexpr (IO == IO_BF16) x = bf16_bits_to_f32(e[j]); else x = e[j];
-          sG[row * DK + c + j] = x;
+          for (int j = 0; j < EPV; ++j) sG[row * DK + c + j] = live ? elem_of(w, j) : 0.f;
         }
       }
-    }
+      if constexpr (RAW) {
 #pragma unroll
-    for (int v = 0; v < VV; ++v) {
-      const int seg = tid + v * NT, row = seg / VROW, c = (seg % VROW) * EPV;
-      *reinterpret_cast<uint4*>(sV + row * LVT + c) = pv[v];
-    }
-    if (tid < CH) {
-      sBeta[tid] = pb;
-      if constexpr (GATE == GATE_SCALAR) sGr[tid] = pls;   // raw log-gate; scanned below
+        for (int j = 0; j < KTT; ++j) {
+          const int task = tid + j * NT, i = task % DK, rg = task / DK;
+          put_run(sKT + i * LCH + 8 * rg, pkt[j], 8 * rg, nrows);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < VTT; ++j) {
+        const int task = tid + j * NT, c = task % DVT, rg = task / DVT;
+        put_run(sVT + c * LCH + 8 * rg, pvt[j], 8 * rg, nrows);
+      }
+      if constexpr (RAW) {
+        if (wave == 0) {            // inclusive scan of the log-gate over the chunk rows
+          const bool live = lane < nrows;
+          const float be = live ? pb : 0.f;
+          float g = 0.f, gread = 0.f;
+          if constexpr (GATE == GATE_SCALAR) {
+            g = live ? pls : 0.f;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+              const float y = __shfl_up(g, off);
+              if (lane >= off) g += y;
+            }
+            const float gprev = __shfl_up(g, 1);
+            gread = p.literal ? (lane == 0 ? 0.f : gprev) : g;
+          }
+          const float gC = __shfl(g, 63);
+          sBr[lane] = be;
+          sGr[lane] = g;
+          sGrd[lane] = gread;
+          sEw[lane] = be * __expf(gread);
+          sEo[lane] = __expf(g);
+          sEd[lane] = __expf(gC - g);
+          if (lane == 0) sGamR[0] = __expf(gC);
+        }
+      } else {
+        if (tid < CH) sBc[tid] = tid < nrows ? pb : 0.f;
+      }
     }
     if (n + 1 < nchunks) prefetch(n + 1);
     __syncthreads();
 
-    // ---- (1) log-gate scan and, for raw gates, the transposed operands ------------
-    if constexpr (RAW) {
-      if (wave == 0) {
-        float g = 0.f, gread = 0.f;
-        if constexpr (GATE == GATE_SCALAR) {
-          g = sGr[lane];
-#pragma unroll
-          for (int off = 1; off < 64; off <<= 1) {
-            const float y = __shfl_up(g, off);
-            if (lane >= off) g += y;
-          }
-          const float gprev = __shfl_up(g, 1);
-          gread = p.literal ? (lane == 0 ? 0.f : gprev) : g;
-        }
-        const float gC = __shfl(g, 63);
-        const float be = sBr[lane];
-        sGr[lane] = g;
-        sGrd[lane] = gread;
-        sEw[lane] = be * __expf(gread);
-        sEo[lane] = __expf(g);
-        sEd[lane] = __expf(gC - g);
-        if (lane == 0) sGamR[0] = __expf(gC);
-      }
-      // k transposed: column i, rows 8rg..8rg+7 -> one contiguous run of KT
-      for (int task = tid; task < DK * 8; task += NT) {
-        const int i = task % DK, rg = task / DK;
-        T buf[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) buf[j] = sK[(8 * rg + j) * LDK + i];
-#pragma unroll
-        for (int j = 0; j < 8; j += 4) {
-          frag f;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) f[e] = buf[j + e];
-          *reinterpret_cast<frag*>(sKT + i * LCH + 8 * rg + j) = f;
-        }
-      }
-    } else {
+    if constexpr (!RAW) {
       // per-channel scan over the rows of each channel
       constexpr int NSEG = L::NSEG, SEGL = CH / NSEG;
       if (tid < NSEG * DK) {
@@ -367,22 +438,7 @@ __global__ __launch_bounds__(NW * 64) void chunk_fwd_kernel(ChunkParams p, int n
             for (int r = seg * SEGL; r < (seg + 1) * SEGL; ++r) sG[r * DK + i] += pre;
         }
       }
-    }
-    // beta * v, transposed
-    for (int task = tid; task < DVT * 8; task += NT) {
-      const int c = task % DVT, rg = task / DVT;
-      frag f0, f1;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        f0[e] = O::from(sBeta[8 * rg + e] * O::to(sV[(8 * rg + e) * LVT + c]));
-        f1[e] = O::from(sBeta[8 * rg + 4 + e] * O::to(sV[(8 * rg + 4 + e) * LVT + c]));
-      }
-      *reinterpret_cast<frag*>(sVT + c * LCH + 8 * rg) = f0;
-      *reinterpret_cast<frag*>(sVT + c * LCH + 8 * rg + 4) = f1;
-    }
-    __syncthreads();
-
-    if constexpr (!RAW) {
+      __syncthreads();
       // decayed operands; X_K and X_Q overwrite the raw tiles in place
       for (int i = tid; i < DK; i += NT) {
         sGamC[i] = __expf(sG[(CH - 1) * DK + i]);
@@ -419,9 +475,10 @@ __global__ __launch_bounds__(NW * 64) void chunk_fwd_kernel(ChunkParams p, int n
     }
 
     // ---- (2) 16x16 blocks of A (strictly lower) and P (lower incl. diagonal) ------
-    // Wave 0 computes the four diagonal blocks of A and inverts them while the
-    // other waves compute the off-diagonal blocks of A and all blocks of P.
-    auto block_product = [&](bool isP, int R, int J) -> f32x4 {
+    // Each wave forms the diagonal blocks of A it owns and inverts them in
+    // registers; the 16 off-diagonal A blocks and P blocks are split evenly.
+    auto block_product = [&](auto is_p, int R, int J) -> f32x4 {
+      constexpr bool isP = decltype(is_p)::value;
       const T* rows = isP ? sQ : sK;
       const T* cols = RAW ? sK : sY;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -441,64 +498,40 @@ __global__ __launch_bounds__(NW * 64) void chunk_fwd_kernel(ChunkParams p, int n
         }
         acc = O::mma2(acc, a0, a1, b0, b1);
       }
-      return acc;
-    };
-    auto store_block = [&](bool isP, int R, int J, f32x4 acc) {
+      // decay and beta factors, then the causal mask
       const int j = 16 * J + lr;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int rr = 4 * lg + s, r = 16 * R + rr;
         float val = acc[s];
         if constexpr (GATE == GATE_SCALAR) val *= __expf((isP ? sGr[r] : sGrd[r]) - sGr[j]);
-        if (!isP) {
-          if constexpr (RAW) val *= sBr[r];
-          sA[r * LA + j] = (R == J && rr <= lr) ? 0.f : val;
-        } else {
-          sP[r * LCH + j] = O::from((R == J && rr < lr) ? 0.f : val);
+        if constexpr (RAW) {
+          if (!isP) val *= sBr[r];
         }
+        acc[s] = (R == J && (isP ? rr < lr : rr <= lr)) ? 0.f : val;
       }
+      return acc;
     };
-    constexpr int W0 = NW == 2 ? 4 : 0;             // off-diagonal tasks taken by wave 0
-    constexpr int PER = NW > 1 ? (16 - W0 + NW - 2) / (NW - 1) : 16;
-    if (wave == 0) {
+    for (int R = wave; R < 4; R += NW) {
+      const f32x4 x = unit_lower_inverse(block_product(std::false_type{}, R, R), sScr + wave * 16 * L::LSC, lr, lg);
 #pragma unroll
-      for (int R = 0; R < 4; ++R) store_block(false, R, R, block_product(false, R, R));
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      // unit-lower inverse of each diagonal block, one column per lane
-      const int R = lane >> 4, j = lane & 15;
-      float x[16];
+      for (int s = 0; s < 4; ++s) sXi[(16 * R + 4 * lg + s) * LXI + lr] = O::from(x[s]);
+    }
+    {
+      // tasks [lo, hi) of the list: 6 strictly-lower A blocks, then 10 P blocks
+      const int lo = 16 * wave / NW, hi = 16 * (wave + 1) / NW;
+      for (int t = lo; t < (hi < 6 ? hi : 6); ++t) {
+        const int R = 1 + (t >= 1) + (t >= 3), J = t - R * (R - 1) / 2;
+        const f32x4 acc = block_product(std::false_type{}, R, J);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float* arow = sA + (16 * R + i) * LA + 16 * R;
-        float s0 = (i == j) ? 1.f : 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-#pragma unroll
-        for (int kk = 0; kk + 3 < i; kk += 4) {
-          s0 -= arow[kk] * x[kk];
-          s1 -= arow[kk + 1] * x[kk + 1];
-          s2 -= arow[kk + 2] * x[kk + 2];
-          s3 -= arow[kk + 3] * x[kk + 3];
-        }
-#pragma unroll
-        for (int kk = i & ~3; kk < i; ++kk) s0 -= arow[kk] * x[kk];
-        x[i] = (s0 + s1) + (s2 + s3);
+        for (int s = 0; s < 4; ++s) sA[(16 * R + 4 * lg + s) * LA + 16 * J + lr] = acc[s];
       }
+      for (int t = (lo > 6 ? lo : 6); t < hi; ++t) {
+        const int u = t - 6;
+        const int R = (u >= 1) + (u >= 3) + (u >= 6), J = u - R * (R + 1) / 2;
+        const f32x4 acc = block_product(std::true_type{}, R, J);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sXi[(16 * R + i) * LXI + j] = O::from(x[i]);
-#pragma unroll
-      for (int t = 16 - W0; t < 16; ++t) {
-        bool isP; int R2, J2;
-        other_task(t, isP, R2, J2);
-        store_block(isP, R2, J2, block_product(isP, R2, J2));
-      }
-    } else {
-      const int lo = (wave - 1) * PER;
-      const int hi = lo + PER < 16 - W0 ? lo + PER : 16 - W0;
-      for (int t = lo; t < hi; ++t) {
-        bool isP; int R2, J2;
-        other_task(t, isP, R2, J2);
-        store_block(isP, R2, J2, block_product(isP, R2, J2));
+        for (int s = 0; s < 4; ++s) sP[(16 * R + 4 * lg + s) * LCH + 16 * J + lr] = O::from(acc[s]);
       }
     }
     __syncthreads();
@@ -530,6 +563,8 @@ __global__ __launch_bounds__(NW * 64) void chunk_fwd_kernel(ChunkParams p, int n
           }
         } else {
           acc = O::f32(O::ld(sVT + (16 * wave + lr) * LCH + 16 * R + 4 * lg));
+#pragma unroll
+          for (int s = 0; s < 4; ++s) acc[s] *= sBeta[16 * R + 4 * lg + s];
         }
         int J = 0;
 #pragma unroll
