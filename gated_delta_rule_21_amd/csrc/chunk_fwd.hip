@@ -26,12 +26,18 @@
 // whole sequence.  An accumulator tile (lane l: column l%16, rows 4(l/16)+s) is
 // the operand layout of the next product, so W*S, the output and the state
 // update chain through registers.  The d_v-independent per-chunk work (log-gate
-// scan, the 16x16 blocks of A and of the masked score matrix P, the four
-// diagonal 16x16 inverses) is shared by the waves through LDS.  (I + A)^{-1} is
-// never formed: each wave solves for its own columns of W and U by forward
-// substitution over the four 16-row blocks.  The next chunk's q, k, v, beta and
-// log-gate are loaded into registers (16-byte loads) while the current chunk
-// computes.
+// scan, the 16x16 blocks of A and of the masked score matrix P, the diagonal
+// 16x16 inverses) is shared by the waves through LDS.  (I + A)^{-1} is never
+// formed: each wave solves for its own columns of W and U by forward
+// substitution over the four 16-row blocks.
+//
+// Memory.  q, k, v, beta and the log-gate are read once per chunk with buffer
+// loads into registers one chunk ahead of their use; a buffer's range ends at
+// the last token of the sequence, so the rows of a ragged last chunk read as
+// zero.  Tiles sit row-major in LDS; products that contract over the chunk rows
+// (the state update, the right-hand sides of W and U) read them with the gfx950
+// LDS transpose load, so no transposed copy is made.  The output is computed
+// transposed, so each lane stores four adjacent columns.
 //
 // Gates.  With no gate or a scalar gate the decay factors are per row and per
 // column of the 64x64 intra-chunk matrices, so the products run on the raw
@@ -58,8 +64,17 @@ template <int IO> struct Op;
 template <> struct Op<IO_BF16> {
   typedef __bf16 T;
   typedef bf16x4 frag;
-  static constexpr int PAD = 8;
+  static constexpr int PAD = 16;     // row stride = 8 (mod 64) dwords: conflict-free fragment reads
   static __device__ __forceinline__ frag ld(const T* p) { return *reinterpret_cast<const frag*>(p); }
+  // Fragment holding M[r0 + 4*lg + s][c0 + lr], s = 0..3, of a row-major tile M:
+  // the gfx950 LDS transpose load gathers it from 16 lanes' 8-byte reads.
+  static __device__ __forceinline__ frag ld_tr(const T* m, int ld, int r0, int c0, int lr, int lg) {
+    const T* a = m + (r0 + 4 * lg + (lr >> 2)) * ld + c0 + 4 * (lr & 3);
+    typedef __attribute__((ext_vector_type(4))) short v4s;
+    typedef __attribute__((address_space(3))) v4s lds_v4s;
+    const v4s x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(const_cast<T*>(a)));
+    return __builtin_bit_cast(frag, x);
+  }
   static __device__ __forceinline__ frag cvt(f32x4 x) { return to_bf16x4(x); }
   static __device__ __forceinline__ f32x4 f32(frag x) {
     f32x4 r;
@@ -68,7 +83,6 @@ template <> struct Op<IO_BF16> {
     return r;
   }
   static __device__ __forceinline__ T from(float x) { return static_cast<__bf16>(x); }
-  static __device__ __forceinline__ float to(T x) { return static_cast<float>(x); }
   static __device__ __forceinline__ f32x4 mma2(f32x4 acc, frag a0, frag a1, frag b0, frag b1) {
     return mma_k32_bf16(acc, a0, a1, b0, b1);
   }
@@ -79,10 +93,15 @@ template <> struct Op<IO_F32> {
   typedef f32x4 frag;
   static constexpr int PAD = 4;
   static __device__ __forceinline__ frag ld(const T* p) { return *reinterpret_cast<const frag*>(p); }
+  static __device__ __forceinline__ frag ld_tr(const T* m, int ld, int r0, int c0, int lr, int lg) {
+    frag f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) f[s] = m[(r0 + 4 * lg + s) * ld + c0 + lr];
+    return f;
+  }
   static __device__ __forceinline__ frag cvt(f32x4 x) { return x; }
   static __device__ __forceinline__ f32x4 f32(frag x) { return x; }
   static __device__ __forceinline__ T from(float x) { return x; }
-  static __device__ __forceinline__ float to(T x) { return x; }
   static __device__ __forceinline__ f32x4 mma2(f32x4 acc, frag a0, frag a1, frag b0, frag b1) {
     return mma_k16_f32(mma_k16_f32(acc, a0, b0), a1, b1);
   }
@@ -91,8 +110,8 @@ template <> struct Op<IO_F32> {
 
 constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
 
-// LDS layout (bytes).  Row-major [64][DK] tiles use stride LDK, transposed
-// [*][64] tiles stride LCH; both carry padding against bank conflicts.
+// LDS layout (bytes).  Row-major tiles: [64][DK] with stride LDK, the v tile
+// [64][DVT] with stride LVT, the 64x64 matrices with stride LCH.
 template <int IO, int GATE, int DK, int NW>
 struct Layout {
   typedef typename Op<IO>::T T;
@@ -100,38 +119,36 @@ struct Layout {
   static constexpr int PAD = Op<IO>::PAD;
   static constexpr int LDK = DK + PAD;
   static constexpr int LCH = CH + PAD;
-  static constexpr int LA = CH + 4;
-  static constexpr int LXI = 16 + PAD;
+  static constexpr int LXI = 16 + (sizeof(T) == 2 ? 8 : 4);
   static constexpr int LSC = 20;                       // per-wave 16x16 fp32 scratch stride
   static constexpr int DVT = 16 * NW;
+  static constexpr int LVT = DVT + PAD;
   static constexpr int NSEG = (64 * NW) / DK > 0 ? (64 * NW) / DK : 1;
   static constexpr size_t RM = size_t(CH) * LDK * sizeof(T);      // [64][DK]
-  static constexpr size_t TR = size_t(DK) * LCH * sizeof(T);      // [DK][64]
-  static constexpr size_t A_B = size_t(CH) * LA * 4;
-  static constexpr size_t P_B = size_t(CH) * LCH * sizeof(T);
+  static constexpr size_t MM = size_t(CH) * LCH * sizeof(T);      // [64][64]
   static constexpr size_t XI_B = size_t(CH) * LXI * sizeof(T);
-  static constexpr size_t VT_B = size_t(DVT) * LCH * sizeof(T);
+  static constexpr size_t V_B = size_t(CH) * LVT * sizeof(T);
   static constexpr size_t SC_B = size_t(NW) * 16 * LSC * 4;
   // common regions
-  static constexpr size_t OFF_K = 0;                     // raw k (channel: X_K in place), then W
-  static constexpr size_t OFF_Q = OFF_K + RM;            // raw q (channel: X_Q in place)
-  static constexpr size_t OFF_VT = OFF_Q + RM;           // raw v tile, transposed
-  static constexpr size_t OFF_XI = OFF_VT + VT_B;        // inverses of the diagonal blocks
+  static constexpr size_t OFF_K = 0;                     // raw k (per-channel gate: X_K in place)
+  static constexpr size_t OFF_Q = OFF_K + RM;            // raw q (per-channel gate: X_Q in place)
+  static constexpr size_t OFF_V = OFF_Q + RM;            // raw v tile
+  static constexpr size_t OFF_XI = OFF_V + V_B;          // inverses of the diagonal blocks
   static constexpr size_t OFF_SC = OFF_XI + XI_B;        // per-wave scratch of the inversion
   static constexpr size_t OFF_X = OFF_SC + SC_B;         // gate-dependent regions start here
   // raw gates
-  static constexpr size_t R_KT = OFF_X;                  // k transposed
-  static constexpr size_t R_A = R_KT + TR;
-  static constexpr size_t R_P = R_A + A_B;
-  static constexpr size_t R_SMALL = R_P + P_B;           // beta, g, g_read, e_w, e_o, e_d, gamma
+  static constexpr size_t R_W = OFF_X;
+  static constexpr size_t R_A = R_W + RM;                // -A (off-diagonal blocks)
+  static constexpr size_t R_P = R_A + MM;
+  static constexpr size_t R_SMALL = R_P + MM;            // beta, g, g_read, e_w, e_o, e_d, gamma
   static constexpr size_t R_TOTAL = R_SMALL + 7 * CH * 4;
-  // per-channel gate
+  // per-channel gate (W reuses X_K)
   static constexpr size_t C_Y = OFF_X;                   // column operand of the score blocks
-  static constexpr size_t C_QH = C_Y + RM;
-  static constexpr size_t C_KRT = C_QH + RM;
-  static constexpr size_t C_KDT = C_KRT + TR;
-  static constexpr size_t C_G = C_KDT + TR;              // g [64][DK] fp32, then A and P
-  static constexpr size_t C_G_B = cmax(size_t(CH) * DK * 4, A_B + P_B);
+  static constexpr size_t C_QH = C_Y + RM;               // q e^{g}
+  static constexpr size_t C_KR = C_QH + RM;              // beta k e^{g_read}
+  static constexpr size_t C_KD = C_KR + RM;              // k e^{g_63 - g}
+  static constexpr size_t C_G = C_KD + RM;               // g [64][DK] fp32, then -A and P
+  static constexpr size_t C_G_B = cmax(size_t(CH) * DK * 4, 2 * MM);
   static constexpr size_t C_BETA = C_G + C_G_B;
   static constexpr size_t C_GAM = C_BETA + CH * 4;
   static constexpr size_t C_M = C_GAM + DK * 4;
@@ -141,14 +158,6 @@ struct Layout {
 };
 
 __device__ __forceinline__ int strict_pair(int R, int J) { return R * (R - 1) / 2 + J; }
-
-__device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
-// x if keep else 0, component by component (a whole-vector select can be lowered
-// through private memory)
-__device__ __forceinline__ uint4 keep_or_zero(bool keep, uint4 x) {
-  const uint32_t m = keep ? 0xffffffffu : 0u;
-  return make_uint4(x.x & m, x.y & m, x.z & m, x.w & m);
-}
 
 // Ordering point for LDS traffic between the lanes of one wave.
 __device__ __forceinline__ void wave_sync() {
@@ -208,25 +217,23 @@ __global__ __launch_bounds__(NW * 64) void chunk_fwd_kernel(ChunkParams p, int n
   constexpr int DVT = 16 * NW;
   constexpr int DKT = DK / 16;
   constexpr int CBW = DKT / NW;          // 16-channel blocks of W solved per wave
-  constexpr int LDK = L::LDK, LCH = L::LCH, LA = L::LA, LXI = L::LXI;
-  constexpr int EPV = 16 / int(sizeof(elem));   // elements per 16-byte load
-  constexpr int KROW = DK / EPV;
-  constexpr int KV = CH * KROW / NT;            // row-major 16-byte pieces of a k (q) tile per thread
-  constexpr int KTT = RAW ? DK * 8 / NT : 1;    // 8-row column runs of k^T per thread
-  constexpr int VTT = DVT * 8 / NT;             // 8-row column runs of v^T per thread
+  constexpr int LDK = L::LDK, LCH = L::LCH, LXI = L::LXI, LVT = L::LVT;
+  constexpr int ESZ = int(sizeof(elem));
+  constexpr int EPV = 16 / ESZ;          // elements per 16-byte load
+  constexpr int KROW = DK / EPV, VROW = DVT / EPV;
+  constexpr int KV = CH * KROW / NT;     // 16-byte pieces of a k (q) tile per thread
+  constexpr int VV = CH * VROW / NT;     // 16-byte pieces of the v tile per thread
   static_assert(CBW >= 1 && CBW * NW == DKT, "channel blocks must split over waves");
-  static_assert(KV * NT == CH * KROW && VTT * NT == DVT * 8 && (!RAW || KTT * NT == DK * 8), "even split");
+  static_assert(KV * NT == CH * KROW && VV * NT == CH * VROW && VV >= 1, "tile loads must split evenly");
   static_assert(L::TOTAL <= 163840, "LDS budget");
 
   __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
   T* sK = reinterpret_cast<T*>(smem + L::OFF_K);
   T* sQ = reinterpret_cast<T*>(smem + L::OFF_Q);
-  T* sVT = reinterpret_cast<T*>(smem + L::OFF_VT);
+  T* sV = reinterpret_cast<T*>(smem + L::OFF_V);
   T* sXi = reinterpret_cast<T*>(smem + L::OFF_XI);
   float* sScr = reinterpret_cast<float*>(smem + L::OFF_SC);
-  T* sW = sK;                       // k is dead once A and P are formed
   // raw-gate regions
-  T* sKT = reinterpret_cast<T*>(smem + L::R_KT);
   float* sSmall = reinterpret_cast<float*>(smem + L::R_SMALL);
   float* sBr = sSmall;              // beta
   float* sGr = sSmall + CH;         // g
@@ -238,23 +245,18 @@ __global__ __launch_bounds__(NW * 64) void chunk_fwd_kernel(ChunkParams p, int n
   // per-channel regions
   T* sY = reinterpret_cast<T*>(smem + L::C_Y);
   T* sQh = reinterpret_cast<T*>(smem + L::C_QH);
-  T* sKrT = reinterpret_cast<T*>(smem + L::C_KRT);
-  T* sKdT = reinterpret_cast<T*>(smem + L::C_KDT);
+  T* sKr = reinterpret_cast<T*>(smem + L::C_KR);
+  T* sKd = reinterpret_cast<T*>(smem + L::C_KD);
   float* sG = reinterpret_cast<float*>(smem + L::C_G);
   float* sBc = reinterpret_cast<float*>(smem + L::C_BETA);
   float* sGamC = reinterpret_cast<float*>(smem + L::C_GAM);
   float* sM = reinterpret_cast<float*>(smem + L::C_M);
   float* sTot = reinterpret_cast<float*>(smem + L::C_TOT);
-  float* sA = RAW ? reinterpret_cast<float*>(smem + L::R_A) : sG;
-  T* sP = RAW ? reinterpret_cast<T*>(smem + L::R_P) : reinterpret_cast<T*>(smem + L::C_G + L::A_B);
+  // shared names
+  T* sW = RAW ? reinterpret_cast<T*>(smem + L::R_W) : sK;   // X_K is dead once A and P exist
+  T* sA = RAW ? reinterpret_cast<T*>(smem + L::R_A) : reinterpret_cast<T*>(smem + L::C_G);
+  T* sP = RAW ? reinterpret_cast<T*>(smem + L::R_P) : reinterpret_cast<T*>(smem + L::C_G + L::MM);
   float* sBeta = RAW ? sBr : sBc;
-
-  const elem* gq = static_cast<const elem*>(p.q);
-  const elem* gk = static_cast<const elem*>(p.k);
-  const elem* gv = static_cast<const elem*>(p.v);
-  const elem* gbeta = static_cast<const elem*>(p.beta);
-  const elem* gla = static_cast<const elem*>(p.log_a);
-  elem* go = static_cast<elem*>(p.o);
 
   // Block -> (head, d_v tile).  Consecutive logical blocks land on one XCD (the
   // hardware deals block ids round-robin over 8 XCDs), so the tiles of one head
@@ -267,6 +269,7 @@ __global__ __launch_bounds__(NW * 64) void chunk_fwd_kernel(ChunkParams p, int n
   const int64_t bb = bh / p.H, hh = bh % p.H;
   const int dv = p.d_v;
   const int col0 = tile * DVT;
+  const int H = static_cast<int>(p.H);
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -275,7 +278,29 @@ __global__ __launch_bounds__(NW * 64) void chunk_fwd_kernel(ChunkParams p, int n
   const int lg = lane >> 4;
   const int scol = col0 + 16 * wave + lr;   // this lane's state column
 
-  auto tok = [&](int64_t t) -> int64_t { return (bb * p.T + t) * p.H + hh; };
+  // Buffers over this sequence's (b, h) slice; each range ends after the last token.
+  const int64_t row0 = bb * p.T * p.H + hh;            // token-row index of (b, t = 0, h)
+  const uint32_t span = static_cast<uint32_t>(p.T > 0 ? (p.T - 1) * p.H + 1 : 0);   // rows in range
+  const rsrc_t rk = make_rsrc(static_cast<const elem*>(p.k) + row0 * DK, span * DK * ESZ);
+  const rsrc_t rq = make_rsrc(static_cast<const elem*>(p.q) + row0 * DK, span * DK * ESZ);
+  const rsrc_t rv = make_rsrc(static_cast<const elem*>(p.v) + row0 * dv, span * dv * ESZ);
+  const rsrc_t ro = make_rsrc(static_cast<const elem*>(p.o) + row0 * dv, span * dv * ESZ);
+  const rsrc_t rb = make_rsrc(static_cast<const elem*>(p.beta) + row0, span * ESZ);
+  const rsrc_t rl = make_rsrc(static_cast<const elem*>(p.log_a) + row0 * (GATE == GATE_CHANNEL ? DK : 1),
+                              GATE == GATE_NONE ? 0u : span * (GATE == GATE_CHANNEL ? DK : 1) * ESZ);
+  // per-thread byte offsets within a chunk (the chunk start goes in the scalar offset)
+  uint32_t offk[KV], offv[VV];
+#pragma unroll
+  for (int v = 0; v < KV; ++v) {
+    const int seg = tid + v * NT;
+    offk[v] = static_cast<uint32_t>(((seg / KROW) * H * DK + (seg % KROW) * EPV) * ESZ);
+  }
+#pragma unroll
+  for (int v = 0; v < VV; ++v) {
+    const int seg = tid + v * NT;
+    offv[v] = static_cast<uint32_t>(((seg / VROW) * H * dv + col0 + (seg % VROW) * EPV) * ESZ);
+  }
+  const uint32_t offb = static_cast<uint32_t>((tid % CH) * H * ESZ);
 
   // State slice: S[t][s] = S[16t + 4lg + s][scol].
   f32x4 S[DKT];
@@ -286,69 +311,33 @@ __global__ __launch_bounds__(NW * 64) void chunk_fwd_kernel(ChunkParams p, int n
       S[t][s] = p.S0 ? p.S0[(bh * DK + 16 * t + 4 * lg + s) * dv + scol] : 0.f;
 
   // ---- register prefetch of one chunk's inputs ----------------------------------
-  // Rows past the end of the sequence are read from the last valid row (so no
-  // load needs a guard and none stalls the issuing wave) and zeroed when the
-  // registers are written to LDS.
-  constexpr int RW = 8 * int(sizeof(elem)) / 4;         // 32-bit words in an 8-element run
-  uint4 pk[KV], pq[KV], pl[GATE == GATE_CHANNEL ? KV : 1];
-  uint32_t pkt[KTT][RW], pvt[VTT][RW];
-  // element e of a 16-byte piece / of an 8-element run, as float
-  auto elem_of = [&](const uint32_t* w, int e) -> float {
-    if constexpr (IO == IO_BF16) return bf16_bits_to_f32(static_cast<uint16_t>(w[e >> 1] >> (16 * (e & 1))));
-    else return __uint_as_float(w[e]);
-  };
-  auto load_run = [&](uint32_t* w, const elem* base, int64_t t0m, int row0, int last, int64_t stride)
-      __attribute__((always_inline)) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int row = row0 + e;
-      const elem x = base[tok(t0m + (row < last ? row : last)) * stride];
-      if constexpr (IO == IO_BF16) {
-        if (e & 1) w[e >> 1] |= uint32_t(x) << 16; else w[e >> 1] = uint32_t(x);
-      } else {
-        w[e] = __float_as_uint(x);
-      }
-    }
-  };
+  u32x4 pk[KV], pq[KV], pl[GATE == GATE_CHANNEL ? KV : 1], pv[VV];
   float pb = 0.f, pls = 0.f;
+  auto to_f32 = [&](uint32_t bits) -> float {
+    if constexpr (IO == IO_BF16) return bf16_bits_to_f32(static_cast<uint16_t>(bits));
+    else return __uint_as_float(bits);
+  };
   auto prefetch = [&](int64_t m) __attribute__((always_inline)) {
-    const int64_t t0m = m * CH;
-    const int last = static_cast<int>(p.T - t0m < CH ? p.T - t0m : CH) - 1;
+    const uint32_t sk = static_cast<uint32_t>(m * CH * H * DK * ESZ);
+    const uint32_t sv = static_cast<uint32_t>(m * CH * H * dv * ESZ);
+    const uint32_t sb = static_cast<uint32_t>(m * CH * H * ESZ);
 #pragma unroll
     for (int v = 0; v < KV; ++v) {
-      const int seg = tid + v * NT, row = seg / KROW, c = (seg % KROW) * EPV;
-      const int64_t off = tok(t0m + (row < last ? row : last)) * DK + c;
-      pk[v] = ldg16(gk + off);
-      pq[v] = ldg16(gq + off);
-      if constexpr (GATE == GATE_CHANNEL) pl[v] = ldg16(gla + off);
+      pk[v] = buf_load16(rk, offk[v], sk);
+      pq[v] = buf_load16(rq, offk[v], sk);
+      if constexpr (GATE == GATE_CHANNEL) pl[v] = buf_load16(rl, offk[v], sk);
     }
-    if constexpr (RAW) {
 #pragma unroll
-      for (int j = 0; j < KTT; ++j) {
-        const int task = tid + j * NT, i = task % DK, rg = task / DK;
-        load_run(pkt[j], gk + i, t0m, 8 * rg, last, DK);
+    for (int v = 0; v < VV; ++v) pv[v] = buf_load16(rv, offv[v], sv);
+    if (tid < CH) {
+      if constexpr (IO == IO_BF16) {
+        pb = to_f32(buf_load2(rb, offb, sb));
+        if constexpr (GATE == GATE_SCALAR) pls = to_f32(buf_load2(rl, offb, sb));
+      } else {
+        pb = to_f32(buf_load4(rb, offb, sb));
+        if constexpr (GATE == GATE_SCALAR) pls = to_f32(buf_load4(rl, offb, sb));
       }
     }
-#pragma unroll
-    for (int j = 0; j < VTT; ++j) {
-      const int task = tid + j * NT, c = task % DVT, rg = task / DVT;
-      load_run(pvt[j], gv + col0 + c, t0m, 8 * rg, last, dv);
-    }
-    if (tid < CH) {
-      const int row = tid < last ? tid : last;
-      pb = Io<IO>::load(gbeta, tok(t0m + row));
-      if constexpr (GATE == GATE_SCALAR) pls = Io<IO>::load(gla, tok(t0m + row));
-    }
-  };
-  auto put_run = [&](T* dst, const uint32_t* w, int row0, int nrows) __attribute__((always_inline)) {   // 8 rows of one column
-    frag f0, f1;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      f0[e] = O::from(row0 + e < nrows ? elem_of(w, e) : 0.f);
-      f1[e] = O::from(row0 + 4 + e < nrows ? elem_of(w, e + 4) : 0.f);
-    }
-    *reinterpret_cast<frag*>(dst) = f0;
-    *reinterpret_cast<frag*>(dst + 4) = f1;
   };
 
   const int64_t nchunks = (p.T + CH - 1) / CH;
@@ -356,61 +345,50 @@ __global__ __launch_bounds__(NW * 64) void chunk_fwd_kernel(ChunkParams p, int n
 
   for (int64_t n = 0; n < nchunks; ++n) {
     const int64_t t0 = n * CH;
-    const int nrows = static_cast<int>(p.T - t0 < CH ? p.T - t0 : CH);
 
     // ---- (0) chunk from registers into LDS, per-chunk log-gate; next chunk's loads
-    {
 #pragma unroll
-      for (int v = 0; v < KV; ++v) {
-        const int seg = tid + v * NT, row = seg / KROW, c = (seg % KROW) * EPV;
-        const bool live = row < nrows;
-        *reinterpret_cast<uint4*>(sK + row * LDK + c) = keep_or_zero(live, pk[v]);
-        *reinterpret_cast<uint4*>(sQ + row * LDK + c) = keep_or_zero(live, pq[v]);
-        if constexpr (GATE == GATE_CHANNEL) {
-          const uint32_t w[4] = {pl[v].x, pl[v].y, pl[v].z, pl[v].w};
+    for (int v = 0; v < KV; ++v) {
+      const int seg = tid + v * NT, row = seg / KROW, c = (seg % KROW) * EPV;
+      *reinterpret_cast<u32x4*>(sK + row * LDK + c) = pk[v];
+      *reinterpret_cast<u32x4*>(sQ + row * LDK + c) = pq[v];
+      if constexpr (GATE == GATE_CHANNEL) {
 #pragma unroll
-          for (int j = 0; j < EPV; ++j) sG[row * DK + c + j] = live ? elem_of(w, j) : 0.f;
+        for (int j = 0; j < EPV; ++j) {
+          const uint32_t w = pl[v][j * ESZ / 4];
+          sG[row * DK + c + j] = to_f32(ESZ == 2 ? (w >> (16 * (j & 1))) & 0xffffu : w);
         }
       }
-      if constexpr (RAW) {
+    }
 #pragma unroll
-        for (int j = 0; j < KTT; ++j) {
-          const int task = tid + j * NT, i = task % DK, rg = task / DK;
-          put_run(sKT + i * LCH + 8 * rg, pkt[j], 8 * rg, nrows);
-        }
-      }
+    for (int v = 0; v < VV; ++v) {
+      const int seg = tid + v * NT, row = seg / VROW, c = (seg % VROW) * EPV;
+      *reinterpret_cast<u32x4*>(sV + row * LVT + c) = pv[v];
+    }
+    if constexpr (RAW) {
+      if (wave == 0) {              // inclusive scan of the log-gate over the chunk rows
+        float g = 0.f, gread = 0.f;
+        if constexpr (GATE == GATE_SCALAR) {
+          g = pls;
 #pragma unroll
-      for (int j = 0; j < VTT; ++j) {
-        const int task = tid + j * NT, c = task % DVT, rg = task / DVT;
-        put_run(sVT + c * LCH + 8 * rg, pvt[j], 8 * rg, nrows);
-      }
-      if constexpr (RAW) {
-        if (wave == 0) {            // inclusive scan of the log-gate over the chunk rows
-          const bool live = lane < nrows;
-          const float be = live ? pb : 0.f;
-          float g = 0.f, gread = 0.f;
-          if constexpr (GATE == GATE_SCALAR) {
-            g = live ? pls : 0.f;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-              const float y = __shfl_up(g, off);
-              if (lane >= off) g += y;
-            }
-            const float gprev = __shfl_up(g, 1);
-            gread = p.literal ? (lane == 0 ? 0.f : gprev) : g;
+          for (int off = 1; off < 64; off <<= 1) {
+            const float y = __shfl_up(g, off);
+            if (lane >= off) g += y;
           }
-          const float gC = __shfl(g, 63);
-          sBr[lane] = be;
-          sGr[lane] = g;
-          sGrd[lane] = gread;
-          sEw[lane] = be * __expf(gread);
-          sEo[lane] = __expf(g);
-          sEd[lane] = __expf(gC - g);
-          if (lane == 0) sGamR[0] = __expf(gC);
+          const float gprev = __shfl_up(g, 1);
+          gread = p.literal ? (lane == 0 ? 0.f : gprev) : g;
         }
-      } else {
-        if (tid < CH) sBc[tid] = tid < nrows ? pb : 0.f;
+        const float gC = __shfl(g, 63);
+        sBr[lane] = pb;
+        sGr[lane] = g;
+        sGrd[lane] = gread;
+        sEw[lane] = pb * __expf(gread);
+        sEo[lane] = __expf(g);
+        sEd[lane] = __expf(gC - g);
+        if (lane == 0) sGamR[0] = __expf(gC);
       }
+    } else {
+      if (tid < CH) sBc[tid] = pb;
     }
     if (n + 1 < nchunks) prefetch(n + 1);
     __syncthreads();
@@ -453,7 +431,7 @@ __global__ __launch_bounds__(NW * 64) void chunk_fwd_kernel(ChunkParams p, int n
         const f32x4 kk = O::f32(O::ld(sK + r * LDK + i0));
         const f32x4 qq = O::f32(O::ld(sQ + r * LDK + i0));
         const float be = sBeta[r];
-        f32x4 xk, y, xq, qh;
+        f32x4 xk, y, xq, qh, kr, kd;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int i = i0 + j;
@@ -463,13 +441,15 @@ __global__ __launch_bounds__(NW * 64) void chunk_fwd_kernel(ChunkParams p, int n
           y[j] = kk[j] * __expf(gR - g);
           xq[j] = qq[j] * __expf(g - gR);
           qh[j] = qq[j] * __expf(g);
-          sKrT[i * LCH + r] = O::from(be * kk[j] * __expf(gread));
-          sKdT[i * LCH + r] = O::from(kk[j] * __expf(gC - g));
+          kr[j] = be * kk[j] * __expf(gread);
+          kd[j] = kk[j] * __expf(gC - g);
         }
         *reinterpret_cast<frag*>(sK + r * LDK + i0) = O::cvt(xk);
         *reinterpret_cast<frag*>(sY + r * LDK + i0) = O::cvt(y);
         *reinterpret_cast<frag*>(sQ + r * LDK + i0) = O::cvt(xq);
         *reinterpret_cast<frag*>(sQh + r * LDK + i0) = O::cvt(qh);
+        *reinterpret_cast<frag*>(sKr + r * LDK + i0) = O::cvt(kr);
+        *reinterpret_cast<frag*>(sKd + r * LDK + i0) = O::cvt(kd);
       }
       __syncthreads();
     }
@@ -524,7 +504,7 @@ __global__ __launch_bounds__(NW * 64) void chunk_fwd_kernel(ChunkParams p, int n
         const int R = 1 + (t >= 1) + (t >= 3), J = t - R * (R - 1) / 2;
         const f32x4 acc = block_product(std::false_type{}, R, J);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) sA[(16 * R + 4 * lg + s) * LA + 16 * J + lr] = acc[s];
+        for (int s = 0; s < 4; ++s) sA[(16 * R + 4 * lg + s) * LCH + 16 * J + lr] = O::from(-acc[s]);
       }
       for (int t = (lo > 6 ? lo : 6); t < hi; ++t) {
         const int u = t - 6;
@@ -542,27 +522,24 @@ __global__ __launch_bounds__(NW * 64) void chunk_fwd_kernel(ChunkParams p, int n
     constexpr int NB = CBW + 1;
     f32x4 outf[NB][4];
     frag outb[NB][4];
+    const T* wsrc = RAW ? sK : sKr;
 #pragma unroll
     for (int R = 0; R < 4; ++R) {
       frag aR[3];
 #pragma unroll
-      for (int J = 0; J < R; ++J)
-        aR[J] = O::cvt(-*reinterpret_cast<const f32x4*>(sA + (16 * R + lr) * LA + 16 * J + 4 * lg));
+      for (int J = 0; J < R; ++J) aR[J] = O::ld(sA + (16 * R + lr) * LCH + 16 * J + 4 * lg);
       const frag xi = O::ld(sXi + (16 * R + lr) * LXI + 4 * lg);
 #pragma unroll
       for (int c = 0; c < NB; ++c) {
         f32x4 acc;
         if (c < CBW) {
-          const int ch = (wave * CBW + c) * 16 + lr;
+          acc = O::f32(O::ld_tr(wsrc, LDK, 16 * R, (wave * CBW + c) * 16, lr, lg));
           if constexpr (RAW) {
-            acc = O::f32(O::ld(sKT + ch * LCH + 16 * R + 4 * lg));
 #pragma unroll
             for (int s = 0; s < 4; ++s) acc[s] *= sEw[16 * R + 4 * lg + s];
-          } else {
-            acc = O::f32(O::ld(sKrT + ch * LCH + 16 * R + 4 * lg));
           }
         } else {
-          acc = O::f32(O::ld(sVT + (16 * wave + lr) * LCH + 16 * R + 4 * lg));
+          acc = O::f32(O::ld_tr(sV, LVT, 16 * R, 16 * wave, lr, lg));
 #pragma unroll
           for (int s = 0; s < 4; ++s) acc[s] *= sBeta[16 * R + 4 * lg + s];
         }
@@ -613,6 +590,7 @@ __global__ __launch_bounds__(NW * 64) void chunk_fwd_kernel(ChunkParams p, int n
     // O^T tile (rows = this wave's 16 columns, columns = 16 tokens):
     //   S^T (Q e^g)^T + Delta^T P^T; a lane ends up with 4 adjacent output columns.
     const T* qsrc = RAW ? sQ : sQh;
+    const uint32_t so = static_cast<uint32_t>(t0 * H * dv * ESZ);
 #pragma unroll
     for (int R = 0; R < 4; ++R) {
       f32x4 oq = {0.f, 0.f, 0.f, 0.f}, op = {0.f, 0.f, 0.f, 0.f};
@@ -629,19 +607,22 @@ __global__ __launch_bounds__(NW * 64) void chunk_fwd_kernel(ChunkParams p, int n
       const int r = 16 * R + lr;
       f32x4 ov;
       if constexpr (GATE == GATE_SCALAR) ov = oq * sEo[r] + op; else ov = oq + op;
-      if (r < nrows) {
-        elem* dst = go + tok(t0 + r) * dv + col0 + 16 * wave + 4 * lg;
-        if constexpr (IO == IO_BF16) {
-          const uint32_t lo = uint32_t(f32_to_bf16_bits(ov[0])) | (uint32_t(f32_to_bf16_bits(ov[1])) << 16);
-          const uint32_t hi = uint32_t(f32_to_bf16_bits(ov[2])) | (uint32_t(f32_to_bf16_bits(ov[3])) << 16);
-          *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
-        } else {
-          *reinterpret_cast<float4*>(dst) = make_float4(ov[0], ov[1], ov[2], ov[3]);
-        }
+      // rows past the end of the sequence fall outside the buffer and are dropped
+      const uint32_t voff = static_cast<uint32_t>((r * H * dv + col0 + 16 * wave + 4 * lg) * ESZ);
+      if constexpr (IO == IO_BF16) {
+        u32x2 w;
+        w[0] = uint32_t(f32_to_bf16_bits(ov[0])) | (uint32_t(f32_to_bf16_bits(ov[1])) << 16);
+        w[1] = uint32_t(f32_to_bf16_bits(ov[2])) | (uint32_t(f32_to_bf16_bits(ov[3])) << 16);
+        buf_store8(w, ro, voff, so);
+      } else {
+        u32x4 w;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) w[s] = __float_as_uint(ov[s]);
+        buf_store16(w, ro, voff, so);
       }
     }
     // S' = diag(e^{g_63}) S + (K e^{g_63 - g})^T Delta
-    const T* kdt = RAW ? sKT : sKdT;
+    const T* kdsrc = RAW ? sK : sKd;
 #pragma unroll
     for (int t = 0; t < DKT; ++t) {
       f32x4 acc = S[t];
@@ -651,9 +632,10 @@ __global__ __launch_bounds__(NW * 64) void chunk_fwd_kernel(ChunkParams p, int n
       } else if constexpr (GATE == GATE_SCALAR) {
         acc = acc * sGamR[0];
       }
-      const T* kr = kdt + (16 * t + lr) * LCH + 4 * lg;
-      acc = O::mma2(acc, O::ld(kr), O::ld(kr + 16), Ds[0], Ds[1]);
-      acc = O::mma2(acc, O::ld(kr + 32), O::ld(kr + 48), Ds[2], Ds[3]);
+      acc = O::mma2(acc, O::ld_tr(kdsrc, LDK, 0, 16 * t, lr, lg), O::ld_tr(kdsrc, LDK, 16, 16 * t, lr, lg),
+                    Ds[0], Ds[1]);
+      acc = O::mma2(acc, O::ld_tr(kdsrc, LDK, 32, 16 * t, lr, lg), O::ld_tr(kdsrc, LDK, 48, 16 * t, lr, lg),
+                    Ds[2], Ds[3]);
       S[t] = acc;
     }
     __syncthreads();                          // LDS is rewritten by the next chunk

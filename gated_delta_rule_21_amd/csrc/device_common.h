@@ -84,4 +84,33 @@ __device__ __forceinline__ f32x4 mma_k16_f32(f32x4 acc, f32x4 a, f32x4 b) {
   return acc;
 }
 
+// ---------------------------------------------------------------------------
+// Buffer resources: a base address plus a byte range.  Loads past the range
+// return zero and stores past it are dropped, which is how the kernels handle
+// the ragged end of a sequence without per-lane guards.
+// ---------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // third descriptor word: 32-bit data format, as for untyped gfx9 buffer access
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+__device__ __forceinline__ uint32_t buf_load4(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+__device__ __forceinline__ uint16_t buf_load2(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
+__device__ __forceinline__ void buf_store8(u32x2 x, rsrc_t r, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b64(x, r, voff, soff, 0);
+}
+__device__ __forceinline__ void buf_store16(u32x4 x, rsrc_t r, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b128(x, r, voff, soff, 0);
+}
+
 }  // namespace gdr

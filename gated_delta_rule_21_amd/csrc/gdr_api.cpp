@@ -68,6 +68,13 @@ gdr_status check_desc(const gdr_desc* d, bool decode) {
   if (!mul_ok(d->B, d->H, &bh) || !mul_ok(bh, d->T, &bth) || !mul_ok(bth, 128, &x) || !mul_ok(bh, 128 * 128 * 4, &x))
     return fail(GDR_ERR_INVALID_ARG, "sizes overflow");
   if (bh * 8 > INT32_MAX) return fail(GDR_ERR_UNSUPPORTED, "B*H = %lld exceeds the grid limit", (long long)bh);
+  // The kernels address one sequence's (b, h) slice with 32-bit byte offsets.
+  const int64_t esz = d->io == GDR_BF16 ? 2 : 4;
+  const int64_t dmax = d->d_k > d->d_v ? d->d_k : d->d_v;
+  int64_t seq_bytes;
+  if (!mul_ok(d->T, d->H, &seq_bytes) || !mul_ok(seq_bytes, dmax * esz, &seq_bytes) || seq_bytes > INT32_MAX)
+    return fail(GDR_ERR_UNSUPPORTED, "T*H*max(d_k,d_v)*elem_size = %lld bytes exceeds 2^31 - 1 per sequence",
+                (long long)seq_bytes);
   return GDR_OK;
 }
 
