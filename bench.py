@@ -33,8 +33,10 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PROFILE_DIR = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = [os.path.join(ROOT, "gated_delta_rule_21_amd", "csrc", n)
-                  for n in ("chunk_fwd.hip", "device_common.h")]
+CHUNK_SOURCES = [os.path.join(ROOT, "gated_delta_rule_21_amd", "csrc", n)
+                 for n in ("chunk_fwd.hip", "device_common.h")]
+DECODE_SOURCES = [os.path.join(ROOT, "gated_delta_rule_21_amd", "csrc", n)
+                  for n in ("decode_step.hip", "device_common.h")]
 
 
 def chunk_algorithmic(wl, with_S0: bool):
@@ -66,15 +68,15 @@ def decode_bytes(wl):
     return wl.N * wl.H * per
 
 
-def kernel_source_digest() -> str:
+def source_digest(paths) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in paths:
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def profiled_traffic(name: str):
+def profiled_traffic(name: str, sources):
     """HBM bytes per launch from a committed rocprofv3 counter summary, if it was
     taken on the current kernel source (None otherwise)."""
     path = os.path.join(PROFILE_DIR, name)
@@ -83,38 +85,55 @@ def profiled_traffic(name: str):
     text = open(path).read()
     m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
     m_s = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
-    if not m_b or not m_s or m_s.group(1) != kernel_source_digest():
+    if not m_b or not m_s or m_s.group(1) != source_digest(sources):
         return None
     return float(m_b.group(1))
 
 
 # ------------------------------------------------------------------ CPU baseline
-def cpu_baseline_child(T: int, heads: int) -> None:
-    """Run the oracle on batch 0, `heads` heads, T tokens of the gated workload."""
+def cpu_baseline_child(T: int, heads: int, batches: int) -> None:
+    """Run the oracle on `batches` sequences x `heads` heads x T tokens of the gated workload."""
     import numpy as np
     from oracle import forward
     from workloads import CONFIGS, slice_inputs
     wl = CONFIGS[3]
-    sl = [slice_inputs(wl, 0, h, T) for h in range(heads)]
-    st = lambda n: np.stack([s[n] for s in sl], axis=1)[None]
+    sl = [[slice_inputs(wl, b, h, T) for h in range(heads)] for b in range(batches)]
+    st = lambda n: np.stack([np.stack([s[n] for s in row], axis=1) for row in sl], axis=0)
     args = [st(n) for n in ("q", "k", "v", "beta", "log_a")]
+    del sl
     t0 = time.perf_counter()
     forward(*args, None)
     dt = time.perf_counter() - t0
-    print(json.dumps({"seconds": dt, "T": T, "heads": heads}))
+    print(json.dumps({"seconds": dt, "T": T, "heads": heads, "batches": batches}))
 
 
-def cpu_baseline(T: int, heads: int, H_total: int):
+def cpu_baseline(T: int, heads: int, batches: int, H_total: int):
     env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1")
     out = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-baseline-child",
-                          "--cpu-T", str(T), "--cpu-heads", str(heads)],
+                          "--cpu-T", str(T), "--cpu-heads", str(heads), "--cpu-batches", str(batches)],
                          capture_output=True, text=True, env=env, check=True)
     r = json.loads(out.stdout.strip().splitlines()[-1])
-    head_tok_s = r["heads"] * r["T"] / r["seconds"]
+    head_tok_s = r["batches"] * r["heads"] * r["T"] / r["seconds"]
     return {"value": head_tok_s / H_total, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": (f"fp64 token-by-token oracle (NumPy, one thread) on batch 0, {heads} of {H_total} heads, "
-                       f"{T} tokens of the gated workload; {r['seconds']:.1f} s; tokens/s = head-tokens/s / H"),
+            "sample": (f"fp64 token-by-token oracle (NumPy, one thread) on {batches} sequences x {heads} of "
+                       f"{H_total} heads x {T} tokens of the gated workload, S0 = 0; {r['seconds']:.1f} s; "
+                       "tokens/s = head-tokens/s / H"),
             "seconds": round(r["seconds"], 2)}
+
+
+def copy_calibration(log, nbytes: int = 1 << 30, reps: int = 3):
+    """Streaming elementwise kernel over fp32 that reads `nbytes` and writes `nbytes`
+    (torch.neg, out of place).  Profiled beside the hot path, it gives the scale
+    between the HBM byte counters and bytes actually moved."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    log(f"copy calibration: {reps} x torch.neg over {nbytes} bytes read + {nbytes} written")
+    del src, dst
 
 
 # ------------------------------------------------------------------ GPU legs
@@ -188,7 +207,7 @@ def bench_decode(args, log):
             "workload": wl.name, "bytes_per_step": nbytes,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4),
-                         "traffic": profiled_traffic("decode_step_n256h32d128_counters.md")}}
+                         "traffic": profiled_traffic("decode_step_n256h32d128_counters.md", DECODE_SOURCES)}}
 
 
 def main():
@@ -201,12 +220,15 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-T", type=int, default=8192)
     ap.add_argument("--cpu-heads", type=int, default=16)
+    ap.add_argument("--cpu-batches", type=int, default=4)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 1 GiB streaming copy first (for scaling HBM byte counters)")
     ap.add_argument("--cpu-baseline-child", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--quiet", action="store_true")
     args = ap.parse_args()
 
     if args.cpu_baseline_child:
-        cpu_baseline_child(args.cpu_T, args.cpu_heads)
+        cpu_baseline_child(args.cpu_T, args.cpu_heads, args.cpu_batches)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -221,6 +243,8 @@ def main():
         sys.exit(1)
     import gated_delta_rule_21_amd as gdr
     gdr.load()
+    if args.copy_calibration:
+        copy_calibration(log)
 
     wl, ms, nbytes, flops = bench_chunk(args, log)
     tok_s = wl.B * wl.T / (ms * 1e-3)
@@ -230,7 +254,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle sample")
-        cpu = cpu_baseline(args.cpu_T, args.cpu_heads, wl.H)
+        cpu = cpu_baseline(args.cpu_T, args.cpu_heads, args.cpu_batches, wl.H)
 
     line = {
         "metric": "tokens/s + % MFMA peak, gated delta-rule chunk fwd T=8192 d=128; decode GB/s",
@@ -252,7 +276,7 @@ def main():
         "mfma_frac_useful": round(tflops / BF16_PEAK_TFLOPS, 4),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "traffic": profiled_traffic("chunk_fwd_gated_b8h16t8192d128_counters.md")},
+                     "traffic": profiled_traffic("chunk_fwd_gated_b8h16t8192d128_counters.md", CHUNK_SOURCES)},
         "algorithmic_bytes_per_launch": nbytes,
         "useful_flops_per_launch": flops,
         "decode": decode,

@@ -1,0 +1,131 @@
+"""Turn rocprofv3 CSV output into the short text summaries kept beside the library.
+
+    python -m gated_delta_rule_21_amd.profile_summary stats KERNEL_STATS_CSV --command "..." > out.md
+    python -m gated_delta_rule_21_amd.profile_summary counters FETCH_CSV WRITE_CSV \\
+        --kernel chunk_fwd_kernel --algorithmic-bytes N --command "..." > out.md
+
+`stats` keeps the rows of a `--kernel-trace --stats` summary (kernel_stats.csv).
+`counters` reads two `--pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs
+(counter_collection.csv, values in KiB per dispatch).  It scales each counter by
+what the same counter reads for the streaming calibration kernel (torch.neg over
+1 GiB of fp32: 2^30 bytes read, 2^30 written), then reports HBM bytes per
+launch of the named kernel.
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import os
+import statistics
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CAL_KERNEL = "neg_kernel"          # substring of torch's elementwise negation kernel
+CAL_BYTES = 1 << 30
+
+
+def short_name(name: str) -> str:
+    name = name.split("(")[0]
+    return name.replace("void ", "")[:110]
+
+
+def kernel_source_digest() -> str:
+    """sha256 (first 16 hex digits) of the chunk-forward sources, as bench.py computes it."""
+    h = hashlib.sha256()
+    for n in ("chunk_fwd.hip", "device_common.h"):
+        with open(os.path.join(ROOT, "gated_delta_rule_21_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def decode_source_digest() -> str:
+    h = hashlib.sha256()
+    for n in ("decode_step.hip", "device_common.h"):
+        with open(os.path.join(ROOT, "gated_delta_rule_21_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stats(path: str, command: str, top: int) -> str:
+    rows = list(csv.DictReader(open(path)))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    out = ["# rocprofv3 kernel-trace statistics", "", "command:", "", "```", command, "```", "",
+           "| kernel | calls | avg us | min us | max us | total ms | % |", "|---|---|---|---|---|---|---|"]
+    for r in rows[:top]:
+        out.append(f"| `{short_name(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                   f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.2f} |")
+    return "\n".join(out) + "\n"
+
+
+def per_dispatch(path: str, counter: str):
+    vals = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        key = (r["Dispatch_Id"], r["Kernel_Name"])
+        vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+    return vals
+
+
+def pick(vals, sub: str):
+    return [v for (d, n), v in vals.items() if sub in n]
+
+
+def counters(fetch_csv: str, write_csv: str, kernel: str, algorithmic: float, command: str,
+             digest: str) -> str:
+    f = per_dispatch(fetch_csv, "FETCH_SIZE")
+    w = per_dispatch(write_csv, "WRITE_SIZE")
+    cf, cw = pick(f, CAL_KERNEL), pick(w, CAL_KERNEL)
+    kf, kw = pick(f, kernel), pick(w, kernel)
+    if not (cf and cw and kf and kw):
+        raise SystemExit(f"missing dispatches: cal {len(cf)}/{len(cw)}, kernel {len(kf)}/{len(kw)}")
+    sf = CAL_BYTES / (1024 * statistics.median(cf))
+    sw = CAL_BYTES / (1024 * statistics.median(cw))
+    fb = statistics.median(kf) * 1024 * sf
+    wb = statistics.median(kw) * 1024 * sw
+    tot = fb + wb
+    out = ["# HBM traffic counters", "", f"kernel: `{kernel}`", "", "commands (one counter per run):", "",
+           "```", command, "```", "",
+           "| quantity | value |", "|---|---|",
+           f"| calibration FETCH_SIZE (KiB, median of {len(cf)}) | {statistics.median(cf):.1f} |",
+           f"| calibration WRITE_SIZE (KiB, median of {len(cw)}) | {statistics.median(cw):.1f} |",
+           f"| calibration bytes read / written | {CAL_BYTES} / {CAL_BYTES} |",
+           f"| read scale (bytes per counted byte) | {sf:.4f} |",
+           f"| write scale (bytes per counted byte) | {sw:.4f} |",
+           f"| kernel FETCH_SIZE (KiB, median of {len(kf)}) | {statistics.median(kf):.1f} |",
+           f"| kernel WRITE_SIZE (KiB, median of {len(kw)}) | {statistics.median(kw):.1f} |",
+           f"| kernel HBM bytes read (scaled) | {fb:.4e} |",
+           f"| kernel HBM bytes written (scaled) | {wb:.4e} |",
+           f"| algorithmic bytes per launch | {algorithmic:.4e} |",
+           f"| traffic / algorithmic | {tot / algorithmic:.3f} |",
+           "", f"hbm_bytes_per_launch: {tot:.6e}", f"kernel_source_sha256_16: {digest}", ""]
+    return "\n".join(out)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    a = sub.add_parser("stats")
+    a.add_argument("csv")
+    a.add_argument("--command", required=True)
+    a.add_argument("--top", type=int, default=8)
+    b = sub.add_parser("counters")
+    b.add_argument("fetch_csv")
+    b.add_argument("write_csv")
+    b.add_argument("--kernel", required=True)
+    b.add_argument("--algorithmic-bytes", type=float, required=True)
+    b.add_argument("--command", required=True)
+    args = ap.parse_args(argv)
+    if args.cmd == "stats":
+        sys.stdout.write(stats(args.csv, args.command, args.top))
+    else:
+        digest = decode_source_digest() if "decode" in args.kernel else kernel_source_digest()
+        sys.stdout.write(counters(args.fetch_csv, args.write_csv, args.kernel, args.algorithmic_bytes,
+                                  args.command, digest))
+
+
+if __name__ == "__main__":
+    main()
