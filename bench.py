@@ -34,7 +34,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 CHUNK_SOURCES = [os.path.join(ROOT, "gated_delta_rule_21_amd", "csrc", n)
-                 for n in ("chunk_fwd.hip", "device_common.h")]
+                 for n in ("chunk_prep.hip", "chunk_fwd.hip", "chunk_common.h", "device_common.h")]
 DECODE_SOURCES = [os.path.join(ROOT, "gated_delta_rule_21_amd", "csrc", n)
                   for n in ("decode_step.hip", "device_common.h")]
 
@@ -149,10 +149,12 @@ def bench_chunk(args, log):
     del inp
     o = torch.empty((wl.B, wl.T, wl.H, wl.d_v), dtype=torch.bfloat16, device="cuda")
     S_T = torch.empty((wl.B, wl.H, wl.d_k, wl.d_v), dtype=torch.float32, device="cuda")
+    ws = torch.empty(gdr.chunk_workspace_size(wl.B, wl.T, wl.H, wl.d_k, wl.d_v, torch.bfloat16, wl.gate),
+                     dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
     def step():
-        gdr.chunk_fwd(q, k, v, beta, log_a, None, o=o, S_T=S_T)     # S0 = 0 for this workload
+        gdr.chunk_fwd(q, k, v, beta, log_a, None, o=o, S_T=S_T, workspace=ws)     # S0 = 0 for this workload
 
     for _ in range(args.warmup):
         step()

@@ -3,8 +3,9 @@
 Public calls (thin wrappers over the C ABI in include/gdr.h):
     chunk_fwd(q, k, v, beta, log_a=None, S0=None, form="page")  -> (o, S_T)
     recurrent_step(q, k, v, beta, log_a, S, form="page")         -> (o, S_new)
+    chunk_workspace_size(B, T, H, d_k, d_v, dtype)               -> bytes of scratch
 """
 
-from ._lib import EXPORTED, GdrError, LIB_PATH, chunk_fwd, load, recurrent_step
+from ._lib import EXPORTED, GdrError, LIB_PATH, chunk_fwd, chunk_workspace_size, load, recurrent_step
 
-__all__ = ["EXPORTED", "GdrError", "LIB_PATH", "chunk_fwd", "load", "recurrent_step"]
+__all__ = ["EXPORTED", "GdrError", "LIB_PATH", "chunk_fwd", "chunk_workspace_size", "load", "recurrent_step"]

@@ -22,7 +22,7 @@ GDR_F32, GDR_BF16 = 0, 1
 GATES = {"none": 0, "scalar": 1, "channel": 2}
 FORMS = {"page": 0, "literal": 1}
 
-EXPORTED = ("gdr_chunk_fwd", "gdr_recurrent_step", "gdr_status_string", "gdr_last_error", "gdr_version")
+EXPORTED = ("gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_recurrent_step", "gdr_status_string", "gdr_last_error", "gdr_version")
 
 
 class GdrDesc(ctypes.Structure):
@@ -52,8 +52,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
             raise RuntimeError(f"{p} is missing: build it with `python -m gated_delta_rule_21_amd.build`")
         lib = ctypes.CDLL(p)
         vp = ctypes.c_void_p
+        lib.gdr_chunk_fwd_workspace_size.restype = ctypes.c_int
+        lib.gdr_chunk_fwd_workspace_size.argtypes = [ctypes.POINTER(GdrDesc), ctypes.POINTER(ctypes.c_size_t)]
         lib.gdr_chunk_fwd.restype = ctypes.c_int
-        lib.gdr_chunk_fwd.argtypes = [ctypes.POINTER(GdrDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.gdr_chunk_fwd.argtypes = [ctypes.POINTER(GdrDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         lib.gdr_recurrent_step.restype = ctypes.c_int
         lib.gdr_recurrent_step.argtypes = [ctypes.POINTER(GdrDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.gdr_status_string.restype = ctypes.c_char_p
@@ -113,12 +115,25 @@ def _stream_handle(stream) -> int:
     return s.cuda_stream
 
 
+def chunk_workspace_size(B: int, T: int, H: int, d_k: int, d_v: int, dtype=torch.bfloat16,
+                         gate: str = "scalar") -> int:
+    """Bytes of scratch gdr_chunk_fwd needs for these sizes (gdr_chunk_fwd_workspace_size)."""
+    lib = load()
+    io = 1 if dtype == torch.bfloat16 else 0
+    desc = GdrDesc(B, T, H, d_k, d_v, 64, io, GATES[gate], 0)
+    n = ctypes.c_size_t(0)
+    _check(lib, lib.gdr_chunk_fwd_workspace_size(ctypes.byref(desc), ctypes.byref(n)))
+    return int(n.value)
+
+
 def chunk_fwd(q, k, v, beta, log_a=None, S0=None, *, form: str = "page", o=None, S_T=None,
-              want_state: bool = True, stream=None):
+              want_state: bool = True, workspace=None, stream=None):
     """gdr_chunk_fwd on torch tensors.  q, k [B, T, H, d_k]; v [B, T, H, d_v];
     beta [B, T, H]; log_a None, [B, T, H] or [B, T, H, d_k] (all one I/O dtype);
-    S0 None or [B, H, d_k, d_v] float32.  Returns (o, S_T) (S_T None when
-    want_state is False).  Asynchronous on the current (or given) stream."""
+    S0 None or [B, H, d_k, d_v] float32.  `workspace` is an optional uint8 device
+    tensor of at least chunk_workspace_size() bytes (allocated per call when
+    None).  Returns (o, S_T) (S_T None when want_state is False).  Asynchronous on
+    the current (or given) stream."""
     lib = load()
     B, T, H, dk = k.shape
     dv = v.shape[-1]
@@ -140,8 +155,14 @@ def chunk_fwd(q, k, v, beta, log_a=None, S0=None, *, form: str = "page", o=None,
     if S_T is not None:
         _require(S_T, "S_T", torch.float32, (B, H, dk, dv))
     desc = GdrDesc(B, T, H, dk, dv, 64, _io_of(q), gate, FORMS[form])
+    need = ctypes.c_size_t(0)
+    _check(lib, lib.gdr_chunk_fwd_workspace_size(ctypes.byref(desc), ctypes.byref(need)))
+    if workspace is None:
+        workspace = torch.empty(max(int(need.value), 1), dtype=torch.uint8, device=q.device)
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous() or workspace.device != q.device:
+        raise ValueError("workspace must be a contiguous uint8 tensor on the inputs' device")
     st = lib.gdr_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_a), _ptr(S0),
-                           _ptr(o), _ptr(S_T), _stream_handle(stream))
+                           _ptr(o), _ptr(S_T), _ptr(workspace), workspace.numel(), _stream_handle(stream))
     _check(lib, st)
     return o, S_T
 

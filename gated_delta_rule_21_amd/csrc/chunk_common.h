@@ -1,0 +1,122 @@
+// Pieces shared by the two chunk-forward kernels (the per-chunk transform and
+// the sequential state pass): operand access for the I/O dtype, wave-level
+// ordering, and the inverse of a unit lower triangular 16x16 block.
+#pragma once
+
+#include "device_common.h"
+
+namespace gdr {
+
+constexpr int CH = 64;   // chunk length
+
+template <int IO> struct Op;
+template <> struct Op<IO_BF16> {
+  typedef __bf16 T;
+  typedef bf16x4 frag;
+  static constexpr int PAD = 8;      // row stride 4 (mod 32) dwords: fewest LDS bank conflicts (measured)
+  static __device__ __forceinline__ frag ld(const T* p) { return *reinterpret_cast<const frag*>(p); }
+  // Fragment holding M[r0 + 4*lg + s][c0 + lr], s = 0..3, of a row-major tile M:
+  // the gfx950 LDS transpose load gathers it from 16 lanes' 8-byte reads.
+  static __device__ __forceinline__ frag ld_tr(const T* m, int ld, int r0, int c0, int lr, int lg) {
+    const T* a = m + (r0 + 4 * lg + (lr >> 2)) * ld + c0 + 4 * (lr & 3);
+    typedef __attribute__((ext_vector_type(4))) short v4s;
+    typedef __attribute__((address_space(3))) v4s lds_v4s;
+    const v4s x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(const_cast<T*>(a)));
+    return __builtin_bit_cast(frag, x);
+  }
+  static __device__ __forceinline__ frag cvt(f32x4 x) { return to_bf16x4(x); }
+  static __device__ __forceinline__ f32x4 f32(frag x) {
+    f32x4 r;
+    r[0] = static_cast<float>(x[0]); r[1] = static_cast<float>(x[1]);
+    r[2] = static_cast<float>(x[2]); r[3] = static_cast<float>(x[3]);
+    return r;
+  }
+  static __device__ __forceinline__ T from(float x) { return static_cast<__bf16>(x); }
+  static __device__ __forceinline__ f32x4 mma2(f32x4 acc, frag a0, frag a1, frag b0, frag b1) {
+    return mma_k32_bf16(acc, a0, a1, b0, b1);
+  }
+  static __device__ __forceinline__ f32x4 mma1(f32x4 acc, frag a, frag b) { return mma_k16_bf16(acc, a, b); }
+};
+template <> struct Op<IO_F32> {
+  typedef float T;
+  typedef f32x4 frag;
+  static constexpr int PAD = 4;
+  static __device__ __forceinline__ frag ld(const T* p) { return *reinterpret_cast<const frag*>(p); }
+  static __device__ __forceinline__ frag ld_tr(const T* m, int ld, int r0, int c0, int lr, int lg) {
+    frag f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) f[s] = m[(r0 + 4 * lg + s) * ld + c0 + lr];
+    return f;
+  }
+  static __device__ __forceinline__ frag cvt(f32x4 x) { return x; }
+  static __device__ __forceinline__ f32x4 f32(frag x) { return x; }
+  static __device__ __forceinline__ T from(float x) { return x; }
+  static __device__ __forceinline__ f32x4 mma2(f32x4 acc, frag a0, frag a1, frag b0, frag b1) {
+    return mma_k16_f32(mma_k16_f32(acc, a0, b0), a1, b1);
+  }
+  static __device__ __forceinline__ f32x4 mma1(f32x4 acc, frag a, frag b) { return mma_k16_f32(acc, a, b); }
+};
+
+constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
+
+// Workspace record of one (sequence, head, chunk), written by the per-chunk
+// transform and read by the state pass: T = (I + A)^{-1} and the masked score
+// matrix P, each [64][64] row-major in the I/O dtype, then per-row fp32 factors
+// [5][64] (no gate / scalar gate): beta, e^{g_read}, e^{g}, e^{g_63 - g}, e^{g_63}.
+template <int ESZ>
+struct WsRec {
+  static constexpr uint32_t T_OFF = 0;
+  static constexpr uint32_t P_OFF = CH * CH * ESZ;
+  static constexpr uint32_t F_OFF = 2 * CH * CH * ESZ;
+  static constexpr uint32_t BYTES = F_OFF + 5 * CH * 4;
+};
+
+__device__ __forceinline__ int strict_pair(int R, int J) { return R * (R - 1) / 2 + J; }
+
+// Ordering point for LDS traffic between the lanes of one wave.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// (I + N)^{-1} of a strictly lower 16x16 block N held as an accumulator tile, by
+// the finite Neumann product (I - N)(I + N^2)(I + N^4)(I + N^8) (N^16 = 0), on
+// fp32 MFMA.  `scr` is this wave's 16x16 fp32 scratch, used to turn an
+// accumulator tile into a row-major A operand.
+__device__ __forceinline__ f32x4 unit_lower_inverse(f32x4 N, float* scr, int lr, int lg) {
+  constexpr int LSC = 20;
+  auto put = [&](f32x4 M) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) scr[(4 * lg + s) * LSC + lr] = M[s];
+  };
+  auto rows = [&]() -> f32x4 { return *reinterpret_cast<const f32x4*>(scr + lr * LSC + 4 * lg); };
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  f32x4 Y;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) Y[s] = (4 * lg + s == lr ? 1.f : 0.f) - N[s];
+  put(N);
+  wave_sync();
+  f32x4 a = rows();
+  wave_sync();
+  f32x4 P = mma_k16_f32(zero, a, N);          // N^2
+  put(P);
+  wave_sync();
+  a = rows();
+  wave_sync();
+  Y = mma_k16_f32(Y, a, Y);                   // (I + N^2)(I - N)
+  P = mma_k16_f32(zero, a, P);                // N^4
+  put(P);
+  wave_sync();
+  a = rows();
+  wave_sync();
+  Y = mma_k16_f32(Y, a, Y);
+  P = mma_k16_f32(zero, a, P);                // N^8
+  put(P);
+  wave_sync();
+  a = rows();
+  wave_sync();
+  return mma_k16_f32(Y, a, Y);
+}
+
+}  // namespace gdr

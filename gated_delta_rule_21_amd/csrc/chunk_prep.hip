@@ -1,0 +1,372 @@
+// Per-chunk transform of the gated delta rule on gfx950: everything about a
+// chunk that does not depend on the state, for every (batch, head, chunk) at once.
+//
+// "Moonshot AI's New Attention Architecture: Key Innovations Explained", §3
+// Hardware-Friendly Algorithm: inside a chunk, the delta-rule correction terms
+// come from a unit lower triangular system whose strictly lower part is the
+// beta-weighted, gate-decayed Gram matrix of the chunk's keys, and the output
+// adds a causally masked product of queries and keys; neither depends on the
+// state passed between chunks.  With g_r the inclusive running sum of log a over
+// the chunk rows (§5 Practical Considerations: the gate in the log domain),
+//     A = strict_lower( diag(beta) (K * e^{g_read}) (K * e^{-g})^T ),
+//     T = (I + A)^{-1},
+//     P = lower_incl( (Q * e^{g}) (K * e^{-g})^T ),
+// where g_read = g when the decay precedes the erase and g_{r-1} when the erase
+// reads the undecayed state.  Written per chunk (the workspace record): T and P
+// row-major in the I/O dtype and, without a per-channel gate, the per-row
+// factors beta, e^{g_read}, e^{g}, e^{g_63 - g}, e^{g_63} in fp32.
+//
+// One workgroup of four waves per chunk.  Wave R forms the diagonal block A_RR
+// and inverts I + A_RR by the finite Neumann product on fp32 MFMA; the six
+// blocks below the diagonal are shared out.  Then wave J walks down block
+// column J of T by forward substitution,
+//     T_JJ = (I + A_JJ)^{-1},   T_RJ = -(I + A_RR)^{-1} sum_{J <= m < R} A_Rm T_mJ,
+// keeping the T blocks of its column in accumulators (an accumulator tile is
+// the B operand layout of the next product), while the waves with shorter
+// columns form more of the ten blocks of P.
+//
+// Per-channel gate: the decay sits inside the d_k contraction, so the operands
+// are built decayed; the factor e^{g_r - g_j} is split at the first row of each
+// 16-row block (e^{g_r - g_16R} on the row operand, e^{g_16J - g_j} on the column
+// operand, e^{g_16R - g_16J} on the column operand of blocks below the
+// diagonal), so no operand carries more than 15 tokens of decay.
+#include <type_traits>
+
+#include "chunk_common.h"
+#include "launchers.h"
+
+namespace gdr {
+
+template <int IO, int GATE, int DK>
+struct PrepLayout {
+  typedef typename Op<IO>::T T;
+  static constexpr bool RAW = GATE != GATE_CHANNEL;
+  static constexpr int PAD = Op<IO>::PAD;
+  static constexpr int LDK = DK + PAD;
+  static constexpr int LCH = CH + PAD;
+  static constexpr int LSC = 20;
+  static constexpr int NSEG = 256 / DK;                  // row segments of the per-channel scan
+  static constexpr size_t RM = size_t(CH) * LDK * sizeof(T);
+  static constexpr size_t MM = size_t(CH) * LCH * sizeof(T);
+  static constexpr size_t OFF_K = 0;                      // raw k; per-channel: beta k e^{g_read - g_16R}
+  static constexpr size_t OFF_Q = OFF_K + RM;             // raw q; per-channel: q e^{g - g_16R}
+  static constexpr size_t OFF_A = OFF_Q + RM;             // A, blocks below the diagonal
+  static constexpr size_t OFF_T = OFF_A + MM;             // result tiles
+  static constexpr size_t OFF_P = OFF_T + MM;
+  static constexpr size_t OFF_SC = OFF_P + MM;            // per-wave 16x16 fp32 scratch
+  static constexpr size_t OFF_X = OFF_SC + 4 * 16 * LSC * 4;
+  // no gate / scalar gate: beta, g, g_read
+  static constexpr size_t R_TOTAL = OFF_X + 3 * CH * 4;
+  // per-channel gate
+  static constexpr size_t C_Y = OFF_X;                    // column operand k e^{g_16J - g}
+  static constexpr size_t C_G = C_Y + RM;                 // g [64][DK] fp32
+  static constexpr size_t C_BETA = C_G + size_t(CH) * DK * 4;
+  static constexpr size_t C_M = C_BETA + CH * 4;          // e^{g_16R - g_16J}, 6 block pairs
+  static constexpr size_t C_TOT = C_M + 6 * DK * 4;
+  static constexpr size_t C_TOTAL = C_TOT + NSEG * DK * 4;
+  static constexpr size_t TOTAL = RAW ? R_TOTAL : C_TOTAL;
+};
+
+template <int IO, int GATE, int DK>
+__global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkParams p, int64_t nchunks) {
+  typedef Op<IO> O;
+  typedef typename O::T T;
+  typedef typename Io<IO>::elem elem;
+  typedef PrepLayout<IO, GATE, DK> L;
+  constexpr bool RAW = L::RAW;
+  constexpr int NT = 256;
+  constexpr int LDK = L::LDK, LCH = L::LCH;
+  constexpr int ESZ = int(sizeof(elem));
+  typedef WsRec<ESZ> W;
+  constexpr int EPV = 16 / ESZ;                 // elements per 16-byte piece
+  constexpr int KROW = DK / EPV;
+  constexpr int KV = CH * KROW / NT;            // 16-byte pieces of the k (q) tile per thread
+  constexpr int TROW = CH / EPV;
+  constexpr int TV = CH * TROW / NT;            // 16-byte pieces of a 64x64 tile per thread
+  static_assert(KV * NT == CH * KROW && TV * NT == CH * TROW, "tile pieces must split evenly");
+  static_assert(L::TOTAL <= 163840, "LDS budget");
+
+  __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
+  T* sK = reinterpret_cast<T*>(smem + L::OFF_K);
+  T* sQ = reinterpret_cast<T*>(smem + L::OFF_Q);
+  T* sA = reinterpret_cast<T*>(smem + L::OFF_A);
+  T* sT = reinterpret_cast<T*>(smem + L::OFF_T);
+  T* sP = reinterpret_cast<T*>(smem + L::OFF_P);
+  float* sScr = reinterpret_cast<float*>(smem + L::OFF_SC);
+  float* sBr = reinterpret_cast<float*>(smem + L::OFF_X);
+  float* sGr = sBr + CH;
+  float* sGrd = sBr + 2 * CH;
+  T* sY = reinterpret_cast<T*>(smem + L::C_Y);
+  float* sG = reinterpret_cast<float*>(smem + L::C_G);
+  float* sBc = reinterpret_cast<float*>(smem + L::C_BETA);
+  float* sM = reinterpret_cast<float*>(smem + L::C_M);
+  float* sTot = reinterpret_cast<float*>(smem + L::C_TOT);
+
+  const int64_t bh = blockIdx.x / nchunks;
+  const int64_t n = blockIdx.x % nchunks;
+  const int64_t bb = bh / p.H, hh = bh % p.H;
+  const int H = static_cast<int>(p.H);
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int lr = lane & 15;
+  const int lg = lane >> 4;
+  char* rec = static_cast<char*>(p.ws) + (bh * nchunks + n) * W::BYTES;
+
+  // The chunk's rows through buffers whose range ends at the sequence's last
+  // token: rows of a ragged last chunk read as zero.
+  const int64_t t0 = n * CH;
+  const int64_t row0 = (bb * p.T + t0) * p.H + hh;      // token row of (b, t0, h)
+  const int64_t left = p.T - t0;                         // >= 1
+  const uint32_t span = static_cast<uint32_t>(((left < CH ? left : CH) - 1) * p.H + 1);
+  const rsrc_t rk = make_rsrc(static_cast<const elem*>(p.k) + row0 * DK, span * DK * ESZ);
+  const rsrc_t rq = make_rsrc(static_cast<const elem*>(p.q) + row0 * DK, span * DK * ESZ);
+  const rsrc_t rb = make_rsrc(static_cast<const elem*>(p.beta) + row0, span * ESZ);
+  const rsrc_t rl = make_rsrc(static_cast<const elem*>(p.log_a) + row0 * (GATE == GATE_CHANNEL ? DK : 1),
+                              GATE == GATE_NONE ? 0u : span * (GATE == GATE_CHANNEL ? DK : 1) * ESZ);
+  auto to_f32 = [&](uint32_t bits) -> float {
+    if constexpr (IO == IO_BF16) return bf16_bits_to_f32(static_cast<uint16_t>(bits));
+    else return __uint_as_float(bits);
+  };
+  auto load1 = [&](rsrc_t r, uint32_t off) -> float {
+    if constexpr (IO == IO_BF16) return to_f32(buf_load2(r, off, 0));
+    else return to_f32(buf_load4(r, off, 0));
+  };
+
+  // ---- chunk into LDS -------------------------------------------------------------
+#pragma unroll
+  for (int v = 0; v < KV; ++v) {
+    const int seg = tid + v * NT, row = seg / KROW, c = (seg % KROW) * EPV;
+    const uint32_t off = static_cast<uint32_t>((row * H * DK + c) * ESZ);
+    *reinterpret_cast<u32x4*>(sK + row * LDK + c) = buf_load16(rk, off, 0);
+    *reinterpret_cast<u32x4*>(sQ + row * LDK + c) = buf_load16(rq, off, 0);
+    if constexpr (GATE == GATE_CHANNEL) {
+      const u32x4 w4 = buf_load16(rl, off, 0);
+#pragma unroll
+      for (int j = 0; j < EPV; ++j) {
+        const uint32_t w = w4[j * ESZ / 4];
+        sG[row * DK + c + j] = to_f32(ESZ == 2 ? (w >> (16 * (j & 1))) & 0xffffu : w);
+      }
+    }
+  }
+  if constexpr (RAW) {
+    if (wave == 0) {              // inclusive scan of the log-gate; per-row factors
+      const uint32_t off = static_cast<uint32_t>(lane * H * ESZ);
+      const float b = load1(rb, off);
+      float g = 0.f, gread = 0.f;
+      if constexpr (GATE == GATE_SCALAR) {
+        g = load1(rl, off);
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+          const float y = __shfl_up(g, d);
+          if (lane >= d) g += y;
+        }
+        const float gprev = __shfl_up(g, 1);
+        gread = p.literal ? (lane == 0 ? 0.f : gprev) : g;
+      }
+      const float gC = __shfl(g, 63);
+      sBr[lane] = b;
+      sGr[lane] = g;
+      sGrd[lane] = gread;
+      float* f = reinterpret_cast<float*>(rec + W::F_OFF);
+      f[lane] = b;
+      f[CH + lane] = __expf(gread);
+      f[2 * CH + lane] = __expf(g);
+      f[3 * CH + lane] = __expf(gC - g);
+      f[4 * CH + lane] = __expf(gC);
+    }
+  } else {
+    if (tid < CH) sBc[tid] = load1(rb, static_cast<uint32_t>(tid * H * ESZ));
+  }
+  __syncthreads();
+
+  if constexpr (!RAW) {
+    // inclusive scan of the gate down each key channel, in NSEG row segments
+    constexpr int NSEG = L::NSEG, SEGL = CH / NSEG;
+    {
+      const int i = tid % DK, seg = tid / DK;
+      float acc = 0.f;
+#pragma unroll 8
+      for (int r = seg * SEGL; r < (seg + 1) * SEGL; ++r) {
+        acc += sG[r * DK + i];
+        sG[r * DK + i] = acc;
+      }
+      sTot[seg * DK + i] = acc;
+    }
+    if constexpr (NSEG > 1) {
+      __syncthreads();
+      const int i = tid % DK, seg = tid / DK;
+      float pre = 0.f;
+      for (int s2 = 0; s2 < seg; ++s2) pre += sTot[s2 * DK + i];
+      if (seg > 0)
+        for (int r = seg * SEGL; r < (seg + 1) * SEGL; ++r) sG[r * DK + i] += pre;
+    }
+    __syncthreads();
+    for (int i = tid; i < DK; i += NT) {
+#pragma unroll
+      for (int R = 1; R < 4; ++R)
+#pragma unroll
+        for (int J = 0; J < R; ++J)
+          sM[strict_pair(R, J) * DK + i] = __expf(sG[16 * R * DK + i] - sG[16 * J * DK + i]);
+    }
+    // decayed operands; the row operands overwrite the raw tiles in place
+    for (int task = tid; task < CH * (DK / 4); task += NT) {
+      const int r = task / (DK / 4), i0 = (task % (DK / 4)) * 4, R = r >> 4;
+      const f32x4 kk = O::f32(O::ld(sK + r * LDK + i0));
+      const f32x4 qq = O::f32(O::ld(sQ + r * LDK + i0));
+      const float be = sBc[r];
+      f32x4 xk, xq, y;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = i0 + j;
+        const float g = sG[r * DK + i], gR = sG[16 * R * DK + i];
+        const float gread = p.literal ? (r > 0 ? sG[(r - 1) * DK + i] : 0.f) : g;
+        xk[j] = be * kk[j] * __expf(gread - gR);
+        xq[j] = qq[j] * __expf(g - gR);
+        y[j] = kk[j] * __expf(gR - g);
+      }
+      *reinterpret_cast<typename O::frag*>(sK + r * LDK + i0) = O::cvt(xk);
+      *reinterpret_cast<typename O::frag*>(sQ + r * LDK + i0) = O::cvt(xq);
+      *reinterpret_cast<typename O::frag*>(sY + r * LDK + i0) = O::cvt(y);
+    }
+    __syncthreads();
+  }
+
+  // ---- 16x16 blocks of A (strictly lower) and P (lower incl. diagonal) ------------------
+  auto block = [&](auto is_p, int R, int J) -> f32x4 {
+    constexpr bool isP = decltype(is_p)::value;
+    const T* rows = isP ? sQ : sK;
+    const T* cols = RAW ? sK : sY;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < DK / 32; ++kb) {
+      const int c = 32 * kb + 4 * lg;
+      const auto a0 = O::ld(rows + (16 * R + lr) * LDK + c);
+      const auto a1 = O::ld(rows + (16 * R + lr) * LDK + c + 16);
+      auto b0 = O::ld(cols + (16 * J + lr) * LDK + c);
+      auto b1 = O::ld(cols + (16 * J + lr) * LDK + c + 16);
+      if constexpr (GATE == GATE_CHANNEL) {
+        if (R > J) {
+          const float* m = sM + strict_pair(R, J) * DK + c;
+          b0 = O::cvt(O::f32(b0) * *reinterpret_cast<const f32x4*>(m));
+          b1 = O::cvt(O::f32(b1) * *reinterpret_cast<const f32x4*>(m + 16));
+        }
+      }
+      acc = O::mma2(acc, a0, a1, b0, b1);
+    }
+    const int j = 16 * J + lr;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int rr = 4 * lg + s, r = 16 * R + rr;
+      float val = acc[s];
+      if constexpr (GATE == GATE_SCALAR) val *= __expf((isP ? sGr[r] : sGrd[r]) - sGr[j]);
+      if constexpr (RAW && !isP) val *= sBr[r];
+      acc[s] = (R == J && (isP ? rr < lr : rr <= lr)) ? 0.f : val;
+    }
+    return acc;
+  };
+
+  // diagonal block of this wave: T_RR = (I + A_RR)^{-1}; zero blocks right of it
+  const int R0 = wave;
+  const f32x4 Dw = unit_lower_inverse(block(std::false_type{}, R0, R0), sScr + wave * 16 * L::LSC, lr, lg);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int r = 16 * R0 + 4 * lg + s;
+    sT[r * LCH + 16 * R0 + lr] = O::from(Dw[s]);
+#pragma unroll
+    for (int J = 0; J < 4; ++J)
+      if (J > R0) {
+        sT[r * LCH + 16 * J + lr] = O::from(0.f);
+        sP[r * LCH + 16 * J + lr] = O::from(0.f);
+      }
+  }
+  // the six blocks of A below the diagonal, (1,0) (2,0) (2,1) (3,0) (3,1) (3,2):
+  // task t goes to wave 3 - t % 4, so the wave with the longest column solve gets fewest
+#pragma unroll
+  for (int t = 0; t < 6; ++t) {
+    if (3 - (t & 3) != wave) continue;
+    const int R = 1 + (t >= 1) + (t >= 3), J = t - R * (R - 1) / 2;
+    const f32x4 acc = block(std::false_type{}, R, J);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) sA[(16 * R + 4 * lg + s) * LCH + 16 * J + lr] = O::from(acc[s]);
+  }
+  __syncthreads();
+
+  // ---- block column J = wave of T by forward substitution ------------------------------
+  {
+    const int J = wave;
+    typename O::frag Tb[4];
+    Tb[0] = Tb[1] = Tb[2] = Tb[3] = O::cvt(Dw);
+#pragma unroll
+    for (int R = 1; R < 4; ++R) {
+      if (R <= J) continue;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < 3; ++m)
+        if (m >= J && m < R) acc = O::mma1(acc, O::ld(sA + (16 * R + lr) * LCH + 16 * m + 4 * lg), Tb[m]);
+      f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      z = O::mma1(z, O::ld(sT + (16 * R + lr) * LCH + 16 * R + 4 * lg), O::cvt(acc));
+      z = -z;
+      Tb[R] = O::cvt(z);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) sT[(16 * R + 4 * lg + s) * LCH + 16 * J + lr] = O::from(z[s]);
+    }
+  }
+  // ---- P blocks (0,0) (1,0) (1,1) (2,0) ... (3,3): wave w takes w + 1 of them ------------
+  {
+    const int first = 10 - (wave + 1) * (wave + 2) / 2;
+    for (int u = first; u < first + wave + 1; ++u) {
+      const int R = (u >= 1) + (u >= 3) + (u >= 6), J = u - R * (R + 1) / 2;
+      const f32x4 acc = block(std::true_type{}, R, J);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) sP[(16 * R + 4 * lg + s) * LCH + 16 * J + lr] = O::from(acc[s]);
+    }
+  }
+  __syncthreads();
+
+  // ---- T and P to the workspace record, row-major [64][64] ------------------------------
+  elem* dT = reinterpret_cast<elem*>(rec + W::T_OFF);
+  elem* dP = reinterpret_cast<elem*>(rec + W::P_OFF);
+#pragma unroll
+  for (int v = 0; v < TV; ++v) {
+    const int seg = tid + v * NT, row = seg / TROW, c = (seg % TROW) * EPV;
+    *reinterpret_cast<u32x4*>(dT + row * CH + c) = *reinterpret_cast<const u32x4*>(sT + row * LCH + c);
+    *reinterpret_cast<u32x4*>(dP + row * CH + c) = *reinterpret_cast<const u32x4*>(sP + row * LCH + c);
+  }
+}
+
+template <int IO, int GATE, int DK>
+static hipError_t launch_prep_t(const ChunkParams& p, int64_t nchunks, hipStream_t stream) {
+  const int64_t nblk = p.B * p.H * nchunks;
+  hipLaunchKernelGGL((chunk_prep_kernel<IO, GATE, DK>), dim3(static_cast<unsigned>(nblk)), dim3(256), 0, stream, p,
+                     nchunks);
+  return hipGetLastError();
+}
+
+template <int IO, int GATE>
+static hipError_t launch_prep_g(const ChunkParams& p, int64_t nchunks, hipStream_t stream) {
+  if (p.d_k == 128) {
+    if constexpr (IO == IO_F32) return hipErrorInvalidValue;
+    else return launch_prep_t<IO, GATE, 128>(p, nchunks, stream);
+  }
+  if (p.d_k == 64) return launch_prep_t<IO, GATE, 64>(p, nchunks, stream);
+  return hipErrorInvalidValue;
+}
+
+template <int IO>
+static hipError_t launch_prep_io(const ChunkParams& p, int64_t nchunks, hipStream_t stream) {
+  switch (p.gate) {
+    case GATE_NONE: return launch_prep_g<IO, GATE_NONE>(p, nchunks, stream);
+    case GATE_SCALAR: return launch_prep_g<IO, GATE_SCALAR>(p, nchunks, stream);
+    case GATE_CHANNEL: return launch_prep_g<IO, GATE_CHANNEL>(p, nchunks, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_chunk_prep(const ChunkParams& p, hipStream_t stream) {
+  const int64_t nchunks = (p.T + CH - 1) / CH;
+  if (p.B * p.H * nchunks == 0) return hipSuccess;
+  return p.io == IO_BF16 ? launch_prep_io<IO_BF16>(p, nchunks, stream) : launch_prep_io<IO_F32>(p, nchunks, stream);
+}
+
+}  // namespace gdr

@@ -67,7 +67,8 @@ gdr_status check_desc(const gdr_desc* d, bool decode) {
   int64_t bh, bth, x;
   if (!mul_ok(d->B, d->H, &bh) || !mul_ok(bh, d->T, &bth) || !mul_ok(bth, 128, &x) || !mul_ok(bh, 128 * 128 * 4, &x))
     return fail(GDR_ERR_INVALID_ARG, "sizes overflow");
-  if (bh * 8 > INT32_MAX) return fail(GDR_ERR_UNSUPPORTED, "B*H = %lld exceeds the grid limit", (long long)bh);
+  if (bh * 8 > INT32_MAX || bh * ((d->T + 63) / 64) > INT32_MAX)
+    return fail(GDR_ERR_UNSUPPORTED, "B*H = %lld (x chunks) exceeds the grid limit", (long long)bh);
   // The kernels address one sequence's (b, h) slice with 32-bit byte offsets.
   const int64_t esz = d->io == GDR_BF16 ? 2 : 4;
   const int64_t dmax = d->d_k > d->d_v ? d->d_k : d->d_v;
@@ -75,6 +76,9 @@ gdr_status check_desc(const gdr_desc* d, bool decode) {
   if (!mul_ok(d->T, d->H, &seq_bytes) || !mul_ok(seq_bytes, dmax * esz, &seq_bytes) || seq_bytes > INT32_MAX)
     return fail(GDR_ERR_UNSUPPORTED, "T*H*max(d_k,d_v)*elem_size = %lld bytes exceeds 2^31 - 1 per sequence",
                 (long long)seq_bytes);
+  // ... and one sequence's workspace records the same way
+  if (!decode && static_cast<int64_t>(gdr::chunk_workspace_bytes(1, d->T, 1, d->io)) > INT32_MAX)
+    return fail(GDR_ERR_UNSUPPORTED, "T = %lld: the per-sequence workspace exceeds 2^31 - 1 bytes", (long long)d->T);
   return GDR_OK;
 }
 
@@ -113,12 +117,28 @@ const char* gdr_last_error(void) { return g_last_error.c_str(); }
 
 int gdr_version(void) { return 100; }
 
+gdr_status gdr_chunk_fwd_workspace_size(const gdr_desc* d, size_t* bytes) {
+  try {
+    g_last_error.clear();
+    if (!bytes) return fail(GDR_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = 0;
+    gdr_status st = check_desc(d, false);
+    if (st != GDR_OK) return st;
+    *bytes = gdr::chunk_workspace_bytes(d->B, d->T, d->H, d->io);
+    return GDR_OK;
+  } catch (...) {
+    return fail(GDR_ERR_INVALID_ARG, "internal error");
+  }
+}
+
 gdr_status gdr_chunk_fwd(const gdr_desc* d, const void* q, const void* k, const void* v, const void* beta,
-                         const void* log_a, const float* S0, void* o, float* S_T, void* stream) {
+                         const void* log_a, const float* S0, void* o, float* S_T, void* workspace,
+                         size_t workspace_bytes, void* stream) {
   try {
     g_last_error.clear();
     gdr_status st = check_desc(d, false);
     if (st != GDR_OK) return st;
+    const size_t ws_need = gdr::chunk_workspace_bytes(d->B, d->T, d->H, d->io);
     const int64_t esz = d->io == GDR_BF16 ? 2 : 4;
     const int64_t ntok = d->B * d->T * d->H;
     const bool any = d->T > 0;
@@ -129,24 +149,30 @@ gdr_status gdr_chunk_fwd(const gdr_desc* d, const void* q, const void* k, const 
       if (!beta) return fail(GDR_ERR_INVALID_ARG, "beta is NULL");
       if (!o) return fail(GDR_ERR_INVALID_ARG, "o is NULL");
       if (d->gate != GDR_GATE_NONE && !log_a) return fail(GDR_ERR_INVALID_ARG, "log_a is NULL but a gate is requested");
+      if (!workspace) return fail(GDR_ERR_INVALID_ARG, "workspace is NULL (%zu bytes needed)", ws_need);
+      if (workspace_bytes < ws_need)
+        return fail(GDR_ERR_INVALID_ARG, "workspace_bytes = %zu, %zu needed", workspace_bytes, ws_need);
     }
     if (d->gate == GDR_GATE_NONE && log_a) return fail(GDR_ERR_INVALID_ARG, "log_a must be NULL for GDR_GATE_NONE");
     if ((st = check_align("q", q, 16)) || (st = check_align("k", k, 16)) || (st = check_align("v", v, 16)) ||
         (st = check_align("o", o, 16)) || (st = check_align("S0", S0, 16)) || (st = check_align("S_T", S_T, 16)) ||
-        (st = check_align("beta", beta, esz)) || (st = check_align("log_a", log_a, esz)))
+        (st = check_align("beta", beta, esz)) || (st = check_align("log_a", log_a, esz)) ||
+        (st = check_align("workspace", workspace, 16)))
       return st;
     const int64_t gate_w = d->gate == GDR_GATE_NONE ? 0 : d->gate == GDR_GATE_SCALAR ? 1 : d->d_k;
     const int64_t state_bytes = d->B * d->H * d->d_k * d->d_v * 4;
     Span all[] = {span("q", q, ntok * d->d_k * esz), span("k", k, ntok * d->d_k * esz),
                   span("v", v, ntok * d->d_v * esz), span("beta", beta, ntok * esz),
                   span("log_a", log_a, ntok * gate_w * esz), span("S0", S0, state_bytes),
-                  span("o", o, ntok * d->d_v * esz), span("S_T", S_T, state_bytes)};
-    Span outs[] = {all[6], all[7]};
+                  span("o", o, ntok * d->d_v * esz), span("S_T", S_T, state_bytes),
+                  span("workspace", d->T > 0 ? workspace : nullptr, static_cast<int64_t>(ws_need))};
+    Span outs[] = {all[6], all[7], all[8]};
     if (S_T && S0 == S_T) all[5].hi = all[5].lo;   // exact in-place update of the state is allowed
-    if ((st = check_no_overlap(outs, 2, all, 8))) return st;
+    if ((st = check_no_overlap(outs, 3, all, 9))) return st;
 
     gdr::ChunkParams p;
     p.q = q; p.k = k; p.v = v; p.beta = beta; p.log_a = log_a; p.S0 = S0; p.o = o; p.S_T = S_T;
+    p.ws = workspace;
     p.B = d->B; p.T = d->T; p.H = d->H;
     p.d_k = static_cast<int>(d->d_k); p.d_v = static_cast<int>(d->d_v);
     p.io = d->io; p.gate = d->gate; p.literal = d->form == GDR_FORM_LITERAL;

@@ -29,12 +29,16 @@ struct ChunkParams {
   const float* S0;    // may be null (zero initial state)
   void* o;
   float* S_T;         // may be null (not written)
+  void* ws;           // per-chunk inverses T, B*H*ceil(T/64) tiles of 64x64 in the I/O dtype
   int64_t B, T, H;
   int d_k, d_v;
   int io, gate, literal;
 };
 
 hipError_t launch_decode_step(const DecodeParams& p, hipStream_t stream);
+// Per-chunk transform (T tiles into p.ws), then the state pass; one stream, in order.
+hipError_t launch_chunk_prep(const ChunkParams& p, hipStream_t stream);
 hipError_t launch_chunk_fwd(const ChunkParams& p, hipStream_t stream);
+size_t chunk_workspace_bytes(int64_t B, int64_t T, int64_t H, int io);
 
 }  // namespace gdr

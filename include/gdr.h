@@ -19,10 +19,11 @@
  *
  * Conventions shared by every entry point
  * ---------------------------------------
- *  - Every pointer argument is a DEVICE pointer except `desc`, which is a host
- *    pointer read during the call only.  The caller owns every buffer; the
- *    library allocates no device memory, keeps no mutable global state and
- *    is safe to call from several host threads.
+ *  - Every pointer argument is a DEVICE pointer except `desc` (and the size
+ *    out-parameter of gdr_chunk_fwd_workspace_size), which are host pointers
+ *    used during the call only.  The caller owns every buffer, scratch
+ *    included; the library allocates no device memory, keeps no mutable global
+ *    state and is safe to call from several host threads.
  *  - Work is enqueued asynchronously on `stream` (0 = the null stream).  The
  *    library never synchronises; the caller synchronises before reading results.
  *  - All tensors are dense, contiguous and row-major in the layouts given
@@ -84,6 +85,21 @@ typedef struct {
 } gdr_desc;
 
 /*
+ * gdr_chunk_fwd_workspace_size -- device scratch that gdr_chunk_fwd needs.
+ *
+ * Writes to *bytes the size of the workspace for a forward described by desc.
+ * Per (sequence, head, chunk) it holds what the chunk contributes independently
+ * of the state ("Moonshot AI's New Attention Architecture", §3): the inverse
+ * (I + A)^{-1} of the chunk's unit lower triangular system (its WY correction
+ * terms are that solve applied to the keys and values) and the causally masked
+ * query-key score matrix, both 64 x 64 in the I/O dtype, plus five rows of 64
+ * fp32 per-token gate factors.  That is B * H * ceil(T / 64) * (8192 * elem +
+ * 1280) bytes (0 when T == 0).  Returns the same errors as gdr_chunk_fwd's
+ * descriptor checks; *bytes is 0 on error.
+ */
+gdr_status gdr_chunk_fwd_workspace_size(const gdr_desc* desc, size_t* bytes);
+
+/*
  * gdr_chunk_fwd -- forward over whole sequences with the chunkwise-parallel form.
  *
  * Defined by the recurrence above, run token by token from S0 for each (b, h)
@@ -104,12 +120,24 @@ typedef struct {
  *          the same pointer as S0 (updated in place) but must not otherwise
  *          overlap any argument.
  *   o must not overlap any input or S_T.
+ *   workspace        device scratch of at least gdr_chunk_fwd_workspace_size()
+ *                    bytes, 16-byte aligned, overlapping no other argument (may
+ *                    be NULL when T == 0).  Its contents on entry do not matter
+ *                    and are overwritten; it may be reused once the call's work
+ *                    on `stream` has finished (or by later work on the same
+ *                    stream).  Calls that overlap in time need separate ones.
+ *   workspace_bytes  its size in bytes.
+ *
+ * Two kernels run in order on `stream`: the per-chunk transform (cumulative
+ * log-gate, the gated Gram blocks of the keys, (I + A)^{-1}, the masked score
+ * matrix) for all chunks at once, then the sequential state pass with the output.
  *
  * T == 0 writes S_T = S0 (or zeros).  T need not be a multiple of the chunk.
  */
 gdr_status gdr_chunk_fwd(const gdr_desc* desc, const void* q, const void* k, const void* v,
                          const void* beta, const void* log_a, const float* S0, void* o,
-                         float* S_T, void* stream /* hipStream_t */);
+                         float* S_T, void* workspace, size_t workspace_bytes,
+                         void* stream /* hipStream_t */);
 
 /*
  * gdr_recurrent_step -- one decode token for B independent sequences.

@@ -52,13 +52,49 @@ def _desc(**kw):
     return GdrDesc(**d)
 
 
-def _ptrs(n=8, start=FAKE, stride=1 << 24):
+def _ptrs(n=9, start=FAKE, stride=1 << 24):
     return [start + i * stride for i in range(n)]
 
 
-def _chunk(lib, d, ptrs):
-    q, k, v, beta, log_a, S0, o, S_T = ptrs
-    return lib.gdr_chunk_fwd(None if d is None else ctypes.byref(d), q, k, v, beta, log_a, S0, o, S_T, None)
+def _ws_size(lib, d):
+    n = ctypes.c_size_t(12345)
+    st = lib.gdr_chunk_fwd_workspace_size(None if d is None else ctypes.byref(d), ctypes.byref(n))
+    return st, n.value
+
+
+def _chunk(lib, d, ptrs, ws_bytes=None):
+    q, k, v, beta, log_a, S0, o, S_T = ptrs[:8]
+    ws = ptrs[8] if len(ptrs) > 8 else None
+    if ws_bytes is None:
+        ws_bytes = _ws_size(lib, d)[1] if d is not None else 0
+    return lib.gdr_chunk_fwd(None if d is None else ctypes.byref(d), q, k, v, beta, log_a, S0, o, S_T,
+                             ws, ws_bytes, None)
+
+
+def test_workspace_size(lib):
+    rec = lambda esz: 2 * 64 * 64 * esz + 5 * 64 * 4     # T, P, five rows of fp32 factors
+    assert _ws_size(lib, _desc(B=2, T=130, H=3)) == (OK, 2 * 3 * 3 * rec(2))        # bf16, 3 chunks
+    assert _ws_size(lib, _desc(io=0, d_k=64, T=64)) == (OK, 2 * 1 * rec(4))         # fp32, 1 chunk
+    assert _ws_size(lib, _desc(T=0)) == (OK, 0)
+    assert _ws_size(lib, None) == (INVALID, 0)
+    assert _ws_size(lib, _desc(d_k=96)) == (UNSUPPORTED, 0)
+    assert lib.gdr_chunk_fwd_workspace_size(ctypes.byref(_desc()), None) == INVALID
+
+
+def test_workspace_checks(lib):
+    p = _ptrs()
+    p[8] = None
+    assert _chunk(lib, _desc(), p) == INVALID                  # missing workspace
+    assert b"workspace" in lib.gdr_last_error()
+    need = _ws_size(lib, _desc())[1]
+    assert _chunk(lib, _desc(), _ptrs(), ws_bytes=need - 1) == INVALID
+    p = _ptrs()
+    p[8] += 8
+    assert _chunk(lib, _desc(), p) == ALIGN                    # workspace 16-byte alignment
+    p = _ptrs()
+    p[8] = p[6] + 64                                           # workspace inside o
+    assert _chunk(lib, _desc(), p) == INVALID
+    assert b"overlaps" in lib.gdr_last_error()
 
 
 def test_null_desc(lib):
@@ -114,7 +150,7 @@ def test_output_overlapping_input_is_rejected(lib):
 
 
 def _step(lib, d, ptrs):
-    q, k, v, beta, log_a, S, S_new, o = ptrs
+    q, k, v, beta, log_a, S, S_new, o = ptrs[:8]
     return lib.gdr_recurrent_step(ctypes.byref(d), q, k, v, beta, log_a, S, S_new, o, None)
 
 

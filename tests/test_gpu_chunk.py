@@ -114,6 +114,29 @@ def test_state_updated_in_place():
     check("S_T", host(S), S_ref, TOL["bf16"])
 
 
+def test_caller_workspace_reused_and_dirty():
+    """A caller workspace full of NaN bit patterns is overwritten before use, and
+    one workspace serves calls of different sizes and gates in a row."""
+    need_gpu()
+    import torch
+    from tests.gpu_util import dev, host
+    import gated_delta_rule_21_amd as gdr
+    big = gdr.chunk_workspace_size(2, 260, 3, 128, 128, torch.bfloat16)
+    ws = torch.full((big,), 0xFF, dtype=torch.uint8, device="cuda")
+    for name, shape, gate, seed in (("ws1", (2, 260, 3, 128, 128), "channel", 47),
+                                    ("ws2", (1, 70, 2, 64, 128), "scalar", 53)):
+        inp = chunk_inputs(_wl(name, *shape, gate=gate, seed=seed))
+        S0 = torch.from_numpy(inp["S0"]).cuda()
+        o, S = gdr.chunk_fwd(*(dev(inp[n], "bf16") for n in ("q", "k", "v", "beta", "log_a")), S0, workspace=ws)
+        torch.cuda.synchronize()
+        o_ref, S_ref = oracle_chunk(inp)
+        check(f"{name} o", host(o), o_ref, TOL["bf16"])
+        check(f"{name} S_T", host(S), S_ref, TOL["bf16"])
+    with pytest.raises(gdr.GdrError):
+        inp = chunk_inputs(_wl("ws3", 2, 260, 4, 128, 128, gate="scalar", seed=59))   # needs more than `big`
+        gdr.chunk_fwd(*(dev(inp[n], "bf16") for n in ("q", "k", "v", "beta", "log_a")), None, workspace=ws)
+
+
 # ---- full-size workloads: whole-tensor run on the GPU, sampled (b, h) slices
 #      checked against the oracle one slice at a time -----------------------------
 def _sampled(cfg):
