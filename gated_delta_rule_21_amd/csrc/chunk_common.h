@@ -60,9 +60,11 @@ template <> struct Op<IO_F32> {
 constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
 
 // Workspace record of one (sequence, head, chunk), written by the per-chunk
-// transform and read by the state pass: T = (I + A)^{-1} and the masked score
-// matrix P, each [64][64] row-major in the I/O dtype, then per-row fp32 factors
-// [5][64] (no gate / scalar gate): beta, e^{g_read}, e^{g}, e^{g_63 - g}, e^{g_63}.
+// transform and read by the state pass: T^T (the transpose of T = (I + A)^{-1})
+// and the masked score matrix P, each [64][64] row-major in the I/O dtype (only
+// the blocks on or above the diagonal of T^T and on or below the diagonal of P
+// are written; the others are never read), then per-row fp32 factors [5][64]
+// (no gate / scalar gate): beta, e^{g_read}, e^{g}, e^{g_63 - g}, e^{g_63}.
 template <int ESZ>
 struct WsRec {
   static constexpr uint32_t T_OFF = 0;
@@ -117,6 +119,37 @@ __device__ __forceinline__ f32x4 unit_lower_inverse(f32x4 N, float* scr, int lr,
   a = rows();
   wave_sync();
   return mma_k16_f32(Y, a, Y);
+}
+
+// (I + N)^{-1} of a strictly lower 16x16 block N, in registers, for one wave.
+// N and Nt are the accumulator tiles of N and of N^T.  An accumulator tile of X
+// fed back as the B operand of a product stands for X, and as the A operand for
+// X^T, so both orientations of every power are formed side by side:
+//     D = (I - N)(I + N^2)(I + N^4)(I + N^8)   (N^16 = 0; the factors commute)
+// Returns D in D and D^T in Dt (both accumulator tiles); 12 products on the
+// MFMA of the I/O dtype with fp32 accumulation.
+template <class O>
+__device__ __forceinline__ void unit_lower_inverse_pair(f32x4 N, f32x4 Nt, f32x4& D, f32x4& Dt, int lr, int lg) {
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  f32x4 Y, Yt;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const float id = 4 * lg + s == lr ? 1.f : 0.f;
+    Y[s] = id - N[s];
+    Yt[s] = id - Nt[s];
+  }
+  const f32x4 N2 = O::mma1(z, O::cvt(Nt), O::cvt(N));      // N N
+  const f32x4 N2t = O::mma1(z, O::cvt(N), O::cvt(Nt));     // N^T N^T
+  Y = O::mma1(Y, O::cvt(N2t), O::cvt(Y));                  // (I + N^2) Y
+  Yt = O::mma1(Yt, O::cvt(N2), O::cvt(Yt));                // (Y (I + N^2))^T
+  const f32x4 N4 = O::mma1(z, O::cvt(N2t), O::cvt(N2));
+  const f32x4 N4t = O::mma1(z, O::cvt(N2), O::cvt(N2t));
+  Y = O::mma1(Y, O::cvt(N4t), O::cvt(Y));
+  Yt = O::mma1(Yt, O::cvt(N4), O::cvt(Yt));
+  const f32x4 N8 = O::mma1(z, O::cvt(N4t), O::cvt(N4));
+  const f32x4 N8t = O::mma1(z, O::cvt(N4), O::cvt(N4t));
+  D = O::mma1(Y, O::cvt(N8t), O::cvt(Y));
+  Dt = O::mma1(Yt, O::cvt(N8), O::cvt(Yt));
 }
 
 }  // namespace gdr

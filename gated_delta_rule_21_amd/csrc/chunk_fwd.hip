@@ -71,11 +71,14 @@ struct Layout {
   static constexpr size_t OFF_K = 0;                     // raw k (per-channel: k e^{g_read})
   static constexpr size_t OFF_Q = OFF_K + RM;            // raw q (per-channel: q e^{g})
   static constexpr size_t OFF_V = OFF_Q + RM;            // raw v tile
-  static constexpr size_t OFF_T = OFF_V + V_B;           // T = (I + A)^{-1}
+  static constexpr size_t OFF_T = OFF_V + V_B;           // T^T, T = (I + A)^{-1}
   static constexpr size_t OFF_P = OFF_T + MM;            // P
   static constexpr size_t OFF_F = OFF_P + MM;            // beta, e^{g_read}, e^{g}, e^{g_63 - g}, e^{g_63}
   static constexpr size_t OFF_X = OFF_F + 5 * CH * 4;    // per-channel regions start here
-  static constexpr size_t R_TOTAL = OFF_X;
+  // no gate / scalar gate: the regions above, twice when that fits (chunk n is
+  // read from one copy while chunk n+1 is written to the other)
+  static constexpr int NB = (RAW && 2 * OFF_X <= 163840) ? 2 : 1;
+  static constexpr size_t R_TOTAL = NB * OFF_X;
   // per-channel gate
   static constexpr size_t C_KD = OFF_X;                  // k e^{g_63 - g}
   static constexpr size_t C_G = C_KD + RM;               // g [64][DK] fp32
@@ -109,18 +112,8 @@ __global__ __launch_bounds__(NW * 64) void chunk_fwd_kernel(ChunkParams p, int n
                 "tile loads must split evenly");
   static_assert(L::TOTAL <= 163840, "LDS budget");
 
+  constexpr int NB = L::NB;
   __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
-  T* sK = reinterpret_cast<T*>(smem + L::OFF_K);
-  T* sQ = reinterpret_cast<T*>(smem + L::OFF_Q);
-  T* sV = reinterpret_cast<T*>(smem + L::OFF_V);
-  T* sT = reinterpret_cast<T*>(smem + L::OFF_T);
-  T* sP = reinterpret_cast<T*>(smem + L::OFF_P);
-  float* sF = reinterpret_cast<float*>(smem + L::OFF_F);
-  float* sBeta = sF;                // beta
-  float* sEr = sF + CH;             // e^{g_read}    (rows of K S)
-  float* sEo = sF + 2 * CH;         // e^{g}         (output rows)
-  float* sEd = sF + 3 * CH;         // e^{g_63 - g}  (Delta rows in the state update)
-  float* sGamR = sF + 4 * CH;       // e^{g_63}
   // per-channel regions
   T* sKd = reinterpret_cast<T*>(smem + L::C_KD);
   float* sG = reinterpret_cast<float*>(smem + L::C_G);
@@ -141,7 +134,7 @@ __global__ __launch_bounds__(NW * 64) void chunk_fwd_kernel(ChunkParams p, int n
   const int H = static_cast<int>(p.H);
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform across the wave
   const int lane = tid & 63;
   const int lr = lane & 15;
   const int lg = lane >> 4;
@@ -214,17 +207,19 @@ __global__ __launch_bounds__(NW * 64) void chunk_fwd_kernel(ChunkParams p, int n
     }
   };
 
-  if (nchunks > 0) prefetch(0);
-
-  for (int64_t n = 0; n < nchunks; ++n) {
-    const int64_t t0 = n * CH;
-
-    // ---- chunk from registers into LDS, per-chunk log-gate; next chunk's loads -----
+  // the prefetched chunk from registers into one LDS copy
+  auto store_chunk = [&](char* base) __attribute__((always_inline)) {
+    T* dK = reinterpret_cast<T*>(base + L::OFF_K);
+    T* dQ = reinterpret_cast<T*>(base + L::OFF_Q);
+    T* dV = reinterpret_cast<T*>(base + L::OFF_V);
+    T* dT = reinterpret_cast<T*>(base + L::OFF_T);
+    T* dP = reinterpret_cast<T*>(base + L::OFF_P);
+    float* dF = reinterpret_cast<float*>(base + L::OFF_F);
 #pragma unroll
     for (int v = 0; v < KV; ++v) {
       const int seg = tid + v * NT, row = seg / KROW, c = (seg % KROW) * EPV;
-      *reinterpret_cast<u32x4*>(sK + row * LDK + c) = pk[v];
-      *reinterpret_cast<u32x4*>(sQ + row * LDK + c) = pq[v];
+      *reinterpret_cast<u32x4*>(dK + row * LDK + c) = pk[v];
+      *reinterpret_cast<u32x4*>(dQ + row * LDK + c) = pq[v];
       if constexpr (GATE == GATE_CHANNEL) {
 #pragma unroll
         for (int j = 0; j < EPV; ++j) {
@@ -236,21 +231,57 @@ __global__ __launch_bounds__(NW * 64) void chunk_fwd_kernel(ChunkParams p, int n
 #pragma unroll
     for (int v = 0; v < VV; ++v) {
       const int seg = tid + v * NT, row = seg / VROW, c = (seg % VROW) * EPV;
-      *reinterpret_cast<u32x4*>(sV + row * LVT + c) = pv[v];
+      *reinterpret_cast<u32x4*>(dV + row * LVT + c) = pv[v];
     }
 #pragma unroll
     for (int v = 0; v < TV; ++v) {
       const int seg = tid + v * NT, row = seg / TROW, c = (seg % TROW) * EPV;
-      *reinterpret_cast<u32x4*>(sT + row * LCH + c) = pt[v];
-      *reinterpret_cast<u32x4*>(sP + row * LCH + c) = pp[v];
+      *reinterpret_cast<u32x4*>(dT + row * LCH + c) = pt[v];
+      *reinterpret_cast<u32x4*>(dP + row * LCH + c) = pp[v];
     }
     if constexpr (RAW) {
-      if (tid < FV) *reinterpret_cast<u32x4*>(sF + 4 * tid) = pf;
+      if (tid < FV) *reinterpret_cast<u32x4*>(dF + 4 * tid) = pf;
     } else {
-      if (tid < CH) sBeta[tid] = pb;
+      if (tid < CH) dF[tid] = pb;
     }
-    if (n + 1 < nchunks) prefetch(n + 1);
+  };
+
+  if (nchunks > 0) prefetch(0);
+  if constexpr (NB == 2) {
+    if (nchunks > 0) {
+      store_chunk(smem);
+      if (nchunks > 1) prefetch(1);
+    }
     __syncthreads();
+  }
+
+  for (int64_t n = 0; n < nchunks; ++n) {
+    const int64_t t0 = n * CH;
+    char* cur = smem + (NB == 2 ? (n & 1) * L::OFF_X : 0);
+    const T* sK = reinterpret_cast<const T*>(cur + L::OFF_K);
+    const T* sQ = reinterpret_cast<const T*>(cur + L::OFF_Q);
+    const T* sV = reinterpret_cast<const T*>(cur + L::OFF_V);
+    const T* sT = reinterpret_cast<const T*>(cur + L::OFF_T);
+    const T* sP = reinterpret_cast<const T*>(cur + L::OFF_P);
+    const float* sF = reinterpret_cast<const float*>(cur + L::OFF_F);
+    const float* sBeta = sF;                // beta
+    const float* sEr = sF + CH;             // e^{g_read}    (rows of K S)
+    const float* sEo = sF + 2 * CH;         // e^{g}         (output rows)
+    const float* sEd = sF + 3 * CH;         // e^{g_63 - g}  (Delta rows in the state update)
+    const float* sGamR = sF + 4 * CH;       // e^{g_63}
+
+    // ---- next chunk's tiles into LDS and the loads after it; per-channel gate -------
+    if constexpr (NB == 2) {
+      // the other copy was last read in the previous chunk, before its closing barrier
+      if (n + 1 < nchunks) {
+        store_chunk(smem + ((n + 1) & 1) * L::OFF_X);
+        if (n + 2 < nchunks) prefetch(n + 2);
+      }
+    } else {
+      store_chunk(smem);
+      if (n + 1 < nchunks) prefetch(n + 1);
+      __syncthreads();
+    }
 
     if constexpr (!RAW) {
       // per-channel scan over the rows of each channel
@@ -292,8 +323,8 @@ __global__ __launch_bounds__(NW * 64) void chunk_fwd_kernel(ChunkParams p, int n
           qh[j] = qq[j] * __expf(g);
           kd[j] = kk[j] * __expf(gC - g);
         }
-        *reinterpret_cast<frag*>(sK + r * LDK + i0) = O::cvt(kr);
-        *reinterpret_cast<frag*>(sQ + r * LDK + i0) = O::cvt(qh);
+        *reinterpret_cast<frag*>(const_cast<T*>(sK) + r * LDK + i0) = O::cvt(kr);
+        *reinterpret_cast<frag*>(const_cast<T*>(sQ) + r * LDK + i0) = O::cvt(qh);
         *reinterpret_cast<frag*>(sKd + r * LDK + i0) = O::cvt(kd);
       }
       __syncthreads();
@@ -324,13 +355,14 @@ __global__ __launch_bounds__(NW * 64) void chunk_fwd_kernel(ChunkParams p, int n
     }
     frag Db[4], Ds[4];
 #pragma unroll
-    for (int R = 0; R < 4; ++R) {            // Delta_R = sum_{m <= R} T_Rm R_m
-      const T* tr = sT + (16 * R + lr) * LCH + 4 * lg;
+    for (int R = 0; R < 4; ++R) {            // Delta_R = sum_{m <= R} T_Rm R_m; rows of T from T^T
       f32x4 d = {0.f, 0.f, 0.f, 0.f};
       int m = 0;
 #pragma unroll
-      for (; m + 1 <= R; m += 2) d = O::mma2(d, O::ld(tr + 16 * m), O::ld(tr + 16 * (m + 1)), Rb[m], Rb[m + 1]);
-      if (m <= R) d = O::mma1(d, O::ld(tr + 16 * m), Rb[m]);
+      for (; m + 1 <= R; m += 2)
+        d = O::mma2(d, O::ld_tr(sT, LCH, 16 * m, 16 * R, lr, lg), O::ld_tr(sT, LCH, 16 * (m + 1), 16 * R, lr, lg),
+                    Rb[m], Rb[m + 1]);
+      if (m <= R) d = O::mma1(d, O::ld_tr(sT, LCH, 16 * m, 16 * R, lr, lg), Rb[m]);
       Db[R] = O::cvt(d);
       if constexpr (GATE == GATE_SCALAR) {
         f32x4 ds;
@@ -365,10 +397,7 @@ __global__ __launch_bounds__(NW * 64) void chunk_fwd_kernel(ChunkParams p, int n
       // rows past the end of the sequence fall outside the buffer and are dropped
       const uint32_t voff = static_cast<uint32_t>((r * H * dv + col0 + 16 * wave + 4 * lg) * ESZ);
       if constexpr (IO == IO_BF16) {
-        u32x2 w;
-        w[0] = uint32_t(f32_to_bf16_bits(ov[0])) | (uint32_t(f32_to_bf16_bits(ov[1])) << 16);
-        w[1] = uint32_t(f32_to_bf16_bits(ov[2])) | (uint32_t(f32_to_bf16_bits(ov[3])) << 16);
-        buf_store8(w, ro, voff, so);
+        buf_store8(__builtin_bit_cast(u32x2, to_bf16x4(ov)), ro, voff, so);
       } else {
         u32x4 w;
 #pragma unroll
@@ -393,7 +422,7 @@ __global__ __launch_bounds__(NW * 64) void chunk_fwd_kernel(ChunkParams p, int n
                     Ds[2], Ds[3]);
       S[t] = acc;
     }
-    __syncthreads();                          // LDS is rewritten by the next chunk
+    __syncthreads();                          // this copy of LDS is rewritten after the next chunk
   }
 
   if (p.S_T) {

@@ -12,24 +12,35 @@
 //     T = (I + A)^{-1},
 //     P = lower_incl( (Q * e^{g}) (K * e^{-g})^T ),
 // where g_read = g when the decay precedes the erase and g_{r-1} when the erase
-// reads the undecayed state.  Written per chunk (the workspace record): T and P
-// row-major in the I/O dtype and, without a per-channel gate, the per-row
+// reads the undecayed state; without a per-channel gate also the per-row
 // factors beta, e^{g_read}, e^{g}, e^{g_63 - g}, e^{g_63} in fp32.
 //
-// One workgroup of four waves per chunk.  Wave R forms the diagonal block A_RR
-// and inverts I + A_RR by the finite Neumann product on fp32 MFMA; the six
-// blocks below the diagonal are shared out.  Then wave J walks down block
-// column J of T by forward substitution,
-//     T_JJ = (I + A_JJ)^{-1},   T_RJ = -(I + A_RR)^{-1} sum_{J <= m < R} A_Rm T_mJ,
-// keeping the T blocks of its column in accumulators (an accumulator tile is
-// the B operand layout of the next product), while the waves with shorter
-// columns form more of the ten blocks of P.
+// Written per chunk (the workspace record): T^T and P row-major, so that the
+// state pass reads T's rows with the LDS transpose load and P's rows directly.
 //
-// Per-channel gate: the decay sits inside the d_k contraction, so the operands
-// are built decayed; the factor e^{g_r - g_j} is split at the first row of each
-// 16-row block (e^{g_r - g_16R} on the row operand, e^{g_16J - g_j} on the column
+// No gate / scalar gate (chunk_prep_reg_kernel): one wave per chunk, every
+// operand in registers.  The Gram sums run over d_k, so k and q are loaded as
+// 16-byte pieces straight into MFMA operand registers (A and B take the same
+// channel order, which leaves each sum unchanged).  An accumulator tile of X
+// stands for X as the B operand of a product and for X^T as the A operand, so:
+// the blocks A_Rm are formed transposed (operands swapped), which is the A
+// operand of the solve; the symmetric diagonal Gram block gives both
+// orientations of A_RR, whose inverse D_R is a finite Neumann product in
+// registers (both orientations again); then row block R of T follows by
+// forward substitution,
+//     T_RR = D_R,   T_RJ = -D_R sum_{J <= m < R} A_Rm T_mJ,
+// with T blocks kept as B operands.  P blocks are formed transposed too, which
+// is the layout of P's rows.  Everything is stored 8 bytes per lane from the
+// accumulators; no LDS is used beyond 768 bytes of per-row factors.
+//
+// Per-channel gate (chunk_prep_lds_kernel): the decay sits inside the d_k
+// contraction, so decayed operands are built in LDS by a four-wave workgroup
+// per chunk; the factor e^{g_r - g_j} is split at the first row of each 16-row
+// block (e^{g_r - g_16R} on the row operand, e^{g_16J - g_j} on the column
 // operand, e^{g_16R - g_16J} on the column operand of blocks below the
-// diagonal), so no operand carries more than 15 tokens of decay.
+// diagonal), so no operand carries more than 15 tokens of decay.  Wave R
+// inverts I + A_RR (Neumann product on fp32 MFMA), the blocks below the diagonal
+// are shared out, and wave J walks down block column J of T.
 #include <type_traits>
 
 #include "chunk_common.h"
@@ -68,7 +79,7 @@ struct PrepLayout {
 };
 
 template <int IO, int GATE, int DK>
-__global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkParams p, int64_t nchunks) {
+__global__ __launch_bounds__(256) void chunk_prep_lds_kernel(ChunkParams p, int64_t nchunks) {
   typedef Op<IO> O;
   typedef typename O::T T;
   typedef typename Io<IO>::elem elem;
@@ -102,9 +113,11 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkParams p, int64_t 
   float* sM = reinterpret_cast<float*>(smem + L::C_M);
   float* sTot = reinterpret_cast<float*>(smem + L::C_TOT);
 
-  const int64_t bh = blockIdx.x / nchunks;
-  const int64_t n = blockIdx.x % nchunks;
-  const int64_t bb = bh / p.H, hh = bh % p.H;
+  // block order (batch, chunk, head), head fastest (see chunk_prep_reg_kernel)
+  const int64_t hh = blockIdx.x % p.H;
+  const int64_t n = (blockIdx.x / p.H) % nchunks;
+  const int64_t bb = blockIdx.x / (p.H * nchunks);
+  const int64_t bh = bb * p.H + hh;
   const int H = static_cast<int>(p.H);
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -266,20 +279,11 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkParams p, int64_t 
     return acc;
   };
 
-  // diagonal block of this wave: T_RR = (I + A_RR)^{-1}; zero blocks right of it
+  // diagonal block of this wave: T_RR = (I + A_RR)^{-1}, stored transposed (sT holds T^T)
   const int R0 = wave;
   const f32x4 Dw = unit_lower_inverse(block(std::false_type{}, R0, R0), sScr + wave * 16 * L::LSC, lr, lg);
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const int r = 16 * R0 + 4 * lg + s;
-    sT[r * LCH + 16 * R0 + lr] = O::from(Dw[s]);
-#pragma unroll
-    for (int J = 0; J < 4; ++J)
-      if (J > R0) {
-        sT[r * LCH + 16 * J + lr] = O::from(0.f);
-        sP[r * LCH + 16 * J + lr] = O::from(0.f);
-      }
-  }
+  for (int s = 0; s < 4; ++s) sT[(16 * R0 + lr) * LCH + 16 * R0 + 4 * lg + s] = O::from(Dw[s]);
   // the six blocks of A below the diagonal, (1,0) (2,0) (2,1) (3,0) (3,1) (3,2):
   // task t goes to wave 3 - t % 4, so the wave with the longest column solve gets fewest
 #pragma unroll
@@ -305,11 +309,11 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkParams p, int64_t 
       for (int m = 0; m < 3; ++m)
         if (m >= J && m < R) acc = O::mma1(acc, O::ld(sA + (16 * R + lr) * LCH + 16 * m + 4 * lg), Tb[m]);
       f32x4 z = {0.f, 0.f, 0.f, 0.f};
-      z = O::mma1(z, O::ld(sT + (16 * R + lr) * LCH + 16 * R + 4 * lg), O::cvt(acc));
+      z = O::mma1(z, O::ld_tr(sT, LCH, 16 * R, 16 * R, lr, lg), O::cvt(acc));   // rows of D_R from T^T
       z = -z;
       Tb[R] = O::cvt(z);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) sT[(16 * R + 4 * lg + s) * LCH + 16 * J + lr] = O::from(z[s]);
+      for (int s = 0; s < 4; ++s) sT[(16 * J + lr) * LCH + 16 * R + 4 * lg + s] = O::from(z[s]);
     }
   }
   // ---- P blocks (0,0) (1,0) (1,1) (2,0) ... (3,3): wave w takes w + 1 of them ------------
@@ -324,7 +328,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkParams p, int64_t 
   }
   __syncthreads();
 
-  // ---- T and P to the workspace record, row-major [64][64] ------------------------------
+  // ---- T^T and P to the workspace record, row-major [64][64] ----------------------------
   elem* dT = reinterpret_cast<elem*>(rec + W::T_OFF);
   elem* dP = reinterpret_cast<elem*>(rec + W::P_OFF);
 #pragma unroll
@@ -335,11 +339,196 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkParams p, int64_t 
   }
 }
 
+// ---------------------------------------------------------------------------------
+// No gate / scalar gate: one wave per (sequence, head, chunk), operands in registers.
+// ---------------------------------------------------------------------------------
+template <int IO, int GATE, int DK>
+__global__ __launch_bounds__(256) void chunk_prep_reg_kernel(ChunkParams p, int64_t nchunks, int64_t ntasks) {
+  typedef Op<IO> O;
+  typedef typename O::frag frag;
+  typedef typename Io<IO>::elem elem;
+  constexpr int ESZ = int(sizeof(elem));
+  typedef WsRec<ESZ> W;
+  constexpr int EPV = 16 / ESZ;                 // elements per 16-byte piece
+  constexpr int NSTEP = DK / (4 * EPV);         // products over d_k (four lane groups, one piece each)
+  static_assert(GATE != GATE_CHANNEL, "per-channel gate uses chunk_prep_lds_kernel");
+  static_assert(NSTEP * 4 * EPV == DK, "d_k must split into pieces");
+
+  __shared__ __attribute__((aligned(16))) float sfac[4][3 * CH];   // per wave: beta, g, g_read
+  // the wave index is uniform across the wave; saying so keeps every address
+  // and buffer descriptor derived from it in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int lr = lane & 15;
+  const int lg = lane >> 4;
+  // Task order (batch, chunk, head), head fastest: waves running side by side read
+  // the whole token rows [t][H][d_k] of one chunk of one sequence together.
+  const int64_t task = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  if (task >= ntasks) return;                   // this wave has no chunk (no workgroup barriers below)
+  const int64_t hh = task % p.H;
+  const int64_t n = (task / p.H) % nchunks;
+  const int64_t bb = task / (p.H * nchunks);
+  const int64_t bh = bb * p.H + hh;
+  const int H = static_cast<int>(p.H);
+  char* rec = static_cast<char*>(p.ws) + (bh * nchunks + n) * W::BYTES;
+  float* sB = sfac[wave];
+  float* sG = sB + CH;
+  float* sGr = sB + 2 * CH;
+
+  // The chunk's rows through buffers whose range ends at the sequence's last token.
+  const int64_t t0 = n * CH;
+  const int64_t row0 = (bb * p.T + t0) * p.H + hh;
+  const int64_t left = p.T - t0;
+  const uint32_t span = static_cast<uint32_t>(((left < CH ? left : CH) - 1) * p.H + 1);
+  const rsrc_t rk = make_rsrc(static_cast<const elem*>(p.k) + row0 * DK, span * DK * ESZ);
+  const rsrc_t rq = make_rsrc(static_cast<const elem*>(p.q) + row0 * DK, span * DK * ESZ);
+  const rsrc_t rb = make_rsrc(static_cast<const elem*>(p.beta) + row0, span * ESZ);
+  const rsrc_t rl = make_rsrc(static_cast<const elem*>(p.log_a) + row0, GATE == GATE_NONE ? 0u : span * ESZ);
+  auto load1 = [&](rsrc_t r, uint32_t off) -> float {
+    if constexpr (IO == IO_BF16) return bf16_bits_to_f32(buf_load2(r, off, 0));
+    else return __uint_as_float(buf_load4(r, off, 0));
+  };
+  // piece i of row block R: row 16R + lr, channels [(4i + lg) EPV, (4i + lg + 1) EPV)
+  auto piece_off = [&](int R, int i) -> uint32_t {
+    return static_cast<uint32_t>(((16 * R + lr) * H * DK + (4 * i + lg) * EPV) * ESZ);
+  };
+  u32x4 kf[4][NSTEP];
+#pragma unroll
+  for (int R = 0; R < 4; ++R)
+#pragma unroll
+    for (int i = 0; i < NSTEP; ++i) kf[R][i] = buf_load16(rk, piece_off(R, i), 0);
+
+  // ---- per-row gate factors (lane = row) ---------------------------------------------
+  {
+    const uint32_t off = static_cast<uint32_t>(lane * H * ESZ);
+    const float b = load1(rb, off);
+    float g = 0.f, gread = 0.f;
+    if constexpr (GATE == GATE_SCALAR) {
+      g = load1(rl, off);
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const float y = __shfl_up(g, d);
+        if (lane >= d) g += y;
+      }
+      const float gprev = __shfl_up(g, 1);
+      gread = p.literal ? (lane == 0 ? 0.f : gprev) : g;
+    }
+    const float gC = __shfl(g, 63);
+    sB[lane] = b;
+    sG[lane] = g;
+    sGr[lane] = gread;
+    float* f = reinterpret_cast<float*>(rec + W::F_OFF);
+    f[lane] = b;
+    f[CH + lane] = __expf(gread);
+    f[2 * CH + lane] = __expf(g);
+    f[3 * CH + lane] = __expf(gC - g);
+    f[4 * CH + lane] = __expf(gC);
+  }
+  wave_sync();
+
+  auto gram = [&](const u32x4* a, const u32x4* b) -> f32x4 {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NSTEP; ++i) {
+      if constexpr (IO == IO_BF16) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[i]), __builtin_bit_cast(bf16x8, b[i]),
+                                                     acc, 0, 0, 0);
+      } else {
+        acc = mma_k16_f32(acc, __builtin_bit_cast(f32x4, a[i]), __builtin_bit_cast(f32x4, b[i]));
+      }
+    }
+    return acc;
+  };
+  // four consecutive elements of a row of a [64][64] record matrix
+  auto store4 = [&](uint32_t base, int row, int col, f32x4 x) {
+    char* d = rec + base + static_cast<uint32_t>((row * CH + col) * ESZ);
+    if constexpr (IO == IO_BF16) *reinterpret_cast<u32x2*>(d) = __builtin_bit_cast(u32x2, to_bf16x4(x));
+    else *reinterpret_cast<u32x4*>(d) = __builtin_bit_cast(u32x4, x);
+  };
+  // element s of a transposed-product tile sits at row r = 16R + lr, column j = 16J + 4lg + s;
+  // A factor: beta_r e^{g_read_r - g_j}
+  auto a_factor = [&](f32x4 acc, int R, int J) -> f32x4 {
+    const float br = sB[16 * R + lr], grr = sGr[16 * R + lr];
+    const f32x4 gj = *reinterpret_cast<const f32x4*>(sG + 16 * J + 4 * lg);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      float v = acc[s] * br;
+      if constexpr (GATE == GATE_SCALAR) v *= __expf(grr - gj[s]);
+      acc[s] = (R == J && lr <= 4 * lg + s) ? 0.f : v;
+    }
+    return acc;
+  };
+
+  frag Tb[4][4];                                  // Tb[R][J] = T_RJ as a B operand (J <= R)
+#pragma unroll
+  for (int R = 0; R < 4; ++R) {
+    u32x4 qf[NSTEP];
+#pragma unroll
+    for (int i = 0; i < NSTEP; ++i) qf[i] = buf_load16(rq, piece_off(R, i), 0);
+
+    // A_Rm (m < R) as A operands: transposed Gram blocks
+    frag aRow[3];
+#pragma unroll
+    for (int m = 0; m < R; ++m) aRow[m] = O::cvt(a_factor(gram(kf[m], kf[R]), R, m));
+    // diagonal block, both orientations, and its inverse
+    const f32x4 G = gram(kf[R], kf[R]);
+    const f32x4 Nt = a_factor(G, R, R);         // accumulator tile of A_RR^T
+    f32x4 N;                                       // accumulator tile of A_RR: row 16R+4lg+s, column 16R+lr
+    {
+      const f32x4 br = *reinterpret_cast<const f32x4*>(sB + 16 * R + 4 * lg);
+      const f32x4 grr = *reinterpret_cast<const f32x4*>(sGr + 16 * R + 4 * lg);
+      const float gj = sG[16 * R + lr];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        float v = G[s] * br[s];
+        if constexpr (GATE == GATE_SCALAR) v *= __expf(grr[s] - gj);
+        N[s] = (4 * lg + s > lr) ? v : 0.f;
+      }
+    }
+    f32x4 D, Dt;
+    unit_lower_inverse_pair<O>(N, Nt, D, Dt, lr, lg);
+    Tb[R][R] = O::cvt(D);
+    store4(W::T_OFF, 16 * R + lr, 16 * R + 4 * lg, D);     // T^T block (R, R)
+    const frag dA = O::cvt(Dt);                             // D_R as an A operand
+#pragma unroll
+    for (int J = 0; J < R; ++J) {
+      f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = J; m < R; ++m) y = O::mma1(y, aRow[m], Tb[m][J]);
+      f32x4 t = {0.f, 0.f, 0.f, 0.f};
+      t = O::mma1(t, dA, O::cvt(y));
+      t = -t;
+      Tb[R][J] = O::cvt(t);
+      store4(W::T_OFF, 16 * J + lr, 16 * R + 4 * lg, t);   // T^T block (J, R)
+    }
+
+    // P row block R: transposed products give P's rows; factor e^{g_r - g_j}, mask r >= j
+    const float gr = sG[16 * R + lr];
+#pragma unroll
+    for (int J = 0; J <= R; ++J) {
+      f32x4 acc = gram(kf[J], qf);
+      const f32x4 gj = *reinterpret_cast<const f32x4*>(sG + 16 * J + 4 * lg);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        float v = acc[s];
+        if constexpr (GATE == GATE_SCALAR) v *= __expf(gr - gj[s]);
+        acc[s] = (J == R && lr < 4 * lg + s) ? 0.f : v;
+      }
+      store4(W::P_OFF, 16 * R + lr, 16 * J + 4 * lg, acc);
+    }
+  }
+}
+
 template <int IO, int GATE, int DK>
 static hipError_t launch_prep_t(const ChunkParams& p, int64_t nchunks, hipStream_t stream) {
-  const int64_t nblk = p.B * p.H * nchunks;
-  hipLaunchKernelGGL((chunk_prep_kernel<IO, GATE, DK>), dim3(static_cast<unsigned>(nblk)), dim3(256), 0, stream, p,
-                     nchunks);
+  const int64_t ntasks = p.B * p.H * nchunks;
+  if constexpr (GATE == GATE_CHANNEL) {
+    hipLaunchKernelGGL((chunk_prep_lds_kernel<IO, GATE, DK>), dim3(static_cast<unsigned>(ntasks)), dim3(256), 0,
+                       stream, p, nchunks);
+  } else {
+    hipLaunchKernelGGL((chunk_prep_reg_kernel<IO, GATE, DK>), dim3(static_cast<unsigned>((ntasks + 3) / 4)),
+                       dim3(256), 0, stream, p, nchunks, ntasks);
+  }
   return hipGetLastError();
 }
 
