@@ -34,7 +34,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 CHUNK_SOURCES = [os.path.join(ROOT, "gated_delta_rule_21_amd", "csrc", n)
-                 for n in ("chunk_prep.hip", "chunk_fwd.hip", "chunk_common.h", "device_common.h")]
+                 for n in ("chunk_prep.hip", "chunk_state.hip", "chunk_fwd.hip", "chunk_common.h", "device_common.h")]
 DECODE_SOURCES = [os.path.join(ROOT, "gated_delta_rule_21_amd", "csrc", n)
                   for n in ("decode_step.hip", "device_common.h")]
 

@@ -60,18 +60,35 @@ template <> struct Op<IO_F32> {
 constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
 
 // Workspace record of one (sequence, head, chunk), written by the per-chunk
-// transform and read by the state pass: T^T (the transpose of T = (I + A)^{-1})
-// and the masked score matrix P, each [64][64] row-major in the I/O dtype (only
-// the blocks on or above the diagonal of T^T and on or below the diagonal of P
-// are written; the others are never read), then per-row fp32 factors [5][64]
-// (no gate / scalar gate): beta, e^{g_read}, e^{g}, e^{g_63 - g}, e^{g_63}.
+// transform and read by the state pass.  Two 64x64 matrices are kept as their
+// ten 16x16 blocks on one side of the diagonal, block u = R(R+1)/2 + J for
+// J <= R, each block row-major, in the I/O dtype:
+//   T region: block u holds (T_RJ)^T, the transpose of block (R, J) of
+//             T = (I + A)^{-1} (lower triangular);
+//   P region: block u holds P_RJ of the masked score matrix (lower triangular;
+//             written only where the state pass reads it: per-channel gate and
+//             fp32 I/O);
+// then six fp32 rows of 64 per-row factors (no gate / scalar gate): beta,
+// e^{g_read}, e^{g}, e^{g_63 - g}, e^{g_63}, g.
 template <int ESZ>
 struct WsRec {
+  static constexpr int BLK = 256;                        // elements per 16x16 block
   static constexpr uint32_t T_OFF = 0;
-  static constexpr uint32_t P_OFF = CH * CH * ESZ;
-  static constexpr uint32_t F_OFF = 2 * CH * CH * ESZ;
-  static constexpr uint32_t BYTES = F_OFF + 5 * CH * 4;
+  static constexpr uint32_t P_OFF = 10 * BLK * ESZ;
+  static constexpr uint32_t F_OFF = 20 * BLK * ESZ;
+  static constexpr int NF = 6;
+  static constexpr uint32_t BYTES = F_OFF + NF * CH * 4;
+  // byte offset of element (a, b) of block (R, J)
+  static __device__ __forceinline__ uint32_t at(int R, int J, int a, int b) {
+    return static_cast<uint32_t>(((R * (R + 1) / 2 + J) * BLK + a * 16 + b) * ESZ);
+  }
 };
+
+// Block (R, J), J <= R, of the ten-block order above.
+__device__ __forceinline__ void tri_block(int u, int& R, int& J) {
+  R = (u >= 1) + (u >= 3) + (u >= 6);
+  J = u - R * (R + 1) / 2;
+}
 
 __device__ __forceinline__ int strict_pair(int R, int J) { return R * (R - 1) / 2 + J; }
 

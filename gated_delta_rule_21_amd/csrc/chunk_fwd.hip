@@ -73,8 +73,8 @@ struct Layout {
   static constexpr size_t OFF_V = OFF_Q + RM;            // raw v tile
   static constexpr size_t OFF_T = OFF_V + V_B;           // T^T, T = (I + A)^{-1}
   static constexpr size_t OFF_P = OFF_T + MM;            // P
-  static constexpr size_t OFF_F = OFF_P + MM;            // beta, e^{g_read}, e^{g}, e^{g_63 - g}, e^{g_63}
-  static constexpr size_t OFF_X = OFF_F + 5 * CH * 4;    // per-channel regions start here
+  static constexpr size_t OFF_F = OFF_P + MM;            // beta, e^{g_read}, e^{g}, e^{g_63 - g}, e^{g_63}, g
+  static constexpr size_t OFF_X = OFF_F + 6 * CH * 4;    // per-channel regions start here
   // no gate / scalar gate: the regions above, twice when that fits (chunk n is
   // read from one copy while chunk n+1 is written to the other)
   static constexpr int NB = (RAW && 2 * OFF_X <= 163840) ? 2 : 1;
@@ -103,12 +103,14 @@ __global__ __launch_bounds__(NW * 64) void chunk_fwd_kernel(ChunkParams p, int n
   constexpr int ESZ = int(sizeof(elem));
   typedef WsRec<ESZ> W;
   constexpr int EPV = 16 / ESZ;          // elements per 16-byte load
-  constexpr int KROW = DK / EPV, VROW = DVT / EPV, TROW = CH / EPV;
+  constexpr int KROW = DK / EPV, VROW = DVT / EPV;
   constexpr int KV = CH * KROW / NT;     // 16-byte pieces of a k (q) tile per thread
   constexpr int VV = CH * VROW / NT;     // 16-byte pieces of the v tile per thread
-  constexpr int TV = CH * TROW / NT;     // 16-byte pieces of the T tile per thread
-  constexpr int FV = 5 * CH * 4 / 16;    // 16-byte pieces of the factor rows (threads 0..FV-1)
-  static_assert(KV * NT == CH * KROW && VV * NT == CH * VROW && TV * NT == CH * TROW && VV >= 1 && FV <= NT,
+  constexpr int PPB = W::BLK * ESZ / 16; // 16-byte pieces per record block
+  constexpr int PPR = PPB / 16;          // ... per block row
+  constexpr int TV = (10 * PPB + NT - 1) / NT;   // pieces of the T (P) blocks per thread
+  constexpr int FV = W::NF * CH * 4 / 16;        // pieces of the factor rows (threads 0..FV-1)
+  static_assert(KV * NT == CH * KROW && VV * NT == CH * VROW && VV >= 1 && FV <= NT,
                 "tile loads must split evenly");
   static_assert(L::TOTAL <= 163840, "LDS budget");
 
@@ -197,8 +199,11 @@ __global__ __launch_bounds__(NW * 64) void chunk_fwd_kernel(ChunkParams p, int n
     for (int v = 0; v < VV; ++v) pv[v] = buf_load16(rv, offv[v], sv);
 #pragma unroll
     for (int v = 0; v < TV; ++v) {
-      pt[v] = buf_load16(rw, W::T_OFF + static_cast<uint32_t>((tid + v * NT) * 16), sw);
-      pp[v] = buf_load16(rw, W::P_OFF + static_cast<uint32_t>((tid + v * NT) * 16), sw);
+      const int pc = tid + v * NT;
+      if (pc < 10 * PPB) {
+        pt[v] = buf_load16(rw, W::T_OFF + static_cast<uint32_t>(pc * 16), sw);
+        pp[v] = buf_load16(rw, W::P_OFF + static_cast<uint32_t>(pc * 16), sw);
+      }
     }
     if constexpr (RAW) {
       if (tid < FV) pf = buf_load16(rw, W::F_OFF + static_cast<uint32_t>(tid * 16), sw);
@@ -235,9 +240,14 @@ __global__ __launch_bounds__(NW * 64) void chunk_fwd_kernel(ChunkParams p, int n
     }
 #pragma unroll
     for (int v = 0; v < TV; ++v) {
-      const int seg = tid + v * NT, row = seg / TROW, c = (seg % TROW) * EPV;
-      *reinterpret_cast<u32x4*>(dT + row * LCH + c) = pt[v];
-      *reinterpret_cast<u32x4*>(dP + row * LCH + c) = pp[v];
+      const int pc = tid + v * NT;
+      if (pc < 10 * PPB) {                 // block u holds (T_RJ)^T and P_RJ: T^T and P tiles
+        int R, J;
+        tri_block(pc / PPB, R, J);
+        const int a = (pc % PPB) / PPR, b0 = (pc % PPR) * EPV;
+        *reinterpret_cast<u32x4*>(dT + (16 * J + a) * LCH + 16 * R + b0) = pt[v];
+        *reinterpret_cast<u32x4*>(dP + (16 * R + a) * LCH + 16 * J + b0) = pp[v];
+      }
     }
     if constexpr (RAW) {
       if (tid < FV) *reinterpret_cast<u32x4*>(dF + 4 * tid) = pf;
@@ -470,10 +480,14 @@ static hipError_t launch_chunk_g(const ChunkParams& p, hipStream_t stream) {
 
 template <int IO>
 static hipError_t launch_chunk_io(const ChunkParams& p, hipStream_t stream) {
-  switch (p.gate) {
-    case GATE_NONE: return launch_chunk_g<IO, GATE_NONE>(p, stream);
-    case GATE_SCALAR: return launch_chunk_g<IO, GATE_SCALAR>(p, stream);
-    case GATE_CHANNEL: return launch_chunk_g<IO, GATE_CHANNEL>(p, stream);
+  if constexpr (IO == IO_F32) {
+    switch (p.gate) {
+      case GATE_NONE: return launch_chunk_g<IO, GATE_NONE>(p, stream);
+      case GATE_SCALAR: return launch_chunk_g<IO, GATE_SCALAR>(p, stream);
+      case GATE_CHANNEL: return launch_chunk_g<IO, GATE_CHANNEL>(p, stream);
+    }
+  } else {
+    if (p.gate == GATE_CHANNEL) return launch_chunk_g<IO, GATE_CHANNEL>(p, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -482,6 +496,8 @@ hipError_t launch_chunk_fwd(const ChunkParams& p, hipStream_t stream) {
   if (p.B * p.H == 0) return hipSuccess;
   hipError_t e = launch_chunk_prep(p, stream);
   if (e != hipSuccess) return e;
+  // bf16 without a per-channel gate: chain and helper waves (chunk_state.hip)
+  if (p.io == IO_BF16 && p.gate != GATE_CHANNEL) return launch_chunk_state_pipe(p, stream);
   return p.io == IO_BF16 ? launch_chunk_io<IO_BF16>(p, stream) : launch_chunk_io<IO_F32>(p, stream);
 }
 

@@ -13,10 +13,14 @@
 //     P = lower_incl( (Q * e^{g}) (K * e^{-g})^T ),
 // where g_read = g when the decay precedes the erase and g_{r-1} when the erase
 // reads the undecayed state; without a per-channel gate also the per-row
-// factors beta, e^{g_read}, e^{g}, e^{g_63 - g}, e^{g_63} in fp32.
+// factors beta, e^{g_read}, e^{g}, e^{g_63 - g}, e^{g_63}, g in fp32.
 //
-// Written per chunk (the workspace record): T^T and P row-major, so that the
-// state pass reads T's rows with the LDS transpose load and P's rows directly.
+// Written per chunk (the workspace record): the ten non-zero 16x16 blocks of T,
+// each transposed, so that the state pass reads T's rows with the LDS
+// transpose load, and (per-channel gate, fp32 I/O) the ten blocks of P.  With
+// bf16 I/O and no per-channel gate the state pass forms P itself from the q and
+// k tiles it holds anyway, which saves reading q here and a round trip of P
+// through memory.
 //
 // No gate / scalar gate (chunk_prep_reg_kernel): one wave per chunk, every
 // operand in registers.  The Gram sums run over d_k, so k and q are loaded as
@@ -29,9 +33,10 @@
 // registers (both orientations again); then row block R of T follows by
 // forward substitution,
 //     T_RR = D_R,   T_RJ = -D_R sum_{J <= m < R} A_Rm T_mJ,
-// with T blocks kept as B operands.  P blocks are formed transposed too, which
-// is the layout of P's rows.  Everything is stored 8 bytes per lane from the
-// accumulators; no LDS is used beyond 768 bytes of per-row factors.
+// with T blocks kept as B operands.  P blocks (fp32 I/O) are formed transposed
+// too, which is the layout of P's rows.  Everything is stored from the
+// accumulators, four elements per lane, one whole 16x16 block per instruction;
+// no LDS is used beyond 768 bytes of per-row factors.
 //
 // Per-channel gate (chunk_prep_lds_kernel): the decay sits inside the d_k
 // contraction, so decayed operands are built in LDS by a four-wave workgroup
@@ -92,9 +97,7 @@ __global__ __launch_bounds__(256) void chunk_prep_lds_kernel(ChunkParams p, int6
   constexpr int EPV = 16 / ESZ;                 // elements per 16-byte piece
   constexpr int KROW = DK / EPV;
   constexpr int KV = CH * KROW / NT;            // 16-byte pieces of the k (q) tile per thread
-  constexpr int TROW = CH / EPV;
-  constexpr int TV = CH * TROW / NT;            // 16-byte pieces of a 64x64 tile per thread
-  static_assert(KV * NT == CH * KROW && TV * NT == CH * TROW, "tile pieces must split evenly");
+  static_assert(KV * NT == CH * KROW, "tile pieces must split evenly");
   static_assert(L::TOTAL <= 163840, "LDS budget");
 
   __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
@@ -328,14 +331,17 @@ __global__ __launch_bounds__(256) void chunk_prep_lds_kernel(ChunkParams p, int6
   }
   __syncthreads();
 
-  // ---- T^T and P to the workspace record, row-major [64][64] ----------------------------
-  elem* dT = reinterpret_cast<elem*>(rec + W::T_OFF);
-  elem* dP = reinterpret_cast<elem*>(rec + W::P_OFF);
-#pragma unroll
-  for (int v = 0; v < TV; ++v) {
-    const int seg = tid + v * NT, row = seg / TROW, c = (seg % TROW) * EPV;
-    *reinterpret_cast<u32x4*>(dT + row * CH + c) = *reinterpret_cast<const u32x4*>(sT + row * LCH + c);
-    *reinterpret_cast<u32x4*>(dP + row * CH + c) = *reinterpret_cast<const u32x4*>(sP + row * LCH + c);
+  // ---- the ten blocks of T (transposed) and of P to the workspace record -----------------
+  constexpr int PPB = W::BLK * ESZ / 16;         // 16-byte pieces per block
+  constexpr int PPR = PPB / 16;                  // pieces per block row
+  for (int pc = tid; pc < 10 * PPB; pc += NT) {
+    int R, J;
+    tri_block(pc / PPB, R, J);
+    const int a = (pc % PPB) / PPR, b0 = (pc % PPR) * EPV;
+    *reinterpret_cast<u32x4*>(rec + W::T_OFF + pc * 16) =
+        *reinterpret_cast<const u32x4*>(sT + (16 * J + a) * LCH + 16 * R + b0);
+    *reinterpret_cast<u32x4*>(rec + W::P_OFF + pc * 16) =
+        *reinterpret_cast<const u32x4*>(sP + (16 * R + a) * LCH + 16 * J + b0);
   }
 }
 
@@ -423,6 +429,7 @@ __global__ __launch_bounds__(256) void chunk_prep_reg_kernel(ChunkParams p, int6
     f[2 * CH + lane] = __expf(g);
     f[3 * CH + lane] = __expf(gC - g);
     f[4 * CH + lane] = __expf(gC);
+    f[5 * CH + lane] = g;
   }
   wave_sync();
 
@@ -439,9 +446,9 @@ __global__ __launch_bounds__(256) void chunk_prep_reg_kernel(ChunkParams p, int6
     }
     return acc;
   };
-  // four consecutive elements of a row of a [64][64] record matrix
-  auto store4 = [&](uint32_t base, int row, int col, f32x4 x) {
-    char* d = rec + base + static_cast<uint32_t>((row * CH + col) * ESZ);
+  // four consecutive elements of a row of a record block
+  auto store4 = [&](uint32_t off, f32x4 x) {
+    char* d = rec + off;
     if constexpr (IO == IO_BF16) *reinterpret_cast<u32x2*>(d) = __builtin_bit_cast(u32x2, to_bf16x4(x));
     else *reinterpret_cast<u32x4*>(d) = __builtin_bit_cast(u32x4, x);
   };
@@ -459,12 +466,15 @@ __global__ __launch_bounds__(256) void chunk_prep_reg_kernel(ChunkParams p, int6
     return acc;
   };
 
+  constexpr bool WITH_P = IO == IO_F32;           // bf16: the state pass forms P itself
   frag Tb[4][4];                                  // Tb[R][J] = T_RJ as a B operand (J <= R)
 #pragma unroll
   for (int R = 0; R < 4; ++R) {
     u32x4 qf[NSTEP];
+    if constexpr (WITH_P) {
 #pragma unroll
-    for (int i = 0; i < NSTEP; ++i) qf[i] = buf_load16(rq, piece_off(R, i), 0);
+      for (int i = 0; i < NSTEP; ++i) qf[i] = buf_load16(rq, piece_off(R, i), 0);
+    }
 
     // A_Rm (m < R) as A operands: transposed Gram blocks
     frag aRow[3];
@@ -488,7 +498,7 @@ __global__ __launch_bounds__(256) void chunk_prep_reg_kernel(ChunkParams p, int6
     f32x4 D, Dt;
     unit_lower_inverse_pair<O>(N, Nt, D, Dt, lr, lg);
     Tb[R][R] = O::cvt(D);
-    store4(W::T_OFF, 16 * R + lr, 16 * R + 4 * lg, D);     // T^T block (R, R)
+    store4(W::T_OFF + W::at(R, R, lr, 4 * lg), D);         // (T_RR)^T
     const frag dA = O::cvt(Dt);                             // D_R as an A operand
 #pragma unroll
     for (int J = 0; J < R; ++J) {
@@ -499,10 +509,11 @@ __global__ __launch_bounds__(256) void chunk_prep_reg_kernel(ChunkParams p, int6
       t = O::mma1(t, dA, O::cvt(y));
       t = -t;
       Tb[R][J] = O::cvt(t);
-      store4(W::T_OFF, 16 * J + lr, 16 * R + 4 * lg, t);   // T^T block (J, R)
+      store4(W::T_OFF + W::at(R, J, lr, 4 * lg), t);       // (T_RJ)^T
     }
 
     // P row block R: transposed products give P's rows; factor e^{g_r - g_j}, mask r >= j
+    if constexpr (!WITH_P) continue;
     const float gr = sG[16 * R + lr];
 #pragma unroll
     for (int J = 0; J <= R; ++J) {
@@ -514,7 +525,7 @@ __global__ __launch_bounds__(256) void chunk_prep_reg_kernel(ChunkParams p, int6
         if constexpr (GATE == GATE_SCALAR) v *= __expf(gr - gj[s]);
         acc[s] = (J == R && lr < 4 * lg + s) ? 0.f : v;
       }
-      store4(W::P_OFF, 16 * R + lr, 16 * J + 4 * lg, acc);
+      store4(W::P_OFF + W::at(R, J, lr, 4 * lg), acc);
     }
   }
 }

@@ -1,0 +1,367 @@
+// State pass of the chunkwise gated delta rule on gfx950 for bf16 I/O without a
+// per-channel gate: chain waves and helper waves working side by side.
+//
+// "Moonshot AI's New Attention Architecture: Key Innovations Explained", §3
+// Hardware-Friendly Algorithm: between chunks only the d_k x d_v state is
+// passed on, and within a chunk the rest is dense lower-triangular products.
+// Per chunk (rows r = 0..63, g_r = inclusive running sum of log a over the
+// chunk, S the state entering it, T = (I + A)^{-1} from the per-chunk
+// transform; scalar gate, so the decay factors are per row):
+//   Delta = T diag(beta) (V - diag(e^{g_read}) K S)
+//   O     = diag(e^{g}) Q S + P Delta,   P = lower_incl( e^{g_r - g_j} q_r . k_j )
+//   S'    = e^{g_63} S + K^T diag(e^{g_63 - g}) Delta
+//
+// Only K S -> Delta -> S' lies on the sequential chain from chunk to chunk.
+// One workgroup owns one (batch, head, d_v tile of 16*NWC columns) and runs
+// 2*NWC waves, two per SIMD:
+//   chain wave c  (c < NWC) keeps columns 16c..16c+15 of S in MFMA accumulators
+//                 and forms K S, Q S, the residual, Delta and the state update;
+//   helper wave c (NWC + c) moves the next chunk into LDS and the one after
+//                 into registers, forms a share of P, and after the chain wave
+//                 has Delta finishes column group c of the output
+//                 (Q S from the chain wave, plus P Delta).
+// Per chunk n:  [barrier]  chain: Q S, K S, residual, Delta -> LDS exchange
+//                          helper: tiles of chunk n+1 -> LDS, loads of n+2, P
+//               [barrier]  chain: S update;  helper: P Delta, output stores.
+// The tiles (k, q, v, T, per-row factors) are double-buffered in LDS: chunk n
+// is read from one copy while chunk n+1 is written to the other.
+//
+// Operand layouts as elsewhere in this library: an accumulator tile (lane l:
+// column l%16, rows 4(l/16)+s) is the B operand of the next product and, as the
+// A operand, stands for its transpose; rows of T are read from T^T with the
+// LDS transpose load; the output is formed transposed so each lane stores four
+// adjacent columns.
+#include "chunk_common.h"
+#include "launchers.h"
+
+namespace gdr {
+
+// LDS row strides (bf16 elements), measured on gfx950 at 8 waves per CU: reads
+// of 8-byte row fragments (lane l: row l%16) run fastest when a row is 2 (mod 32)
+// dwords long, transpose reads (ds_read_b64_tr_b16) when it is 8 (mod 32)
+// dwords long; the k tile is read both ways and takes 4 (mod 32), good for both.
+template <int DK, int NWC>
+struct PipeLayout {
+  static constexpr int LDK = DK + 8;                     // k: row and transpose reads
+  static constexpr int LDQ = DK + 4;                     // q: row reads (8-byte aligned rows)
+  static constexpr int DVT = 16 * NWC;
+  static constexpr int LVT = DVT + 16;                   // v: transpose reads
+  static constexpr int LCT = CH + 16;                    // T^T: transpose reads
+  static constexpr int LCP = CH + 4;                     // P: row reads
+  static constexpr size_t KB = size_t(CH) * LDK * 2;
+  static constexpr size_t QB = size_t(CH) * LDQ * 2;
+  static constexpr size_t VB = size_t(CH) * LVT * 2;
+  static constexpr size_t TB = size_t(CH) * LCT * 2;
+  // one copy of a chunk's tiles
+  static constexpr size_t B_K = 0;
+  static constexpr size_t B_Q = B_K + KB;
+  static constexpr size_t B_V = B_Q + QB;
+  static constexpr size_t B_T = B_V + VB;                // T^T (the ten blocks on or above the diagonal)
+  static constexpr size_t B_F = B_T + TB;                // beta, e^{g_read}, e^{g}, e^{g_63 - g}, e^{g_63}, g
+  static constexpr size_t BUF = B_F + 6 * CH * 4;
+  // single copies
+  static constexpr size_t OFF_P = 2 * BUF;               // P (helpers only)
+  static constexpr size_t OFF_XO = OFF_P + size_t(CH) * LCP * 2;   // Q S per chain wave, accumulator tiles
+  static constexpr size_t OFF_XD = OFF_XO + size_t(NWC) * 4 * 64 * 16;   // Delta per chain wave, bf16
+  static constexpr size_t TOTAL = OFF_XD + size_t(NWC) * 4 * 64 * 8;
+};
+
+template <int GATE, int DK, int NWC>
+__global__ __launch_bounds__(NWC * 128) void chunk_state_pipe_kernel(ChunkParams p, int n_tiles) {
+  typedef Op<IO_BF16> O;
+  typedef __bf16 T;
+  typedef bf16x4 frag;
+  typedef uint16_t elem;
+  typedef PipeLayout<DK, NWC> L;
+  typedef WsRec<2> W;
+  constexpr int ESZ = 2, EPV = 8;
+  constexpr int NH = NWC * 64;                   // helper threads
+  constexpr int DVT = 16 * NWC;
+  constexpr int DKT = DK / 16;
+  constexpr int LDK = L::LDK, LDQ = L::LDQ, LVT = L::LVT, LCT = L::LCT, LCP = L::LCP;
+  constexpr int KROW = DK / EPV, VROW = DVT / EPV;
+  constexpr int HK = CH * KROW / NH;             // 16-byte pieces of the k (q) tile per helper thread
+  constexpr int HV = CH * VROW / NH;             // ... of the v tile
+  constexpr int PPB = W::BLK * ESZ / 16, PPR = PPB / 16;
+  constexpr int HT = (10 * PPB + NH - 1) / NH;   // ... of the T blocks
+  constexpr int NFP = W::NF * CH * 4 / 16;       // pieces of the factor rows (helper threads 0..NFP-1)
+  static_assert(HK * NH == CH * KROW && HV * NH == CH * VROW && HV >= 1 && NFP <= NH, "tile split");
+  static_assert(GATE != GATE_CHANNEL, "per-channel gate uses chunk_fwd_kernel");
+  static_assert(L::TOTAL <= 163840, "LDS budget");
+
+  __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
+  T* sP = reinterpret_cast<T*>(smem + L::OFF_P);
+  f32x4* xO = reinterpret_cast<f32x4*>(smem + L::OFF_XO);
+  frag* xD = reinterpret_cast<frag*>(smem + L::OFF_XD);
+
+  // Block -> (head, d_v tile); consecutive logical blocks on one XCD (block ids
+  // are dealt round-robin over 8 XCDs), so a head's tiles share that L2.
+  const int nblk = gridDim.x;
+  int lb = blockIdx.x;
+  if ((nblk & 7) == 0) lb = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
+  const int64_t bh = lb / n_tiles;
+  const int tile = lb % n_tiles;
+  const int64_t bb = bh / p.H, hh = bh % p.H;
+  const int dv = p.d_v;
+  const int col0 = tile * DVT;
+  const int H = static_cast<int>(p.H);
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform across the wave
+  const bool chain = wave < NWC;
+  const int cw = chain ? wave : wave - NWC;                      // column group
+  const int lane = tid & 63;
+  const int lr = lane & 15;
+  const int lg = lane >> 4;
+  const int ht = tid - NH;                                       // helper thread index
+
+  const int64_t nchunks = (p.T + CH - 1) / CH;
+  const int64_t row0 = bb * p.T * p.H + hh;
+  const uint32_t span = static_cast<uint32_t>(p.T > 0 ? (p.T - 1) * p.H + 1 : 0);
+  const rsrc_t rk = make_rsrc(static_cast<const elem*>(p.k) + row0 * DK, span * DK * ESZ);
+  const rsrc_t rq = make_rsrc(static_cast<const elem*>(p.q) + row0 * DK, span * DK * ESZ);
+  const rsrc_t rv = make_rsrc(static_cast<const elem*>(p.v) + row0 * dv, span * dv * ESZ);
+  const rsrc_t ro = make_rsrc(static_cast<const elem*>(p.o) + row0 * dv, span * dv * ESZ);
+  const rsrc_t rw = make_rsrc(static_cast<const char*>(p.ws) + bh * nchunks * W::BYTES,
+                              static_cast<uint32_t>(nchunks * W::BYTES));
+
+  // ---- helpers: loads one chunk ahead in registers, stores into an LDS copy ----------
+  u32x4 pk[HK], pq[HK], pv[HV], pt[HT], pf;
+  auto prefetch = [&](int64_t m) __attribute__((always_inline)) {
+    const uint32_t sk = static_cast<uint32_t>(m * CH * H * DK * ESZ);
+    const uint32_t sv = static_cast<uint32_t>(m * CH * H * dv * ESZ);
+    const uint32_t sw = static_cast<uint32_t>(m * W::BYTES);
+#pragma unroll
+    for (int v = 0; v < HK; ++v) {
+      const int seg = ht + v * NH;
+      const uint32_t off = static_cast<uint32_t>(((seg / KROW) * H * DK + (seg % KROW) * EPV) * ESZ);
+      pk[v] = buf_load16(rk, off, sk);
+      pq[v] = buf_load16(rq, off, sk);
+    }
+#pragma unroll
+    for (int v = 0; v < HV; ++v) {
+      const int seg = ht + v * NH;
+      pv[v] = buf_load16(rv, static_cast<uint32_t>(((seg / VROW) * H * dv + col0 + (seg % VROW) * EPV) * ESZ), sv);
+    }
+#pragma unroll
+    for (int v = 0; v < HT; ++v) {
+      const int pc = ht + v * NH;
+      if (pc < 10 * PPB) pt[v] = buf_load16(rw, W::T_OFF + static_cast<uint32_t>(pc * 16), sw);
+    }
+    if (ht < NFP) pf = buf_load16(rw, W::F_OFF + static_cast<uint32_t>(ht * 16), sw);
+  };
+  auto store_chunk = [&](char* base) __attribute__((always_inline)) {
+    T* dK = reinterpret_cast<T*>(base + L::B_K);
+    T* dQ = reinterpret_cast<T*>(base + L::B_Q);
+    T* dV = reinterpret_cast<T*>(base + L::B_V);
+    T* dT = reinterpret_cast<T*>(base + L::B_T);
+#pragma unroll
+    for (int v = 0; v < HK; ++v) {
+      const int seg = ht + v * NH, row = seg / KROW, c = (seg % KROW) * EPV;
+      *reinterpret_cast<u32x4*>(dK + row * LDK + c) = pk[v];
+      u32x2* q2 = reinterpret_cast<u32x2*>(dQ + row * LDQ + c);     // q rows are 8-byte aligned
+      q2[0] = u32x2{pq[v][0], pq[v][1]};
+      q2[1] = u32x2{pq[v][2], pq[v][3]};
+    }
+#pragma unroll
+    for (int v = 0; v < HV; ++v) {
+      const int seg = ht + v * NH, row = seg / VROW, c = (seg % VROW) * EPV;
+      *reinterpret_cast<u32x4*>(dV + row * LVT + c) = pv[v];
+    }
+#pragma unroll
+    for (int v = 0; v < HT; ++v) {
+      const int pc = ht + v * NH;
+      if (pc < 10 * PPB) {               // block u holds (T_RJ)^T: rows 16J.., columns 16R.. of T^T
+        int R, J;
+        tri_block(pc / PPB, R, J);
+        const int a = (pc % PPB) / PPR, b0 = (pc % PPR) * EPV;
+        *reinterpret_cast<u32x4*>(dT + (16 * J + a) * LCT + 16 * R + b0) = pt[v];
+      }
+    }
+    if (ht < NFP) *reinterpret_cast<u32x4*>(base + L::B_F + ht * 16) = pf;
+  };
+
+  // A chunk's LDS copy.
+  struct Tiles {
+    const T *K, *Q, *V, *Tt;
+    const float *beta, *er, *eo, *ed, *gam, *g;   // per-row factors
+  };
+  auto tiles = [&](int64_t n) __attribute__((always_inline)) {
+    const char* cur = smem + (n & 1) * L::BUF;
+    const float* f = reinterpret_cast<const float*>(cur + L::B_F);
+    return Tiles{reinterpret_cast<const T*>(cur + L::B_K), reinterpret_cast<const T*>(cur + L::B_Q),
+                 reinterpret_cast<const T*>(cur + L::B_V), reinterpret_cast<const T*>(cur + L::B_T),
+                 f, f + CH, f + 2 * CH, f + 3 * CH, f + 4 * CH, f + 5 * CH};
+  };
+
+  // The two roles run separate loops with the same two barriers per chunk (the
+  // role is uniform per wave), so neither keeps the other's registers live.
+  if (chain) {
+    // ---- chain waves: this column group's slice of S in accumulators ------------------
+    const int scol = col0 + 16 * cw + lr;
+    f32x4 S[DKT];
+#pragma unroll
+    for (int t = 0; t < DKT; ++t)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) S[t][s] = p.S0 ? p.S0[(bh * DK + 16 * t + 4 * lg + s) * dv + scol] : 0.f;
+    __syncthreads();                            // chunk 0 in LDS
+
+    for (int64_t n = 0; n < nchunks; ++n) {
+      const Tiles c = tiles(n);
+      // Q S (output partials), K S, residual
+      frag Sb[DKT], Rb[4], Ds[4];
+#pragma unroll
+      for (int t = 0; t < DKT; ++t) Sb[t] = O::cvt(S[t]);
+#pragma unroll
+      for (int R = 0; R < 4; ++R) {
+        f32x4 x = {0.f, 0.f, 0.f, 0.f}, oq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < DK / 32; ++kb) {
+          const T* kr = c.K + (16 * R + lr) * LDK + 32 * kb + 4 * lg;
+          const T* qr = c.Q + (16 * R + lr) * LDQ + 32 * kb + 4 * lg;
+          x = O::mma2(x, O::ld(kr), O::ld(kr + 16), Sb[2 * kb], Sb[2 * kb + 1]);
+          oq = O::mma2(oq, Sb[2 * kb], Sb[2 * kb + 1], O::ld(qr), O::ld(qr + 16));
+        }
+        xO[(cw * 4 + R) * 64 + lane] = oq;
+        const f32x4 vv = O::f32(O::ld_tr(c.V, LVT, 16 * R, 16 * cw, lr, lg));
+        const f32x4 be = *reinterpret_cast<const f32x4*>(c.beta + 16 * R + 4 * lg);
+        const f32x4 er = *reinterpret_cast<const f32x4*>(c.er + 16 * R + 4 * lg);
+        f32x4 rr;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) rr[s] = be[s] * (vv[s] - (GATE == GATE_SCALAR ? x[s] * er[s] : x[s]));
+        Rb[R] = O::cvt(rr);
+      }
+      // Delta_R = sum_{m <= R} T_Rm R_m; rows of T from T^T
+#pragma unroll
+      for (int R = 0; R < 4; ++R) {
+        f32x4 d = {0.f, 0.f, 0.f, 0.f};
+        int m = 0;
+#pragma unroll
+        for (; m + 1 <= R; m += 2)
+          d = O::mma2(d, O::ld_tr(c.Tt, LCT, 16 * m, 16 * R, lr, lg), O::ld_tr(c.Tt, LCT, 16 * (m + 1), 16 * R, lr, lg),
+                      Rb[m], Rb[m + 1]);
+        if (m <= R) d = O::mma1(d, O::ld_tr(c.Tt, LCT, 16 * m, 16 * R, lr, lg), Rb[m]);
+        xD[(cw * 4 + R) * 64 + lane] = O::cvt(d);
+        if constexpr (GATE == GATE_SCALAR) {
+          const f32x4 ed = *reinterpret_cast<const f32x4*>(c.ed + 16 * R + 4 * lg);
+          Ds[R] = O::cvt(d * ed);
+        } else {
+          Ds[R] = O::cvt(d);
+        }
+      }
+      __syncthreads();                          // Delta, Q S and P complete
+      // S' = e^{g_63} S + K^T diag(e^{g_63 - g}) Delta
+      const float gam = GATE == GATE_SCALAR ? c.gam[0] : 1.f;
+#pragma unroll
+      for (int t = 0; t < DKT; ++t) {
+        f32x4 acc = S[t];
+        if constexpr (GATE == GATE_SCALAR) acc = acc * gam;
+        acc = O::mma2(acc, O::ld_tr(c.K, LDK, 0, 16 * t, lr, lg), O::ld_tr(c.K, LDK, 16, 16 * t, lr, lg), Ds[0], Ds[1]);
+        acc = O::mma2(acc, O::ld_tr(c.K, LDK, 32, 16 * t, lr, lg), O::ld_tr(c.K, LDK, 48, 16 * t, lr, lg), Ds[2], Ds[3]);
+        S[t] = acc;
+      }
+      __syncthreads();                          // next chunk's tiles in place; exchange free
+    }
+    if (p.S_T) {
+#pragma unroll
+      for (int t = 0; t < DKT; ++t)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) p.S_T[(bh * DK + 16 * t + 4 * lg + s) * dv + scol] = S[t][s];
+    }
+  } else {
+    // ---- helper waves -------------------------------------------------------------------
+    if (nchunks > 0) {
+      prefetch(0);
+      store_chunk(smem);
+      if (nchunks > 1) prefetch(1);
+    }
+    __syncthreads();                            // chunk 0 in LDS
+
+    for (int64_t n = 0; n < nchunks; ++n) {
+      const Tiles c = tiles(n);
+      // next chunk into the other LDS copy (last read before the previous chunk's
+      // closing barrier), loads of the one after, then a share of P
+      if (n + 1 < nchunks) {
+        store_chunk(smem + ((n + 1) & 1) * L::BUF);
+        if (n + 2 < nchunks) prefetch(n + 2);
+      }
+      const int lo = 10 * cw / NWC, hi = 10 * (cw + 1) / NWC;
+      for (int u = lo; u < hi; ++u) {
+        int R, J;
+        tri_block(u, R, J);
+        // (P_RJ)^T = K_J Q_R^T: lane holds P[16R + lr][16J + 4lg + s], four adjacent columns
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < DK / 32; ++kb) {
+          const int k0 = 32 * kb + 4 * lg;
+          acc = O::mma2(acc, O::ld(c.K + (16 * J + lr) * LDK + k0), O::ld(c.K + (16 * J + lr) * LDK + k0 + 16),
+                        O::ld(c.Q + (16 * R + lr) * LDQ + k0), O::ld(c.Q + (16 * R + lr) * LDQ + k0 + 16));
+        }
+        const int r = 16 * R + lr;
+        const float gr = c.g[r];
+        const f32x4 gj = *reinterpret_cast<const f32x4*>(c.g + 16 * J + 4 * lg);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          float val = acc[s];
+          if constexpr (GATE == GATE_SCALAR) val *= __expf(gr - gj[s]);
+          acc[s] = (R == J && lr < 4 * lg + s) ? 0.f : val;
+        }
+        *reinterpret_cast<frag*>(sP + r * LCP + 16 * J + 4 * lg) = O::cvt(acc);
+      }
+      __syncthreads();                          // Delta, Q S and P complete
+      // O^T tile of column group cw: (Q S)^T e^{g} + Delta^T P^T; 4 adjacent columns per
+      // lane; rows past the end of the sequence fall outside the buffer
+      frag Db[4];
+#pragma unroll
+      for (int R = 0; R < 4; ++R) Db[R] = xD[(cw * 4 + R) * 64 + lane];
+      const uint32_t so = static_cast<uint32_t>(n * CH * H * dv * ESZ);
+#pragma unroll
+      for (int R = 0; R < 4; ++R) {
+        f32x4 op = {0.f, 0.f, 0.f, 0.f};
+        const T* pr = sP + (16 * R + lr) * LCP + 4 * lg;
+        int J = 0;
+#pragma unroll
+        for (; J + 1 <= R; J += 2) op = O::mma2(op, Db[J], Db[J + 1], O::ld(pr + 16 * J), O::ld(pr + 16 * (J + 1)));
+        if (J <= R) op = O::mma1(op, Db[J], O::ld(pr + 16 * J));
+        const f32x4 oq = xO[(cw * 4 + R) * 64 + lane];
+        const int r = 16 * R + lr;
+        const f32x4 ov = GATE == GATE_SCALAR ? oq * c.eo[r] + op : oq + op;
+        const uint32_t voff = static_cast<uint32_t>((r * H * dv + col0 + 16 * cw + 4 * lg) * ESZ);
+        buf_store8(__builtin_bit_cast(u32x2, to_bf16x4(ov)), ro, voff, so);
+      }
+      __syncthreads();                          // next chunk's tiles in place; exchange free
+    }
+  }
+}
+
+template <int GATE, int DK, int NWC>
+static hipError_t launch_pipe_t(const ChunkParams& p, hipStream_t stream) {
+  const int n_tiles = p.d_v / (16 * NWC);
+  const int64_t nblk = p.B * p.H * n_tiles;
+  hipLaunchKernelGGL((chunk_state_pipe_kernel<GATE, DK, NWC>), dim3(static_cast<unsigned>(nblk)), dim3(NWC * 128),
+                     0, stream, p, n_tiles);
+  return hipGetLastError();
+}
+
+template <int GATE, int DK>
+static hipError_t launch_pipe_dk(const ChunkParams& p, hipStream_t stream) {
+  // 64 columns per workgroup when that still gives one workgroup per CU, else 32
+  if (p.B * p.H * (p.d_v / 64) >= 256) return launch_pipe_t<GATE, DK, 4>(p, stream);
+  return launch_pipe_t<GATE, DK, 2>(p, stream);
+}
+
+template <int GATE>
+static hipError_t launch_pipe_g(const ChunkParams& p, hipStream_t stream) {
+  if (p.d_k == 128) return launch_pipe_dk<GATE, 128>(p, stream);
+  if (p.d_k == 64) return launch_pipe_dk<GATE, 64>(p, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_chunk_state_pipe(const ChunkParams& p, hipStream_t stream) {
+  if (p.io != IO_BF16) return hipErrorInvalidValue;
+  if (p.gate == GATE_NONE) return launch_pipe_g<GATE_NONE>(p, stream);
+  if (p.gate == GATE_SCALAR) return launch_pipe_g<GATE_SCALAR>(p, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gdr

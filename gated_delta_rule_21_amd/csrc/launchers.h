@@ -38,6 +38,7 @@ struct ChunkParams {
 hipError_t launch_decode_step(const DecodeParams& p, hipStream_t stream);
 // Per-chunk transform (T tiles into p.ws), then the state pass; one stream, in order.
 hipError_t launch_chunk_prep(const ChunkParams& p, hipStream_t stream);
+hipError_t launch_chunk_state_pipe(const ChunkParams& p, hipStream_t stream);   // bf16, no per-channel gate
 hipError_t launch_chunk_fwd(const ChunkParams& p, hipStream_t stream);
 size_t chunk_workspace_bytes(int64_t B, int64_t T, int64_t H, int io);
 

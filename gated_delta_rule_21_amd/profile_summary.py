@@ -34,7 +34,7 @@ def short_name(name: str) -> str:
 def kernel_source_digest() -> str:
     """sha256 (first 16 hex digits) of the chunk-forward sources, as bench.py computes it."""
     h = hashlib.sha256()
-    for n in ("chunk_prep.hip", "chunk_fwd.hip", "chunk_common.h", "device_common.h"):
+    for n in ("chunk_prep.hip", "chunk_state.hip", "chunk_fwd.hip", "chunk_common.h", "device_common.h"):
         with open(os.path.join(ROOT, "gated_delta_rule_21_amd", "csrc", n), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

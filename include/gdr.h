@@ -91,11 +91,12 @@ typedef struct {
  * Per (sequence, head, chunk) it holds what the chunk contributes independently
  * of the state ("Moonshot AI's New Attention Architecture", §3): the inverse
  * (I + A)^{-1} of the chunk's unit lower triangular system (its WY correction
- * terms are that solve applied to the keys and values) and the causally masked
- * query-key score matrix, both 64 x 64 in the I/O dtype, plus five rows of 64
- * fp32 per-token gate factors.  That is B * H * ceil(T / 64) * (8192 * elem +
- * 1280) bytes (0 when T == 0).  Returns the same errors as gdr_chunk_fwd's
- * descriptor checks; *bytes is 0 on error.
+ * terms are that solve applied to the keys and values) and room for the
+ * causally masked query-key score matrix, each as the ten 16 x 16 blocks of a
+ * 64 x 64 triangle in the I/O dtype, plus six rows of 64 fp32 per-token gate
+ * factors.  That is B * H * ceil(T / 64) * (5120 * elem + 1536) bytes (0 when
+ * T == 0).  Returns the same errors as gdr_chunk_fwd's descriptor checks;
+ * *bytes is 0 on error.
  */
 gdr_status gdr_chunk_fwd_workspace_size(const gdr_desc* desc, size_t* bytes);
 

@@ -72,7 +72,7 @@ def _chunk(lib, d, ptrs, ws_bytes=None):
 
 
 def test_workspace_size(lib):
-    rec = lambda esz: 2 * 64 * 64 * esz + 5 * 64 * 4     # T, P, five rows of fp32 factors
+    rec = lambda esz: 2 * 10 * 256 * esz + 6 * 64 * 4    # ten 16x16 blocks of T and of P, six factor rows
     assert _ws_size(lib, _desc(B=2, T=130, H=3)) == (OK, 2 * 3 * 3 * rec(2))        # bf16, 3 chunks
     assert _ws_size(lib, _desc(io=0, d_k=64, T=64)) == (OK, 2 * 1 * rec(4))         # fp32, 1 chunk
     assert _ws_size(lib, _desc(T=0)) == (OK, 0)
