@@ -37,12 +37,13 @@
 namespace gdr {
 
 // LDS row strides (bf16 elements), measured on gfx950 at 8 waves per CU: reads
-// of 8-byte row fragments (lane l: row l%16) run fastest when a row is 2 (mod 32)
-// dwords long, transpose reads (ds_read_b64_tr_b16) when it is 8 (mod 32)
-// dwords long; the k tile is read both ways and takes 4 (mod 32), good for both.
+// of 8-byte row fragments (lane l: row l%16) run fastest (~121 B/clk) when a row
+// is 2 or 6 (mod 8) dwords long, transpose reads (ds_read_b64_tr_b16) at 168 B/clk
+// when it is 8 (mod 32) dwords and at 128 B/clk for most other lengths; the k
+// tile is read both ways and takes 6 (mod 32) dwords (121 and 128 B/clk).
 template <int DK, int NWC>
 struct PipeLayout {
-  static constexpr int LDK = DK + 8;                     // k: row and transpose reads
+  static constexpr int LDK = DK + 12;                    // k: row and transpose reads (8-byte aligned rows)
   static constexpr int LDQ = DK + 4;                     // q: row reads (8-byte aligned rows)
   static constexpr int DVT = 16 * NWC;
   static constexpr int LVT = DVT + 16;                   // v: transpose reads
@@ -158,8 +159,10 @@ __global__ __launch_bounds__(NWC * 128) void chunk_state_pipe_kernel(ChunkParams
 #pragma unroll
     for (int v = 0; v < HK; ++v) {
       const int seg = ht + v * NH, row = seg / KROW, c = (seg % KROW) * EPV;
-      *reinterpret_cast<u32x4*>(dK + row * LDK + c) = pk[v];
-      u32x2* q2 = reinterpret_cast<u32x2*>(dQ + row * LDQ + c);     // q rows are 8-byte aligned
+      u32x2* k2 = reinterpret_cast<u32x2*>(dK + row * LDK + c);     // k, q rows are 8-byte aligned
+      k2[0] = u32x2{pk[v][0], pk[v][1]};
+      k2[1] = u32x2{pk[v][2], pk[v][3]};
+      u32x2* q2 = reinterpret_cast<u32x2*>(dQ + row * LDQ + c);
       q2[0] = u32x2{pq[v][0], pq[v][1]};
       q2[1] = u32x2{pq[v][2], pq[v][3]};
     }
