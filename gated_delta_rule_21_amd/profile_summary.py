@@ -74,34 +74,40 @@ def pick(vals, sub: str):
     return [v for (d, n), v in vals.items() if sub in n]
 
 
-def counters(fetch_csv: str, write_csv: str, kernel: str, algorithmic: float, command: str,
+def counters(fetch_csv: str, write_csv: str, kernels: str, algorithmic: float, command: str,
              digest: str) -> str:
+    """`kernels`: comma-separated name substrings; the traffic of one call of the
+    operation is the sum over them (each kernel runs once per call)."""
     f = per_dispatch(fetch_csv, "FETCH_SIZE")
     w = per_dispatch(write_csv, "WRITE_SIZE")
     cf, cw = pick(f, CAL_KERNEL), pick(w, CAL_KERNEL)
-    kf, kw = pick(f, kernel), pick(w, kernel)
-    if not (cf and cw and kf and kw):
-        raise SystemExit(f"missing dispatches: cal {len(cf)}/{len(cw)}, kernel {len(kf)}/{len(kw)}")
+    if not (cf and cw):
+        raise SystemExit("missing calibration dispatches")
     sf = CAL_BYTES / (1024 * statistics.median(cf))
     sw = CAL_BYTES / (1024 * statistics.median(cw))
-    fb = statistics.median(kf) * 1024 * sf
-    wb = statistics.median(kw) * 1024 * sw
-    tot = fb + wb
-    out = ["# HBM traffic counters", "", f"kernel: `{kernel}`", "", "commands (one counter per run):", "",
+    out = ["# HBM traffic counters", "", f"kernels: `{kernels}`", "", "commands (one counter per run):", "",
            "```", command, "```", "",
            "| quantity | value |", "|---|---|",
            f"| calibration FETCH_SIZE (KiB, median of {len(cf)}) | {statistics.median(cf):.1f} |",
            f"| calibration WRITE_SIZE (KiB, median of {len(cw)}) | {statistics.median(cw):.1f} |",
            f"| calibration bytes read / written | {CAL_BYTES} / {CAL_BYTES} |",
            f"| read scale (bytes per counted byte) | {sf:.4f} |",
-           f"| write scale (bytes per counted byte) | {sw:.4f} |",
-           f"| kernel FETCH_SIZE (KiB, median of {len(kf)}) | {statistics.median(kf):.1f} |",
-           f"| kernel WRITE_SIZE (KiB, median of {len(kw)}) | {statistics.median(kw):.1f} |",
-           f"| kernel HBM bytes read (scaled) | {fb:.4e} |",
-           f"| kernel HBM bytes written (scaled) | {wb:.4e} |",
-           f"| algorithmic bytes per launch | {algorithmic:.4e} |",
-           f"| traffic / algorithmic | {tot / algorithmic:.3f} |",
-           "", f"hbm_bytes_per_launch: {tot:.6e}", f"kernel_source_sha256_16: {digest}", ""]
+           f"| write scale (bytes per counted byte) | {sw:.4f} |"]
+    tot = 0.0
+    for k in kernels.split(","):
+        kf, kw = pick(f, k), pick(w, k)
+        if not (kf and kw):
+            raise SystemExit(f"missing dispatches of {k}")
+        fb = statistics.median(kf) * 1024 * sf
+        wb = statistics.median(kw) * 1024 * sw
+        tot += fb + wb
+        out += [f"| `{k}` FETCH_SIZE / WRITE_SIZE (KiB, median of {len(kf)}) | "
+                f"{statistics.median(kf):.1f} / {statistics.median(kw):.1f} |",
+                f"| `{k}` HBM bytes read / written (scaled) | {fb:.4e} / {wb:.4e} |"]
+    out += [f"| HBM bytes per call (all kernels) | {tot:.4e} |",
+            f"| algorithmic bytes per call | {algorithmic:.4e} |",
+            f"| traffic / algorithmic | {tot / algorithmic:.3f} |",
+            "", f"hbm_bytes_per_launch: {tot:.6e}", f"kernel_source_sha256_16: {digest}", ""]
     return "\n".join(out)
 
 
@@ -115,7 +121,7 @@ def main(argv=None):
     b = sub.add_parser("counters")
     b.add_argument("fetch_csv")
     b.add_argument("write_csv")
-    b.add_argument("--kernel", required=True)
+    b.add_argument("--kernel", required=True, help="name substring, or several separated by commas")
     b.add_argument("--algorithmic-bytes", type=float, required=True)
     b.add_argument("--command", required=True)
     args = ap.parse_args(argv)
