@@ -141,11 +141,13 @@ def bench_chunk(args, log):
     import torch
     import gated_delta_rule_21_amd as gdr
     from workloads import CONFIGS, chunk_inputs
-    wl = CONFIGS[3]
+    wl = CONFIGS[args.chunk_config]
     log(f"generating {wl.name}")
     inp = chunk_inputs(wl)
     dev = lambda x: None if x is None else torch.from_numpy(x).to(torch.bfloat16).cuda()
     q, k, v, beta, log_a = (dev(inp[n]) for n in ("q", "k", "v", "beta", "log_a"))
+    with_S0 = wl.s0_std > 0
+    S0 = torch.from_numpy(inp["S0"]).cuda() if with_S0 else None
     del inp
     o = torch.empty((wl.B, wl.T, wl.H, wl.d_v), dtype=torch.bfloat16, device="cuda")
     S_T = torch.empty((wl.B, wl.H, wl.d_k, wl.d_v), dtype=torch.float32, device="cuda")
@@ -154,7 +156,7 @@ def bench_chunk(args, log):
     stream = torch.cuda.current_stream()
 
     def step():
-        gdr.chunk_fwd(q, k, v, beta, log_a, None, o=o, S_T=S_T, workspace=ws)     # S0 = 0 for this workload
+        gdr.chunk_fwd(q, k, v, beta, log_a, S0, o=o, S_T=S_T, workspace=ws)
 
     for _ in range(args.warmup):
         step()
@@ -169,7 +171,7 @@ def bench_chunk(args, log):
     wall = time.perf_counter() - t0
     ms = ev0.elapsed_time(ev1) / args.steps
     log(f"chunk forward: {ms:.3f} ms/step (wall {1e3 * wall / args.steps:.3f} ms/step)")
-    nbytes, flops = chunk_algorithmic(wl, with_S0=False)
+    nbytes, flops = chunk_algorithmic(wl, with_S0=with_S0)
     return wl, ms, nbytes, flops
 
 
@@ -218,6 +220,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--chunk-config", type=int, default=3, choices=(2, 3, 4),
+                    help="chunk-forward workload (3 = the gated workload of the headline metric)")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-T", type=int, default=8192)
@@ -272,13 +276,15 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "H": wl.H, "d_k": wl.d_k, "d_v": wl.d_v,
-                   "chunk": wl.chunk, "gate": wl.gate, "io": wl.io, "state": "fp32", "S0": "zero",
+                   "chunk": wl.chunk, "gate": wl.gate, "io": wl.io, "state": "fp32",
+                   "S0": "N(0, %g^2)" % wl.s0_std if wl.s0_std > 0 else "zero",
                    "global_batch": wl.B, "seq_len": wl.T, "parallelism": "none (1 GPU)"},
         "tflops_useful": round(tflops, 2),
         "mfma_frac_useful": round(tflops / BF16_PEAK_TFLOPS, 4),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "traffic": profiled_traffic("chunk_fwd_gated_b8h16t8192d128_counters.md", CHUNK_SOURCES)},
+                     "traffic": (profiled_traffic("chunk_fwd_gated_b8h16t8192d128_counters.md", CHUNK_SOURCES)
+                                 if args.chunk_config == 3 else None)},
         "algorithmic_bytes_per_launch": nbytes,
         "useful_flops_per_launch": flops,
         "decode": decode,

@@ -113,15 +113,16 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeParams p) {
     d[j] = b * (vv[j] - uc);
   }
 
-  // S' = S~ + k delta^T, written over the same addresses that were read.
+  // S' = S~ + k delta^T, written over the same addresses that were read, with
+  // non-temporal stores (the state is not read again in this step; measured
+  // faster than ordinary stores for this read-all-then-write-all pattern).
   float* Sn = p.S_new + sid * (DK * DV);
 #pragma unroll
   for (int m = 0; m < RPT; ++m) {
     const int i = rg + RG * m;
     const float ki = s_k[i];
-    float4 s = st[m];
-    s.x += ki * d[0]; s.y += ki * d[1]; s.z += ki * d[2]; s.w += ki * d[3];
-    *reinterpret_cast<float4*>(Sn + i * DV + 4 * cg) = s;
+    f32x4 s = {st[m].x + ki * d[0], st[m].y + ki * d[1], st[m].z + ki * d[2], st[m].w + ki * d[3]};
+    __builtin_nontemporal_store(s, reinterpret_cast<f32x4*>(Sn + i * DV + 4 * cg));
   }
   if (rg == 0) {
     elem* o = static_cast<elem*>(p.o);
