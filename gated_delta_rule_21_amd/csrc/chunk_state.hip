@@ -13,18 +13,17 @@
 //
 // Only K S -> Delta -> S' lies on the sequential chain from chunk to chunk.
 // One workgroup owns one (batch, head, d_v tile of 16*NWC columns) and runs
-// 2*NWC waves, two per SIMD:
-//   chain wave c  (c < NWC) keeps columns 16c..16c+15 of S in MFMA accumulators
-//                 and forms K S, Q S, the residual, Delta and the state update;
-//   helper wave c (NWC + c) moves the next chunk into LDS and the one after
-//                 into registers, forms a share of P, and after the chain wave
-//                 has Delta finishes column group c of the output
-//                 (Q S from the chain wave, plus P Delta).
-// Per chunk n:  [barrier]  chain: Q S, K S, residual, Delta -> LDS exchange
-//                          helper: tiles of chunk n+1 -> LDS, loads of n+2, P
-//               [barrier]  chain: S update;  helper: P Delta, output stores.
-// The tiles (k, q, v, T, per-row factors) are double-buffered in LDS: chunk n
-// is read from one copy while chunk n+1 is written to the other.
+// 2*NWC waves, two per SIMD, with one barrier per chunk:
+//   chain wave c  (c < NWC) keeps columns 16c..16c+15 of S in MFMA accumulators.
+//                 In the step of chunk n it first finishes the output of chunk
+//                 n-1 (Q S and Delta of that chunk kept in registers, plus P of
+//                 that chunk), then forms K S, Q S, the residual, Delta and the
+//                 state update of chunk n;
+//   helper wave c (NWC + c) moves chunk n+1 from registers into the other LDS
+//                 copy, loads chunk n+2, and forms its share of P of chunk n.
+// The output of a chunk is written one step late, which is what lets P be
+// formed beside the chain without a second barrier.  The tiles (k, q, v, T,
+// per-row factors) and P are double-buffered in LDS.
 //
 // Operand layouts as elsewhere in this library: an accumulator tile (lane l:
 // column l%16, rows 4(l/16)+s) is the B operand of the next product and, as the
@@ -60,11 +59,10 @@ struct PipeLayout {
   static constexpr size_t B_T = B_V + VB;                // T^T (the ten blocks on or above the diagonal)
   static constexpr size_t B_F = B_T + TB;                // beta, e^{g_read}, e^{g}, e^{g_63 - g}, e^{g_63}, g
   static constexpr size_t BUF = B_F + 6 * CH * 4;
-  // single copies
-  static constexpr size_t OFF_P = 2 * BUF;               // P (helpers only)
-  static constexpr size_t OFF_XO = OFF_P + size_t(CH) * LCP * 2;   // Q S per chain wave, accumulator tiles
-  static constexpr size_t OFF_XD = OFF_XO + size_t(NWC) * 4 * 64 * 16;   // Delta per chain wave, bf16
-  static constexpr size_t TOTAL = OFF_XD + size_t(NWC) * 4 * 64 * 8;
+  // P of chunk n in copy n % 2
+  static constexpr size_t PB = size_t(CH) * LCP * 2;
+  static constexpr size_t OFF_P = 2 * BUF;
+  static constexpr size_t TOTAL = OFF_P + 2 * PB;
 };
 
 template <int GATE, int DK, int NWC>
@@ -91,9 +89,9 @@ __global__ __launch_bounds__(NWC * 128) void chunk_state_pipe_kernel(ChunkParams
   static_assert(L::TOTAL <= 163840, "LDS budget");
 
   __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
-  T* sP = reinterpret_cast<T*>(smem + L::OFF_P);
-  f32x4* xO = reinterpret_cast<f32x4*>(smem + L::OFF_XO);
-  frag* xD = reinterpret_cast<frag*>(smem + L::OFF_XD);
+  auto p_tile = [&](int64_t n) __attribute__((always_inline)) {
+    return reinterpret_cast<T*>(smem + L::OFF_P + (n & 1) * L::PB);
+  };
 
   // Block -> (head, d_v tile); consecutive logical blocks on one XCD (block ids
   // are dealt round-robin over 8 XCDs), so a head's tiles share that L2.
@@ -207,10 +205,34 @@ __global__ __launch_bounds__(NWC * 128) void chunk_state_pipe_kernel(ChunkParams
     for (int t = 0; t < DKT; ++t)
 #pragma unroll
       for (int s = 0; s < 4; ++s) S[t][s] = p.S0 ? p.S0[(bh * DK + 16 * t + 4 * lg + s) * dv + scol] : 0.f;
+    // the previous chunk's Q S (rows 16R + lr of O^T tiles), Delta and e^{g} of its rows
+    f32x4 oq_prev[4];
+    frag db_prev[4];
+    float eo_prev[4];
+    // O^T tile of column group cw of chunk m: (Q S)^T e^{g} + Delta^T P^T; four adjacent
+    // columns per lane; rows past the end of the sequence fall outside the buffer
+    auto put_output = [&](int64_t m) __attribute__((always_inline)) {
+      const T* sP = p_tile(m);
+      const uint32_t so = static_cast<uint32_t>(m * CH * H * dv * ESZ);
+#pragma unroll
+      for (int R = 0; R < 4; ++R) {
+        f32x4 op = {0.f, 0.f, 0.f, 0.f};
+        const T* pr = sP + (16 * R + lr) * LCP + 4 * lg;
+        int J = 0;
+#pragma unroll
+        for (; J + 1 <= R; J += 2)
+          op = O::mma2(op, db_prev[J], db_prev[J + 1], O::ld(pr + 16 * J), O::ld(pr + 16 * (J + 1)));
+        if (J <= R) op = O::mma1(op, db_prev[J], O::ld(pr + 16 * J));
+        const f32x4 ov = GATE == GATE_SCALAR ? oq_prev[R] * eo_prev[R] + op : oq_prev[R] + op;
+        const uint32_t voff = static_cast<uint32_t>(((16 * R + lr) * H * dv + col0 + 16 * cw + 4 * lg) * ESZ);
+        buf_store8(__builtin_bit_cast(u32x2, to_bf16x4(ov)), ro, voff, so);
+      }
+    };
     __syncthreads();                            // chunk 0 in LDS
 
     for (int64_t n = 0; n < nchunks; ++n) {
       const Tiles c = tiles(n);
+      if (n > 0) put_output(n - 1);             // P of chunk n-1 is complete
       // Q S (output partials), K S, residual
       frag Sb[DKT], Rb[4], Ds[4];
 #pragma unroll
@@ -225,7 +247,8 @@ __global__ __launch_bounds__(NWC * 128) void chunk_state_pipe_kernel(ChunkParams
           x = O::mma2(x, O::ld(kr), O::ld(kr + 16), Sb[2 * kb], Sb[2 * kb + 1]);
           oq = O::mma2(oq, Sb[2 * kb], Sb[2 * kb + 1], O::ld(qr), O::ld(qr + 16));
         }
-        xO[(cw * 4 + R) * 64 + lane] = oq;
+        oq_prev[R] = oq;
+        eo_prev[R] = GATE == GATE_SCALAR ? c.eo[16 * R + lr] : 1.f;
         const f32x4 vv = O::f32(O::ld_tr(c.V, LVT, 16 * R, 16 * cw, lr, lg));
         const f32x4 be = *reinterpret_cast<const f32x4*>(c.beta + 16 * R + 4 * lg);
         const f32x4 er = *reinterpret_cast<const f32x4*>(c.er + 16 * R + 4 * lg);
@@ -244,15 +267,14 @@ __global__ __launch_bounds__(NWC * 128) void chunk_state_pipe_kernel(ChunkParams
           d = O::mma2(d, O::ld_tr(c.Tt, LCT, 16 * m, 16 * R, lr, lg), O::ld_tr(c.Tt, LCT, 16 * (m + 1), 16 * R, lr, lg),
                       Rb[m], Rb[m + 1]);
         if (m <= R) d = O::mma1(d, O::ld_tr(c.Tt, LCT, 16 * m, 16 * R, lr, lg), Rb[m]);
-        xD[(cw * 4 + R) * 64 + lane] = O::cvt(d);
+        db_prev[R] = O::cvt(d);
         if constexpr (GATE == GATE_SCALAR) {
           const f32x4 ed = *reinterpret_cast<const f32x4*>(c.ed + 16 * R + 4 * lg);
           Ds[R] = O::cvt(d * ed);
         } else {
-          Ds[R] = O::cvt(d);
+          Ds[R] = db_prev[R];
         }
       }
-      __syncthreads();                          // Delta, Q S and P complete
       // S' = e^{g_63} S + K^T diag(e^{g_63 - g}) Delta
       const float gam = GATE == GATE_SCALAR ? c.gam[0] : 1.f;
 #pragma unroll
@@ -263,8 +285,9 @@ __global__ __launch_bounds__(NWC * 128) void chunk_state_pipe_kernel(ChunkParams
         acc = O::mma2(acc, O::ld_tr(c.K, LDK, 32, 16 * t, lr, lg), O::ld_tr(c.K, LDK, 48, 16 * t, lr, lg), Ds[2], Ds[3]);
         S[t] = acc;
       }
-      __syncthreads();                          // next chunk's tiles in place; exchange free
+      __syncthreads();                          // next chunk's tiles and this chunk's P in place
     }
+    if (nchunks > 0) put_output(nchunks - 1);
     if (p.S_T) {
 #pragma unroll
       for (int t = 0; t < DKT; ++t)
@@ -282,12 +305,15 @@ __global__ __launch_bounds__(NWC * 128) void chunk_state_pipe_kernel(ChunkParams
 
     for (int64_t n = 0; n < nchunks; ++n) {
       const Tiles c = tiles(n);
-      // next chunk into the other LDS copy (last read before the previous chunk's
-      // closing barrier), loads of the one after, then a share of P
+      // next chunk into the other LDS copy (last read before this step's opening
+      // barrier), loads of the one after
       if (n + 1 < nchunks) {
         store_chunk(smem + ((n + 1) & 1) * L::BUF);
         if (n + 2 < nchunks) prefetch(n + 2);
       }
+      // this helper's share of P of chunk n into copy n % 2 (copy n % 2 was last
+      // read by the chain waves in the previous step, before the opening barrier)
+      T* sP = p_tile(n);
       const int lo = 10 * cw / NWC, hi = 10 * (cw + 1) / NWC;
       for (int u = lo; u < hi; ++u) {
         int R, J;
@@ -311,28 +337,7 @@ __global__ __launch_bounds__(NWC * 128) void chunk_state_pipe_kernel(ChunkParams
         }
         *reinterpret_cast<frag*>(sP + r * LCP + 16 * J + 4 * lg) = O::cvt(acc);
       }
-      __syncthreads();                          // Delta, Q S and P complete
-      // O^T tile of column group cw: (Q S)^T e^{g} + Delta^T P^T; 4 adjacent columns per
-      // lane; rows past the end of the sequence fall outside the buffer
-      frag Db[4];
-#pragma unroll
-      for (int R = 0; R < 4; ++R) Db[R] = xD[(cw * 4 + R) * 64 + lane];
-      const uint32_t so = static_cast<uint32_t>(n * CH * H * dv * ESZ);
-#pragma unroll
-      for (int R = 0; R < 4; ++R) {
-        f32x4 op = {0.f, 0.f, 0.f, 0.f};
-        const T* pr = sP + (16 * R + lr) * LCP + 4 * lg;
-        int J = 0;
-#pragma unroll
-        for (; J + 1 <= R; J += 2) op = O::mma2(op, Db[J], Db[J + 1], O::ld(pr + 16 * J), O::ld(pr + 16 * (J + 1)));
-        if (J <= R) op = O::mma1(op, Db[J], O::ld(pr + 16 * J));
-        const f32x4 oq = xO[(cw * 4 + R) * 64 + lane];
-        const int r = 16 * R + lr;
-        const f32x4 ov = GATE == GATE_SCALAR ? oq * c.eo[r] + op : oq + op;
-        const uint32_t voff = static_cast<uint32_t>((r * H * dv + col0 + 16 * cw + 4 * lg) * ESZ);
-        buf_store8(__builtin_bit_cast(u32x2, to_bf16x4(ov)), ro, voff, so);
-      }
-      __syncthreads();                          // next chunk's tiles in place; exchange free
+      __syncthreads();                          // next chunk's tiles and this chunk's P in place
     }
   }
 }
