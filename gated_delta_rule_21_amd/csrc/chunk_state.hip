@@ -12,15 +12,17 @@
 //   S'    = e^{g_63} S + K^T diag(e^{g_63 - g}) Delta
 //
 // Only K S -> Delta -> S' lies on the sequential chain from chunk to chunk.
-// One workgroup owns one (batch, head, d_v tile of 16*NWC columns) and runs
-// 2*NWC waves, two per SIMD, with one barrier per chunk:
-//   chain wave c  (c < NWC) keeps columns 16c..16c+15 of S in MFMA accumulators.
-//                 In the step of chunk n it first finishes the output of chunk
-//                 n-1 (Q S and Delta of that chunk kept in registers, plus P of
-//                 that chunk), then forms K S, Q S, the residual, Delta and the
-//                 state update of chunk n;
-//   helper wave c (NWC + c) moves chunk n+1 from registers into the other LDS
-//                 copy, loads chunk n+2, and forms its share of P of chunk n.
+// One workgroup owns one (batch, head, d_v tile of 16*CG*NCH columns) and runs
+// NCH chain waves and NHW helper waves, with one barrier per chunk:
+//   chain wave c  (c < NCH) keeps CG groups of 16 columns of S in MFMA
+//                 accumulators; every operand fragment it reads from LDS (rows
+//                 of k, q, T, K^T and P) serves all its groups.  In the step of
+//                 chunk n it first finishes the output of chunk n-1 (Q S and
+//                 Delta of that chunk kept in registers, plus P of that chunk),
+//                 then forms K S, Q S, the residual, Delta and the state update
+//                 of chunk n;
+//   helper wave h moves chunk n+1 from registers into the other LDS copy, loads
+//                 chunk n+2, and forms its share of P of chunk n.
 // The output of a chunk is written one step late, which is what lets P be
 // formed beside the chain without a second barrier.  The tiles (k, q, v, T,
 // per-row factors) and P are double-buffered in LDS.
@@ -40,11 +42,11 @@ namespace gdr {
 // is 2 or 6 (mod 8) dwords long, transpose reads (ds_read_b64_tr_b16) at 168 B/clk
 // when it is 8 (mod 32) dwords and at 128 B/clk for most other lengths; the k
 // tile is read both ways and takes 6 (mod 32) dwords (121 and 128 B/clk).
-template <int DK, int NWC>
+template <int DK, int DVT_>
 struct PipeLayout {
   static constexpr int LDK = DK + 12;                    // k: row and transpose reads (8-byte aligned rows)
   static constexpr int LDQ = DK + 4;                     // q: row reads (8-byte aligned rows)
-  static constexpr int DVT = 16 * NWC;
+  static constexpr int DVT = DVT_;
   static constexpr int LVT = DVT + 16;                   // v: transpose reads
   static constexpr int LCT = CH + 16;                    // T^T: transpose reads
   static constexpr int LCP = CH + 4;                     // P: row reads
@@ -65,17 +67,17 @@ struct PipeLayout {
   static constexpr size_t TOTAL = OFF_P + 2 * PB;
 };
 
-template <int GATE, int DK, int NWC>
-__global__ __launch_bounds__(NWC * 128) void chunk_state_pipe_kernel(ChunkParams p, int n_tiles) {
+template <int GATE, int DK, int NCH, int CG, int NHW>
+__global__ __launch_bounds__((NCH + NHW) * 64) void chunk_state_pipe_kernel(ChunkParams p, int n_tiles) {
   typedef Op<IO_BF16> O;
   typedef __bf16 T;
   typedef bf16x4 frag;
   typedef uint16_t elem;
-  typedef PipeLayout<DK, NWC> L;
+  constexpr int DVT = 16 * CG * NCH;            // columns per workgroup
+  typedef PipeLayout<DK, DVT> L;
   typedef WsRec<2> W;
   constexpr int ESZ = 2, EPV = 8;
-  constexpr int NH = NWC * 64;                   // helper threads
-  constexpr int DVT = 16 * NWC;
+  constexpr int NH = NHW * 64;                   // helper threads
   constexpr int DKT = DK / 16;
   constexpr int LDK = L::LDK, LDQ = L::LDQ, LVT = L::LVT, LCT = L::LCT, LCP = L::LCP;
   constexpr int KROW = DK / EPV, VROW = DVT / EPV;
@@ -107,12 +109,12 @@ __global__ __launch_bounds__(NWC * 128) void chunk_state_pipe_kernel(ChunkParams
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform across the wave
-  const bool chain = wave < NWC;
-  const int cw = chain ? wave : wave - NWC;                      // column group
+  const bool chain = wave < NCH;
+  const int cw = chain ? wave : wave - NCH;      // chain: its columns 16 CG cw ..; helper: its index
   const int lane = tid & 63;
   const int lr = lane & 15;
   const int lg = lane >> 4;
-  const int ht = tid - NH;                                       // helper thread index
+  const int ht = tid - 64 * NCH;                 // helper thread index
 
   const int64_t nchunks = (p.T + CH - 1) / CH;
   const int64_t row0 = bb * p.T * p.H + hh;
@@ -198,34 +200,51 @@ __global__ __launch_bounds__(NWC * 128) void chunk_state_pipe_kernel(ChunkParams
   // The two roles run separate loops with the same two barriers per chunk (the
   // role is uniform per wave), so neither keeps the other's registers live.
   if (chain) {
-    // ---- chain waves: this column group's slice of S in accumulators ------------------
-    const int scol = col0 + 16 * cw + lr;
-    f32x4 S[DKT];
+    // ---- chain waves: CG groups of 16 columns of S in MFMA accumulators --------------------
+    // Every operand fragment read from LDS (rows of k, q, T, K^T, P) serves all CG groups.
+    const int c0 = 16 * CG * cw;                // first column of this wave within the tile
+    f32x4 S[CG][DKT];
 #pragma unroll
-    for (int t = 0; t < DKT; ++t)
+    for (int g = 0; g < CG; ++g)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) S[t][s] = p.S0 ? p.S0[(bh * DK + 16 * t + 4 * lg + s) * dv + scol] : 0.f;
+      for (int t = 0; t < DKT; ++t)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          S[g][t][s] = p.S0 ? p.S0[(bh * DK + 16 * t + 4 * lg + s) * dv + col0 + c0 + 16 * g + lr] : 0.f;
     // the previous chunk's Q S (rows 16R + lr of O^T tiles), Delta and e^{g} of its rows
-    f32x4 oq_prev[4];
-    frag db_prev[4];
+    f32x4 oq_prev[CG][4];
+    frag db_prev[CG][4];
     float eo_prev[4];
-    // O^T tile of column group cw of chunk m: (Q S)^T e^{g} + Delta^T P^T; four adjacent
-    // columns per lane; rows past the end of the sequence fall outside the buffer
+    // O^T tiles of chunk m: (Q S)^T e^{g} + Delta^T P^T; four adjacent columns per lane;
+    // rows past the end of the sequence fall outside the buffer
     auto put_output = [&](int64_t m) __attribute__((always_inline)) {
       const T* sP = p_tile(m);
       const uint32_t so = static_cast<uint32_t>(m * CH * H * dv * ESZ);
 #pragma unroll
       for (int R = 0; R < 4; ++R) {
-        f32x4 op = {0.f, 0.f, 0.f, 0.f};
+        f32x4 op[CG];
+#pragma unroll
+        for (int g = 0; g < CG; ++g) op[g] = f32x4{0.f, 0.f, 0.f, 0.f};
         const T* pr = sP + (16 * R + lr) * LCP + 4 * lg;
         int J = 0;
 #pragma unroll
-        for (; J + 1 <= R; J += 2)
-          op = O::mma2(op, db_prev[J], db_prev[J + 1], O::ld(pr + 16 * J), O::ld(pr + 16 * (J + 1)));
-        if (J <= R) op = O::mma1(op, db_prev[J], O::ld(pr + 16 * J));
-        const f32x4 ov = GATE == GATE_SCALAR ? oq_prev[R] * eo_prev[R] + op : oq_prev[R] + op;
-        const uint32_t voff = static_cast<uint32_t>(((16 * R + lr) * H * dv + col0 + 16 * cw + 4 * lg) * ESZ);
-        buf_store8(__builtin_bit_cast(u32x2, to_bf16x4(ov)), ro, voff, so);
+        for (; J + 1 <= R; J += 2) {
+          const frag p0 = O::ld(pr + 16 * J), p1 = O::ld(pr + 16 * (J + 1));
+#pragma unroll
+          for (int g = 0; g < CG; ++g) op[g] = O::mma2(op[g], db_prev[g][J], db_prev[g][J + 1], p0, p1);
+        }
+        if (J <= R) {
+          const frag p0 = O::ld(pr + 16 * J);
+#pragma unroll
+          for (int g = 0; g < CG; ++g) op[g] = O::mma1(op[g], db_prev[g][J], p0);
+        }
+#pragma unroll
+        for (int g = 0; g < CG; ++g) {
+          const f32x4 ov = GATE == GATE_SCALAR ? oq_prev[g][R] * eo_prev[R] + op[g] : oq_prev[g][R] + op[g];
+          const uint32_t voff =
+              static_cast<uint32_t>(((16 * R + lr) * H * dv + col0 + c0 + 16 * g + 4 * lg) * ESZ);
+          buf_store8(__builtin_bit_cast(u32x2, to_bf16x4(ov)), ro, voff, so);
+        }
       }
     };
     __syncthreads();                            // chunk 0 in LDS
@@ -234,65 +253,92 @@ __global__ __launch_bounds__(NWC * 128) void chunk_state_pipe_kernel(ChunkParams
       const Tiles c = tiles(n);
       if (n > 0) put_output(n - 1);             // P of chunk n-1 is complete
       // Q S (output partials), K S, residual
-      frag Sb[DKT], Rb[4], Ds[4];
+      frag Sb[CG][DKT], Rb[CG][4], Ds[CG][4];
 #pragma unroll
-      for (int t = 0; t < DKT; ++t) Sb[t] = O::cvt(S[t]);
+      for (int g = 0; g < CG; ++g)
+#pragma unroll
+        for (int t = 0; t < DKT; ++t) Sb[g][t] = O::cvt(S[g][t]);
 #pragma unroll
       for (int R = 0; R < 4; ++R) {
-        f32x4 x = {0.f, 0.f, 0.f, 0.f}, oq = {0.f, 0.f, 0.f, 0.f};
+        f32x4 x[CG], oq[CG];
+#pragma unroll
+        for (int g = 0; g < CG; ++g) x[g] = oq[g] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < DK / 32; ++kb) {
           const T* kr = c.K + (16 * R + lr) * LDK + 32 * kb + 4 * lg;
           const T* qr = c.Q + (16 * R + lr) * LDQ + 32 * kb + 4 * lg;
-          x = O::mma2(x, O::ld(kr), O::ld(kr + 16), Sb[2 * kb], Sb[2 * kb + 1]);
-          oq = O::mma2(oq, Sb[2 * kb], Sb[2 * kb + 1], O::ld(qr), O::ld(qr + 16));
+          const frag k0 = O::ld(kr), k1 = O::ld(kr + 16), q0 = O::ld(qr), q1 = O::ld(qr + 16);
+#pragma unroll
+          for (int g = 0; g < CG; ++g) {
+            x[g] = O::mma2(x[g], k0, k1, Sb[g][2 * kb], Sb[g][2 * kb + 1]);
+            oq[g] = O::mma2(oq[g], Sb[g][2 * kb], Sb[g][2 * kb + 1], q0, q1);
+          }
         }
-        oq_prev[R] = oq;
         eo_prev[R] = GATE == GATE_SCALAR ? c.eo[16 * R + lr] : 1.f;
-        const f32x4 vv = O::f32(O::ld_tr(c.V, LVT, 16 * R, 16 * cw, lr, lg));
         const f32x4 be = *reinterpret_cast<const f32x4*>(c.beta + 16 * R + 4 * lg);
         const f32x4 er = *reinterpret_cast<const f32x4*>(c.er + 16 * R + 4 * lg);
-        f32x4 rr;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) rr[s] = be[s] * (vv[s] - (GATE == GATE_SCALAR ? x[s] * er[s] : x[s]));
-        Rb[R] = O::cvt(rr);
+        for (int g = 0; g < CG; ++g) {
+          oq_prev[g][R] = oq[g];
+          const f32x4 vv = O::f32(O::ld_tr(c.V, LVT, 16 * R, c0 + 16 * g, lr, lg));
+          f32x4 rr;
+#pragma unroll
+          for (int s = 0; s < 4; ++s) rr[s] = be[s] * (vv[s] - (GATE == GATE_SCALAR ? x[g][s] * er[s] : x[g][s]));
+          Rb[g][R] = O::cvt(rr);
+        }
       }
       // Delta_R = sum_{m <= R} T_Rm R_m; rows of T from T^T
 #pragma unroll
       for (int R = 0; R < 4; ++R) {
-        f32x4 d = {0.f, 0.f, 0.f, 0.f};
+        f32x4 d[CG];
+#pragma unroll
+        for (int g = 0; g < CG; ++g) d[g] = f32x4{0.f, 0.f, 0.f, 0.f};
         int m = 0;
 #pragma unroll
-        for (; m + 1 <= R; m += 2)
-          d = O::mma2(d, O::ld_tr(c.Tt, LCT, 16 * m, 16 * R, lr, lg), O::ld_tr(c.Tt, LCT, 16 * (m + 1), 16 * R, lr, lg),
-                      Rb[m], Rb[m + 1]);
-        if (m <= R) d = O::mma1(d, O::ld_tr(c.Tt, LCT, 16 * m, 16 * R, lr, lg), Rb[m]);
-        db_prev[R] = O::cvt(d);
-        if constexpr (GATE == GATE_SCALAR) {
-          const f32x4 ed = *reinterpret_cast<const f32x4*>(c.ed + 16 * R + 4 * lg);
-          Ds[R] = O::cvt(d * ed);
-        } else {
-          Ds[R] = db_prev[R];
+        for (; m + 1 <= R; m += 2) {
+          const frag t0 = O::ld_tr(c.Tt, LCT, 16 * m, 16 * R, lr, lg);
+          const frag t1 = O::ld_tr(c.Tt, LCT, 16 * (m + 1), 16 * R, lr, lg);
+#pragma unroll
+          for (int g = 0; g < CG; ++g) d[g] = O::mma2(d[g], t0, t1, Rb[g][m], Rb[g][m + 1]);
+        }
+        if (m <= R) {
+          const frag t0 = O::ld_tr(c.Tt, LCT, 16 * m, 16 * R, lr, lg);
+#pragma unroll
+          for (int g = 0; g < CG; ++g) d[g] = O::mma1(d[g], t0, Rb[g][m]);
+        }
+        const f32x4 ed = GATE == GATE_SCALAR ? *reinterpret_cast<const f32x4*>(c.ed + 16 * R + 4 * lg)
+                                             : f32x4{1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+        for (int g = 0; g < CG; ++g) {
+          db_prev[g][R] = O::cvt(d[g]);
+          Ds[g][R] = GATE == GATE_SCALAR ? O::cvt(d[g] * ed) : db_prev[g][R];
         }
       }
       // S' = e^{g_63} S + K^T diag(e^{g_63 - g}) Delta
       const float gam = GATE == GATE_SCALAR ? c.gam[0] : 1.f;
 #pragma unroll
       for (int t = 0; t < DKT; ++t) {
-        f32x4 acc = S[t];
-        if constexpr (GATE == GATE_SCALAR) acc = acc * gam;
-        acc = O::mma2(acc, O::ld_tr(c.K, LDK, 0, 16 * t, lr, lg), O::ld_tr(c.K, LDK, 16, 16 * t, lr, lg), Ds[0], Ds[1]);
-        acc = O::mma2(acc, O::ld_tr(c.K, LDK, 32, 16 * t, lr, lg), O::ld_tr(c.K, LDK, 48, 16 * t, lr, lg), Ds[2], Ds[3]);
-        S[t] = acc;
+        const frag a0 = O::ld_tr(c.K, LDK, 0, 16 * t, lr, lg), a1 = O::ld_tr(c.K, LDK, 16, 16 * t, lr, lg);
+        const frag a2 = O::ld_tr(c.K, LDK, 32, 16 * t, lr, lg), a3 = O::ld_tr(c.K, LDK, 48, 16 * t, lr, lg);
+#pragma unroll
+        for (int g = 0; g < CG; ++g) {
+          f32x4 acc = S[g][t];
+          if constexpr (GATE == GATE_SCALAR) acc = acc * gam;
+          acc = O::mma2(acc, a0, a1, Ds[g][0], Ds[g][1]);
+          S[g][t] = O::mma2(acc, a2, a3, Ds[g][2], Ds[g][3]);
+        }
       }
       __syncthreads();                          // next chunk's tiles and this chunk's P in place
     }
     if (nchunks > 0) put_output(nchunks - 1);
     if (p.S_T) {
 #pragma unroll
-      for (int t = 0; t < DKT; ++t)
+      for (int g = 0; g < CG; ++g)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) p.S_T[(bh * DK + 16 * t + 4 * lg + s) * dv + scol] = S[t][s];
+        for (int t = 0; t < DKT; ++t)
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            p.S_T[(bh * DK + 16 * t + 4 * lg + s) * dv + col0 + c0 + 16 * g + lr] = S[g][t][s];
     }
   } else {
     // ---- helper waves -------------------------------------------------------------------
@@ -314,7 +360,7 @@ __global__ __launch_bounds__(NWC * 128) void chunk_state_pipe_kernel(ChunkParams
       // this helper's share of P of chunk n into copy n % 2 (copy n % 2 was last
       // read by the chain waves in the previous step, before the opening barrier)
       T* sP = p_tile(n);
-      const int lo = 10 * cw / NWC, hi = 10 * (cw + 1) / NWC;
+      const int lo = 10 * cw / NHW, hi = 10 * (cw + 1) / NHW;
       for (int u = lo; u < hi; ++u) {
         int R, J;
         tri_block(u, R, J);
@@ -342,20 +388,23 @@ __global__ __launch_bounds__(NWC * 128) void chunk_state_pipe_kernel(ChunkParams
   }
 }
 
-template <int GATE, int DK, int NWC>
+template <int GATE, int DK, int NCH, int CG, int NHW>
 static hipError_t launch_pipe_t(const ChunkParams& p, hipStream_t stream) {
-  const int n_tiles = p.d_v / (16 * NWC);
+  const int n_tiles = p.d_v / (16 * CG * NCH);
   const int64_t nblk = p.B * p.H * n_tiles;
-  hipLaunchKernelGGL((chunk_state_pipe_kernel<GATE, DK, NWC>), dim3(static_cast<unsigned>(nblk)), dim3(NWC * 128),
-                     0, stream, p, n_tiles);
+  hipLaunchKernelGGL((chunk_state_pipe_kernel<GATE, DK, NCH, CG, NHW>), dim3(static_cast<unsigned>(nblk)),
+                     dim3((NCH + NHW) * 64), 0, stream, p, n_tiles);
   return hipGetLastError();
 }
 
 template <int GATE, int DK>
 static hipError_t launch_pipe_dk(const ChunkParams& p, hipStream_t stream) {
-  // 64 columns per workgroup when that still gives one workgroup per CU, else 32
-  if (p.B * p.H * (p.d_v / 64) >= 256) return launch_pipe_t<GATE, DK, 4>(p, stream);
-  return launch_pipe_t<GATE, DK, 2>(p, stream);
+  // 64 columns per workgroup when that still gives one workgroup per CU, else 32.
+  // Measured on the gated workload (state pass): 4 chain waves of 16 columns with 4
+  // helpers 364 us; 2 chain waves of 32 columns with 4 helpers 378 us; with 2
+  // helpers 419 and 416 us.
+  if (p.B * p.H * (p.d_v / 64) >= 256) return launch_pipe_t<GATE, DK, 4, 1, 4>(p, stream);
+  return launch_pipe_t<GATE, DK, 2, 1, 2>(p, stream);
 }
 
 template <int GATE>
