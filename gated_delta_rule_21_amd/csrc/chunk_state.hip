@@ -21,8 +21,10 @@
 //                 Delta of that chunk kept in registers, plus P of that chunk),
 //                 then forms K S, Q S, the residual, Delta and the state update
 //                 of chunk n;
-//   helper wave h moves chunk n+1 from registers into the other LDS copy, loads
-//                 chunk n+2, and forms its share of P of chunk n.
+//   helper wave h forms the rows of P of chunk n in row blocks h, h + NHW, ..,
+//                 then moves chunk n+1 from registers into the other LDS copy and
+//                 loads chunk n+2 (P first: it needs no memory, while the stores
+//                 wait for loads issued a step earlier).
 // The output of a chunk is written one step late, which is what lets P be
 // formed beside the chain without a second barrier.  The tiles (k, q, v, T,
 // per-row factors) and P are double-buffered in LDS.
@@ -197,11 +199,15 @@ __global__ __launch_bounds__((NCH + NHW) * 64) void chunk_state_pipe_kernel(Chun
                  f, f + CH, f + 2 * CH, f + 3 * CH, f + 4 * CH, f + 5 * CH};
   };
 
-  // The two roles run separate loops with the same two barriers per chunk (the
+  // The two roles run separate loops with the same one barrier per chunk (the
   // role is uniform per wave), so neither keeps the other's registers live.
   if (chain) {
     // ---- chain waves: CG groups of 16 columns of S in MFMA accumulators --------------------
     // Every operand fragment read from LDS (rows of k, q, T, K^T, P) serves all CG groups.
+    // The step is software-pipelined by hand: each stage issues the LDS reads of the
+    // next one before its own products, and scheduling fences keep the compiler from
+    // sinking those reads to their first use (which would expose the LDS latency on
+    // every product).
     const int c0 = 16 * CG * cw;                // first column of this wave within the tile
     f32x4 S[CG][DKT];
 #pragma unroll
@@ -215,79 +221,156 @@ __global__ __launch_bounds__((NCH + NHW) * 64) void chunk_state_pipe_kernel(Chun
     f32x4 oq_prev[CG][4];
     frag db_prev[CG][4];
     float eo_prev[4];
-    // O^T tiles of chunk m: (Q S)^T e^{g} + Delta^T P^T; four adjacent columns per lane;
-    // rows past the end of the sequence fall outside the buffer
-    auto put_output = [&](int64_t m) __attribute__((always_inline)) {
-      const T* sP = p_tile(m);
-      const uint32_t so = static_cast<uint32_t>(m * CH * H * dv * ESZ);
 #pragma unroll
-      for (int R = 0; R < 4; ++R) {
-        f32x4 op[CG];
+    for (int R = 0; R < 4; ++R) {
+      eo_prev[R] = 0.f;
 #pragma unroll
-        for (int g = 0; g < CG; ++g) op[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const T* pr = sP + (16 * R + lr) * LCP + 4 * lg;
-        int J = 0;
-#pragma unroll
-        for (; J + 1 <= R; J += 2) {
-          const frag p0 = O::ld(pr + 16 * J), p1 = O::ld(pr + 16 * (J + 1));
-#pragma unroll
-          for (int g = 0; g < CG; ++g) op[g] = O::mma2(op[g], db_prev[g][J], db_prev[g][J + 1], p0, p1);
-        }
-        if (J <= R) {
-          const frag p0 = O::ld(pr + 16 * J);
-#pragma unroll
-          for (int g = 0; g < CG; ++g) op[g] = O::mma1(op[g], db_prev[g][J], p0);
-        }
-#pragma unroll
-        for (int g = 0; g < CG; ++g) {
-          const f32x4 ov = GATE == GATE_SCALAR ? oq_prev[g][R] * eo_prev[R] + op[g] : oq_prev[g][R] + op[g];
-          const uint32_t voff =
-              static_cast<uint32_t>(((16 * R + lr) * H * dv + col0 + c0 + 16 * g + 4 * lg) * ESZ);
-          buf_store8(__builtin_bit_cast(u32x2, to_bf16x4(ov)), ro, voff, so);
-        }
+      for (int g = 0; g < CG; ++g) {
+        oq_prev[g][R] = f32x4{0.f, 0.f, 0.f, 0.f};
+        db_prev[g][R] = O::cvt(oq_prev[g][R]);
       }
-    };
+    }
+    // Output voffset per (R, g); before the first chunk there is no output yet, and the
+    // offset is pushed past the end of the buffer so the hardware drops those stores.
+    uint32_t vo[4][CG];
+#pragma unroll
+    for (int R = 0; R < 4; ++R)
+#pragma unroll
+      for (int g = 0; g < CG; ++g)
+        vo[R][g] = static_cast<uint32_t>(((16 * R + lr) * H * dv + col0 + c0 + 16 * g + 4 * lg) * ESZ);
+    constexpr uint32_t DROP = 0x80000000u;     // beyond any sequence (at most 2^31 - 1 bytes)
+    constexpr int NKB = DK / 32;
     __syncthreads();                            // chunk 0 in LDS
 
     for (int64_t n = 0; n < nchunks; ++n) {
       const Tiles c = tiles(n);
-      if (n > 0) put_output(n - 1);             // P of chunk n-1 is complete
-      // Q S (output partials), K S, residual
-      frag Sb[CG][DKT], Rb[CG][4], Ds[CG][4];
+      const T* sP = p_tile(n - 1);
+      frag kf[2][2 * NKB], qf[2][2 * NKB];      // rows of k and q of one row block, double-buffered
+      frag vt[4][CG];                           // v (transposed) of each row block
+      f32x4 be[4], er[4];
+      float eo[4];
+      auto load_rows = [&](int b, int R) __attribute__((always_inline)) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const T* kr = c.K + (16 * R + lr) * LDK + 32 * kb + 4 * lg;
+          const T* qr = c.Q + (16 * R + lr) * LDQ + 32 * kb + 4 * lg;
+          kf[b][2 * kb] = O::ld(kr);
+          kf[b][2 * kb + 1] = O::ld(kr + 16);
+          qf[b][2 * kb] = O::ld(qr);
+          qf[b][2 * kb + 1] = O::ld(qr + 16);
+        }
+#pragma unroll
+        for (int g = 0; g < CG; ++g) vt[R][g] = O::ld_tr(c.V, LVT, 16 * R, c0 + 16 * g, lr, lg);
+        be[R] = *reinterpret_cast<const f32x4*>(c.beta + 16 * R + 4 * lg);
+        er[R] = *reinterpret_cast<const f32x4*>(c.er + 16 * R + 4 * lg);
+        eo[R] = GATE == GATE_SCALAR ? c.eo[16 * R + lr] : 1.f;
+      };
+
+      // stage A: P of the previous chunk, rows of block 0; S to bf16
+      frag pf[10];
+#pragma unroll
+      for (int R = 0; R < 4; ++R)
+#pragma unroll
+        for (int J = 0; J <= R; ++J) pf[R * (R + 1) / 2 + J] = O::ld(sP + (16 * R + lr) * LCP + 16 * J + 4 * lg);
+      load_rows(0, 0);
+      frag Sb[CG][DKT];
 #pragma unroll
       for (int g = 0; g < CG; ++g)
 #pragma unroll
         for (int t = 0; t < DKT; ++t) Sb[g][t] = O::cvt(S[g][t]);
-#pragma unroll
-      for (int R = 0; R < 4; ++R) {
-        f32x4 x[CG], oq[CG];
-#pragma unroll
-        for (int g = 0; g < CG; ++g) x[g] = oq[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < DK / 32; ++kb) {
-          const T* kr = c.K + (16 * R + lr) * LDK + 32 * kb + 4 * lg;
-          const T* qr = c.Q + (16 * R + lr) * LDQ + 32 * kb + 4 * lg;
-          const frag k0 = O::ld(kr), k1 = O::ld(kr + 16), q0 = O::ld(qr), q1 = O::ld(qr + 16);
-#pragma unroll
-          for (int g = 0; g < CG; ++g) {
-            x[g] = O::mma2(x[g], k0, k1, Sb[g][2 * kb], Sb[g][2 * kb + 1]);
-            oq[g] = O::mma2(oq[g], Sb[g][2 * kb], Sb[g][2 * kb + 1], q0, q1);
-          }
-        }
-        eo_prev[R] = GATE == GATE_SCALAR ? c.eo[16 * R + lr] : 1.f;
-        const f32x4 be = *reinterpret_cast<const f32x4*>(c.beta + 16 * R + 4 * lg);
-        const f32x4 er = *reinterpret_cast<const f32x4*>(c.er + 16 * R + 4 * lg);
+
+      // stages KS(R): K S and Q S of row block R; the residual of block R-1 (its K S has
+      // had a stage to drain); the previous chunk's output after block 0
+      f32x4 x[4][CG];
+      frag Rb[CG][4];
+      frag tf[10];                              // rows of T (from T^T)
+      f32x4 ed[4];
+      float gam = 1.f;
+      auto resid = [&](int R) __attribute__((always_inline)) {
 #pragma unroll
         for (int g = 0; g < CG; ++g) {
-          oq_prev[g][R] = oq[g];
-          const f32x4 vv = O::f32(O::ld_tr(c.V, LVT, 16 * R, c0 + 16 * g, lr, lg));
+          const f32x4 vv = O::f32(vt[R][g]);
           f32x4 rr;
 #pragma unroll
-          for (int s = 0; s < 4; ++s) rr[s] = be[s] * (vv[s] - (GATE == GATE_SCALAR ? x[g][s] * er[s] : x[g][s]));
+          for (int s = 0; s < 4; ++s)
+            rr[s] = be[R][s] * (vv[s] - (GATE == GATE_SCALAR ? x[R][g][s] * er[R][s] : x[R][g][s]));
           Rb[g][R] = O::cvt(rr);
         }
+      };
+#pragma unroll
+      for (int R = 0; R < 4; ++R) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (R < 3) {
+          load_rows((R + 1) & 1, R + 1);
+        } else {
+#pragma unroll
+          for (int Rr = 0; Rr < 4; ++Rr)
+#pragma unroll
+            for (int m = 0; m <= Rr; ++m) tf[Rr * (Rr + 1) / 2 + m] = O::ld_tr(c.Tt, LCT, 16 * m, 16 * Rr, lr, lg);
+#pragma unroll
+          for (int Rr = 0; Rr < 4; ++Rr)
+            ed[Rr] = GATE == GATE_SCALAR ? *reinterpret_cast<const f32x4*>(c.ed + 16 * Rr + 4 * lg)
+                                         : f32x4{1.f, 1.f, 1.f, 1.f};
+          if constexpr (GATE == GATE_SCALAR) gam = c.gam[0];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4 oq[CG];
+#pragma unroll
+        for (int g = 0; g < CG; ++g) x[R][g] = oq[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int g = 0; g < CG; ++g) {
+            x[R][g] = O::mma2(x[R][g], kf[R & 1][2 * kb], kf[R & 1][2 * kb + 1], Sb[g][2 * kb], Sb[g][2 * kb + 1]);
+            oq[g] = O::mma2(oq[g], Sb[g][2 * kb], Sb[g][2 * kb + 1], qf[R & 1][2 * kb], qf[R & 1][2 * kb + 1]);
+          }
+        if (R == 0) {
+          // O^T tiles of chunk n-1: (Q S)^T e^{g} + Delta^T P^T, four adjacent columns per lane;
+          // rows past the end of the sequence fall outside the buffer
+          const uint32_t so = n > 0 ? static_cast<uint32_t>((n - 1) * CH * H * dv * ESZ) : 0u;
+          const uint32_t drop = n > 0 ? 0u : DROP;
+#pragma unroll
+          for (int Ro = 0; Ro < 4; ++Ro) {
+            f32x4 op[CG];
+#pragma unroll
+            for (int g = 0; g < CG; ++g) op[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+            int J = 0;
+#pragma unroll
+            for (; J + 1 <= Ro; J += 2)
+#pragma unroll
+              for (int g = 0; g < CG; ++g)
+                op[g] = O::mma2(op[g], db_prev[g][J], db_prev[g][J + 1], pf[Ro * (Ro + 1) / 2 + J],
+                                pf[Ro * (Ro + 1) / 2 + J + 1]);
+            if (J <= Ro)
+#pragma unroll
+              for (int g = 0; g < CG; ++g) op[g] = O::mma1(op[g], db_prev[g][J], pf[Ro * (Ro + 1) / 2 + J]);
+#pragma unroll
+            for (int g = 0; g < CG; ++g) {
+              const f32x4 ov = GATE == GATE_SCALAR ? oq_prev[g][Ro] * eo_prev[Ro] + op[g] : oq_prev[g][Ro] + op[g];
+              buf_store8(__builtin_bit_cast(u32x2, to_bf16x4(ov)), ro, vo[Ro][g] + drop, so);
+            }
+          }
+        } else {
+          resid(R - 1);
+        }
+#pragma unroll
+        for (int g = 0; g < CG; ++g) oq_prev[g][R] = oq[g];
+        eo_prev[R] = eo[R];
       }
-      // Delta_R = sum_{m <= R} T_Rm R_m; rows of T from T^T
+
+      // stage Delta: Delta_R = sum_{m <= R} T_Rm R_m; first rows of K^T for the update
+      frag ktf[2][8];                           // K^T fragments of two 16-row tiles, double-buffered
+      auto load_kt = [&](int b, int tp) __attribute__((always_inline)) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ktf[b][4 * h + i] = O::ld_tr(c.K, LDK, 16 * i, 16 * (2 * tp + h), lr, lg);
+      };
+      __builtin_amdgcn_sched_barrier(0);
+      load_kt(0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      resid(3);
+      frag Ds[CG][4];
 #pragma unroll
       for (int R = 0; R < 4; ++R) {
         f32x4 d[CG];
@@ -295,42 +378,64 @@ __global__ __launch_bounds__((NCH + NHW) * 64) void chunk_state_pipe_kernel(Chun
         for (int g = 0; g < CG; ++g) d[g] = f32x4{0.f, 0.f, 0.f, 0.f};
         int m = 0;
 #pragma unroll
-        for (; m + 1 <= R; m += 2) {
-          const frag t0 = O::ld_tr(c.Tt, LCT, 16 * m, 16 * R, lr, lg);
-          const frag t1 = O::ld_tr(c.Tt, LCT, 16 * (m + 1), 16 * R, lr, lg);
+        for (; m + 1 <= R; m += 2)
 #pragma unroll
-          for (int g = 0; g < CG; ++g) d[g] = O::mma2(d[g], t0, t1, Rb[g][m], Rb[g][m + 1]);
-        }
-        if (m <= R) {
-          const frag t0 = O::ld_tr(c.Tt, LCT, 16 * m, 16 * R, lr, lg);
+          for (int g = 0; g < CG; ++g)
+            d[g] = O::mma2(d[g], tf[R * (R + 1) / 2 + m], tf[R * (R + 1) / 2 + m + 1], Rb[g][m], Rb[g][m + 1]);
+        if (m <= R)
 #pragma unroll
-          for (int g = 0; g < CG; ++g) d[g] = O::mma1(d[g], t0, Rb[g][m]);
-        }
-        const f32x4 ed = GATE == GATE_SCALAR ? *reinterpret_cast<const f32x4*>(c.ed + 16 * R + 4 * lg)
-                                             : f32x4{1.f, 1.f, 1.f, 1.f};
+          for (int g = 0; g < CG; ++g) d[g] = O::mma1(d[g], tf[R * (R + 1) / 2 + m], Rb[g][m]);
 #pragma unroll
         for (int g = 0; g < CG; ++g) {
           db_prev[g][R] = O::cvt(d[g]);
-          Ds[g][R] = GATE == GATE_SCALAR ? O::cvt(d[g] * ed) : db_prev[g][R];
+          Ds[g][R] = GATE == GATE_SCALAR ? O::cvt(d[g] * ed[R]) : db_prev[g][R];
         }
       }
-      // S' = e^{g_63} S + K^T diag(e^{g_63 - g}) Delta
-      const float gam = GATE == GATE_SCALAR ? c.gam[0] : 1.f;
+
+      // stages U(tp): S' = e^{g_63} S + K^T diag(e^{g_63 - g}) Delta, two 16-row tiles each
 #pragma unroll
-      for (int t = 0; t < DKT; ++t) {
-        const frag a0 = O::ld_tr(c.K, LDK, 0, 16 * t, lr, lg), a1 = O::ld_tr(c.K, LDK, 16, 16 * t, lr, lg);
-        const frag a2 = O::ld_tr(c.K, LDK, 32, 16 * t, lr, lg), a3 = O::ld_tr(c.K, LDK, 48, 16 * t, lr, lg);
+      for (int tp = 0; tp < DKT / 2; ++tp) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (tp + 1 < DKT / 2) load_kt((tp + 1) & 1, tp + 1);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int g = 0; g < CG; ++g) {
-          f32x4 acc = S[g][t];
-          if constexpr (GATE == GATE_SCALAR) acc = acc * gam;
-          acc = O::mma2(acc, a0, a1, Ds[g][0], Ds[g][1]);
-          S[g][t] = O::mma2(acc, a2, a3, Ds[g][2], Ds[g][3]);
+        for (int h = 0; h < 2; ++h) {
+          const int t = 2 * tp + h;
+#pragma unroll
+          for (int g = 0; g < CG; ++g) {
+            f32x4 acc = S[g][t];
+            if constexpr (GATE == GATE_SCALAR) acc = acc * gam;
+            acc = O::mma2(acc, ktf[tp & 1][4 * h], ktf[tp & 1][4 * h + 1], Ds[g][0], Ds[g][1]);
+            S[g][t] = O::mma2(acc, ktf[tp & 1][4 * h + 2], ktf[tp & 1][4 * h + 3], Ds[g][2], Ds[g][3]);
+          }
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
       __syncthreads();                          // next chunk's tiles and this chunk's P in place
     }
-    if (nchunks > 0) put_output(nchunks - 1);
+    // output of the last chunk
+    if (nchunks > 0) {
+      const T* sP = p_tile(nchunks - 1);
+      const uint32_t so = static_cast<uint32_t>((nchunks - 1) * CH * H * dv * ESZ);
+#pragma unroll
+      for (int R = 0; R < 4; ++R) {
+        f32x4 op[CG];
+#pragma unroll
+        for (int g = 0; g < CG; ++g) op[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const T* pr = sP + (16 * R + lr) * LCP + 4 * lg;
+#pragma unroll
+        for (int J = 0; J <= R; ++J) {
+          const frag p0 = O::ld(pr + 16 * J);
+#pragma unroll
+          for (int g = 0; g < CG; ++g) op[g] = O::mma1(op[g], db_prev[g][J], p0);
+        }
+#pragma unroll
+        for (int g = 0; g < CG; ++g) {
+          const f32x4 ov = GATE == GATE_SCALAR ? oq_prev[g][R] * eo_prev[R] + op[g] : oq_prev[g][R] + op[g];
+          buf_store8(__builtin_bit_cast(u32x2, to_bf16x4(ov)), ro, vo[R][g], so);
+        }
+      }
+    }
     if (p.S_T) {
 #pragma unroll
       for (int g = 0; g < CG; ++g)
@@ -351,37 +456,42 @@ __global__ __launch_bounds__((NCH + NHW) * 64) void chunk_state_pipe_kernel(Chun
 
     for (int64_t n = 0; n < nchunks; ++n) {
       const Tiles c = tiles(n);
+      // this helper's share of P of chunk n into copy n % 2 (copy n % 2 was last
+      // read by the chain waves in the previous step, before the opening barrier)
+      T* sP = p_tile(n);
+      // rows 16R.. of P for R = cw, cw + NHW, ..: the rows of q are read once per row block
+      for (int R = cw; R < 4; R += NHW) {
+        frag qf[DK / 16];
+#pragma unroll
+        for (int kb = 0; kb < DK / 32; ++kb) {
+          qf[2 * kb] = O::ld(c.Q + (16 * R + lr) * LDQ + 32 * kb + 4 * lg);
+          qf[2 * kb + 1] = O::ld(c.Q + (16 * R + lr) * LDQ + 32 * kb + 4 * lg + 16);
+        }
+        const int r = 16 * R + lr;
+        const float gr = c.g[r];
+        for (int J = 0; J <= R; ++J) {
+          // (P_RJ)^T = K_J Q_R^T: lane holds P[16R + lr][16J + 4lg + s], four adjacent columns
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kb = 0; kb < DK / 32; ++kb) {
+            const T* kr = c.K + (16 * J + lr) * LDK + 32 * kb + 4 * lg;
+            acc = O::mma2(acc, O::ld(kr), O::ld(kr + 16), qf[2 * kb], qf[2 * kb + 1]);
+          }
+          const f32x4 gj = *reinterpret_cast<const f32x4*>(c.g + 16 * J + 4 * lg);
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            float val = acc[s];
+            if constexpr (GATE == GATE_SCALAR) val *= __expf(gr - gj[s]);
+            acc[s] = (R == J && lr < 4 * lg + s) ? 0.f : val;
+          }
+          *reinterpret_cast<frag*>(sP + r * LCP + 16 * J + 4 * lg) = O::cvt(acc);
+        }
+      }
       // next chunk into the other LDS copy (last read before this step's opening
       // barrier), loads of the one after
       if (n + 1 < nchunks) {
         store_chunk(smem + ((n + 1) & 1) * L::BUF);
         if (n + 2 < nchunks) prefetch(n + 2);
-      }
-      // this helper's share of P of chunk n into copy n % 2 (copy n % 2 was last
-      // read by the chain waves in the previous step, before the opening barrier)
-      T* sP = p_tile(n);
-      const int lo = 10 * cw / NHW, hi = 10 * (cw + 1) / NHW;
-      for (int u = lo; u < hi; ++u) {
-        int R, J;
-        tri_block(u, R, J);
-        // (P_RJ)^T = K_J Q_R^T: lane holds P[16R + lr][16J + 4lg + s], four adjacent columns
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < DK / 32; ++kb) {
-          const int k0 = 32 * kb + 4 * lg;
-          acc = O::mma2(acc, O::ld(c.K + (16 * J + lr) * LDK + k0), O::ld(c.K + (16 * J + lr) * LDK + k0 + 16),
-                        O::ld(c.Q + (16 * R + lr) * LDQ + k0), O::ld(c.Q + (16 * R + lr) * LDQ + k0 + 16));
-        }
-        const int r = 16 * R + lr;
-        const float gr = c.g[r];
-        const f32x4 gj = *reinterpret_cast<const f32x4*>(c.g + 16 * J + 4 * lg);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          float val = acc[s];
-          if constexpr (GATE == GATE_SCALAR) val *= __expf(gr - gj[s]);
-          acc[s] = (R == J && lr < 4 * lg + s) ? 0.f : val;
-        }
-        *reinterpret_cast<frag*>(sP + r * LCP + 16 * J + 4 * lg) = O::cvt(acc);
       }
       __syncthreads();                          // next chunk's tiles and this chunk's P in place
     }
@@ -401,8 +511,9 @@ template <int GATE, int DK>
 static hipError_t launch_pipe_dk(const ChunkParams& p, hipStream_t stream) {
   // 64 columns per workgroup when that still gives one workgroup per CU, else 32.
   // Measured on the gated workload (state pass): 4 chain waves of 16 columns with 4
-  // helpers 364 us; 2 chain waves of 32 columns with 4 helpers 378 us; with 2
-  // helpers 419 and 416 us.
+  // helpers is fastest; 2 chain waves of 32 columns (2 or 4 helpers) and 4 chain
+  // waves with 2 helpers were 8-50% slower (32-column chain waves run out of
+  // registers).
   if (p.B * p.H * (p.d_v / 64) >= 256) return launch_pipe_t<GATE, DK, 4, 1, 4>(p, stream);
   return launch_pipe_t<GATE, DK, 2, 1, 2>(p, stream);
 }
