@@ -68,8 +68,12 @@ constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
 //   P region: block u holds P_RJ of the masked score matrix (lower triangular;
 //             written only where the state pass reads it: per-channel gate and
 //             fp32 I/O);
-// then six fp32 rows of 64 per-row factors (no gate / scalar gate): beta,
-// e^{g_read}, e^{g}, e^{g_63 - g}, e^{g_63}, g.
+// then six fp32 rows of 64 factors: with no gate or a scalar gate the per-row
+// beta, e^{g_read}, e^{g}, e^{g_63 - g}, e^{g_63}, g; with a per-channel gate
+// beta (row 0) and the per-channel decay e^{g_63} of the chunk (from row 1 on,
+// d_k values).  With bf16 I/O and a per-channel gate the record goes on with the
+// three decayed operands of the state pass, each row-major [64][d_k] in bf16:
+// k e^{g_read}, q e^{g}, k e^{g_63 - g} (every factor is at most 1).
 template <int ESZ>
 struct WsRec {
   static constexpr int BLK = 256;                        // elements per 16x16 block
@@ -78,11 +82,17 @@ struct WsRec {
   static constexpr uint32_t F_OFF = 20 * BLK * ESZ;
   static constexpr int NF = 6;
   static constexpr uint32_t BYTES = F_OFF + NF * CH * 4;
+  static constexpr uint32_t X_OFF = BYTES;               // decayed operands (bf16, per-channel gate)
   // byte offset of element (a, b) of block (R, J)
   static __device__ __forceinline__ uint32_t at(int R, int J, int a, int b) {
     return static_cast<uint32_t>(((R * (R + 1) / 2 + J) * BLK + a * 16 + b) * ESZ);
   }
 };
+
+// Bytes of one record for the I/O type, gate and d_k.
+__host__ __device__ constexpr uint32_t rec_bytes(int io, int gate, int dk) {
+  return io == IO_BF16 ? WsRec<2>::BYTES + (gate == GATE_CHANNEL ? 3u * CH * dk * 2u : 0u) : WsRec<4>::BYTES;
+}
 
 // Block (R, J), J <= R, of the ten-block order above.
 __device__ __forceinline__ void tri_block(int u, int& R, int& J) {

@@ -155,6 +155,7 @@ __global__ __launch_bounds__(NW * 64) void chunk_fwd_kernel(ChunkParams p, int n
                               GATE == GATE_NONE ? 0u : span * (GATE == GATE_CHANNEL ? DK : 1) * ESZ);
   const rsrc_t rw = make_rsrc(static_cast<const char*>(p.ws) + bh * nchunks * W::BYTES,
                               static_cast<uint32_t>(nchunks * W::BYTES));
+  static_assert(IO == IO_F32, "bf16 I/O runs the chain/helper kernel (chunk_state.hip)");
   // per-thread byte offsets within a chunk (the chunk start goes in the scalar offset)
   uint32_t offk[KV], offv[VV];
 #pragma unroll
@@ -452,42 +453,18 @@ static hipError_t launch_chunk_t(const ChunkParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int IO, int GATE, int DK>
-static hipError_t launch_chunk_dk(const ChunkParams& p, hipStream_t stream) {
-  if constexpr (IO == IO_F32) {
-    return launch_chunk_t<IO, GATE, DK, 2>(p, stream);
-  } else {
-    // Four waves (64 columns per workgroup) when that still gives at least one
-    // workgroup per CU, otherwise two waves (32 columns) to fill the 256 CUs.
-    const int64_t wg4 = p.B * p.H * (p.d_v / 64);
-    if (wg4 >= 256) return launch_chunk_t<IO, GATE, DK, 4>(p, stream);
-    return launch_chunk_t<IO, GATE, DK, 2>(p, stream);
-  }
-}
-
 template <int IO, int GATE>
 static hipError_t launch_chunk_g(const ChunkParams& p, hipStream_t stream) {
-  if (p.d_k == 128) {
-    if constexpr (IO == IO_F32) {
-      return hipErrorInvalidValue;   // fp32 I/O: d_k = 64 only (LDS budget)
-    } else {
-      return launch_chunk_dk<IO, GATE, 128>(p, stream);
-    }
-  }
-  if (p.d_k == 64) return launch_chunk_dk<IO, GATE, 64>(p, stream);
+  // fp32 I/O: d_k = 64 only (LDS budget); two waves, 32 columns per workgroup
+  if (p.d_k == 64) return launch_chunk_t<IO, GATE, 64, 2>(p, stream);
   return hipErrorInvalidValue;
 }
 
-template <int IO>
-static hipError_t launch_chunk_io(const ChunkParams& p, hipStream_t stream) {
-  if constexpr (IO == IO_F32) {
-    switch (p.gate) {
-      case GATE_NONE: return launch_chunk_g<IO, GATE_NONE>(p, stream);
-      case GATE_SCALAR: return launch_chunk_g<IO, GATE_SCALAR>(p, stream);
-      case GATE_CHANNEL: return launch_chunk_g<IO, GATE_CHANNEL>(p, stream);
-    }
-  } else {
-    if (p.gate == GATE_CHANNEL) return launch_chunk_g<IO, GATE_CHANNEL>(p, stream);
+static hipError_t launch_chunk_f32(const ChunkParams& p, hipStream_t stream) {
+  switch (p.gate) {
+    case GATE_NONE: return launch_chunk_g<IO_F32, GATE_NONE>(p, stream);
+    case GATE_SCALAR: return launch_chunk_g<IO_F32, GATE_SCALAR>(p, stream);
+    case GATE_CHANNEL: return launch_chunk_g<IO_F32, GATE_CHANNEL>(p, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -496,14 +473,14 @@ hipError_t launch_chunk_fwd(const ChunkParams& p, hipStream_t stream) {
   if (p.B * p.H == 0) return hipSuccess;
   hipError_t e = launch_chunk_prep(p, stream);
   if (e != hipSuccess) return e;
-  // bf16 without a per-channel gate: chain and helper waves (chunk_state.hip)
-  if (p.io == IO_BF16 && p.gate != GATE_CHANNEL) return launch_chunk_state_pipe(p, stream);
-  return p.io == IO_BF16 ? launch_chunk_io<IO_BF16>(p, stream) : launch_chunk_io<IO_F32>(p, stream);
+  // bf16 I/O: chain and helper waves (chunk_state.hip); fp32 I/O: this file's kernel
+  if (p.io == IO_BF16) return launch_chunk_state_pipe(p, stream);
+  return launch_chunk_f32(p, stream);
 }
 
-size_t chunk_workspace_bytes(int64_t B, int64_t T, int64_t H, int io) {
+size_t chunk_workspace_bytes(int64_t B, int64_t T, int64_t H, int io, int gate, int d_k) {
   const int64_t nchunks = (T + CH - 1) / CH;
-  return static_cast<size_t>(B * H * nchunks) * (io == IO_BF16 ? WsRec<2>::BYTES : WsRec<4>::BYTES);
+  return static_cast<size_t>(B * H * nchunks) * rec_bytes(io, gate, d_k);
 }
 
 }  // namespace gdr

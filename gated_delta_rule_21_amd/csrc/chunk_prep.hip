@@ -20,7 +20,10 @@
 // transpose load, and (per-channel gate, fp32 I/O) the ten blocks of P.  With
 // bf16 I/O and no per-channel gate the state pass forms P itself from the q and
 // k tiles it holds anyway, which saves reading q here and a round trip of P
-// through memory.
+// through memory.  With bf16 I/O and a per-channel gate the record also carries
+// the state pass's decayed operands k e^{g_read}, q e^{g}, k e^{g_63 - g}, beta and
+// the chunk's per-channel decay e^{g_63}: they are formed once per (sequence,
+// head, chunk) here rather than once per d_v tile there.
 //
 // No gate / scalar gate (chunk_prep_reg_kernel): one wave per chunk, every
 // operand in registers.  The Gram sums run over d_k, so k and q are loaded as
@@ -127,7 +130,7 @@ __global__ __launch_bounds__(256) void chunk_prep_lds_kernel(ChunkParams p, int6
   const int lane = tid & 63;
   const int lr = lane & 15;
   const int lg = lane >> 4;
-  char* rec = static_cast<char*>(p.ws) + (bh * nchunks + n) * W::BYTES;
+  char* rec = static_cast<char*>(p.ws) + (bh * nchunks + n) * rec_bytes(IO, GATE, DK);
 
   // The chunk's rows through buffers whose range ends at the sequence's last
   // token: rows of a ragged last chunk read as zero.
@@ -232,18 +235,35 @@ __global__ __launch_bounds__(256) void chunk_prep_lds_kernel(ChunkParams p, int6
       const f32x4 qq = O::f32(O::ld(sQ + r * LDK + i0));
       const float be = sBc[r];
       f32x4 xk, xq, y;
+      f32x4 sk, sq, sd;   // state-pass operands (bf16 I/O): k e^{g_read}, q e^{g}, k e^{g_63 - g}
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int i = i0 + j;
-        const float g = sG[r * DK + i], gR = sG[16 * R * DK + i];
+        const float g = sG[r * DK + i], gR = sG[16 * R * DK + i], gC = sG[(CH - 1) * DK + i];
         const float gread = p.literal ? (r > 0 ? sG[(r - 1) * DK + i] : 0.f) : g;
         xk[j] = be * kk[j] * __expf(gread - gR);
         xq[j] = qq[j] * __expf(g - gR);
         y[j] = kk[j] * __expf(gR - g);
+        if constexpr (IO == IO_BF16) {
+          sk[j] = kk[j] * __expf(gread);
+          sq[j] = qq[j] * __expf(g);
+          sd[j] = kk[j] * __expf(gC - g);
+        }
       }
       *reinterpret_cast<typename O::frag*>(sK + r * LDK + i0) = O::cvt(xk);
       *reinterpret_cast<typename O::frag*>(sQ + r * LDK + i0) = O::cvt(xq);
       *reinterpret_cast<typename O::frag*>(sY + r * LDK + i0) = O::cvt(y);
+      if constexpr (IO == IO_BF16) {
+        char* x = rec + W::X_OFF + (r * DK + i0) * 2;
+        *reinterpret_cast<u32x2*>(x) = __builtin_bit_cast(u32x2, to_bf16x4(sk));
+        *reinterpret_cast<u32x2*>(x + CH * DK * 2) = __builtin_bit_cast(u32x2, to_bf16x4(sq));
+        *reinterpret_cast<u32x2*>(x + 2 * CH * DK * 2) = __builtin_bit_cast(u32x2, to_bf16x4(sd));
+      }
+    }
+    if constexpr (IO == IO_BF16) {   // factor rows of the state pass: beta, then e^{g_63} per channel
+      float* f = reinterpret_cast<float*>(rec + W::F_OFF);
+      if (tid < CH) f[tid] = sBc[tid];
+      for (int i = tid; i < DK; i += NT) f[CH + i] = __expf(sG[(CH - 1) * DK + i]);
     }
     __syncthreads();
   }
@@ -376,7 +396,7 @@ __global__ __launch_bounds__(256) void chunk_prep_reg_kernel(ChunkParams p, int6
   const int64_t bb = task / (p.H * nchunks);
   const int64_t bh = bb * p.H + hh;
   const int H = static_cast<int>(p.H);
-  char* rec = static_cast<char*>(p.ws) + (bh * nchunks + n) * W::BYTES;
+  char* rec = static_cast<char*>(p.ws) + (bh * nchunks + n) * rec_bytes(IO, GATE, DK);
   float* sB = sfac[wave];
   float* sG = sB + CH;
   float* sGr = sB + 2 * CH;

@@ -44,7 +44,7 @@ namespace gdr {
 // is 2 or 6 (mod 8) dwords long, transpose reads (ds_read_b64_tr_b16) at 168 B/clk
 // when it is 8 (mod 32) dwords and at 128 B/clk for most other lengths; the k
 // tile is read both ways and takes 6 (mod 32) dwords (121 and 128 B/clk).
-template <int DK, int DVT_>
+template <int DK, int DVT_, bool CHAN>
 struct PipeLayout {
   static constexpr int LDK = DK + 12;                    // k: row and transpose reads (8-byte aligned rows)
   static constexpr int LDQ = DK + 4;                     // q: row reads (8-byte aligned rows)
@@ -61,8 +61,9 @@ struct PipeLayout {
   static constexpr size_t B_Q = B_K + KB;
   static constexpr size_t B_V = B_Q + QB;
   static constexpr size_t B_T = B_V + VB;                // T^T (the ten blocks on or above the diagonal)
-  static constexpr size_t B_F = B_T + TB;                // beta, e^{g_read}, e^{g}, e^{g_63 - g}, e^{g_63}, g
-  static constexpr size_t BUF = B_F + 6 * CH * 4;
+  static constexpr size_t B_F = B_T + TB;                // factor rows of the workspace record
+  static constexpr size_t B_KD = B_F + 6 * CH * 4;       // per-channel gate: k e^{g_63 - g} (transpose reads)
+  static constexpr size_t BUF = B_KD + (CHAN ? KB : 0);
   // P of chunk n in copy n % 2
   static constexpr size_t PB = size_t(CH) * LCP * 2;
   static constexpr size_t OFF_P = 2 * BUF;
@@ -76,8 +77,10 @@ __global__ __launch_bounds__((NCH + NHW) * 64) void chunk_state_pipe_kernel(Chun
   typedef bf16x4 frag;
   typedef uint16_t elem;
   constexpr int DVT = 16 * CG * NCH;            // columns per workgroup
-  typedef PipeLayout<DK, DVT> L;
+  constexpr bool CHAN = GATE == GATE_CHANNEL;
+  typedef PipeLayout<DK, DVT, CHAN> L;
   typedef WsRec<2> W;
+  constexpr uint32_t RB = rec_bytes(IO_BF16, GATE, DK);   // bytes per chunk record
   constexpr int ESZ = 2, EPV = 8;
   constexpr int NH = NHW * 64;                   // helper threads
   constexpr int DKT = DK / 16;
@@ -89,7 +92,6 @@ __global__ __launch_bounds__((NCH + NHW) * 64) void chunk_state_pipe_kernel(Chun
   constexpr int HT = (10 * PPB + NH - 1) / NH;   // ... of the T blocks
   constexpr int NFP = W::NF * CH * 4 / 16;       // pieces of the factor rows (helper threads 0..NFP-1)
   static_assert(HK * NH == CH * KROW && HV * NH == CH * VROW && HV >= 1 && NFP <= NH, "tile split");
-  static_assert(GATE != GATE_CHANNEL, "per-channel gate uses chunk_fwd_kernel");
   static_assert(L::TOTAL <= 163840, "LDS budget");
 
   __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
@@ -125,21 +127,30 @@ __global__ __launch_bounds__((NCH + NHW) * 64) void chunk_state_pipe_kernel(Chun
   const rsrc_t rq = make_rsrc(static_cast<const elem*>(p.q) + row0 * DK, span * DK * ESZ);
   const rsrc_t rv = make_rsrc(static_cast<const elem*>(p.v) + row0 * dv, span * dv * ESZ);
   const rsrc_t ro = make_rsrc(static_cast<const elem*>(p.o) + row0 * dv, span * dv * ESZ);
-  const rsrc_t rw = make_rsrc(static_cast<const char*>(p.ws) + bh * nchunks * W::BYTES,
-                              static_cast<uint32_t>(nchunks * W::BYTES));
+  const rsrc_t rw = make_rsrc(static_cast<const char*>(p.ws) + bh * nchunks * RB,
+                              static_cast<uint32_t>(nchunks * RB));
 
   // ---- helpers: loads one chunk ahead in registers, stores into an LDS copy ----------
-  u32x4 pk[HK], pq[HK], pv[HV], pt[HT], pf;
+  // Per-channel gate: k, q and k e^{g_63 - g} come decayed from the record (row-major
+  // [64][d_k] each), and so does P, which is loaded a step after the tiles.
+  u32x4 pk[HK], pq[HK], pkd[CHAN ? HK : 1], pv[HV], pt[HT], pp[CHAN ? HT : 1], pf;
   auto prefetch = [&](int64_t m) __attribute__((always_inline)) {
     const uint32_t sk = static_cast<uint32_t>(m * CH * H * DK * ESZ);
     const uint32_t sv = static_cast<uint32_t>(m * CH * H * dv * ESZ);
-    const uint32_t sw = static_cast<uint32_t>(m * W::BYTES);
+    const uint32_t sw = static_cast<uint32_t>(m * RB);
 #pragma unroll
     for (int v = 0; v < HK; ++v) {
       const int seg = ht + v * NH;
-      const uint32_t off = static_cast<uint32_t>(((seg / KROW) * H * DK + (seg % KROW) * EPV) * ESZ);
-      pk[v] = buf_load16(rk, off, sk);
-      pq[v] = buf_load16(rq, off, sk);
+      if constexpr (CHAN) {
+        const uint32_t off = W::X_OFF + static_cast<uint32_t>(((seg / KROW) * DK + (seg % KROW) * EPV) * ESZ);
+        pk[v] = buf_load16(rw, off, sw);
+        pq[v] = buf_load16(rw, off + CH * DK * ESZ, sw);
+        pkd[v] = buf_load16(rw, off + 2 * CH * DK * ESZ, sw);
+      } else {
+        const uint32_t off = static_cast<uint32_t>(((seg / KROW) * H * DK + (seg % KROW) * EPV) * ESZ);
+        pk[v] = buf_load16(rk, off, sk);
+        pq[v] = buf_load16(rq, off, sk);
+      }
     }
 #pragma unroll
     for (int v = 0; v < HV; ++v) {
@@ -152,6 +163,28 @@ __global__ __launch_bounds__((NCH + NHW) * 64) void chunk_state_pipe_kernel(Chun
       if (pc < 10 * PPB) pt[v] = buf_load16(rw, W::T_OFF + static_cast<uint32_t>(pc * 16), sw);
     }
     if (ht < NFP) pf = buf_load16(rw, W::F_OFF + static_cast<uint32_t>(ht * 16), sw);
+  };
+  auto prefetch_p = [&](int64_t m) __attribute__((always_inline)) {
+    const uint32_t sw = static_cast<uint32_t>(m * RB);
+#pragma unroll
+    for (int v = 0; v < HT; ++v) {
+      const int pc = ht + v * NH;
+      if (pc < 10 * PPB) pp[v] = buf_load16(rw, W::P_OFF + static_cast<uint32_t>(pc * 16), sw);
+    }
+  };
+  auto store_p = [&](T* sP) __attribute__((always_inline)) {
+#pragma unroll
+    for (int v = 0; v < HT; ++v) {
+      const int pc = ht + v * NH;
+      if (pc < 10 * PPB) {               // block u holds P_RJ: rows 16R.., columns 16J.. of P
+        int R, J;
+        tri_block(pc / PPB, R, J);
+        const int a = (pc % PPB) / PPR, b0 = (pc % PPR) * EPV;
+        u32x2* d2 = reinterpret_cast<u32x2*>(sP + (16 * R + a) * LCP + 16 * J + b0);   // 8-byte aligned rows
+        d2[0] = u32x2{pp[v][0], pp[v][1]};
+        d2[1] = u32x2{pp[v][2], pp[v][3]};
+      }
+    }
   };
   auto store_chunk = [&](char* base) __attribute__((always_inline)) {
     T* dK = reinterpret_cast<T*>(base + L::B_K);
@@ -167,6 +200,11 @@ __global__ __launch_bounds__((NCH + NHW) * 64) void chunk_state_pipe_kernel(Chun
       u32x2* q2 = reinterpret_cast<u32x2*>(dQ + row * LDQ + c);
       q2[0] = u32x2{pq[v][0], pq[v][1]};
       q2[1] = u32x2{pq[v][2], pq[v][3]};
+      if constexpr (CHAN) {
+        u32x2* d2 = reinterpret_cast<u32x2*>(reinterpret_cast<T*>(base + L::B_KD) + row * LDK + c);
+        d2[0] = u32x2{pkd[v][0], pkd[v][1]};
+        d2[1] = u32x2{pkd[v][2], pkd[v][3]};
+      }
     }
 #pragma unroll
     for (int v = 0; v < HV; ++v) {
@@ -188,14 +226,16 @@ __global__ __launch_bounds__((NCH + NHW) * 64) void chunk_state_pipe_kernel(Chun
 
   // A chunk's LDS copy.
   struct Tiles {
-    const T *K, *Q, *V, *Tt;
-    const float *beta, *er, *eo, *ed, *gam, *g;   // per-row factors
+    const T *K, *Q, *V, *Tt, *KD;
+    // per-row factors; per-channel gate: beta, then e^{g_63} per channel from the row of er on
+    const float *beta, *er, *eo, *ed, *gam, *g;
   };
   auto tiles = [&](int64_t n) __attribute__((always_inline)) {
     const char* cur = smem + (n & 1) * L::BUF;
     const float* f = reinterpret_cast<const float*>(cur + L::B_F);
     return Tiles{reinterpret_cast<const T*>(cur + L::B_K), reinterpret_cast<const T*>(cur + L::B_Q),
                  reinterpret_cast<const T*>(cur + L::B_V), reinterpret_cast<const T*>(cur + L::B_T),
+                 reinterpret_cast<const T*>(cur + (CHAN ? L::B_KD : L::B_K)),
                  f, f + CH, f + 2 * CH, f + 3 * CH, f + 4 * CH, f + 5 * CH};
   };
 
@@ -360,11 +400,15 @@ __global__ __launch_bounds__((NCH + NHW) * 64) void chunk_state_pipe_kernel(Chun
 
       // stage Delta: Delta_R = sum_{m <= R} T_Rm R_m; first rows of K^T for the update
       frag ktf[2][8];                           // K^T fragments of two 16-row tiles, double-buffered
+      f32x4 gc[2][2];                           // per-channel gate: e^{g_63} of those rows of S
       auto load_kt = [&](int b, int tp) __attribute__((always_inline)) {
+        if constexpr (CHAN)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) gc[b][h] = *reinterpret_cast<const f32x4*>(c.er + 16 * (2 * tp + h) + 4 * lg);
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) ktf[b][4 * h + i] = O::ld_tr(c.K, LDK, 16 * i, 16 * (2 * tp + h), lr, lg);
+          for (int i = 0; i < 4; ++i) ktf[b][4 * h + i] = O::ld_tr(c.KD, LDK, 16 * i, 16 * (2 * tp + h), lr, lg);
       };
       __builtin_amdgcn_sched_barrier(0);
       load_kt(0, 0);
@@ -405,6 +449,7 @@ __global__ __launch_bounds__((NCH + NHW) * 64) void chunk_state_pipe_kernel(Chun
           for (int g = 0; g < CG; ++g) {
             f32x4 acc = S[g][t];
             if constexpr (GATE == GATE_SCALAR) acc = acc * gam;
+            if constexpr (CHAN) acc = acc * gc[tp & 1][h];
             acc = O::mma2(acc, ktf[tp & 1][4 * h], ktf[tp & 1][4 * h + 1], Ds[g][0], Ds[g][1]);
             S[g][t] = O::mma2(acc, ktf[tp & 1][4 * h + 2], ktf[tp & 1][4 * h + 3], Ds[g][2], Ds[g][3]);
           }
@@ -449,6 +494,7 @@ __global__ __launch_bounds__((NCH + NHW) * 64) void chunk_state_pipe_kernel(Chun
     // ---- helper waves -------------------------------------------------------------------
     if (nchunks > 0) {
       prefetch(0);
+      if constexpr (CHAN) prefetch_p(0);
       store_chunk(smem);
       if (nchunks > 1) prefetch(1);
     }
@@ -459,8 +505,12 @@ __global__ __launch_bounds__((NCH + NHW) * 64) void chunk_state_pipe_kernel(Chun
       // this helper's share of P of chunk n into copy n % 2 (copy n % 2 was last
       // read by the chain waves in the previous step, before the opening barrier)
       T* sP = p_tile(n);
+      if constexpr (CHAN) {                     // P of chunk n from the record
+        store_p(sP);
+        if (n + 1 < nchunks) prefetch_p(n + 1);
+      }
       // rows 16R.. of P for R = cw, cw + NHW, ..: the rows of q are read once per row block
-      for (int R = cw; R < 4; R += NHW) {
+      for (int R = cw; R < (CHAN ? 0 : 4); R += NHW) {
         frag qf[DK / 16];
 #pragma unroll
         for (int kb = 0; kb < DK / 32; ++kb) {
@@ -509,13 +559,18 @@ static hipError_t launch_pipe_t(const ChunkParams& p, hipStream_t stream) {
 
 template <int GATE, int DK>
 static hipError_t launch_pipe_dk(const ChunkParams& p, hipStream_t stream) {
-  // 64 columns per workgroup when that still gives one workgroup per CU, else 32.
-  // Measured on the gated workload (state pass): 4 chain waves of 16 columns with 4
-  // helpers is fastest; 2 chain waves of 32 columns (2 or 4 helpers) and 4 chain
-  // waves with 2 helpers were 8-50% slower (32-column chain waves run out of
-  // registers).
-  if (p.B * p.H * (p.d_v / 64) >= 256) return launch_pipe_t<GATE, DK, 4, 1, 4>(p, stream);
-  return launch_pipe_t<GATE, DK, 2, 1, 2>(p, stream);
+  if constexpr (GATE == GATE_CHANNEL) {
+    // per-channel gate: the third operand tile leaves LDS room for 32 columns only
+    return launch_pipe_t<GATE, DK, 2, 1, 2>(p, stream);
+  } else {
+    // 64 columns per workgroup when that still gives one workgroup per CU, else 32.
+    // Measured on the gated workload (state pass): 4 chain waves of 16 columns with
+    // 4 helpers is fastest; 2 chain waves of 32 columns (2 or 4 helpers) and 4
+    // chain waves with 2 helpers were 8-50% slower (32-column chain waves run out
+    // of registers).
+    if (p.B * p.H * (p.d_v / 64) >= 256) return launch_pipe_t<GATE, DK, 4, 1, 4>(p, stream);
+    return launch_pipe_t<GATE, DK, 2, 1, 2>(p, stream);
+  }
 }
 
 template <int GATE>
@@ -529,6 +584,7 @@ hipError_t launch_chunk_state_pipe(const ChunkParams& p, hipStream_t stream) {
   if (p.io != IO_BF16) return hipErrorInvalidValue;
   if (p.gate == GATE_NONE) return launch_pipe_g<GATE_NONE>(p, stream);
   if (p.gate == GATE_SCALAR) return launch_pipe_g<GATE_SCALAR>(p, stream);
+  if (p.gate == GATE_CHANNEL) return launch_pipe_g<GATE_CHANNEL>(p, stream);
   return hipErrorInvalidValue;
 }
 

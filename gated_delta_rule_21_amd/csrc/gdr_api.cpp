@@ -77,7 +77,7 @@ gdr_status check_desc(const gdr_desc* d, bool decode) {
     return fail(GDR_ERR_UNSUPPORTED, "T*H*max(d_k,d_v)*elem_size = %lld bytes exceeds 2^31 - 1 per sequence",
                 (long long)seq_bytes);
   // ... and one sequence's workspace records the same way
-  if (!decode && static_cast<int64_t>(gdr::chunk_workspace_bytes(1, d->T, 1, d->io)) > INT32_MAX)
+  if (!decode && static_cast<int64_t>(gdr::chunk_workspace_bytes(1, d->T, 1, d->io, d->gate, static_cast<int>(d->d_k))) > INT32_MAX)
     return fail(GDR_ERR_UNSUPPORTED, "T = %lld: the per-sequence workspace exceeds 2^31 - 1 bytes", (long long)d->T);
   return GDR_OK;
 }
@@ -124,7 +124,7 @@ gdr_status gdr_chunk_fwd_workspace_size(const gdr_desc* d, size_t* bytes) {
     *bytes = 0;
     gdr_status st = check_desc(d, false);
     if (st != GDR_OK) return st;
-    *bytes = gdr::chunk_workspace_bytes(d->B, d->T, d->H, d->io);
+    *bytes = gdr::chunk_workspace_bytes(d->B, d->T, d->H, d->io, d->gate, static_cast<int>(d->d_k));
     return GDR_OK;
   } catch (...) {
     return fail(GDR_ERR_INVALID_ARG, "internal error");
@@ -138,7 +138,7 @@ gdr_status gdr_chunk_fwd(const gdr_desc* d, const void* q, const void* k, const 
     g_last_error.clear();
     gdr_status st = check_desc(d, false);
     if (st != GDR_OK) return st;
-    const size_t ws_need = gdr::chunk_workspace_bytes(d->B, d->T, d->H, d->io);
+    const size_t ws_need = gdr::chunk_workspace_bytes(d->B, d->T, d->H, d->io, d->gate, static_cast<int>(d->d_k));
     const int64_t esz = d->io == GDR_BF16 ? 2 : 4;
     const int64_t ntok = d->B * d->T * d->H;
     const bool any = d->T > 0;

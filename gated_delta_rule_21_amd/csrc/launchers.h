@@ -29,7 +29,7 @@ struct ChunkParams {
   const float* S0;    // may be null (zero initial state)
   void* o;
   float* S_T;         // may be null (not written)
-  void* ws;           // per-chunk inverses T, B*H*ceil(T/64) tiles of 64x64 in the I/O dtype
+  void* ws;           // per-chunk records of the transform (chunk_workspace_bytes)
   int64_t B, T, H;
   int d_k, d_v;
   int io, gate, literal;
@@ -38,8 +38,9 @@ struct ChunkParams {
 hipError_t launch_decode_step(const DecodeParams& p, hipStream_t stream);
 // Per-chunk transform (T tiles into p.ws), then the state pass; one stream, in order.
 hipError_t launch_chunk_prep(const ChunkParams& p, hipStream_t stream);
-hipError_t launch_chunk_state_pipe(const ChunkParams& p, hipStream_t stream);   // bf16, no per-channel gate
+hipError_t launch_chunk_state_pipe(const ChunkParams& p, hipStream_t stream);   // bf16 I/O
 hipError_t launch_chunk_fwd(const ChunkParams& p, hipStream_t stream);
-size_t chunk_workspace_bytes(int64_t B, int64_t T, int64_t H, int io);
+// B*H*ceil(T/64) records of the per-chunk transform (see WsRec in chunk_common.h)
+size_t chunk_workspace_bytes(int64_t B, int64_t T, int64_t H, int io, int gate, int d_k);
 
 }  // namespace gdr

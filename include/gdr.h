@@ -94,9 +94,12 @@ typedef struct {
  * terms are that solve applied to the keys and values) and room for the
  * causally masked query-key score matrix, each as the ten 16 x 16 blocks of a
  * 64 x 64 triangle in the I/O dtype, plus six rows of 64 fp32 per-token gate
- * factors.  That is B * H * ceil(T / 64) * (5120 * elem + 1536) bytes (0 when
- * T == 0).  Returns the same errors as gdr_chunk_fwd's descriptor checks;
- * *bytes is 0 on error.
+ * factors.  With bf16 I/O and a per-channel gate each record also holds the
+ * chunk's three decayed key/query operands (64 x d_k bf16 each), formed once per
+ * chunk rather than once per d_v tile.  That is B * H * ceil(T / 64) *
+ * (5120 * elem + 1536) bytes, plus B * H * ceil(T / 64) * 384 * d_k bytes for
+ * bf16 with a per-channel gate (0 when T == 0).  Returns the same errors as
+ * gdr_chunk_fwd's descriptor checks; *bytes is 0 on error.
  */
 gdr_status gdr_chunk_fwd_workspace_size(const gdr_desc* desc, size_t* bytes);
 

@@ -75,6 +75,10 @@ def test_workspace_size(lib):
     rec = lambda esz: 2 * 10 * 256 * esz + 6 * 64 * 4    # ten 16x16 blocks of T and of P, six factor rows
     assert _ws_size(lib, _desc(B=2, T=130, H=3)) == (OK, 2 * 3 * 3 * rec(2))        # bf16, 3 chunks
     assert _ws_size(lib, _desc(io=0, d_k=64, T=64)) == (OK, 2 * 1 * rec(4))         # fp32, 1 chunk
+    # bf16 with a per-channel gate: the three decayed [64][d_k] operands follow each record
+    assert _ws_size(lib, _desc(gate=2, T=65)) == (OK, 2 * 2 * (rec(2) + 3 * 64 * 128 * 2))
+    assert _ws_size(lib, _desc(gate=2, d_k=64, T=64)) == (OK, 2 * (rec(2) + 3 * 64 * 64 * 2))
+    assert _ws_size(lib, _desc(gate=2, io=0, d_k=64, T=64)) == (OK, 2 * rec(4))     # fp32: no operands
     assert _ws_size(lib, _desc(T=0)) == (OK, 0)
     assert _ws_size(lib, None) == (INVALID, 0)
     assert _ws_size(lib, _desc(d_k=96)) == (UNSUPPORTED, 0)

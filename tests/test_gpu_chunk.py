@@ -121,7 +121,7 @@ def test_caller_workspace_reused_and_dirty():
     import torch
     from tests.gpu_util import dev, host
     import gated_delta_rule_21_amd as gdr
-    big = gdr.chunk_workspace_size(2, 260, 3, 128, 128, torch.bfloat16)
+    big = gdr.chunk_workspace_size(2, 260, 3, 128, 128, torch.bfloat16, "channel")
     ws = torch.full((big,), 0xFF, dtype=torch.uint8, device="cuda")
     for name, shape, gate, seed in (("ws1", (2, 260, 3, 128, 128), "channel", 47),
                                     ("ws2", (1, 70, 2, 64, 128), "scalar", 53)):
@@ -133,7 +133,7 @@ def test_caller_workspace_reused_and_dirty():
         check(f"{name} o", host(o), o_ref, TOL["bf16"])
         check(f"{name} S_T", host(S), S_ref, TOL["bf16"])
     with pytest.raises(gdr.GdrError):
-        inp = chunk_inputs(_wl("ws3", 2, 260, 4, 128, 128, gate="scalar", seed=59))   # needs more than `big`
+        inp = chunk_inputs(_wl("ws3", 2, 260, 4, 128, 128, gate="channel", seed=59))  # needs more than `big`
         gdr.chunk_fwd(*(dev(inp[n], "bf16") for n in ("q", "k", "v", "beta", "log_a")), None, workspace=ws)
 
 
