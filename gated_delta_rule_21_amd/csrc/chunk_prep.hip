@@ -41,9 +41,9 @@
 // accumulators, four elements per lane, one whole 16x16 block per instruction;
 // no LDS is used beyond 768 bytes of per-row factors.
 //
-// Per-channel gate (chunk_prep_lds_kernel): the decay sits inside the d_k
-// contraction, so decayed operands are built in LDS by a four-wave workgroup
-// per chunk; the factor e^{g_r - g_j} is split at the first row of each 16-row
+// Per-channel gate (chunk_prep_chan_kernel for bf16 I/O, chunk_prep_lds_kernel
+// for fp32 I/O): the decay sits inside the d_k contraction, so decayed operands
+// are built in LDS by a four-wave workgroup per chunk; the factor e^{g_r - g_j} is split at the first row of each 16-row
 // block (e^{g_r - g_16R} on the row operand, e^{g_16J - g_j} on the column
 // operand, e^{g_16R - g_16J} on the column operand of blocks below the
 // diagonal), so no operand carries more than 15 tokens of decay.  Wave R
@@ -130,7 +130,8 @@ __global__ __launch_bounds__(256) void chunk_prep_lds_kernel(ChunkParams p, int6
   const int lane = tid & 63;
   const int lr = lane & 15;
   const int lg = lane >> 4;
-  char* rec = static_cast<char*>(p.ws) + (bh * nchunks + n) * rec_bytes(IO, GATE, DK);
+  char* rec = static_cast<char*>(p.ws) + (bh * nchunks + n) * W::BYTES;
+  static_assert(IO == IO_F32 || GATE != GATE_CHANNEL, "bf16 per-channel gate: chunk_prep_chan_kernel");
 
   // The chunk's rows through buffers whose range ends at the sequence's last
   // token: rows of a ragged last chunk read as zero.
@@ -235,35 +236,18 @@ __global__ __launch_bounds__(256) void chunk_prep_lds_kernel(ChunkParams p, int6
       const f32x4 qq = O::f32(O::ld(sQ + r * LDK + i0));
       const float be = sBc[r];
       f32x4 xk, xq, y;
-      f32x4 sk, sq, sd;   // state-pass operands (bf16 I/O): k e^{g_read}, q e^{g}, k e^{g_63 - g}
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int i = i0 + j;
-        const float g = sG[r * DK + i], gR = sG[16 * R * DK + i], gC = sG[(CH - 1) * DK + i];
+        const float g = sG[r * DK + i], gR = sG[16 * R * DK + i];
         const float gread = p.literal ? (r > 0 ? sG[(r - 1) * DK + i] : 0.f) : g;
         xk[j] = be * kk[j] * __expf(gread - gR);
         xq[j] = qq[j] * __expf(g - gR);
         y[j] = kk[j] * __expf(gR - g);
-        if constexpr (IO == IO_BF16) {
-          sk[j] = kk[j] * __expf(gread);
-          sq[j] = qq[j] * __expf(g);
-          sd[j] = kk[j] * __expf(gC - g);
-        }
       }
       *reinterpret_cast<typename O::frag*>(sK + r * LDK + i0) = O::cvt(xk);
       *reinterpret_cast<typename O::frag*>(sQ + r * LDK + i0) = O::cvt(xq);
       *reinterpret_cast<typename O::frag*>(sY + r * LDK + i0) = O::cvt(y);
-      if constexpr (IO == IO_BF16) {
-        char* x = rec + W::X_OFF + (r * DK + i0) * 2;
-        *reinterpret_cast<u32x2*>(x) = __builtin_bit_cast(u32x2, to_bf16x4(sk));
-        *reinterpret_cast<u32x2*>(x + CH * DK * 2) = __builtin_bit_cast(u32x2, to_bf16x4(sq));
-        *reinterpret_cast<u32x2*>(x + 2 * CH * DK * 2) = __builtin_bit_cast(u32x2, to_bf16x4(sd));
-      }
-    }
-    if constexpr (IO == IO_BF16) {   // factor rows of the state pass: beta, then e^{g_63} per channel
-      float* f = reinterpret_cast<float*>(rec + W::F_OFF);
-      if (tid < CH) f[tid] = sBc[tid];
-      for (int i = tid; i < DK; i += NT) f[CH + i] = __expf(sG[(CH - 1) * DK + i]);
     }
     __syncthreads();
   }
@@ -362,6 +346,277 @@ __global__ __launch_bounds__(256) void chunk_prep_lds_kernel(ChunkParams p, int6
         *reinterpret_cast<const u32x4*>(sT + (16 * J + a) * LCH + 16 * R + b0);
     *reinterpret_cast<u32x4*>(rec + W::P_OFF + pc * 16) =
         *reinterpret_cast<const u32x4*>(sP + (16 * R + a) * LCH + 16 * J + b0);
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// Per-channel gate, bf16 I/O: one 256-thread workgroup per (sequence, head, chunk).
+//
+// Thread (cq, sg) owns channels 4cq..4cq+3 of the SL rows of segment sg.  It loads
+// its pieces of k, q and log a straight into registers (for each row the
+// threads of a segment read one contiguous stretch), runs the inclusive scan of
+// the gate down its rows in registers, and takes the totals of the segments
+// above it from LDS.  With g_16R the gate at the first row of the thread's
+// 16-row block, every factor it needs comes from three exponentials per element:
+//     a = e^{g - g_16R} <= 1,  b = e^{g_16R - g},  d = e^{g_63 - g} <= 1,
+// and e^{g_16R} once per channel: the split operands of the Gram and score blocks
+// (beta k e^{g_read - g_16R}, q a, k b) go to LDS, the state pass's operands
+// (k e^{g_read}, q e^{g}, k d) to the workspace record.  Then, as in
+// chunk_prep_lds_kernel, wave R inverts I + A_RR (fp32 MFMA), the blocks of A
+// below the diagonal are shared out and wave J walks down block column J of T;
+// the blocks of P are formed transposed and stored from the accumulators.  78 KB
+// of LDS: two workgroups per CU overlap each other's loads and barriers.
+// ---------------------------------------------------------------------------------
+template <int DK>
+struct ChanLayout {
+  static constexpr int LDK = DK + 4;                      // b64 row reads (row 2 mod 8 dwords)
+  static constexpr int LCH = CH + 8;                      // 16-byte aligned rows (T^T copied out in pieces)
+  static constexpr int LSC = 20;
+  static constexpr int NQ = DK / 4;                       // channel quads
+  static constexpr int NSG = 256 / NQ;                    // row segments
+  static constexpr int SL = CH / NSG;                     // rows per segment (8 or 4: inside one 16-row block)
+  static constexpr size_t RM = size_t(CH) * LDK * 2;
+  static constexpr size_t MM = size_t(CH) * LCH * 2;
+  static constexpr size_t OFF_K = 0;                      // beta k e^{g_read - g_16R}
+  static constexpr size_t OFF_Q = OFF_K + RM;             // q e^{g - g_16R}
+  static constexpr size_t OFF_Y = OFF_Q + RM;             // k e^{g_16J - g}
+  static constexpr size_t OFF_A = OFF_Y + RM;             // A below the diagonal; first the segment totals
+  static constexpr size_t OFF_T = OFF_A + MM;             // T^T
+  static constexpr size_t OFF_SC = OFF_T + MM;            // per-wave 16x16 fp32 scratch
+  static constexpr size_t OFF_GB = OFF_SC + 4 * 16 * LSC * 4;   // g at rows 0, 16, 32, 48
+  static constexpr size_t OFF_M = OFF_GB + 4 * DK * 4;    // e^{g_16R - g_16J}, 6 block pairs
+  static constexpr size_t TOTAL = OFF_M + 6 * DK * 4;
+  static_assert(NSG * SL == CH && 16 % SL == 0, "segments inside 16-row blocks");
+  static_assert(size_t(NSG) * DK * 4 <= MM, "segment totals fit in the A region");
+};
+
+template <int DK>
+__global__ __launch_bounds__(256, 2) void chunk_prep_chan_kernel(ChunkParams p, int64_t nchunks) {
+  typedef Op<IO_BF16> O;
+  typedef __bf16 T;
+  typedef uint16_t elem;
+  typedef ChanLayout<DK> L;
+  typedef WsRec<2> W;
+  constexpr int NT = 256, ESZ = 2, EPV = 8;
+  constexpr int LDK = L::LDK, LCH = L::LCH, NQ = L::NQ, NSG = L::NSG, SL = L::SL;
+  static_assert(L::TOTAL <= 81920, "two workgroups per CU");
+
+  __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
+  T* sK = reinterpret_cast<T*>(smem + L::OFF_K);
+  T* sQ = reinterpret_cast<T*>(smem + L::OFF_Q);
+  T* sY = reinterpret_cast<T*>(smem + L::OFF_Y);
+  T* sA = reinterpret_cast<T*>(smem + L::OFF_A);
+  float* sTot = reinterpret_cast<float*>(smem + L::OFF_A);
+  T* sT = reinterpret_cast<T*>(smem + L::OFF_T);
+  float* sScr = reinterpret_cast<float*>(smem + L::OFF_SC);
+  float* sGb = reinterpret_cast<float*>(smem + L::OFF_GB);
+  float* sM = reinterpret_cast<float*>(smem + L::OFF_M);
+
+  // block order (batch, chunk, head), head fastest (see chunk_prep_reg_kernel)
+  const int64_t hh = blockIdx.x % p.H;
+  const int64_t n = (blockIdx.x / p.H) % nchunks;
+  const int64_t bb = blockIdx.x / (p.H * nchunks);
+  const int64_t bh = bb * p.H + hh;
+  const int H = static_cast<int>(p.H);
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int lr = lane & 15;
+  const int lg = lane >> 4;
+  char* rec = static_cast<char*>(p.ws) + (bh * nchunks + n) * rec_bytes(IO_BF16, GATE_CHANNEL, DK);
+
+  // the chunk's rows; rows of a ragged last chunk read as zero (no decay, no update)
+  const int64_t t0 = n * CH;
+  const int64_t row0 = (bb * p.T + t0) * p.H + hh;
+  const int64_t left = p.T - t0;
+  const uint32_t span = static_cast<uint32_t>(((left < CH ? left : CH) - 1) * p.H + 1);
+  const rsrc_t rk = make_rsrc(static_cast<const elem*>(p.k) + row0 * DK, span * DK * ESZ);
+  const rsrc_t rq = make_rsrc(static_cast<const elem*>(p.q) + row0 * DK, span * DK * ESZ);
+  const rsrc_t rl = make_rsrc(static_cast<const elem*>(p.log_a) + row0 * DK, span * DK * ESZ);
+  const rsrc_t rb = make_rsrc(static_cast<const elem*>(p.beta) + row0, span * ESZ);
+
+  const int cq = tid % NQ, sg = tid / NQ, c0 = 4 * cq, r0 = sg * SL, R = r0 / 16;
+  u32x2 kr[SL], qr[SL], la[SL];
+  float be[SL];
+#pragma unroll
+  for (int j = 0; j < SL; ++j) {
+    const uint32_t off = static_cast<uint32_t>(((r0 + j) * H * DK + c0) * ESZ);
+    kr[j] = buf_load8(rk, off, 0);
+    qr[j] = buf_load8(rq, off, 0);
+    la[j] = buf_load8(rl, off, 0);
+    be[j] = bf16_bits_to_f32(buf_load2(rb, static_cast<uint32_t>((r0 + j) * H * ESZ), 0));
+  }
+  auto el = [](u32x2 w, int c) -> float {       // element c of four packed bf16
+    const uint32_t x = w[c >> 1];
+    return __uint_as_float((c & 1) ? (x & 0xffff0000u) : (x << 16));
+  };
+
+  // inclusive scan of the gate down each channel: this segment in registers ...
+  float g[SL][4];
+  f32x4 run = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < SL; ++j)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      run[c] += el(la[j], c);
+      g[j][c] = run[c];
+    }
+  *reinterpret_cast<f32x4*>(sTot + sg * DK + c0) = run;
+  __syncthreads();
+  // ... plus the totals of the segments above
+  f32x4 pre = {0.f, 0.f, 0.f, 0.f};
+  for (int s2 = 0; s2 < sg; ++s2) pre += *reinterpret_cast<const f32x4*>(sTot + s2 * DK + c0);
+#pragma unroll
+  for (int j = 0; j < SL; ++j)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) g[j][c] += pre[c];
+  if (r0 % 16 == 0) *reinterpret_cast<f32x4*>(sGb + R * DK + c0) = f32x4{g[0][0], g[0][1], g[0][2], g[0][3]};
+  __syncthreads();                              // g at the block starts in place; totals no longer read
+
+  for (int i = tid; i < DK; i += NT) {
+#pragma unroll
+    for (int Rm = 1; Rm < 4; ++Rm)
+#pragma unroll
+      for (int J = 0; J < Rm; ++J) sM[strict_pair(Rm, J) * DK + i] = __expf(sGb[Rm * DK + i] - sGb[J * DK + i]);
+  }
+  const f32x4 gR = *reinterpret_cast<const f32x4*>(sGb + R * DK + c0);
+  f32x4 eR, eprev;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    eR[c] = __expf(gR[c]);                      // e^{g_16R}
+    eprev[c] = __expf(pre[c] - gR[c]);          // literal form, first row: e^{g_{r0-1} - g_16R}
+  }
+  // g_63 of each channel: the bottom segment holds it and shares it through the
+  // segment-total region (nobody reads the totals after the last barrier)
+  if (sg == NSG - 1)
+    *reinterpret_cast<f32x4*>(sTot + c0) = f32x4{g[SL - 1][0], g[SL - 1][1], g[SL - 1][2], g[SL - 1][3]};
+  __syncthreads();
+  const f32x4 g63 = *reinterpret_cast<const f32x4*>(sTot + c0);
+  float* f = reinterpret_cast<float*>(rec + W::F_OFF);
+  if (sg == 0) *reinterpret_cast<f32x4*>(f + CH + c0) =
+      f32x4{__expf(g63[0]), __expf(g63[1]), __expf(g63[2]), __expf(g63[3])};   // e^{g_63} per channel
+  if (cq == 0)
+#pragma unroll
+    for (int j = 0; j < SL; ++j) f[r0 + j] = be[j];                                  // beta
+
+  // operands
+  f32x4 aprev = eprev;                          // e^{g_{r-1} - g_16R} of the previous row
+#pragma unroll
+  for (int j = 0; j < SL; ++j) {
+    const int r = r0 + j;
+    f32x4 xk, xq, y, sk, sq, sd;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float kk = el(kr[j], c), qq = el(qr[j], c);
+      const float a = __expf(g[j][c] - gR[c]);
+      const float ar = p.literal ? aprev[c] : a;             // e^{g_read - g_16R}
+      aprev[c] = a;
+      xk[c] = be[j] * kk * ar;
+      xq[c] = qq * a;
+      y[c] = kk * __expf(gR[c] - g[j][c]);
+      sk[c] = kk * ar * eR[c];
+      sq[c] = qq * a * eR[c];
+      sd[c] = kk * __expf(g63[c] - g[j][c]);
+    }
+    *reinterpret_cast<bf16x4*>(sK + r * LDK + c0) = O::cvt(xk);
+    *reinterpret_cast<bf16x4*>(sQ + r * LDK + c0) = O::cvt(xq);
+    *reinterpret_cast<bf16x4*>(sY + r * LDK + c0) = O::cvt(y);
+    char* x = rec + W::X_OFF + (r * DK + c0) * ESZ;
+    *reinterpret_cast<u32x2*>(x) = __builtin_bit_cast(u32x2, to_bf16x4(sk));
+    *reinterpret_cast<u32x2*>(x + CH * DK * ESZ) = __builtin_bit_cast(u32x2, to_bf16x4(sq));
+    *reinterpret_cast<u32x2*>(x + 2 * CH * DK * ESZ) = __builtin_bit_cast(u32x2, to_bf16x4(sd));
+  }
+  __syncthreads();
+
+  // ---- 16x16 blocks: rows (R) of sK or sQ against rows (J) of sY, the column operand
+  // carrying e^{g_16R - g_16J} below the diagonal.  With `tr` the product is formed
+  // transposed (operands swapped): acc[s] is element (16R + lr, 16J + 4lg + s)
+  // instead of (16R + 4lg + s, 16J + lr).
+  auto block = [&](const T* rows, int Rb, int J, bool tr) -> f32x4 {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < DK / 32; ++kb) {
+      const int c = 32 * kb + 4 * lg;
+      const bf16x4 a0 = O::ld(rows + (16 * Rb + lr) * LDK + c), a1 = O::ld(rows + (16 * Rb + lr) * LDK + c + 16);
+      bf16x4 b0 = O::ld(sY + (16 * J + lr) * LDK + c), b1 = O::ld(sY + (16 * J + lr) * LDK + c + 16);
+      if (Rb > J) {
+        const float* m = sM + strict_pair(Rb, J) * DK + c;
+        b0 = O::cvt(O::f32(b0) * *reinterpret_cast<const f32x4*>(m));
+        b1 = O::cvt(O::f32(b1) * *reinterpret_cast<const f32x4*>(m + 16));
+      }
+      acc = tr ? O::mma2(acc, b0, b1, a0, a1) : O::mma2(acc, a0, a1, b0, b1);
+    }
+    return acc;
+  };
+  auto a_block = [&](int Rb, int J) -> f32x4 {  // strictly lower part of A
+    f32x4 acc = block(sK, Rb, J, false);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      if (Rb == J && 4 * lg + s <= lr) acc[s] = 0.f;
+    return acc;
+  };
+
+  // diagonal block of this wave: T_RR = (I + A_RR)^{-1}, stored transposed (sT holds T^T)
+  const int R0 = wave;
+  const f32x4 Dw = unit_lower_inverse(a_block(R0, R0), sScr + wave * 16 * L::LSC, lr, lg);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) sT[(16 * R0 + lr) * LCH + 16 * R0 + 4 * lg + s] = O::from(Dw[s]);
+  // the six blocks of A below the diagonal: task t goes to wave 3 - t % 4, so the
+  // wave with the longest column solve gets fewest
+#pragma unroll
+  for (int t = 0; t < 6; ++t) {
+    if (3 - (t & 3) != wave) continue;
+    const int Rb = 1 + (t >= 1) + (t >= 3), J = t - Rb * (Rb - 1) / 2;
+    const f32x4 acc = a_block(Rb, J);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) sA[(16 * Rb + 4 * lg + s) * LCH + 16 * J + lr] = O::from(acc[s]);
+  }
+  __syncthreads();
+
+  // ---- block column J = wave of T by forward substitution ------------------------------
+  {
+    const int J = wave;
+    bf16x4 Tb[4];
+    Tb[0] = Tb[1] = Tb[2] = Tb[3] = O::cvt(Dw);
+#pragma unroll
+    for (int Rb = 1; Rb < 4; ++Rb) {
+      if (Rb <= J) continue;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < 3; ++m)
+        if (m >= J && m < Rb) acc = O::mma1(acc, O::ld(sA + (16 * Rb + lr) * LCH + 16 * m + 4 * lg), Tb[m]);
+      f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      z = O::mma1(z, O::ld_tr(sT, LCH, 16 * Rb, 16 * Rb, lr, lg), O::cvt(acc));   // rows of D_R from T^T
+      z = -z;
+      Tb[Rb] = O::cvt(z);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) sT[(16 * J + lr) * LCH + 16 * Rb + 4 * lg + s] = O::from(z[s]);
+    }
+  }
+  // ---- P blocks (0,0) (1,0) (1,1) (2,0) ... (3,3): wave w takes w + 1 of them, formed
+  // transposed (four adjacent columns per lane) and stored straight to the record
+  {
+    const int first = 10 - (wave + 1) * (wave + 2) / 2;
+    for (int u = first; u < first + wave + 1; ++u) {
+      int Rb, J;
+      tri_block(u, Rb, J);
+      f32x4 acc = block(sQ, Rb, J, true);
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        if (Rb == J && 4 * lg + s > lr) acc[s] = 0.f;
+      *reinterpret_cast<u32x2*>(rec + W::P_OFF + W::at(Rb, J, lr, 4 * lg)) = __builtin_bit_cast(u32x2, to_bf16x4(acc));
+    }
+  }
+  __syncthreads();
+
+  // ---- the ten blocks of T (transposed) to the record -----------------------------------
+  constexpr int PPB = W::BLK * ESZ / 16, PPR = PPB / 16;
+  for (int pc = tid; pc < 10 * PPB; pc += NT) {
+    int Rb, J;
+    tri_block(pc / PPB, Rb, J);
+    const int a = (pc % PPB) / PPR, b0 = (pc % PPR) * EPV;
+    *reinterpret_cast<u32x4*>(rec + W::T_OFF + pc * 16) =
+        *reinterpret_cast<const u32x4*>(sT + (16 * J + a) * LCH + 16 * Rb + b0);
   }
 }
 
@@ -553,7 +808,10 @@ __global__ __launch_bounds__(256) void chunk_prep_reg_kernel(ChunkParams p, int6
 template <int IO, int GATE, int DK>
 static hipError_t launch_prep_t(const ChunkParams& p, int64_t nchunks, hipStream_t stream) {
   const int64_t ntasks = p.B * p.H * nchunks;
-  if constexpr (GATE == GATE_CHANNEL) {
+  if constexpr (GATE == GATE_CHANNEL && IO == IO_BF16) {
+    hipLaunchKernelGGL((chunk_prep_chan_kernel<DK>), dim3(static_cast<unsigned>(ntasks)), dim3(256), 0, stream, p,
+                       nchunks);
+  } else if constexpr (GATE == GATE_CHANNEL) {
     hipLaunchKernelGGL((chunk_prep_lds_kernel<IO, GATE, DK>), dim3(static_cast<unsigned>(ntasks)), dim3(256), 0,
                        stream, p, nchunks);
   } else {
