@@ -22,7 +22,8 @@ GDR_F32, GDR_BF16 = 0, 1
 GATES = {"none": 0, "scalar": 1, "channel": 2}
 FORMS = {"page": 0, "literal": 1}
 
-EXPORTED = ("gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_recurrent_step", "gdr_status_string", "gdr_last_error", "gdr_version")
+EXPORTED = ("gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_chunk_fwd_varlen_workspace_size",
+            "gdr_chunk_fwd_varlen", "gdr_recurrent_step", "gdr_status_string", "gdr_last_error", "gdr_version")
 
 
 class GdrDesc(ctypes.Structure):
@@ -56,6 +57,12 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         lib.gdr_chunk_fwd_workspace_size.argtypes = [ctypes.POINTER(GdrDesc), ctypes.POINTER(ctypes.c_size_t)]
         lib.gdr_chunk_fwd.restype = ctypes.c_int
         lib.gdr_chunk_fwd.argtypes = [ctypes.POINTER(GdrDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        lib.gdr_chunk_fwd_varlen_workspace_size.restype = ctypes.c_int
+        lib.gdr_chunk_fwd_varlen_workspace_size.argtypes = [ctypes.POINTER(GdrDesc), ctypes.c_int64,
+                                                            ctypes.POINTER(ctypes.c_size_t)]
+        lib.gdr_chunk_fwd_varlen.restype = ctypes.c_int
+        lib.gdr_chunk_fwd_varlen.argtypes = [ctypes.POINTER(GdrDesc), vp, ctypes.c_int64, vp, vp, vp, vp, vp, vp,
+                                             vp, vp, vp, ctypes.c_size_t, vp]
         lib.gdr_recurrent_step.restype = ctypes.c_int
         lib.gdr_recurrent_step.argtypes = [ctypes.POINTER(GdrDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.gdr_status_string.restype = ctypes.c_char_p
@@ -163,6 +170,60 @@ def chunk_fwd(q, k, v, beta, log_a=None, S0=None, *, form: str = "page", o=None,
         raise ValueError("workspace must be a contiguous uint8 tensor on the inputs' device")
     st = lib.gdr_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_a), _ptr(S0),
                            _ptr(o), _ptr(S_T), _ptr(workspace), workspace.numel(), _stream_handle(stream))
+    _check(lib, st)
+    return o, S_T
+
+
+def chunk_varlen_workspace_size(T: int, n_seq: int, H: int, d_k: int, d_v: int, dtype=torch.bfloat16,
+                                gate: str = "scalar") -> int:
+    """Bytes of scratch gdr_chunk_fwd_varlen needs (gdr_chunk_fwd_varlen_workspace_size)."""
+    lib = load()
+    desc = GdrDesc(1, T, H, d_k, d_v, 64, 1 if dtype == torch.bfloat16 else 0, GATES[gate], 0)
+    n = ctypes.c_size_t(0)
+    _check(lib, lib.gdr_chunk_fwd_varlen_workspace_size(ctypes.byref(desc), int(n_seq), ctypes.byref(n)))
+    return int(n.value)
+
+
+def chunk_fwd_varlen(q, k, v, beta, log_a, cu_seqlens, S0=None, *, form: str = "page", o=None, S_T=None,
+                     want_state: bool = True, workspace=None, stream=None):
+    """gdr_chunk_fwd_varlen on torch tensors: sequences packed along T.
+    q, k [1, T, H, d_k]; v [1, T, H, d_v]; beta [1, T, H]; log_a None, [1, T, H] or
+    [1, T, H, d_k] (bf16); cu_seqlens int32 device tensor [N + 1] of offsets;
+    S0 None or [N, H, d_k, d_v] float32.  Returns (o [1, T, H, d_v], S_T [N, H, d_k, d_v])."""
+    lib = load()
+    B, T, H, dk = k.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous() \
+            or cu_seqlens.device != q.device:
+        raise ValueError("cu_seqlens must be a contiguous 1-D int32 tensor on the inputs' device")
+    N = cu_seqlens.numel() - 1
+    _require(q, "q", dt, (1, T, H, dk))
+    _require(k, "k", dt, (1, T, H, dk))
+    _require(v, "v", dt, (1, T, H, dv))
+    _require(beta, "beta", dt, (1, T, H))
+    gate = _gate_of(log_a, beta.shape, k.shape)
+    if log_a is not None:
+        _require(log_a, "log_a", dt, tuple(log_a.shape))
+    if S0 is not None:
+        _require(S0, "S0", torch.float32, (N, H, dk, dv))
+    if o is None:
+        o = torch.empty((1, T, H, dv), dtype=dt, device=q.device)
+    _require(o, "o", dt, (1, T, H, dv))
+    if want_state and S_T is None:
+        S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+    if S_T is not None:
+        _require(S_T, "S_T", torch.float32, (N, H, dk, dv))
+    desc = GdrDesc(1, T, H, dk, dv, 64, _io_of(q), gate, FORMS[form])
+    need = ctypes.c_size_t(0)
+    _check(lib, lib.gdr_chunk_fwd_varlen_workspace_size(ctypes.byref(desc), N, ctypes.byref(need)))
+    if workspace is None:
+        workspace = torch.empty(max(int(need.value), 1), dtype=torch.uint8, device=q.device)
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous() or workspace.device != q.device:
+        raise ValueError("workspace must be a contiguous uint8 tensor on the inputs' device")
+    st = lib.gdr_chunk_fwd_varlen(ctypes.byref(desc), _ptr(cu_seqlens), N, _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                                  _ptr(log_a), _ptr(S0), _ptr(o), _ptr(S_T), _ptr(workspace), workspace.numel(),
+                                  _stream_handle(stream))
     _check(lib, st)
     return o, S_T
 

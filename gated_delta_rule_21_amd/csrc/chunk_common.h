@@ -4,6 +4,7 @@
 #pragma once
 
 #include "device_common.h"
+#include "launchers.h"
 
 namespace gdr {
 
@@ -92,6 +93,60 @@ struct WsRec {
 // Bytes of one record for the I/O type, gate and d_k.
 __host__ __device__ constexpr uint32_t rec_bytes(int io, int gate, int dk) {
   return io == IO_BF16 ? WsRec<2>::BYTES + (gate == GATE_CHANNEL ? 3u * CH * dk * 2u : 0u) : WsRec<4>::BYTES;
+}
+
+// Where one (sequence b, head h) lies.  Fixed-length batches ([B, T, H, .]
+// tensors): tokens b T .. b T + T - 1, records (b H + h) ceil(T / 64) onwards.
+// Packed sequences (p.cu set; [1, T, H, .] tensors, p.B sequences): tokens
+// cu[b] .. cu[b+1] - 1, clamped to [0, T] with a length of at least 0 so that a
+// malformed offset table still stays inside the tensors, and records
+// h p.nslots + floor(cu[b] / 64) + b onwards.  For non-decreasing offsets those
+// record ranges are disjoint (sequence b's last chunk lies below b + 1's first
+// slot) and end below h p.nslots + ceil(T / 64) + B - 1.
+struct SeqSpan {
+  int64_t t0, len, rec0;
+};
+// A wave-uniform 64-bit value, kept in scalar registers (buffer descriptors built
+// from values the compiler cannot prove uniform go through waterfall loops).
+__device__ __forceinline__ int64_t uni64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(x) >> 32));
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+__device__ __forceinline__ int64_t seq_start(const ChunkParams& p, int64_t b) {
+  const int64_t a = p.cu[b];
+  return a < 0 ? 0 : (a > p.T ? p.T : a);
+}
+__device__ __forceinline__ SeqSpan seq_span(const ChunkParams& p, int64_t b, int64_t h) {
+  if (!p.cu) return SeqSpan{b * p.T, p.T, (b * p.H + h) * ((p.T + CH - 1) / CH)};
+  const int64_t a = seq_start(p, b);
+  int64_t e = p.cu[b + 1];
+  e = e < a ? a : (e > p.T ? p.T : e);
+  return SeqSpan{uni64(a), uni64(e - a), uni64(h * p.nslots + a / CH + b)};
+}
+// Tasks of the per-chunk transform, head fastest: fixed-length batches
+// (b, chunk, h) for B H ceil(T / 64) tasks; packed sequences (slot, h) for
+// H nslots tasks, the sequence of a slot found by bisection over the slot bases.
+// Returns false for a task with no chunk (a slot past the end of its sequence).
+__device__ __forceinline__ int64_t prep_tasks_fixed(const ChunkParams& p) { return p.B * p.H * ((p.T + CH - 1) / CH); }
+__device__ __forceinline__ bool prep_task(const ChunkParams& p, int64_t task, int64_t& b, int64_t& n, int64_t& h) {
+  h = task % p.H;
+  if (!p.cu) {
+    const int64_t nch = (p.T + CH - 1) / CH;
+    n = (task / p.H) % nch;
+    b = task / (p.H * nch);
+    return true;
+  }
+  const int64_t slot = task / p.H;
+  int64_t lo = 0, hi = p.B - 1;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi + 1) / 2;
+    if (seq_start(p, mid) / CH + mid <= slot) lo = mid; else hi = mid - 1;
+  }
+  b = uni64(lo);
+  const SeqSpan s = seq_span(p, b, h);
+  n = uni64(slot - (s.t0 / CH + b));
+  return n >= 0 && n * CH < s.len;
 }
 
 // Block (R, J), J <= R, of the ten-block order above.

@@ -155,7 +155,7 @@ __global__ __launch_bounds__(NW * 64) void chunk_fwd_kernel(ChunkParams p, int n
                               GATE == GATE_NONE ? 0u : span * (GATE == GATE_CHANNEL ? DK : 1) * ESZ);
   const rsrc_t rw = make_rsrc(static_cast<const char*>(p.ws) + bh * nchunks * W::BYTES,
                               static_cast<uint32_t>(nchunks * W::BYTES));
-  static_assert(IO == IO_F32, "bf16 I/O runs the chain/helper kernel (chunk_state.hip)");
+  static_assert(IO == IO_F32, "bf16 I/O runs the chain/helper kernel (chunk_state.hip)");   // fixed-length only
   // per-thread byte offsets within a chunk (the chunk start goes in the scalar offset)
   uint32_t offk[KV], offv[VV];
 #pragma unroll
@@ -481,6 +481,10 @@ hipError_t launch_chunk_fwd(const ChunkParams& p, hipStream_t stream) {
 size_t chunk_workspace_bytes(int64_t B, int64_t T, int64_t H, int io, int gate, int d_k) {
   const int64_t nchunks = (T + CH - 1) / CH;
   return static_cast<size_t>(B * H * nchunks) * rec_bytes(io, gate, d_k);
+}
+
+size_t chunk_varlen_workspace_bytes(int64_t T, int64_t n_seq, int64_t H, int io, int gate, int d_k) {
+  return static_cast<size_t>(H * chunk_varlen_slots(T, n_seq)) * rec_bytes(io, gate, d_k);
 }
 
 }  // namespace gdr

@@ -87,7 +87,7 @@ struct PrepLayout {
 };
 
 template <int IO, int GATE, int DK>
-__global__ __launch_bounds__(256) void chunk_prep_lds_kernel(ChunkParams p, int64_t nchunks) {
+__global__ __launch_bounds__(256) void chunk_prep_lds_kernel(ChunkParams p) {
   typedef Op<IO> O;
   typedef typename O::T T;
   typedef typename Io<IO>::elem elem;
@@ -119,25 +119,24 @@ __global__ __launch_bounds__(256) void chunk_prep_lds_kernel(ChunkParams p, int6
   float* sM = reinterpret_cast<float*>(smem + L::C_M);
   float* sTot = reinterpret_cast<float*>(smem + L::C_TOT);
 
-  // block order (batch, chunk, head), head fastest (see chunk_prep_reg_kernel)
-  const int64_t hh = blockIdx.x % p.H;
-  const int64_t n = (blockIdx.x / p.H) % nchunks;
-  const int64_t bb = blockIdx.x / (p.H * nchunks);
-  const int64_t bh = bb * p.H + hh;
+  // block order (batch or slot, chunk, head), head fastest (see chunk_prep_reg_kernel)
+  int64_t bb, n, hh;
+  if (!prep_task(p, blockIdx.x, bb, n, hh)) return;   // whole workgroup: no chunk for this slot
+  const SeqSpan sq = seq_span(p, bb, hh);
   const int H = static_cast<int>(p.H);
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int lr = lane & 15;
   const int lg = lane >> 4;
-  char* rec = static_cast<char*>(p.ws) + (bh * nchunks + n) * W::BYTES;
+  char* rec = static_cast<char*>(p.ws) + (sq.rec0 + n) * W::BYTES;
   static_assert(IO == IO_F32 || GATE != GATE_CHANNEL, "bf16 per-channel gate: chunk_prep_chan_kernel");
 
   // The chunk's rows through buffers whose range ends at the sequence's last
   // token: rows of a ragged last chunk read as zero.
   const int64_t t0 = n * CH;
-  const int64_t row0 = (bb * p.T + t0) * p.H + hh;      // token row of (b, t0, h)
-  const int64_t left = p.T - t0;                         // >= 1
+  const int64_t row0 = (sq.t0 + t0) * p.H + hh;         // token row of (b, t0, h)
+  const int64_t left = sq.len - t0;                      // >= 1
   const uint32_t span = static_cast<uint32_t>(((left < CH ? left : CH) - 1) * p.H + 1);
   const rsrc_t rk = make_rsrc(static_cast<const elem*>(p.k) + row0 * DK, span * DK * ESZ);
   const rsrc_t rq = make_rsrc(static_cast<const elem*>(p.q) + row0 * DK, span * DK * ESZ);
@@ -391,7 +390,7 @@ struct ChanLayout {
 };
 
 template <int DK>
-__global__ __launch_bounds__(256, 2) void chunk_prep_chan_kernel(ChunkParams p, int64_t nchunks) {
+__global__ __launch_bounds__(256, 2) void chunk_prep_chan_kernel(ChunkParams p) {
   typedef Op<IO_BF16> O;
   typedef __bf16 T;
   typedef uint16_t elem;
@@ -412,23 +411,22 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_chan_kernel(ChunkParams p, 
   float* sGb = reinterpret_cast<float*>(smem + L::OFF_GB);
   float* sM = reinterpret_cast<float*>(smem + L::OFF_M);
 
-  // block order (batch, chunk, head), head fastest (see chunk_prep_reg_kernel)
-  const int64_t hh = blockIdx.x % p.H;
-  const int64_t n = (blockIdx.x / p.H) % nchunks;
-  const int64_t bb = blockIdx.x / (p.H * nchunks);
-  const int64_t bh = bb * p.H + hh;
+  // block order (batch or slot, chunk, head), head fastest (see chunk_prep_reg_kernel)
+  int64_t bb, n, hh;
+  if (!prep_task(p, blockIdx.x, bb, n, hh)) return;   // whole workgroup: no chunk for this slot
+  const SeqSpan sq = seq_span(p, bb, hh);
   const int H = static_cast<int>(p.H);
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int lr = lane & 15;
   const int lg = lane >> 4;
-  char* rec = static_cast<char*>(p.ws) + (bh * nchunks + n) * rec_bytes(IO_BF16, GATE_CHANNEL, DK);
+  char* rec = static_cast<char*>(p.ws) + (sq.rec0 + n) * rec_bytes(IO_BF16, GATE_CHANNEL, DK);
 
   // the chunk's rows; rows of a ragged last chunk read as zero (no decay, no update)
   const int64_t t0 = n * CH;
-  const int64_t row0 = (bb * p.T + t0) * p.H + hh;
-  const int64_t left = p.T - t0;
+  const int64_t row0 = (sq.t0 + t0) * p.H + hh;
+  const int64_t left = sq.len - t0;
   const uint32_t span = static_cast<uint32_t>(((left < CH ? left : CH) - 1) * p.H + 1);
   const rsrc_t rk = make_rsrc(static_cast<const elem*>(p.k) + row0 * DK, span * DK * ESZ);
   const rsrc_t rq = make_rsrc(static_cast<const elem*>(p.q) + row0 * DK, span * DK * ESZ);
@@ -624,7 +622,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_chan_kernel(ChunkParams p, 
 // No gate / scalar gate: one wave per (sequence, head, chunk), operands in registers.
 // ---------------------------------------------------------------------------------
 template <int IO, int GATE, int DK>
-__global__ __launch_bounds__(256) void chunk_prep_reg_kernel(ChunkParams p, int64_t nchunks, int64_t ntasks) {
+__global__ __launch_bounds__(256) void chunk_prep_reg_kernel(ChunkParams p, int64_t ntasks) {
   typedef Op<IO> O;
   typedef typename O::frag frag;
   typedef typename Io<IO>::elem elem;
@@ -642,24 +640,23 @@ __global__ __launch_bounds__(256) void chunk_prep_reg_kernel(ChunkParams p, int6
   const int lane = threadIdx.x & 63;
   const int lr = lane & 15;
   const int lg = lane >> 4;
-  // Task order (batch, chunk, head), head fastest: waves running side by side read
-  // the whole token rows [t][H][d_k] of one chunk of one sequence together.
+  // Task order (batch or slot, chunk, head), head fastest: waves running side by
+  // side read the whole token rows [t][H][d_k] of one chunk of one sequence together.
   const int64_t task = static_cast<int64_t>(blockIdx.x) * 4 + wave;
   if (task >= ntasks) return;                   // this wave has no chunk (no workgroup barriers below)
-  const int64_t hh = task % p.H;
-  const int64_t n = (task / p.H) % nchunks;
-  const int64_t bb = task / (p.H * nchunks);
-  const int64_t bh = bb * p.H + hh;
+  int64_t bb, n, hh;
+  if (!prep_task(p, task, bb, n, hh)) return;   // a slot past the end of its sequence
+  const SeqSpan sq = seq_span(p, bb, hh);
   const int H = static_cast<int>(p.H);
-  char* rec = static_cast<char*>(p.ws) + (bh * nchunks + n) * rec_bytes(IO, GATE, DK);
+  char* rec = static_cast<char*>(p.ws) + (sq.rec0 + n) * rec_bytes(IO, GATE, DK);
   float* sB = sfac[wave];
   float* sG = sB + CH;
   float* sGr = sB + 2 * CH;
 
   // The chunk's rows through buffers whose range ends at the sequence's last token.
   const int64_t t0 = n * CH;
-  const int64_t row0 = (bb * p.T + t0) * p.H + hh;
-  const int64_t left = p.T - t0;
+  const int64_t row0 = (sq.t0 + t0) * p.H + hh;
+  const int64_t left = sq.len - t0;
   const uint32_t span = static_cast<uint32_t>(((left < CH ? left : CH) - 1) * p.H + 1);
   const rsrc_t rk = make_rsrc(static_cast<const elem*>(p.k) + row0 * DK, span * DK * ESZ);
   const rsrc_t rq = make_rsrc(static_cast<const elem*>(p.q) + row0 * DK, span * DK * ESZ);
@@ -807,16 +804,15 @@ __global__ __launch_bounds__(256) void chunk_prep_reg_kernel(ChunkParams p, int6
 
 template <int IO, int GATE, int DK>
 static hipError_t launch_prep_t(const ChunkParams& p, int64_t nchunks, hipStream_t stream) {
-  const int64_t ntasks = p.B * p.H * nchunks;
+  const int64_t ntasks = p.cu ? p.H * p.nslots : p.B * p.H * nchunks;
   if constexpr (GATE == GATE_CHANNEL && IO == IO_BF16) {
-    hipLaunchKernelGGL((chunk_prep_chan_kernel<DK>), dim3(static_cast<unsigned>(ntasks)), dim3(256), 0, stream, p,
-                       nchunks);
+    hipLaunchKernelGGL((chunk_prep_chan_kernel<DK>), dim3(static_cast<unsigned>(ntasks)), dim3(256), 0, stream, p);
   } else if constexpr (GATE == GATE_CHANNEL) {
     hipLaunchKernelGGL((chunk_prep_lds_kernel<IO, GATE, DK>), dim3(static_cast<unsigned>(ntasks)), dim3(256), 0,
-                       stream, p, nchunks);
+                       stream, p);
   } else {
     hipLaunchKernelGGL((chunk_prep_reg_kernel<IO, GATE, DK>), dim3(static_cast<unsigned>((ntasks + 3) / 4)),
-                       dim3(256), 0, stream, p, nchunks, ntasks);
+                       dim3(256), 0, stream, p, ntasks);
   }
   return hipGetLastError();
 }
@@ -844,6 +840,7 @@ static hipError_t launch_prep_io(const ChunkParams& p, int64_t nchunks, hipStrea
 hipError_t launch_chunk_prep(const ChunkParams& p, hipStream_t stream) {
   const int64_t nchunks = (p.T + CH - 1) / CH;
   if (p.B * p.H * nchunks == 0) return hipSuccess;
+  if (p.cu && p.io != IO_BF16) return hipErrorInvalidValue;   // packed sequences: bf16 kernels only
   return p.io == IO_BF16 ? launch_prep_io<IO_BF16>(p, nchunks, stream) : launch_prep_io<IO_F32>(p, nchunks, stream);
 }
 

@@ -121,15 +121,16 @@ __global__ __launch_bounds__((NCH + NHW) * 64) void chunk_state_pipe_kernel(Chun
   const int lg = lane >> 4;
   const int ht = tid - 64 * NCH;                 // helper thread index
 
-  const int64_t nchunks = (p.T + CH - 1) / CH;
-  const int64_t row0 = bb * p.T * p.H + hh;
-  const uint32_t span = static_cast<uint32_t>(p.T > 0 ? (p.T - 1) * p.H + 1 : 0);
+  // this sequence's tokens (a packed sequence's come from the offset table)
+  const SeqSpan sq = seq_span(p, bb, hh);
+  const int64_t nchunks = (sq.len + CH - 1) / CH;
+  const int64_t row0 = sq.t0 * p.H + hh;
+  const uint32_t span = static_cast<uint32_t>(sq.len > 0 ? (sq.len - 1) * p.H + 1 : 0);
   const rsrc_t rk = make_rsrc(static_cast<const elem*>(p.k) + row0 * DK, span * DK * ESZ);
   const rsrc_t rq = make_rsrc(static_cast<const elem*>(p.q) + row0 * DK, span * DK * ESZ);
   const rsrc_t rv = make_rsrc(static_cast<const elem*>(p.v) + row0 * dv, span * dv * ESZ);
   const rsrc_t ro = make_rsrc(static_cast<const elem*>(p.o) + row0 * dv, span * dv * ESZ);
-  const rsrc_t rw = make_rsrc(static_cast<const char*>(p.ws) + bh * nchunks * RB,
-                              static_cast<uint32_t>(nchunks * RB));
+  const rsrc_t rw = make_rsrc(static_cast<const char*>(p.ws) + sq.rec0 * RB, static_cast<uint32_t>(nchunks * RB));
 
   // ---- helpers: loads one chunk ahead in registers, stores into an LDS copy ----------
   // Per-channel gate: k, q and k e^{g_63 - g} come decayed from the record (row-major

@@ -131,55 +131,116 @@ gdr_status gdr_chunk_fwd_workspace_size(const gdr_desc* d, size_t* bytes) {
   }
 }
 
+}  // extern "C"
+
+namespace {
+
+// The forward over fixed-length batches (cu == nullptr) or packed sequences.
+gdr_status chunk_fwd_impl(const gdr_desc* d, const int32_t* cu, int64_t n_seq, const void* q, const void* k,
+                          const void* v, const void* beta, const void* log_a, const float* S0, void* o, float* S_T,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  gdr_status st = check_desc(d, false);
+  if (st != GDR_OK) return st;
+  const bool packed = cu != nullptr || n_seq != 0;
+  if (packed) {
+    if (!cu) return fail(GDR_ERR_INVALID_ARG, "cu_seqlens is NULL");
+    if (n_seq < 1) return fail(GDR_ERR_INVALID_ARG, "n_seq = %lld must be >= 1", (long long)n_seq);
+    if (d->B != 1) return fail(GDR_ERR_INVALID_ARG, "B = %lld: packed sequences take B = 1 (all tokens in T)", (long long)d->B);
+    if (d->io != GDR_BF16) return fail(GDR_ERR_UNSUPPORTED, "packed sequences: bf16 I/O only");
+    int64_t x;
+    if (!mul_ok(n_seq, d->H, &x) || x * 8 > INT32_MAX || d->H * gdr::chunk_varlen_slots(d->T, n_seq) > INT32_MAX)
+      return fail(GDR_ERR_UNSUPPORTED, "n_seq = %lld: exceeds the grid limit", (long long)n_seq);
+  }
+  const int64_t nseq = packed ? n_seq : d->B;        // sequences, and states in S0 / S_T
+  const size_t ws_need =
+      packed ? gdr::chunk_varlen_workspace_bytes(d->T, n_seq, d->H, d->io, d->gate, static_cast<int>(d->d_k))
+             : gdr::chunk_workspace_bytes(d->B, d->T, d->H, d->io, d->gate, static_cast<int>(d->d_k));
+  const int64_t esz = d->io == GDR_BF16 ? 2 : 4;
+  const int64_t ntok = d->B * d->T * d->H;
+  const bool any = d->T > 0;
+  if (any) {
+    if (!q) return fail(GDR_ERR_INVALID_ARG, "q is NULL");
+    if (!k) return fail(GDR_ERR_INVALID_ARG, "k is NULL");
+    if (!v) return fail(GDR_ERR_INVALID_ARG, "v is NULL");
+    if (!beta) return fail(GDR_ERR_INVALID_ARG, "beta is NULL");
+    if (!o) return fail(GDR_ERR_INVALID_ARG, "o is NULL");
+    if (d->gate != GDR_GATE_NONE && !log_a) return fail(GDR_ERR_INVALID_ARG, "log_a is NULL but a gate is requested");
+    if (!workspace) return fail(GDR_ERR_INVALID_ARG, "workspace is NULL (%zu bytes needed)", ws_need);
+    if (workspace_bytes < ws_need)
+      return fail(GDR_ERR_INVALID_ARG, "workspace_bytes = %zu, %zu needed", workspace_bytes, ws_need);
+  }
+  if (d->gate == GDR_GATE_NONE && log_a) return fail(GDR_ERR_INVALID_ARG, "log_a must be NULL for GDR_GATE_NONE");
+  if ((st = check_align("q", q, 16)) || (st = check_align("k", k, 16)) || (st = check_align("v", v, 16)) ||
+      (st = check_align("o", o, 16)) || (st = check_align("S0", S0, 16)) || (st = check_align("S_T", S_T, 16)) ||
+      (st = check_align("beta", beta, esz)) || (st = check_align("log_a", log_a, esz)) ||
+      (st = check_align("workspace", workspace, 16)) || (st = check_align("cu_seqlens", cu, 4)))
+    return st;
+  const int64_t gate_w = d->gate == GDR_GATE_NONE ? 0 : d->gate == GDR_GATE_SCALAR ? 1 : d->d_k;
+  const int64_t state_bytes = nseq * d->H * d->d_k * d->d_v * 4;
+  Span all[] = {span("q", q, ntok * d->d_k * esz), span("k", k, ntok * d->d_k * esz),
+                span("v", v, ntok * d->d_v * esz), span("beta", beta, ntok * esz),
+                span("log_a", log_a, ntok * gate_w * esz), span("S0", S0, state_bytes),
+                span("o", o, ntok * d->d_v * esz), span("S_T", S_T, state_bytes),
+                span("workspace", d->T > 0 ? workspace : nullptr, static_cast<int64_t>(ws_need)),
+                span("cu_seqlens", cu, packed ? (n_seq + 1) * 4 : 0)};
+  Span outs[] = {all[6], all[7], all[8]};
+  if (S_T && S0 == S_T) all[5].hi = all[5].lo;   // exact in-place update of the state is allowed
+  if ((st = check_no_overlap(outs, 3, all, 10))) return st;
+
+  gdr::ChunkParams p;
+  p.q = q; p.k = k; p.v = v; p.beta = beta; p.log_a = log_a; p.S0 = S0; p.o = o; p.S_T = S_T;
+  p.ws = workspace;
+  p.B = nseq; p.T = d->T; p.H = d->H;
+  p.d_k = static_cast<int>(d->d_k); p.d_v = static_cast<int>(d->d_v);
+  p.io = d->io; p.gate = d->gate; p.literal = d->form == GDR_FORM_LITERAL;
+  p.cu = cu;
+  p.nslots = packed ? gdr::chunk_varlen_slots(d->T, n_seq) : 0;
+  if (d->T == 0 && !S_T) return GDR_OK;
+  hipError_t e = gdr::launch_chunk_fwd(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(GDR_ERR_HIP, "chunk forward launch failed: %s", hipGetErrorString(e));
+  return GDR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 gdr_status gdr_chunk_fwd(const gdr_desc* d, const void* q, const void* k, const void* v, const void* beta,
                          const void* log_a, const float* S0, void* o, float* S_T, void* workspace,
                          size_t workspace_bytes, void* stream) {
   try {
     g_last_error.clear();
+    return chunk_fwd_impl(d, nullptr, 0, q, k, v, beta, log_a, S0, o, S_T, workspace, workspace_bytes, stream);
+  } catch (...) {
+    return fail(GDR_ERR_INVALID_ARG, "internal error");
+  }
+}
+
+gdr_status gdr_chunk_fwd_varlen_workspace_size(const gdr_desc* d, int64_t n_seq, size_t* bytes) {
+  try {
+    g_last_error.clear();
+    if (!bytes) return fail(GDR_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = 0;
     gdr_status st = check_desc(d, false);
     if (st != GDR_OK) return st;
-    const size_t ws_need = gdr::chunk_workspace_bytes(d->B, d->T, d->H, d->io, d->gate, static_cast<int>(d->d_k));
-    const int64_t esz = d->io == GDR_BF16 ? 2 : 4;
-    const int64_t ntok = d->B * d->T * d->H;
-    const bool any = d->T > 0;
-    if (any) {
-      if (!q) return fail(GDR_ERR_INVALID_ARG, "q is NULL");
-      if (!k) return fail(GDR_ERR_INVALID_ARG, "k is NULL");
-      if (!v) return fail(GDR_ERR_INVALID_ARG, "v is NULL");
-      if (!beta) return fail(GDR_ERR_INVALID_ARG, "beta is NULL");
-      if (!o) return fail(GDR_ERR_INVALID_ARG, "o is NULL");
-      if (d->gate != GDR_GATE_NONE && !log_a) return fail(GDR_ERR_INVALID_ARG, "log_a is NULL but a gate is requested");
-      if (!workspace) return fail(GDR_ERR_INVALID_ARG, "workspace is NULL (%zu bytes needed)", ws_need);
-      if (workspace_bytes < ws_need)
-        return fail(GDR_ERR_INVALID_ARG, "workspace_bytes = %zu, %zu needed", workspace_bytes, ws_need);
-    }
-    if (d->gate == GDR_GATE_NONE && log_a) return fail(GDR_ERR_INVALID_ARG, "log_a must be NULL for GDR_GATE_NONE");
-    if ((st = check_align("q", q, 16)) || (st = check_align("k", k, 16)) || (st = check_align("v", v, 16)) ||
-        (st = check_align("o", o, 16)) || (st = check_align("S0", S0, 16)) || (st = check_align("S_T", S_T, 16)) ||
-        (st = check_align("beta", beta, esz)) || (st = check_align("log_a", log_a, esz)) ||
-        (st = check_align("workspace", workspace, 16)))
-      return st;
-    const int64_t gate_w = d->gate == GDR_GATE_NONE ? 0 : d->gate == GDR_GATE_SCALAR ? 1 : d->d_k;
-    const int64_t state_bytes = d->B * d->H * d->d_k * d->d_v * 4;
-    Span all[] = {span("q", q, ntok * d->d_k * esz), span("k", k, ntok * d->d_k * esz),
-                  span("v", v, ntok * d->d_v * esz), span("beta", beta, ntok * esz),
-                  span("log_a", log_a, ntok * gate_w * esz), span("S0", S0, state_bytes),
-                  span("o", o, ntok * d->d_v * esz), span("S_T", S_T, state_bytes),
-                  span("workspace", d->T > 0 ? workspace : nullptr, static_cast<int64_t>(ws_need))};
-    Span outs[] = {all[6], all[7], all[8]};
-    if (S_T && S0 == S_T) all[5].hi = all[5].lo;   // exact in-place update of the state is allowed
-    if ((st = check_no_overlap(outs, 3, all, 9))) return st;
-
-    gdr::ChunkParams p;
-    p.q = q; p.k = k; p.v = v; p.beta = beta; p.log_a = log_a; p.S0 = S0; p.o = o; p.S_T = S_T;
-    p.ws = workspace;
-    p.B = d->B; p.T = d->T; p.H = d->H;
-    p.d_k = static_cast<int>(d->d_k); p.d_v = static_cast<int>(d->d_v);
-    p.io = d->io; p.gate = d->gate; p.literal = d->form == GDR_FORM_LITERAL;
-    if (d->T == 0 && !S_T) return GDR_OK;
-    hipError_t e = gdr::launch_chunk_fwd(p, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return fail(GDR_ERR_HIP, "chunk forward launch failed: %s", hipGetErrorString(e));
+    if (n_seq < 1) return fail(GDR_ERR_INVALID_ARG, "n_seq = %lld must be >= 1", (long long)n_seq);
+    if (d->B != 1) return fail(GDR_ERR_INVALID_ARG, "B = %lld: packed sequences take B = 1 (all tokens in T)", (long long)d->B);
+    if (d->io != GDR_BF16) return fail(GDR_ERR_UNSUPPORTED, "packed sequences: bf16 I/O only");
+    *bytes = gdr::chunk_varlen_workspace_bytes(d->T, n_seq, d->H, d->io, d->gate, static_cast<int>(d->d_k));
     return GDR_OK;
+  } catch (...) {
+    return fail(GDR_ERR_INVALID_ARG, "internal error");
+  }
+}
+
+gdr_status gdr_chunk_fwd_varlen(const gdr_desc* d, const int32_t* cu_seqlens, int64_t n_seq, const void* q,
+                                const void* k, const void* v, const void* beta, const void* log_a, const float* S0,
+                                void* o, float* S_T, void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    g_last_error.clear();
+    if (!cu_seqlens) return fail(GDR_ERR_INVALID_ARG, "cu_seqlens is NULL");
+    return chunk_fwd_impl(d, cu_seqlens, n_seq, q, k, v, beta, log_a, S0, o, S_T, workspace, workspace_bytes,
+                          stream);
   } catch (...) {
     return fail(GDR_ERR_INVALID_ARG, "internal error");
   }

@@ -30,9 +30,14 @@ struct ChunkParams {
   void* o;
   float* S_T;         // may be null (not written)
   void* ws;           // per-chunk records of the transform (chunk_workspace_bytes)
-  int64_t B, T, H;
+  int64_t B, T, H;    // packed sequences: B = number of sequences, T = total tokens
   int d_k, d_v;
   int io, gate, literal;
+  // Packed variable-length sequences (null for fixed-length batches): device int32
+  // offsets cu[0..B], sequence b = tokens [cu[b], cu[b+1]) of [1, T, H, .] tensors;
+  // nslots = records per head in the workspace (chunk_varlen_slots).
+  const int32_t* cu;
+  int64_t nslots;
 };
 
 hipError_t launch_decode_step(const DecodeParams& p, hipStream_t stream);
@@ -42,5 +47,9 @@ hipError_t launch_chunk_state_pipe(const ChunkParams& p, hipStream_t stream);   
 hipError_t launch_chunk_fwd(const ChunkParams& p, hipStream_t stream);
 // B*H*ceil(T/64) records of the per-chunk transform (see WsRec in chunk_common.h)
 size_t chunk_workspace_bytes(int64_t B, int64_t T, int64_t H, int io, int gate, int d_k);
+// Packed sequences: record slots per head for n_seq sequences of T tokens in all
+// (sequence b's chunks start at slot floor(cu[b] / 64) + b), and the workspace bytes.
+inline int64_t chunk_varlen_slots(int64_t T, int64_t n_seq) { return (T + 63) / 64 + n_seq; }
+size_t chunk_varlen_workspace_bytes(int64_t T, int64_t n_seq, int64_t H, int io, int gate, int d_k);
 
 }  // namespace gdr

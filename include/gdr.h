@@ -144,6 +144,43 @@ gdr_status gdr_chunk_fwd(const gdr_desc* desc, const void* q, const void* k, con
                          void* stream /* hipStream_t */);
 
 /*
+ * gdr_chunk_fwd_varlen_workspace_size -- workspace of gdr_chunk_fwd_varlen.
+ *
+ * desc describes the packed tensors (desc->B must be 1, desc->T = total
+ * tokens); n_seq >= 1 is the number of sequences.  Sequence i's chunks use
+ * record slots from floor(cu_seqlens[i] / 64) + i on, so H * (ceil(T / 64) +
+ * n_seq) records of the size given under gdr_chunk_fwd_workspace_size cover
+ * any split of the T tokens.  bf16 I/O only (GDR_ERR_UNSUPPORTED otherwise).
+ */
+gdr_status gdr_chunk_fwd_varlen_workspace_size(const gdr_desc* desc, int64_t n_seq, size_t* bytes);
+
+/*
+ * gdr_chunk_fwd_varlen -- gdr_chunk_fwd over variable-length sequences packed
+ * along T (one prefill batch of prompts of different lengths).
+ *
+ * The recurrence runs independently on each sequence i = tokens
+ * cu_seqlens[i] .. cu_seqlens[i+1] - 1 of the packed tensors, from S0[i]; a
+ * sequence boundary is an independent restart of the same operator, so the
+ * result for each sequence equals gdr_chunk_fwd on that sequence alone.
+ *
+ *   cu_seqlens  device int32 [n_seq + 1], 0 = cu[0] <= cu[1] <= ... <= cu[n_seq]
+ *               = T (not checked by the library: the kernels clamp each entry to
+ *               [0, T] and each length to >= 0, so a malformed table cannot make
+ *               them read or write outside the tensors, but its results are
+ *               undefined).  Empty sequences are allowed (S_T[i] = S0[i]).
+ *   q, k   [1, T, H, d_k] bf16   v, o [1, T, H, d_v] bf16   beta [1, T, H] bf16
+ *   log_a  NULL / [1, T, H] / [1, T, H, d_k] bf16
+ *   S0     [n_seq, H, d_k, d_v] fp32 or NULL;  S_T [n_seq, H, d_k, d_v] fp32 or NULL
+ *   workspace  at least gdr_chunk_fwd_varlen_workspace_size() bytes.
+ * Other rules (alignment, aliasing, errors) as for gdr_chunk_fwd; desc->B must be
+ * 1 and desc->io GDR_BF16.
+ */
+gdr_status gdr_chunk_fwd_varlen(const gdr_desc* desc, const int32_t* cu_seqlens, int64_t n_seq,
+                                const void* q, const void* k, const void* v, const void* beta,
+                                const void* log_a, const float* S0, void* o, float* S_T,
+                                void* workspace, size_t workspace_bytes, void* stream /* hipStream_t */);
+
+/*
  * gdr_recurrent_step -- one decode token for B independent sequences.
  *
  * One step of the recurrence above with a constant-size state ("Moonshot AI's

@@ -167,3 +167,45 @@ def test_decode_checks(lib):
     p[5] = None
     assert _step(lib, _desc(T=1), p) == INVALID
     assert _step(lib, _desc(T=1, d_k=32), _ptrs()) == UNSUPPORTED
+
+
+# ---- packed variable-length sequences -------------------------------------------------------
+def _ws_varlen(lib, d, n_seq):
+    n = ctypes.c_size_t(12345)
+    st = lib.gdr_chunk_fwd_varlen_workspace_size(None if d is None else ctypes.byref(d), n_seq, ctypes.byref(n))
+    return st, n.value
+
+
+def _chunk_varlen(lib, d, cu, n_seq, ptrs, ws_bytes=None):
+    q, k, v, beta, log_a, S0, o, S_T = ptrs[:8]
+    ws = ptrs[8] if len(ptrs) > 8 else None
+    if ws_bytes is None:
+        ws_bytes = _ws_varlen(lib, d, n_seq)[1] if d is not None else 0
+    return lib.gdr_chunk_fwd_varlen(None if d is None else ctypes.byref(d), cu, n_seq, q, k, v, beta, log_a, S0, o,
+                                    S_T, ws, ws_bytes, None)
+
+
+def test_varlen_workspace_size(lib):
+    rec = 2 * 10 * 256 * 2 + 6 * 64 * 4
+    # record slots per head: ceil(T / 64) + n_seq (sequence i starts at slot floor(cu[i] / 64) + i)
+    assert _ws_varlen(lib, _desc(T=130, H=3), 4) == (OK, 3 * (3 + 4) * rec)
+    assert _ws_varlen(lib, _desc(T=130, H=3, gate=2), 2) == (OK, 3 * (3 + 2) * (rec + 3 * 64 * 128 * 2))
+    assert _ws_varlen(lib, _desc(T=130, H=3), 0) == (INVALID, 0)
+    assert _ws_varlen(lib, _desc(B=2), 2) == (INVALID, 0)                  # packed tensors take B = 1
+    assert _ws_varlen(lib, _desc(io=0, d_k=64), 2) == (UNSUPPORTED, 0)     # bf16 only
+    assert _ws_varlen(lib, None, 2) == (INVALID, 0)
+
+
+def test_varlen_argument_checks(lib):
+    cu = FAKE + 0x7F000000                     # never dereferenced
+    assert _chunk_varlen(lib, _desc(B=2), cu, 2, _ptrs()) == INVALID
+    assert _chunk_varlen(lib, _desc(), None, 2, _ptrs()) == INVALID
+    assert b"cu_seqlens" in lib.gdr_last_error()
+    assert _chunk_varlen(lib, _desc(), cu, 0, _ptrs()) == INVALID
+    assert _chunk_varlen(lib, _desc(io=0, d_k=64), cu, 2, _ptrs()) == UNSUPPORTED
+    assert _chunk_varlen(lib, _desc(), cu + 2, 2, _ptrs()) == ALIGN
+    p = _ptrs()
+    assert _chunk_varlen(lib, _desc(), p[6] + 16, 2, p) == INVALID        # offsets inside o
+    assert b"overlaps" in lib.gdr_last_error()
+    need = _ws_varlen(lib, _desc(), 2)[1]
+    assert _chunk_varlen(lib, _desc(), cu, 2, _ptrs(), ws_bytes=need - 1) == INVALID

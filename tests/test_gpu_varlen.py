@@ -1,0 +1,138 @@
+"""GPU parity of gdr_chunk_fwd_varlen (variable-length sequences packed along T)
+against the fp64 oracle run on each sequence alone, and the prefill -> decode
+handoff (the packed forward's final states feed gdr_recurrent_step).
+
+A sequence boundary restarts the recurrence from that sequence's own initial
+state, so each packed sequence must match the oracle of that sequence alone
+(tolerance as for gdr_chunk_fwd: relative L2 2e-2 for bf16 I/O), and must equal
+bit for bit what gdr_chunk_fwd gives for the sequence on its own.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import forward as oracle_forward, recurrent_step as oracle_step, rel_l2
+from tests.gpu_util import TOL, check, dev, host, need_gpu, say
+from workloads import Workload, chunk_inputs
+
+pytestmark = pytest.mark.gpu
+
+LENS = [0, 1, 63, 64, 65, 130, 200, 7]          # empty, single token, around a chunk, several chunks
+
+
+def _inputs(lens, H, dk, dv, gate, seed):
+    """Packed tokens of all sequences ([1, sum(lens), H, .]) and one initial state per sequence."""
+    T = int(sum(lens))
+    inp = chunk_inputs(Workload("varlen", B=1, T=T, H=H, d_k=dk, d_v=dv, io="bf16", gate=gate, s0_std=0.0,
+                                seed=seed))
+    S0 = chunk_inputs(Workload("varlen_s0", B=len(lens), T=1, H=H, d_k=dk, d_v=dv, io="bf16", gate=gate,
+                               s0_std=0.02, seed=seed + 1))["S0"]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    return inp, S0, cu
+
+
+def _seq(a, lo, hi):
+    return None if a is None else np.ascontiguousarray(a[:, lo:hi])
+
+
+def _oracle(inp, S0, cu, form="page"):
+    N = len(cu) - 1
+    o = np.zeros(inp["v"].shape)
+    S = np.zeros(S0.shape)
+    for i in range(N):
+        lo, hi = int(cu[i]), int(cu[i + 1])
+        oi, Si = oracle_forward(*(_seq(inp[n], lo, hi) for n in ("q", "k", "v", "beta", "log_a")), S0[i:i + 1],
+                                form=form)
+        o[:, lo:hi] = oi
+        S[i] = Si[0]
+    return o, S
+
+
+def _gpu(inp, S0, cu, form="page"):
+    import torch
+    import gated_delta_rule_21_amd as gdr
+    o, S = gdr.chunk_fwd_varlen(*(dev(inp[n], "bf16") for n in ("q", "k", "v", "beta", "log_a")),
+                                torch.from_numpy(cu).cuda(), torch.from_numpy(S0).cuda(), form=form)
+    torch.cuda.synchronize()
+    return o, S
+
+
+def _check_each(o, S, o_ref, S_ref, cu):
+    check("o", host(o), o_ref, TOL["bf16"])
+    check("S_T", host(S), S_ref, TOL["bf16"])
+    Sh = host(S)
+    for i in range(len(cu) - 1):            # every sequence on its own, short ones included
+        e = rel_l2(Sh[i], S_ref[i])
+        assert e <= TOL["bf16"], f"sequence {i} (length {cu[i + 1] - cu[i]}): S_T rel_l2 {e:.3e}"
+
+
+@pytest.mark.parametrize("gate", ["none", "scalar", "channel"])
+@pytest.mark.parametrize("dk", [128, 64])
+def test_varlen_matches_oracle_per_sequence(gate, dk):
+    need_gpu()
+    say(f"case varlen gate={gate} d_k={dk} lens={LENS}")
+    inp, S0, cu = _inputs(LENS, 2, dk, 128, gate, seed=61 + dk + len(gate))
+    o, S = _gpu(inp, S0, cu)
+    o_ref, S_ref = _oracle(inp, S0, cu)
+    _check_each(o, S, o_ref, S_ref, cu)
+
+
+def test_varlen_literal_ordering():
+    need_gpu()
+    inp, S0, cu = _inputs(LENS, 2, 128, 128, "channel", seed=71)
+    o, S = _gpu(inp, S0, cu, form="literal")
+    o_ref, S_ref = _oracle(inp, S0, cu, form="literal")
+    _check_each(o, S, o_ref, S_ref, cu)
+
+
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+def test_varlen_equals_separate_calls(gate):
+    """Each packed sequence gives bit for bit what gdr_chunk_fwd gives on it alone."""
+    need_gpu()
+    import torch
+    import gated_delta_rule_21_amd as gdr
+    inp, S0, cu = _inputs(LENS, 2, 128, 128, gate, seed=73)
+    o, S = _gpu(inp, S0, cu)
+    o, S = o.cpu(), S.cpu()
+    for i in range(len(cu) - 1):
+        lo, hi = int(cu[i]), int(cu[i + 1])
+        if hi == lo:
+            assert torch.equal(S[i], torch.from_numpy(S0[i])), f"empty sequence {i}: S_T != S0"
+            continue
+        oi, Si = gdr.chunk_fwd(*(dev(_seq(inp[n], lo, hi), "bf16") for n in ("q", "k", "v", "beta", "log_a")),
+                               torch.from_numpy(S0[i:i + 1]).cuda())
+        torch.cuda.synchronize()
+        assert torch.equal(o[:, lo:hi], oi.cpu()), f"sequence {i}: o differs"
+        assert torch.equal(S[i:i + 1], Si.cpu()), f"sequence {i}: S_T differs"
+
+
+def test_varlen_many_sequences_wide():
+    """More workgroups than CUs (4 x 64 heads x 2 tiles), lengths from 1 to 300."""
+    need_gpu()
+    rs = np.random.RandomState(5)
+    lens = [int(x) for x in rs.randint(1, 300, size=4)]
+    inp, S0, cu = _inputs(lens, 64, 128, 128, "scalar", seed=79)
+    o, S = _gpu(inp, S0, cu)
+    o_ref, S_ref = _oracle(inp, S0, cu)
+    _check_each(o, S, o_ref, S_ref, cu)
+
+
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+def test_prefill_then_decode_handoff(gate):
+    """Packed prefill, then one decode token per sequence from the prefill's final
+    states, equals the oracle over each sequence plus that token."""
+    need_gpu()
+    import torch
+    import gated_delta_rule_21_amd as gdr
+    lens = [1, 64, 65, 200]
+    N, H, dk, dv = len(lens), 2, 128, 128
+    inp, S0, cu = _inputs(lens, H, dk, dv, gate, seed=83)
+    tok = chunk_inputs(Workload("next", B=N, T=1, H=H, d_k=dk, d_v=dv, io="bf16", gate=gate, s0_std=0.0, seed=89))
+    _, S = _gpu(inp, S0, cu)
+    step = {n: (None if tok[n] is None else np.ascontiguousarray(tok[n][:, 0])) for n in ("q", "k", "v", "beta", "log_a")}
+    o_dec, S_dec = gdr.recurrent_step(*(dev(step[n], "bf16") for n in ("q", "k", "v", "beta", "log_a")), S)
+    torch.cuda.synchronize()
+    _, S_pre = _oracle(inp, S0, cu)
+    o_ref, S_ref = oracle_step(S_pre, step["q"], step["k"], step["v"], step["beta"], step["log_a"])
+    check("decode o", host(o_dec), o_ref, TOL["bf16"])
+    check("decode S", host(S_dec), S_ref, TOL["bf16"])
