@@ -6,7 +6,10 @@ B=8, H=16, T=8192, d_k=d_v=128, chunk 64, bf16 I/O, fp32 state), which runs ever
 stage of the chunkwise forward (log-gate scan, intra-chunk WY terms, state pass,
 output, final state).  The headline value is tokens/s (B*T per step) with the
 inputs already resident in HBM.  The decode step (256 sequences x 32 heads,
-fp32 128x128 states, bf16 tokens) is timed in the same run and reported as GB/s.
+fp32 128x128 states, bf16 tokens) is timed in the same run and reported as GB/s,
+and so is the serving handoff: a packed prefill of 32 prompts of log-uniform
+lengths in [128, 8192] (H=16, d=128, scalar gate) through gdr_chunk_fwd_varlen,
+then decode steps on the states it hands over (`handoff`).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
@@ -214,6 +217,73 @@ def bench_decode(args, log):
                          "traffic": profiled_traffic("decode_step_n256h32d128_counters.md", DECODE_SOURCES)}}
 
 
+def handoff_lengths(n_seq: int = 32, lo: int = 128, hi: int = 8192, seed: int = 6):
+    """Prompt lengths of the serving mix: log-uniform on [lo, hi], seeded."""
+    import numpy as np
+    rs = np.random.RandomState(seed)
+    return [int(round(x)) for x in np.exp(rs.uniform(np.log(lo), np.log(hi), size=n_seq))]
+
+
+def bench_handoff(args, log):
+    """Packed prefill of a batch of prompts of mixed lengths, then decode steps on the
+    states it hands over (the serving steps on either side of the chunk forward)."""
+    import numpy as np
+    import torch
+    import gated_delta_rule_21_amd as gdr
+    from workloads import Workload, chunk_inputs
+    lens = handoff_lengths()
+    N, H, dk, dv, total = len(lens), 16, 128, 128, int(sum(lens))
+    log(f"generating the handoff mix ({N} prompts, {total} tokens)")
+    inp = chunk_inputs(Workload("handoff_prefill", B=1, T=total, H=H, d_k=dk, d_v=dv, io="bf16", gate="scalar",
+                                s0_std=0.0, seed=6))
+    n_sets = 16
+    tok = chunk_inputs(Workload("handoff_tokens", B=N, T=n_sets, H=H, d_k=dk, d_v=dv, io="bf16", gate="scalar",
+                                s0_std=0.0, seed=7))
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).cuda()
+    q, k, v, beta, log_a = (dev(inp[n]) for n in ("q", "k", "v", "beta", "log_a"))
+    tq, tk, tv, tb, tl = ([dev(tok[n][:, j]) for j in range(n_sets)] for n in ("q", "k", "v", "beta", "log_a"))
+    del inp, tok
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device="cuda")
+    o = torch.empty((1, total, H, dv), dtype=torch.bfloat16, device="cuda")
+    S = torch.empty((N, H, dk, dv), dtype=torch.float32, device="cuda")
+    od = torch.empty((N, H, dv), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(gdr.chunk_varlen_workspace_size(total, N, H, dk, dv, torch.bfloat16, "scalar"),
+                     dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    prefill = lambda: gdr.chunk_fwd_varlen(q, k, v, beta, log_a, cu, None, o=o, S_T=S, workspace=ws)
+    decode = lambda j: gdr.recurrent_step(tq[j % n_sets], tk[j % n_sets], tv[j % n_sets], tb[j % n_sets],
+                                          tl[j % n_sets], S, o=od)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    reps, dsteps = 5, 200
+    for _ in range(2):
+        prefill()
+        decode(0)
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for _ in range(reps):
+        prefill()
+    ev[1].record(stream)
+    prefill()
+    decode(0)
+    ev[2].record(stream)
+    for j in range(1, dsteps + 1):
+        decode(j)
+    ev[3].record(stream)
+    torch.cuda.synchronize()
+    pre_ms = ev[0].elapsed_time(ev[1]) / reps
+    first_ms = ev[1].elapsed_time(ev[2])
+    dec_ms = ev[2].elapsed_time(ev[3]) / dsteps
+    dec_bytes = N * H * (2 * 4 * dk * dv + 2 * (2 * dk + 2 * dv + 2))
+    log(f"handoff: prefill {pre_ms:.3f} ms ({total / (pre_ms * 1e-3) / 1e6:.1f} M tokens/s), "
+        f"decode {dec_ms * 1e3:.1f} us/step")
+    return {"workload": "handoff_gated_n%d_h%d_d%d_loguniform128-8192" % (N, H, dk),
+            "n_seq": N, "total_tokens": total, "min_len": min(lens), "max_len": max(lens),
+            "prefill_ms": round(pre_ms, 4), "prefill_tokens_per_s": round(total / (pre_ms * 1e-3), 1),
+            "prefill_plus_first_decode_ms": round(first_ms, 4),
+            "decode_us_per_step": round(dec_ms * 1e3, 2), "decode_steps": dsteps,
+            "decode_GBps": round(dec_bytes / (dec_ms * 1e-3) / 1e9, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -223,6 +293,8 @@ def main():
     ap.add_argument("--chunk-config", type=int, default=3, choices=(2, 3, 4),
                     help="chunk-forward workload (3 = the gated workload of the headline metric)")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-handoff", action="store_true",
+                    help="skip the packed-prefill -> decode handoff leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-T", type=int, default=8192)
     ap.add_argument("--cpu-heads", type=int, default=16)
@@ -257,6 +329,7 @@ def main():
     gbs = nbytes / (ms * 1e-3) / 1e9
     tflops = flops / (ms * 1e-3) / 1e12
     decode = None if args.no_decode else bench_decode(args, log)
+    handoff = None if args.no_handoff else bench_handoff(args, log)
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle sample")
@@ -288,6 +361,7 @@ def main():
         "algorithmic_bytes_per_launch": nbytes,
         "useful_flops_per_launch": flops,
         "decode": decode,
+        "handoff": handoff,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
