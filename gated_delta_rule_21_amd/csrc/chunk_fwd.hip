@@ -474,7 +474,16 @@ hipError_t launch_chunk_fwd(const ChunkParams& p, hipStream_t stream) {
   hipError_t e = launch_chunk_prep(p, stream);
   if (e != hipSuccess) return e;
   // bf16 I/O: chain and helper waves (chunk_state.hip); fp32 I/O: this file's kernel
-  if (p.io == IO_BF16) return launch_chunk_state_pipe(p, stream);
+  if (p.io == IO_BF16) {
+    if (!p.cu) return launch_chunk_state_pipe(p, stream);
+    // packed sequences: the state pass takes them longest first
+    ChunkParams q = p;
+    int32_t* order = reinterpret_cast<int32_t*>(
+        static_cast<char*>(p.ws) + chunk_varlen_records_bytes(p.T, p.B, p.H, p.io, p.gate, p.d_k));
+    q.order = order;
+    if ((e = launch_varlen_order(q, order, stream)) != hipSuccess) return e;
+    return launch_chunk_state_pipe(q, stream);
+  }
   return launch_chunk_f32(p, stream);
 }
 
@@ -483,8 +492,53 @@ size_t chunk_workspace_bytes(int64_t B, int64_t T, int64_t H, int io, int gate, 
   return static_cast<size_t>(B * H * nchunks) * rec_bytes(io, gate, d_k);
 }
 
-size_t chunk_varlen_workspace_bytes(int64_t T, int64_t n_seq, int64_t H, int io, int gate, int d_k) {
+size_t chunk_varlen_records_bytes(int64_t T, int64_t n_seq, int64_t H, int io, int gate, int d_k) {
   return static_cast<size_t>(H * chunk_varlen_slots(T, n_seq)) * rec_bytes(io, gate, d_k);
+}
+
+size_t chunk_varlen_workspace_bytes(int64_t T, int64_t n_seq, int64_t H, int io, int gate, int d_k) {
+  return chunk_varlen_records_bytes(T, n_seq, H, io, gate, d_k) + static_cast<size_t>((n_seq * 4 + 15) / 16 * 16);
+}
+
+// Rank of each packed sequence by length, longest first (ties by index): thread i
+// counts the sequences that go before it.  The lengths pass through LDS in tiles.
+// Above VARLEN_RANK_MAX sequences the order is the identity.
+constexpr int64_t VARLEN_RANK_MAX = 16384;
+__device__ __forceinline__ int64_t clamped_len(const ChunkParams& p, int64_t j) {   // as in seq_span
+  int64_t a = p.cu[j], e = p.cu[j + 1];
+  a = a < 0 ? 0 : (a > p.T ? p.T : a);
+  e = e < a ? a : (e > p.T ? p.T : e);
+  return e - a;
+}
+
+__global__ __launch_bounds__(256) void varlen_order_kernel(ChunkParams p, int32_t* order) {
+  __shared__ int64_t tile[256];
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t N = p.B;
+  const int64_t li = i < N ? clamped_len(p, i) : 0;
+  if (N > VARLEN_RANK_MAX) {
+    if (i < N) order[i] = static_cast<int32_t>(i);
+    return;
+  }
+  int64_t rank = 0;
+  for (int64_t j0 = 0; j0 < N; j0 += 256) {
+    __syncthreads();
+    const int64_t j = j0 + threadIdx.x;
+    if (j < N) tile[threadIdx.x] = clamped_len(p, j);
+    __syncthreads();
+    const int64_t n = N - j0 < 256 ? N - j0 : 256;
+    for (int64_t t = 0; t < n; ++t) {
+      const int64_t lj = tile[t];
+      rank += (lj > li || (lj == li && j0 + t < i)) ? 1 : 0;
+    }
+  }
+  if (i < N) order[rank] = static_cast<int32_t>(i);
+}
+
+hipError_t launch_varlen_order(const ChunkParams& p, int32_t* order, hipStream_t stream) {
+  const unsigned nb = static_cast<unsigned>((p.B + 255) / 256);
+  hipLaunchKernelGGL(varlen_order_kernel, dim3(nb), dim3(256), 0, stream, p, order);
+  return hipGetLastError();
 }
 
 }  // namespace gdr

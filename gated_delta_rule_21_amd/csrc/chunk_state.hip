@@ -100,13 +100,30 @@ __global__ __launch_bounds__((NCH + NHW) * 64) void chunk_state_pipe_kernel(Chun
     return reinterpret_cast<T*>(smem + L::OFF_P + (n & 1) * L::PB);
   };
 
-  // Block -> (head, d_v tile); consecutive logical blocks on one XCD (block ids
-  // are dealt round-robin over 8 XCDs), so a head's tiles share that L2.
+  // Block -> (sequence, head, d_v tile).  Block ids are dealt round-robin over the
+  // 8 XCDs and each XCD runs its share in order.  Fixed-length batches: consecutive
+  // logical blocks on one XCD, so a head's tiles share that L2.  Packed sequences:
+  // (sequence, head) items longest sequence first, item i on XCD i % 8 with its
+  // tiles side by side there, so the longest chains start first everywhere.
   const int nblk = gridDim.x;
-  int lb = blockIdx.x;
-  if ((nblk & 7) == 0) lb = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
-  const int64_t bh = lb / n_tiles;
-  const int tile = lb % n_tiles;
+  int64_t bh;
+  int tile;
+  if (p.order && (p.B * p.H) % 8 == 0) {
+    const int xcd = blockIdx.x & 7, pos = blockIdx.x >> 3;
+    const int64_t item = static_cast<int64_t>(pos / n_tiles) * 8 + xcd;
+    tile = pos % n_tiles;
+    bh = static_cast<int64_t>(p.order[item / p.H]) * p.H + item % p.H;
+  } else if (p.order) {
+    const int64_t item = blockIdx.x / n_tiles;
+    tile = blockIdx.x % n_tiles;
+    bh = static_cast<int64_t>(p.order[item / p.H]) * p.H + item % p.H;
+  } else {
+    int lb = blockIdx.x;
+    if ((nblk & 7) == 0) lb = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
+    bh = lb / n_tiles;
+    tile = lb % n_tiles;
+  }
+  bh = uni64(bh);
   const int64_t bb = bh / p.H, hh = bh % p.H;
   const int dv = p.d_v;
   const int col0 = tile * DVT;

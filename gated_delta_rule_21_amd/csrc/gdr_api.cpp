@@ -195,6 +195,7 @@ gdr_status chunk_fwd_impl(const gdr_desc* d, const int32_t* cu, int64_t n_seq, c
   p.io = d->io; p.gate = d->gate; p.literal = d->form == GDR_FORM_LITERAL;
   p.cu = cu;
   p.nslots = packed ? gdr::chunk_varlen_slots(d->T, n_seq) : 0;
+  p.order = nullptr;
   if (d->T == 0 && !S_T) return GDR_OK;
   hipError_t e = gdr::launch_chunk_fwd(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(GDR_ERR_HIP, "chunk forward launch failed: %s", hipGetErrorString(e));

@@ -38,6 +38,7 @@ struct ChunkParams {
   // nslots = records per head in the workspace (chunk_varlen_slots).
   const int32_t* cu;
   int64_t nslots;
+  const int32_t* order;   // packed sequences: longest first (in the workspace, after the records)
 };
 
 hipError_t launch_decode_step(const DecodeParams& p, hipStream_t stream);
@@ -48,8 +49,13 @@ hipError_t launch_chunk_fwd(const ChunkParams& p, hipStream_t stream);
 // B*H*ceil(T/64) records of the per-chunk transform (see WsRec in chunk_common.h)
 size_t chunk_workspace_bytes(int64_t B, int64_t T, int64_t H, int io, int gate, int d_k);
 // Packed sequences: record slots per head for n_seq sequences of T tokens in all
-// (sequence b's chunks start at slot floor(cu[b] / 64) + b), and the workspace bytes.
+// (sequence b's chunks start at slot floor(cu[b] / 64) + b), and the workspace bytes:
+// the records, then the order of the sequences by length (n_seq int32, 16-byte
+// padded) in which the state pass takes them.
 inline int64_t chunk_varlen_slots(int64_t T, int64_t n_seq) { return (T + 63) / 64 + n_seq; }
+size_t chunk_varlen_records_bytes(int64_t T, int64_t n_seq, int64_t H, int io, int gate, int d_k);
 size_t chunk_varlen_workspace_bytes(int64_t T, int64_t n_seq, int64_t H, int io, int gate, int d_k);
+// Longest-first order of packed sequences into `order` (n_seq int32).
+hipError_t launch_varlen_order(const ChunkParams& p, int32_t* order, hipStream_t stream);
 
 }  // namespace gdr

@@ -150,7 +150,9 @@ gdr_status gdr_chunk_fwd(const gdr_desc* desc, const void* q, const void* k, con
  * tokens); n_seq >= 1 is the number of sequences.  Sequence i's chunks use
  * record slots from floor(cu_seqlens[i] / 64) + i on, so H * (ceil(T / 64) +
  * n_seq) records of the size given under gdr_chunk_fwd_workspace_size cover
- * any split of the T tokens.  bf16 I/O only (GDR_ERR_UNSUPPORTED otherwise).
+ * any split of the T tokens; then 4 * n_seq bytes (rounded up to 16) hold the
+ * order, longest sequence first, in which the state pass takes the sequences.
+ * bf16 I/O only (GDR_ERR_UNSUPPORTED otherwise).
  */
 gdr_status gdr_chunk_fwd_varlen_workspace_size(const gdr_desc* desc, int64_t n_seq, size_t* bytes);
 

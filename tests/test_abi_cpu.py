@@ -187,9 +187,11 @@ def _chunk_varlen(lib, d, cu, n_seq, ptrs, ws_bytes=None):
 
 def test_varlen_workspace_size(lib):
     rec = 2 * 10 * 256 * 2 + 6 * 64 * 4
-    # record slots per head: ceil(T / 64) + n_seq (sequence i starts at slot floor(cu[i] / 64) + i)
-    assert _ws_varlen(lib, _desc(T=130, H=3), 4) == (OK, 3 * (3 + 4) * rec)
-    assert _ws_varlen(lib, _desc(T=130, H=3, gate=2), 2) == (OK, 3 * (3 + 2) * (rec + 3 * 64 * 128 * 2))
+    # record slots per head: ceil(T / 64) + n_seq (sequence i starts at slot floor(cu[i] / 64) + i),
+    # then the longest-first order of the sequences (n_seq int32, padded to 16 bytes)
+    assert _ws_varlen(lib, _desc(T=130, H=3), 4) == (OK, 3 * (3 + 4) * rec + 16)
+    assert _ws_varlen(lib, _desc(T=130, H=3), 5) == (OK, 3 * (3 + 5) * rec + 32)
+    assert _ws_varlen(lib, _desc(T=130, H=3, gate=2), 2) == (OK, 3 * (3 + 2) * (rec + 3 * 64 * 128 * 2) + 16)
     assert _ws_varlen(lib, _desc(T=130, H=3), 0) == (INVALID, 0)
     assert _ws_varlen(lib, _desc(B=2), 2) == (INVALID, 0)                  # packed tensors take B = 1
     assert _ws_varlen(lib, _desc(io=0, d_k=64), 2) == (UNSUPPORTED, 0)     # bf16 only

@@ -136,3 +136,26 @@ def test_prefill_then_decode_handoff(gate):
     o_ref, S_ref = oracle_step(S_pre, step["q"], step["k"], step["v"], step["beta"], step["log_a"])
     check("decode o", host(o_dec), o_ref, TOL["bf16"])
     check("decode S", host(S_dec), S_ref, TOL["bf16"])
+
+
+def test_varlen_order_longest_first():
+    """The state pass takes packed sequences longest first: the order it leaves at
+    the end of the caller's workspace is a permutation sorted by length, ties by
+    index; with N * H not a multiple of 8 (the non-interleaved block mapping)."""
+    need_gpu()
+    import torch
+    import gated_delta_rule_21_amd as gdr
+    lens = [5, 300, 64, 300, 0, 17, 129]
+    N, H = len(lens), 3
+    inp, S0, cu = _inputs(lens, H, 128, 128, "scalar", seed=97)
+    size = gdr.chunk_varlen_workspace_size(int(sum(lens)), N, H, 128, 128, torch.bfloat16, "scalar")
+    ws = torch.zeros(size, dtype=torch.uint8, device="cuda")
+    o, S = gdr.chunk_fwd_varlen(*(dev(inp[n], "bf16") for n in ("q", "k", "v", "beta", "log_a")),
+                                torch.from_numpy(cu).cuda(), torch.from_numpy(S0).cuda(), workspace=ws)
+    torch.cuda.synchronize()
+    tail = (N * 4 + 15) // 16 * 16
+    order = ws[size - tail:size - tail + 4 * N].cpu().view(torch.int32).numpy()
+    want = sorted(range(N), key=lambda i: (-lens[i], i))
+    assert list(order) == want, (list(order), want)
+    o_ref, S_ref = _oracle(inp, S0, cu)
+    _check_each(o, S, o_ref, S_ref, cu)
