@@ -13,6 +13,10 @@ Sources (web pages; cited by title and section):
                  Preconditioning in Linear Attention", Technical Summary §1
                  "Problem Statement" -- the delta rule as one online gradient
                  step on the per-token regression loss 0.5*||S k - v||^2.
+  [OSDN §2.1]    same page, §2.1 "Algebraic Equivalence and Hardware
+                 Preservation" -- right-preconditioning that step by
+                 diag(d_t) writes along the scaled key k~_t = d_t * k_t while
+                 the residual still reads the state along k_t.
 
 What is computed (the plain definition; no chunking, no reordering).  The
 state is key-major, S in R^{d_k x d_v}.  For each (batch, head) independently
@@ -38,6 +42,11 @@ evidence, in the design notes):
   * erase=False drops the erase term: S_t = D_t S_{t-1} + beta_t k_t v_t^T (the
     write-only linear-attention state of [Moonshot §2]).  Used by pins only.
   * No query scaling, no normalisation of q or k inside the operator.
+  * kw (optional) is the write key of [OSDN §2.1]: the step becomes
+    S_t = S~ + kw_t delta^T with delta still from S~^T k_t, i.e. key-major
+    S_t = (I - beta_t kw_t k_t^T) S~ + beta_t kw_t v_t^T.  kw = k is the
+    update above.  The pages give it for the ungated delta rule; with a gate the
+    decay is applied first as above (a reading, used only if asked for).
 
 Parity status: pinned (see the oracle pin tests): special cases, closed forms,
 invariants, an exact-rational brute force of the transition-matrix product,
@@ -63,11 +72,12 @@ def gate_kind(beta: np.ndarray, log_a: np.ndarray | None, k: np.ndarray) -> str:
     raise ValueError(f"log_a shape {log_a.shape} matches neither beta {beta.shape} nor k {k.shape}")
 
 
-def recurrent_step(S, q, k, v, beta, log_a=None, *, form="page", erase=True):
+def recurrent_step(S, q, k, v, beta, log_a=None, *, form="page", erase=True, kw=None):
     """One token of the recurrence for a batch of independent states.
 
     S: [..., d_k, d_v]; q, k: [..., d_k]; v: [..., d_v]; beta: [...];
-    log_a: None, [...] (scalar gate) or [..., d_k] (per key channel).
+    log_a: None, [...] (scalar gate) or [..., d_k] (per key channel);
+    kw: None (write along k) or the write key [..., d_k] of [OSDN §2.1].
     Returns (o [..., d_v], S_new [..., d_k, d_v]), all float64.
     """
     if form not in ("page", "literal"):
@@ -96,16 +106,18 @@ def recurrent_step(S, q, k, v, beta, log_a=None, *, form="page", erase=True):
     else:
         delta = beta[..., None] * v
 
-    S_new = S_dec + k[..., :, None] * delta[..., None, :]         # + k delta^T
+    k_write = k if kw is None else np.asarray(kw, dtype=np.float64)
+    S_new = S_dec + k_write[..., :, None] * delta[..., None, :]   # + k delta^T (kw delta^T)
     o = np.einsum("...kv,...k->...v", S_new, q)                   # S_t^T q_t
     return o, S_new
 
 
-def forward(q, k, v, beta, log_a=None, S0=None, *, form="page", erase=True):
+def forward(q, k, v, beta, log_a=None, S0=None, *, form="page", erase=True, kw=None):
     """Run the recurrence over a whole sequence.
 
     Layouts (token-major): q, k [B, T, H, d_k]; v [B, T, H, d_v]; beta [B, T, H];
-    log_a None, [B, T, H] or [B, T, H, d_k]; S0 None (zeros) or [B, H, d_k, d_v].
+    log_a None, [B, T, H] or [B, T, H, d_k]; S0 None (zeros) or [B, H, d_k, d_v];
+    kw None or the write keys [B, T, H, d_k] ([OSDN §2.1]).
     Returns (o [B, T, H, d_v], S_T [B, H, d_k, d_v]) in float64.
     """
     q = np.asarray(q, dtype=np.float64)
@@ -122,7 +134,7 @@ def forward(q, k, v, beta, log_a=None, S0=None, *, form="page", erase=True):
     for t in range(T):
         la = None if kind == "none" else log_a[:, t]
         o[:, t], S = recurrent_step(S, q[:, t], k[:, t], v[:, t], beta[:, t], la,
-                                    form=form, erase=erase)
+                                    form=form, erase=erase, kw=None if kw is None else kw[:, t])
     return o, S
 
 

@@ -23,13 +23,21 @@ Per chunk of c rows (state S entering the chunk, key-major d_k x d_v):
     Delta  U - W S
     O      (Q * exp(g)) S + lower_incl((Q * exp(g)) Kb^T) Delta
     S'     diag(exp(g_c)) S + (K * exp(g_c - g))^T Delta
+
+With a write key kw ("OSDN: Improving Delta Rule with Provable Online
+Preconditioning in Linear Attention", §2.1: the write side of the step uses
+k~ = d * k, the read side k), the key in the Gram matrix's columns, in the
+scores and in the state write becomes kw: Kb = KW * exp(-g) and
+S' = diag(exp(g_c)) S + (KW * exp(g_c - g))^T Delta, while Kr (the rows of the
+Gram matrix and the read of S) stays K.
 """
 
 import numpy as np
 
 
-def chunk_forward(q, k, v, beta, log_a, S0, C, form="page", keep=False):
+def chunk_forward(q, k, v, beta, log_a, S0, C, form="page", keep=False, kw=None):
     q, k, v, beta = (np.asarray(x, np.float64) for x in (q, k, v, beta))
+    kw = k if kw is None else np.asarray(kw, np.float64)
     B, T, H, dk = k.shape
     dv = v.shape[-1]
     o = np.zeros((B, T, H, dv))
@@ -42,6 +50,7 @@ def chunk_forward(q, k, v, beta, log_a, S0, C, form="page", keep=False):
                 c1 = min(T, c0 + C)
                 c = c1 - c0
                 K, Q, V, be = k[b, c0:c1, h], q[b, c0:c1, h], v[b, c0:c1, h], beta[b, c0:c1, h]
+                KW = kw[b, c0:c1, h]
                 if log_a is None:
                     L = np.zeros((c, dk))
                 elif np.ndim(log_a) == 3:
@@ -51,7 +60,7 @@ def chunk_forward(q, k, v, beta, log_a, S0, C, form="page", keep=False):
                 g = np.cumsum(L, axis=0)
                 g_read = g if form == "page" else g - L
                 Kr = K * np.exp(g_read)
-                Kb = K * np.exp(-g)
+                Kb = KW * np.exp(-g)
                 A = np.tril(be[:, None] * (Kr @ Kb.T), -1)
                 Tm = np.linalg.inv(np.eye(c) + A)
                 W = Tm @ (be[:, None] * Kr)
@@ -62,6 +71,6 @@ def chunk_forward(q, k, v, beta, log_a, S0, C, form="page", keep=False):
                 o[b, c0:c1, h] = Qh @ S + P @ D
                 if keep and b == 0 and h == 0:
                     inter.append(dict(g=g, A=A, T=Tm, W=W, U=U, Delta=D, P=P, S_in=S.copy()))
-                S = np.exp(g[-1])[:, None] * S + (K * np.exp(g[-1] - g)).T @ D
+                S = np.exp(g[-1])[:, None] * S + (KW * np.exp(g[-1] - g)).T @ D
             S_out[b, h] = S
     return (o, S_out, inter) if keep else (o, S_out)

@@ -16,6 +16,12 @@ Sources:
                  (delta rule = one gradient step on 0.5*||S k - v||^2).
   [OSDN §3]      same page, §3 Theoretical Guarantees (gated Newton condition
                  beta * <d, k^2> = 1; with d = 1 it reads beta * ||k||^2 = 1).
+  [OSDN §2.1-2.2] same page: the right-preconditioned step writes along
+                 k~ = d * k (§2.1), and its surrogate
+                 h = (f(S_t) - f(S_{t-1})) / ||grad f(S_{t-1})||^2 has the closed
+                 form ((1 - beta <d, k^2>)^2 - 1) / (2 ||k||^2) (§2.2).
+
+The write-key pins (WKEY_PINS) take fwd(..., kw=...) with kw the write keys.
 """
 
 from __future__ import annotations
@@ -278,6 +284,81 @@ def pin_l_norm_bound(fwd):
     v2 = np.zeros_like(v2)
     _, S_T2 = fwd(q2, k2, v2, beta2, None, S02)
     assert np.linalg.norm(S_T2) < 0.5 * np.linalg.norm(S02), "erase with v = 0 did not shrink the state"
+
+
+# ---------------------------------------------------------------------------
+# Write-key pins ([OSDN §2.1, §2.2]).
+# P-m  One step with write key kw = d * k scales the regression residual
+#      v - S^T k by exactly (1 - beta <d, k^2>), and the surrogate
+#      h = (f(S_t) - f(S_{t-1})) / ||grad f(S_{t-1})||_F^2, f(S) = 0.5 ||S^T k - v||^2,
+#      equals the page's closed form ((1 - beta <d, k^2>)^2 - 1) / (2 ||k||^2)
+#      whatever S and v are.  [OSDN §2.2]
+def pin_m_write_key_surrogate_closed_form(fwd):
+    rng = _rng(31)
+    for _ in range(4):
+        q, k, v, beta, _, S0 = _rand_inputs(rng, B=2, T=1, H=3, dk=5, dv=4, unit_keys=False)
+        d = rng.uniform(0.2, 2.0, k.shape)
+        _, S1 = fwd(q, k, v, beta, None, S0, kw=d * k)
+        kk, vv, bb, dd = k[:, 0], v[:, 0], beta[:, 0], d[:, 0]
+        r0 = vv - np.einsum("bhkv,bhk->bhv", S0, kk)
+        r1 = vv - np.einsum("bhkv,bhk->bhv", S1, kk)
+        c = 1.0 - bb * np.sum(dd * kk * kk, axis=-1)
+        _close(r1, c[..., None] * r0, tol=1e-12, what="write-key residual factor")
+        f0, f1 = 0.5 * np.sum(r0 ** 2, -1), 0.5 * np.sum(r1 ** 2, -1)
+        grad2 = np.sum(r0 ** 2, -1) * np.sum(kk ** 2, -1)          # ||(S^T k - v) k^T||_F^2
+        _close((f1 - f0) / grad2, (c ** 2 - 1.0) / (2.0 * np.sum(kk ** 2, -1)), tol=1e-10,
+               what="surrogate h closed form")
+
+
+# P-n  d = 1 (write key = key) is the plain delta rule, and a write key that is
+#      zero writes nothing: the state stays S0 and the outputs read S0.  [OSDN §2.1]
+def pin_n_write_key_special_cases(fwd):
+    q, k, v, beta, _, S0 = _rand_inputs(_rng(32))
+    o, S = fwd(q, k, v, beta, None, S0)
+    o1, S1 = fwd(q, k, v, beta, None, S0, kw=k.copy())
+    _close(o1, o, what="kw = k: o")
+    _close(S1, S, what="kw = k: S")
+    o0, S0b = fwd(q, k, v, beta, None, S0, kw=np.zeros_like(k))
+    _close(S0b, S0, what="kw = 0: S")
+    _close(o0, np.einsum("bhkv,bthk->bthv", S0, q), what="kw = 0: o = S0^T q")
+
+
+# P-o  Exact rational brute force of the write-key recurrence in matrix form,
+#        S_t = (I - beta_t kw_t k_t^T) S_{t-1} + beta_t kw_t v_t^T,   o_t = S_t^T q_t,
+#      the key-major transpose of [OSDN §2.1]'s S_t = S_{t-1} + beta_t (v_t - S_{t-1} k_t) kw_t^T.
+def pin_o_write_key_exact_rational(fwd):
+    rng = _rng(33)
+    dk, dv, T = 3, 2, 6
+
+    def rat(lo, hi, den=8):
+        return Fraction(int(rng.integers(lo * den, hi * den + 1)), den)
+
+    q = [[rat(-2, 2) for _ in range(dk)] for _ in range(T)]
+    k = [[rat(-1, 1) for _ in range(dk)] for _ in range(T)]
+    kw = [[rat(-1, 1) for _ in range(dk)] for _ in range(T)]
+    v = [[rat(-2, 2) for _ in range(dv)] for _ in range(T)]
+    beta = [Fraction(int(rng.integers(1, 8)), 8) for _ in range(T)]
+    S = [[rat(-1, 1) for _ in range(dv)] for _ in range(dk)]
+    S0 = [row[:] for row in S]
+    outs = []
+    for t in range(T):
+        M = [[(Fraction(1) if i == j else Fraction(0)) - beta[t] * kw[t][i] * k[t][j] for j in range(dk)]
+             for i in range(dk)]
+        S = _frac_matmul(M, S)
+        S = [[S[i][j] + beta[t] * kw[t][i] * v[t][j] for j in range(dv)] for i in range(dk)]
+        outs.append([sum((S[i][j] * q[t][i] for i in range(dk)), Fraction(0)) for j in range(dv)])
+    f = lambda x: np.array(x, dtype=np.float64)
+    o, S_T = fwd(f(q)[None, :, None], f(k)[None, :, None], f(v)[None, :, None], f(beta)[None, :, None], None,
+                 f(S0)[None, None], kw=f(kw)[None, :, None])
+    _close(o[0, :, 0], f(outs), tol=1e-12, what="write-key exact o")
+    _close(S_T[0, 0], f(S), tol=1e-12, what="write-key exact S_T")
+
+
+WKEY_PINS = [
+    ("P-m", pin_m_write_key_surrogate_closed_form),
+    ("P-n", pin_n_write_key_special_cases),
+    ("P-o", pin_o_write_key_exact_rational),
+]
 
 
 PINS = [

@@ -30,3 +30,15 @@ def test_chunk_form_equals_oracle(gate, form, C):
     o, S = chunk_forward(q, k, v, beta, log_a, S0, C, form=form)
     assert np.max(np.abs(o - o_ref)) <= 1e-12 * max(1, np.max(np.abs(o_ref)))
     assert np.max(np.abs(S - S_ref)) <= 1e-12 * max(1, np.max(np.abs(S_ref)))
+
+
+@pytest.mark.parametrize("C", [1, 8, 64])
+def test_write_key_chunk_form_equals_oracle(C):
+    """Write keys kw = d * k (OSDN §2.1) with d in (0.2, 2): the chunk equations with kw
+    in the Gram columns, the scores and the state write reproduce the oracle."""
+    q, k, v, beta, _, S0 = _inputs(100 + C, 1, 131, 2, 12, 7, "none")
+    d = np.random.default_rng(C).uniform(0.2, 2.0, k.shape)
+    o_ref, S_ref = forward(q, k, v, beta, None, S0, kw=d * k)
+    o, S = chunk_forward(q, k, v, beta, None, S0, C, kw=d * k)
+    assert np.max(np.abs(o - o_ref)) <= 1e-12 * max(1, np.max(np.abs(o_ref)))
+    assert np.max(np.abs(S - S_ref)) <= 1e-12 * max(1, np.max(np.abs(S_ref)))

@@ -97,3 +97,58 @@ def test_unmutated_copy_passes_every_pin():
     fwd = _make_forward("none")
     for name, pin in PINS:
         pin(fwd)
+
+
+# ---- the write key of the preconditioned step ---------------------------------------------
+def _make_wkey_forward(mutation):
+    """A copy of the (ungated) write-key recurrence with one deliberate error."""
+    def forward(q, k, v, beta, log_a=None, S0=None, *, form="page", erase=True, kw=None):
+        assert log_a is None
+        B, T, H, dk = k.shape
+        dv = v.shape[-1]
+        kw = k if kw is None else kw
+        S = np.zeros((B, H, dk, dv)) if S0 is None else np.array(S0, float)
+        o = np.zeros((B, T, H, dv))
+        for t in range(T):
+            kr, kwr = k[:, t], kw[:, t]
+            if mutation == "erase_reads_write_key":
+                kr = kwr
+            elif mutation == "keys_swapped":
+                kr, kwr = kwr, kr
+            elif mutation == "write_along_key":
+                kwr = kr
+            pred = np.einsum("...kv,...k->...v", S, kr)
+            b = beta[:, t][..., None]
+            delta = (v[:, t] - pred) if mutation == "no_beta" else b * (v[:, t] - pred)
+            S_new = S + kwr[..., :, None] * delta[..., None, :]
+            if mutation == "write_key_squared":
+                S_new = S + (kwr * kwr / np.where(kr == 0, 1, kr))[..., :, None] * delta[..., None, :]
+            o[:, t] = np.einsum("...kv,...k->...v", S if mutation == "read_before_write" else S_new, q[:, t])
+            S = S_new
+        return o, S
+
+    return forward
+
+
+WKEY_MUTATIONS = ["erase_reads_write_key", "keys_swapped", "write_along_key", "no_beta",
+                  "write_key_squared", "read_before_write"]
+
+
+@pytest.mark.parametrize("mutation", WKEY_MUTATIONS)
+def test_write_key_mutant_is_caught(mutation):
+    from tests.oracle_pins import WKEY_PINS
+    fwd = _make_wkey_forward(mutation)
+    caught = []
+    for name, pin in WKEY_PINS:
+        try:
+            pin(fwd)
+        except (AssertionError, ValueError, IndexError, np.linalg.LinAlgError):
+            caught.append(name)
+    assert caught, f"mutation {mutation!r} passed every write-key pin"
+
+
+def test_unmutated_write_key_copy_passes():
+    from tests.oracle_pins import WKEY_PINS
+    fwd = _make_wkey_forward("none")
+    for name, pin in WKEY_PINS:
+        pin(fwd)

@@ -7,13 +7,18 @@ import numpy as np
 import pytest
 
 from oracle import forward, recurrent_step, rel_l2
-from tests.oracle_pins import PINS
+from tests.oracle_pins import PINS, WKEY_PINS
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_worked_examples.json")
 
 
 @pytest.mark.parametrize("name,pin", PINS, ids=[n for n, _ in PINS])
 def test_pin(name, pin):
+    pin(forward)
+
+
+@pytest.mark.parametrize("name,pin", WKEY_PINS, ids=[n for n, _ in WKEY_PINS])
+def test_write_key_pin(name, pin):
     pin(forward)
 
 
