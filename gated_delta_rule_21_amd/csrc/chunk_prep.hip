@@ -631,6 +631,7 @@ __global__ __launch_bounds__(256) void chunk_prep_reg_kernel(ChunkParams p, int6
   constexpr int EPV = 16 / ESZ;                 // elements per 16-byte piece
   constexpr int NSTEP = DK / (4 * EPV);         // products over d_k (four lane groups, one piece each)
   static_assert(GATE != GATE_CHANNEL, "per-channel gate uses chunk_prep_lds_kernel");
+  static_assert(GATE != GATE_WKEY || IO == IO_BF16, "write key: bf16 I/O only");
   static_assert(NSTEP * 4 * EPV == DK, "d_k must split into pieces");
 
   __shared__ __attribute__((aligned(16))) float sfac[4][3 * CH];   // per wave: beta, g, g_read
@@ -661,11 +662,16 @@ __global__ __launch_bounds__(256) void chunk_prep_reg_kernel(ChunkParams p, int6
   const rsrc_t rk = make_rsrc(static_cast<const elem*>(p.k) + row0 * DK, span * DK * ESZ);
   const rsrc_t rq = make_rsrc(static_cast<const elem*>(p.q) + row0 * DK, span * DK * ESZ);
   const rsrc_t rb = make_rsrc(static_cast<const elem*>(p.beta) + row0, span * ESZ);
-  const rsrc_t rl = make_rsrc(static_cast<const elem*>(p.log_a) + row0, GATE == GATE_NONE ? 0u : span * ESZ);
+  const rsrc_t rl = make_rsrc(static_cast<const elem*>(p.log_a) + row0, GATE == GATE_SCALAR ? span * ESZ : 0u);
   auto load1 = [&](rsrc_t r, uint32_t off) -> float {
     if constexpr (IO == IO_BF16) return bf16_bits_to_f32(buf_load2(r, off, 0));
     else return __uint_as_float(buf_load4(r, off, 0));
   };
+  // Write key (GATE_WKEY): the Gram matrix pairs the key of row r with the write
+  // key of row j, A_rj = beta_r (k_r . kw_j), so kw takes the place of k on the
+  // column side of every A block.
+  constexpr bool WK = GATE == GATE_WKEY;
+  const rsrc_t rkw = make_rsrc(static_cast<const elem*>(WK ? p.kw : p.k) + row0 * DK, span * DK * ESZ);
   // piece i of row block R: row 16R + lr, channels [(4i + lg) EPV, (4i + lg + 1) EPV)
   auto piece_off = [&](int R, int i) -> uint32_t {
     return static_cast<uint32_t>(((16 * R + lr) * H * DK + (4 * i + lg) * EPV) * ESZ);
@@ -675,6 +681,16 @@ __global__ __launch_bounds__(256) void chunk_prep_reg_kernel(ChunkParams p, int6
   for (int R = 0; R < 4; ++R)
 #pragma unroll
     for (int i = 0; i < NSTEP; ++i) kf[R][i] = buf_load16(rk, piece_off(R, i), 0);
+  u32x4 kwf[WK ? 4 : 1][NSTEP];
+  if constexpr (WK)
+#pragma unroll
+    for (int R = 0; R < 4; ++R)
+#pragma unroll
+      for (int i = 0; i < NSTEP; ++i) kwf[R][i] = buf_load16(rkw, piece_off(R, i), 0);
+  auto kcol = [&](int R) -> const u32x4* {       // column-side key pieces of row block R
+    if constexpr (WK) return kwf[R];
+    else return kf[R];
+  };
 
   // ---- per-row gate factors (lane = row) ---------------------------------------------
   {
@@ -751,18 +767,21 @@ __global__ __launch_bounds__(256) void chunk_prep_reg_kernel(ChunkParams p, int6
     // A_Rm (m < R) as A operands: transposed Gram blocks
     frag aRow[3];
 #pragma unroll
-    for (int m = 0; m < R; ++m) aRow[m] = O::cvt(a_factor(gram(kf[m], kf[R]), R, m));
-    // diagonal block, both orientations, and its inverse
-    const f32x4 G = gram(kf[R], kf[R]);
+    for (int m = 0; m < R; ++m) aRow[m] = O::cvt(a_factor(gram(kcol(m), kf[R]), R, m));
+    // diagonal block, both orientations, and its inverse (without a write key the
+    // Gram block is symmetric and one product serves both)
+    const f32x4 G = gram(kcol(R), kf[R]);
     const f32x4 Nt = a_factor(G, R, R);         // accumulator tile of A_RR^T
     f32x4 N;                                       // accumulator tile of A_RR: row 16R+4lg+s, column 16R+lr
     {
+      f32x4 G2 = G;
+      if constexpr (WK) G2 = gram(kf[R], kcol(R));
       const f32x4 br = *reinterpret_cast<const f32x4*>(sB + 16 * R + 4 * lg);
       const f32x4 grr = *reinterpret_cast<const f32x4*>(sGr + 16 * R + 4 * lg);
       const float gj = sG[16 * R + lr];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        float v = G[s] * br[s];
+        float v = G2[s] * br[s];
         if constexpr (GATE == GATE_SCALAR) v *= __expf(grr[s] - gj);
         N[s] = (4 * lg + s > lr) ? v : 0.f;
       }
@@ -829,6 +848,11 @@ static hipError_t launch_prep_g(const ChunkParams& p, int64_t nchunks, hipStream
 
 template <int IO>
 static hipError_t launch_prep_io(const ChunkParams& p, int64_t nchunks, hipStream_t stream) {
+  if (p.kw) {
+    if constexpr (IO == IO_BF16) return p.gate == GATE_NONE ? launch_prep_g<IO, GATE_WKEY>(p, nchunks, stream)
+                                                          : hipErrorInvalidValue;
+    else return hipErrorInvalidValue;
+  }
   switch (p.gate) {
     case GATE_NONE: return launch_prep_g<IO, GATE_NONE>(p, nchunks, stream);
     case GATE_SCALAR: return launch_prep_g<IO, GATE_SCALAR>(p, nchunks, stream);

@@ -78,7 +78,8 @@ __global__ __launch_bounds__((NCH + NHW) * 64) void chunk_state_pipe_kernel(Chun
   typedef uint16_t elem;
   constexpr int DVT = 16 * CG * NCH;            // columns per workgroup
   constexpr bool CHAN = GATE == GATE_CHANNEL;
-  typedef PipeLayout<DK, DVT, CHAN> L;
+  constexpr bool WK = GATE == GATE_WKEY;          // write key: K^T and P take kw instead of k
+  typedef PipeLayout<DK, DVT, CHAN || WK> L;
   typedef WsRec<2> W;
   constexpr uint32_t RB = rec_bytes(IO_BF16, GATE, DK);   // bytes per chunk record
   constexpr int ESZ = 2, EPV = 8;
@@ -145,6 +146,7 @@ __global__ __launch_bounds__((NCH + NHW) * 64) void chunk_state_pipe_kernel(Chun
   const uint32_t span = static_cast<uint32_t>(sq.len > 0 ? (sq.len - 1) * p.H + 1 : 0);
   const rsrc_t rk = make_rsrc(static_cast<const elem*>(p.k) + row0 * DK, span * DK * ESZ);
   const rsrc_t rq = make_rsrc(static_cast<const elem*>(p.q) + row0 * DK, span * DK * ESZ);
+  const rsrc_t rkw = make_rsrc(static_cast<const elem*>(WK ? p.kw : p.k) + row0 * DK, span * DK * ESZ);
   const rsrc_t rv = make_rsrc(static_cast<const elem*>(p.v) + row0 * dv, span * dv * ESZ);
   const rsrc_t ro = make_rsrc(static_cast<const elem*>(p.o) + row0 * dv, span * dv * ESZ);
   const rsrc_t rw = make_rsrc(static_cast<const char*>(p.ws) + sq.rec0 * RB, static_cast<uint32_t>(nchunks * RB));
@@ -152,7 +154,7 @@ __global__ __launch_bounds__((NCH + NHW) * 64) void chunk_state_pipe_kernel(Chun
   // ---- helpers: loads one chunk ahead in registers, stores into an LDS copy ----------
   // Per-channel gate: k, q and k e^{g_63 - g} come decayed from the record (row-major
   // [64][d_k] each), and so does P, which is loaded a step after the tiles.
-  u32x4 pk[HK], pq[HK], pkd[CHAN ? HK : 1], pv[HV], pt[HT], pp[CHAN ? HT : 1], pf;
+  u32x4 pk[HK], pq[HK], pkd[(CHAN || WK) ? HK : 1], pv[HV], pt[HT], pp[CHAN ? HT : 1], pf;
   auto prefetch = [&](int64_t m) __attribute__((always_inline)) {
     const uint32_t sk = static_cast<uint32_t>(m * CH * H * DK * ESZ);
     const uint32_t sv = static_cast<uint32_t>(m * CH * H * dv * ESZ);
@@ -170,6 +172,7 @@ __global__ __launch_bounds__((NCH + NHW) * 64) void chunk_state_pipe_kernel(Chun
         const uint32_t off = static_cast<uint32_t>(((seg / KROW) * H * DK + (seg % KROW) * EPV) * ESZ);
         pk[v] = buf_load16(rk, off, sk);
         pq[v] = buf_load16(rq, off, sk);
+        if constexpr (WK) pkd[v] = buf_load16(rkw, off, sk);
       }
     }
 #pragma unroll
@@ -222,7 +225,7 @@ __global__ __launch_bounds__((NCH + NHW) * 64) void chunk_state_pipe_kernel(Chun
       u32x2* q2 = reinterpret_cast<u32x2*>(dQ + row * LDQ + c);
       q2[0] = u32x2{pq[v][0], pq[v][1]};
       q2[1] = u32x2{pq[v][2], pq[v][3]};
-      if constexpr (CHAN) {
+      if constexpr (CHAN || WK) {
         u32x2* d2 = reinterpret_cast<u32x2*>(reinterpret_cast<T*>(base + L::B_KD) + row * LDK + c);
         d2[0] = u32x2{pkd[v][0], pkd[v][1]};
         d2[1] = u32x2{pkd[v][2], pkd[v][3]};
@@ -258,7 +261,7 @@ __global__ __launch_bounds__((NCH + NHW) * 64) void chunk_state_pipe_kernel(Chun
     const float* f = reinterpret_cast<const float*>(cur + L::B_F);
     return Tiles{reinterpret_cast<const T*>(cur + L::B_K), reinterpret_cast<const T*>(cur + L::B_Q),
                  reinterpret_cast<const T*>(cur + L::B_V), reinterpret_cast<const T*>(cur + L::B_T),
-                 reinterpret_cast<const T*>(cur + (CHAN ? L::B_KD : L::B_K)),
+                 reinterpret_cast<const T*>(cur + ((CHAN || WK) ? L::B_KD : L::B_K)),
                  f, f + CH, f + 2 * CH, f + 3 * CH, f + 4 * CH, f + 5 * CH};
   };
 
@@ -547,7 +550,7 @@ __global__ __launch_bounds__((NCH + NHW) * 64) void chunk_state_pipe_kernel(Chun
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kb = 0; kb < DK / 32; ++kb) {
-            const T* kr = c.K + (16 * J + lr) * LDK + 32 * kb + 4 * lg;
+            const T* kr = c.KD + (16 * J + lr) * LDK + 32 * kb + 4 * lg;   // k, or the write key
             acc = O::mma2(acc, O::ld(kr), O::ld(kr + 16), qf[2 * kb], qf[2 * kb + 1]);
           }
           const f32x4 gj = *reinterpret_cast<const f32x4*>(c.g + 16 * J + 4 * lg);
@@ -584,8 +587,8 @@ template <int GATE, int DK>
 static hipError_t launch_pipe_dk(const ChunkParams& p, hipStream_t stream) {
   // 32 columns per workgroup: 2 chain waves and 4 helpers (measured: 15-20% faster
   // than 2 helpers, as fast as 6, on the per-channel and the no-gate workloads).
-  if constexpr (GATE == GATE_CHANNEL) {
-    // per-channel gate: the third operand tile leaves LDS room for 32 columns only
+  if constexpr (GATE == GATE_CHANNEL || GATE == GATE_WKEY) {
+    // per-channel gate, write key: the third operand tile leaves LDS room for 32 columns only
     return launch_pipe_t<GATE, DK, 2, 1, 4>(p, stream);
   } else {
     // 64 columns per workgroup when that still gives one workgroup per CU, else 32.
@@ -607,6 +610,7 @@ static hipError_t launch_pipe_g(const ChunkParams& p, hipStream_t stream) {
 
 hipError_t launch_chunk_state_pipe(const ChunkParams& p, hipStream_t stream) {
   if (p.io != IO_BF16) return hipErrorInvalidValue;
+  if (p.kw) return p.gate == GATE_NONE ? launch_pipe_g<GATE_WKEY>(p, stream) : hipErrorInvalidValue;
   if (p.gate == GATE_NONE) return launch_pipe_g<GATE_NONE>(p, stream);
   if (p.gate == GATE_SCALAR) return launch_pipe_g<GATE_SCALAR>(p, stream);
   if (p.gate == GATE_CHANNEL) return launch_pipe_g<GATE_CHANNEL>(p, stream);

@@ -6,6 +6,10 @@
 //
 //     S~ = diag(a) S,   u = S~^T k,   delta = beta (v - u),
 //     S' = S~ + k delta^T,   o = S'^T q = S~^T q + delta (k . q).
+// With a write key kw ("OSDN: Improving Delta Rule with Provable Online
+// Preconditioning in Linear Attention", §2.1: the right-preconditioned step)
+// the state is written along kw instead: S' = S~ + kw delta^T, o gains
+// delta (kw . q); the residual still reads along k.
 //
 // The step is bound by HBM bandwidth: each state (d_k*d_v*4 bytes) is read once
 // and written once.  One 256-thread workgroup owns one state; each thread keeps
@@ -32,7 +36,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeParams p) {
   const int rg = tid / TPR;
   const int wave = tid / 64;
 
-  __shared__ float s_k[DK], s_q[DK], s_a[DK];
+  __shared__ float s_k[DK], s_q[DK], s_a[DK], s_kw[DK];
   __shared__ float s_u[4][DV], s_w[4][DV];
   __shared__ float s_kq;
 
@@ -52,6 +56,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeParams p) {
   if (tid < DK) {
     s_k[tid] = Io<IO>::load(k, sid * DK + tid);
     s_q[tid] = Io<IO>::load(q, sid * DK + tid);
+    s_kw[tid] = p.kw ? Io<IO>::load(static_cast<const elem*>(p.kw), sid * DK + tid) : s_k[tid];
     if (GATE == GATE_CHANNEL) s_a[tid] = __expf(Io<IO>::load(log_a, sid * DK + tid));
   }
   float a_scalar = 1.f;
@@ -62,9 +67,9 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeParams p) {
   for (int j = 0; j < 4; ++j) vv[j] = Io<IO>::load(v, sid * DV + 4 * cg + j);
   __syncthreads();
 
-  if (wave == 0) {  // k . q, reduced across the first wave
+  if (wave == 0) {  // (write key) . q, reduced across the first wave
     float kq = 0.f;
-    for (int i = tid; i < DK; i += 64) kq += s_k[i] * s_q[i];
+    for (int i = tid; i < DK; i += 64) kq += s_kw[i] * s_q[i];
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) kq += __shfl_xor(kq, off);
     if (tid == 0) s_kq = kq;
@@ -120,7 +125,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeParams p) {
 #pragma unroll
   for (int m = 0; m < RPT; ++m) {
     const int i = rg + RG * m;
-    const float ki = s_k[i];
+    const float ki = s_kw[i];
     f32x4 s = {st[m].x + ki * d[0], st[m].y + ki * d[1], st[m].z + ki * d[2], st[m].w + ki * d[3]};
     __builtin_nontemporal_store(s, reinterpret_cast<f32x4*>(Sn + i * DV + 4 * cg));
   }

@@ -8,6 +8,9 @@ namespace gdr {
 
 enum IoType { IO_F32 = 0, IO_BF16 = 1 };
 enum GateKind { GATE_NONE = 0, GATE_SCALAR = 1, GATE_CHANNEL = 2 };
+// Kernel variant (never a value of the C ABI's gate): no gate, and a separate write
+// key k~ for the state write (the right-preconditioned delta rule).
+constexpr int GATE_WKEY = 3;
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;

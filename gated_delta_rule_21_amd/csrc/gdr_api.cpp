@@ -138,7 +138,7 @@ namespace {
 // The forward over fixed-length batches (cu == nullptr) or packed sequences.
 gdr_status chunk_fwd_impl(const gdr_desc* d, const int32_t* cu, int64_t n_seq, const void* q, const void* k,
                           const void* v, const void* beta, const void* log_a, const float* S0, void* o, float* S_T,
-                          void* workspace, size_t workspace_bytes, void* stream) {
+                          void* workspace, size_t workspace_bytes, void* stream, const void* kw = nullptr) {
   gdr_status st = check_desc(d, false);
   if (st != GDR_OK) return st;
   const bool packed = cu != nullptr || n_seq != 0;
@@ -173,7 +173,8 @@ gdr_status chunk_fwd_impl(const gdr_desc* d, const int32_t* cu, int64_t n_seq, c
   if ((st = check_align("q", q, 16)) || (st = check_align("k", k, 16)) || (st = check_align("v", v, 16)) ||
       (st = check_align("o", o, 16)) || (st = check_align("S0", S0, 16)) || (st = check_align("S_T", S_T, 16)) ||
       (st = check_align("beta", beta, esz)) || (st = check_align("log_a", log_a, esz)) ||
-      (st = check_align("workspace", workspace, 16)) || (st = check_align("cu_seqlens", cu, 4)))
+      (st = check_align("workspace", workspace, 16)) || (st = check_align("cu_seqlens", cu, 4)) ||
+      (st = check_align("kw", kw, 16)))
     return st;
   const int64_t gate_w = d->gate == GDR_GATE_NONE ? 0 : d->gate == GDR_GATE_SCALAR ? 1 : d->d_k;
   const int64_t state_bytes = nseq * d->H * d->d_k * d->d_v * 4;
@@ -182,10 +183,11 @@ gdr_status chunk_fwd_impl(const gdr_desc* d, const int32_t* cu, int64_t n_seq, c
                 span("log_a", log_a, ntok * gate_w * esz), span("S0", S0, state_bytes),
                 span("o", o, ntok * d->d_v * esz), span("S_T", S_T, state_bytes),
                 span("workspace", d->T > 0 ? workspace : nullptr, static_cast<int64_t>(ws_need)),
-                span("cu_seqlens", cu, packed ? (n_seq + 1) * 4 : 0)};
+                span("cu_seqlens", cu, packed ? (n_seq + 1) * 4 : 0),
+                span("kw", kw, kw ? ntok * d->d_k * esz : 0)};
   Span outs[] = {all[6], all[7], all[8]};
   if (S_T && S0 == S_T) all[5].hi = all[5].lo;   // exact in-place update of the state is allowed
-  if ((st = check_no_overlap(outs, 3, all, 10))) return st;
+  if ((st = check_no_overlap(outs, 3, all, 11))) return st;
 
   gdr::ChunkParams p;
   p.q = q; p.k = k; p.v = v; p.beta = beta; p.log_a = log_a; p.S0 = S0; p.o = o; p.S_T = S_T;
@@ -196,6 +198,7 @@ gdr_status chunk_fwd_impl(const gdr_desc* d, const int32_t* cu, int64_t n_seq, c
   p.cu = cu;
   p.nslots = packed ? gdr::chunk_varlen_slots(d->T, n_seq) : 0;
   p.order = nullptr;
+  p.kw = kw;
   if (d->T == 0 && !S_T) return GDR_OK;
   hipError_t e = gdr::launch_chunk_fwd(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(GDR_ERR_HIP, "chunk forward launch failed: %s", hipGetErrorString(e));
@@ -247,44 +250,90 @@ gdr_status gdr_chunk_fwd_varlen(const gdr_desc* d, const int32_t* cu_seqlens, in
   }
 }
 
+}  // extern "C"
+
+namespace {
+
+gdr_status recurrent_step_impl(const gdr_desc* d, const void* q, const void* k, const void* kw, const void* v,
+                               const void* beta, const void* log_a, const float* S, float* S_new, void* o,
+                               void* stream) {
+  gdr_status st = check_desc(d, true);
+  if (st != GDR_OK) return st;
+  const int64_t esz = d->io == GDR_BF16 ? 2 : 4;
+  const int64_t n = d->B * d->H;
+  if (!q) return fail(GDR_ERR_INVALID_ARG, "q is NULL");
+  if (!k) return fail(GDR_ERR_INVALID_ARG, "k is NULL");
+  if (!v) return fail(GDR_ERR_INVALID_ARG, "v is NULL");
+  if (!beta) return fail(GDR_ERR_INVALID_ARG, "beta is NULL");
+  if (!S) return fail(GDR_ERR_INVALID_ARG, "S is NULL");
+  if (!S_new) return fail(GDR_ERR_INVALID_ARG, "S_new is NULL");
+  if (!o) return fail(GDR_ERR_INVALID_ARG, "o is NULL");
+  if (d->gate != GDR_GATE_NONE && !log_a) return fail(GDR_ERR_INVALID_ARG, "log_a is NULL but a gate is requested");
+  if (d->gate == GDR_GATE_NONE && log_a) return fail(GDR_ERR_INVALID_ARG, "log_a must be NULL for GDR_GATE_NONE");
+  if ((st = check_align("q", q, 16)) || (st = check_align("k", k, 16)) || (st = check_align("v", v, 16)) ||
+      (st = check_align("o", o, 16)) || (st = check_align("S", S, 16)) || (st = check_align("S_new", S_new, 16)) ||
+      (st = check_align("beta", beta, esz)) || (st = check_align("log_a", log_a, esz)) ||
+      (st = check_align("kw", kw, 16)))
+    return st;
+  const int64_t gate_w = d->gate == GDR_GATE_NONE ? 0 : d->gate == GDR_GATE_SCALAR ? 1 : d->d_k;
+  const int64_t state_bytes = n * d->d_k * d->d_v * 4;
+  Span all[] = {span("q", q, n * d->d_k * esz), span("k", k, n * d->d_k * esz), span("v", v, n * d->d_v * esz),
+                span("beta", beta, n * esz), span("log_a", log_a, n * gate_w * esz), span("S", S, state_bytes),
+                span("o", o, n * d->d_v * esz), span("S_new", S_new, state_bytes),
+                span("kw", kw, kw ? n * d->d_k * esz : 0)};
+  Span outs[] = {all[6], all[7]};
+  if (S == S_new) all[5].hi = all[5].lo;   // exact in-place update is allowed
+  if ((st = check_no_overlap(outs, 2, all, 9))) return st;
+
+  gdr::DecodeParams p;
+  p.q = q; p.k = k; p.v = v; p.beta = beta; p.log_a = log_a; p.S = S; p.S_new = S_new; p.o = o;
+  p.n_states = n;
+  p.d_k = static_cast<int>(d->d_k); p.d_v = static_cast<int>(d->d_v);
+  p.io = d->io; p.gate = d->gate; p.literal = d->form == GDR_FORM_LITERAL;
+  p.kw = kw;
+  hipError_t e = gdr::launch_decode_step(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(GDR_ERR_HIP, "decode step launch failed: %s", hipGetErrorString(e));
+  return GDR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 gdr_status gdr_recurrent_step(const gdr_desc* d, const void* q, const void* k, const void* v, const void* beta,
                               const void* log_a, const float* S, float* S_new, void* o, void* stream) {
   try {
     g_last_error.clear();
-    gdr_status st = check_desc(d, true);
-    if (st != GDR_OK) return st;
-    const int64_t esz = d->io == GDR_BF16 ? 2 : 4;
-    const int64_t n = d->B * d->H;
-    if (!q) return fail(GDR_ERR_INVALID_ARG, "q is NULL");
-    if (!k) return fail(GDR_ERR_INVALID_ARG, "k is NULL");
-    if (!v) return fail(GDR_ERR_INVALID_ARG, "v is NULL");
-    if (!beta) return fail(GDR_ERR_INVALID_ARG, "beta is NULL");
-    if (!S) return fail(GDR_ERR_INVALID_ARG, "S is NULL");
-    if (!S_new) return fail(GDR_ERR_INVALID_ARG, "S_new is NULL");
-    if (!o) return fail(GDR_ERR_INVALID_ARG, "o is NULL");
-    if (d->gate != GDR_GATE_NONE && !log_a) return fail(GDR_ERR_INVALID_ARG, "log_a is NULL but a gate is requested");
-    if (d->gate == GDR_GATE_NONE && log_a) return fail(GDR_ERR_INVALID_ARG, "log_a must be NULL for GDR_GATE_NONE");
-    if ((st = check_align("q", q, 16)) || (st = check_align("k", k, 16)) || (st = check_align("v", v, 16)) ||
-        (st = check_align("o", o, 16)) || (st = check_align("S", S, 16)) || (st = check_align("S_new", S_new, 16)) ||
-        (st = check_align("beta", beta, esz)) || (st = check_align("log_a", log_a, esz)))
-      return st;
-    const int64_t gate_w = d->gate == GDR_GATE_NONE ? 0 : d->gate == GDR_GATE_SCALAR ? 1 : d->d_k;
-    const int64_t state_bytes = n * d->d_k * d->d_v * 4;
-    Span all[] = {span("q", q, n * d->d_k * esz), span("k", k, n * d->d_k * esz), span("v", v, n * d->d_v * esz),
-                  span("beta", beta, n * esz), span("log_a", log_a, n * gate_w * esz), span("S", S, state_bytes),
-                  span("o", o, n * d->d_v * esz), span("S_new", S_new, state_bytes)};
-    Span outs[] = {all[6], all[7]};
-    if (S == S_new) all[5].hi = all[5].lo;   // exact in-place update is allowed
-    if ((st = check_no_overlap(outs, 2, all, 8))) return st;
+    return recurrent_step_impl(d, q, k, nullptr, v, beta, log_a, S, S_new, o, stream);
+  } catch (...) {
+    return fail(GDR_ERR_INVALID_ARG, "internal error");
+  }
+}
 
-    gdr::DecodeParams p;
-    p.q = q; p.k = k; p.v = v; p.beta = beta; p.log_a = log_a; p.S = S; p.S_new = S_new; p.o = o;
-    p.n_states = n;
-    p.d_k = static_cast<int>(d->d_k); p.d_v = static_cast<int>(d->d_v);
-    p.io = d->io; p.gate = d->gate; p.literal = d->form == GDR_FORM_LITERAL;
-    hipError_t e = gdr::launch_decode_step(p, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return fail(GDR_ERR_HIP, "decode step launch failed: %s", hipGetErrorString(e));
-    return GDR_OK;
+gdr_status gdr_recurrent_step_wkey(const gdr_desc* d, const void* q, const void* k, const void* kw, const void* v,
+                                   const void* beta, const float* S, float* S_new, void* o, void* stream) {
+  try {
+    g_last_error.clear();
+    if (!kw) return fail(GDR_ERR_INVALID_ARG, "kw is NULL");
+    if (d && d->gate != GDR_GATE_NONE)
+      return fail(GDR_ERR_UNSUPPORTED, "write key: no gate only (the preconditioned delta rule)");
+    return recurrent_step_impl(d, q, k, kw, v, beta, nullptr, S, S_new, o, stream);
+  } catch (...) {
+    return fail(GDR_ERR_INVALID_ARG, "internal error");
+  }
+}
+
+gdr_status gdr_chunk_fwd_wkey(const gdr_desc* d, const void* q, const void* k, const void* kw, const void* v,
+                              const void* beta, const float* S0, void* o, float* S_T, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  try {
+    g_last_error.clear();
+    if (!kw) return fail(GDR_ERR_INVALID_ARG, "kw is NULL");
+    if (d && d->gate != GDR_GATE_NONE)
+      return fail(GDR_ERR_UNSUPPORTED, "write key: no gate only (the preconditioned delta rule)");
+    if (d && d->io != GDR_BF16) return fail(GDR_ERR_UNSUPPORTED, "write key chunk forward: bf16 I/O only");
+    return chunk_fwd_impl(d, nullptr, 0, q, k, v, beta, nullptr, S0, o, S_T, workspace, workspace_bytes, stream,
+                          kw);
   } catch (...) {
     return fail(GDR_ERR_INVALID_ARG, "internal error");
   }

@@ -18,6 +18,7 @@ struct DecodeParams {
   int64_t n_states;   // B * H
   int d_k, d_v;
   int io, gate, literal;
+  const void* kw;     // write key [B, H, d_k] (the state is written along it), or null: along k
 };
 
 struct ChunkParams {
@@ -39,6 +40,7 @@ struct ChunkParams {
   const int32_t* cu;
   int64_t nslots;
   const int32_t* order;   // packed sequences: longest first (in the workspace, after the records)
+  const void* kw;         // write key [B, T, H, d_k] (no gate, bf16), or null: the state is written along k
 };
 
 hipError_t launch_decode_step(const DecodeParams& p, hipStream_t stream);

@@ -210,6 +210,33 @@ const char* gdr_last_error(void);
 /* Library version as major*10000 + minor*100 + patch. */
 int gdr_version(void);
 
+/*
+ * gdr_chunk_fwd_wkey / gdr_recurrent_step_wkey -- the delta rule with a separate
+ * write key ("OSDN: Improving Delta Rule with Provable Online Preconditioning in
+ * Linear Attention", §2.1: right-preconditioning the delta-rule step by
+ * diag(d_t) is the same as writing along the scaled key kw_t = d_t * k_t while
+ * the residual still reads along k_t; the chunkwise pipeline is unchanged with
+ * kw in place of k on the write side).  Key-major, per token:
+ *
+ *     S_t = (I - beta_t kw_t k_t^T) S_{t-1} + beta_t kw_t v_t^T,    o_t = S_t^T q_t.
+ *
+ * kw = k is gdr_chunk_fwd / gdr_recurrent_step with GDR_GATE_NONE.  The caller
+ * forms kw (the pages' preconditioner scan is not part of this call).
+ *
+ *   kw  same shape, dtype and alignment rules as k ([B, T, H, d_k] for the
+ *       forward, [B, H, d_k] for the step); may alias k or q (it is only read).
+ * Every other argument, the workspace (same size as gdr_chunk_fwd_workspace_size
+ * with GDR_GATE_NONE) and the errors are as for gdr_chunk_fwd / gdr_recurrent_step.
+ * desc->gate must be GDR_GATE_NONE (GDR_ERR_UNSUPPORTED otherwise); the forward
+ * takes bf16 I/O only, the step both dtypes.
+ */
+gdr_status gdr_chunk_fwd_wkey(const gdr_desc* desc, const void* q, const void* k, const void* kw,
+                              const void* v, const void* beta, const float* S0, void* o, float* S_T,
+                              void* workspace, size_t workspace_bytes, void* stream /* hipStream_t */);
+gdr_status gdr_recurrent_step_wkey(const gdr_desc* desc, const void* q, const void* k, const void* kw,
+                                   const void* v, const void* beta, const float* S, float* S_new,
+                                   void* o, void* stream /* hipStream_t */);
+
 #ifdef __cplusplus
 }
 #endif

@@ -211,3 +211,38 @@ def test_varlen_argument_checks(lib):
     assert b"overlaps" in lib.gdr_last_error()
     need = _ws_varlen(lib, _desc(), 2)[1]
     assert _chunk_varlen(lib, _desc(), cu, 2, _ptrs(), ws_bytes=need - 1) == INVALID
+
+
+# ---- write key (the preconditioned delta rule) -------------------------------------------
+def _chunk_wkey(lib, d, kw, ptrs, ws_bytes=None):
+    q, k, v, beta, log_a, S0, o, S_T = ptrs[:8]
+    ws = ptrs[8] if len(ptrs) > 8 else None
+    if ws_bytes is None:
+        ws_bytes = _ws_size(lib, d)[1] if d is not None else 0
+    return lib.gdr_chunk_fwd_wkey(None if d is None else ctypes.byref(d), q, k, kw, v, beta, S0, o, S_T, ws,
+                                  ws_bytes, None)
+
+
+def test_write_key_chunk_checks(lib):
+    kw = FAKE + 0x7F000000                     # never dereferenced
+    assert _chunk_wkey(lib, _desc(gate=1), kw, _ptrs()) == UNSUPPORTED      # no gate only
+    assert _chunk_wkey(lib, _desc(gate=0), None, _ptrs()) == INVALID
+    assert b"kw" in lib.gdr_last_error()
+    assert _chunk_wkey(lib, _desc(gate=0, io=0, d_k=64), kw, _ptrs()) == UNSUPPORTED   # bf16 only
+    assert _chunk_wkey(lib, _desc(gate=0), kw + 8, _ptrs()) == ALIGN
+    p = _ptrs()
+    assert _chunk_wkey(lib, _desc(gate=0), p[6] + 64, p) == INVALID          # kw inside o
+    assert b"overlaps" in lib.gdr_last_error()
+
+
+def test_write_key_step_checks(lib):
+    kw = FAKE + 0x7F000000
+    p = _ptrs()
+    d = _desc(T=1, gate=0)
+    call = lambda d, kw: lib.gdr_recurrent_step_wkey(ctypes.byref(d), p[0], p[1], kw, p[2], p[3], p[5], p[7], p[6],
+                                                     None)
+    assert call(_desc(T=1, gate=1), kw) == UNSUPPORTED
+    assert call(d, None) == INVALID
+    assert call(d, kw + 4) == ALIGN
+    assert call(d, p[7] + 64) == INVALID                                   # kw inside S_new
+    assert b"overlaps" in lib.gdr_last_error()

@@ -1,0 +1,96 @@
+"""GPU parity of the write-key entry points (gdr_chunk_fwd_wkey,
+gdr_recurrent_step_wkey) against the fp64 oracle with the same write keys.
+
+The write key is kw = d * k ("OSDN: Improving Delta Rule with Provable Online
+Preconditioning in Linear Attention", §2.1) with a seeded preconditioner d drawn
+uniformly from (0.2, 2) per (token, head, channel), rounded to the I/O dtype like
+every other input.  Tolerances as for the plain forward and step (relative L2:
+2e-2 for bf16 I/O with an fp32 state, 1e-4 for fp32 I/O).
+"""
+
+import numpy as np
+import pytest
+
+from oracle import forward as oracle_forward, recurrent_step as oracle_step, rel_l2
+from tests.gpu_util import TOL, check, dev, host, need_gpu, say
+from workloads import Workload, chunk_inputs
+from workloads.inputs import round_to_io
+
+pytestmark = pytest.mark.gpu
+
+
+def _wkey_inputs(B, T, H, dk, dv, seed, io="bf16", s0=0.02):
+    inp = chunk_inputs(Workload("wkey", B=B, T=T, H=H, d_k=dk, d_v=dv, io=io, gate="none", s0_std=s0, seed=seed))
+    d = np.random.default_rng([seed, 7]).uniform(0.2, 2.0, inp["k"].shape)
+    inp["kw"] = round_to_io(d * inp["k"], io)
+    return inp
+
+
+@pytest.mark.parametrize("shape", [(2, 200, 3, 128, 128), (1, 130, 2, 64, 128), (1, 65, 2, 128, 64),
+                                   (2, 1, 2, 128, 128), (1, 300, 64, 128, 128)],
+                         ids=lambda s: "B%dT%dH%d_dk%d_dv%d" % s)
+def test_write_key_chunk_fwd(shape):
+    need_gpu()
+    import torch
+    import gated_delta_rule_21_amd as gdr
+    B, T, H, dk, dv = shape
+    say(f"case write key {shape}")
+    inp = _wkey_inputs(B, T, H, dk, dv, seed=101 + T)
+    o, S = gdr.chunk_fwd(*(dev(inp[n], "bf16") for n in ("q", "k", "v", "beta")), None,
+                         torch.from_numpy(inp["S0"]).cuda(), kw=dev(inp["kw"], "bf16"))
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_forward(inp["q"], inp["k"], inp["v"], inp["beta"], None, inp["S0"], kw=inp["kw"])
+    check("o", host(o), o_ref, TOL["bf16"])
+    check("S_T", host(S), S_ref, TOL["bf16"])
+
+
+def test_write_key_equal_to_key_is_deltanet():
+    """kw = k gives the no-gate forward (OSDN §2.1 with d = 1)."""
+    need_gpu()
+    import torch
+    import gated_delta_rule_21_amd as gdr
+    inp = _wkey_inputs(2, 150, 2, 128, 128, seed=113)
+    args = [dev(inp[n], "bf16") for n in ("q", "k", "v", "beta")]
+    S0 = torch.from_numpy(inp["S0"]).cuda()
+    o1, S1 = gdr.chunk_fwd(*args, None, S0, kw=args[1])
+    o2, S2 = gdr.chunk_fwd(*args, None, S0)
+    torch.cuda.synchronize()
+    assert rel_l2(host(o1), host(o2)) <= 1e-6 and rel_l2(host(S1), host(S2)) <= 1e-6
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_write_key_decode_step(io):
+    need_gpu()
+    import torch
+    import gated_delta_rule_21_amd as gdr
+    inp = _wkey_inputs(16, 1, 4, 128, 128, seed=127, io=io, s0=0.05)
+    st = {n: np.ascontiguousarray(inp[n][:, 0]) for n in ("q", "k", "v", "beta", "kw")}
+    S = torch.from_numpy(inp["S0"]).cuda()
+    o, S_new = gdr.recurrent_step(*(dev(st[n], io) for n in ("q", "k", "v", "beta")), None, S,
+                                  S_new=torch.empty_like(S), kw=dev(st["kw"], io))
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_step(inp["S0"], st["q"], st["k"], st["v"], st["beta"], None, kw=st["kw"])
+    check("o", host(o), o_ref, TOL[io])
+    check("S_new", host(S_new), S_ref, TOL[io])
+
+
+def test_write_key_prefill_then_decode():
+    """The forward's final state continues with write-key decode steps: the same
+    as the oracle over the longer sequence."""
+    need_gpu()
+    import torch
+    import gated_delta_rule_21_amd as gdr
+    inp = _wkey_inputs(2, 133, 2, 128, 128, seed=131)
+    T0 = 130
+    part = lambda n, sl: np.ascontiguousarray(inp[n][:, sl])
+    o, S = gdr.chunk_fwd(*(dev(part(n, slice(0, T0)), "bf16") for n in ("q", "k", "v", "beta")), None,
+                         torch.from_numpy(inp["S0"]).cuda(), kw=dev(part("kw", slice(0, T0)), "bf16"))
+    outs = []
+    for t in range(T0, 133):
+        ot, S = gdr.recurrent_step(*(dev(part(n, t), "bf16") for n in ("q", "k", "v", "beta")), None, S,
+                                   kw=dev(part("kw", t), "bf16"))
+        outs.append(host(ot))
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_forward(inp["q"], inp["k"], inp["v"], inp["beta"], None, inp["S0"], kw=inp["kw"])
+    check("decode o", np.stack(outs, axis=1), o_ref[:, T0:], TOL["bf16"])
+    check("S", host(S), S_ref, TOL["bf16"])
