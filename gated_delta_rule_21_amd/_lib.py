@@ -24,7 +24,7 @@ FORMS = {"page": 0, "literal": 1}
 
 EXPORTED = ("gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_chunk_fwd_varlen_workspace_size",
             "gdr_chunk_fwd_varlen", "gdr_recurrent_step", "gdr_chunk_fwd_wkey", "gdr_recurrent_step_wkey",
-            "gdr_status_string", "gdr_last_error", "gdr_version")
+            "gdr_precond_scan", "gdr_status_string", "gdr_last_error", "gdr_version")
 
 
 class GdrDesc(ctypes.Structure):
@@ -71,6 +71,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         lib.gdr_recurrent_step_wkey.argtypes = [ctypes.POINTER(GdrDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.gdr_recurrent_step.restype = ctypes.c_int
         lib.gdr_recurrent_step.argtypes = [ctypes.POINTER(GdrDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.gdr_precond_scan.restype = ctypes.c_int
+        lib.gdr_precond_scan.argtypes = [ctypes.POINTER(GdrDesc), vp, vp, vp, ctypes.c_float, vp, vp, vp, vp]
         lib.gdr_status_string.restype = ctypes.c_char_p
         lib.gdr_status_string.argtypes = [ctypes.c_int]
         lib.gdr_last_error.restype = ctypes.c_char_p
@@ -279,3 +281,34 @@ def recurrent_step(q, k, v, beta, log_a, S, *, S_new=None, o=None, form: str = "
                                 _ptr(S_new), _ptr(o), _stream_handle(stream))
     _check(lib, st)
     return o, S_new
+
+
+def precond_scan(k, beta, eta: float, r=None, d0=None, *, kw=None, d_T=None, want_state: bool = True,
+                 stream=None):
+    """gdr_precond_scan on torch tensors: the preconditioner scan that produces
+    the write keys kw_t = d_t * k_t.  k [B, T, H, d_k]; beta [B, T, H]; r None
+    (no forgetting) or [B, T, H] retention (same I/O dtype); eta step size;
+    d0 None (ones) or [B, H, d_k] float32.  Returns (kw [B, T, H, d_k] in the
+    I/O dtype, d_T [B, H, d_k] float32, None when want_state is False).
+    d_T may be d0 (updated in place)."""
+    lib = load()
+    B, T, H, dk = k.shape
+    dt = k.dtype
+    _require(k, "k", dt, (B, T, H, dk))
+    _require(beta, "beta", dt, (B, T, H))
+    if r is not None:
+        _require(r, "r", dt, (B, T, H))
+    if d0 is not None:
+        _require(d0, "d0", torch.float32, (B, H, dk))
+    if kw is None:
+        kw = torch.empty((B, T, H, dk), dtype=dt, device=k.device)
+    _require(kw, "kw", dt, (B, T, H, dk))
+    if want_state and d_T is None:
+        d_T = torch.empty((B, H, dk), dtype=torch.float32, device=k.device)
+    if d_T is not None:
+        _require(d_T, "d_T", torch.float32, (B, H, dk))
+    desc = GdrDesc(B, T, H, dk, dk, 64, _io_of(k), 0, 0)
+    st = lib.gdr_precond_scan(ctypes.byref(desc), _ptr(k), _ptr(beta), _ptr(r), float(eta), _ptr(d0), _ptr(kw),
+                              _ptr(d_T), _stream_handle(stream))
+    _check(lib, st)
+    return kw, d_T

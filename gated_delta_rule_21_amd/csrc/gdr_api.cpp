@@ -323,6 +323,55 @@ gdr_status gdr_recurrent_step_wkey(const gdr_desc* d, const void* q, const void*
   }
 }
 
+gdr_status gdr_precond_scan(const gdr_desc* d, const void* k, const void* beta, const void* r, float eta,
+                            const float* d0, void* kw, float* d_T, void* stream) {
+  try {
+    g_last_error.clear();
+    if (!d) return fail(GDR_ERR_INVALID_ARG, "desc is NULL");
+    if (d->io != GDR_F32 && d->io != GDR_BF16) return fail(GDR_ERR_INVALID_ARG, "io dtype %d is not GDR_F32/GDR_BF16", d->io);
+    if (d->B < 1) return fail(GDR_ERR_INVALID_ARG, "B = %lld must be >= 1", (long long)d->B);
+    if (d->H < 1) return fail(GDR_ERR_INVALID_ARG, "H = %lld must be >= 1", (long long)d->H);
+    if (d->T < 0) return fail(GDR_ERR_INVALID_ARG, "T = %lld must be >= 0", (long long)d->T);
+    if (d->d_k != 64 && d->d_k != 128) return fail(GDR_ERR_UNSUPPORTED, "d_k = %lld: supported 64, 128", (long long)d->d_k);
+    if (!(eta == eta) || eta > 3.0e38f || eta < -3.0e38f) return fail(GDR_ERR_INVALID_ARG, "eta is not finite");
+    const int64_t esz = d->io == GDR_BF16 ? 2 : 4;
+    int64_t bh = 0, bth = 0, elems = 0, bytes = 0;
+    if (!mul_ok(d->B, d->H, &bh) || !mul_ok(bh, d->T, &bth) || !mul_ok(bth, d->d_k, &elems) ||
+        !mul_ok(elems, esz, &bytes))
+      return fail(GDR_ERR_INVALID_ARG, "sizes overflow");
+    if (bh > INT32_MAX) return fail(GDR_ERR_UNSUPPORTED, "B*H = %lld exceeds the grid limit", (long long)bh);
+    if ((d->T + 64) * d->H * d->d_k * esz > INT32_MAX)   // 32-bit offsets within one sequence, one chunk past its end
+      return fail(GDR_ERR_UNSUPPORTED, "(T + 64)*H*d_k*elem_size = %lld bytes exceeds 2^31 - 1 per sequence",
+                  (long long)((d->T + 64) * d->H * d->d_k * esz));
+    if (d->T > 0) {
+      if (!k) return fail(GDR_ERR_INVALID_ARG, "k is NULL");
+      if (!beta) return fail(GDR_ERR_INVALID_ARG, "beta is NULL");
+      if (!kw) return fail(GDR_ERR_INVALID_ARG, "kw is NULL");
+    }
+    gdr_status st;
+    if ((st = check_align("k", k, 16)) || (st = check_align("kw", kw, 16)) || (st = check_align("beta", beta, esz)) ||
+        (st = check_align("r", r, esz)) || (st = check_align("d0", d0, 4)) || (st = check_align("d_T", d_T, 4)))
+      return st;
+    const int64_t dbytes = bh * d->d_k * 4;
+    Span all[] = {span("k", d->T > 0 ? k : nullptr, bytes), span("beta", d->T > 0 ? beta : nullptr, bth * esz),
+                  span("r", d->T > 0 ? r : nullptr, bth * esz), span("d0", d0, dbytes),
+                  span("kw", d->T > 0 ? kw : nullptr, bytes), span("d_T", d_T, dbytes)};
+    Span outs[] = {all[4], all[5]};
+    if (d0 && d0 == d_T) all[3].hi = all[3].lo;   // exact in-place update is allowed
+    if ((st = check_no_overlap(outs, 2, all, 6))) return st;
+
+    gdr::PrecondParams p;
+    p.k = k; p.beta = beta; p.r = r; p.d0 = d0; p.kw = kw; p.d_T = d_T;
+    p.B = d->B; p.T = d->T; p.H = d->H;
+    p.d_k = static_cast<int>(d->d_k); p.io = d->io; p.eta = eta;
+    hipError_t e = gdr::launch_precond_scan(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(GDR_ERR_HIP, "preconditioner scan launch failed: %s", hipGetErrorString(e));
+    return GDR_OK;
+  } catch (...) {
+    return fail(GDR_ERR_INVALID_ARG, "internal error");
+  }
+}
+
 gdr_status gdr_chunk_fwd_wkey(const gdr_desc* d, const void* q, const void* k, const void* kw, const void* v,
                               const void* beta, const float* S0, void* o, float* S_T, void* workspace,
                               size_t workspace_bytes, void* stream) {

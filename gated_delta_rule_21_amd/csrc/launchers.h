@@ -43,7 +43,20 @@ struct ChunkParams {
   const void* kw;         // write key [B, T, H, d_k] (no gate, bf16), or null: the state is written along k
 };
 
+struct PrecondParams {
+  const void* k;        // [B, T, H, d_k] io dtype
+  const void* beta;     // [B, T, H] io dtype
+  const void* r;        // [B, T, H] io dtype retention, or null (none)
+  const float* d0;      // [B, H, d_k] starting preconditioner, or null (ones)
+  void* kw;             // [B, T, H, d_k] io dtype write keys
+  float* d_T;           // [B, H, d_k] final preconditioner, or null
+  int64_t B, T, H;
+  int d_k, io;
+  float eta;
+};
 hipError_t launch_decode_step(const DecodeParams& p, hipStream_t stream);
+// Preconditioner scan: one workgroup per (sequence, head).
+hipError_t launch_precond_scan(const PrecondParams& p, hipStream_t stream);
 // Per-chunk transform (T tiles into p.ws), then the state pass; one stream, in order.
 hipError_t launch_chunk_prep(const ChunkParams& p, hipStream_t stream);
 hipError_t launch_chunk_state_pipe(const ChunkParams& p, hipStream_t stream);   // bf16 I/O

@@ -1,0 +1,468 @@
+// Preconditioner scan of the preconditioned delta rule on gfx950.
+//
+// "OSDN: Improving Delta Rule with Provable Online Preconditioning in Linear
+// Attention", §2.2: a first phase runs over the keys alone; each token's write
+// key is the current diagonal preconditioner times the key, after which the
+// preconditioner takes one online-gradient step on the closed-form surrogate
+// h_t(d) = ((1 - beta_t <d, k_t^2>)^2 - 1) / (2 ||k_t||^2).  §2.3 (APF) scales
+// the preconditioner by a per-token retention r_t.  Per (sequence, head):
+//
+//     kw_t    = d_t * k_t
+//     d_{t+1} = r_t d_t + e_t w_t,     w_t = k_t^2,
+//     e_t     = gam_t - alf_t <d_t, w_t>,   gam_t = eta beta_t / n_t,
+//                                           alf_t = eta beta_t^2 / n_t,  n_t = ||k_t||^2
+//
+// (a descent step; a zero key adds nothing).  This is a delta rule whose state
+// is the vector d: erase coefficient alf_t, key w_t, retention r_t.
+//
+// bf16 I/O: the chunkwise form of that recurrence (the same derivation as the
+// chunkwise delta rule, with a state of width one).  With g_t the sum of
+// log r_j over the chunk's tokens j < t, a chunk of 64 tokens starting from d_0:
+//
+//     x_t = <d_t, w_t> = e^{g_t} <w_t, d_0> + sum_{s<t} e^{g_t - g_{s+1}} e_s <w_t, w_s>
+//     e   = (I + M)^{-1} b,   M_ts = alf_t e^{g_t - g_{s+1}} <w_t, w_s> (s < t),
+//                             b_t  = gam_t - alf_t e^{g_t} <w_t, d_0>
+//     d_t = e^{g_t} d_0 + sum_{s<t} e^{g_t - g_{s+1}} e_s w_s        (kw_t = d_t * k_t)
+//     d_64 = e^{g_64} d_0 + sum_s e^{g_64 - g_{s+1}} e_s w_s.
+//
+// One 256-thread workgroup owns one (sequence, head) and walks its chunks in
+// order.  The Gram matrix of the w_t and the product that forms every d_t run on
+// MFMA with bf16 operands and fp32 accumulation; the unit lower triangular solve
+// is a forward substitution by one wave (lane t holds row t of M, each step
+// broadcasts e_s); the preconditioner itself, <w_t, d_0> and the chunk-end
+// update stay in fp32 (w_t = k_t^2 is exact in fp32 for a bf16 key).
+//
+// fp32 I/O: a token-by-token scan, one wave per (sequence, head).
+#include "chunk_common.h"
+
+namespace gdr {
+
+namespace {
+
+template <int CTRL, int ROW_MASK = 0xF, bool BOUND_ZERO = false>
+__device__ __forceinline__ float dpp(float old, float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL, ROW_MASK, 0xF,
+                                                    BOUND_ZERO));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave (rows of 16 by shifts, then
+// the row totals carried across rows).
+__device__ __forceinline__ float wave_prefix_sum(float v) {
+  v += dpp<0x111, 0xF, true>(0.f, v);   // row_shr:1
+  v += dpp<0x112, 0xF, true>(0.f, v);   // row_shr:2
+  v += dpp<0x114, 0xF, true>(0.f, v);   // row_shr:4
+  v += dpp<0x118, 0xF, true>(0.f, v);   // row_shr:8
+  v += dpp<0x142, 0xA>(0.f, v);         // row_bcast:15 into rows 1 and 3
+  v += dpp<0x143, 0xC>(0.f, v);         // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
+// Sum over the wave, the same value returned to every lane.
+__device__ __forceinline__ float wave_sum(float v) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_prefix_sum(v)), 63));
+}
+
+// Sum over aligned groups of four lanes, returned to all four.
+__device__ __forceinline__ float quad_sum(float v) {
+  v += dpp<0xB1>(0.f, v);   // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(0.f, v);   // quad_perm [2,3,0,1]
+  return v;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// fp32 I/O: token by token.  Lane l holds channels l*CPL .. l*CPL + CPL - 1.
+// ---------------------------------------------------------------------------
+template <int DK, bool HAS_R>
+__global__ __launch_bounds__(64) void precond_scan_seq_kernel(PrecondParams p) {
+  constexpr int CPL = DK / 64;
+  constexpr int U = 16;   // tokens per block; the next block is loaded while this one runs
+  const int64_t bh = blockIdx.x;
+  const int64_t b = bh / p.H, h = bh - b * p.H;
+  const int64_t T = p.T, H = p.H;
+  const int lane = threadIdx.x;
+  const float* __restrict__ k = static_cast<const float*>(p.k);
+  const float* __restrict__ beta = static_cast<const float*>(p.beta);
+  const float* __restrict__ r = static_cast<const float*>(p.r);
+  float* __restrict__ kw = static_cast<float*>(p.kw);
+
+  float d[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) d[i] = p.d0 ? p.d0[bh * DK + lane * CPL + i] : 1.f;
+
+  float kc[U][CPL], bc[U], rc[U], kn[U][CPL], bn[U], rn[U];
+  // Tokens past the end read the last token (in bounds) and are skipped.
+  auto load = [&](int64_t t0, float (&kx)[U][CPL], float (&bx)[U], float (&rx)[U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t row = (b * T + (t0 + u < T ? t0 + u : T - 1)) * H + h;
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) kx[u][i] = k[row * DK + lane * CPL + i];
+      bx[u] = beta[row];
+      rx[u] = HAS_R ? r[row] : 1.f;
+    }
+  };
+  if (T > 0) load(0, kc, bc, rc);
+  for (int64_t t0 = 0; t0 < T; t0 += U) {
+    if (t0 + U < T) load(t0 + U, kn, bn, rn);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (t0 + u >= T) break;
+      const int64_t row = (b * T + t0 + u) * H + h;
+      float w[CPL], x = 0.f, n = 0.f;
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        w[i] = kc[u][i] * kc[u][i];
+        x = fmaf(d[i], w[i], x);
+        n += w[i];
+        kw[row * DK + lane * CPL + i] = d[i] * kc[u][i];
+      }
+      x = wave_sum(x);
+      n = wave_sum(n);
+      const float bt = bc[u];
+      const float e = n > 0.f ? p.eta * bt * (1.f - bt * x) / n : 0.f;
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) d[i] = fmaf(e, w[i], rc[u] * d[i]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      bc[u] = bn[u];
+      rc[u] = rn[u];
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) kc[u][i] = kn[u][i];
+    }
+  }
+  if (p.d_T) {
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) p.d_T[bh * DK + lane * CPL + i] = d[i];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 I/O: chunkwise, one workgroup (4 waves) per (sequence, head).
+// ---------------------------------------------------------------------------
+template <int DK>
+struct PsLayout {
+  static constexpr int LDK = DK + 8;    // bf16 row stride of the key and w tiles
+  static constexpr int LM = CH + 4;     // fp32 row stride of M
+  static constexpr int LL = CH + 8;     // bf16 row stride of the coefficient matrix L
+  static constexpr int NP = DK / 2;     // channel pairs in the chunk-end update
+  static constexpr int NQ = 256 / NP;   // token groups in the chunk-end update
+  static constexpr int TPQ = CH / NQ;   // tokens per group
+  static constexpr int KV = DK / 32;    // 16-byte key loads per thread
+  static constexpr size_t K_OFF = 0;
+  static constexpr size_t W_OFF = K_OFF + size_t(CH) * LDK * 2;
+  static constexpr size_t M_OFF = W_OFF + size_t(CH) * LDK * 2;
+  static constexpr size_t L_OFF = M_OFF + size_t(CH) * LM * 4;
+  static constexpr size_t D_OFF = L_OFF + size_t(CH) * LL * 2;    // d, two buffers
+  static constexpr size_t Q_OFF = D_OFF + size_t(2) * DK * 4;     // update partials [NQ][DK]
+  static constexpr size_t T_OFF = Q_OFF + size_t(NQ) * DK * 4;    // per-token rows
+  static constexpr int TR_N = 0, TR_P = 1, TR_BETA = 2, TR_GEX = 3, TR_GIN = 4, TR_E = 5, TR_C = 6, TR_ROWS = 7;
+  static constexpr size_t BYTES = T_OFF + size_t(TR_ROWS) * CH * 4;
+};
+
+// Output of one wave: the 16 tokens of block TB (t = 16 TB + lr) over all d_k
+// channels.  D^T = e^{g_t} d_0 1^T + W^T L^T is formed as 16x16 tiles (rows:
+// channels, columns: tokens), so each lane ends with four consecutive channels of
+// one token; kw = D * k goes out as 8-byte stores.
+template <int DK, bool HAS_R, int TB>
+__device__ __forceinline__ void precond_out_block(const __bf16* Wb, const __bf16* Lb, const __bf16* Kb,
+                                                  const float* d0, const float* tgex, rsrc_t kwr, uint32_t soff,
+                                                  int64_t H, int64_t h, int lr, int lg) {
+  typedef PsLayout<DK> L;
+  typedef Op<IO_BF16> op;
+  const int t = 16 * TB + lr;
+  const float Rt = HAS_R ? __expf(tgex[t]) : 1.f;
+  op::frag lf[TB + 1];
+#pragma unroll
+  for (int sb = 0; sb <= TB; ++sb) lf[sb] = op::ld(Lb + t * L::LL + 16 * sb + 4 * lg);
+  const uint32_t voff = static_cast<uint32_t>((t * H + h) * DK + 4 * lg) * 2;
+#pragma unroll
+  for (int c0 = 0; c0 < DK; c0 += 16) {
+    const f32x4 dv = *reinterpret_cast<const f32x4*>(d0 + c0 + 4 * lg);
+    f32x4 acc = {Rt * dv[0], Rt * dv[1], Rt * dv[2], Rt * dv[3]};
+#pragma unroll
+    for (int sb = 0; sb + 1 <= TB; sb += 2)
+      acc = op::mma2(acc, op::ld_tr(Wb, L::LDK, 16 * sb, c0, lr, lg), op::ld_tr(Wb, L::LDK, 16 * sb + 16, c0, lr, lg),
+                     lf[sb], lf[sb + 1]);
+    if ((TB & 1) == 0) acc = op::mma1(acc, op::ld_tr(Wb, L::LDK, 16 * TB, c0, lr, lg), lf[TB]);
+    const f32x4 kv = op::f32(op::ld(Kb + t * L::LDK + c0 + 4 * lg));
+    const f32x4 o = {acc[0] * kv[0], acc[1] * kv[1], acc[2] * kv[2], acc[3] * kv[3]};
+    buf_store8(__builtin_bit_cast(u32x2, to_bf16x4(o)), kwr, voff + 2 * c0, soff);
+  }
+}
+
+template <int DK, bool HAS_R>
+__global__ __launch_bounds__(256) void precond_scan_chunk_kernel(PrecondParams p) {
+  typedef PsLayout<DK> L;
+  typedef Op<IO_BF16> op;
+  typedef op::T bf;
+  __shared__ __align__(16) unsigned char smem[L::BYTES];
+  bf* Kb = reinterpret_cast<bf*>(smem + L::K_OFF);
+  bf* Wb = reinterpret_cast<bf*>(smem + L::W_OFF);
+  float* Ms = reinterpret_cast<float*>(smem + L::M_OFF);
+  bf* Lb = reinterpret_cast<bf*>(smem + L::L_OFF);
+  float* dbuf = reinterpret_cast<float*>(smem + L::D_OFF);
+  float* part = reinterpret_cast<float*>(smem + L::Q_OFF);
+  float* tok = reinterpret_cast<float*>(smem + L::T_OFF);
+  float* tn = tok + L::TR_N * CH;
+  float* tP = tok + L::TR_P * CH;
+  float* tbeta = tok + L::TR_BETA * CH;
+  float* tgex = tok + L::TR_GEX * CH;
+  float* tgin = tok + L::TR_GIN * CH;
+  float* te = tok + L::TR_E * CH;
+  float* tc = tok + L::TR_C * CH;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int64_t bh = blockIdx.x;
+  const int64_t b = bh / p.H, h = bh - b * p.H;
+  const int64_t T = p.T, H = p.H;
+  const float eta = p.eta;
+
+  // Buffer ranges over this sequence's slab: loads past the last token return
+  // zero and stores there are dropped, so the ragged last chunk needs no branch.
+  const uint32_t slab = static_cast<uint32_t>(T * H);
+  const rsrc_t kr = make_rsrc(static_cast<const uint16_t*>(p.k) + b * T * H * DK, slab * DK * 2);
+  const rsrc_t kwr = make_rsrc(static_cast<uint16_t*>(p.kw) + b * T * H * DK, slab * DK * 2);
+  const rsrc_t br = make_rsrc(static_cast<const uint16_t*>(p.beta) + b * T * H, slab * 2);
+  const rsrc_t rr = make_rsrc(HAS_R ? static_cast<const uint16_t*>(p.r) + b * T * H : nullptr, HAS_R ? slab * 2 : 0);
+
+  // Zero M once: blocks above the diagonal are never written.
+  for (int i = tid; i < CH * L::LM; i += 256) Ms[i] = 0.f;
+  if (tid < DK) dbuf[tid] = p.d0 ? p.d0[bh * DK + tid] : 1.f;
+
+  // Loader roles: thread (token lt, quarter lq) loads channels 8*(lq + 4j) .. +7;
+  // every lane also loads the factors of token `lane` (wave 0 uses them).
+  const int lt = tid >> 2, lq = tid & 3;
+  const uint32_t kvoff = static_cast<uint32_t>((lt * H + h) * DK + 8 * lq) * 2;
+  const uint32_t bvoff = static_cast<uint32_t>(lane * H + h) * 2;
+  u32x4 kreg[L::KV];
+  uint16_t beta_r = 0, r_r = 0;
+  auto load_chunk = [&](int64_t t0) {
+    const uint32_t so = static_cast<uint32_t>(t0 * H * DK * 2);
+#pragma unroll
+    for (int j = 0; j < L::KV; ++j) kreg[j] = buf_load16(kr, kvoff + 64 * j, so);
+    beta_r = buf_load2(br, bvoff, static_cast<uint32_t>(t0 * H * 2));
+    if (HAS_R) r_r = buf_load2(rr, bvoff, static_cast<uint32_t>(t0 * H * 2));
+  };
+  const int64_t nch = (T + CH - 1) / CH;
+  if (nch > 0) load_chunk(0);
+  __syncthreads();
+
+  int cur = 0;
+  for (int64_t n = 0; n < nch; ++n) {
+    const int64_t t0 = n * CH;
+    const float* d0 = dbuf + cur * DK;
+
+    // ---- S1: stage k and bf16(k^2); n_t and <w_t, d_0> in fp32 ----------------
+    {
+      float sn = 0.f, sp = 0.f;
+#pragma unroll
+      for (int j = 0; j < L::KV; ++j) {
+        const int c = 8 * (lq + 4 * j);
+        const f32x4 da = *reinterpret_cast<const f32x4*>(d0 + c);
+        const f32x4 db = *reinterpret_cast<const f32x4*>(d0 + c + 4);
+        float w[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float k0 = __uint_as_float(kreg[j][e] << 16), k1 = __uint_as_float(kreg[j][e] & 0xFFFF0000u);
+          w[2 * e] = k0 * k0;
+          w[2 * e + 1] = k1 * k1;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          sn += w[e];
+          sp = fmaf(w[e], e < 4 ? da[e] : db[e - 4], sp);
+        }
+        *reinterpret_cast<u32x4*>(Kb + lt * L::LDK + c) = kreg[j];
+        bf16x8 wb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) wb[e] = static_cast<__bf16>(w[e]);
+        *reinterpret_cast<bf16x8*>(Wb + lt * L::LDK + c) = wb;
+      }
+      sn = quad_sum(sn);
+      sp = quad_sum(sp);
+      if (lq == 0) { tn[lt] = sn; tP[lt] = sp; }
+      if (wave == 0) {
+        const bool ok = t0 + lane < T;
+        const float lrv = HAS_R && ok ? __logf(bf16_bits_to_f32(r_r)) : 0.f;
+        const float gin = HAS_R ? wave_prefix_sum(lrv) : 0.f;
+        tbeta[lane] = bf16_bits_to_f32(beta_r);   // zero past the end
+        tgin[lane] = gin;
+        tgex[lane] = gin - lrv;
+      }
+      // Prefetch the next chunk while this one is processed.
+      if (n + 1 < nch) load_chunk(t0 + CH);
+    }
+    __syncthreads();
+
+    // ---- S2: M = alf_t e^{g_t - g_{s+1}} <w_t, w_s> (s < t) on MFMA -----------
+    float bt_chain = 0.f;
+    {
+      // Ten lower-triangular 16x16 tiles (R, J), J <= R: wave w takes tiles w,
+      // w + 4 and w + 8; waves 2 and 3 have only two (their third is computed
+      // again and not stored, which keeps the code free of branches).
+      f32x4 acc[3];
+      int Rs[3], Js[3];
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        const int u = wave + 4 * i < 10 ? wave + 4 * i : wave + 4;
+        Rs[i] = u < 1 ? 0 : u < 3 ? 1 : u < 6 ? 2 : 3;
+        Js[i] = u - Rs[i] * (Rs[i] + 1) / 2;
+        acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int k0 = 0; k0 < DK; k0 += 32) {
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+          const bf* arow = Wb + (16 * Rs[i] + lr) * L::LDK + 4 * lg + k0;
+          const bf* brow = Wb + (16 * Js[i] + lr) * L::LDK + 4 * lg + k0;
+          acc[i] = op::mma2(acc[i], op::ld(arow), op::ld(arow + 16), op::ld(brow), op::ld(brow + 16));
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        if (i < 2 || wave < 2) {
+          const int t4 = 16 * Rs[i] + 4 * lg, s = 16 * Js[i] + lr;
+          const f32x4 nn = *reinterpret_cast<const f32x4*>(tn + t4);
+          const f32x4 be = *reinterpret_cast<const f32x4*>(tbeta + t4);
+          const f32x4 gx = *reinterpret_cast<const f32x4*>(tgex + t4);
+          const float gs = tgin[s];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float alf = nn[q] > 0.f ? eta * be[q] * be[q] * __builtin_amdgcn_rcpf(nn[q]) : 0.f;
+            const float dec = HAS_R ? __expf(gx[q] - gs) : 1.f;
+            Ms[(t4 + q) * L::LM + s] = s < t4 + q ? alf * dec * acc[i][q] : 0.f;
+          }
+        }
+      }
+      if (wave == 0) {
+        const float nn = tn[lane], be = tbeta[lane];
+        const float gam = nn > 0.f ? eta * be * __builtin_amdgcn_rcpf(nn) : 0.f;   // alf_t = gam_t beta_t
+        const float Rt = HAS_R ? __expf(tgex[lane]) : 1.f;
+        bt_chain = gam - gam * be * Rt * tP[lane];
+      }
+    }
+    __syncthreads();
+
+    // ---- S3: forward substitution (I + M) e = b on one wave --------------------
+    if (wave == 0) {
+      float m[CH];
+      const float* mrow = Ms + lane * L::LM;
+#pragma unroll
+      for (int i = 0; i < CH; i += 4) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(mrow + i);
+        m[i] = v[0]; m[i + 1] = v[1]; m[i + 2] = v[2]; m[i + 3] = v[3];
+      }
+      float acc = bt_chain;
+#pragma unroll
+      for (int s = 0; s < CH; ++s) {
+        const float es = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), s));
+        acc = fmaf(-m[s], es, acc);
+      }
+      te[lane] = acc;
+      tc[lane] = HAS_R ? __expf(tgin[CH - 1] - tgin[lane]) * acc : acc;
+    }
+    __syncthreads();
+
+    // ---- S4: L_ts = e^{g_t - g_{s+1}} e_s (s < t) in bf16; chunk-end partials --
+    {
+      const int t = tid >> 2, s0 = 16 * (tid & 3);
+      const float gt = tgex[t];
+      float gi[16], ev[16];
+#pragma unroll
+      for (int i = 0; i < 16; i += 4) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(tgin + s0 + i);
+        const f32x4 e = *reinterpret_cast<const f32x4*>(te + s0 + i);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) { gi[i + q] = a[q]; ev[i + q] = e[q]; }
+      }
+      bf16x8 lo, hi;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float v = (HAS_R ? __expf(gt - gi[i]) : 1.f) * ev[i];
+        const float x = s0 + i < t ? v : 0.f;
+        if (i < 8) lo[i] = static_cast<__bf16>(x); else hi[i - 8] = static_cast<__bf16>(x);
+      }
+      *reinterpret_cast<bf16x8*>(Lb + t * L::LL + s0) = lo;
+      *reinterpret_cast<bf16x8*>(Lb + t * L::LL + s0 + 8) = hi;
+
+      const int cp = tid % L::NP, qd = tid / L::NP;
+      float cs[L::TPQ];
+      uint32_t ku[L::TPQ];
+#pragma unroll
+      for (int i = 0; i < L::TPQ; i += 4) {
+        const f32x4 c = *reinterpret_cast<const f32x4*>(tc + qd * L::TPQ + i);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) cs[i + q] = c[q];
+      }
+#pragma unroll
+      for (int i = 0; i < L::TPQ; ++i)
+        ku[i] = *reinterpret_cast<const uint32_t*>(Kb + (qd * L::TPQ + i) * L::LDK + 2 * cp);
+      float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < L::TPQ; ++i) {
+        const float k0 = __uint_as_float(ku[i] << 16), k1 = __uint_as_float(ku[i] & 0xFFFF0000u);
+        a0 = fmaf(cs[i], k0 * k0, a0);
+        a1 = fmaf(cs[i], k1 * k1, a1);
+      }
+      *reinterpret_cast<float2*>(part + qd * DK + 2 * cp) = make_float2(a0, a1);
+    }
+    __syncthreads();
+
+    // ---- S5: kw_t = (e^{g_t} d_0 + sum_s L_ts w_s) * k_t on MFMA; d_64 -------------
+    {
+      const uint32_t so = static_cast<uint32_t>(t0 * H * DK * 2);
+      switch (wave) {
+        case 0: precond_out_block<DK, HAS_R, 0>(Wb, Lb, Kb, d0, tgex, kwr, so, H, h, lr, lg); break;
+        case 1: precond_out_block<DK, HAS_R, 1>(Wb, Lb, Kb, d0, tgex, kwr, so, H, h, lr, lg); break;
+        case 2: precond_out_block<DK, HAS_R, 2>(Wb, Lb, Kb, d0, tgex, kwr, so, H, h, lr, lg); break;
+        default: precond_out_block<DK, HAS_R, 3>(Wb, Lb, Kb, d0, tgex, kwr, so, H, h, lr, lg); break;
+      }
+      if (tid < DK) {
+        const float RC = HAS_R ? __expf(tgin[CH - 1]) : 1.f;
+        float s = RC * d0[tid];
+#pragma unroll
+        for (int q = 0; q < L::NQ; ++q) s += part[q * DK + tid];
+        dbuf[(cur ^ 1) * DK + tid] = s;
+      }
+    }
+    __syncthreads();
+    cur ^= 1;
+  }
+  if (p.d_T && tid < DK) p.d_T[bh * DK + tid] = dbuf[cur * DK + tid];
+}
+
+template <int DK, bool HAS_R>
+static hipError_t launch_chunk_t(const PrecondParams& p, hipStream_t stream) {
+  constexpr size_t lds = PsLayout<DK>::BYTES;
+  static_assert(lds <= 160 * 1024, "LDS budget");
+  hipLaunchKernelGGL((precond_scan_chunk_kernel<DK, HAS_R>), dim3(static_cast<unsigned>(p.B * p.H)), dim3(256),
+                     0, stream, p);
+  return hipGetLastError();
+}
+
+template <int DK, bool HAS_R>
+static hipError_t launch_seq_t(const PrecondParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL((precond_scan_seq_kernel<DK, HAS_R>), dim3(static_cast<unsigned>(p.B * p.H)), dim3(64), 0,
+                     stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_precond_scan(const PrecondParams& p, hipStream_t stream) {
+  if (p.B * p.H == 0) return hipSuccess;
+  const bool hr = p.r != nullptr;
+  if (p.io == IO_BF16) {
+    if (p.d_k == 128) return hr ? launch_chunk_t<128, true>(p, stream) : launch_chunk_t<128, false>(p, stream);
+    if (p.d_k == 64) return hr ? launch_chunk_t<64, true>(p, stream) : launch_chunk_t<64, false>(p, stream);
+    return hipErrorInvalidValue;
+  }
+  if (p.d_k == 128) return hr ? launch_seq_t<128, true>(p, stream) : launch_seq_t<128, false>(p, stream);
+  if (p.d_k == 64) return hr ? launch_seq_t<64, true>(p, stream) : launch_seq_t<64, false>(p, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gdr

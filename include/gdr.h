@@ -237,6 +237,42 @@ gdr_status gdr_recurrent_step_wkey(const gdr_desc* desc, const void* q, const vo
                                    const void* v, const void* beta, const float* S, float* S_new,
                                    void* o, void* stream /* hipStream_t */);
 
+/*
+ * gdr_precond_scan -- the preconditioner scan that produces the write keys of the
+ * preconditioned delta rule ("OSDN: Improving Delta Rule with Provable Online
+ * Preconditioning in Linear Attention", §2.2: a first phase over the keys alone;
+ * each token's write key is the diagonal preconditioner d_t times the key, then
+ * d takes one online-gradient step on the closed-form surrogate
+ * h_t(d) = ((1 - beta_t <d, k_t^2>)^2 - 1) / (2 ||k_t||^2); §2.3: adaptive
+ * preconditioner forgetting multiplies d by a per-token, per-head retention r_t).
+ * For each (b, h) independently, token by token from d_0:
+ *
+ *     kw_t    = d_t * k_t                                  (elementwise)
+ *     d_{t+1} = r_t d_t + eta beta_t (1 - beta_t <d_t, k_t^2>) k_t^2 / ||k_t||^2
+ *
+ * a descent step on h_t (a zero key adds nothing; r_t = 1 without forgetting).
+ * The kw it writes is the write key of gdr_chunk_fwd_wkey / gdr_recurrent_step_wkey.
+ *
+ * desc: B, T (>= 0), H, d_k (64 or 128) and io are read; d_v, chunk, gate and
+ * form are ignored.
+ *   k     [B, T, H, d_k]  io dtype, 16-byte aligned
+ *   beta  [B, T, H]       io dtype
+ *   r     [B, T, H]       io dtype retention (> 0; the kernels take its log), or
+ *         NULL for no forgetting
+ *   eta   step size, finite
+ *   d0    [B, H, d_k] fp32 preconditioner before token 0, or NULL (all ones)
+ *   kw    [B, T, H, d_k]  io dtype, written, 16-byte aligned (k, beta and kw may
+ *         be NULL only when T == 0)
+ *   d_T   [B, H, d_k] fp32 preconditioner after the last token, or NULL to skip
+ *         it; may be the same pointer as d0 (updated in place)
+ * kw and d_T overlap no other argument (except d_T == d0).  T == 0 writes
+ * d_T = d0 (or ones).  bf16 runs the chunkwise form (bf16 products with fp32
+ * accumulation for the key Gram matrix and the per-token preconditioners; the
+ * preconditioner carried between chunks in fp32); fp32 runs token by token in fp32.
+ */
+gdr_status gdr_precond_scan(const gdr_desc* desc, const void* k, const void* beta, const void* r, float eta,
+                            const float* d0, void* kw, float* d_T, void* stream /* hipStream_t */);
+
 #ifdef __cplusplus
 }
 #endif

@@ -246,3 +246,33 @@ def test_write_key_step_checks(lib):
     assert call(d, kw + 4) == ALIGN
     assert call(d, p[7] + 64) == INVALID                                   # kw inside S_new
     assert b"overlaps" in lib.gdr_last_error()
+
+
+def _scan(lib, d, k, beta, r, eta, d0, kw, d_T):
+    return lib.gdr_precond_scan(None if d is None else ctypes.byref(d), k, beta, r, eta, d0, kw, d_T, None)
+
+
+def test_precond_scan_checks(lib):
+    k, beta, r, d0, kw, dT = _ptrs(6)
+    d = _desc(gate=0)
+    assert _scan(lib, None, k, beta, r, 1.0, d0, kw, dT) == INVALID
+    for field, value, code in (("io", 7, INVALID), ("B", 0, INVALID), ("H", 0, INVALID), ("T", -1, INVALID),
+                               ("d_k", 96, UNSUPPORTED)):
+        assert _scan(lib, _desc(gate=0, **{field: value}), k, beta, r, 1.0, d0, kw, dT) == code, field
+    for eta in (float("nan"), float("inf"), -float("inf")):
+        assert _scan(lib, d, k, beta, r, eta, d0, kw, dT) == INVALID
+    assert _scan(lib, d, None, beta, r, 1.0, d0, kw, dT) == INVALID
+    assert _scan(lib, d, k, None, r, 1.0, d0, kw, dT) == INVALID
+    assert _scan(lib, d, k, beta, r, 1.0, d0, None, dT) == INVALID
+    assert _scan(lib, d, k + 8, beta, r, 1.0, d0, kw, dT) == ALIGN
+    assert _scan(lib, d, k, beta, r, 1.0, d0, kw + 8, dT) == ALIGN
+    assert _scan(lib, d, k, beta + 1, r, 1.0, d0, kw, dT) == ALIGN
+    assert _scan(lib, d, k, beta, r + 1, 1.0, d0, kw, dT) == ALIGN
+    assert _scan(lib, d, k, beta, r, 1.0, d0 + 2, kw, dT) == ALIGN
+    assert _scan(lib, _desc(gate=0, io=0, d_k=64), k, beta + 2, r, 1.0, d0, kw, dT) == ALIGN   # fp32: 4 bytes
+    assert _scan(lib, d, k, beta, r, 1.0, d0, k + 64, dT) == INVALID            # kw inside k
+    assert b"kw overlaps k" in lib.gdr_last_error()
+    assert _scan(lib, d, k, beta, r, 1.0, d0, kw, kw + 256) == INVALID          # d_T inside kw
+    assert _scan(lib, d, k, beta, r, 1.0, d0, kw, d0 + 16) == INVALID           # d_T partly over d0
+    assert _scan(lib, d, k, beta, r, 1.0, dT, k + 64, dT) == INVALID            # d_T == d0 is allowed ...
+    assert b"kw overlaps k" in lib.gdr_last_error()                             # ... the error is kw's

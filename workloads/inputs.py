@@ -20,6 +20,14 @@ regenerated on its own):
   * every tensor is rounded float64 -> float32 (round to nearest even) and, for
     bf16 I/O, float32 -> bf16 (round to nearest even).  S0 stays float32.
 
+Preconditioner-scan inputs reuse k and beta of the (b, h) slice above (the
+scan runs over the same keys as the forward) and draw, per (b, h), the
+retention r_t = sigmoid(z + 3) (z standard normal, stream SeedSequence([seed, b,
+h, 2]); median 0.95, all in (0, 1)) and a starting preconditioner
+d0 ~ U(0.5, 1.5) (stream SeedSequence([seed, b, h, 3]), float32).  The step
+size is PRECOND_ETA.  The pages give no value for either; these keep d of order
+one over long sequences.
+
 Decode workloads draw, per (sequence n, head h), S0 from SeedSequence([seed, n,
 h, 1]) and the token stream from SeedSequence([seed, n, h]) as a [steps,
 2*d_k + d_v + 2] array (row s = step s: q, k, v, beta logit, gate logit).
@@ -34,7 +42,8 @@ import numpy as np
 
 __all__ = [
     "Workload", "CONFIGS", "DECODE_CONFIG", "round_to_io", "bf16_round",
-    "slice_inputs", "chunk_inputs", "decode_slice", "decode_inputs",
+    "slice_inputs", "chunk_inputs", "decode_slice", "decode_inputs", "PRECOND_ETA",
+    "precond_slice", "precond_inputs",
 ]
 
 
@@ -230,3 +239,36 @@ def decode_inputs(wl: DecodeWorkload, steps: Optional[int] = None) -> dict:
                 log_a[:, n, h] = s["log_a"]
             S0[n, h] = s["S0"]
     return dict(q=q, k=k, v=v, beta=beta, log_a=log_a, S0=S0)
+
+
+PRECOND_ETA = 1.0
+
+
+def precond_slice(wl: Workload, b: int, h: int, T: Optional[int] = None) -> dict:
+    """Preconditioner-scan inputs of one (b, h) slice: k [T, d_k]; beta [T];
+    r [T] (retention); d0 [d_k] float32."""
+    T = wl.T if T is None else T
+    s = slice_inputs(wl, b, h, T)
+    rr = np.random.Generator(np.random.PCG64(np.random.SeedSequence([wl.seed, b, h, 2])))
+    r = round_to_io(_sigmoid(rr.standard_normal(T) + 3.0), wl.io)
+    rd = np.random.Generator(np.random.PCG64(np.random.SeedSequence([wl.seed, b, h, 3])))
+    d0 = rd.uniform(0.5, 1.5, wl.d_k).astype(np.float32)
+    return dict(k=s["k"], beta=s["beta"], r=r, d0=d0)
+
+
+def precond_inputs(wl: Workload, T: Optional[int] = None) -> dict:
+    """All slices: k [B, T, H, d_k]; beta, r [B, T, H]; d0 [B, H, d_k] float32."""
+    T = wl.T if T is None else T
+    B, H, dk = wl.B, wl.H, wl.d_k
+    k = np.empty((B, T, H, dk), np.float32)
+    beta = np.empty((B, T, H), np.float32)
+    r = np.empty((B, T, H), np.float32)
+    d0 = np.empty((B, H, dk), np.float32)
+    for b in range(B):
+        for h in range(H):
+            s = precond_slice(wl, b, h, T)
+            k[b, :, h] = s["k"]
+            beta[b, :, h] = s["beta"]
+            r[b, :, h] = s["r"]
+            d0[b, h] = s["d0"]
+    return dict(k=k, beta=beta, r=r, d0=d0)
