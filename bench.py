@@ -9,7 +9,9 @@ inputs already resident in HBM.  The decode step (256 sequences x 32 heads,
 fp32 128x128 states, bf16 tokens) is timed in the same run and reported as GB/s,
 and so is the serving handoff: a packed prefill of 32 prompts of log-uniform
 lengths in [128, 8192] (H=16, d=128, scalar gate) through gdr_chunk_fwd_varlen,
-then decode steps on the states it hands over (`handoff`).
+then decode steps on the states it hands over (`handoff`), and the
+preconditioner scan of the preconditioned delta rule (with forgetting) over the
+workload's keys (`precond_scan`, GB/s against HBM peak).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
@@ -40,6 +42,8 @@ CHUNK_SOURCES = [os.path.join(ROOT, "gated_delta_rule_21_amd", "csrc", n)
                  for n in ("chunk_prep.hip", "chunk_state.hip", "chunk_fwd.hip", "chunk_common.h", "device_common.h")]
 DECODE_SOURCES = [os.path.join(ROOT, "gated_delta_rule_21_amd", "csrc", n)
                   for n in ("decode_step.hip", "device_common.h")]
+PRECOND_SOURCES = [os.path.join(ROOT, "gated_delta_rule_21_amd", "csrc", n)
+                   for n in ("precond_scan.hip", "chunk_common.h", "device_common.h")]
 
 
 def chunk_algorithmic(wl, with_S0: bool):
@@ -175,7 +179,7 @@ def bench_chunk(args, log):
     ms = ev0.elapsed_time(ev1) / args.steps
     log(f"chunk forward: {ms:.3f} ms/step (wall {1e3 * wall / args.steps:.3f} ms/step)")
     nbytes, flops = chunk_algorithmic(wl, with_S0=with_S0)
-    return wl, ms, nbytes, flops
+    return wl, ms, nbytes, flops, (k, beta)
 
 
 def bench_decode(args, log):
@@ -215,6 +219,50 @@ def bench_decode(args, log):
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4),
                          "traffic": profiled_traffic("decode_step_n256h32d128_counters.md", DECODE_SOURCES)}}
+
+
+def precond_bytes(B: int, T: int, H: int, d_k: int, esz: int, apf: bool) -> int:
+    """Bytes of one preconditioner scan: k, beta (and r) read once, d0 read, kw and
+    d_T written once."""
+    ntok = B * T * H
+    return ntok * (2 * d_k * esz + esz * (2 if apf else 1)) + 2 * B * H * d_k * 4
+
+
+def bench_precond(args, log, wl, k, beta):
+    """The preconditioner scan (with forgetting) over the keys of the chunk workload."""
+    import torch
+    import gated_delta_rule_21_amd as gdr
+    from workloads import PRECOND_ETA, precond_factors
+    log("generating the scan's retention and starting preconditioner")
+    f = precond_factors(wl)
+    r = torch.from_numpy(f["r"]).to(torch.bfloat16).cuda()
+    d0 = torch.from_numpy(f["d0"]).cuda()
+    kw = torch.empty_like(k)
+    dT = torch.empty_like(d0)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        gdr.precond_scan(k, beta, PRECOND_ETA, r, d0, kw=kw, d_T=dT)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    nbytes = precond_bytes(wl.B, wl.T, wl.H, wl.d_k, 2, True)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"preconditioner scan: {ms * 1e3:.1f} us, {gbs:.0f} GB/s")
+    return {"workload": "osdn_precond_scan_apf_b%dh%dt%dd%d_bf16" % (wl.B, wl.H, wl.T, wl.d_k),
+            "value": round(gbs, 1), "unit": "GB/s", "us_per_launch": round(ms * 1e3, 2),
+            "tokens_per_s": round(wl.B * wl.T / (ms * 1e-3), 1), "bytes_per_launch": nbytes,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": profiled_traffic("precond_scan_b8h16t8192d128_counters.md", PRECOND_SOURCES)}}
 
 
 def handoff_lengths(n_seq: int = 32, lo: int = 128, hi: int = 8192, seed: int = 6):
@@ -295,6 +343,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-handoff", action="store_true",
                     help="skip the packed-prefill -> decode handoff leg")
+    ap.add_argument("--no-precond", action="store_true", help="skip the preconditioner-scan leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-T", type=int, default=8192)
     ap.add_argument("--cpu-heads", type=int, default=16)
@@ -324,12 +373,14 @@ def main():
     if args.copy_calibration:
         copy_calibration(log)
 
-    wl, ms, nbytes, flops = bench_chunk(args, log)
+    wl, ms, nbytes, flops, (k, beta) = bench_chunk(args, log)
     tok_s = wl.B * wl.T / (ms * 1e-3)
     gbs = nbytes / (ms * 1e-3) / 1e9
     tflops = flops / (ms * 1e-3) / 1e12
     decode = None if args.no_decode else bench_decode(args, log)
     handoff = None if args.no_handoff else bench_handoff(args, log)
+    precond = None if args.no_precond else bench_precond(args, log, wl, k, beta)
+    del k, beta
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle sample")
@@ -362,6 +413,7 @@ def main():
         "useful_flops_per_launch": flops,
         "decode": decode,
         "handoff": handoff,
+        "precond_scan": precond,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -340,9 +340,9 @@ gdr_status gdr_precond_scan(const gdr_desc* d, const void* k, const void* beta, 
         !mul_ok(elems, esz, &bytes))
       return fail(GDR_ERR_INVALID_ARG, "sizes overflow");
     if (bh > INT32_MAX) return fail(GDR_ERR_UNSUPPORTED, "B*H = %lld exceeds the grid limit", (long long)bh);
-    if ((d->T + 64) * d->H * d->d_k * esz > INT32_MAX)   // 32-bit offsets within one sequence, one chunk past its end
-      return fail(GDR_ERR_UNSUPPORTED, "(T + 64)*H*d_k*elem_size = %lld bytes exceeds 2^31 - 1 per sequence",
-                  (long long)((d->T + 64) * d->H * d->d_k * esz));
+    if ((d->T + 128) * d->H * d->d_k * esz > INT32_MAX)   // 32-bit offsets within a sequence, two chunks past its end
+      return fail(GDR_ERR_UNSUPPORTED, "(T + 128)*H*d_k*elem_size = %lld bytes exceeds 2^31 - 1 per sequence",
+                  (long long)((d->T + 128) * d->H * d->d_k * esz));
     if (d->T > 0) {
       if (!k) return fail(GDR_ERR_INVALID_ARG, "k is NULL");
       if (!beta) return fail(GDR_ERR_INVALID_ARG, "beta is NULL");

@@ -146,50 +146,78 @@ template <int DK>
 struct PsLayout {
   static constexpr int LDK = DK + 8;    // bf16 row stride of the key and w tiles
   static constexpr int LM = CH + 4;     // fp32 row stride of M
-  static constexpr int LL = CH + 8;     // bf16 row stride of the coefficient matrix L
   static constexpr int NP = DK / 2;     // channel pairs in the chunk-end update
   static constexpr int NQ = 256 / NP;   // token groups in the chunk-end update
   static constexpr int TPQ = CH / NQ;   // tokens per group
   static constexpr int KV = DK / 32;    // 16-byte key loads per thread
+  static constexpr int CT = DK / 64;    // 16-channel output tiles per wave
   static constexpr size_t K_OFF = 0;
   static constexpr size_t W_OFF = K_OFF + size_t(CH) * LDK * 2;
   static constexpr size_t M_OFF = W_OFF + size_t(CH) * LDK * 2;
-  static constexpr size_t L_OFF = M_OFF + size_t(CH) * LM * 4;
-  static constexpr size_t D_OFF = L_OFF + size_t(CH) * LL * 2;    // d, two buffers
+  static constexpr size_t D_OFF = M_OFF + size_t(CH) * LM * 4;    // d, two buffers
   static constexpr size_t Q_OFF = D_OFF + size_t(2) * DK * 4;     // update partials [NQ][DK]
   static constexpr size_t T_OFF = Q_OFF + size_t(NQ) * DK * 4;    // per-token rows
-  static constexpr int TR_N = 0, TR_P = 1, TR_BETA = 2, TR_GEX = 3, TR_GIN = 4, TR_E = 5, TR_C = 6, TR_ROWS = 7;
+  // n_t, <w_t, d_0>, beta_t, g_t, g_{t+1}, e^{g_t}, e^{-g_{t+1}}, e_t (scaled), c_t
+  static constexpr int TR_N = 0, TR_P = 1, TR_BETA = 2, TR_GEX = 3, TR_GIN = 4, TR_R = 5, TR_IR = 6, TR_EH = 7,
+                       TR_C = 8, TR_ROWS = 9;
   static constexpr size_t BYTES = T_OFF + size_t(TR_ROWS) * CH * 4;
 };
 
-// Output of one wave: the 16 tokens of block TB (t = 16 TB + lr) over all d_k
-// channels.  D^T = e^{g_t} d_0 1^T + W^T L^T is formed as 16x16 tiles (rows:
-// channels, columns: tokens), so each lane ends with four consecutive channels of
-// one token; kw = D * k goes out as 8-byte stores.
-template <int DK, bool HAS_R, int TB>
-__device__ __forceinline__ void precond_out_block(const __bf16* Wb, const __bf16* Lb, const __bf16* Kb,
-                                                  const float* d0, const float* tgex, rsrc_t kwr, uint32_t soff,
-                                                  int64_t H, int64_t h, int lr, int lg) {
+// The factored form of the decays (e^{g_t - g_{s+1}} = e^{g_t} e^{-g_{s+1}}) is
+// used when the chunk's total log-retention is at least this; both factors then
+// stay within fp32 range.  Below it, each entry takes its own exponential.
+constexpr float PS_FACTOR_MIN_G = -80.f;
+
+// Gram tiles of one wave: (R, J) blocks of W W^T, J <= R, as (row, col) lists.
+// Every wave loads only the 16-token row blocks its tiles use.
+template <int W> struct PsGram;
+template <> struct PsGram<0> { static constexpr int N = 3, NEED = 0x3; static constexpr int R[3] = {0, 1, 1}, J[3] = {0, 0, 1}; };
+template <> struct PsGram<1> { static constexpr int N = 3, NEED = 0x7; static constexpr int R[3] = {2, 2, 2}, J[3] = {0, 1, 2}; };
+template <> struct PsGram<2> { static constexpr int N = 2, NEED = 0xB; static constexpr int R[3] = {3, 3, 0}, J[3] = {0, 1, 0}; };
+template <> struct PsGram<3> { static constexpr int N = 2, NEED = 0xC; static constexpr int R[3] = {3, 3, 0}, J[3] = {2, 3, 0}; };
+
+// M_ts = alf_t e^{g_t - g_{s+1}} <w_t, w_s> for s < t (0 elsewhere) into Ms.
+template <int DK, bool HAS_R, int W>
+__device__ __forceinline__ void precond_gram(const __bf16* Wb, float* Ms, const float* tok, float eta, bool fact,
+                                             int lr, int lg) {
   typedef PsLayout<DK> L;
   typedef Op<IO_BF16> op;
-  const int t = 16 * TB + lr;
-  const float Rt = HAS_R ? __expf(tgex[t]) : 1.f;
-  op::frag lf[TB + 1];
+  typedef PsGram<W> G;
+  f32x4 acc[G::N];
 #pragma unroll
-  for (int sb = 0; sb <= TB; ++sb) lf[sb] = op::ld(Lb + t * L::LL + 16 * sb + 4 * lg);
-  const uint32_t voff = static_cast<uint32_t>((t * H + h) * DK + 4 * lg) * 2;
+  for (int i = 0; i < G::N; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int c0 = 0; c0 < DK; c0 += 16) {
-    const f32x4 dv = *reinterpret_cast<const f32x4*>(d0 + c0 + 4 * lg);
-    f32x4 acc = {Rt * dv[0], Rt * dv[1], Rt * dv[2], Rt * dv[3]};
+  for (int k0 = 0; k0 < DK; k0 += 32) {
+    op::frag lo[4], hi[4];
 #pragma unroll
-    for (int sb = 0; sb + 1 <= TB; sb += 2)
-      acc = op::mma2(acc, op::ld_tr(Wb, L::LDK, 16 * sb, c0, lr, lg), op::ld_tr(Wb, L::LDK, 16 * sb + 16, c0, lr, lg),
-                     lf[sb], lf[sb + 1]);
-    if ((TB & 1) == 0) acc = op::mma1(acc, op::ld_tr(Wb, L::LDK, 16 * TB, c0, lr, lg), lf[TB]);
-    const f32x4 kv = op::f32(op::ld(Kb + t * L::LDK + c0 + 4 * lg));
-    const f32x4 o = {acc[0] * kv[0], acc[1] * kv[1], acc[2] * kv[2], acc[3] * kv[3]};
-    buf_store8(__builtin_bit_cast(u32x2, to_bf16x4(o)), kwr, voff + 2 * c0, soff);
+    for (int R = 0; R < 4; ++R)
+      if (G::NEED & (1 << R)) {
+        const __bf16* row = Wb + (16 * R + lr) * L::LDK + k0 + 4 * lg;
+        lo[R] = op::ld(row);
+        hi[R] = op::ld(row + 16);
+      }
+#pragma unroll
+    for (int i = 0; i < G::N; ++i)
+      acc[i] = op::mma2(acc[i], lo[G::R[i]], hi[G::R[i]], lo[G::J[i]], hi[G::J[i]]);
+  }
+  const float* tn = tok + L::TR_N * CH;
+  const float* tbeta = tok + L::TR_BETA * CH;
+#pragma unroll
+  for (int i = 0; i < G::N; ++i) {
+    const int t4 = 16 * G::R[i] + 4 * lg, s = 16 * G::J[i] + lr;
+    const f32x4 nn = *reinterpret_cast<const f32x4*>(tn + t4);
+    const f32x4 be = *reinterpret_cast<const f32x4*>(tbeta + t4);
+    const f32x4 rt = *reinterpret_cast<const f32x4*>(tok + L::TR_R * CH + t4);
+    const f32x4 gx = *reinterpret_cast<const f32x4*>(tok + L::TR_GEX * CH + t4);
+    const float irs = tok[L::TR_IR * CH + s], gs = tok[L::TR_GIN * CH + s];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      // A zero key has a zero Gram row, so a clamped n_t is enough.
+      const float alf = eta * be[q] * be[q] * __builtin_amdgcn_rcpf(fmaxf(nn[q], 1e-30f));
+      float dec = 1.f;
+      if (HAS_R) dec = fact ? rt[q] * irs : __expf(fminf(gx[q] - gs, 0.f));
+      Ms[(t4 + q) * L::LM + s] = (s < t4 + q ? 1.f : 0.f) * alf * dec * acc[i][q];
+    }
   }
 }
 
@@ -202,7 +230,6 @@ __global__ __launch_bounds__(256) void precond_scan_chunk_kernel(PrecondParams p
   bf* Kb = reinterpret_cast<bf*>(smem + L::K_OFF);
   bf* Wb = reinterpret_cast<bf*>(smem + L::W_OFF);
   float* Ms = reinterpret_cast<float*>(smem + L::M_OFF);
-  bf* Lb = reinterpret_cast<bf*>(smem + L::L_OFF);
   float* dbuf = reinterpret_cast<float*>(smem + L::D_OFF);
   float* part = reinterpret_cast<float*>(smem + L::Q_OFF);
   float* tok = reinterpret_cast<float*>(smem + L::T_OFF);
@@ -211,11 +238,15 @@ __global__ __launch_bounds__(256) void precond_scan_chunk_kernel(PrecondParams p
   float* tbeta = tok + L::TR_BETA * CH;
   float* tgex = tok + L::TR_GEX * CH;
   float* tgin = tok + L::TR_GIN * CH;
-  float* te = tok + L::TR_E * CH;
+  float* tR = tok + L::TR_R * CH;
+  float* tIR = tok + L::TR_IR * CH;
+  float* teh = tok + L::TR_EH * CH;
   float* tc = tok + L::TR_C * CH;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  // the wave index is uniform: keeping it scalar makes every wave test a scalar
+  // branch (and keeps buffer offsets in scalar registers)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int lr = lane & 15, lg = lane >> 4;
   const int64_t bh = blockIdx.x;
   const int64_t b = bh / p.H, h = bh - b * p.H;
@@ -242,113 +273,94 @@ __global__ __launch_bounds__(256) void precond_scan_chunk_kernel(PrecondParams p
   u32x4 kreg[L::KV];
   uint16_t beta_r = 0, r_r = 0;
   auto load_chunk = [&](int64_t t0) {
-    const uint32_t so = static_cast<uint32_t>(t0 * H * DK * 2);
+    const uint32_t so = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(t0 * H * DK * 2));
+    const uint32_t sb = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(t0 * H * 2));
 #pragma unroll
     for (int j = 0; j < L::KV; ++j) kreg[j] = buf_load16(kr, kvoff + 64 * j, so);
-    beta_r = buf_load2(br, bvoff, static_cast<uint32_t>(t0 * H * 2));
-    if (HAS_R) r_r = buf_load2(rr, bvoff, static_cast<uint32_t>(t0 * H * 2));
+    beta_r = buf_load2(br, bvoff, sb);
+    if (HAS_R) r_r = buf_load2(rr, bvoff, sb);
   };
   const int64_t nch = (T + CH - 1) / CH;
-  if (nch > 0) load_chunk(0);
+  load_chunk(0);
+  __syncthreads();   // M zeroed, d_0 in place
+
+  // ---- stage: k and bf16(k^2) into LDS, n_t, the chunk's log-retention sums ----
+  // Run for chunk 0 before the loop and for chunk n + 1 at the bottom of
+  // iteration n (after chunk n's output stores, so the wait for the prefetched
+  // keys is not also a wait for those stores).  It then prefetches the chunk
+  // after, unconditionally: past the last chunk the loads fall outside the
+  // buffer range and return zeros without touching memory, and a loop body
+  // without branches lets the compiler count outstanding loads exactly.
+  auto stage = [&](int64_t n) {
+    const int64_t t0 = n * CH;
+    float sn = 0.f;
+#pragma unroll
+    for (int j = 0; j < L::KV; ++j) {
+      const int c = 8 * (lq + 4 * j);
+      bf16x8 wb;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float k0 = __uint_as_float(kreg[j][e] << 16), k1 = __uint_as_float(kreg[j][e] & 0xFFFF0000u);
+        sn = fmaf(k0, k0, sn);
+        sn = fmaf(k1, k1, sn);
+        wb[2 * e] = static_cast<__bf16>(k0 * k0);
+        wb[2 * e + 1] = static_cast<__bf16>(k1 * k1);
+      }
+      *reinterpret_cast<u32x4*>(Kb + lt * L::LDK + c) = kreg[j];
+      *reinterpret_cast<bf16x8*>(Wb + lt * L::LDK + c) = wb;
+    }
+    sn = quad_sum(sn);
+    if (lq == 0) tn[lt] = sn;
+    if (wave == 0) {
+      const bool ok = t0 + lane < T;
+      const float lrv = HAS_R && ok ? __logf(bf16_bits_to_f32(r_r)) : 0.f;
+      const float gin = HAS_R ? wave_prefix_sum(lrv) : 0.f;
+      tbeta[lane] = bf16_bits_to_f32(beta_r);   // zero past the end
+      tgin[lane] = gin;
+      tgex[lane] = gin - lrv;
+      tR[lane] = HAS_R ? __expf(gin - lrv) : 1.f;
+      tIR[lane] = HAS_R ? __expf(-gin) : 1.f;     // used only when the chunk's sum is >= the factor bound
+    }
+    load_chunk(t0 + CH);
+  };
+  stage(0);
   __syncthreads();
 
-  int cur = 0;
+  int cur = 0;            // d_0 of the chunk being processed is dbuf[cur]
   for (int64_t n = 0; n < nch; ++n) {
     const int64_t t0 = n * CH;
     const float* d0 = dbuf + cur * DK;
+    const float gC = tgin[CH - 1];                       // the chunk's total log-retention
+    const bool fact = !HAS_R || gC >= PS_FACTOR_MIN_G;   // uniform
 
-    // ---- S1: stage k and bf16(k^2); n_t and <w_t, d_0> in fp32 ----------------
+    // ---- Gram: M on MFMA; <w_t, d_0> in fp32 --------------------------------------
     {
-      float sn = 0.f, sp = 0.f;
+      switch (wave) {
+        case 0: precond_gram<DK, HAS_R, 0>(Wb, Ms, tok, eta, fact, lr, lg); break;
+        case 1: precond_gram<DK, HAS_R, 1>(Wb, Ms, tok, eta, fact, lr, lg); break;
+        case 2: precond_gram<DK, HAS_R, 2>(Wb, Ms, tok, eta, fact, lr, lg); break;
+        default: precond_gram<DK, HAS_R, 3>(Wb, Ms, tok, eta, fact, lr, lg); break;
+      }
+      float sp = 0.f;
 #pragma unroll
       for (int j = 0; j < L::KV; ++j) {
         const int c = 8 * (lq + 4 * j);
+        const u32x4 kv = *reinterpret_cast<const u32x4*>(Kb + lt * L::LDK + c);
         const f32x4 da = *reinterpret_cast<const f32x4*>(d0 + c);
         const f32x4 db = *reinterpret_cast<const f32x4*>(d0 + c + 4);
-        float w[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float k0 = __uint_as_float(kreg[j][e] << 16), k1 = __uint_as_float(kreg[j][e] & 0xFFFF0000u);
-          w[2 * e] = k0 * k0;
-          w[2 * e + 1] = k1 * k1;
+          const float k0 = __uint_as_float(kv[e] << 16), k1 = __uint_as_float(kv[e] & 0xFFFF0000u);
+          sp = fmaf(k0 * k0, e < 2 ? da[2 * e] : db[2 * e - 4], sp);
+          sp = fmaf(k1 * k1, e < 2 ? da[2 * e + 1] : db[2 * e - 3], sp);
         }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          sn += w[e];
-          sp = fmaf(w[e], e < 4 ? da[e] : db[e - 4], sp);
-        }
-        *reinterpret_cast<u32x4*>(Kb + lt * L::LDK + c) = kreg[j];
-        bf16x8 wb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) wb[e] = static_cast<__bf16>(w[e]);
-        *reinterpret_cast<bf16x8*>(Wb + lt * L::LDK + c) = wb;
       }
-      sn = quad_sum(sn);
       sp = quad_sum(sp);
-      if (lq == 0) { tn[lt] = sn; tP[lt] = sp; }
-      if (wave == 0) {
-        const bool ok = t0 + lane < T;
-        const float lrv = HAS_R && ok ? __logf(bf16_bits_to_f32(r_r)) : 0.f;
-        const float gin = HAS_R ? wave_prefix_sum(lrv) : 0.f;
-        tbeta[lane] = bf16_bits_to_f32(beta_r);   // zero past the end
-        tgin[lane] = gin;
-        tgex[lane] = gin - lrv;
-      }
-      // Prefetch the next chunk while this one is processed.
-      if (n + 1 < nch) load_chunk(t0 + CH);
+      if (lq == 0) tP[lt] = sp;
     }
     __syncthreads();
 
-    // ---- S2: M = alf_t e^{g_t - g_{s+1}} <w_t, w_s> (s < t) on MFMA -----------
-    float bt_chain = 0.f;
-    {
-      // Ten lower-triangular 16x16 tiles (R, J), J <= R: wave w takes tiles w,
-      // w + 4 and w + 8; waves 2 and 3 have only two (their third is computed
-      // again and not stored, which keeps the code free of branches).
-      f32x4 acc[3];
-      int Rs[3], Js[3];
-#pragma unroll
-      for (int i = 0; i < 3; ++i) {
-        const int u = wave + 4 * i < 10 ? wave + 4 * i : wave + 4;
-        Rs[i] = u < 1 ? 0 : u < 3 ? 1 : u < 6 ? 2 : 3;
-        Js[i] = u - Rs[i] * (Rs[i] + 1) / 2;
-        acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-      for (int k0 = 0; k0 < DK; k0 += 32) {
-#pragma unroll
-        for (int i = 0; i < 3; ++i) {
-          const bf* arow = Wb + (16 * Rs[i] + lr) * L::LDK + 4 * lg + k0;
-          const bf* brow = Wb + (16 * Js[i] + lr) * L::LDK + 4 * lg + k0;
-          acc[i] = op::mma2(acc[i], op::ld(arow), op::ld(arow + 16), op::ld(brow), op::ld(brow + 16));
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 3; ++i) {
-        if (i < 2 || wave < 2) {
-          const int t4 = 16 * Rs[i] + 4 * lg, s = 16 * Js[i] + lr;
-          const f32x4 nn = *reinterpret_cast<const f32x4*>(tn + t4);
-          const f32x4 be = *reinterpret_cast<const f32x4*>(tbeta + t4);
-          const f32x4 gx = *reinterpret_cast<const f32x4*>(tgex + t4);
-          const float gs = tgin[s];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float alf = nn[q] > 0.f ? eta * be[q] * be[q] * __builtin_amdgcn_rcpf(nn[q]) : 0.f;
-            const float dec = HAS_R ? __expf(gx[q] - gs) : 1.f;
-            Ms[(t4 + q) * L::LM + s] = s < t4 + q ? alf * dec * acc[i][q] : 0.f;
-          }
-        }
-      }
-      if (wave == 0) {
-        const float nn = tn[lane], be = tbeta[lane];
-        const float gam = nn > 0.f ? eta * be * __builtin_amdgcn_rcpf(nn) : 0.f;   // alf_t = gam_t beta_t
-        const float Rt = HAS_R ? __expf(tgex[lane]) : 1.f;
-        bt_chain = gam - gam * be * Rt * tP[lane];
-      }
-    }
-    __syncthreads();
-
-    // ---- S3: forward substitution (I + M) e = b on one wave --------------------
+    // ---- forward substitution (I + M) e = b on one wave -----------------------------
     if (wave == 0) {
       float m[CH];
       const float* mrow = Ms + lane * L::LM;
@@ -357,39 +369,78 @@ __global__ __launch_bounds__(256) void precond_scan_chunk_kernel(PrecondParams p
         const f32x4 v = *reinterpret_cast<const f32x4*>(mrow + i);
         m[i] = v[0]; m[i + 1] = v[1]; m[i + 2] = v[2]; m[i + 3] = v[3];
       }
-      float acc = bt_chain;
+      const float nn = tn[lane], be = tbeta[lane];
+      const float gam = nn > 0.f ? eta * be * __builtin_amdgcn_rcpf(nn) : 0.f;   // alf_t = gam_t beta_t
+      float acc = gam - gam * be * tR[lane] * tP[lane];
 #pragma unroll
       for (int s = 0; s < CH; ++s) {
         const float es = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), s));
         acc = fmaf(-m[s], es, acc);
       }
-      te[lane] = acc;
-      tc[lane] = HAS_R ? __expf(tgin[CH - 1] - tgin[lane]) * acc : acc;
+      // e_t e^{-g_{t+1}} for the factored output; e_t itself otherwise
+      teh[lane] = fact && HAS_R ? acc * tIR[lane] : acc;
+      tc[lane] = HAS_R ? __expf(gC - tgin[lane]) * acc : acc;
     }
     __syncthreads();
 
-    // ---- S4: L_ts = e^{g_t - g_{s+1}} e_s (s < t) in bf16; chunk-end partials --
+    // ---- output kw_t = d_t * k_t on MFMA; chunk-end update partials -----------------
+    // D^T = W^T L^T + d_0 e^{g_t} as 16x16 tiles (rows: channels, columns: tokens):
+    // each lane ends with four consecutive channels of one token.  Wave w takes
+    // channel tiles CT*w .. CT*w + CT - 1 for all four token blocks.  Factored:
+    // D_t = e^{g_t} (d_0 + sum_{s<t} e_s e^{-g_{s+1}} w_s); otherwise each
+    // L_ts = e^{g_t - g_{s+1}} e_s is formed with its own exponential.
     {
-      const int t = tid >> 2, s0 = 16 * (tid & 3);
-      const float gt = tgex[t];
-      float gi[16], ev[16];
+      op::frag ef[4], edf[4];   // factored operands: off-diagonal and diagonal (masked) blocks
+      if (fact) {
 #pragma unroll
-      for (int i = 0; i < 16; i += 4) {
-        const f32x4 a = *reinterpret_cast<const f32x4*>(tgin + s0 + i);
-        const f32x4 e = *reinterpret_cast<const f32x4*>(te + s0 + i);
+        for (int sb = 0; sb < 4; ++sb) {
+          const f32x4 ev = *reinterpret_cast<const f32x4*>(teh + 16 * sb + 4 * lg);
+          f32x4 dm;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) { gi[i + q] = a[q]; ev[i + q] = e[q]; }
+          for (int j = 0; j < 4; ++j) dm[j] = 4 * lg + j < lr ? ev[j] : 0.f;
+          ef[sb] = op::cvt(ev);
+          edf[sb] = op::cvt(dm);
+        }
       }
-      bf16x8 lo, hi;
+      auto bfrag = [&](int TB, int sb) -> op::frag {
+        if (fact) return sb < TB ? ef[sb] : edf[sb];
+        const int t = 16 * TB + lr;
+        const float gt = tgex[t];
+        const f32x4 gi = *reinterpret_cast<const f32x4*>(tgin + 16 * sb + 4 * lg);
+        const f32x4 ev = *reinterpret_cast<const f32x4*>(teh + 16 * sb + 4 * lg);
+        f32x4 x;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float v = (HAS_R ? __expf(gt - gi[i]) : 1.f) * ev[i];
-        const float x = s0 + i < t ? v : 0.f;
-        if (i < 8) lo[i] = static_cast<__bf16>(x); else hi[i - 8] = static_cast<__bf16>(x);
+        for (int j = 0; j < 4; ++j)
+          x[j] = (16 * sb + 4 * lg + j < t ? 1.f : 0.f) * __expf(fminf(gt - gi[j], 0.f)) * ev[j];
+        return op::cvt(x);
+      };
+      const uint32_t so = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(t0 * H * DK * 2));
+#pragma unroll
+      for (int ci = 0; ci < L::CT; ++ci) {
+        const int c0 = 16 * (L::CT * wave + ci);
+        op::frag af[4];
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb) af[sb] = op::ld_tr(Wb, L::LDK, 16 * sb, c0, lr, lg);
+        const f32x4 dv = *reinterpret_cast<const f32x4*>(d0 + c0 + 4 * lg);
+#pragma unroll
+        for (int TB = 0; TB < 4; ++TB) {
+          const int t = 16 * TB + lr;
+          const float Rt = tR[t];
+          const float pre = fact ? 1.f : Rt, post = fact ? Rt : 1.f;
+          f32x4 acc = {pre * dv[0], pre * dv[1], pre * dv[2], pre * dv[3]};
+#pragma unroll
+          for (int sb = 0; sb + 1 <= TB; sb += 2)
+            acc = op::mma2(acc, af[sb], af[sb + 1], bfrag(TB, sb), bfrag(TB, sb + 1));
+          if ((TB & 1) == 0) acc = op::mma1(acc, af[TB], bfrag(TB, TB));
+          const f32x4 kv = op::f32(op::ld(Kb + t * L::LDK + c0 + 4 * lg));
+          const f32x4 o = {post * acc[0] * kv[0], post * acc[1] * kv[1], post * acc[2] * kv[2],
+                           post * acc[3] * kv[3]};
+          const uint32_t voff = static_cast<uint32_t>((t * H + h) * DK + c0 + 4 * lg) * 2;
+          buf_store8(__builtin_bit_cast(u32x2, to_bf16x4(o)), kwr, voff, so);
+        }
       }
-      *reinterpret_cast<bf16x8*>(Lb + t * L::LL + s0) = lo;
-      *reinterpret_cast<bf16x8*>(Lb + t * L::LL + s0 + 8) = hi;
 
+      // partial sums of c_s w_s over token groups, for the chunk-end preconditioner
       const int cp = tid % L::NP, qd = tid / L::NP;
       float cs[L::TPQ];
       uint32_t ku[L::TPQ];
@@ -411,27 +462,19 @@ __global__ __launch_bounds__(256) void precond_scan_chunk_kernel(PrecondParams p
       }
       *reinterpret_cast<float2*>(part + qd * DK + 2 * cp) = make_float2(a0, a1);
     }
+    const float RC = HAS_R ? __expf(gC) : 1.f;
     __syncthreads();
 
-    // ---- S5: kw_t = (e^{g_t} d_0 + sum_s L_ts w_s) * k_t on MFMA; d_64 -------------
-    {
-      const uint32_t so = static_cast<uint32_t>(t0 * H * DK * 2);
-      switch (wave) {
-        case 0: precond_out_block<DK, HAS_R, 0>(Wb, Lb, Kb, d0, tgex, kwr, so, H, h, lr, lg); break;
-        case 1: precond_out_block<DK, HAS_R, 1>(Wb, Lb, Kb, d0, tgex, kwr, so, H, h, lr, lg); break;
-        case 2: precond_out_block<DK, HAS_R, 2>(Wb, Lb, Kb, d0, tgex, kwr, so, H, h, lr, lg); break;
-        default: precond_out_block<DK, HAS_R, 3>(Wb, Lb, Kb, d0, tgex, kwr, so, H, h, lr, lg); break;
-      }
-      if (tid < DK) {
-        const float RC = HAS_R ? __expf(tgin[CH - 1]) : 1.f;
-        float s = RC * d0[tid];
+    // ---- chunk-end preconditioner d_64 = e^{g_64} d_0 + sum_s c_s w_s; next stage ----
+    if (tid < DK) {
+      float s = RC * d0[tid];
 #pragma unroll
-        for (int q = 0; q < L::NQ; ++q) s += part[q * DK + tid];
-        dbuf[(cur ^ 1) * DK + tid] = s;
-      }
+      for (int q = 0; q < L::NQ; ++q) s += part[q * DK + tid];
+      dbuf[(cur ^ 1) * DK + tid] = s;
     }
-    __syncthreads();
     cur ^= 1;
+    stage(n + 1);   // past the last chunk: zeros, never read
+    __syncthreads();
   }
   if (p.d_T && tid < DK) p.d_T[bh * DK + tid] = dbuf[cur * DK + tid];
 }

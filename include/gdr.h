@@ -266,7 +266,8 @@ gdr_status gdr_recurrent_step_wkey(const gdr_desc* desc, const void* q, const vo
  *   d_T   [B, H, d_k] fp32 preconditioner after the last token, or NULL to skip
  *         it; may be the same pointer as d0 (updated in place)
  * kw and d_T overlap no other argument (except d_T == d0).  T == 0 writes
- * d_T = d0 (or ones).  bf16 runs the chunkwise form (bf16 products with fp32
+ * d_T = d0 (or ones).  (T + 128) * H * d_k * elem_size may not exceed 2^31 - 1
+ * bytes (GDR_ERR_UNSUPPORTED): offsets within one sequence are 32-bit.  bf16 runs the chunkwise form (bf16 products with fp32
  * accumulation for the key Gram matrix and the per-token preconditioners; the
  * preconditioner carried between chunks in fp32); fp32 runs token by token in fp32.
  */

@@ -149,3 +149,15 @@ def test_full_size_scan_sampled():
                                     s["r"][None, :, None], s["d0"][None, None])
         check(f"kw[b={b},h={h}]", host(kw[b, :, h]), kw_ref[0, :, 0], TOL["bf16"])
         check(f"d_T[b={b},h={h}]", host(dT[b, h]), d_ref[0, 0], TOL["bf16"])
+
+
+def test_scan_strong_forgetting_within_a_chunk():
+    """Twenty tokens of retention 1e-3 inside one chunk (a total log-retention
+    near -140, below which the chunkwise kernel forms every decay factor with its
+    own exponential instead of factoring it)."""
+    need_gpu()
+    inp = _inputs(2, 200, 2, 128, seed=19)
+    inp["r"][:, 70:90] = np.float32(0.00099945068359375)    # bf16-exact
+    inp["r"][1, 140:150] = np.float32(0.00099945068359375)
+    _run(inp, "bf16")
+    _run(inp, "f32")

@@ -43,7 +43,7 @@ import numpy as np
 __all__ = [
     "Workload", "CONFIGS", "DECODE_CONFIG", "round_to_io", "bf16_round",
     "slice_inputs", "chunk_inputs", "decode_slice", "decode_inputs", "PRECOND_ETA",
-    "precond_slice", "precond_inputs",
+    "precond_slice", "precond_inputs", "precond_factors",
 ]
 
 
@@ -244,16 +244,33 @@ def decode_inputs(wl: DecodeWorkload, steps: Optional[int] = None) -> dict:
 PRECOND_ETA = 1.0
 
 
+def _precond_factor_slice(wl: Workload, b: int, h: int, T: int):
+    rr = np.random.Generator(np.random.PCG64(np.random.SeedSequence([wl.seed, b, h, 2])))
+    r = round_to_io(_sigmoid(rr.standard_normal(T) + 3.0), wl.io)
+    rd = np.random.Generator(np.random.PCG64(np.random.SeedSequence([wl.seed, b, h, 3])))
+    d0 = rd.uniform(0.5, 1.5, wl.d_k).astype(np.float32)
+    return r, d0
+
+
 def precond_slice(wl: Workload, b: int, h: int, T: Optional[int] = None) -> dict:
     """Preconditioner-scan inputs of one (b, h) slice: k [T, d_k]; beta [T];
     r [T] (retention); d0 [d_k] float32."""
     T = wl.T if T is None else T
     s = slice_inputs(wl, b, h, T)
-    rr = np.random.Generator(np.random.PCG64(np.random.SeedSequence([wl.seed, b, h, 2])))
-    r = round_to_io(_sigmoid(rr.standard_normal(T) + 3.0), wl.io)
-    rd = np.random.Generator(np.random.PCG64(np.random.SeedSequence([wl.seed, b, h, 3])))
-    d0 = rd.uniform(0.5, 1.5, wl.d_k).astype(np.float32)
+    r, d0 = _precond_factor_slice(wl, b, h, T)
     return dict(k=s["k"], beta=s["beta"], r=r, d0=d0)
+
+
+def precond_factors(wl: Workload, T: Optional[int] = None) -> dict:
+    """The scan's own inputs for all slices (the keys and beta being those of
+    chunk_inputs): r [B, T, H]; d0 [B, H, d_k] float32."""
+    T = wl.T if T is None else T
+    r = np.empty((wl.B, T, wl.H), np.float32)
+    d0 = np.empty((wl.B, wl.H, wl.d_k), np.float32)
+    for b in range(wl.B):
+        for h in range(wl.H):
+            r[b, :, h], d0[b, h] = _precond_factor_slice(wl, b, h, T)
+    return dict(r=r, d0=d0)
 
 
 def precond_inputs(wl: Workload, T: Optional[int] = None) -> dict:
