@@ -177,9 +177,9 @@ template <> struct PsGram<2> { static constexpr int N = 2, NEED = 0xB; static co
 template <> struct PsGram<3> { static constexpr int N = 2, NEED = 0xC; static constexpr int R[3] = {3, 3, 0}, J[3] = {2, 3, 0}; };
 
 // M_ts = alf_t e^{g_t - g_{s+1}} <w_t, w_s> for s < t (0 elsewhere) into Ms.
-template <int DK, bool HAS_R, int W>
-__device__ __forceinline__ void precond_gram(const __bf16* Wb, float* Ms, const float* tok, float eta, bool fact,
-                                             int lr, int lg) {
+template <int DK, bool HAS_R, int W, bool FACT, typename Side>
+__device__ __forceinline__ void precond_gram(const __bf16* Wb, float* Ms, const float* tok, float eta, int lr,
+                                             int lg, Side side) {
   typedef PsLayout<DK> L;
   typedef Op<IO_BF16> op;
   typedef PsGram<W> G;
@@ -200,6 +200,7 @@ __device__ __forceinline__ void precond_gram(const __bf16* Wb, float* Ms, const 
     for (int i = 0; i < G::N; ++i)
       acc[i] = op::mma2(acc[i], lo[G::R[i]], hi[G::R[i]], lo[G::J[i]], hi[G::J[i]]);
   }
+  side();   // independent fp32 work, overlapping the products in flight
   const float* tn = tok + L::TR_N * CH;
   const float* tbeta = tok + L::TR_BETA * CH;
 #pragma unroll
@@ -215,8 +216,72 @@ __device__ __forceinline__ void precond_gram(const __bf16* Wb, float* Ms, const 
       // A zero key has a zero Gram row, so a clamped n_t is enough.
       const float alf = eta * be[q] * be[q] * __builtin_amdgcn_rcpf(fmaxf(nn[q], 1e-30f));
       float dec = 1.f;
-      if (HAS_R) dec = fact ? rt[q] * irs : __expf(fminf(gx[q] - gs, 0.f));
+      if (HAS_R) dec = FACT ? rt[q] * irs : __expf(fminf(gx[q] - gs, 0.f));
       Ms[(t4 + q) * L::LM + s] = (s < t4 + q ? 1.f : 0.f) * alf * dec * acc[i][q];
+    }
+  }
+}
+
+// Output of one wave: kw_t = d_t * k_t for channel tiles CT*w .. CT*w + CT - 1 and
+// all four 16-token blocks.  D^T = W^T L^T + d_0 e^{g_t} is formed as 16x16 tiles
+// (rows: channels, columns: tokens), so each lane ends with four consecutive
+// channels of one token.  FACT: D_t = e^{g_t} (d_0 + sum_{s<t} e_s e^{-g_{s+1}} w_s)
+// (teh holds e_s e^{-g_{s+1}}); otherwise each L_ts = e^{g_t - g_{s+1}} e_s is formed
+// with its own exponential (teh holds e_s).
+template <int DK, bool FACT, typename Side>
+__device__ __forceinline__ void precond_output(const __bf16* Wb, const __bf16* Kb, const float* d0, const float* tok,
+                                               rsrc_t kwr, uint32_t so, int64_t H, int64_t h, int wave, int lr,
+                                               int lg, Side side) {
+  typedef PsLayout<DK> L;
+  typedef Op<IO_BF16> op;
+  const float* teh = tok + L::TR_EH * CH;
+  const float* tR = tok + L::TR_R * CH;
+  op::frag ef[4], edf[4];   // factored operands: off-diagonal and diagonal (masked) blocks
+  if (FACT) {
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) {
+      const f32x4 ev = *reinterpret_cast<const f32x4*>(teh + 16 * sb + 4 * lg);
+      f32x4 dm;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dm[j] = 4 * lg + j < lr ? ev[j] : 0.f;
+      ef[sb] = op::cvt(ev);
+      edf[sb] = op::cvt(dm);
+    }
+  }
+  auto bfrag = [&](int TB, int sb) -> op::frag {
+    if (FACT) return sb < TB ? ef[sb] : edf[sb];
+    const int t = 16 * TB + lr;
+    const float gt = tok[L::TR_GEX * CH + t];
+    const f32x4 gi = *reinterpret_cast<const f32x4*>(tok + L::TR_GIN * CH + 16 * sb + 4 * lg);
+    const f32x4 ev = *reinterpret_cast<const f32x4*>(teh + 16 * sb + 4 * lg);
+    f32x4 x;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      x[j] = (16 * sb + 4 * lg + j < t ? 1.f : 0.f) * __expf(fminf(gt - gi[j], 0.f)) * ev[j];
+    return op::cvt(x);
+  };
+  side();   // independent fp32 work, scheduled among the products below
+#pragma unroll
+  for (int ci = 0; ci < L::CT; ++ci) {
+    const int c0 = 16 * (L::CT * wave + ci);
+    op::frag af[4];
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) af[sb] = op::ld_tr(Wb, L::LDK, 16 * sb, c0, lr, lg);
+    const f32x4 dv = *reinterpret_cast<const f32x4*>(d0 + c0 + 4 * lg);
+#pragma unroll
+    for (int TB = 0; TB < 4; ++TB) {
+      const int t = 16 * TB + lr;
+      const float Rt = tR[t];
+      const float pre = FACT ? 1.f : Rt, post = FACT ? Rt : 1.f;
+      f32x4 acc = {pre * dv[0], pre * dv[1], pre * dv[2], pre * dv[3]};
+#pragma unroll
+      for (int sb = 0; sb + 1 <= TB; sb += 2)
+        acc = op::mma2(acc, af[sb], af[sb + 1], bfrag(TB, sb), bfrag(TB, sb + 1));
+      if ((TB & 1) == 0) acc = op::mma1(acc, af[TB], bfrag(TB, TB));
+      const f32x4 kv = op::f32(op::ld(Kb + t * L::LDK + c0 + 4 * lg));
+      const f32x4 o = {post * acc[0] * kv[0], post * acc[1] * kv[1], post * acc[2] * kv[2], post * acc[3] * kv[3]};
+      const uint32_t voff = static_cast<uint32_t>((t * H + h) * DK + c0 + 4 * lg) * 2;
+      buf_store8(__builtin_bit_cast(u32x2, to_bf16x4(o)), kwr, voff, so);
     }
   }
 }
@@ -330,29 +395,43 @@ __global__ __launch_bounds__(256) void precond_scan_chunk_kernel(PrecondParams p
   for (int64_t n = 0; n < nch; ++n) {
     const int64_t t0 = n * CH;
     const float* d0 = dbuf + cur * DK;
-    const float gC = tgin[CH - 1];                       // the chunk's total log-retention
-    const bool fact = !HAS_R || gC >= PS_FACTOR_MIN_G;   // uniform
+    const float gC = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(tgin[CH - 1])));
+    const bool fact = !HAS_R || gC >= PS_FACTOR_MIN_G;   // the chunk's total log-retention decides
 
     // ---- Gram: M on MFMA; <w_t, d_0> in fp32 --------------------------------------
     {
-      switch (wave) {
-        case 0: precond_gram<DK, HAS_R, 0>(Wb, Ms, tok, eta, fact, lr, lg); break;
-        case 1: precond_gram<DK, HAS_R, 1>(Wb, Ms, tok, eta, fact, lr, lg); break;
-        case 2: precond_gram<DK, HAS_R, 2>(Wb, Ms, tok, eta, fact, lr, lg); break;
-        default: precond_gram<DK, HAS_R, 3>(Wb, Ms, tok, eta, fact, lr, lg); break;
-      }
+      // <w_t, d_0> in fp32: thread (token lt, quarter lq) over its 32 channels
       float sp = 0.f;
+      auto pdot = [&]() {
 #pragma unroll
-      for (int j = 0; j < L::KV; ++j) {
-        const int c = 8 * (lq + 4 * j);
-        const u32x4 kv = *reinterpret_cast<const u32x4*>(Kb + lt * L::LDK + c);
-        const f32x4 da = *reinterpret_cast<const f32x4*>(d0 + c);
-        const f32x4 db = *reinterpret_cast<const f32x4*>(d0 + c + 4);
+        for (int j = 0; j < L::KV; ++j) {
+          const int c = 8 * (lq + 4 * j);
+          const u32x4 kv = *reinterpret_cast<const u32x4*>(Kb + lt * L::LDK + c);
+          const f32x4 da = *reinterpret_cast<const f32x4*>(d0 + c);
+          const f32x4 db = *reinterpret_cast<const f32x4*>(d0 + c + 4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float k0 = __uint_as_float(kv[e] << 16), k1 = __uint_as_float(kv[e] & 0xFFFF0000u);
-          sp = fmaf(k0 * k0, e < 2 ? da[2 * e] : db[2 * e - 4], sp);
-          sp = fmaf(k1 * k1, e < 2 ? da[2 * e + 1] : db[2 * e - 3], sp);
+          for (int e = 0; e < 4; ++e) {
+            const float k0 = __uint_as_float(kv[e] << 16), k1 = __uint_as_float(kv[e] & 0xFFFF0000u);
+            sp = fmaf(k0 * k0, e < 2 ? da[2 * e] : db[2 * e - 4], sp);
+            sp = fmaf(k1 * k1, e < 2 ? da[2 * e + 1] : db[2 * e - 3], sp);
+          }
+        }
+      };
+      // (the factored and per-element forms are separate code paths under one
+      // uniform branch, so neither computes the other's exponentials)
+      if (fact) {
+        switch (wave) {
+          case 0: precond_gram<DK, HAS_R, 0, true>(Wb, Ms, tok, eta, lr, lg, pdot); break;
+          case 1: precond_gram<DK, HAS_R, 1, true>(Wb, Ms, tok, eta, lr, lg, pdot); break;
+          case 2: precond_gram<DK, HAS_R, 2, true>(Wb, Ms, tok, eta, lr, lg, pdot); break;
+          default: precond_gram<DK, HAS_R, 3, true>(Wb, Ms, tok, eta, lr, lg, pdot); break;
+        }
+      } else {
+        switch (wave) {
+          case 0: precond_gram<DK, HAS_R, 0, false>(Wb, Ms, tok, eta, lr, lg, pdot); break;
+          case 1: precond_gram<DK, HAS_R, 1, false>(Wb, Ms, tok, eta, lr, lg, pdot); break;
+          case 2: precond_gram<DK, HAS_R, 2, false>(Wb, Ms, tok, eta, lr, lg, pdot); break;
+          default: precond_gram<DK, HAS_R, 3, false>(Wb, Ms, tok, eta, lr, lg, pdot); break;
         }
       }
       sp = quad_sum(sp);
@@ -390,76 +469,31 @@ __global__ __launch_bounds__(256) void precond_scan_chunk_kernel(PrecondParams p
     // D_t = e^{g_t} (d_0 + sum_{s<t} e_s e^{-g_{s+1}} w_s); otherwise each
     // L_ts = e^{g_t - g_{s+1}} e_s is formed with its own exponential.
     {
-      op::frag ef[4], edf[4];   // factored operands: off-diagonal and diagonal (masked) blocks
-      if (fact) {
-#pragma unroll
-        for (int sb = 0; sb < 4; ++sb) {
-          const f32x4 ev = *reinterpret_cast<const f32x4*>(teh + 16 * sb + 4 * lg);
-          f32x4 dm;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) dm[j] = 4 * lg + j < lr ? ev[j] : 0.f;
-          ef[sb] = op::cvt(ev);
-          edf[sb] = op::cvt(dm);
-        }
-      }
-      auto bfrag = [&](int TB, int sb) -> op::frag {
-        if (fact) return sb < TB ? ef[sb] : edf[sb];
-        const int t = 16 * TB + lr;
-        const float gt = tgex[t];
-        const f32x4 gi = *reinterpret_cast<const f32x4*>(tgin + 16 * sb + 4 * lg);
-        const f32x4 ev = *reinterpret_cast<const f32x4*>(teh + 16 * sb + 4 * lg);
-        f32x4 x;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          x[j] = (16 * sb + 4 * lg + j < t ? 1.f : 0.f) * __expf(fminf(gt - gi[j], 0.f)) * ev[j];
-        return op::cvt(x);
-      };
-      const uint32_t so = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(t0 * H * DK * 2));
-#pragma unroll
-      for (int ci = 0; ci < L::CT; ++ci) {
-        const int c0 = 16 * (L::CT * wave + ci);
-        op::frag af[4];
-#pragma unroll
-        for (int sb = 0; sb < 4; ++sb) af[sb] = op::ld_tr(Wb, L::LDK, 16 * sb, c0, lr, lg);
-        const f32x4 dv = *reinterpret_cast<const f32x4*>(d0 + c0 + 4 * lg);
-#pragma unroll
-        for (int TB = 0; TB < 4; ++TB) {
-          const int t = 16 * TB + lr;
-          const float Rt = tR[t];
-          const float pre = fact ? 1.f : Rt, post = fact ? Rt : 1.f;
-          f32x4 acc = {pre * dv[0], pre * dv[1], pre * dv[2], pre * dv[3]};
-#pragma unroll
-          for (int sb = 0; sb + 1 <= TB; sb += 2)
-            acc = op::mma2(acc, af[sb], af[sb + 1], bfrag(TB, sb), bfrag(TB, sb + 1));
-          if ((TB & 1) == 0) acc = op::mma1(acc, af[TB], bfrag(TB, TB));
-          const f32x4 kv = op::f32(op::ld(Kb + t * L::LDK + c0 + 4 * lg));
-          const f32x4 o = {post * acc[0] * kv[0], post * acc[1] * kv[1], post * acc[2] * kv[2],
-                           post * acc[3] * kv[3]};
-          const uint32_t voff = static_cast<uint32_t>((t * H + h) * DK + c0 + 4 * lg) * 2;
-          buf_store8(__builtin_bit_cast(u32x2, to_bf16x4(o)), kwr, voff, so);
-        }
-      }
-
       // partial sums of c_s w_s over token groups, for the chunk-end preconditioner
       const int cp = tid % L::NP, qd = tid / L::NP;
-      float cs[L::TPQ];
-      uint32_t ku[L::TPQ];
-#pragma unroll
-      for (int i = 0; i < L::TPQ; i += 4) {
-        const f32x4 c = *reinterpret_cast<const f32x4*>(tc + qd * L::TPQ + i);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) cs[i + q] = c[q];
-      }
-#pragma unroll
-      for (int i = 0; i < L::TPQ; ++i)
-        ku[i] = *reinterpret_cast<const uint32_t*>(Kb + (qd * L::TPQ + i) * L::LDK + 2 * cp);
       float a0 = 0.f, a1 = 0.f;
+      auto partials = [&]() {
+        float cs[L::TPQ];
+        uint32_t ku[L::TPQ];
 #pragma unroll
-      for (int i = 0; i < L::TPQ; ++i) {
-        const float k0 = __uint_as_float(ku[i] << 16), k1 = __uint_as_float(ku[i] & 0xFFFF0000u);
-        a0 = fmaf(cs[i], k0 * k0, a0);
-        a1 = fmaf(cs[i], k1 * k1, a1);
-      }
+        for (int i = 0; i < L::TPQ; i += 4) {
+          const f32x4 c = *reinterpret_cast<const f32x4*>(tc + qd * L::TPQ + i);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) cs[i + q] = c[q];
+        }
+#pragma unroll
+        for (int i = 0; i < L::TPQ; ++i)
+          ku[i] = *reinterpret_cast<const uint32_t*>(Kb + (qd * L::TPQ + i) * L::LDK + 2 * cp);
+#pragma unroll
+        for (int i = 0; i < L::TPQ; ++i) {
+          const float k0 = __uint_as_float(ku[i] << 16), k1 = __uint_as_float(ku[i] & 0xFFFF0000u);
+          a0 = fmaf(cs[i], k0 * k0, a0);
+          a1 = fmaf(cs[i], k1 * k1, a1);
+        }
+      };
+      const uint32_t so = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(t0 * H * DK * 2));
+      if (fact) precond_output<DK, true>(Wb, Kb, d0, tok, kwr, so, H, h, wave, lr, lg, partials);
+      else precond_output<DK, false>(Wb, Kb, d0, tok, kwr, so, H, h, wave, lr, lg, partials);
       *reinterpret_cast<float2*>(part + qd * DK + 2 * cp) = make_float2(a0, a1);
     }
     const float RC = HAS_R ? __expf(gC) : 1.f;
