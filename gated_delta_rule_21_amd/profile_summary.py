@@ -48,6 +48,14 @@ def decode_source_digest() -> str:
     return h.hexdigest()[:16]
 
 
+def precond_source_digest() -> str:
+    h = hashlib.sha256()
+    for n in ("precond_scan.hip", "chunk_common.h", "device_common.h"):
+        with open(os.path.join(ROOT, "gated_delta_rule_21_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
 def stats(path: str, command: str, top: int) -> str:
     rows = list(csv.DictReader(open(path)))
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
@@ -128,7 +136,8 @@ def main(argv=None):
     if args.cmd == "stats":
         sys.stdout.write(stats(args.csv, args.command, args.top))
     else:
-        digest = decode_source_digest() if "decode" in args.kernel else kernel_source_digest()
+        digest = (decode_source_digest() if "decode" in args.kernel else
+                  precond_source_digest() if "precond" in args.kernel else kernel_source_digest())
         sys.stdout.write(counters(args.fetch_csv, args.write_csv, args.kernel, args.algorithmic_bytes,
                                   args.command, digest))
 
