@@ -140,27 +140,43 @@ __global__ __launch_bounds__(64) void precond_scan_seq_kernel(PrecondParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 I/O: chunkwise, one workgroup (4 waves) per (sequence, head).
+// bf16 I/O: chunkwise and software-pipelined, one 512-thread workgroup (8 waves)
+// per (sequence, head).  Iteration n of the chunk loop runs, between barriers:
+//   1. wave 0: forward substitution of chunk n (the dependent chain);
+//      waves 1-4: output k~ of chunk n-1;  waves 5-6: Gram matrix M of chunk
+//      n+1;  wave 7: stage chunk n+2 into LDS and prefetch chunk n+3;
+//   2. all: partial sums of the chunk-end update of chunk n;
+//   3. d_0 of chunk n+1;
+//   4. all: <w_t, d_0> of chunk n+1.
+// Only steps 1 (the substitution), 2, 3 and 4 are on the chain; the output,
+// the Gram matrix and the staging of neighbouring chunks run beside it.  Key
+// tiles are kept for four chunks (n-1 .. n+2) and w = k^2 is formed from them
+// as operands are loaded.
 // ---------------------------------------------------------------------------
 template <int DK>
 struct PsLayout {
-  static constexpr int LDK = DK + 8;    // bf16 row stride of the key and w tiles
-  static constexpr int LM = CH + 4;     // fp32 row stride of M
-  static constexpr int NP = DK / 2;     // channel pairs in the chunk-end update
-  static constexpr int NQ = 256 / NP;   // token groups in the chunk-end update
-  static constexpr int TPQ = CH / NQ;   // tokens per group
-  static constexpr int KV = DK / 32;    // 16-byte key loads per thread
-  static constexpr int CT = DK / 64;    // 16-channel output tiles per wave
+  static constexpr int NW = 8, NT = 64 * NW;   // waves, threads
+  static constexpr int LDK = DK + 8;           // bf16 row stride of the key tiles
+  static constexpr int LM = CH + 4;            // fp32 row stride of M
+  static constexpr int NKB = 4;                // key tiles of chunks n-1 .. n+2
+  static constexpr int NP = DK / 2;            // channel pairs in the chunk-end update
+  static constexpr int NQ = NT / NP;           // token groups in the chunk-end update
+  static constexpr int TPQ = CH / NQ;          // tokens per group
+  static constexpr int KV = DK / 32;           // 16-byte key pieces per loader lane and round
+  static constexpr int CT = DK / 64;           // 16-channel output tiles per output wave
+  static constexpr int PCH = DK / 8;           // channels per thread in <w_t, d_0>
+  static constexpr size_t KB_BYTES = size_t(CH) * LDK * 2;
+  static constexpr size_t M_BYTES = size_t(CH) * LM * 4;
   static constexpr size_t K_OFF = 0;
-  static constexpr size_t W_OFF = K_OFF + size_t(CH) * LDK * 2;
-  static constexpr size_t M_OFF = W_OFF + size_t(CH) * LDK * 2;
-  static constexpr size_t D_OFF = M_OFF + size_t(CH) * LM * 4;    // d, two buffers
-  static constexpr size_t Q_OFF = D_OFF + size_t(2) * DK * 4;     // update partials [NQ][DK]
-  static constexpr size_t T_OFF = Q_OFF + size_t(NQ) * DK * 4;    // per-token rows
+  static constexpr size_t M_OFF = K_OFF + NKB * KB_BYTES;
+  static constexpr size_t D_OFF = M_OFF + 2 * M_BYTES;          // d_0, two chunks
+  static constexpr size_t Q_OFF = D_OFF + size_t(2) * DK * 4;   // update partials [NQ][DK]
+  static constexpr size_t T_OFF = Q_OFF + size_t(NQ) * DK * 4;  // per-token rows, four chunks
   // n_t, <w_t, d_0>, beta_t, g_t, g_{t+1}, e^{g_t}, e^{-g_{t+1}}, e_t (scaled), c_t
   static constexpr int TR_N = 0, TR_P = 1, TR_BETA = 2, TR_GEX = 3, TR_GIN = 4, TR_R = 5, TR_IR = 6, TR_EH = 7,
                        TR_C = 8, TR_ROWS = 9;
-  static constexpr size_t BYTES = T_OFF + size_t(TR_ROWS) * CH * 4;
+  static constexpr size_t TOK_FLOATS = size_t(TR_ROWS) * CH;
+  static constexpr size_t BYTES = T_OFF + NKB * TOK_FLOATS * 4;
 };
 
 // The factored form of the decays (e^{g_t - g_{s+1}} = e^{g_t} e^{-g_{s+1}}) is
@@ -168,18 +184,27 @@ struct PsLayout {
 // stay within fp32 range.  Below it, each entry takes its own exponential.
 constexpr float PS_FACTOR_MIN_G = -80.f;
 
-// Gram tiles of one wave: (R, J) blocks of W W^T, J <= R, as (row, col) lists.
-// Every wave loads only the 16-token row blocks its tiles use.
+// bf16 squares of four bf16 keys (w = k^2 as an MFMA operand).
+__device__ __forceinline__ bf16x4 ps_sq(bf16x4 k) {
+  const f32x4 x = Op<IO_BF16>::f32(k);
+  return to_bf16x4(f32x4{x[0] * x[0], x[1] * x[1], x[2] * x[2], x[3] * x[3]});
+}
+
+// Gram tiles of the two Gram waves: (R, J) blocks of W W^T, J <= R.
 template <int W> struct PsGram;
-template <> struct PsGram<0> { static constexpr int N = 3, NEED = 0x3; static constexpr int R[3] = {0, 1, 1}, J[3] = {0, 0, 1}; };
-template <> struct PsGram<1> { static constexpr int N = 3, NEED = 0x7; static constexpr int R[3] = {2, 2, 2}, J[3] = {0, 1, 2}; };
-template <> struct PsGram<2> { static constexpr int N = 2, NEED = 0xB; static constexpr int R[3] = {3, 3, 0}, J[3] = {0, 1, 0}; };
-template <> struct PsGram<3> { static constexpr int N = 2, NEED = 0xC; static constexpr int R[3] = {3, 3, 0}, J[3] = {2, 3, 0}; };
+template <> struct PsGram<0> {
+  static constexpr int N = 5, NEED = 0x7;
+  static constexpr int R[5] = {0, 1, 1, 2, 2}, J[5] = {0, 0, 1, 0, 1};
+};
+template <> struct PsGram<1> {
+  static constexpr int N = 5, NEED = 0xF;
+  static constexpr int R[5] = {2, 3, 3, 3, 3}, J[5] = {2, 0, 1, 2, 3};
+};
 
 // M_ts = alf_t e^{g_t - g_{s+1}} <w_t, w_s> for s < t (0 elsewhere) into Ms.
-template <int DK, bool HAS_R, int W, bool FACT, typename Side>
-__device__ __forceinline__ void precond_gram(const __bf16* Wb, float* Ms, const float* tok, float eta, int lr,
-                                             int lg, Side side) {
+template <int DK, bool HAS_R, int W, bool FACT>
+__device__ __forceinline__ void precond_gram(const __bf16* Kb, float* Ms, const float* tok, float eta, int lr,
+                                             int lg) {
   typedef PsLayout<DK> L;
   typedef Op<IO_BF16> op;
   typedef PsGram<W> G;
@@ -192,22 +217,19 @@ __device__ __forceinline__ void precond_gram(const __bf16* Wb, float* Ms, const 
 #pragma unroll
     for (int R = 0; R < 4; ++R)
       if (G::NEED & (1 << R)) {
-        const __bf16* row = Wb + (16 * R + lr) * L::LDK + k0 + 4 * lg;
-        lo[R] = op::ld(row);
-        hi[R] = op::ld(row + 16);
+        const __bf16* row = Kb + (16 * R + lr) * L::LDK + k0 + 4 * lg;
+        lo[R] = ps_sq(op::ld(row));
+        hi[R] = ps_sq(op::ld(row + 16));
       }
 #pragma unroll
     for (int i = 0; i < G::N; ++i)
       acc[i] = op::mma2(acc[i], lo[G::R[i]], hi[G::R[i]], lo[G::J[i]], hi[G::J[i]]);
   }
-  side();   // independent fp32 work, overlapping the products in flight
-  const float* tn = tok + L::TR_N * CH;
-  const float* tbeta = tok + L::TR_BETA * CH;
 #pragma unroll
   for (int i = 0; i < G::N; ++i) {
     const int t4 = 16 * G::R[i] + 4 * lg, s = 16 * G::J[i] + lr;
-    const f32x4 nn = *reinterpret_cast<const f32x4*>(tn + t4);
-    const f32x4 be = *reinterpret_cast<const f32x4*>(tbeta + t4);
+    const f32x4 nn = *reinterpret_cast<const f32x4*>(tok + L::TR_N * CH + t4);
+    const f32x4 be = *reinterpret_cast<const f32x4*>(tok + L::TR_BETA * CH + t4);
     const f32x4 rt = *reinterpret_cast<const f32x4*>(tok + L::TR_R * CH + t4);
     const f32x4 gx = *reinterpret_cast<const f32x4*>(tok + L::TR_GEX * CH + t4);
     const float irs = tok[L::TR_IR * CH + s], gs = tok[L::TR_GIN * CH + s];
@@ -222,16 +244,15 @@ __device__ __forceinline__ void precond_gram(const __bf16* Wb, float* Ms, const 
   }
 }
 
-// Output of one wave: kw_t = d_t * k_t for channel tiles CT*w .. CT*w + CT - 1 and
-// all four 16-token blocks.  D^T = W^T L^T + d_0 e^{g_t} is formed as 16x16 tiles
-// (rows: channels, columns: tokens), so each lane ends with four consecutive
-// channels of one token.  FACT: D_t = e^{g_t} (d_0 + sum_{s<t} e_s e^{-g_{s+1}} w_s)
-// (teh holds e_s e^{-g_{s+1}}); otherwise each L_ts = e^{g_t - g_{s+1}} e_s is formed
-// with its own exponential (teh holds e_s).
-template <int DK, bool FACT, typename Side>
-__device__ __forceinline__ void precond_output(const __bf16* Wb, const __bf16* Kb, const float* d0, const float* tok,
-                                               rsrc_t kwr, uint32_t so, int64_t H, int64_t h, int wave, int lr,
-                                               int lg, Side side) {
+// Output of one output wave (ow = 0..3): k~_t = d_t * k_t for channel tiles
+// CT*ow .. CT*ow + CT - 1 and all four 16-token blocks.  D^T = W^T L^T + d_0 e^{g_t}
+// is formed as 16x16 tiles (rows: channels, columns: tokens), so each lane ends
+// with four consecutive channels of one token.  FACT: D_t = e^{g_t} (d_0 +
+// sum_{s<t} e_s e^{-g_{s+1}} w_s) (the EH row holds e_s e^{-g_{s+1}}); otherwise each
+// L_ts = e^{g_t - g_{s+1}} e_s is formed with its own exponential (EH holds e_s).
+template <int DK, bool FACT>
+__device__ __forceinline__ void precond_output(const __bf16* Kb, const float* d0, const float* tok, rsrc_t kwr,
+                                               uint32_t so, int64_t H, int64_t h, int ow, int lr, int lg) {
   typedef PsLayout<DK> L;
   typedef Op<IO_BF16> op;
   const float* teh = tok + L::TR_EH * CH;
@@ -260,13 +281,12 @@ __device__ __forceinline__ void precond_output(const __bf16* Wb, const __bf16* K
       x[j] = (16 * sb + 4 * lg + j < t ? 1.f : 0.f) * __expf(fminf(gt - gi[j], 0.f)) * ev[j];
     return op::cvt(x);
   };
-  side();   // independent fp32 work, scheduled among the products below
 #pragma unroll
   for (int ci = 0; ci < L::CT; ++ci) {
-    const int c0 = 16 * (L::CT * wave + ci);
+    const int c0 = 16 * (L::CT * ow + ci);
     op::frag af[4];
 #pragma unroll
-    for (int sb = 0; sb < 4; ++sb) af[sb] = op::ld_tr(Wb, L::LDK, 16 * sb, c0, lr, lg);
+    for (int sb = 0; sb < 4; ++sb) af[sb] = ps_sq(op::ld_tr(Kb, L::LDK, 16 * sb, c0, lr, lg));
     const f32x4 dv = *reinterpret_cast<const f32x4*>(d0 + c0 + 4 * lg);
 #pragma unroll
     for (int TB = 0; TB < 4; ++TB) {
@@ -287,29 +307,19 @@ __device__ __forceinline__ void precond_output(const __bf16* Wb, const __bf16* K
 }
 
 template <int DK, bool HAS_R>
-__global__ __launch_bounds__(256) void precond_scan_chunk_kernel(PrecondParams p) {
+__global__ __launch_bounds__(512) void precond_scan_chunk_kernel(PrecondParams p) {
   typedef PsLayout<DK> L;
   typedef Op<IO_BF16> op;
   typedef op::T bf;
   __shared__ __align__(16) unsigned char smem[L::BYTES];
-  bf* Kb = reinterpret_cast<bf*>(smem + L::K_OFF);
-  bf* Wb = reinterpret_cast<bf*>(smem + L::W_OFF);
-  float* Ms = reinterpret_cast<float*>(smem + L::M_OFF);
+  auto kbuf = [&](int64_t i) { return reinterpret_cast<bf*>(smem + L::K_OFF + (i & 3) * L::KB_BYTES); };
+  auto mbuf = [&](int64_t i) { return reinterpret_cast<float*>(smem + L::M_OFF + (i & 1) * L::M_BYTES); };
+  auto tbuf = [&](int64_t i) { return reinterpret_cast<float*>(smem + L::T_OFF) + (i & 3) * L::TOK_FLOATS; };
   float* dbuf = reinterpret_cast<float*>(smem + L::D_OFF);
   float* part = reinterpret_cast<float*>(smem + L::Q_OFF);
-  float* tok = reinterpret_cast<float*>(smem + L::T_OFF);
-  float* tn = tok + L::TR_N * CH;
-  float* tP = tok + L::TR_P * CH;
-  float* tbeta = tok + L::TR_BETA * CH;
-  float* tgex = tok + L::TR_GEX * CH;
-  float* tgin = tok + L::TR_GIN * CH;
-  float* tR = tok + L::TR_R * CH;
-  float* tIR = tok + L::TR_IR * CH;
-  float* teh = tok + L::TR_EH * CH;
-  float* tc = tok + L::TR_C * CH;
 
   const int tid = threadIdx.x;
-  // the wave index is uniform: keeping it scalar makes every wave test a scalar
+  // the wave index is uniform: keeping it scalar makes every role test a scalar
   // branch (and keeps buffer offsets in scalar registers)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int lr = lane & 15, lg = lane >> 4;
@@ -317,6 +327,7 @@ __global__ __launch_bounds__(256) void precond_scan_chunk_kernel(PrecondParams p
   const int64_t b = bh / p.H, h = bh - b * p.H;
   const int64_t T = p.T, H = p.H;
   const float eta = p.eta;
+  const int64_t nch = (T + CH - 1) / CH;
 
   // Buffer ranges over this sequence's slab: loads past the last token return
   // zero and stores there are dropped, so the ragged last chunk needs no branch.
@@ -326,199 +337,189 @@ __global__ __launch_bounds__(256) void precond_scan_chunk_kernel(PrecondParams p
   const rsrc_t br = make_rsrc(static_cast<const uint16_t*>(p.beta) + b * T * H, slab * 2);
   const rsrc_t rr = make_rsrc(HAS_R ? static_cast<const uint16_t*>(p.r) + b * T * H : nullptr, HAS_R ? slab * 2 : 0);
 
-  // Zero M once: blocks above the diagonal are never written.
-  for (int i = tid; i < CH * L::LM; i += 256) Ms[i] = 0.f;
+  // Both M buffers zeroed once: blocks above the diagonal are never written.
+  for (int i = tid; i < 2 * CH * L::LM; i += L::NT) reinterpret_cast<float*>(smem + L::M_OFF)[i] = 0.f;
   if (tid < DK) dbuf[tid] = p.d0 ? p.d0[bh * DK + tid] : 1.f;
 
-  // Loader roles: thread (token lt, quarter lq) loads channels 8*(lq + 4j) .. +7;
-  // every lane also loads the factors of token `lane` (wave 0 uses them).
-  const int lt = tid >> 2, lq = tid & 3;
-  const uint32_t kvoff = static_cast<uint32_t>((lt * H + h) * DK + 8 * lq) * 2;
-  const uint32_t bvoff = static_cast<uint32_t>(lane * H + h) * 2;
-  u32x4 kreg[L::KV];
+  // ---- the staging wave (wave 7): lane (token 16i + lane/4, quarter lane%4) in
+  // round i loads channels 8*(quarter + 4j) .. +7; lane also loads the factors of
+  // token `lane`.  Loads for chunk c + 1 are issued as soon as chunk c is staged.
+  const int sq = lane & 3, st = lane >> 2;
+  u32x4 kreg[4][L::KV];
   uint16_t beta_r = 0, r_r = 0;
-  auto load_chunk = [&](int64_t t0) {
-    const uint32_t so = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(t0 * H * DK * 2));
-    const uint32_t sb = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(t0 * H * 2));
+  auto load_chunk = [&](int64_t c) {
+    const uint32_t so = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(c * CH * H * DK * 2));
+    const uint32_t sb = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(c * CH * H * 2));
 #pragma unroll
-    for (int j = 0; j < L::KV; ++j) kreg[j] = buf_load16(kr, kvoff + 64 * j, so);
-    beta_r = buf_load2(br, bvoff, sb);
-    if (HAS_R) r_r = buf_load2(rr, bvoff, sb);
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < L::KV; ++j)
+        kreg[i][j] = buf_load16(kr, static_cast<uint32_t>(((16 * i + st) * H + h) * DK + 8 * (sq + 4 * j)) * 2, so);
+    beta_r = buf_load2(br, static_cast<uint32_t>(lane * H + h) * 2, sb);
+    if (HAS_R) r_r = buf_load2(rr, static_cast<uint32_t>(lane * H + h) * 2, sb);
   };
-  const int64_t nch = (T + CH - 1) / CH;
-  load_chunk(0);
+  auto stage = [&](int64_t c) {
+    bf* Kb = kbuf(c);
+    float* tk = tbuf(c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * i + st;
+      float sn = 0.f;
+#pragma unroll
+      for (int j = 0; j < L::KV; ++j) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float k0 = __uint_as_float(kreg[i][j][e] << 16), k1 = __uint_as_float(kreg[i][j][e] & 0xFFFF0000u);
+          sn = fmaf(k0, k0, sn);
+          sn = fmaf(k1, k1, sn);
+        }
+        *reinterpret_cast<u32x4*>(Kb + t * L::LDK + 8 * (sq + 4 * j)) = kreg[i][j];
+      }
+      sn = quad_sum(sn);
+      if (sq == 0) tk[L::TR_N * CH + t] = sn;
+    }
+    const bool ok = c * CH + lane < T;
+    const float lrv = HAS_R && ok ? __logf(bf16_bits_to_f32(r_r)) : 0.f;
+    const float gin = HAS_R ? wave_prefix_sum(lrv) : 0.f;
+    tk[L::TR_BETA * CH + lane] = bf16_bits_to_f32(beta_r);   // zero past the end
+    tk[L::TR_GIN * CH + lane] = gin;
+    tk[L::TR_GEX * CH + lane] = gin - lrv;
+    tk[L::TR_R * CH + lane] = HAS_R ? __expf(gin - lrv) : 1.f;
+    tk[L::TR_IR * CH + lane] = HAS_R ? __expf(-gin) : 1.f;   // used only when the factored form is
+  };
+  auto factored = [&](int64_t c) {   // the chunk's total log-retention allows the factored form
+    if (!HAS_R) return true;
+    const float gC = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(tbuf(c)[L::TR_GIN * CH + CH - 1])));
+    return gC >= PS_FACTOR_MIN_G;
+  };
+  if (wave == L::NW - 1 && nch > 0) load_chunk(0);
   __syncthreads();   // M zeroed, d_0 in place
 
-  // ---- stage: k and bf16(k^2) into LDS, n_t, the chunk's log-retention sums ----
-  // Run for chunk 0 before the loop and for chunk n + 1 at the bottom of
-  // iteration n (after chunk n's output stores, so the wait for the prefetched
-  // keys is not also a wait for those stores).  It then prefetches the chunk
-  // after, unconditionally: past the last chunk the loads fall outside the
-  // buffer range and return zeros without touching memory, and a loop body
-  // without branches lets the compiler count outstanding loads exactly.
-  auto stage = [&](int64_t n) {
-    const int64_t t0 = n * CH;
-    float sn = 0.f;
-#pragma unroll
-    for (int j = 0; j < L::KV; ++j) {
-      const int c = 8 * (lq + 4 * j);
-      bf16x8 wb;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float k0 = __uint_as_float(kreg[j][e] << 16), k1 = __uint_as_float(kreg[j][e] & 0xFFFF0000u);
-        sn = fmaf(k0, k0, sn);
-        sn = fmaf(k1, k1, sn);
-        wb[2 * e] = static_cast<__bf16>(k0 * k0);
-        wb[2 * e + 1] = static_cast<__bf16>(k1 * k1);
-      }
-      *reinterpret_cast<u32x4*>(Kb + lt * L::LDK + c) = kreg[j];
-      *reinterpret_cast<bf16x8*>(Wb + lt * L::LDK + c) = wb;
-    }
-    sn = quad_sum(sn);
-    if (lq == 0) tn[lt] = sn;
+  for (int64_t n = -2; n <= nch; ++n) {
+    // ---- 1. substitution (n) | output (n-1) | Gram (n+1) | stage (n+2) --------------
     if (wave == 0) {
-      const bool ok = t0 + lane < T;
-      const float lrv = HAS_R && ok ? __logf(bf16_bits_to_f32(r_r)) : 0.f;
-      const float gin = HAS_R ? wave_prefix_sum(lrv) : 0.f;
-      tbeta[lane] = bf16_bits_to_f32(beta_r);   // zero past the end
-      tgin[lane] = gin;
-      tgex[lane] = gin - lrv;
-      tR[lane] = HAS_R ? __expf(gin - lrv) : 1.f;
-      tIR[lane] = HAS_R ? __expf(-gin) : 1.f;     // used only when the chunk's sum is >= the factor bound
+      if (n >= 0 && n < nch) {
+        const float* tk = tbuf(n);
+        float m[CH];
+        const float* mrow = mbuf(n) + lane * L::LM;
+#pragma unroll
+        for (int i = 0; i < CH; i += 4) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(mrow + i);
+          m[i] = v[0]; m[i + 1] = v[1]; m[i + 2] = v[2]; m[i + 3] = v[3];
+        }
+        const float nn = tk[L::TR_N * CH + lane], be = tk[L::TR_BETA * CH + lane];
+        const float gam = nn > 0.f ? eta * be * __builtin_amdgcn_rcpf(nn) : 0.f;   // alf_t = gam_t beta_t
+        float acc = gam - gam * be * tk[L::TR_R * CH + lane] * tk[L::TR_P * CH + lane];
+#pragma unroll
+        for (int s = 0; s < CH; ++s) {
+          const float es = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), s));
+          acc = fmaf(-m[s], es, acc);
+        }
+        const bool fact = factored(n);
+        float* tkw = tbuf(n);
+        // e_t e^{-g_{t+1}} for the factored output; e_t itself otherwise
+        tkw[L::TR_EH * CH + lane] = fact && HAS_R ? acc * tk[L::TR_IR * CH + lane] : acc;
+        tkw[L::TR_C * CH + lane] =
+            HAS_R ? __expf(tk[L::TR_GIN * CH + CH - 1] - tk[L::TR_GIN * CH + lane]) * acc : acc;
+      }
+    } else if (wave <= 4) {
+      if (n >= 1 && n <= nch) {
+        const int64_t c = n - 1;
+        const uint32_t so = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(c * CH * H * DK * 2));
+        if (factored(c)) precond_output<DK, true>(kbuf(c), dbuf + (c & 1) * DK, tbuf(c), kwr, so, H, h, wave - 1, lr, lg);
+        else precond_output<DK, false>(kbuf(c), dbuf + (c & 1) * DK, tbuf(c), kwr, so, H, h, wave - 1, lr, lg);
+      }
+    } else if (wave <= 6) {
+      if (n + 1 >= 0 && n + 1 < nch) {
+        const int64_t c = n + 1;
+        const bool fact = factored(c);
+        if (wave == 5) {
+          if (fact) precond_gram<DK, HAS_R, 0, true>(kbuf(c), mbuf(c), tbuf(c), eta, lr, lg);
+          else precond_gram<DK, HAS_R, 0, false>(kbuf(c), mbuf(c), tbuf(c), eta, lr, lg);
+        } else {
+          if (fact) precond_gram<DK, HAS_R, 1, true>(kbuf(c), mbuf(c), tbuf(c), eta, lr, lg);
+          else precond_gram<DK, HAS_R, 1, false>(kbuf(c), mbuf(c), tbuf(c), eta, lr, lg);
+        }
+      }
+    } else {
+      if (n + 2 < nch) {
+        stage(n + 2);
+        if (n + 3 < nch) load_chunk(n + 3);
+      }
     }
-    load_chunk(t0 + CH);
-  };
-  stage(0);
-  __syncthreads();
+    __syncthreads();
 
-  int cur = 0;            // d_0 of the chunk being processed is dbuf[cur]
-  for (int64_t n = 0; n < nch; ++n) {
-    const int64_t t0 = n * CH;
-    const float* d0 = dbuf + cur * DK;
-    const float gC = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(tgin[CH - 1])));
-    const bool fact = !HAS_R || gC >= PS_FACTOR_MIN_G;   // the chunk's total log-retention decides
+    // ---- 2. partial sums of c_s w_s over token groups (chunk n) ----------------------
+    if (n >= 0 && n < nch) {
+      const bf* Kb = kbuf(n);
+      const float* tc = tbuf(n) + L::TR_C * CH;
+      const int cp = tid % L::NP, qd = tid / L::NP;
+      float cs[L::TPQ];
+      uint32_t ku[L::TPQ];
+#pragma unroll
+      for (int i = 0; i < L::TPQ; i += 4) {
+        const f32x4 cv = *reinterpret_cast<const f32x4*>(tc + qd * L::TPQ + i);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) cs[i + q] = cv[q];
+      }
+#pragma unroll
+      for (int i = 0; i < L::TPQ; ++i)
+        ku[i] = *reinterpret_cast<const uint32_t*>(Kb + (qd * L::TPQ + i) * L::LDK + 2 * cp);
+      float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < L::TPQ; ++i) {
+        const float k0 = __uint_as_float(ku[i] << 16), k1 = __uint_as_float(ku[i] & 0xFFFF0000u);
+        a0 = fmaf(cs[i], k0 * k0, a0);
+        a1 = fmaf(cs[i], k1 * k1, a1);
+      }
+      *reinterpret_cast<float2*>(part + qd * DK + 2 * cp) = make_float2(a0, a1);
+    }
+    __syncthreads();
 
-    // ---- Gram: M on MFMA; <w_t, d_0> in fp32 --------------------------------------
-    {
-      // <w_t, d_0> in fp32: thread (token lt, quarter lq) over its 32 channels
+    // ---- 3. d_0 of chunk n+1 = e^{g_64} d_0 + sum_s c_s w_s ------------------------
+    if (n >= 0 && n < nch && tid < DK) {
+      const float RC = HAS_R ? __expf(tbuf(n)[L::TR_GIN * CH + CH - 1]) : 1.f;
+      float s = RC * dbuf[(n & 1) * DK + tid];
+#pragma unroll
+      for (int q = 0; q < L::NQ; ++q) s += part[q * DK + tid];
+      dbuf[((n + 1) & 1) * DK + tid] = s;
+    }
+    __syncthreads();
+
+    // ---- 4. <w_t, d_0> of chunk n+1, fp32: thread (token tid/8, eighth) -------------
+    if (n + 1 >= 0 && n + 1 < nch) {
+      const int64_t c = n + 1;
+      const int t = tid >> 3, e8 = tid & 7;
+      const bf* row = kbuf(c) + t * L::LDK + L::PCH * e8;
+      const float* d0 = dbuf + (c & 1) * DK + L::PCH * e8;
       float sp = 0.f;
-      auto pdot = [&]() {
 #pragma unroll
-        for (int j = 0; j < L::KV; ++j) {
-          const int c = 8 * (lq + 4 * j);
-          const u32x4 kv = *reinterpret_cast<const u32x4*>(Kb + lt * L::LDK + c);
-          const f32x4 da = *reinterpret_cast<const f32x4*>(d0 + c);
-          const f32x4 db = *reinterpret_cast<const f32x4*>(d0 + c + 4);
+      for (int j = 0; j < L::PCH; j += 8) {
+        const u32x4 kv = *reinterpret_cast<const u32x4*>(row + j);
+        const f32x4 da = *reinterpret_cast<const f32x4*>(d0 + j);
+        const f32x4 db = *reinterpret_cast<const f32x4*>(d0 + j + 4);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float k0 = __uint_as_float(kv[e] << 16), k1 = __uint_as_float(kv[e] & 0xFFFF0000u);
-            sp = fmaf(k0 * k0, e < 2 ? da[2 * e] : db[2 * e - 4], sp);
-            sp = fmaf(k1 * k1, e < 2 ? da[2 * e + 1] : db[2 * e - 3], sp);
-          }
-        }
-      };
-      // (the factored and per-element forms are separate code paths under one
-      // uniform branch, so neither computes the other's exponentials)
-      if (fact) {
-        switch (wave) {
-          case 0: precond_gram<DK, HAS_R, 0, true>(Wb, Ms, tok, eta, lr, lg, pdot); break;
-          case 1: precond_gram<DK, HAS_R, 1, true>(Wb, Ms, tok, eta, lr, lg, pdot); break;
-          case 2: precond_gram<DK, HAS_R, 2, true>(Wb, Ms, tok, eta, lr, lg, pdot); break;
-          default: precond_gram<DK, HAS_R, 3, true>(Wb, Ms, tok, eta, lr, lg, pdot); break;
-        }
-      } else {
-        switch (wave) {
-          case 0: precond_gram<DK, HAS_R, 0, false>(Wb, Ms, tok, eta, lr, lg, pdot); break;
-          case 1: precond_gram<DK, HAS_R, 1, false>(Wb, Ms, tok, eta, lr, lg, pdot); break;
-          case 2: precond_gram<DK, HAS_R, 2, false>(Wb, Ms, tok, eta, lr, lg, pdot); break;
-          default: precond_gram<DK, HAS_R, 3, false>(Wb, Ms, tok, eta, lr, lg, pdot); break;
+        for (int e = 0; e < 4; ++e) {
+          const float k0 = __uint_as_float(kv[e] << 16), k1 = __uint_as_float(kv[e] & 0xFFFF0000u);
+          sp = fmaf(k0 * k0, e < 2 ? da[2 * e] : db[2 * e - 4], sp);
+          sp = fmaf(k1 * k1, e < 2 ? da[2 * e + 1] : db[2 * e - 3], sp);
         }
       }
       sp = quad_sum(sp);
-      if (lq == 0) tP[lt] = sp;
+      sp += dpp<0x141>(0.f, sp);   // row_half_mirror: the other quad of the 8
+      if (e8 == 0) tbuf(c)[L::TR_P * CH + t] = sp;
     }
-    __syncthreads();
-
-    // ---- forward substitution (I + M) e = b on one wave -----------------------------
-    if (wave == 0) {
-      float m[CH];
-      const float* mrow = Ms + lane * L::LM;
-#pragma unroll
-      for (int i = 0; i < CH; i += 4) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(mrow + i);
-        m[i] = v[0]; m[i + 1] = v[1]; m[i + 2] = v[2]; m[i + 3] = v[3];
-      }
-      const float nn = tn[lane], be = tbeta[lane];
-      const float gam = nn > 0.f ? eta * be * __builtin_amdgcn_rcpf(nn) : 0.f;   // alf_t = gam_t beta_t
-      float acc = gam - gam * be * tR[lane] * tP[lane];
-#pragma unroll
-      for (int s = 0; s < CH; ++s) {
-        const float es = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), s));
-        acc = fmaf(-m[s], es, acc);
-      }
-      // e_t e^{-g_{t+1}} for the factored output; e_t itself otherwise
-      teh[lane] = fact && HAS_R ? acc * tIR[lane] : acc;
-      tc[lane] = HAS_R ? __expf(gC - tgin[lane]) * acc : acc;
-    }
-    __syncthreads();
-
-    // ---- output kw_t = d_t * k_t on MFMA; chunk-end update partials -----------------
-    // D^T = W^T L^T + d_0 e^{g_t} as 16x16 tiles (rows: channels, columns: tokens):
-    // each lane ends with four consecutive channels of one token.  Wave w takes
-    // channel tiles CT*w .. CT*w + CT - 1 for all four token blocks.  Factored:
-    // D_t = e^{g_t} (d_0 + sum_{s<t} e_s e^{-g_{s+1}} w_s); otherwise each
-    // L_ts = e^{g_t - g_{s+1}} e_s is formed with its own exponential.
-    {
-      // partial sums of c_s w_s over token groups, for the chunk-end preconditioner
-      const int cp = tid % L::NP, qd = tid / L::NP;
-      float a0 = 0.f, a1 = 0.f;
-      auto partials = [&]() {
-        float cs[L::TPQ];
-        uint32_t ku[L::TPQ];
-#pragma unroll
-        for (int i = 0; i < L::TPQ; i += 4) {
-          const f32x4 c = *reinterpret_cast<const f32x4*>(tc + qd * L::TPQ + i);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) cs[i + q] = c[q];
-        }
-#pragma unroll
-        for (int i = 0; i < L::TPQ; ++i)
-          ku[i] = *reinterpret_cast<const uint32_t*>(Kb + (qd * L::TPQ + i) * L::LDK + 2 * cp);
-#pragma unroll
-        for (int i = 0; i < L::TPQ; ++i) {
-          const float k0 = __uint_as_float(ku[i] << 16), k1 = __uint_as_float(ku[i] & 0xFFFF0000u);
-          a0 = fmaf(cs[i], k0 * k0, a0);
-          a1 = fmaf(cs[i], k1 * k1, a1);
-        }
-      };
-      const uint32_t so = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(t0 * H * DK * 2));
-      if (fact) precond_output<DK, true>(Wb, Kb, d0, tok, kwr, so, H, h, wave, lr, lg, partials);
-      else precond_output<DK, false>(Wb, Kb, d0, tok, kwr, so, H, h, wave, lr, lg, partials);
-      *reinterpret_cast<float2*>(part + qd * DK + 2 * cp) = make_float2(a0, a1);
-    }
-    const float RC = HAS_R ? __expf(gC) : 1.f;
-    __syncthreads();
-
-    // ---- chunk-end preconditioner d_64 = e^{g_64} d_0 + sum_s c_s w_s; next stage ----
-    if (tid < DK) {
-      float s = RC * d0[tid];
-#pragma unroll
-      for (int q = 0; q < L::NQ; ++q) s += part[q * DK + tid];
-      dbuf[(cur ^ 1) * DK + tid] = s;
-    }
-    cur ^= 1;
-    stage(n + 1);   // past the last chunk: zeros, never read
     __syncthreads();
   }
-  if (p.d_T && tid < DK) p.d_T[bh * DK + tid] = dbuf[cur * DK + tid];
+  if (p.d_T && tid < DK) p.d_T[bh * DK + tid] = dbuf[(nch & 1) * DK + tid];
 }
 
 template <int DK, bool HAS_R>
 static hipError_t launch_chunk_t(const PrecondParams& p, hipStream_t stream) {
   constexpr size_t lds = PsLayout<DK>::BYTES;
   static_assert(lds <= 160 * 1024, "LDS budget");
-  hipLaunchKernelGGL((precond_scan_chunk_kernel<DK, HAS_R>), dim3(static_cast<unsigned>(p.B * p.H)), dim3(256),
-                     0, stream, p);
+  hipLaunchKernelGGL((precond_scan_chunk_kernel<DK, HAS_R>), dim3(static_cast<unsigned>(p.B * p.H)),
+                     dim3(PsLayout<DK>::NT), 0, stream, p);
   return hipGetLastError();
 }
 
