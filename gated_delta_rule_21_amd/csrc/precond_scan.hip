@@ -142,9 +142,10 @@ __global__ __launch_bounds__(64) void precond_scan_seq_kernel(PrecondParams p) {
 // ---------------------------------------------------------------------------
 // bf16 I/O: chunkwise and software-pipelined, one 512-thread workgroup (8 waves)
 // per (sequence, head).  Iteration n of the chunk loop runs, between barriers:
-//   1. wave 0: forward substitution of chunk n (the dependent chain);
-//      waves 1-4: output k~ of chunk n-1;  waves 5-6: Gram matrix M of chunk
-//      n+1;  wave 7: stage chunk n+2 into LDS and prefetch chunk n+3;
+//   1. wave 0: forward substitution of chunk n (the dependent chain), then two
+//      tiles of the Gram matrix M of chunk n+1;  waves 1-4: output k~ of chunk
+//      n-1;  waves 5-6: the rest of M of chunk n+1;  wave 7: stage chunk n+2
+//      into LDS and prefetch chunk n+3;
 //   2. all: partial sums of the chunk-end update of chunk n;
 //   3. d_0 of chunk n+1;
 //   4. all: <w_t, d_0> of chunk n+1.
@@ -190,15 +191,20 @@ __device__ __forceinline__ bf16x4 ps_sq(bf16x4 k) {
   return to_bf16x4(f32x4{x[0] * x[0], x[1] * x[1], x[2] * x[2], x[3] * x[3]});
 }
 
-// Gram tiles of the two Gram waves: (R, J) blocks of W W^T, J <= R.
+// Gram tiles, (R, J) blocks of W W^T with J <= R: four each for the two Gram
+// waves, two for the substitution wave once its chain is done.
 template <int W> struct PsGram;
 template <> struct PsGram<0> {
-  static constexpr int N = 5, NEED = 0x7;
-  static constexpr int R[5] = {0, 1, 1, 2, 2}, J[5] = {0, 0, 1, 0, 1};
+  static constexpr int N = 4, NEED = 0x7;
+  static constexpr int R[4] = {0, 1, 1, 2}, J[4] = {0, 0, 1, 0};
 };
 template <> struct PsGram<1> {
-  static constexpr int N = 5, NEED = 0xF;
-  static constexpr int R[5] = {2, 3, 3, 3, 3}, J[5] = {2, 0, 1, 2, 3};
+  static constexpr int N = 4, NEED = 0xF;
+  static constexpr int R[4] = {3, 3, 3, 3}, J[4] = {0, 1, 2, 3};
+};
+template <> struct PsGram<2> {
+  static constexpr int N = 2, NEED = 0x6;
+  static constexpr int R[4] = {2, 2, 0, 0}, J[4] = {1, 2, 0, 0};
 };
 
 // M_ts = alf_t e^{g_t - g_{s+1}} <w_t, w_s> for s < t (0 elsewhere) into Ms.
@@ -421,6 +427,11 @@ __global__ __launch_bounds__(512) void precond_scan_chunk_kernel(PrecondParams p
         tkw[L::TR_EH * CH + lane] = fact && HAS_R ? acc * tk[L::TR_IR * CH + lane] : acc;
         tkw[L::TR_C * CH + lane] =
             HAS_R ? __expf(tk[L::TR_GIN * CH + CH - 1] - tk[L::TR_GIN * CH + lane]) * acc : acc;
+      }
+      if (n + 1 >= 0 && n + 1 < nch) {   // its share of the Gram matrix of chunk n+1
+        const int64_t c = n + 1;
+        if (factored(c)) precond_gram<DK, HAS_R, 2, true>(kbuf(c), mbuf(c), tbuf(c), eta, lr, lg);
+        else precond_gram<DK, HAS_R, 2, false>(kbuf(c), mbuf(c), tbuf(c), eta, lr, lg);
       }
     } else if (wave <= 4) {
       if (n >= 1 && n <= nch) {
