@@ -44,15 +44,21 @@ namespace gdr {
 // is 2 or 6 (mod 8) dwords long, transpose reads (ds_read_b64_tr_b16) at 168 B/clk
 // when it is 8 (mod 32) dwords and at 128 B/clk for most other lengths; the k
 // tile is read both ways and takes 6 (mod 32) dwords (121 and 128 B/clk).
-template <int DK, int DVT_, bool CHAN>
+template <int DK, int DVT_, bool CHAN, bool KROW>
 struct PipeLayout {
   static constexpr int LDK = DK + 12;                    // k: row and transpose reads (8-byte aligned rows)
+  // With a write key, k is read by rows only (the transposed reads take the write
+  // key): the measured row-read stride for k, and a tighter one for the write key,
+  // bring 64 columns within the 160 KB of LDS.
+  static constexpr int LDKK = KROW ? DK + 4 : LDK;       // stride of the k tile
+  static constexpr int LDKD = KROW ? DK + 8 : LDK;       // stride of the third tile
   static constexpr int LDQ = DK + 4;                     // q: row reads (8-byte aligned rows)
   static constexpr int DVT = DVT_;
   static constexpr int LVT = DVT + 16;                   // v: transpose reads
   static constexpr int LCT = CH + 16;                    // T^T: transpose reads
   static constexpr int LCP = CH + 4;                     // P: row reads
-  static constexpr size_t KB = size_t(CH) * LDK * 2;
+  static constexpr size_t KB = size_t(CH) * LDKK * 2;
+  static constexpr size_t KDB = size_t(CH) * LDKD * 2;
   static constexpr size_t QB = size_t(CH) * LDQ * 2;
   static constexpr size_t VB = size_t(CH) * LVT * 2;
   static constexpr size_t TB = size_t(CH) * LCT * 2;
@@ -63,7 +69,7 @@ struct PipeLayout {
   static constexpr size_t B_T = B_V + VB;                // T^T (the ten blocks on or above the diagonal)
   static constexpr size_t B_F = B_T + TB;                // factor rows of the workspace record
   static constexpr size_t B_KD = B_F + 6 * CH * 4;       // per-channel gate: k e^{g_63 - g} (transpose reads)
-  static constexpr size_t BUF = B_KD + (CHAN ? KB : 0);
+  static constexpr size_t BUF = B_KD + (CHAN ? KDB : 0);
   // P of chunk n in copy n % 2
   static constexpr size_t PB = size_t(CH) * LCP * 2;
   static constexpr size_t OFF_P = 2 * BUF;
@@ -79,13 +85,13 @@ __global__ __launch_bounds__((NCH + NHW) * 64) void chunk_state_pipe_kernel(Chun
   constexpr int DVT = 16 * CG * NCH;            // columns per workgroup
   constexpr bool CHAN = GATE == GATE_CHANNEL;
   constexpr bool WK = GATE == GATE_WKEY;          // write key: K^T and P take kw instead of k
-  typedef PipeLayout<DK, DVT, CHAN || WK> L;
+  typedef PipeLayout<DK, DVT, CHAN || WK, WK> L;
   typedef WsRec<2> W;
   constexpr uint32_t RB = rec_bytes(IO_BF16, GATE, DK);   // bytes per chunk record
   constexpr int ESZ = 2, EPV = 8;
   constexpr int NH = NHW * 64;                   // helper threads
   constexpr int DKT = DK / 16;
-  constexpr int LDK = L::LDK, LDQ = L::LDQ, LVT = L::LVT, LCT = L::LCT, LCP = L::LCP;
+  constexpr int LDKK = L::LDKK, LDKD = L::LDKD, LDQ = L::LDQ, LVT = L::LVT, LCT = L::LCT, LCP = L::LCP;
   constexpr int KROW = DK / EPV, VROW = DVT / EPV;
   constexpr int NKP = CH * KROW, NVP = CH * VROW; // 16-byte pieces of the k (q) tile, of the v tile
   constexpr int HK = (NKP + NH - 1) / NH;        // ... per helper thread (the last round guarded
@@ -219,14 +225,14 @@ __global__ __launch_bounds__((NCH + NHW) * 64) void chunk_state_pipe_kernel(Chun
     for (int v = 0; v < HK; ++v) {
       const int seg = ht + v * NH, row = seg / KROW, c = (seg % KROW) * EPV;
       if (NKP % NH != 0 && seg >= NKP) break;
-      u32x2* k2 = reinterpret_cast<u32x2*>(dK + row * LDK + c);     // k, q rows are 8-byte aligned
+      u32x2* k2 = reinterpret_cast<u32x2*>(dK + row * LDKK + c);    // k, q rows are 8-byte aligned
       k2[0] = u32x2{pk[v][0], pk[v][1]};
       k2[1] = u32x2{pk[v][2], pk[v][3]};
       u32x2* q2 = reinterpret_cast<u32x2*>(dQ + row * LDQ + c);
       q2[0] = u32x2{pq[v][0], pq[v][1]};
       q2[1] = u32x2{pq[v][2], pq[v][3]};
       if constexpr (CHAN || WK) {
-        u32x2* d2 = reinterpret_cast<u32x2*>(reinterpret_cast<T*>(base + L::B_KD) + row * LDK + c);
+        u32x2* d2 = reinterpret_cast<u32x2*>(reinterpret_cast<T*>(base + L::B_KD) + row * LDKD + c);
         d2[0] = u32x2{pkd[v][0], pkd[v][1]};
         d2[1] = u32x2{pkd[v][2], pkd[v][3]};
       }
@@ -318,7 +324,7 @@ __global__ __launch_bounds__((NCH + NHW) * 64) void chunk_state_pipe_kernel(Chun
       auto load_rows = [&](int b, int R) __attribute__((always_inline)) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
-          const T* kr = c.K + (16 * R + lr) * LDK + 32 * kb + 4 * lg;
+          const T* kr = c.K + (16 * R + lr) * LDKK + 32 * kb + 4 * lg;
           const T* qr = c.Q + (16 * R + lr) * LDQ + 32 * kb + 4 * lg;
           kf[b][2 * kb] = O::ld(kr);
           kf[b][2 * kb + 1] = O::ld(kr + 16);
@@ -434,7 +440,7 @@ __global__ __launch_bounds__((NCH + NHW) * 64) void chunk_state_pipe_kernel(Chun
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) ktf[b][4 * h + i] = O::ld_tr(c.KD, LDK, 16 * i, 16 * (2 * tp + h), lr, lg);
+          for (int i = 0; i < 4; ++i) ktf[b][4 * h + i] = O::ld_tr(c.KD, LDKD, 16 * i, 16 * (2 * tp + h), lr, lg);
       };
       __builtin_amdgcn_sched_barrier(0);
       load_kt(0, 0);
@@ -550,7 +556,7 @@ __global__ __launch_bounds__((NCH + NHW) * 64) void chunk_state_pipe_kernel(Chun
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kb = 0; kb < DK / 32; ++kb) {
-            const T* kr = c.KD + (16 * J + lr) * LDK + 32 * kb + 4 * lg;   // k, or the write key
+            const T* kr = c.KD + (16 * J + lr) * LDKD + 32 * kb + 4 * lg;   // k, or the write key
             acc = O::mma2(acc, O::ld(kr), O::ld(kr + 16), qf[2 * kb], qf[2 * kb + 1]);
           }
           const f32x4 gj = *reinterpret_cast<const f32x4*>(c.g + 16 * J + 4 * lg);
@@ -587,8 +593,10 @@ template <int GATE, int DK>
 static hipError_t launch_pipe_dk(const ChunkParams& p, hipStream_t stream) {
   // 32 columns per workgroup: 2 chain waves and 4 helpers (measured: 15-20% faster
   // than 2 helpers, as fast as 6, on the per-channel and the no-gate workloads).
-  if constexpr (GATE == GATE_CHANNEL || GATE == GATE_WKEY) {
-    // per-channel gate, write key: the third operand tile leaves LDS room for 32 columns only
+  if constexpr (GATE == GATE_CHANNEL) {
+    // per-channel gate: the third operand tile leaves LDS room for 32 columns only
+    return launch_pipe_t<GATE, DK, 2, 1, 4>(p, stream);
+  } else if constexpr (GATE == GATE_WKEY && DK == 64) {
     return launch_pipe_t<GATE, DK, 2, 1, 4>(p, stream);
   } else {
     // 64 columns per workgroup when that still gives one workgroup per CU, else 32.

@@ -27,7 +27,8 @@ def _wkey_inputs(B, T, H, dk, dv, seed, io="bf16", s0=0.02):
 
 
 @pytest.mark.parametrize("shape", [(2, 200, 3, 128, 128), (1, 130, 2, 64, 128), (1, 65, 2, 128, 64),
-                                   (2, 1, 2, 128, 128), (1, 300, 64, 128, 128)],
+                                   (2, 1, 2, 128, 128), (1, 300, 64, 128, 128),
+                                   (2, 130, 64, 128, 128)],   # B*H*(d_v/64) = 256: 64-column state tiles
                          ids=lambda s: "B%dT%dH%d_dk%d_dv%d" % s)
 def test_write_key_chunk_fwd(shape):
     need_gpu()
