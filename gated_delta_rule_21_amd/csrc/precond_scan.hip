@@ -25,8 +25,9 @@
 //     d_t = e^{g_t} d_0 + sum_{s<t} e^{g_t - g_{s+1}} e_s w_s        (kw_t = d_t * k_t)
 //     d_64 = e^{g_64} d_0 + sum_s e^{g_64 - g_{s+1}} e_s w_s.
 //
-// One 256-thread workgroup owns one (sequence, head) and walks its chunks in
-// order.  The Gram matrix of the w_t and the product that forms every d_t run on
+// One 512-thread workgroup owns one (sequence, head) and walks its chunks in
+// order, software-pipelined over neighbouring chunks (see the kernel).  The Gram
+// matrix of the w_t and the product that forms every d_t run on
 // MFMA with bf16 operands and fp32 accumulation; the unit lower triangular solve
 // is a forward substitution by one wave (lane t holds row t of M, each step
 // broadcasts e_s); the preconditioner itself, <w_t, d_0> and the chunk-end
@@ -91,7 +92,7 @@ __global__ __launch_bounds__(64) void precond_scan_seq_kernel(PrecondParams p) {
 #pragma unroll
   for (int i = 0; i < CPL; ++i) d[i] = p.d0 ? p.d0[bh * DK + lane * CPL + i] : 1.f;
 
-  float kc[U][CPL], bc[U], rc[U], kn[U][CPL], bn[U], rn[U];
+  float kc[U][CPL] = {}, bc[U] = {}, rc[U] = {}, kn[U][CPL] = {}, bn[U] = {}, rn[U] = {};
   // Tokens past the end read the last token (in bounds) and are skipped.
   auto load = [&](int64_t t0, float (&kx)[U][CPL], float (&bx)[U], float (&rx)[U]) {
 #pragma unroll
@@ -391,7 +392,7 @@ __global__ __launch_bounds__(512) void precond_scan_chunk_kernel(PrecondParams p
     tk[L::TR_GIN * CH + lane] = gin;
     tk[L::TR_GEX * CH + lane] = gin - lrv;
     tk[L::TR_R * CH + lane] = HAS_R ? __expf(gin - lrv) : 1.f;
-    tk[L::TR_IR * CH + lane] = HAS_R ? __expf(-gin) : 1.f;   // used only when the factored form is
+    tk[L::TR_IR * CH + lane] = HAS_R ? __expf(-gin) : 1.f;   // read only by the factored form
   };
   auto factored = [&](int64_t c) {   // the chunk's total log-retention allows the factored form
     if (!HAS_R) return true;
