@@ -11,7 +11,9 @@ and so is the serving handoff: a packed prefill of 32 prompts of log-uniform
 lengths in [128, 8192] (H=16, d=128, scalar gate) through gdr_chunk_fwd_varlen,
 then decode steps on the states it hands over (`handoff`), and the
 preconditioner scan of the preconditioned delta rule (with forgetting) over the
-workload's keys (`precond_scan`, GB/s against HBM peak).
+workload's keys (`precond_scan`, GB/s against HBM peak), and the chunk forward
+with the write keys it produced (`osdn`: phase 2, no gate, and the two phases'
+tokens/s).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
@@ -179,7 +181,7 @@ def bench_chunk(args, log):
     ms = ev0.elapsed_time(ev1) / args.steps
     log(f"chunk forward: {ms:.3f} ms/step (wall {1e3 * wall / args.steps:.3f} ms/step)")
     nbytes, flops = chunk_algorithmic(wl, with_S0=with_S0)
-    return wl, ms, nbytes, flops, (k, beta)
+    return wl, ms, nbytes, flops, (q, k, v, beta)
 
 
 def bench_decode(args, log):
@@ -257,12 +259,49 @@ def bench_precond(args, log, wl, k, beta):
     nbytes = precond_bytes(wl.B, wl.T, wl.H, wl.d_k, 2, True)
     gbs = nbytes / (ms * 1e-3) / 1e9
     log(f"preconditioner scan: {ms * 1e3:.1f} us, {gbs:.0f} GB/s")
-    return {"workload": "osdn_precond_scan_apf_b%dh%dt%dd%d_bf16" % (wl.B, wl.H, wl.T, wl.d_k),
+    return kw, {"workload": "osdn_precond_scan_apf_b%dh%dt%dd%d_bf16" % (wl.B, wl.H, wl.T, wl.d_k),
             "value": round(gbs, 1), "unit": "GB/s", "us_per_launch": round(ms * 1e3, 2),
             "tokens_per_s": round(wl.B * wl.T / (ms * 1e-3), 1), "bytes_per_launch": nbytes,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4),
                          "traffic": profiled_traffic("precond_scan_b8h16t8192d128_counters.md", PRECOND_SOURCES)}}
+
+
+def bench_wkey(args, log, wl, q, k, v, beta, kw, scan_us):
+    """Phase 2 of the preconditioned delta rule: the chunk forward with the write
+    keys the scan produced (no gate), over the chunk workload's q, k, v, beta."""
+    import torch
+    import gated_delta_rule_21_amd as gdr
+    o = torch.empty_like(v)
+    S_T = torch.empty((wl.B, wl.H, wl.d_k, wl.d_v), dtype=torch.float32, device="cuda")
+    ws = torch.empty(gdr.chunk_workspace_size(wl.B, wl.T, wl.H, wl.d_k, wl.d_v, torch.bfloat16, "none"),
+                     dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        gdr.chunk_fwd(q, k, v, beta, None, None, o=o, S_T=S_T, workspace=ws, kw=kw)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    nbytes, _ = chunk_algorithmic(wl.replace(gate="none"), with_S0=False)
+    nbytes += wl.B * wl.T * wl.H * wl.d_k * 2          # the write keys
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    total_ms = ms + scan_us * 1e-3
+    log(f"write-key forward: {ms * 1e3:.1f} us, {gbs:.0f} GB/s; scan + forward {total_ms * 1e3:.1f} us")
+    return {"workload": "osdn_two_phase_b%dh%dt%dd%d_bf16" % (wl.B, wl.H, wl.T, wl.d_k),
+            "forward_us": round(ms * 1e3, 2), "scan_us": scan_us,
+            "tokens_per_s": round(wl.B * wl.T / (total_ms * 1e-3), 1),
+            "forward_roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                 "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+            "forward_bytes_per_launch": nbytes}
 
 
 def handoff_lengths(n_seq: int = 32, lo: int = 128, hi: int = 8192, seed: int = 6):
@@ -373,14 +412,18 @@ def main():
     if args.copy_calibration:
         copy_calibration(log)
 
-    wl, ms, nbytes, flops, (k, beta) = bench_chunk(args, log)
+    wl, ms, nbytes, flops, (q, k, v, beta) = bench_chunk(args, log)
     tok_s = wl.B * wl.T / (ms * 1e-3)
     gbs = nbytes / (ms * 1e-3) / 1e9
     tflops = flops / (ms * 1e-3) / 1e12
     decode = None if args.no_decode else bench_decode(args, log)
     handoff = None if args.no_handoff else bench_handoff(args, log)
-    precond = None if args.no_precond else bench_precond(args, log, wl, k, beta)
-    del k, beta
+    precond = osdn = None
+    if not args.no_precond:
+        kw, precond = bench_precond(args, log, wl, k, beta)
+        osdn = bench_wkey(args, log, wl, q, k, v, beta, kw, precond["us_per_launch"])
+        del kw
+    del q, k, v, beta
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle sample")
@@ -414,6 +457,7 @@ def main():
         "decode": decode,
         "handoff": handoff,
         "precond_scan": precond,
+        "osdn": osdn,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
