@@ -34,6 +34,8 @@
 // A operand, stands for its transpose; rows of T are read from T^T with the
 // LDS transpose load; the output is formed transposed so each lane stores four
 // adjacent columns.
+#include <type_traits>
+
 #include "chunk_common.h"
 #include "launchers.h"
 
@@ -541,8 +543,11 @@ __global__ __launch_bounds__((NCH + NHW) * 64) void chunk_state_pipe_kernel(Chun
         store_p(sP);
         if (n + 1 < nchunks) prefetch_p(n + 1);
       }
-      // rows 16R.. of P for R = cw, cw + NHW, ..: the rows of q are read once per row block
-      for (int R = cw; R < (CHAN ? 0 : 4); R += NHW) {
+      // rows 16R.. of P: the rows of q are read once per row block, and with R a
+      // compile-time constant the R + 1 blocks of the row are unrolled, so their
+      // product chains and exponentials overlap instead of running one after another
+      auto p_row = [&](auto RC) __attribute__((always_inline)) {
+        constexpr int R = decltype(RC)::value;
         frag qf[DK / 16];
 #pragma unroll
         for (int kb = 0; kb < DK / 32; ++kb) {
@@ -551,6 +556,7 @@ __global__ __launch_bounds__((NCH + NHW) * 64) void chunk_state_pipe_kernel(Chun
         }
         const int r = 16 * R + lr;
         const float gr = c.g[r];
+#pragma unroll
         for (int J = 0; J <= R; ++J) {
           // (P_RJ)^T = K_J Q_R^T: lane holds P[16R + lr][16J + 4lg + s], four adjacent columns
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -567,6 +573,16 @@ __global__ __launch_bounds__((NCH + NHW) * 64) void chunk_state_pipe_kernel(Chun
             acc[s] = (R == J && lr < 4 * lg + s) ? 0.f : val;
           }
           *reinterpret_cast<frag*>(sP + r * LCP + 16 * J + 4 * lg) = O::cvt(acc);
+        }
+      };
+      if constexpr (!CHAN) {
+        for (int R = cw; R < 4; R += NHW) {   // R = cw, cw + NHW, ..
+          switch (R) {
+            case 0: p_row(std::integral_constant<int, 0>()); break;
+            case 1: p_row(std::integral_constant<int, 1>()); break;
+            case 2: p_row(std::integral_constant<int, 2>()); break;
+            default: p_row(std::integral_constant<int, 3>()); break;
+          }
         }
       }
       // next chunk into the other LDS copy (last read before this step's opening
