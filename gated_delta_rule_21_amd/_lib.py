@@ -24,7 +24,8 @@ FORMS = {"page": 0, "literal": 1}
 
 EXPORTED = ("gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_chunk_fwd_varlen_workspace_size",
             "gdr_chunk_fwd_varlen", "gdr_recurrent_step", "gdr_chunk_fwd_wkey", "gdr_recurrent_step_wkey",
-            "gdr_precond_scan", "gdr_status_string", "gdr_last_error", "gdr_version")
+            "gdr_precond_scan", "gdr_status_string", "gdr_last_error", "gdr_version",
+            "gdr_chunk_bwd_workspace_size", "gdr_chunk_bwd")
 
 
 class GdrDesc(ctypes.Structure):
@@ -74,6 +75,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         lib.gdr_precond_scan.restype = ctypes.c_int
         lib.gdr_precond_scan.argtypes = [ctypes.POINTER(GdrDesc), vp, vp, vp, ctypes.c_float, vp, vp, vp, vp]
         lib.gdr_status_string.restype = ctypes.c_char_p
+        lib.gdr_chunk_bwd_workspace_size.restype = ctypes.c_int
+        lib.gdr_chunk_bwd_workspace_size.argtypes = [ctypes.POINTER(GdrDesc), ctypes.POINTER(ctypes.c_size_t)]
+        lib.gdr_chunk_bwd.restype = ctypes.c_int
+        lib.gdr_chunk_bwd.argtypes = [ctypes.POINTER(GdrDesc)] + [vp] * 15 + [ctypes.c_size_t, vp]
         lib.gdr_status_string.argtypes = [ctypes.c_int]
         lib.gdr_last_error.restype = ctypes.c_char_p
         lib.gdr_last_error.argtypes = []
@@ -189,6 +194,58 @@ def chunk_fwd(q, k, v, beta, log_a=None, S0=None, *, form: str = "page", o=None,
                            _ptr(o), _ptr(S_T), _ptr(workspace), workspace.numel(), _stream_handle(stream))
     _check(lib, st)
     return o, S_T
+
+
+def chunk_bwd_workspace_size(B: int, T: int, H: int, d_k: int, d_v: int, dtype=torch.bfloat16,
+                             gate: str = "scalar") -> int:
+    """Bytes of scratch gdr_chunk_bwd needs for these sizes (gdr_chunk_bwd_workspace_size)."""
+    lib = load()
+    io = 1 if dtype == torch.bfloat16 else 0
+    desc = GdrDesc(B, T, H, d_k, d_v, 64, io, GATES[gate], 0)
+    n = ctypes.c_size_t(0)
+    _check(lib, lib.gdr_chunk_bwd_workspace_size(ctypes.byref(desc), ctypes.byref(n)))
+    return int(n.value)
+
+
+def chunk_bwd(q, k, v, beta, log_a, S0, dO, dS_T=None, *, want_dS0: bool = True, workspace=None, stream=None):
+    """gdr_chunk_bwd on torch tensors: the gradients of L = <dO, o> + <dS_T, S_T> for
+    the forward chunk_fwd(q, k, v, beta, log_a, S0) (bf16 I/O, no gate or a scalar
+    gate, decay before the erase).  dO [B, T, H, d_v] bf16; dS_T None or
+    [B, H, d_k, d_v] float32.  Returns dict(dq, dk, dv, dbeta, dlog_a, dS0) (dlog_a
+    None without a gate, dS0 None when want_dS0 is False).  Asynchronous on the
+    current (or given) stream."""
+    lib = load()
+    B, T, H, dk = k.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    _require(q, "q", dt, (B, T, H, dk))
+    _require(k, "k", dt, (B, T, H, dk))
+    _require(v, "v", dt, (B, T, H, dv))
+    _require(beta, "beta", dt, (B, T, H))
+    _require(dO, "dO", dt, (B, T, H, dv))
+    gate = _gate_of(log_a, beta.shape, k.shape)
+    if log_a is not None:
+        _require(log_a, "log_a", dt, tuple(log_a.shape))
+    if S0 is not None:
+        _require(S0, "S0", torch.float32, (B, H, dk, dv))
+    if dS_T is not None:
+        _require(dS_T, "dS_T", torch.float32, (B, H, dk, dv))
+    out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v), dbeta=torch.empty_like(beta),
+               dlog_a=torch.empty_like(log_a) if log_a is not None else None,
+               dS0=torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device) if want_dS0 else None)
+    desc = GdrDesc(B, T, H, dk, dv, 64, _io_of(q), gate, 0)
+    need = ctypes.c_size_t(0)
+    _check(lib, lib.gdr_chunk_bwd_workspace_size(ctypes.byref(desc), ctypes.byref(need)))
+    if workspace is None:
+        workspace = torch.empty(max(int(need.value), 1), dtype=torch.uint8, device=q.device)
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous() or workspace.device != q.device:
+        raise ValueError("workspace must be a contiguous uint8 tensor on the inputs' device")
+    st = lib.gdr_chunk_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_a), _ptr(S0), _ptr(dO),
+                           _ptr(dS_T), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dbeta"]),
+                           _ptr(out["dlog_a"]), _ptr(out["dS0"]), _ptr(workspace), workspace.numel(),
+                           _stream_handle(stream))
+    _check(lib, st)
+    return out
 
 
 def chunk_varlen_workspace_size(T: int, n_seq: int, H: int, d_k: int, d_v: int, dtype=torch.bfloat16,

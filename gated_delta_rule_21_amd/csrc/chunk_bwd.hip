@@ -1,0 +1,861 @@
+// Backward pass of the chunkwise gated delta rule on gfx950: bf16 I/O, no gate or a
+// scalar gate, decay before the erase.
+//
+// The pages print no gradients; these are the reverse-mode derivatives of the
+// chunk form of "Moonshot AI's New Attention Architecture: Key Innovations
+// Explained", §3 Hardware-Friendly Algorithm (and §5: the gate stays in the log
+// domain).  Per chunk (rows r = 0..63, g_r the running sum of log a inside the
+// chunk, D_rj = e^{g_r - g_j}, S the state entering the chunk, dS' the gradient of
+// the state leaving it, dO the gradient of the output):
+//   forward   X = V - diag(e^g) K S,   Delta = T diag(beta) X,   T = (I + A)^{-1},
+//             A = strict_lower(diag(beta) D * K K^T),   P = lower_incl(D * Q K^T),
+//             O = diag(e^g) Q S + P Delta,   S' = e^{g_63} S + K^T diag(e^{g_63 - g}) Delta
+//   reverse   dDelta = P^T dO + diag(e^{g_63 - g}) K dS',   dY = T^T dDelta,
+//             dS = e^{g_63} dS' + Q^T diag(e^g) dO - K^T diag(beta e^g) dY
+//   per chunk dv = diag(beta) dY,   dA = -strict_lower(dY Delta^T),   dP = lower_incl(dO Delta^T),
+//             dq = (D * dP) K + diag(e^g) dO S^T,
+//             dk = (beta D * dA) K + (beta D * dA)^T K + (D * dP)^T Q
+//                  - diag(beta e^g) dY S^T + diag(e^{g_63 - g}) Delta dS'^T,
+//             dbeta_r = sum_v dY X + sum_j dA_rj D_rj (K K^T)_rj,
+//             dg_r = (row sums - column sums of dA * A and dP * P)_r
+//                    - beta_r e^{g_r} k_r . (dY S^T)_r + e^{g_r} q_r . (dO S^T)_r - c_r,
+//             c_r = e^{g_63 - g_r} k_r . (Delta dS'^T)_r,   dg_63 += sum_r c_r + e^{g_63} <dS', S>,
+//             d log a_s = sum_{r >= s} dg_r.
+//
+// Three passes follow the per-chunk transform (chunk_prep.hip, which gives T and
+// the gate factors of every chunk):
+//   1. the states entering each chunk, in order (one workgroup per (sequence,
+//      head, 64 state columns); the state in MFMA accumulators, as in the forward);
+//   2. the gradients of the states leaving each chunk, in reverse order (the same
+//      shape of work, dS in accumulators);
+//   3. every chunk at once: the gradients of q, k, v, beta and log a.
+// Passes 1 and 2 store the states in bf16, the precision the forward's products
+// read them in, value-major ([d_v][d_k] per chunk) so that an accumulator lane
+// writes four adjacent values.
+//
+// Operand fragments (16x16 MFMA tiles, lane l: lr = l % 16, lg = l / 16):
+//   rowf(M, ld, x0, k0) = M[x0 + lr][k0 + 4 lg + s]   (8-byte LDS read)
+//   colf(M, ld, k0, x0) = M[k0 + 4 lg + s][x0 + lr]   (LDS transpose read)
+// For C = A B an A fragment is A[m0 + lr][k0 + 4 lg + s] and a B fragment
+// B[k0 + 4 lg + s][n0 + lr].  mma(a, b) leaves C[m0 + 4 lg + s][n0 + lr] in the lane
+// (the "column" form, whose tiles feed the next product as B fragments); mma(b, a)
+// leaves C[m0 + lr][n0 + 4 lg + s] (the "row" form: one row per lane, four adjacent
+// columns, written with one 8-byte store).
+#include "chunk_common.h"
+#include "launchers.h"
+
+namespace gdr {
+
+namespace {
+
+typedef Op<IO_BF16> O;
+typedef __bf16 T;
+typedef bf16x4 frag;
+typedef WsRec<2> W;
+
+__device__ __forceinline__ frag rowf(const T* m, int ld, int x0, int k0, int lr, int lg) {
+  return O::ld(m + (x0 + lr) * ld + k0 + 4 * lg);
+}
+__device__ __forceinline__ frag colf(const T* m, int ld, int k0, int x0, int lr, int lg) {
+  return O::ld_tr(m, ld, k0, x0, lr, lg);
+}
+__device__ __forceinline__ void st_row(T* m, int ld, int r, int c, f32x4 x) {
+  *reinterpret_cast<frag*>(m + r * ld + c) = to_bf16x4(x);
+}
+__device__ __forceinline__ void buf_store2(uint16_t x, rsrc_t r, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b16(x, r, voff, soff, 0);
+}
+__device__ __forceinline__ u32x2 bits8(f32x4 x) { return __builtin_bit_cast(u32x2, to_bf16x4(x)); }
+
+// Workgroup -> (sequence, head, tile): consecutive logical blocks on one XCD (block
+// ids are dealt round-robin over the 8 XCDs), so the tiles of one head share an L2.
+__device__ __forceinline__ int logical_block() {
+  const int nblk = gridDim.x;
+  int lb = blockIdx.x;
+  if ((nblk & 7) == 0) lb = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
+  return lb;
+}
+
+// ---------------------------------------------------------------------------
+// Passes 1 and 2: the sequential passes.  Four waves, 16 state columns each.
+// LDS: two copies of one chunk's tiles (k, q, a 64-column v or dO tile, T^T, the
+// gate factors), and P of the current chunk (pass 2).
+// ---------------------------------------------------------------------------
+template <int DK>
+struct SeqLayout {
+  static constexpr int LDK = DK + 8;
+  static constexpr int LDV = 64 + 8;
+  static constexpr int LCT = CH + 8;
+  static constexpr size_t KB = size_t(CH) * LDK * 2;
+  static constexpr size_t VB = size_t(CH) * LDV * 2;
+  static constexpr size_t TB = size_t(CH) * LCT * 2;
+  static constexpr size_t O_K = 0, O_Q = O_K + KB, O_V = O_Q + KB, O_T = O_V + VB, O_F = O_T + TB;
+  static constexpr size_t BUF = O_F + 6 * CH * 4;
+  static constexpr size_t O_P = 2 * BUF;
+  static constexpr size_t TOTAL = O_P + TB;
+};
+
+// One chunk's tiles in registers, then into one LDS copy: k (and q), the 64-column
+// tile of v (or dO) from column col0, the T blocks and the factor rows of the record.
+template <int DK, int NT, bool WITH_Q>
+struct SeqStage {
+  typedef SeqLayout<DK> L;
+  static constexpr int KR = DK / 8;                  // 16-byte pieces per k row
+  static constexpr int KP = CH * KR / NT;            // per thread
+  static constexpr int VP = CH * 8 / NT;
+  static constexpr int TP = (10 * 32 + NT - 1) / NT; // T blocks: 32 pieces each
+  static_assert(KP * NT == CH * KR && VP * NT == CH * 8, "tile pieces split evenly");
+  u32x4 k[KP], q[WITH_Q ? KP : 1], v[VP], t[TP], f;
+
+  __device__ __forceinline__ void load(rsrc_t rk, rsrc_t rq, rsrc_t rv, rsrc_t rw, int64_t n, int tid, int H,
+                                       int dv, int col0) {
+    const uint32_t sk = static_cast<uint32_t>(n * CH * H * DK * 2);
+    const uint32_t sv = static_cast<uint32_t>(n * CH * H * dv * 2);
+    const uint32_t sw = static_cast<uint32_t>(n * W::BYTES);
+#pragma unroll
+    for (int i = 0; i < KP; ++i) {
+      const int pc = tid + i * NT;
+      const uint32_t off = static_cast<uint32_t>(((pc / KR) * H * DK + (pc % KR) * 8) * 2);
+      k[i] = buf_load16(rk, off, sk);
+      if constexpr (WITH_Q) q[i] = buf_load16(rq, off, sk);
+    }
+#pragma unroll
+    for (int i = 0; i < VP; ++i) {
+      const int pc = tid + i * NT;
+      v[i] = buf_load16(rv, static_cast<uint32_t>(((pc / 8) * H * dv + col0 + (pc % 8) * 8) * 2), sv);
+    }
+#pragma unroll
+    for (int i = 0; i < TP; ++i) {
+      const int pc = tid + i * NT;
+      if (pc < 320) t[i] = buf_load16(rw, W::T_OFF + static_cast<uint32_t>(pc * 16), sw);
+    }
+    if (tid < 96) f = buf_load16(rw, W::F_OFF + static_cast<uint32_t>(tid * 16), sw);
+  }
+
+  __device__ __forceinline__ void store(char* base, int tid) const {
+    T* dK = reinterpret_cast<T*>(base + L::O_K);
+    T* dQ = reinterpret_cast<T*>(base + L::O_Q);
+    T* dV = reinterpret_cast<T*>(base + L::O_V);
+    T* dT = reinterpret_cast<T*>(base + L::O_T);
+#pragma unroll
+    for (int i = 0; i < KP; ++i) {
+      const int pc = tid + i * NT;
+      *reinterpret_cast<u32x4*>(dK + (pc / KR) * L::LDK + (pc % KR) * 8) = k[i];
+      if constexpr (WITH_Q) *reinterpret_cast<u32x4*>(dQ + (pc / KR) * L::LDK + (pc % KR) * 8) = q[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VP; ++i) {
+      const int pc = tid + i * NT;
+      *reinterpret_cast<u32x4*>(dV + (pc / 8) * L::LDV + (pc % 8) * 8) = v[i];
+    }
+#pragma unroll
+    for (int i = 0; i < TP; ++i) {
+      const int pc = tid + i * NT;
+      if (pc < 320) {                    // block u holds (T_RJ)^T: the T^T tile, blocks on or above the diagonal
+        int R, J;
+        tri_block(pc / 32, R, J);
+        const int a = (pc % 32) / 2, b0 = (pc % 2) * 8;
+        *reinterpret_cast<u32x4*>(dT + (16 * J + a) * L::LCT + 16 * R + b0) = t[i];
+      }
+    }
+    if (tid < 96) *reinterpret_cast<u32x4*>(base + L::O_F + tid * 16) = f;
+  }
+};
+
+// Buffers over one (sequence, head) slice of a [B, T, H, width] tensor; the range
+// ends after the last token, so rows past it read as zero and their stores drop.
+struct Slice {
+  int64_t row0;
+  uint32_t span;
+  __device__ __forceinline__ rsrc_t rs(const void* base, int width) const {
+    return make_rsrc(static_cast<const uint16_t*>(base) + row0 * width, span * width * 2);
+  }
+};
+__device__ __forceinline__ Slice slice_of(const ChunkParams& f, int64_t bb, int64_t hh) {
+  return Slice{bb * f.T * f.H + hh, static_cast<uint32_t>(f.T > 0 ? (f.T - 1) * f.H + 1 : 0)};
+}
+
+// Pass 1: the state entering every chunk, stored in bf16 value-major.
+template <int GATE, int DK>
+__global__ __launch_bounds__(256) void bwd_states_kernel(BwdParams p, int n_tiles) {
+  typedef SeqLayout<DK> L;
+  constexpr int DKT = DK / 16, LDK = L::LDK, LDV = L::LDV, LCT = L::LCT;
+  __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
+  const ChunkParams& f = p.f;
+  const int lb = logical_block();
+  const int64_t bh = lb / n_tiles;
+  const int tile = lb % n_tiles;
+  const int64_t bb = bh / f.H, hh = bh % f.H;
+  const int dv = f.d_v, H = static_cast<int>(f.H), col0 = tile * 64;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int scol = col0 + 16 * wave + lr;
+  const int64_t nch = (f.T + CH - 1) / CH;
+  const Slice sl = slice_of(f, bb, hh);
+  const rsrc_t rk = sl.rs(f.k, DK), rv = sl.rs(f.v, dv);
+  const rsrc_t rw = make_rsrc(static_cast<const char*>(f.ws) + bh * nch * W::BYTES, static_cast<uint32_t>(nch * W::BYTES));
+  const uint32_t sbytes = static_cast<uint32_t>(dv * DK * 2);   // one chunk's state
+  const rsrc_t rst = make_rsrc(static_cast<char*>(p.states) + bh * nch * sbytes, static_cast<uint32_t>(nch * sbytes));
+
+  f32x4 S[DKT];   // S[t][s] = S[16t + 4lg + s][scol]
+#pragma unroll
+  for (int t = 0; t < DKT; ++t)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) S[t][s] = f.S0 ? f.S0[(bh * DK + 16 * t + 4 * lg + s) * dv + scol] : 0.f;
+
+  SeqStage<DK, 256, false> st;
+  if (nch > 0) {
+    st.load(rk, rk, rv, rw, 0, tid, H, dv, col0);
+    st.store(smem, tid);
+    if (nch > 1) st.load(rk, rk, rv, rw, 1, tid, H, dv, col0);
+  }
+  __syncthreads();
+  for (int64_t n = 0; n < nch; ++n) {
+    const char* cur = smem + (n & 1) * L::BUF;
+    const T* sK = reinterpret_cast<const T*>(cur + L::O_K);
+    const T* sV = reinterpret_cast<const T*>(cur + L::O_V);
+    const T* sT = reinterpret_cast<const T*>(cur + L::O_T);
+    const float* sF = reinterpret_cast<const float*>(cur + L::O_F);
+    if (n + 1 < nch) {   // the other copy was last read before the previous barrier
+      st.store(smem + ((n + 1) & 1) * L::BUF, tid);
+      if (n + 2 < nch) st.load(rk, rk, rv, rw, n + 2, tid, H, dv, col0);
+    }
+    const uint32_t so = static_cast<uint32_t>(n) * sbytes;
+#pragma unroll
+    for (int t = 0; t < DKT; ++t) buf_store8(bits8(S[t]), rst, static_cast<uint32_t>((scol * DK + 16 * t + 4 * lg) * 2), so);
+
+    frag Sb[DKT];
+#pragma unroll
+    for (int t = 0; t < DKT; ++t) Sb[t] = O::cvt(S[t]);
+    frag Rb[4];
+#pragma unroll
+    for (int R = 0; R < 4; ++R) {        // diag(beta) X, X = V - diag(e^g) K S
+      f32x4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < DK / 32; ++kb)
+        x = O::mma2(x, rowf(sK, LDK, 16 * R, 32 * kb, lr, lg), rowf(sK, LDK, 16 * R, 32 * kb + 16, lr, lg),
+                    Sb[2 * kb], Sb[2 * kb + 1]);
+      const f32x4 vv = O::f32(colf(sV, LDV, 16 * R, 16 * wave, lr, lg));
+      f32x4 rr;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int r = 16 * R + 4 * lg + s;
+        rr[s] = sF[r] * (vv[s] - (GATE == GATE_SCALAR ? x[s] * sF[CH + r] : x[s]));
+      }
+      Rb[R] = O::cvt(rr);
+    }
+    frag Ds[4];
+#pragma unroll
+    for (int R = 0; R < 4; ++R) {        // Delta = T diag(beta) X, rows of T from T^T; then e^{g_63 - g}
+      f32x4 d = {0.f, 0.f, 0.f, 0.f};
+      int m = 0;
+#pragma unroll
+      for (; m + 1 <= R; m += 2)
+        d = O::mma2(d, colf(sT, LCT, 16 * m, 16 * R, lr, lg), colf(sT, LCT, 16 * (m + 1), 16 * R, lr, lg), Rb[m],
+                    Rb[m + 1]);
+      if (m <= R) d = O::mma1(d, colf(sT, LCT, 16 * m, 16 * R, lr, lg), Rb[m]);
+      if constexpr (GATE == GATE_SCALAR) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) d[s] *= sF[3 * CH + 16 * R + 4 * lg + s];
+      }
+      Ds[R] = O::cvt(d);
+    }
+#pragma unroll
+    for (int t = 0; t < DKT; ++t) {      // S' = e^{g_63} S + K^T (e^{g_63 - g} Delta)
+      f32x4 acc = S[t];
+      if constexpr (GATE == GATE_SCALAR) acc = acc * sF[4 * CH];
+      acc = O::mma2(acc, colf(sK, LDK, 0, 16 * t, lr, lg), colf(sK, LDK, 16, 16 * t, lr, lg), Ds[0], Ds[1]);
+      acc = O::mma2(acc, colf(sK, LDK, 32, 16 * t, lr, lg), colf(sK, LDK, 48, 16 * t, lr, lg), Ds[2], Ds[3]);
+      S[t] = acc;
+    }
+    __syncthreads();
+  }
+}
+
+// Pass 2: the gradient of the state leaving every chunk, last chunk first, and dS0.
+template <int GATE, int DK>
+__global__ __launch_bounds__(256) void bwd_reverse_kernel(BwdParams p, int n_tiles) {
+  typedef SeqLayout<DK> L;
+  constexpr int DKT = DK / 16, LDK = L::LDK, LDV = L::LDV, LCT = L::LCT;
+  __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
+  const ChunkParams& f = p.f;
+  const int lb = logical_block();
+  const int64_t bh = lb / n_tiles;
+  const int tile = lb % n_tiles;
+  const int64_t bb = bh / f.H, hh = bh % f.H;
+  const int dv = f.d_v, H = static_cast<int>(f.H), col0 = tile * 64;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int scol = col0 + 16 * wave + lr;
+  const int64_t nch = (f.T + CH - 1) / CH;
+  const Slice sl = slice_of(f, bb, hh);
+  const rsrc_t rk = sl.rs(f.k, DK), rq = sl.rs(f.q, DK), rdo = sl.rs(p.dO, dv);
+  const rsrc_t rw = make_rsrc(static_cast<const char*>(f.ws) + bh * nch * W::BYTES, static_cast<uint32_t>(nch * W::BYTES));
+  const uint32_t sbytes = static_cast<uint32_t>(dv * DK * 2);
+  const rsrc_t rds = make_rsrc(static_cast<char*>(p.dstates) + bh * nch * sbytes, static_cast<uint32_t>(nch * sbytes));
+  T* sP = reinterpret_cast<T*>(smem + L::O_P);
+
+  f32x4 dS[DKT];   // dS[t][s] = dS[16t + 4lg + s][scol]
+#pragma unroll
+  for (int t = 0; t < DKT; ++t)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) dS[t][s] = p.dS_T ? p.dS_T[(bh * DK + 16 * t + 4 * lg + s) * dv + scol] : 0.f;
+
+  SeqStage<DK, 256, true> st;
+  if (nch > 0) {
+    st.load(rk, rq, rdo, rw, nch - 1, tid, H, dv, col0);
+    st.store(smem + ((nch - 1) & 1) * L::BUF, tid);
+    if (nch > 1) st.load(rk, rq, rdo, rw, nch - 2, tid, H, dv, col0);
+  }
+  __syncthreads();
+  for (int64_t n = nch - 1; n >= 0; --n) {
+    const char* cur = smem + (n & 1) * L::BUF;
+    const T* sK = reinterpret_cast<const T*>(cur + L::O_K);
+    const T* sQ = reinterpret_cast<const T*>(cur + L::O_Q);
+    const T* sO = reinterpret_cast<const T*>(cur + L::O_V);
+    const T* sT = reinterpret_cast<const T*>(cur + L::O_T);
+    const float* sF = reinterpret_cast<const float*>(cur + L::O_F);
+    if (n >= 1) {        // the other copy (chunk n + 1) was last read before the previous barrier
+      st.store(smem + ((n - 1) & 1) * L::BUF, tid);
+      if (n >= 2) st.load(rk, rq, rdo, rw, n - 2, tid, H, dv, col0);
+    }
+    // P of this chunk, blocks u = wave, wave + 4, .. (row form: row 16R + lr)
+    for (int u = wave; u < 10; u += 4) {
+      int R, J;
+      tri_block(u, R, J);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < DK / 32; ++kb)
+        acc = O::mma2(acc, rowf(sK, LDK, 16 * J, 32 * kb, lr, lg), rowf(sK, LDK, 16 * J, 32 * kb + 16, lr, lg),
+                      rowf(sQ, LDK, 16 * R, 32 * kb, lr, lg), rowf(sQ, LDK, 16 * R, 32 * kb + 16, lr, lg));
+      const int r = 16 * R + lr;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int j = 16 * J + 4 * lg + s;
+        float x = j <= r ? acc[s] : 0.f;
+        if constexpr (GATE == GATE_SCALAR) x *= __expf(fminf(sF[5 * CH + r] - sF[5 * CH + j], 0.f));
+        acc[s] = x;
+      }
+      st_row(sP, LCT, r, 16 * J + 4 * lg, acc);
+    }
+    __syncthreads();
+
+    const uint32_t so = static_cast<uint32_t>(n) * sbytes;
+#pragma unroll
+    for (int t = 0; t < DKT; ++t) buf_store8(bits8(dS[t]), rds, static_cast<uint32_t>((scol * DK + 16 * t + 4 * lg) * 2), so);
+
+    frag dSb[DKT];
+#pragma unroll
+    for (int t = 0; t < DKT; ++t) dSb[t] = O::cvt(dS[t]);
+    frag dOf[4], dOg[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      dOf[kb] = colf(sO, LDV, 16 * kb, 16 * wave, lr, lg);
+      if constexpr (GATE == GATE_SCALAR) {
+        f32x4 x = O::f32(dOf[kb]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) x[s] *= sF[2 * CH + 16 * kb + 4 * lg + s];
+        dOg[kb] = O::cvt(x);
+      } else {
+        dOg[kb] = dOf[kb];
+      }
+    }
+    frag dDb[4];
+#pragma unroll
+    for (int M = 0; M < 4; ++M) {        // dDelta = diag(e^{g_63 - g}) K dS' + P^T dO
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < DK / 32; ++kb)
+        acc = O::mma2(acc, rowf(sK, LDK, 16 * M, 32 * kb, lr, lg), rowf(sK, LDK, 16 * M, 32 * kb + 16, lr, lg),
+                      dSb[2 * kb], dSb[2 * kb + 1]);
+      if constexpr (GATE == GATE_SCALAR) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc[s] *= sF[3 * CH + 16 * M + 4 * lg + s];
+      }
+      int kb = M;
+#pragma unroll
+      for (; kb + 1 <= 3; kb += 2)
+        acc = O::mma2(acc, colf(sP, LCT, 16 * kb, 16 * M, lr, lg), colf(sP, LCT, 16 * (kb + 1), 16 * M, lr, lg),
+                      dOf[kb], dOf[kb + 1]);
+      if (kb <= 3) acc = O::mma1(acc, colf(sP, LCT, 16 * kb, 16 * M, lr, lg), dOf[kb]);
+      dDb[M] = O::cvt(acc);
+    }
+    frag Zb[4];
+#pragma unroll
+    for (int M = 0; M < 4; ++M) {        // dY = T^T dDelta; Z = -diag(beta e^g) dY
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      int kb = M;
+#pragma unroll
+      for (; kb + 1 <= 3; kb += 2)
+        acc = O::mma2(acc, rowf(sT, LCT, 16 * M, 16 * kb, lr, lg), rowf(sT, LCT, 16 * M, 16 * (kb + 1), lr, lg),
+                      dDb[kb], dDb[kb + 1]);
+      if (kb <= 3) acc = O::mma1(acc, rowf(sT, LCT, 16 * M, 16 * kb, lr, lg), dDb[kb]);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int r = 16 * M + 4 * lg + s;
+        acc[s] *= -(GATE == GATE_SCALAR ? sF[r] * sF[CH + r] : sF[r]);
+      }
+      Zb[M] = O::cvt(acc);
+    }
+#pragma unroll
+    for (int t = 0; t < DKT; ++t) {      // dS = e^{g_63} dS' + Q^T diag(e^g) dO + K^T Z
+      f32x4 acc = dS[t];
+      if constexpr (GATE == GATE_SCALAR) acc = acc * sF[4 * CH];
+      acc = O::mma2(acc, colf(sQ, LDK, 0, 16 * t, lr, lg), colf(sQ, LDK, 16, 16 * t, lr, lg), dOg[0], dOg[1]);
+      acc = O::mma2(acc, colf(sQ, LDK, 32, 16 * t, lr, lg), colf(sQ, LDK, 48, 16 * t, lr, lg), dOg[2], dOg[3]);
+      acc = O::mma2(acc, colf(sK, LDK, 0, 16 * t, lr, lg), colf(sK, LDK, 16, 16 * t, lr, lg), Zb[0], Zb[1]);
+      acc = O::mma2(acc, colf(sK, LDK, 32, 16 * t, lr, lg), colf(sK, LDK, 48, 16 * t, lr, lg), Zb[2], Zb[3]);
+      dS[t] = acc;
+    }
+    __syncthreads();
+  }
+  if (p.dS0) {
+#pragma unroll
+    for (int t = 0; t < DKT; ++t)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) p.dS0[(bh * DK + 16 * t + 4 * lg + s) * dv + scol] = dS[t][s];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Pass 3: one workgroup of eight waves per chunk.  The d_v columns are taken in
+// halves of 64 (the products over d_v accumulate across them).
+// ---------------------------------------------------------------------------
+template <int DK>
+struct ChunkLayout {
+  static constexpr int LDK = DK + 8;   // q, k, and the value-major states S^T, dS'^T
+  static constexpr int LDV = 64 + 8;   // 64-column tiles
+  static constexpr int LCP = CH + 8;   // 64 x 64 matrices
+  static constexpr size_t KB = size_t(CH) * LDK * 2;
+  static constexpr size_t VB = size_t(CH) * LDV * 2;
+  static constexpr size_t CB = size_t(CH) * LCP * 2;
+  static constexpr size_t O_Q = 0, O_K = O_Q + KB, O_T = O_K + KB, O_F = O_T + CB;
+  static constexpr size_t O_P = O_F + 6 * CH * 4;    // P, then D * dP
+  static constexpr size_t O_AK = O_P + CB;           // beta D * dA
+  static constexpr size_t O_V = O_AK + CB;           // v half, then diag(beta) X
+  static constexpr size_t O_DO = O_V + VB;
+  static constexpr size_t O_DD = O_DO + VB;          // dDelta
+  static constexpr size_t O_DL = O_DD + VB;          // Delta
+  static constexpr size_t O_DY = O_DL + VB;          // dY
+  static constexpr size_t O_S = O_DY + VB;           // S^T half [64][DK]
+  static constexpr size_t O_DS = O_S + KB;           // dS'^T half
+  static constexpr size_t O_RED = O_DS + KB;         // dbeta[64], dg[64], <dS', S>
+  static constexpr size_t TOTAL = O_RED + (2 * CH + 4) * 4;
+};
+
+template <int GATE, int DK>
+__global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdParams p) {
+  typedef ChunkLayout<DK> L;
+  constexpr int NT = 512, NW = 8;
+  constexpr int DKT = DK / 16, LDK = L::LDK, LDV = L::LDV, LCP = L::LCP;
+  constexpr int KR = DK / 8, KP = CH * KR / NT;     // pieces of a [64][DK] tile per thread
+  static_assert(KP * NT == CH * KR, "tile pieces split evenly");
+  static_assert(L::TOTAL <= 163840, "LDS budget");
+  constexpr bool G = GATE == GATE_SCALAR;
+  __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
+  T* sQ = reinterpret_cast<T*>(smem + L::O_Q);
+  T* sK = reinterpret_cast<T*>(smem + L::O_K);
+  T* sT = reinterpret_cast<T*>(smem + L::O_T);
+  const float* sF = reinterpret_cast<const float*>(smem + L::O_F);
+  T* sP = reinterpret_cast<T*>(smem + L::O_P);
+  T* sAk = reinterpret_cast<T*>(smem + L::O_AK);
+  T* sV = reinterpret_cast<T*>(smem + L::O_V);
+  T* sdO = reinterpret_cast<T*>(smem + L::O_DO);
+  T* sdD = reinterpret_cast<T*>(smem + L::O_DD);
+  T* sDl = reinterpret_cast<T*>(smem + L::O_DL);
+  T* sdY = reinterpret_cast<T*>(smem + L::O_DY);
+  T* sS = reinterpret_cast<T*>(smem + L::O_S);
+  T* sdS = reinterpret_cast<T*>(smem + L::O_DS);
+  float* sdb = reinterpret_cast<float*>(smem + L::O_RED);
+  float* sdg = sdb + CH;
+  float* sred = sdg + CH;
+
+  const ChunkParams& f = p.f;
+  const int64_t nch = (f.T + CH - 1) / CH;
+  const int64_t lb = blockIdx.x;
+  const int64_t n = lb % nch, bh = lb / nch;
+  const int64_t bb = bh / f.H, hh = bh % f.H;
+  const int dv = f.d_v, H = static_cast<int>(f.H);
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const Slice sl = slice_of(f, bb, hh);
+  const rsrc_t rq = sl.rs(f.q, DK), rk = sl.rs(f.k, DK), rv = sl.rs(f.v, dv), rdo = sl.rs(p.dO, dv);
+  const rsrc_t rdq = sl.rs(p.dq, DK), rdk = sl.rs(p.dk, DK), rdv = sl.rs(p.dv, dv);
+  const rsrc_t rdb = sl.rs(p.dbeta, 1), rdl = sl.rs(p.dlog_a, G ? 1 : 0);
+  const rsrc_t rw = make_rsrc(static_cast<const char*>(f.ws) + bh * nch * W::BYTES, static_cast<uint32_t>(nch * W::BYTES));
+  const uint32_t sbytes = static_cast<uint32_t>(dv * DK * 2);
+  const rsrc_t rst = make_rsrc(static_cast<const char*>(p.states) + bh * nch * sbytes, static_cast<uint32_t>(nch * sbytes));
+  const rsrc_t rds = make_rsrc(static_cast<const char*>(p.dstates) + bh * nch * sbytes, static_cast<uint32_t>(nch * sbytes));
+  const uint32_t sk = static_cast<uint32_t>(n * CH * H * DK * 2);   // chunk start in q, k (bytes)
+  const uint32_t sv = static_cast<uint32_t>(n * CH * H * dv * 2);   // ... in v, dO
+  const uint32_t sw = static_cast<uint32_t>(n * W::BYTES);
+  const uint32_t ss = static_cast<uint32_t>(n) * sbytes;
+  const uint32_t sb = static_cast<uint32_t>(n * CH * H * 2);        // ... in beta, log a
+  const int nhalf = dv / 64;
+
+  // ---- staging: q, k, T, factors; the first d_v half of v, dO, S^T, dS'^T ----------
+  u32x4 hv, hdo, hs[KP], hds[KP];
+  float sdot = 0.f;                     // this thread's part of <dS', S>
+  auto load_half = [&](int h) __attribute__((always_inline)) {
+    hv = buf_load16(rv, static_cast<uint32_t>(((tid / 8) * H * dv + 64 * h + (tid % 8) * 8) * 2), sv);
+    hdo = buf_load16(rdo, static_cast<uint32_t>(((tid / 8) * H * dv + 64 * h + (tid % 8) * 8) * 2), sv);
+#pragma unroll
+    for (int i = 0; i < KP; ++i) {
+      const int pc = tid + i * NT;
+      const uint32_t off = static_cast<uint32_t>((64 * h * DK + pc * 8) * 2);
+      hs[i] = buf_load16(rst, off, ss);
+      hds[i] = buf_load16(rds, off, ss);
+    }
+  };
+  auto store_half = [&]() __attribute__((always_inline)) {
+    *reinterpret_cast<u32x4*>(sV + (tid / 8) * LDV + (tid % 8) * 8) = hv;
+    *reinterpret_cast<u32x4*>(sdO + (tid / 8) * LDV + (tid % 8) * 8) = hdo;
+#pragma unroll
+    for (int i = 0; i < KP; ++i) {
+      const int pc = tid + i * NT;
+      *reinterpret_cast<u32x4*>(sS + (pc / KR) * LDK + (pc % KR) * 8) = hs[i];
+      *reinterpret_cast<u32x4*>(sdS + (pc / KR) * LDK + (pc % KR) * 8) = hds[i];
+      if constexpr (G) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t a = hs[i][j], b = hds[i][j];
+          sdot += bf16_bits_to_f32(a & 0xffffu) * bf16_bits_to_f32(b & 0xffffu) +
+                  bf16_bits_to_f32(a >> 16) * bf16_bits_to_f32(b >> 16);
+        }
+      }
+    }
+  };
+  {
+    u32x4 hq[KP], hk[KP], ht, hf;
+#pragma unroll
+    for (int i = 0; i < KP; ++i) {
+      const int pc = tid + i * NT;
+      const uint32_t off = static_cast<uint32_t>(((pc / KR) * H * DK + (pc % KR) * 8) * 2);
+      hq[i] = buf_load16(rq, off, sk);
+      hk[i] = buf_load16(rk, off, sk);
+    }
+    if (tid < 320) ht = buf_load16(rw, W::T_OFF + static_cast<uint32_t>(tid * 16), sw);
+    if (tid < 96) hf = buf_load16(rw, W::F_OFF + static_cast<uint32_t>(tid * 16), sw);
+    load_half(0);
+#pragma unroll
+    for (int i = 0; i < KP; ++i) {
+      const int pc = tid + i * NT;
+      *reinterpret_cast<u32x4*>(sQ + (pc / KR) * LDK + (pc % KR) * 8) = hq[i];
+      *reinterpret_cast<u32x4*>(sK + (pc / KR) * LDK + (pc % KR) * 8) = hk[i];
+    }
+    if (tid < 320) {
+      int R, J;
+      tri_block(tid / 32, R, J);
+      const int a = (tid % 32) / 2, b0 = (tid % 2) * 8;
+      *reinterpret_cast<u32x4*>(sT + (16 * J + a) * LCP + 16 * R + b0) = ht;
+    }
+    if (tid < 96) *reinterpret_cast<u32x4*>(smem + L::O_F + tid * 16) = hf;
+    if (tid < 2 * CH + 4) sdb[tid] = 0.f;
+    store_half();
+  }
+  __syncthreads();
+  if (nhalf > 1) load_half(1);
+
+  // ---- the wave's blocks of the 64 x 64 matrices: u = wave, wave + 8 (< 10) -------
+  constexpr int NU = 2;
+  f32x4 Gr[NU], QKr[NU], dAa[NU], dPa[NU];
+#pragma unroll
+  for (int i = 0; i < NU; ++i) {
+    const int u = wave + NW * i;
+    Gr[i] = QKr[i] = dAa[i] = dPa[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (u < 10) {
+      int R, J;
+      tri_block(u, R, J);
+#pragma unroll
+      for (int kb = 0; kb < DK / 32; ++kb) {
+        const frag b0 = rowf(sK, LDK, 16 * J, 32 * kb, lr, lg), b1 = rowf(sK, LDK, 16 * J, 32 * kb + 16, lr, lg);
+        Gr[i] = O::mma2(Gr[i], b0, b1, rowf(sK, LDK, 16 * R, 32 * kb, lr, lg), rowf(sK, LDK, 16 * R, 32 * kb + 16, lr, lg));
+        QKr[i] = O::mma2(QKr[i], b0, b1, rowf(sQ, LDK, 16 * R, 32 * kb, lr, lg), rowf(sQ, LDK, 16 * R, 32 * kb + 16, lr, lg));
+      }
+      const int r = 16 * R + lr;
+      f32x4 pv;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int j = 16 * J + 4 * lg + s;
+        float x = j <= r ? QKr[i][s] : 0.f;
+        if constexpr (G) x *= __expf(fminf(sF[5 * CH + r] - sF[5 * CH + j], 0.f));
+        pv[s] = x;
+      }
+      st_row(sP, LCP, r, 16 * J + 4 * lg, pv);
+    }
+  }
+  __syncthreads();
+
+  // ---- per d_v half -------------------------------------------------------------------
+  constexpr int NX = (4 * DKT) / NW;    // 64 x d_k tiles per wave
+  f32x4 dYS[NX], dOS[NX], DdS[NX];
+#pragma unroll
+  for (int i = 0; i < NX; ++i) dYS[i] = dOS[i] = DdS[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float dbx[2] = {0.f, 0.f};            // sum_v dY X for rows 16 M_i + lr
+  for (int h = 0; h < nhalf; ++h) {
+    if (h > 0) {
+      store_half();
+      __syncthreads();
+    }
+    // X = V - diag(e^g) K S (kept), diag(beta) X over the v tile; dDelta = diag(e^{g_63 - g}) K dS' + P^T dO
+    f32x4 Xr[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int t = wave + NW * i, M = t >> 2, c = t & 3;
+      const int r = 16 * M + lr;
+      f32x4 ks = {0.f, 0.f, 0.f, 0.f}, kd = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < DK / 32; ++kb) {
+        const frag a0 = rowf(sK, LDK, 16 * M, 32 * kb, lr, lg), a1 = rowf(sK, LDK, 16 * M, 32 * kb + 16, lr, lg);
+        ks = O::mma2(ks, rowf(sS, LDK, 16 * c, 32 * kb, lr, lg), rowf(sS, LDK, 16 * c, 32 * kb + 16, lr, lg), a0, a1);
+        kd = O::mma2(kd, rowf(sdS, LDK, 16 * c, 32 * kb, lr, lg), rowf(sdS, LDK, 16 * c, 32 * kb + 16, lr, lg), a0, a1);
+      }
+      const f32x4 vv = O::f32(O::ld(sV + r * LDV + 16 * c + 4 * lg));
+      const float er = G ? sF[2 * CH + r] : 1.f;
+      Xr[i] = vv - ks * er;
+      st_row(sV, LDV, r, 16 * c + 4 * lg, Xr[i] * sF[r]);
+      if constexpr (G) kd = kd * sF[3 * CH + r];
+      int kb = M;
+      for (; kb + 1 <= 3; kb += 2)
+        kd = O::mma2(kd, colf(sdO, LDV, 16 * kb, 16 * c, lr, lg), colf(sdO, LDV, 16 * (kb + 1), 16 * c, lr, lg),
+                     colf(sP, LCP, 16 * kb, 16 * M, lr, lg), colf(sP, LCP, 16 * (kb + 1), 16 * M, lr, lg));
+      if (kb <= 3) kd = O::mma1(kd, colf(sdO, LDV, 16 * kb, 16 * c, lr, lg), colf(sP, LCP, 16 * kb, 16 * M, lr, lg));
+      st_row(sdD, LDV, r, 16 * c + 4 * lg, kd);
+    }
+    __syncthreads();
+    // Delta = T diag(beta) X, dY = T^T dDelta; dv = diag(beta) dY
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int t = wave + NW * i, M = t >> 2, c = t & 3;
+      const int r = 16 * M + lr;
+      f32x4 dl = {0.f, 0.f, 0.f, 0.f}, dy = {0.f, 0.f, 0.f, 0.f};
+      int kb = 0;
+      for (; kb + 1 <= M; kb += 2)
+        dl = O::mma2(dl, colf(sV, LDV, 16 * kb, 16 * c, lr, lg), colf(sV, LDV, 16 * (kb + 1), 16 * c, lr, lg),
+                     colf(sT, LCP, 16 * kb, 16 * M, lr, lg), colf(sT, LCP, 16 * (kb + 1), 16 * M, lr, lg));
+      if (kb <= M) dl = O::mma1(dl, colf(sV, LDV, 16 * kb, 16 * c, lr, lg), colf(sT, LCP, 16 * kb, 16 * M, lr, lg));
+      kb = M;
+      for (; kb + 1 <= 3; kb += 2)
+        dy = O::mma2(dy, colf(sdD, LDV, 16 * kb, 16 * c, lr, lg), colf(sdD, LDV, 16 * (kb + 1), 16 * c, lr, lg),
+                     rowf(sT, LCP, 16 * M, 16 * kb, lr, lg), rowf(sT, LCP, 16 * M, 16 * (kb + 1), lr, lg));
+      if (kb <= 3) dy = O::mma1(dy, colf(sdD, LDV, 16 * kb, 16 * c, lr, lg), rowf(sT, LCP, 16 * M, 16 * kb, lr, lg));
+      buf_store8(bits8(dy * sF[r]), rdv, static_cast<uint32_t>((r * H * dv + 64 * h + 16 * c + 4 * lg) * 2), sv);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) dbx[i] += dy[s] * Xr[i][s];
+      st_row(sDl, LDV, r, 16 * c + 4 * lg, dl);
+      st_row(sdY, LDV, r, 16 * c + 4 * lg, dy);
+    }
+    __syncthreads();
+    // dA += dY Delta^T, dP += dO Delta^T on the wave's blocks; dY S^T, dO S^T, Delta dS'^T
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+      const int u = wave + NW * i;
+      if (u < 10) {
+        int R, J;
+        tri_block(u, R, J);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const frag b0 = rowf(sDl, LDV, 16 * J, 32 * kb, lr, lg), b1 = rowf(sDl, LDV, 16 * J, 32 * kb + 16, lr, lg);
+          dAa[i] = O::mma2(dAa[i], b0, b1, rowf(sdY, LDV, 16 * R, 32 * kb, lr, lg), rowf(sdY, LDV, 16 * R, 32 * kb + 16, lr, lg));
+          dPa[i] = O::mma2(dPa[i], b0, b1, rowf(sdO, LDV, 16 * R, 32 * kb, lr, lg), rowf(sdO, LDV, 16 * R, 32 * kb + 16, lr, lg));
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NX; ++i) {
+      const int t = wave + NW * i, M = t / DKT, ic = t % DKT;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const frag bs0 = colf(sS, LDK, 32 * kb, 16 * ic, lr, lg), bs1 = colf(sS, LDK, 32 * kb + 16, 16 * ic, lr, lg);
+        const frag bd0 = colf(sdS, LDK, 32 * kb, 16 * ic, lr, lg), bd1 = colf(sdS, LDK, 32 * kb + 16, 16 * ic, lr, lg);
+        dYS[i] = O::mma2(dYS[i], bs0, bs1, rowf(sdY, LDV, 16 * M, 32 * kb, lr, lg), rowf(sdY, LDV, 16 * M, 32 * kb + 16, lr, lg));
+        dOS[i] = O::mma2(dOS[i], bs0, bs1, rowf(sdO, LDV, 16 * M, 32 * kb, lr, lg), rowf(sdO, LDV, 16 * M, 32 * kb + 16, lr, lg));
+        DdS[i] = O::mma2(DdS[i], bd0, bd1, rowf(sDl, LDV, 16 * M, 32 * kb, lr, lg), rowf(sDl, LDV, 16 * M, 32 * kb + 16, lr, lg));
+      }
+    }
+    if (h + 1 < nhalf) {
+      __syncthreads();                  // every read of this half's tiles is done
+      if (h + 2 < nhalf) load_half(h + 2);
+    }
+  }
+
+  // ---- beta D * dA and D * dP; dbeta and the row / column sums of dA*A and dP*P --------
+#pragma unroll
+  for (int i = 0; i < NU; ++i) {
+    const int u = wave + NW * i;
+    if (u < 10) {
+      int R, J;
+      tri_block(u, R, J);
+      const int r = 16 * R + lr;
+      const float br = sF[r];
+      f32x4 ak, pk;
+      float db = 0.f, rsum = 0.f;
+      float csum[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int j = 16 * J + 4 * lg + s;
+        const float D = G ? __expf(fminf(sF[5 * CH + r] - sF[5 * CH + j], 0.f)) : 1.f;
+        const float dA = j < r ? -dAa[i][s] : 0.f;
+        const float dP = j <= r ? dPa[i][s] : 0.f;
+        ak[s] = br * D * dA;
+        pk[s] = D * dP;
+        db += dA * D * Gr[i][s];
+        const float e = ak[s] * Gr[i][s] + pk[s] * QKr[i][s];   // dA * A + dP * P
+        rsum += e;
+        csum[s] = e;
+      }
+      st_row(sAk, LCP, r, 16 * J + 4 * lg, ak);
+      st_row(sP, LCP, r, 16 * J + 4 * lg, pk);
+      atomicAdd(&sdb[r], db);
+      if constexpr (G) {
+        atomicAdd(&sdg[r], rsum);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          float x = csum[s];
+          x += __shfl_xor(x, 1);
+          x += __shfl_xor(x, 2);
+          x += __shfl_xor(x, 4);
+          x += __shfl_xor(x, 8);
+          if (lr == 0) atomicAdd(&sdg[16 * J + 4 * lg + s], -x);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int M = (wave + NW * i) >> 2;
+    float x = dbx[i];
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    if (lg == 0) atomicAdd(&sdb[16 * M + lr], x);
+  }
+  if constexpr (G) {
+    float x = sdot;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) x += __shfl_xor(x, d);
+    if (lane == 0) atomicAdd(sred, x);
+  }
+  __syncthreads();
+
+  // ---- dk, dq ---------------------------------------------------------------------------
+  float csum = 0.f;
+#pragma unroll
+  for (int i = 0; i < NX; ++i) {
+    const int t = wave + NW * i, M = t / DKT, ic = t % DKT;
+    const int r = 16 * M + lr;
+    f32x4 gk = {0.f, 0.f, 0.f, 0.f}, gq = {0.f, 0.f, 0.f, 0.f};
+    for (int kb = 0; kb <= M; ++kb) {   // (beta D dA) K, (D dP) K: blocks on or left of the diagonal
+      const frag bk = colf(sK, LDK, 16 * kb, 16 * ic, lr, lg);
+      gk = O::mma1(gk, bk, rowf(sAk, LCP, 16 * M, 16 * kb, lr, lg));
+      gq = O::mma1(gq, bk, rowf(sP, LCP, 16 * M, 16 * kb, lr, lg));
+    }
+    for (int kb = M; kb < 4; ++kb) {    // (beta D dA)^T K + (D dP)^T Q: blocks on or below it
+      gk = O::mma1(gk, colf(sK, LDK, 16 * kb, 16 * ic, lr, lg), colf(sAk, LCP, 16 * kb, 16 * M, lr, lg));
+      gk = O::mma1(gk, colf(sQ, LDK, 16 * kb, 16 * ic, lr, lg), colf(sP, LCP, 16 * kb, 16 * M, lr, lg));
+    }
+    const float br = sF[r];
+    const float eg = G ? sF[2 * CH + r] : 1.f, ed = G ? sF[3 * CH + r] : 1.f;
+    const f32x4 dk = gk - dYS[i] * (br * eg) + DdS[i] * ed;
+    const f32x4 dq = gq + dOS[i] * eg;
+    const uint32_t off = static_cast<uint32_t>((r * H * DK + 16 * ic + 4 * lg) * 2);
+    buf_store8(bits8(dk), rdk, off, sk);
+    buf_store8(bits8(dq), rdq, off, sk);
+    if constexpr (G) {
+      const f32x4 kk = O::f32(O::ld(sK + r * LDK + 16 * ic + 4 * lg));
+      const f32x4 qq = O::f32(O::ld(sQ + r * LDK + 16 * ic + 4 * lg));
+      float a = 0.f, c = 0.f;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        a += eg * (qq[s] * dOS[i][s] - br * kk[s] * dYS[i][s]);
+        c += ed * kk[s] * DdS[i][s];
+      }
+      a -= c;
+      a += __shfl_xor(a, 16);
+      a += __shfl_xor(a, 32);
+      if (lg == 0) atomicAdd(&sdg[r], a);
+      csum += c;
+    }
+  }
+  if constexpr (G) {
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) csum += __shfl_xor(csum, d);
+    if (lane == 0) atomicAdd(&sdg[CH - 1], csum);
+  }
+  __syncthreads();
+
+  // ---- dbeta, d log a (suffix sums of dg over the chunk) ------------------------------
+  if (wave == 0) {
+    const uint32_t off = static_cast<uint32_t>(lane * H * 2);
+    buf_store2(f32_to_bf16_bits(sdb[lane]), rdb, off, sb);
+    if constexpr (G) {
+      float x = sdg[lane];
+      if (lane == CH - 1) x += sF[4 * CH] * sred[0];
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const float y = __shfl_down(x, d);
+        if (lane + d < 64) x += y;
+      }
+      buf_store2(f32_to_bf16_bits(x), rdl, off, sb);
+    }
+  }
+}
+
+// dS0 for sequences of no tokens: the incoming gradient (or zero) passes through.
+__global__ void bwd_copy_state_kernel(const float* src, float* dst, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = src ? src[i] : 0.f;
+}
+
+template <int GATE, int DK>
+hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
+  const ChunkParams& f = p.f;
+  const int64_t nch = (f.T + CH - 1) / CH;
+  const int n_tiles = f.d_v / 64;
+  const int64_t nseq = f.B * f.H * n_tiles;
+  hipLaunchKernelGGL((bwd_states_kernel<GATE, DK>), dim3(static_cast<unsigned>(nseq)), dim3(256), 0, stream, p, n_tiles);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_reverse_kernel<GATE, DK>), dim3(static_cast<unsigned>(nseq)), dim3(256), 0, stream, p, n_tiles);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_chunk_kernel<GATE, DK>), dim3(static_cast<unsigned>(f.B * f.H * nch)), dim3(512), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int GATE>
+hipError_t launch_bwd_g(const BwdParams& p, hipStream_t stream) {
+  if (p.f.d_k == 128) return launch_bwd_t<GATE, 128>(p, stream);
+  if (p.f.d_k == 64) return launch_bwd_t<GATE, 64>(p, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+size_t chunk_bwd_state_bytes(int64_t B, int64_t T, int64_t H, int d_k, int d_v) {
+  return static_cast<size_t>(B * H * ((T + CH - 1) / CH)) * static_cast<size_t>(d_k) * static_cast<size_t>(d_v) * 2u;
+}
+
+size_t chunk_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int d_k, int d_v) {
+  return chunk_workspace_bytes(B, T, H, IO_BF16, GATE_SCALAR, d_k) + 2 * chunk_bwd_state_bytes(B, T, H, d_k, d_v);
+}
+
+hipError_t launch_chunk_bwd(const BwdParams& p, hipStream_t stream) {
+  const ChunkParams& f = p.f;
+  if (f.B * f.H == 0) return hipSuccess;
+  if (f.io != IO_BF16 || f.literal || f.cu || f.kw || (f.gate != GATE_NONE && f.gate != GATE_SCALAR))
+    return hipErrorInvalidValue;
+  if (f.T == 0) {
+    if (!p.dS0) return hipSuccess;
+    const int64_t n = f.B * f.H * f.d_k * f.d_v;
+    hipLaunchKernelGGL(bwd_copy_state_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream, p.dS_T,
+                       p.dS0, n);
+    return hipGetLastError();
+  }
+  hipError_t e = launch_chunk_prep(f, stream);
+  if (e != hipSuccess) return e;
+  return f.gate == GATE_SCALAR ? launch_bwd_g<GATE_SCALAR>(p, stream) : launch_bwd_g<GATE_NONE>(p, stream);
+}
+
+}  // namespace gdr

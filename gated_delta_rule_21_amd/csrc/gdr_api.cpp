@@ -82,6 +82,21 @@ gdr_status check_desc(const gdr_desc* d, bool decode) {
   return GDR_OK;
 }
 
+// The backward: the forward's checks, then what this version implements.
+gdr_status check_bwd_desc(const gdr_desc* d) {
+  gdr_status st = check_desc(d, false);
+  if (st != GDR_OK) return st;
+  if (d->io != GDR_BF16) return fail(GDR_ERR_UNSUPPORTED, "chunk backward: bf16 I/O only");
+  if (d->gate == GDR_GATE_CHANNEL) return fail(GDR_ERR_UNSUPPORTED, "chunk backward: no per-channel gate");
+  if (d->gate == GDR_GATE_SCALAR && d->form == GDR_FORM_LITERAL)
+    return fail(GDR_ERR_UNSUPPORTED, "chunk backward: decay before the erase (GDR_FORM_PAGE) only");
+  // one (sequence, head)'s chunk states are addressed with 32-bit byte offsets
+  const int64_t per_seq = ((d->T + 63) / 64) * d->d_k * d->d_v * 2;
+  if (per_seq > INT32_MAX)
+    return fail(GDR_ERR_UNSUPPORTED, "T = %lld: the per-sequence chunk states exceed 2^31 - 1 bytes", (long long)d->T);
+  return GDR_OK;
+}
+
 gdr_status check_align(const char* name, const void* p, uintptr_t a) {
   if (p && (reinterpret_cast<uintptr_t>(p) % a) != 0)
     return fail(GDR_ERR_ALIGNMENT, "%s = %p is not %u-byte aligned", name, p, (unsigned)a);
@@ -383,6 +398,88 @@ gdr_status gdr_chunk_fwd_wkey(const gdr_desc* d, const void* q, const void* k, c
     if (d && d->io != GDR_BF16) return fail(GDR_ERR_UNSUPPORTED, "write key chunk forward: bf16 I/O only");
     return chunk_fwd_impl(d, nullptr, 0, q, k, v, beta, nullptr, S0, o, S_T, workspace, workspace_bytes, stream,
                           kw);
+  } catch (...) {
+    return fail(GDR_ERR_INVALID_ARG, "internal error");
+  }
+}
+
+
+gdr_status gdr_chunk_bwd_workspace_size(const gdr_desc* d, size_t* bytes) {
+  try {
+    g_last_error.clear();
+    if (!bytes) return fail(GDR_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = 0;
+    gdr_status st = check_bwd_desc(d);
+    if (st != GDR_OK) return st;
+    *bytes = d->T > 0 ? gdr::chunk_bwd_workspace_bytes(d->B, d->T, d->H, static_cast<int>(d->d_k), static_cast<int>(d->d_v)) : 0;
+    return GDR_OK;
+  } catch (...) {
+    return fail(GDR_ERR_INVALID_ARG, "internal error");
+  }
+}
+
+gdr_status gdr_chunk_bwd(const gdr_desc* d, const void* q, const void* k, const void* v, const void* beta,
+                         const void* log_a, const float* S0, const void* dO, const float* dS_T, void* dq, void* dk,
+                         void* dv, void* dbeta, void* dlog_a, float* dS0, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  try {
+    g_last_error.clear();
+    gdr_status st = check_bwd_desc(d);
+    if (st != GDR_OK) return st;
+    const bool gated = d->gate == GDR_GATE_SCALAR;
+    const size_t ws_need =
+        d->T > 0 ? gdr::chunk_bwd_workspace_bytes(d->B, d->T, d->H, static_cast<int>(d->d_k), static_cast<int>(d->d_v)) : 0;
+    if (d->T > 0) {
+      const void* req[] = {q, k, v, beta, dO, dq, dk, dv, dbeta};
+      const char* names[] = {"q", "k", "v", "beta", "dO", "dq", "dk", "dv", "dbeta"};
+      for (int i = 0; i < 9; ++i)
+        if (!req[i]) return fail(GDR_ERR_INVALID_ARG, "%s is NULL", names[i]);
+      if (gated && !log_a) return fail(GDR_ERR_INVALID_ARG, "log_a is NULL but a gate is requested");
+      if (gated && !dlog_a) return fail(GDR_ERR_INVALID_ARG, "dlog_a is NULL but a gate is requested");
+      if (!workspace) return fail(GDR_ERR_INVALID_ARG, "workspace is NULL (%zu bytes needed)", ws_need);
+      if (workspace_bytes < ws_need)
+        return fail(GDR_ERR_INVALID_ARG, "workspace_bytes = %zu, %zu needed", workspace_bytes, ws_need);
+    }
+    if (!gated && log_a) return fail(GDR_ERR_INVALID_ARG, "log_a must be NULL for GDR_GATE_NONE");
+    if (!gated && dlog_a) return fail(GDR_ERR_INVALID_ARG, "dlog_a must be NULL for GDR_GATE_NONE");
+    if ((st = check_align("q", q, 16)) || (st = check_align("k", k, 16)) || (st = check_align("v", v, 16)) ||
+        (st = check_align("dO", dO, 16)) || (st = check_align("dq", dq, 16)) || (st = check_align("dk", dk, 16)) ||
+        (st = check_align("dv", dv, 16)) || (st = check_align("S0", S0, 16)) || (st = check_align("dS_T", dS_T, 16)) ||
+        (st = check_align("dS0", dS0, 16)) || (st = check_align("beta", beta, 2)) ||
+        (st = check_align("dbeta", dbeta, 2)) || (st = check_align("log_a", log_a, 2)) ||
+        (st = check_align("dlog_a", dlog_a, 2)) || (st = check_align("workspace", workspace, 16)))
+      return st;
+    const int64_t ntok = d->B * d->T * d->H;
+    const int64_t state_bytes = d->B * d->H * d->d_k * d->d_v * 4;
+    Span all[] = {span("q", q, ntok * d->d_k * 2), span("k", k, ntok * d->d_k * 2),
+                  span("v", v, ntok * d->d_v * 2), span("beta", beta, ntok * 2),
+                  span("log_a", log_a, gated ? ntok * 2 : 0), span("S0", S0, state_bytes),
+                  span("dO", dO, ntok * d->d_v * 2), span("dS_T", dS_T, state_bytes),
+                  span("dq", dq, ntok * d->d_k * 2), span("dk", dk, ntok * d->d_k * 2),
+                  span("dv", dv, ntok * d->d_v * 2), span("dbeta", dbeta, ntok * 2),
+                  span("dlog_a", dlog_a, gated ? ntok * 2 : 0), span("dS0", dS0, state_bytes),
+                  span("workspace", d->T > 0 ? workspace : nullptr, static_cast<int64_t>(ws_need))};
+    Span outs[] = {all[8], all[9], all[10], all[11], all[12], all[13], all[14]};
+    if (dS0 && dS0 == dS_T) all[7].hi = all[7].lo;   // the final-state gradient may be overwritten by dS0
+    if ((st = check_no_overlap(outs, 7, all, 15))) return st;
+
+    gdr::BwdParams p;
+    gdr::ChunkParams& f = p.f;
+    f.q = q; f.k = k; f.v = v; f.beta = beta; f.log_a = log_a; f.S0 = S0; f.o = nullptr; f.S_T = nullptr;
+    f.ws = workspace;
+    f.B = d->B; f.T = d->T; f.H = d->H;
+    f.d_k = static_cast<int>(d->d_k); f.d_v = static_cast<int>(d->d_v);
+    f.io = d->io; f.gate = d->gate; f.literal = 0;
+    f.cu = nullptr; f.nslots = 0; f.order = nullptr; f.kw = nullptr;
+    p.dO = dO; p.dS_T = dS_T; p.dq = dq; p.dk = dk; p.dv = dv; p.dbeta = dbeta; p.dlog_a = dlog_a; p.dS0 = dS0;
+    const size_t rec = gdr::chunk_workspace_bytes(d->B, d->T, d->H, d->io, d->gate, static_cast<int>(d->d_k));
+    const size_t sb = gdr::chunk_bwd_state_bytes(d->B, d->T, d->H, static_cast<int>(d->d_k), static_cast<int>(d->d_v));
+    p.states = d->T > 0 ? static_cast<char*>(workspace) + rec : nullptr;
+    p.dstates = d->T > 0 ? static_cast<char*>(workspace) + rec + sb : nullptr;
+    if (d->T == 0 && !dS0) return GDR_OK;
+    hipError_t e = gdr::launch_chunk_bwd(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(GDR_ERR_HIP, "chunk backward launch failed: %s", hipGetErrorString(e));
+    return GDR_OK;
   } catch (...) {
     return fail(GDR_ERR_INVALID_ARG, "internal error");
   }

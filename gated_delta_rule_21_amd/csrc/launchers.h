@@ -54,6 +54,22 @@ struct PrecondParams {
   int d_k, io;
   float eta;
 };
+// Backward of the chunk forward (bf16 I/O, no gate or a scalar gate, decay before
+// the erase): f carries the forward's inputs and the workspace records (f.ws);
+// o, S_T and the packed-sequence fields of f are unused.
+struct BwdParams {
+  ChunkParams f;
+  const void* dO;       // [B, T, H, d_v] gradient of the output
+  const float* dS_T;    // [B, H, d_k, d_v] gradient of the final state, or null (zero)
+  void* dq;             // [B, T, H, d_k]
+  void* dk;             // [B, T, H, d_k]
+  void* dv;             // [B, T, H, d_v]
+  void* dbeta;          // [B, T, H]
+  void* dlog_a;         // [B, T, H] (scalar gate), else unused
+  float* dS0;           // [B, H, d_k, d_v], or null (not written)
+  void* states;         // B H ceil(T/64) chunk-start states, bf16 [d_v][d_k] each
+  void* dstates;        // the gradients of the chunk-end states, same layout
+};
 hipError_t launch_decode_step(const DecodeParams& p, hipStream_t stream);
 // Preconditioner scan: one workgroup per (sequence, head).
 hipError_t launch_precond_scan(const PrecondParams& p, hipStream_t stream);
@@ -70,6 +86,12 @@ size_t chunk_workspace_bytes(int64_t B, int64_t T, int64_t H, int io, int gate, 
 inline int64_t chunk_varlen_slots(int64_t T, int64_t n_seq) { return (T + 63) / 64 + n_seq; }
 size_t chunk_varlen_records_bytes(int64_t T, int64_t n_seq, int64_t H, int io, int gate, int d_k);
 size_t chunk_varlen_workspace_bytes(int64_t T, int64_t n_seq, int64_t H, int io, int gate, int d_k);
+// Backward: the per-chunk transform into p.f.ws, then the three passes.
+hipError_t launch_chunk_bwd(const BwdParams& p, hipStream_t stream);
+// Bytes of one set of per-chunk states (bf16), and of the whole backward workspace:
+// the transform's records, the chunk-start states, the chunk-end state gradients.
+size_t chunk_bwd_state_bytes(int64_t B, int64_t T, int64_t H, int d_k, int d_v);
+size_t chunk_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int d_k, int d_v);
 // Longest-first order of packed sequences into `order` (n_seq int32).
 hipError_t launch_varlen_order(const ChunkParams& p, int32_t* order, hipStream_t stream);
 

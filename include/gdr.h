@@ -274,6 +274,58 @@ gdr_status gdr_recurrent_step_wkey(const gdr_desc* desc, const void* q, const vo
 gdr_status gdr_precond_scan(const gdr_desc* desc, const void* k, const void* beta, const void* r, float eta,
                             const float* d0, void* kw, float* d_T, void* stream /* hipStream_t */);
 
+/*
+ * gdr_chunk_bwd_workspace_size -- device scratch that gdr_chunk_bwd needs.
+ *
+ * Writes to *bytes: the per-chunk records of the forward's workspace (see
+ * gdr_chunk_fwd_workspace_size) plus two bf16 d_k x d_v matrices per (sequence,
+ * head, chunk), that is B * H * ceil(T / 64) * (11776 + 4 * d_k * d_v) bytes (0 when
+ * T == 0).  Returns gdr_chunk_bwd's descriptor errors; *bytes is 0 on error.
+ */
+gdr_status gdr_chunk_bwd_workspace_size(const gdr_desc* desc, size_t* bytes);
+
+/*
+ * gdr_chunk_bwd -- gradients of the chunk forward (training).
+ *
+ * For the forward gdr_chunk_fwd(desc, q, k, v, beta, log_a, S0) with output o and
+ * final state S_T, returns the gradients of the scalar L = <dO, o> + <dS_T, S_T>
+ * with respect to q, k, v, beta, log_a and S0.  The pages print no gradients;
+ * these are the reverse-mode derivatives of the recurrence ("Moonshot AI's New
+ * Attention Architecture", §2) taken through its chunk form (§3): the states
+ * entering each chunk are recomputed in order, the gradients of the states
+ * leaving each chunk are carried in reverse order, and then every chunk forms its
+ * token gradients independently (the transposes of the forward's products and of
+ * its triangular solve).  The forward's outputs are not needed: the call
+ * recomputes what it uses from the inputs.
+ *
+ * Supported: bf16 I/O; GDR_GATE_NONE or GDR_GATE_SCALAR; GDR_FORM_PAGE (with
+ * GDR_GATE_NONE either form, they coincide); d_k, d_v in {64, 128}; fixed-length
+ * batches.  Anything else returns GDR_ERR_UNSUPPORTED.
+ *
+ *   q, k, v, beta, log_a, S0   the forward's inputs, as for gdr_chunk_fwd (log_a
+ *                              NULL for GDR_GATE_NONE; S0 NULL = zero state)
+ *   dO     [B, T, H, d_v] bf16  gradient of o
+ *   dS_T   [B, H, d_k, d_v] fp32 gradient of S_T, or NULL (zero)
+ *   dq, dk [B, T, H, d_k] bf16  written
+ *   dv     [B, T, H, d_v] bf16  written
+ *   dbeta  [B, T, H]      bf16  written
+ *   dlog_a [B, T, H]      bf16  written for GDR_GATE_SCALAR; must be NULL otherwise
+ *   dS0    [B, H, d_k, d_v] fp32 written, or NULL (not computed); may equal dS_T
+ *          (overwritten in place), no other alias is allowed
+ *   workspace / workspace_bytes  scratch of at least gdr_chunk_bwd_workspace_size
+ *          bytes, 16-byte aligned, overwritten
+ *
+ * Precision: bf16 products with fp32 accumulation, the carried state and state
+ * gradient in fp32 (stored per chunk in bf16, the precision the products read
+ * them in); reductions over tokens (dbeta, dlog_a) in fp32.  T == 0 writes dS0 =
+ * dS_T (or zeros).  Errors as for gdr_chunk_fwd; besides, one sequence's chunk
+ * states must stay below 2^31 bytes (ceil(T / 64) * d_k * d_v * 2).
+ */
+gdr_status gdr_chunk_bwd(const gdr_desc* desc, const void* q, const void* k, const void* v, const void* beta,
+                         const void* log_a, const float* S0, const void* dO, const float* dS_T, void* dq, void* dk,
+                         void* dv, void* dbeta, void* dlog_a, float* dS0, void* workspace, size_t workspace_bytes,
+                         void* stream /* hipStream_t */);
+
 #ifdef __cplusplus
 }
 #endif

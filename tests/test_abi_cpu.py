@@ -276,3 +276,61 @@ def test_precond_scan_checks(lib):
     assert _scan(lib, d, k, beta, r, 1.0, d0, kw, d0 + 16) == INVALID           # d_T partly over d0
     assert _scan(lib, d, k, beta, r, 1.0, dT, k + 64, dT) == INVALID            # d_T == d0 is allowed ...
     assert b"kw overlaps k" in lib.gdr_last_error()                             # ... the error is kw's
+
+
+def _bwd(lib, d, p, ws_bytes=1 << 40):
+    """gdr_chunk_bwd with p = (q, k, v, beta, log_a, S0, dO, dS_T, dq, dk, dv, dbeta, dlog_a, dS0, ws)."""
+    return lib.gdr_chunk_bwd(None if d is None else ctypes.byref(d), *p[:14], p[14], ws_bytes, None)
+
+
+def test_backward_workspace_size(lib):
+    n = ctypes.c_size_t(7)
+    d = _desc(B=2, T=130, H=3)
+    assert lib.gdr_chunk_bwd_workspace_size(ctypes.byref(d), ctypes.byref(n)) == OK
+    assert n.value == 2 * 3 * 3 * (11776 + 4 * 128 * 128)
+    assert lib.gdr_chunk_bwd_workspace_size(ctypes.byref(_desc(T=0)), ctypes.byref(n)) == OK and n.value == 0
+    for field, value, code in (("io", 0, UNSUPPORTED), ("gate", 2, UNSUPPORTED), ("d_k", 96, UNSUPPORTED),
+                               ("B", 0, INVALID), ("form", 1, UNSUPPORTED)):
+        n.value = 7
+        assert lib.gdr_chunk_bwd_workspace_size(ctypes.byref(_desc(**{field: value})), ctypes.byref(n)) == code, field
+        assert n.value == 0
+    # no gate: the two forms coincide, so the literal form is accepted
+    assert lib.gdr_chunk_bwd_workspace_size(ctypes.byref(_desc(gate=0, form=1)), ctypes.byref(n)) == OK
+
+
+def test_backward_argument_checks(lib):
+    p = _ptrs(15)
+    d = _desc()
+    assert _bwd(lib, None, p) == INVALID
+    for i, name in enumerate(("q", "k", "v", "beta", "log_a", None, "dO", None, "dq", "dk", "dv", "dbeta", "dlog_a",
+                              None, "workspace")):
+        if name is None:          # S0, dS_T and dS0 may be NULL
+            continue
+        bad = list(p)
+        bad[i] = None
+        assert _bwd(lib, d, bad) == INVALID, name
+        assert name.encode() in lib.gdr_last_error()
+    assert _bwd(lib, d, p, ws_bytes=16) == INVALID                         # workspace too small
+    assert _bwd(lib, _desc(gate=0), p) == INVALID                          # log_a given without a gate
+    bad = list(p)
+    bad[4] = None
+    assert _bwd(lib, _desc(gate=0), bad) == INVALID                        # dlog_a given without a gate
+    for i in (0, 6, 8, 13):                                                # 16-byte operands
+        bad = list(p)
+        bad[i] += 8
+        assert _bwd(lib, d, bad) == ALIGN, i
+    bad = list(p)
+    bad[11] += 1
+    assert _bwd(lib, d, bad) == ALIGN                                      # dbeta: 2 bytes
+    bad = list(p)
+    bad[9] = bad[1] + 64                                                   # dk inside k
+    assert _bwd(lib, d, bad) == INVALID
+    assert b"dk overlaps k" in lib.gdr_last_error()
+    bad = list(p)
+    bad[14] = bad[8] + 256                                                 # workspace over dq
+    assert _bwd(lib, d, bad) == INVALID
+    bad = list(p)
+    bad[13] = bad[7]                                                       # dS0 == dS_T is allowed ...
+    bad[9] = bad[1] + 64
+    assert _bwd(lib, d, bad) == INVALID
+    assert b"dk overlaps k" in lib.gdr_last_error()                        # ... the error is dk's

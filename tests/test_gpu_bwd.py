@@ -1,0 +1,174 @@
+"""GPU parity of gdr_chunk_bwd (the gradients of the chunk forward) against the
+fp64 backward oracle.
+
+The pages print no gradients: the oracle is the reverse mode of the token-by-token
+recurrence ("Moonshot AI's New Attention Architecture", §2), pinned by finite
+differences of the forward oracle; the GPU path takes the same derivatives through
+the chunk form of §3.  The loss is L = <dO, o> + <dS_T, S_T>.
+
+Tolerance: relative L2 over each gradient tensor of 2e-2, as for the forward with
+bf16 I/O (bf16 products with fp32 accumulation; the per-chunk states are read in
+bf16 as the forward's products read them).  Inputs: the forward's workloads, with
+dO ~ N(0, 1) and dS_T ~ N(0, 1).
+"""
+
+import numpy as np
+import pytest
+
+from oracle import backward as oracle_backward
+from tests.gpu_util import TOL, check, dev, host, need_gpu, say
+from workloads import CONFIGS, Workload, chunk_inputs, grad_inputs, grad_slice, slice_inputs
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("dq", "dk", "dv", "dbeta", "dlog_a", "dS0")
+
+
+def _inputs(B, T, H, dk, dv, gate, seed, s0_std=0.5):
+    wl = Workload("bwd", B=B, T=T, H=H, d_k=dk, d_v=dv, io="bf16", gate=gate, s0_std=s0_std, seed=seed)
+    x = chunk_inputs(wl)
+    x.update(grad_inputs(wl))
+    return x
+
+
+def _gpu(x, with_S0=True, with_dST=True, want_dS0=True, in_place=False):
+    import torch
+    import gated_delta_rule_21_amd as gdr
+    S0 = torch.from_numpy(x["S0"]).cuda() if with_S0 else None
+    dS_T = torch.from_numpy(x["dS_T"]).cuda() if with_dST else None
+    g = gdr.chunk_bwd(dev(x["q"], "bf16"), dev(x["k"], "bf16"), dev(x["v"], "bf16"), dev(x["beta"], "bf16"),
+                      dev(x["log_a"], "bf16"), S0, dev(x["dO"], "bf16"), dS_T, want_dS0=want_dS0 and not in_place)
+    if in_place:
+        g = gdr.chunk_bwd(dev(x["q"], "bf16"), dev(x["k"], "bf16"), dev(x["v"], "bf16"), dev(x["beta"], "bf16"),
+                          dev(x["log_a"], "bf16"), S0, dev(x["dO"], "bf16"), dS_T, want_dS0=False)
+        _in_place(x, S0, dS_T)
+        g["dS0"] = dS_T
+    torch.cuda.synchronize()
+    return {n: (host(t) if t is not None else None) for n, t in g.items()}
+
+
+def _in_place(x, S0, dS_T):
+    """dS0 written over dS_T through the C ABI (the binding allocates dS0 itself)."""
+    import ctypes
+    import torch
+    import gated_delta_rule_21_amd as gdr
+    from gated_delta_rule_21_amd._lib import GdrDesc, _ptr
+    lib = gdr.load()
+    q, k, v, beta = (dev(x[n], "bf16") for n in ("q", "k", "v", "beta"))
+    log_a, dO = dev(x["log_a"], "bf16"), dev(x["dO"], "bf16")
+    B, T, H, dk = k.shape
+    dv = v.shape[-1]
+    gate = 0 if log_a is None else 1
+    desc = GdrDesc(B, T, H, dk, dv, 64, 1, gate, 0)
+    need = ctypes.c_size_t(0)
+    assert lib.gdr_chunk_bwd_workspace_size(ctypes.byref(desc), ctypes.byref(need)) == 0
+    ws = torch.empty(max(need.value, 1), dtype=torch.uint8, device="cuda")
+    outs = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), torch.empty_like(beta),
+            torch.empty_like(log_a) if log_a is not None else None]
+    st = lib.gdr_chunk_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_a), _ptr(S0), _ptr(dO),
+                           _ptr(dS_T), *[_ptr(t) for t in outs], _ptr(dS_T), _ptr(ws), ws.numel(), None)
+    assert st == 0, lib.gdr_last_error().decode()
+
+
+def _ref(x, with_S0=True, with_dST=True):
+    return oracle_backward(x["q"], x["k"], x["v"], x["beta"], x["log_a"], x["S0"] if with_S0 else None, x["dO"],
+                           x["dS_T"] if with_dST else None)
+
+
+def _compare(got, ref, gate, skip=()):
+    for n in NAMES:
+        if n in skip or (n == "dlog_a" and gate == "none"):
+            continue
+        check(n, got[n], ref[n], TOL["bf16"])
+
+
+SHAPES = [(2, 200, 3, 128, 128), (1, 130, 2, 64, 64), (2, 100, 2, 128, 64), (1, 70, 2, 64, 128)]
+
+
+@pytest.mark.parametrize("gate", ["scalar", "none"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "B%dT%dH%ddk%ddv%d" % s)
+def test_bwd_shapes(gate, shape):
+    need_gpu()
+    say(f"case bwd gate={gate} shape={shape}")
+    x = _inputs(*shape, gate, seed=sum(shape) + (gate == "scalar"))
+    _compare(_gpu(x), _ref(x), gate)
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 129])
+def test_bwd_lengths(T):
+    need_gpu()
+    say(f"case bwd T={T}")
+    x = _inputs(2, T, 2, 128, 128, "scalar", seed=400 + T)
+    _compare(_gpu(x), _ref(x), "scalar")
+
+
+def test_bwd_without_state_terms():
+    """No initial state and no final-state gradient; dS0 not requested."""
+    need_gpu()
+    x = _inputs(2, 150, 2, 128, 128, "scalar", seed=21)
+    got = _gpu(x, with_S0=False, with_dST=False, want_dS0=False)
+    assert got["dS0"] is None
+    _compare(got, _ref(x, with_S0=False, with_dST=False), "scalar", skip=("dS0",))
+
+
+def test_bwd_dS0_in_place():
+    need_gpu()
+    x = _inputs(1, 140, 2, 128, 128, "scalar", seed=23)
+    _compare(_gpu(x, in_place=True), _ref(x), "scalar")
+
+
+def test_bwd_empty_sequence():
+    """T = 0: dS0 is the final-state gradient (zero without one)."""
+    need_gpu()
+    import torch
+    import gated_delta_rule_21_amd as gdr
+    x = _inputs(2, 0, 2, 128, 128, "scalar", seed=25)
+    g = gdr.chunk_bwd(dev(x["q"], "bf16"), dev(x["k"], "bf16"), dev(x["v"], "bf16"), dev(x["beta"], "bf16"),
+                      dev(x["log_a"], "bf16"), torch.from_numpy(x["S0"]).cuda(), dev(x["dO"], "bf16"),
+                      torch.from_numpy(x["dS_T"]).cuda())
+    g0 = gdr.chunk_bwd(dev(x["q"], "bf16"), dev(x["k"], "bf16"), dev(x["v"], "bf16"), dev(x["beta"], "bf16"),
+                       dev(x["log_a"], "bf16"), None, dev(x["dO"], "bf16"), None)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(g["dS0"]), x["dS_T"].astype(np.float64))
+    assert not np.any(host(g0["dS0"]))
+
+
+def test_bwd_strong_forgetting():
+    """Gates of log a = -20 inside chunks (decay factors far below the fp32 range
+    of e^{-g}): every factor the kernels form is e^{x} with x <= 0."""
+    need_gpu()
+    x = _inputs(2, 200, 2, 128, 128, "scalar", seed=27)
+    x["log_a"][:, 70:75] = -20.0
+    x["log_a"][1, 130] = -20.0
+    _compare(_gpu(x), _ref(x), "scalar")
+
+
+def test_bwd_full_size_sampled():
+    """The gated B8 H16 T8192 d128 bf16 workload at full size, in the launch
+    configuration the benchmark times; three (b, h) slices against the oracle run
+    on that slice alone."""
+    need_gpu()
+    import torch
+    import gated_delta_rule_21_amd as gdr
+    wl = CONFIGS[3]
+    say(f"full-size backward {wl.name}: generating inputs")
+    x = chunk_inputs(wl)
+    x.update(grad_inputs(wl))
+    args = [dev(x[n], "bf16") for n in ("q", "k", "v", "beta", "log_a")]
+    S0 = torch.from_numpy(x["S0"]).cuda()
+    dO, dS_T = dev(x["dO"], "bf16"), torch.from_numpy(x["dS_T"]).cuda()
+    del x
+    say("  running GPU")
+    g = gdr.chunk_bwd(*args, S0, dO, dS_T)
+    torch.cuda.synchronize()
+    for n in NAMES:
+        assert bool(torch.isfinite(g[n].float()).all()), n
+    for b, h in [(0, 0), (wl.B - 1, wl.H - 1), (wl.B // 2, wl.H // 3)]:
+        s = slice_inputs(wl, b, h)
+        s.update(grad_slice(wl, b, h))
+        e = lambda a: None if a is None else a[None, :, None]
+        ref = oracle_backward(e(s["q"]), e(s["k"]), e(s["v"]), e(s["beta"]), e(s["log_a"]), s["S0"][None, None],
+                              e(s["dO"]), s["dS_T"][None, None])
+        for n in ("dq", "dk", "dv", "dbeta", "dlog_a"):
+            check(f"{n}[b={b},h={h}]", host(g[n][b, :, h]), ref[n][0, :, 0], TOL["bf16"])
+        check(f"dS0[b={b},h={h}]", host(g["dS0"][b, h]), ref["dS0"][0, 0], TOL["bf16"])

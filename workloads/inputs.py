@@ -28,6 +28,11 @@ d0 ~ U(0.5, 1.5) (stream SeedSequence([seed, b, h, 3]), float32).  The step
 size is PRECOND_ETA.  The pages give no value for either; these keep d of order
 one over long sequences.
 
+Backward workloads add, per (b, h), the gradients of a loss L = <dO, o> +
+<dS_T, S_T>: dO ~ N(0, 1) as a [T, d_v] array (stream SeedSequence([seed, b, h,
+4]), rounded like the inputs) and dS_T ~ N(0, 1) as [d_k, d_v] float32 (stream
+SeedSequence([seed, b, h, 5])), the scale of the outputs and states they stand for.
+
 Decode workloads draw, per (sequence n, head h), S0 from SeedSequence([seed, n,
 h, 1]) and the token stream from SeedSequence([seed, n, h]) as a [steps,
 2*d_k + d_v + 2] array (row s = step s: q, k, v, beta logit, gate logit).
@@ -43,7 +48,7 @@ import numpy as np
 __all__ = [
     "Workload", "CONFIGS", "DECODE_CONFIG", "round_to_io", "bf16_round",
     "slice_inputs", "chunk_inputs", "decode_slice", "decode_inputs", "PRECOND_ETA",
-    "precond_slice", "precond_inputs", "precond_factors",
+    "precond_slice", "precond_inputs", "precond_factors", "grad_slice", "grad_inputs",
 ]
 
 
@@ -289,3 +294,26 @@ def precond_inputs(wl: Workload, T: Optional[int] = None) -> dict:
             r[b, :, h] = s["r"]
             d0[b, h] = s["d0"]
     return dict(k=k, beta=beta, r=r, d0=d0)
+
+
+def grad_slice(wl: Workload, b: int, h: int, T: Optional[int] = None) -> dict:
+    """Output gradients of one (b, h) slice: dO [T, d_v] (I/O dtype values);
+    dS_T [d_k, d_v] float32."""
+    T = wl.T if T is None else T
+    ro = np.random.Generator(np.random.PCG64(np.random.SeedSequence([wl.seed, b, h, 4])))
+    dO = round_to_io(ro.standard_normal((T, wl.d_v)), wl.io)
+    rs = np.random.Generator(np.random.PCG64(np.random.SeedSequence([wl.seed, b, h, 5])))
+    dS_T = rs.standard_normal((wl.d_k, wl.d_v)).astype(np.float32)
+    return dict(dO=dO, dS_T=dS_T)
+
+
+def grad_inputs(wl: Workload, T: Optional[int] = None) -> dict:
+    """All slices: dO [B, T, H, d_v]; dS_T [B, H, d_k, d_v] float32."""
+    T = wl.T if T is None else T
+    dO = np.empty((wl.B, T, wl.H, wl.d_v), np.float32)
+    dS_T = np.empty((wl.B, wl.H, wl.d_k, wl.d_v), np.float32)
+    for b in range(wl.B):
+        for h in range(wl.H):
+            g = grad_slice(wl, b, h, T)
+            dO[b, :, h], dS_T[b, h] = g["dO"], g["dS_T"]
+    return dict(dO=dO, dS_T=dS_T)
