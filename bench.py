@@ -13,7 +13,8 @@ then decode steps on the states it hands over (`handoff`), and the
 preconditioner scan of the preconditioned delta rule (with forgetting) over the
 workload's keys (`precond_scan`, GB/s against HBM peak), and the chunk forward
 with the write keys it produced (`osdn`: phase 2, no gate, and the two phases'
-tokens/s).
+tokens/s), and the backward of the chunk forward over the same workload
+(`backward`: the gradients of q, k, v, beta, log a and S0 for given dO and dS_T).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
@@ -181,7 +182,7 @@ def bench_chunk(args, log):
     ms = ev0.elapsed_time(ev1) / args.steps
     log(f"chunk forward: {ms:.3f} ms/step (wall {1e3 * wall / args.steps:.3f} ms/step)")
     nbytes, flops = chunk_algorithmic(wl, with_S0=with_S0)
-    return wl, ms, nbytes, flops, (q, k, v, beta)
+    return wl, ms, nbytes, flops, (q, k, v, beta, log_a, S0)
 
 
 def bench_decode(args, log):
@@ -265,6 +266,54 @@ def bench_precond(args, log, wl, k, beta):
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4),
                          "traffic": profiled_traffic("precond_scan_b8h16t8192d128_counters.md", PRECOND_SOURCES)}}
+
+
+def bwd_algorithmic(wl):
+    """Useful flops of the backward per launch: per chunk (C = 64, d = d_k = d_v),
+    the chunk-start states 4 C d^2 + C^2 d (K S, T X, K^T Delta), the reverse pass
+    6 C d^2 + 3 C^2 d (P, K dS', P^T dO, T^T dDelta, Q^T dO, K^T Z) and the
+    per-chunk gradients 10 C d^2 + 11 C^2 d (five state products, eleven 64-row
+    products, the masked ones counted at half)."""
+    C, d = 64, wl.d_k
+    per_chunk = 20 * C * d * d + 15 * C * C * d
+    return wl.B * wl.H * ((wl.T + C - 1) // C) * per_chunk
+
+
+def bench_bwd(args, log, wl, q, k, v, beta, log_a, S0):
+    """The backward of the chunk forward over the same workload, with dO ~ N(0, 1)
+    and dS_T ~ N(0, 1); the gradients of every input and of S0."""
+    import torch
+    import gated_delta_rule_21_amd as gdr
+    from workloads import grad_inputs
+    log("generating the output gradients")
+    g = grad_inputs(wl)
+    dO = torch.from_numpy(g["dO"]).to(torch.bfloat16).cuda()
+    dS_T = torch.from_numpy(g["dS_T"]).cuda()
+    del g
+    ws = torch.empty(gdr.chunk_bwd_workspace_size(wl.B, wl.T, wl.H, wl.d_k, wl.d_v, torch.bfloat16, wl.gate),
+                     dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        return gdr.chunk_bwd(q, k, v, beta, log_a, S0, dO, dS_T, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    flops = bwd_algorithmic(wl)
+    tf = flops / (ms * 1e-3) / 1e12
+    log(f"chunk backward: {ms:.3f} ms/step, {tf:.1f} TFLOP/s useful")
+    return {"workload": wl.name + "_backward", "value": round(wl.B * wl.T / (ms * 1e-3), 1), "unit": "tokens/s",
+            "ms_per_launch": round(ms, 4), "useful_flops_per_launch": flops,
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None}}
 
 
 def bench_wkey(args, log, wl, q, k, v, beta, kw, scan_us):
@@ -383,6 +432,7 @@ def main():
     ap.add_argument("--no-handoff", action="store_true",
                     help="skip the packed-prefill -> decode handoff leg")
     ap.add_argument("--no-precond", action="store_true", help="skip the preconditioner-scan leg")
+    ap.add_argument("--no-bwd", action="store_true", help="skip the backward leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-T", type=int, default=8192)
     ap.add_argument("--cpu-heads", type=int, default=16)
@@ -412,7 +462,7 @@ def main():
     if args.copy_calibration:
         copy_calibration(log)
 
-    wl, ms, nbytes, flops, (q, k, v, beta) = bench_chunk(args, log)
+    wl, ms, nbytes, flops, (q, k, v, beta, log_a, S0) = bench_chunk(args, log)
     tok_s = wl.B * wl.T / (ms * 1e-3)
     gbs = nbytes / (ms * 1e-3) / 1e9
     tflops = flops / (ms * 1e-3) / 1e12
@@ -423,7 +473,8 @@ def main():
         kw, precond = bench_precond(args, log, wl, k, beta)
         osdn = bench_wkey(args, log, wl, q, k, v, beta, kw, precond["us_per_launch"])
         del kw
-    del q, k, v, beta
+    bwd = None if args.no_bwd or wl.gate == "channel" else bench_bwd(args, log, wl, q, k, v, beta, log_a, S0)
+    del q, k, v, beta, log_a, S0
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle sample")
@@ -458,6 +509,7 @@ def main():
         "handoff": handoff,
         "precond_scan": precond,
         "osdn": osdn,
+        "backward": bwd,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

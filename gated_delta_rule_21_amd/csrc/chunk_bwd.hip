@@ -66,6 +66,12 @@ __device__ __forceinline__ void buf_store2(uint16_t x, rsrc_t r, uint32_t voff, 
   __builtin_amdgcn_raw_buffer_store_b16(x, r, voff, soff, 0);
 }
 __device__ __forceinline__ u32x2 bits8(f32x4 x) { return __builtin_bit_cast(u32x2, to_bf16x4(x)); }
+// A 16-byte piece into a tile whose rows are 8-byte aligned: two 8-byte stores.
+__device__ __forceinline__ void put16(T* dst, u32x4 x) {
+  u32x2* d = reinterpret_cast<u32x2*>(dst);
+  d[0] = u32x2{x[0], x[1]};
+  d[1] = u32x2{x[2], x[3]};
+}
 
 // Workgroup -> (sequence, head, tile): consecutive logical blocks on one XCD (block
 // ids are dealt round-robin over the 8 XCDs), so the tiles of one head share an L2.
@@ -76,30 +82,41 @@ __device__ __forceinline__ int logical_block() {
   return lb;
 }
 
+// LDS row strides (bf16 elements) by how a tile is read, after the rates measured
+// for the forward on gfx950: 8-byte row fragments run fastest when a row is 2 or 6
+// (mod 8) dwords long, transpose reads when it is 8 (mod 32) dwords; a tile read both
+// ways takes 6 (mod 8).
+constexpr int ld_row(int w) { return w + 4; }     // rows only
+constexpr int ld_tr(int w) { return w + 16; }     // transposed only (w = 64, 128)
+constexpr int ld_both(int w) { return w + 12; }   // both
+
 // ---------------------------------------------------------------------------
 // Passes 1 and 2: the sequential passes.  Four waves, 16 state columns each.
 // LDS: two copies of one chunk's tiles (k, q, a 64-column v or dO tile, T^T, the
-// gate factors), and P of the current chunk (pass 2).
+// gate factors), and P of the current chunk (pass 2).  Pass 1 reads k both ways,
+// v and T^T transposed; pass 2 reads k and q both ways, dO and P transposed, T^T
+// by rows.
 // ---------------------------------------------------------------------------
-template <int DK>
+template <int DK, bool REV>
 struct SeqLayout {
-  static constexpr int LDK = DK + 8;
-  static constexpr int LDV = 64 + 8;
-  static constexpr int LCT = CH + 8;
+  static constexpr int LDK = ld_both(DK);
+  static constexpr int LDV = ld_tr(64);
+  static constexpr int LCT = REV ? ld_row(CH) : ld_tr(CH);
+  static constexpr int LCP = ld_tr(CH);
   static constexpr size_t KB = size_t(CH) * LDK * 2;
   static constexpr size_t VB = size_t(CH) * LDV * 2;
   static constexpr size_t TB = size_t(CH) * LCT * 2;
-  static constexpr size_t O_K = 0, O_Q = O_K + KB, O_V = O_Q + KB, O_T = O_V + VB, O_F = O_T + TB;
+  static constexpr size_t O_K = 0, O_Q = O_K + KB, O_V = O_Q + (REV ? KB : 0), O_T = O_V + VB, O_F = O_T + TB;
   static constexpr size_t BUF = O_F + 6 * CH * 4;
   static constexpr size_t O_P = 2 * BUF;
-  static constexpr size_t TOTAL = O_P + TB;
+  static constexpr size_t TOTAL = O_P + (REV ? size_t(CH) * LCP * 2 : 0);
 };
 
 // One chunk's tiles in registers, then into one LDS copy: k (and q), the 64-column
 // tile of v (or dO) from column col0, the T blocks and the factor rows of the record.
 template <int DK, int NT, bool WITH_Q>
 struct SeqStage {
-  typedef SeqLayout<DK> L;
+  typedef SeqLayout<DK, WITH_Q> L;
   static constexpr int KR = DK / 8;                  // 16-byte pieces per k row
   static constexpr int KP = CH * KR / NT;            // per thread
   static constexpr int VP = CH * 8 / NT;
@@ -140,13 +157,13 @@ struct SeqStage {
 #pragma unroll
     for (int i = 0; i < KP; ++i) {
       const int pc = tid + i * NT;
-      *reinterpret_cast<u32x4*>(dK + (pc / KR) * L::LDK + (pc % KR) * 8) = k[i];
-      if constexpr (WITH_Q) *reinterpret_cast<u32x4*>(dQ + (pc / KR) * L::LDK + (pc % KR) * 8) = q[i];
+      put16(dK + (pc / KR) * L::LDK + (pc % KR) * 8, k[i]);
+      if constexpr (WITH_Q) put16(dQ + (pc / KR) * L::LDK + (pc % KR) * 8, q[i]);
     }
 #pragma unroll
     for (int i = 0; i < VP; ++i) {
       const int pc = tid + i * NT;
-      *reinterpret_cast<u32x4*>(dV + (pc / 8) * L::LDV + (pc % 8) * 8) = v[i];
+      put16(dV + (pc / 8) * L::LDV + (pc % 8) * 8, v[i]);
     }
 #pragma unroll
     for (int i = 0; i < TP; ++i) {
@@ -155,7 +172,7 @@ struct SeqStage {
         int R, J;
         tri_block(pc / 32, R, J);
         const int a = (pc % 32) / 2, b0 = (pc % 2) * 8;
-        *reinterpret_cast<u32x4*>(dT + (16 * J + a) * L::LCT + 16 * R + b0) = t[i];
+        put16(dT + (16 * J + a) * L::LCT + 16 * R + b0, t[i]);
       }
     }
     if (tid < 96) *reinterpret_cast<u32x4*>(base + L::O_F + tid * 16) = f;
@@ -178,7 +195,7 @@ __device__ __forceinline__ Slice slice_of(const ChunkParams& f, int64_t bb, int6
 // Pass 1: the state entering every chunk, stored in bf16 value-major.
 template <int GATE, int DK>
 __global__ __launch_bounds__(256) void bwd_states_kernel(BwdParams p, int n_tiles) {
-  typedef SeqLayout<DK> L;
+  typedef SeqLayout<DK, false> L;
   constexpr int DKT = DK / 16, LDK = L::LDK, LDV = L::LDV, LCT = L::LCT;
   __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
   const ChunkParams& f = p.f;
@@ -276,8 +293,8 @@ __global__ __launch_bounds__(256) void bwd_states_kernel(BwdParams p, int n_tile
 // Pass 2: the gradient of the state leaving every chunk, last chunk first, and dS0.
 template <int GATE, int DK>
 __global__ __launch_bounds__(256) void bwd_reverse_kernel(BwdParams p, int n_tiles) {
-  typedef SeqLayout<DK> L;
-  constexpr int DKT = DK / 16, LDK = L::LDK, LDV = L::LDV, LCT = L::LCT;
+  typedef SeqLayout<DK, true> L;
+  constexpr int DKT = DK / 16, LDK = L::LDK, LDV = L::LDV, LCT = L::LCT, LCP = L::LCP;
   __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
   const ChunkParams& f = p.f;
   const int lb = logical_block();
@@ -338,7 +355,7 @@ __global__ __launch_bounds__(256) void bwd_reverse_kernel(BwdParams p, int n_til
         if constexpr (GATE == GATE_SCALAR) x *= __expf(fminf(sF[5 * CH + r] - sF[5 * CH + j], 0.f));
         acc[s] = x;
       }
-      st_row(sP, LCT, r, 16 * J + 4 * lg, acc);
+      st_row(sP, LCP, r, 16 * J + 4 * lg, acc);
     }
     __syncthreads();
 
@@ -377,9 +394,9 @@ __global__ __launch_bounds__(256) void bwd_reverse_kernel(BwdParams p, int n_til
       int kb = M;
 #pragma unroll
       for (; kb + 1 <= 3; kb += 2)
-        acc = O::mma2(acc, colf(sP, LCT, 16 * kb, 16 * M, lr, lg), colf(sP, LCT, 16 * (kb + 1), 16 * M, lr, lg),
+        acc = O::mma2(acc, colf(sP, LCP, 16 * kb, 16 * M, lr, lg), colf(sP, LCP, 16 * (kb + 1), 16 * M, lr, lg),
                       dOf[kb], dOf[kb + 1]);
-      if (kb <= 3) acc = O::mma1(acc, colf(sP, LCT, 16 * kb, 16 * M, lr, lg), dOf[kb]);
+      if (kb <= 3) acc = O::mma1(acc, colf(sP, LCP, 16 * kb, 16 * M, lr, lg), dOf[kb]);
       dDb[M] = O::cvt(acc);
     }
     frag Zb[4];
@@ -423,11 +440,15 @@ __global__ __launch_bounds__(256) void bwd_reverse_kernel(BwdParams p, int n_til
 // Pass 3: one workgroup of eight waves per chunk.  The d_v columns are taken in
 // halves of 64 (the products over d_v accumulate across them).
 // ---------------------------------------------------------------------------
+// Every tile here is read both ways except dDelta (transposed only), Delta and dY
+// (rows only).
 template <int DK>
 struct ChunkLayout {
-  static constexpr int LDK = DK + 8;   // q, k, and the value-major states S^T, dS'^T
-  static constexpr int LDV = 64 + 8;   // 64-column tiles
-  static constexpr int LCP = CH + 8;   // 64 x 64 matrices
+  static constexpr int LDK = ld_both(DK);   // q, k, and the value-major states S^T, dS'^T
+  static constexpr int LDV = ld_both(64);   // 64-column tiles: v then diag(beta) X, dO
+  static constexpr int LDD = ld_tr(64);     // dDelta
+  static constexpr int LDR = ld_row(64);    // Delta, dY
+  static constexpr int LCP = ld_both(CH);   // 64 x 64 matrices
   static constexpr size_t KB = size_t(CH) * LDK * 2;
   static constexpr size_t VB = size_t(CH) * LDV * 2;
   static constexpr size_t CB = size_t(CH) * LCP * 2;
@@ -437,20 +458,35 @@ struct ChunkLayout {
   static constexpr size_t O_V = O_AK + CB;           // v half, then diag(beta) X
   static constexpr size_t O_DO = O_V + VB;
   static constexpr size_t O_DD = O_DO + VB;          // dDelta
-  static constexpr size_t O_DL = O_DD + VB;          // Delta
-  static constexpr size_t O_DY = O_DL + VB;          // dY
-  static constexpr size_t O_S = O_DY + VB;           // S^T half [64][DK]
+  static constexpr size_t O_DL = O_DD + size_t(CH) * LDD * 2;   // Delta
+  static constexpr size_t O_DY = O_DL + size_t(CH) * LDR * 2;   // dY
+  static constexpr size_t O_S = O_DY + size_t(CH) * LDR * 2;    // S^T half [64][DK]
   static constexpr size_t O_DS = O_S + KB;           // dS'^T half
   static constexpr size_t O_RED = O_DS + KB;         // dbeta[64], dg[64], <dS', S>
   static constexpr size_t TOTAL = O_RED + (2 * CH + 4) * 4;
 };
 
-template <int GATE, int DK>
+// Sum over the 16 lanes of a row (lanes with one lg), returned to all of them.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp<0x128>(v);   // row_ror:8
+  v += dpp<0x124>(v);   // row_ror:4
+  v += dpp<0x122>(v);   // row_ror:2
+  v += dpp<0x121>(v);   // row_ror:1
+  return v;
+}
+
+// One workgroup per chunk (the LDS admits one per compute unit).
+template <int GATE, int DK, int DV>
 __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdParams p) {
   typedef ChunkLayout<DK> L;
   constexpr int NT = 512, NW = 8;
-  constexpr int DKT = DK / 16, LDK = L::LDK, LDV = L::LDV, LCP = L::LCP;
+  constexpr int DKT = DK / 16, LDK = L::LDK, LDV = L::LDV, LDD = L::LDD, LDR = L::LDR, LCP = L::LCP;
   constexpr int KR = DK / 8, KP = CH * KR / NT;     // pieces of a [64][DK] tile per thread
+  constexpr int NHALF = DV / 64;
   static_assert(KP * NT == CH * KR, "tile pieces split evenly");
   static_assert(L::TOTAL <= 163840, "LDS budget");
   constexpr bool G = GATE == GATE_SCALAR;
@@ -474,62 +510,20 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdParams p) {
 
   const ChunkParams& f = p.f;
   const int64_t nch = (f.T + CH - 1) / CH;
-  const int64_t lb = blockIdx.x;
-  const int64_t n = lb % nch, bh = lb / nch;
-  const int64_t bb = bh / f.H, hh = bh % f.H;
-  const int dv = f.d_v, H = static_cast<int>(f.H);
+  const int H = static_cast<int>(f.H);
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
-  const Slice sl = slice_of(f, bb, hh);
-  const rsrc_t rq = sl.rs(f.q, DK), rk = sl.rs(f.k, DK), rv = sl.rs(f.v, dv), rdo = sl.rs(p.dO, dv);
-  const rsrc_t rdq = sl.rs(p.dq, DK), rdk = sl.rs(p.dk, DK), rdv = sl.rs(p.dv, dv);
-  const rsrc_t rdb = sl.rs(p.dbeta, 1), rdl = sl.rs(p.dlog_a, G ? 1 : 0);
-  const rsrc_t rw = make_rsrc(static_cast<const char*>(f.ws) + bh * nch * W::BYTES, static_cast<uint32_t>(nch * W::BYTES));
-  const uint32_t sbytes = static_cast<uint32_t>(dv * DK * 2);
-  const rsrc_t rst = make_rsrc(static_cast<const char*>(p.states) + bh * nch * sbytes, static_cast<uint32_t>(nch * sbytes));
-  const rsrc_t rds = make_rsrc(static_cast<const char*>(p.dstates) + bh * nch * sbytes, static_cast<uint32_t>(nch * sbytes));
-  const uint32_t sk = static_cast<uint32_t>(n * CH * H * DK * 2);   // chunk start in q, k (bytes)
-  const uint32_t sv = static_cast<uint32_t>(n * CH * H * dv * 2);   // ... in v, dO
-  const uint32_t sw = static_cast<uint32_t>(n * W::BYTES);
-  const uint32_t ss = static_cast<uint32_t>(n) * sbytes;
-  const uint32_t sb = static_cast<uint32_t>(n * CH * H * 2);        // ... in beta, log a
-  const int nhalf = dv / 64;
+  constexpr uint32_t SBYTES = DV * DK * 2;          // one chunk's state
 
-  // ---- staging: q, k, T, factors; the first d_v half of v, dO, S^T, dS'^T ----------
-  u32x4 hv, hdo, hs[KP], hds[KP];
-  float sdot = 0.f;                     // this thread's part of <dS', S>
-  auto load_half = [&](int h) __attribute__((always_inline)) {
-    hv = buf_load16(rv, static_cast<uint32_t>(((tid / 8) * H * dv + 64 * h + (tid % 8) * 8) * 2), sv);
-    hdo = buf_load16(rdo, static_cast<uint32_t>(((tid / 8) * H * dv + 64 * h + (tid % 8) * 8) * 2), sv);
-#pragma unroll
-    for (int i = 0; i < KP; ++i) {
-      const int pc = tid + i * NT;
-      const uint32_t off = static_cast<uint32_t>((64 * h * DK + pc * 8) * 2);
-      hs[i] = buf_load16(rst, off, ss);
-      hds[i] = buf_load16(rds, off, ss);
-    }
-  };
-  auto store_half = [&]() __attribute__((always_inline)) {
-    *reinterpret_cast<u32x4*>(sV + (tid / 8) * LDV + (tid % 8) * 8) = hv;
-    *reinterpret_cast<u32x4*>(sdO + (tid / 8) * LDV + (tid % 8) * 8) = hdo;
-#pragma unroll
-    for (int i = 0; i < KP; ++i) {
-      const int pc = tid + i * NT;
-      *reinterpret_cast<u32x4*>(sS + (pc / KR) * LDK + (pc % KR) * 8) = hs[i];
-      *reinterpret_cast<u32x4*>(sdS + (pc / KR) * LDK + (pc % KR) * 8) = hds[i];
-      if constexpr (G) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t a = hs[i][j], b = hds[i][j];
-          sdot += bf16_bits_to_f32(a & 0xffffu) * bf16_bits_to_f32(b & 0xffffu) +
-                  bf16_bits_to_f32(a >> 16) * bf16_bits_to_f32(b >> 16);
-        }
-      }
-    }
-  };
-  {
-    u32x4 hq[KP], hk[KP], ht, hf;
+  // q, k, the T blocks and the factor rows of one chunk, in registers
+  u32x4 hq[KP], hk[KP], ht, hf;
+  auto load_qk = [&](int64_t task) __attribute__((always_inline)) {
+    const int64_t n = task % nch, bh = task / nch;
+    const Slice sl = slice_of(f, bh / f.H, bh % f.H);
+    const rsrc_t rq = sl.rs(f.q, DK), rk = sl.rs(f.k, DK);
+    const rsrc_t rw = make_rsrc(static_cast<const char*>(f.ws) + bh * nch * W::BYTES, static_cast<uint32_t>(nch * W::BYTES));
+    const uint32_t sk = static_cast<uint32_t>(n * CH * H * DK * 2), sw = static_cast<uint32_t>(n * W::BYTES);
 #pragma unroll
     for (int i = 0; i < KP; ++i) {
       const int pc = tid + i * NT;
@@ -539,266 +533,332 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdParams p) {
     }
     if (tid < 320) ht = buf_load16(rw, W::T_OFF + static_cast<uint32_t>(tid * 16), sw);
     if (tid < 96) hf = buf_load16(rw, W::F_OFF + static_cast<uint32_t>(tid * 16), sw);
-    load_half(0);
+  };
+  {
+    const int64_t task = blockIdx.x;
+    load_qk(task);
+    const int64_t n = task % nch, bh = task / nch;
+    const Slice sl = slice_of(f, bh / f.H, bh % f.H);
+    const rsrc_t rv = sl.rs(f.v, DV), rdo = sl.rs(p.dO, DV);
+    const rsrc_t rdq = sl.rs(p.dq, DK), rdk = sl.rs(p.dk, DK), rdv = sl.rs(p.dv, DV);
+    const rsrc_t rdb = sl.rs(p.dbeta, 1), rdl = sl.rs(p.dlog_a, G ? 1 : 0);
+    const rsrc_t rst = make_rsrc(static_cast<const char*>(p.states) + bh * nch * SBYTES, static_cast<uint32_t>(nch * SBYTES));
+    const rsrc_t rds = make_rsrc(static_cast<const char*>(p.dstates) + bh * nch * SBYTES, static_cast<uint32_t>(nch * SBYTES));
+    const uint32_t sk = static_cast<uint32_t>(n * CH * H * DK * 2);   // chunk start in q, k (bytes)
+    const uint32_t sv = static_cast<uint32_t>(n * CH * H * DV * 2);   // ... in v, dO
+    const uint32_t ss = static_cast<uint32_t>(n) * SBYTES;
+    const uint32_t sb = static_cast<uint32_t>(n * CH * H * 2);        // ... in beta, log a
+
+    // one d_v half of v, dO, S^T, dS'^T
+    u32x4 hv, hdo, hs[KP], hds[KP];
+    float sdot = 0.f;                   // this thread's part of <dS', S>
+    auto load_half = [&](int h) __attribute__((always_inline)) {
+      hv = buf_load16(rv, static_cast<uint32_t>(((tid / 8) * H * DV + 64 * h + (tid % 8) * 8) * 2), sv);
+      hdo = buf_load16(rdo, static_cast<uint32_t>(((tid / 8) * H * DV + 64 * h + (tid % 8) * 8) * 2), sv);
+#pragma unroll
+      for (int i = 0; i < KP; ++i) {
+        const uint32_t off = static_cast<uint32_t>((64 * h * DK + (tid + i * NT) * 8) * 2);
+        hs[i] = buf_load16(rst, off, ss);
+        hds[i] = buf_load16(rds, off, ss);
+      }
+    };
+    auto store_half = [&]() __attribute__((always_inline)) {
+      put16(sV + (tid / 8) * LDV + (tid % 8) * 8, hv);
+      put16(sdO + (tid / 8) * LDV + (tid % 8) * 8, hdo);
+#pragma unroll
+      for (int i = 0; i < KP; ++i) {
+        const int pc = tid + i * NT;
+        put16(sS + (pc / KR) * LDK + (pc % KR) * 8, hs[i]);
+        put16(sdS + (pc / KR) * LDK + (pc % KR) * 8, hds[i]);
+        if constexpr (G) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t a = hs[i][j], b = hds[i][j];
+            sdot += bf16_bits_to_f32(a & 0xffffu) * bf16_bits_to_f32(b & 0xffffu) +
+                    bf16_bits_to_f32(a >> 16) * bf16_bits_to_f32(b >> 16);
+          }
+        }
+      }
+    };
+
+    // ---- q, k, T, factors into LDS; the first d_v half is loaded meanwhile ----------
 #pragma unroll
     for (int i = 0; i < KP; ++i) {
       const int pc = tid + i * NT;
-      *reinterpret_cast<u32x4*>(sQ + (pc / KR) * LDK + (pc % KR) * 8) = hq[i];
-      *reinterpret_cast<u32x4*>(sK + (pc / KR) * LDK + (pc % KR) * 8) = hk[i];
+      put16(sQ + (pc / KR) * LDK + (pc % KR) * 8, hq[i]);
+      put16(sK + (pc / KR) * LDK + (pc % KR) * 8, hk[i]);
     }
     if (tid < 320) {
       int R, J;
       tri_block(tid / 32, R, J);
       const int a = (tid % 32) / 2, b0 = (tid % 2) * 8;
-      *reinterpret_cast<u32x4*>(sT + (16 * J + a) * LCP + 16 * R + b0) = ht;
+      put16(sT + (16 * J + a) * LCP + 16 * R + b0, ht);
     }
     if (tid < 96) *reinterpret_cast<u32x4*>(smem + L::O_F + tid * 16) = hf;
     if (tid < 2 * CH + 4) sdb[tid] = 0.f;
-    store_half();
-  }
-  __syncthreads();
-  if (nhalf > 1) load_half(1);
+    load_half(0);
+    __syncthreads();
 
-  // ---- the wave's blocks of the 64 x 64 matrices: u = wave, wave + 8 (< 10) -------
-  constexpr int NU = 2;
-  f32x4 Gr[NU], QKr[NU], dAa[NU], dPa[NU];
+    // ---- the wave's blocks of the 64 x 64 matrices: u = wave, wave + 8 (< 10) -------
+    constexpr int NU = 2;
+    f32x4 Gr[NU], QKr[NU], dAa[NU], dPa[NU];
 #pragma unroll
-  for (int i = 0; i < NU; ++i) {
-    const int u = wave + NW * i;
-    Gr[i] = QKr[i] = dAa[i] = dPa[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (u < 10) {
-      int R, J;
-      tri_block(u, R, J);
+    for (int i = 0; i < NU; ++i) {
+      const int u = wave + NW * i;
+      Gr[i] = QKr[i] = dAa[i] = dPa[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (u < 10) {
+        int R, J;
+        tri_block(u, R, J);
 #pragma unroll
-      for (int kb = 0; kb < DK / 32; ++kb) {
-        const frag b0 = rowf(sK, LDK, 16 * J, 32 * kb, lr, lg), b1 = rowf(sK, LDK, 16 * J, 32 * kb + 16, lr, lg);
-        Gr[i] = O::mma2(Gr[i], b0, b1, rowf(sK, LDK, 16 * R, 32 * kb, lr, lg), rowf(sK, LDK, 16 * R, 32 * kb + 16, lr, lg));
-        QKr[i] = O::mma2(QKr[i], b0, b1, rowf(sQ, LDK, 16 * R, 32 * kb, lr, lg), rowf(sQ, LDK, 16 * R, 32 * kb + 16, lr, lg));
+        for (int kb = 0; kb < DK / 32; ++kb) {
+          const frag b0 = rowf(sK, LDK, 16 * J, 32 * kb, lr, lg), b1 = rowf(sK, LDK, 16 * J, 32 * kb + 16, lr, lg);
+          Gr[i] = O::mma2(Gr[i], b0, b1, rowf(sK, LDK, 16 * R, 32 * kb, lr, lg), rowf(sK, LDK, 16 * R, 32 * kb + 16, lr, lg));
+          QKr[i] = O::mma2(QKr[i], b0, b1, rowf(sQ, LDK, 16 * R, 32 * kb, lr, lg), rowf(sQ, LDK, 16 * R, 32 * kb + 16, lr, lg));
+        }
+        const int r = 16 * R + lr;
+        f32x4 pv;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int j = 16 * J + 4 * lg + s;
+          float x = j <= r ? QKr[i][s] : 0.f;
+          if constexpr (G) x *= __expf(fminf(sF[5 * CH + r] - sF[5 * CH + j], 0.f));
+          pv[s] = x;
+        }
+        st_row(sP, LCP, r, 16 * J + 4 * lg, pv);
       }
-      const int r = 16 * R + lr;
-      f32x4 pv;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int j = 16 * J + 4 * lg + s;
-        float x = j <= r ? QKr[i][s] : 0.f;
-        if constexpr (G) x *= __expf(fminf(sF[5 * CH + r] - sF[5 * CH + j], 0.f));
-        pv[s] = x;
-      }
-      st_row(sP, LCP, r, 16 * J + 4 * lg, pv);
     }
-  }
-  __syncthreads();
+    store_half();                       // the first d_v half, loaded during the products above
+    __syncthreads();
+    if constexpr (NHALF > 1) load_half(1);
 
-  // ---- per d_v half -------------------------------------------------------------------
-  constexpr int NX = (4 * DKT) / NW;    // 64 x d_k tiles per wave
-  f32x4 dYS[NX], dOS[NX], DdS[NX];
+    // ---- per d_v half -------------------------------------------------------------------
+    // 64 x d_k tiles: wave w owns row blocks M = 2 (w / 4) + mi (mi = 0, 1) and column
+    // blocks ic = IC (w % 4) + j (j < IC), so fragments are shared along both
+    constexpr int IC = DKT / 4, NX = 2 * IC;
+    const int Mb = 2 * (wave >> 2), Ib = IC * (wave & 3);
+    f32x4 dYS[NX], dOS[NX], DdS[NX];
 #pragma unroll
-  for (int i = 0; i < NX; ++i) dYS[i] = dOS[i] = DdS[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float dbx[2] = {0.f, 0.f};            // sum_v dY X for rows 16 M_i + lr
-  for (int h = 0; h < nhalf; ++h) {
-    if (h > 0) {
-      store_half();
+    for (int i = 0; i < NX; ++i) dYS[i] = dOS[i] = DdS[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float dbx[2] = {0.f, 0.f};          // sum_v dY X for rows 16 M_i + lr
+#pragma unroll
+    for (int h = 0; h < NHALF; ++h) {
+      if (h > 0) {
+        store_half();
+        __syncthreads();
+      }
+      // X = V - diag(e^g) K S (kept), diag(beta) X over the v tile;
+      // dDelta = diag(e^{g_63 - g}) K dS' + P^T dO.  The wave's tiles (M, c) =
+      // (wave / 4 + 2 i, wave % 4), i = 0, 1, share the column c.
+      f32x4 Xr[2], KS2[2], KD2[2];
+      {
+        const int c = wave & 3;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) KS2[i] = KD2[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < DK / 32; ++kb) {
+          const frag s0 = rowf(sS, LDK, 16 * c, 32 * kb, lr, lg), s1 = rowf(sS, LDK, 16 * c, 32 * kb + 16, lr, lg);
+          const frag d0 = rowf(sdS, LDK, 16 * c, 32 * kb, lr, lg), d1 = rowf(sdS, LDK, 16 * c, 32 * kb + 16, lr, lg);
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const int M = (wave >> 2) + 2 * i;
+            const frag a0 = rowf(sK, LDK, 16 * M, 32 * kb, lr, lg), a1 = rowf(sK, LDK, 16 * M, 32 * kb + 16, lr, lg);
+            KS2[i] = O::mma2(KS2[i], s0, s1, a0, a1);
+            KD2[i] = O::mma2(KD2[i], d0, d1, a0, a1);
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int t = wave + NW * i, M = t >> 2, c = t & 3;
+        const int r = 16 * M + lr;
+        const f32x4 ks = KS2[i];
+        f32x4 kd = KD2[i];
+        const f32x4 vv = O::f32(O::ld(sV + r * LDV + 16 * c + 4 * lg));
+        const float er = G ? sF[CH + r] : 1.f;
+        Xr[i] = vv - ks * er;
+        st_row(sV, LDV, r, 16 * c + 4 * lg, Xr[i] * sF[r]);
+        if constexpr (G) kd = kd * sF[3 * CH + r];
+        int kb = M;
+        for (; kb + 1 <= 3; kb += 2)
+          kd = O::mma2(kd, colf(sdO, LDV, 16 * kb, 16 * c, lr, lg), colf(sdO, LDV, 16 * (kb + 1), 16 * c, lr, lg),
+                       colf(sP, LCP, 16 * kb, 16 * M, lr, lg), colf(sP, LCP, 16 * (kb + 1), 16 * M, lr, lg));
+        if (kb <= 3) kd = O::mma1(kd, colf(sdO, LDV, 16 * kb, 16 * c, lr, lg), colf(sP, LCP, 16 * kb, 16 * M, lr, lg));
+        st_row(sdD, LDD, r, 16 * c + 4 * lg, kd);
+      }
       __syncthreads();
-    }
-    // X = V - diag(e^g) K S (kept), diag(beta) X over the v tile; dDelta = diag(e^{g_63 - g}) K dS' + P^T dO
-    f32x4 Xr[2];
+      // Delta = T diag(beta) X, dY = T^T dDelta; dv = diag(beta) dY
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int t = wave + NW * i, M = t >> 2, c = t & 3;
-      const int r = 16 * M + lr;
-      f32x4 ks = {0.f, 0.f, 0.f, 0.f}, kd = {0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < 2; ++i) {
+        const int t = wave + NW * i, M = t >> 2, c = t & 3;
+        const int r = 16 * M + lr;
+        f32x4 dl = {0.f, 0.f, 0.f, 0.f}, dy = {0.f, 0.f, 0.f, 0.f};
+        int kb = 0;
+        for (; kb + 1 <= M; kb += 2)
+          dl = O::mma2(dl, colf(sV, LDV, 16 * kb, 16 * c, lr, lg), colf(sV, LDV, 16 * (kb + 1), 16 * c, lr, lg),
+                       colf(sT, LCP, 16 * kb, 16 * M, lr, lg), colf(sT, LCP, 16 * (kb + 1), 16 * M, lr, lg));
+        if (kb <= M) dl = O::mma1(dl, colf(sV, LDV, 16 * kb, 16 * c, lr, lg), colf(sT, LCP, 16 * kb, 16 * M, lr, lg));
+        kb = M;
+        for (; kb + 1 <= 3; kb += 2)
+          dy = O::mma2(dy, colf(sdD, LDD, 16 * kb, 16 * c, lr, lg), colf(sdD, LDD, 16 * (kb + 1), 16 * c, lr, lg),
+                       rowf(sT, LCP, 16 * M, 16 * kb, lr, lg), rowf(sT, LCP, 16 * M, 16 * (kb + 1), lr, lg));
+        if (kb <= 3) dy = O::mma1(dy, colf(sdD, LDD, 16 * kb, 16 * c, lr, lg), rowf(sT, LCP, 16 * M, 16 * kb, lr, lg));
+        buf_store8(bits8(dy * sF[r]), rdv, static_cast<uint32_t>((r * H * DV + 64 * h + 16 * c + 4 * lg) * 2), sv);
 #pragma unroll
-      for (int kb = 0; kb < DK / 32; ++kb) {
-        const frag a0 = rowf(sK, LDK, 16 * M, 32 * kb, lr, lg), a1 = rowf(sK, LDK, 16 * M, 32 * kb + 16, lr, lg);
-        ks = O::mma2(ks, rowf(sS, LDK, 16 * c, 32 * kb, lr, lg), rowf(sS, LDK, 16 * c, 32 * kb + 16, lr, lg), a0, a1);
-        kd = O::mma2(kd, rowf(sdS, LDK, 16 * c, 32 * kb, lr, lg), rowf(sdS, LDK, 16 * c, 32 * kb + 16, lr, lg), a0, a1);
+        for (int s = 0; s < 4; ++s) dbx[i] += dy[s] * Xr[i][s];
+        st_row(sDl, LDR, r, 16 * c + 4 * lg, dl);
+        st_row(sdY, LDR, r, 16 * c + 4 * lg, dy);
       }
-      const f32x4 vv = O::f32(O::ld(sV + r * LDV + 16 * c + 4 * lg));
-      const float er = G ? sF[2 * CH + r] : 1.f;
-      Xr[i] = vv - ks * er;
-      st_row(sV, LDV, r, 16 * c + 4 * lg, Xr[i] * sF[r]);
-      if constexpr (G) kd = kd * sF[3 * CH + r];
-      int kb = M;
-      for (; kb + 1 <= 3; kb += 2)
-        kd = O::mma2(kd, colf(sdO, LDV, 16 * kb, 16 * c, lr, lg), colf(sdO, LDV, 16 * (kb + 1), 16 * c, lr, lg),
-                     colf(sP, LCP, 16 * kb, 16 * M, lr, lg), colf(sP, LCP, 16 * (kb + 1), 16 * M, lr, lg));
-      if (kb <= 3) kd = O::mma1(kd, colf(sdO, LDV, 16 * kb, 16 * c, lr, lg), colf(sP, LCP, 16 * kb, 16 * M, lr, lg));
-      st_row(sdD, LDV, r, 16 * c + 4 * lg, kd);
-    }
-    __syncthreads();
-    // Delta = T diag(beta) X, dY = T^T dDelta; dv = diag(beta) dY
+      __syncthreads();
+      // dA += dY Delta^T, dP += dO Delta^T on the wave's blocks; dY S^T, dO S^T, Delta dS'^T
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int t = wave + NW * i, M = t >> 2, c = t & 3;
-      const int r = 16 * M + lr;
-      f32x4 dl = {0.f, 0.f, 0.f, 0.f}, dy = {0.f, 0.f, 0.f, 0.f};
-      int kb = 0;
-      for (; kb + 1 <= M; kb += 2)
-        dl = O::mma2(dl, colf(sV, LDV, 16 * kb, 16 * c, lr, lg), colf(sV, LDV, 16 * (kb + 1), 16 * c, lr, lg),
-                     colf(sT, LCP, 16 * kb, 16 * M, lr, lg), colf(sT, LCP, 16 * (kb + 1), 16 * M, lr, lg));
-      if (kb <= M) dl = O::mma1(dl, colf(sV, LDV, 16 * kb, 16 * c, lr, lg), colf(sT, LCP, 16 * kb, 16 * M, lr, lg));
-      kb = M;
-      for (; kb + 1 <= 3; kb += 2)
-        dy = O::mma2(dy, colf(sdD, LDV, 16 * kb, 16 * c, lr, lg), colf(sdD, LDV, 16 * (kb + 1), 16 * c, lr, lg),
-                     rowf(sT, LCP, 16 * M, 16 * kb, lr, lg), rowf(sT, LCP, 16 * M, 16 * (kb + 1), lr, lg));
-      if (kb <= 3) dy = O::mma1(dy, colf(sdD, LDV, 16 * kb, 16 * c, lr, lg), rowf(sT, LCP, 16 * M, 16 * kb, lr, lg));
-      buf_store8(bits8(dy * sF[r]), rdv, static_cast<uint32_t>((r * H * dv + 64 * h + 16 * c + 4 * lg) * 2), sv);
+      for (int i = 0; i < NU; ++i) {
+        const int u = wave + NW * i;
+        if (u < 10) {
+          int R, J;
+          tri_block(u, R, J);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) dbx[i] += dy[s] * Xr[i][s];
-      st_row(sDl, LDV, r, 16 * c + 4 * lg, dl);
-      st_row(sdY, LDV, r, 16 * c + 4 * lg, dy);
+          for (int kb = 0; kb < 2; ++kb) {
+            const frag b0 = rowf(sDl, LDR, 16 * J, 32 * kb, lr, lg), b1 = rowf(sDl, LDR, 16 * J, 32 * kb + 16, lr, lg);
+            dAa[i] = O::mma2(dAa[i], b0, b1, rowf(sdY, LDR, 16 * R, 32 * kb, lr, lg), rowf(sdY, LDR, 16 * R, 32 * kb + 16, lr, lg));
+            dPa[i] = O::mma2(dPa[i], b0, b1, rowf(sdO, LDV, 16 * R, 32 * kb, lr, lg), rowf(sdO, LDV, 16 * R, 32 * kb + 16, lr, lg));
+          }
+        }
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        frag bs[IC][2], bd[IC][2];
+#pragma unroll
+        for (int j = 0; j < IC; ++j) {
+          const int ic = Ib + j;
+          bs[j][0] = colf(sS, LDK, 32 * kb, 16 * ic, lr, lg);
+          bs[j][1] = colf(sS, LDK, 32 * kb + 16, 16 * ic, lr, lg);
+          bd[j][0] = colf(sdS, LDK, 32 * kb, 16 * ic, lr, lg);
+          bd[j][1] = colf(sdS, LDK, 32 * kb + 16, 16 * ic, lr, lg);
+        }
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi) {
+          const int M = Mb + mi;
+          const frag y0 = rowf(sdY, LDR, 16 * M, 32 * kb, lr, lg), y1 = rowf(sdY, LDR, 16 * M, 32 * kb + 16, lr, lg);
+          const frag o0 = rowf(sdO, LDV, 16 * M, 32 * kb, lr, lg), o1 = rowf(sdO, LDV, 16 * M, 32 * kb + 16, lr, lg);
+          const frag e0 = rowf(sDl, LDR, 16 * M, 32 * kb, lr, lg), e1 = rowf(sDl, LDR, 16 * M, 32 * kb + 16, lr, lg);
+#pragma unroll
+          for (int j = 0; j < IC; ++j) {
+            const int i = mi * IC + j;
+            dYS[i] = O::mma2(dYS[i], bs[j][0], bs[j][1], y0, y1);
+            dOS[i] = O::mma2(dOS[i], bs[j][0], bs[j][1], o0, o1);
+            DdS[i] = O::mma2(DdS[i], bd[j][0], bd[j][1], e0, e1);
+          }
+        }
+      }
+      if (h + 1 < NHALF) __syncthreads();   // every read of this half's tiles is done
     }
-    __syncthreads();
-    // dA += dY Delta^T, dP += dO Delta^T on the wave's blocks; dY S^T, dO S^T, Delta dS'^T
+
+    // ---- beta D * dA and D * dP; dbeta and the row / column sums of dA*A and dP*P ------
 #pragma unroll
     for (int i = 0; i < NU; ++i) {
       const int u = wave + NW * i;
       if (u < 10) {
         int R, J;
         tri_block(u, R, J);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const frag b0 = rowf(sDl, LDV, 16 * J, 32 * kb, lr, lg), b1 = rowf(sDl, LDV, 16 * J, 32 * kb + 16, lr, lg);
-          dAa[i] = O::mma2(dAa[i], b0, b1, rowf(sdY, LDV, 16 * R, 32 * kb, lr, lg), rowf(sdY, LDV, 16 * R, 32 * kb + 16, lr, lg));
-          dPa[i] = O::mma2(dPa[i], b0, b1, rowf(sdO, LDV, 16 * R, 32 * kb, lr, lg), rowf(sdO, LDV, 16 * R, 32 * kb + 16, lr, lg));
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < NX; ++i) {
-      const int t = wave + NW * i, M = t / DKT, ic = t % DKT;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const frag bs0 = colf(sS, LDK, 32 * kb, 16 * ic, lr, lg), bs1 = colf(sS, LDK, 32 * kb + 16, 16 * ic, lr, lg);
-        const frag bd0 = colf(sdS, LDK, 32 * kb, 16 * ic, lr, lg), bd1 = colf(sdS, LDK, 32 * kb + 16, 16 * ic, lr, lg);
-        dYS[i] = O::mma2(dYS[i], bs0, bs1, rowf(sdY, LDV, 16 * M, 32 * kb, lr, lg), rowf(sdY, LDV, 16 * M, 32 * kb + 16, lr, lg));
-        dOS[i] = O::mma2(dOS[i], bs0, bs1, rowf(sdO, LDV, 16 * M, 32 * kb, lr, lg), rowf(sdO, LDV, 16 * M, 32 * kb + 16, lr, lg));
-        DdS[i] = O::mma2(DdS[i], bd0, bd1, rowf(sDl, LDV, 16 * M, 32 * kb, lr, lg), rowf(sDl, LDV, 16 * M, 32 * kb + 16, lr, lg));
-      }
-    }
-    if (h + 1 < nhalf) {
-      __syncthreads();                  // every read of this half's tiles is done
-      if (h + 2 < nhalf) load_half(h + 2);
-    }
-  }
-
-  // ---- beta D * dA and D * dP; dbeta and the row / column sums of dA*A and dP*P --------
-#pragma unroll
-  for (int i = 0; i < NU; ++i) {
-    const int u = wave + NW * i;
-    if (u < 10) {
-      int R, J;
-      tri_block(u, R, J);
-      const int r = 16 * R + lr;
-      const float br = sF[r];
-      f32x4 ak, pk;
-      float db = 0.f, rsum = 0.f;
-      float csum[4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int j = 16 * J + 4 * lg + s;
-        const float D = G ? __expf(fminf(sF[5 * CH + r] - sF[5 * CH + j], 0.f)) : 1.f;
-        const float dA = j < r ? -dAa[i][s] : 0.f;
-        const float dP = j <= r ? dPa[i][s] : 0.f;
-        ak[s] = br * D * dA;
-        pk[s] = D * dP;
-        db += dA * D * Gr[i][s];
-        const float e = ak[s] * Gr[i][s] + pk[s] * QKr[i][s];   // dA * A + dP * P
-        rsum += e;
-        csum[s] = e;
-      }
-      st_row(sAk, LCP, r, 16 * J + 4 * lg, ak);
-      st_row(sP, LCP, r, 16 * J + 4 * lg, pk);
-      atomicAdd(&sdb[r], db);
-      if constexpr (G) {
-        atomicAdd(&sdg[r], rsum);
+        const int r = 16 * R + lr;
+        const float br = sF[r];
+        f32x4 ak, pk;
+        float db = 0.f, rsum = 0.f;
+        float csum[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          float x = csum[s];
-          x += __shfl_xor(x, 1);
-          x += __shfl_xor(x, 2);
-          x += __shfl_xor(x, 4);
-          x += __shfl_xor(x, 8);
-          if (lr == 0) atomicAdd(&sdg[16 * J + 4 * lg + s], -x);
+          const int j = 16 * J + 4 * lg + s;
+          const float D = G ? __expf(fminf(sF[5 * CH + r] - sF[5 * CH + j], 0.f)) : 1.f;
+          const float dA = j < r ? -dAa[i][s] : 0.f;
+          const float dP = j <= r ? dPa[i][s] : 0.f;
+          ak[s] = br * D * dA;
+          pk[s] = D * dP;
+          db += dA * D * Gr[i][s];
+          const float e = ak[s] * Gr[i][s] + pk[s] * QKr[i][s];   // dA * A + dP * P
+          rsum += e;
+          csum[s] = e;
+        }
+        st_row(sAk, LCP, r, 16 * J + 4 * lg, ak);
+        st_row(sP, LCP, r, 16 * J + 4 * lg, pk);
+        atomicAdd(&sdb[r], db);
+        if constexpr (G) {
+          atomicAdd(&sdg[r], rsum);
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const float x = row16_sum(csum[s]);
+            if (lr == 0) atomicAdd(&sdg[16 * J + 4 * lg + s], -x);
+          }
         }
       }
     }
-  }
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int M = (wave + NW * i) >> 2;
-    float x = dbx[i];
-    x += __shfl_xor(x, 16);
-    x += __shfl_xor(x, 32);
-    if (lg == 0) atomicAdd(&sdb[16 * M + lr], x);
-  }
-  if constexpr (G) {
-    float x = sdot;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) x += __shfl_xor(x, d);
-    if (lane == 0) atomicAdd(sred, x);
-  }
-  __syncthreads();
-
-  // ---- dk, dq ---------------------------------------------------------------------------
-  float csum = 0.f;
-#pragma unroll
-  for (int i = 0; i < NX; ++i) {
-    const int t = wave + NW * i, M = t / DKT, ic = t % DKT;
-    const int r = 16 * M + lr;
-    f32x4 gk = {0.f, 0.f, 0.f, 0.f}, gq = {0.f, 0.f, 0.f, 0.f};
-    for (int kb = 0; kb <= M; ++kb) {   // (beta D dA) K, (D dP) K: blocks on or left of the diagonal
-      const frag bk = colf(sK, LDK, 16 * kb, 16 * ic, lr, lg);
-      gk = O::mma1(gk, bk, rowf(sAk, LCP, 16 * M, 16 * kb, lr, lg));
-      gq = O::mma1(gq, bk, rowf(sP, LCP, 16 * M, 16 * kb, lr, lg));
-    }
-    for (int kb = M; kb < 4; ++kb) {    // (beta D dA)^T K + (D dP)^T Q: blocks on or below it
-      gk = O::mma1(gk, colf(sK, LDK, 16 * kb, 16 * ic, lr, lg), colf(sAk, LCP, 16 * kb, 16 * M, lr, lg));
-      gk = O::mma1(gk, colf(sQ, LDK, 16 * kb, 16 * ic, lr, lg), colf(sP, LCP, 16 * kb, 16 * M, lr, lg));
-    }
-    const float br = sF[r];
-    const float eg = G ? sF[2 * CH + r] : 1.f, ed = G ? sF[3 * CH + r] : 1.f;
-    const f32x4 dk = gk - dYS[i] * (br * eg) + DdS[i] * ed;
-    const f32x4 dq = gq + dOS[i] * eg;
-    const uint32_t off = static_cast<uint32_t>((r * H * DK + 16 * ic + 4 * lg) * 2);
-    buf_store8(bits8(dk), rdk, off, sk);
-    buf_store8(bits8(dq), rdq, off, sk);
+    for (int i = 0; i < 2; ++i) atomicAdd(&sdb[16 * ((wave >> 2) + 2 * i) + lr], dbx[i]);
     if constexpr (G) {
-      const f32x4 kk = O::f32(O::ld(sK + r * LDK + 16 * ic + 4 * lg));
-      const f32x4 qq = O::f32(O::ld(sQ + r * LDK + 16 * ic + 4 * lg));
-      float a = 0.f, c = 0.f;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        a += eg * (qq[s] * dOS[i][s] - br * kk[s] * dYS[i][s]);
-        c += ed * kk[s] * DdS[i][s];
-      }
-      a -= c;
-      a += __shfl_xor(a, 16);
-      a += __shfl_xor(a, 32);
-      if (lg == 0) atomicAdd(&sdg[r], a);
-      csum += c;
+      const float x = row16_sum(sdot);
+      if (lr == 0) atomicAdd(sred, x);
     }
-  }
-  if constexpr (G) {
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) csum += __shfl_xor(csum, d);
-    if (lane == 0) atomicAdd(&sdg[CH - 1], csum);
-  }
-  __syncthreads();
+    __syncthreads();
 
-  // ---- dbeta, d log a (suffix sums of dg over the chunk) ------------------------------
-  if (wave == 0) {
-    const uint32_t off = static_cast<uint32_t>(lane * H * 2);
-    buf_store2(f32_to_bf16_bits(sdb[lane]), rdb, off, sb);
-    if constexpr (G) {
-      float x = sdg[lane];
-      if (lane == CH - 1) x += sF[4 * CH] * sred[0];
+    // ---- dk, dq -----------------------------------------------------------------------
+    float csum = 0.f;
 #pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const float y = __shfl_down(x, d);
-        if (lane + d < 64) x += y;
+    for (int i = 0; i < NX; ++i) {
+      const int mi = i / IC, j = i % IC;
+      const int M = Mb + mi, ic = Ib + j;
+      const int r = 16 * M + lr;
+      f32x4 gk = {0.f, 0.f, 0.f, 0.f}, gq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const frag bk = colf(sK, LDK, 16 * kb, 16 * ic, lr, lg);
+        if (kb <= M) {                  // (beta D dA) K, (D dP) K: blocks on or left of the diagonal
+          gk = O::mma1(gk, bk, rowf(sAk, LCP, 16 * M, 16 * kb, lr, lg));
+          gq = O::mma1(gq, bk, rowf(sP, LCP, 16 * M, 16 * kb, lr, lg));
+        }
+        if (kb >= M) {                  // (beta D dA)^T K + (D dP)^T Q: blocks on or below it
+          gk = O::mma1(gk, bk, colf(sAk, LCP, 16 * kb, 16 * M, lr, lg));
+          gk = O::mma1(gk, colf(sQ, LDK, 16 * kb, 16 * ic, lr, lg), colf(sP, LCP, 16 * kb, 16 * M, lr, lg));
+        }
       }
-      buf_store2(f32_to_bf16_bits(x), rdl, off, sb);
+      const float br = sF[r];
+      const float er = G ? sF[CH + r] : 1.f, eg = G ? sF[2 * CH + r] : 1.f, ed = G ? sF[3 * CH + r] : 1.f;
+      const f32x4 dk = gk - dYS[i] * (br * er) + DdS[i] * ed;
+      const f32x4 dq = gq + dOS[i] * eg;
+      const uint32_t off = static_cast<uint32_t>((r * H * DK + 16 * ic + 4 * lg) * 2);
+      buf_store8(bits8(dk), rdk, off, sk);
+      buf_store8(bits8(dq), rdq, off, sk);
+      if constexpr (G) {
+        const f32x4 kk = O::f32(O::ld(sK + r * LDK + 16 * ic + 4 * lg));
+        const f32x4 qq = O::f32(O::ld(sQ + r * LDK + 16 * ic + 4 * lg));
+        float a = 0.f, c = 0.f;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          a += eg * qq[s] * dOS[i][s] - br * er * kk[s] * dYS[i][s];
+          c += ed * kk[s] * DdS[i][s];
+        }
+        atomicAdd(&sdg[r], a - c);
+        csum += c;
+      }
+    }
+    if constexpr (G) {
+      const float x = row16_sum(csum);
+      if (lr == 0) atomicAdd(&sdg[CH - 1], x);
+    }
+    __syncthreads();
+
+    // ---- dbeta, d log a (suffix sums of dg over the chunk) ----------------------------
+    if (wave == 0) {
+      const uint32_t off = static_cast<uint32_t>(lane * H * 2);
+      buf_store2(f32_to_bf16_bits(sdb[lane]), rdb, off, sb);
+      if constexpr (G) {
+        float x = sdg[lane];
+        if (lane == CH - 1) x += sF[4 * CH] * sred[0];
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+          const float y = __shfl_down(x, d);
+          if (lane + d < 64) x += y;
+        }
+        buf_store2(f32_to_bf16_bits(x), rdl, off, sb);
+      }
     }
   }
 }
@@ -820,7 +880,11 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_reverse_kernel<GATE, DK>), dim3(static_cast<unsigned>(nseq)), dim3(256), 0, stream, p, n_tiles);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_chunk_kernel<GATE, DK>), dim3(static_cast<unsigned>(f.B * f.H * nch)), dim3(512), 0, stream, p);
+  const unsigned grid = static_cast<unsigned>(f.B * f.H * nch);
+  if (f.d_v == 128)
+    hipLaunchKernelGGL((bwd_chunk_kernel<GATE, DK, 128>), dim3(grid), dim3(512), 0, stream, p);
+  else
+    hipLaunchKernelGGL((bwd_chunk_kernel<GATE, DK, 64>), dim3(grid), dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 
