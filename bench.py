@@ -47,6 +47,8 @@ DECODE_SOURCES = [os.path.join(ROOT, "gated_delta_rule_21_amd", "csrc", n)
                   for n in ("decode_step.hip", "device_common.h")]
 PRECOND_SOURCES = [os.path.join(ROOT, "gated_delta_rule_21_amd", "csrc", n)
                    for n in ("precond_scan.hip", "chunk_common.h", "device_common.h")]
+BWD_SOURCES = [os.path.join(ROOT, "gated_delta_rule_21_amd", "csrc", n)
+               for n in ("chunk_bwd.hip", "chunk_prep.hip", "chunk_common.h", "device_common.h")]
 
 
 def chunk_algorithmic(wl, with_S0: bool):
@@ -268,6 +270,20 @@ def bench_precond(args, log, wl, k, beta):
                          "traffic": profiled_traffic("precond_scan_b8h16t8192d128_counters.md", PRECOND_SOURCES)}}
 
 
+def bwd_bytes(wl, with_S0: bool):
+    """Bytes of one backward call if every input were read once and every output
+    written once: q, k, v, dO, beta, log_a (S0, dS_T) read; dq, dk, dv, dbeta,
+    dlog_a, dS0 written.  The per-chunk records and the two sets of chunk states
+    the call keeps in its workspace are not counted."""
+    esz = 2
+    ntok = wl.B * wl.T * wl.H
+    gate_w = 1 if wl.gate == "scalar" else 0
+    state = wl.B * wl.H * wl.d_k * wl.d_v * 4
+    rd = ntok * (2 * wl.d_k + 2 * wl.d_v + 1 + gate_w) * esz + state * (2 if with_S0 else 1)
+    wr = ntok * (2 * wl.d_k + wl.d_v + 1 + gate_w) * esz + state
+    return rd + wr
+
+
 def bwd_algorithmic(wl):
     """Useful flops of the backward per launch: per chunk (C = 64, d = d_k = d_v),
     the chunk-start states 4 C d^2 + C^2 d (K S, T X, K^T Delta), the reverse pass
@@ -312,8 +328,10 @@ def bench_bwd(args, log, wl, q, k, v, beta, log_a, S0):
     log(f"chunk backward: {ms:.3f} ms/step, {tf:.1f} TFLOP/s useful")
     return {"workload": wl.name + "_backward", "value": round(wl.B * wl.T / (ms * 1e-3), 1), "unit": "tokens/s",
             "ms_per_launch": round(ms, 4), "useful_flops_per_launch": flops,
+            "algorithmic_bytes_per_launch": bwd_bytes(wl, S0 is not None),
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None}}
+                         "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                         "traffic": profiled_traffic("chunk_bwd_gated_b8h16t8192d128_counters.md", BWD_SOURCES)}}
 
 
 def bench_wkey(args, log, wl, q, k, v, beta, kw, scan_us):

@@ -27,7 +27,7 @@ CAL_BYTES = 1 << 30
 
 
 def short_name(name: str) -> str:
-    name = name.split("(")[0]
+    name = name.replace("(anonymous namespace)::", "").split("(")[0]
     return name.replace("void ", "")[:110]
 
 
@@ -51,6 +51,14 @@ def decode_source_digest() -> str:
 def precond_source_digest() -> str:
     h = hashlib.sha256()
     for n in ("precond_scan.hip", "chunk_common.h", "device_common.h"):
+        with open(os.path.join(ROOT, "gated_delta_rule_21_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def bwd_source_digest() -> str:
+    h = hashlib.sha256()
+    for n in ("chunk_bwd.hip", "chunk_prep.hip", "chunk_common.h", "device_common.h"):
         with open(os.path.join(ROOT, "gated_delta_rule_21_amd", "csrc", n), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -137,7 +145,8 @@ def main(argv=None):
         sys.stdout.write(stats(args.csv, args.command, args.top))
     else:
         digest = (decode_source_digest() if "decode" in args.kernel else
-                  precond_source_digest() if "precond" in args.kernel else kernel_source_digest())
+                  precond_source_digest() if "precond" in args.kernel else
+                  bwd_source_digest() if "bwd" in args.kernel else kernel_source_digest())
         sys.stdout.write(counters(args.fetch_csv, args.write_csv, args.kernel, args.algorithmic_bytes,
                                   args.command, digest))
 
