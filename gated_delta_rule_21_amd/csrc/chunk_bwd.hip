@@ -73,15 +73,6 @@ __device__ __forceinline__ void put16(T* dst, u32x4 x) {
   d[1] = u32x2{x[2], x[3]};
 }
 
-// Workgroup -> (sequence, head, tile): consecutive logical blocks on one XCD (block
-// ids are dealt round-robin over the 8 XCDs), so the tiles of one head share an L2.
-__device__ __forceinline__ int logical_block() {
-  const int nblk = gridDim.x;
-  int lb = blockIdx.x;
-  if ((nblk & 7) == 0) lb = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
-  return lb;
-}
-
 // LDS row strides (bf16 elements) by how a tile is read, after the rates measured
 // for the forward on gfx950: 8-byte row fragments run fastest when a row is 2 or 6
 // (mod 8) dwords long, transpose reads when it is 8 (mod 32) dwords; a tile read both
@@ -91,11 +82,13 @@ constexpr int ld_tr(int w) { return w + 16; }     // transposed only (w = 64, 12
 constexpr int ld_both(int w) { return w + 12; }   // both
 
 // ---------------------------------------------------------------------------
-// Passes 1 and 2: the sequential passes.  Four waves, 16 state columns each.
-// LDS: two copies of one chunk's tiles (k, q, a 64-column v or dO tile, T^T, the
-// gate factors), and P of the current chunk (pass 2).  Pass 1 reads k both ways,
-// v and T^T transposed; pass 2 reads k and q both ways, dO and P transposed, T^T
-// by rows.
+// Passes 1 and 2: the sequential passes.  Neither reads what the other writes, so
+// one launch runs both, and each compute unit holds a workgroup of each (their
+// LDS together fits in one CU's 160 KB).  Four waves per workgroup, 16 state
+// columns each.  LDS: pass 1 keeps two copies of one chunk's tiles (k, a 64-column
+// v tile, T^T, the gate factors); pass 2 one copy (k, q, a 64-column dO tile, T^T,
+// the factors) and P of the chunk.  Pass 1 reads k both ways, v and T^T transposed;
+// pass 2 reads k and q both ways, dO and P transposed, T^T by rows.
 // ---------------------------------------------------------------------------
 template <int DK, bool REV>
 struct SeqLayout {
@@ -108,7 +101,7 @@ struct SeqLayout {
   static constexpr size_t TB = size_t(CH) * LCT * 2;
   static constexpr size_t O_K = 0, O_Q = O_K + KB, O_V = O_Q + (REV ? KB : 0), O_T = O_V + VB, O_F = O_T + TB;
   static constexpr size_t BUF = O_F + 6 * CH * 4;
-  static constexpr size_t O_P = 2 * BUF;
+  static constexpr size_t O_P = (REV ? 1 : 2) * BUF;
   static constexpr size_t TOTAL = O_P + (REV ? size_t(CH) * LCP * 2 : 0);
 };
 
@@ -192,14 +185,13 @@ __device__ __forceinline__ Slice slice_of(const ChunkParams& f, int64_t bb, int6
   return Slice{bb * f.T * f.H + hh, static_cast<uint32_t>(f.T > 0 ? (f.T - 1) * f.H + 1 : 0)};
 }
 
-// Pass 1: the state entering every chunk, stored in bf16 value-major.
+// Pass 1: the state entering every chunk, stored in bf16 value-major.  lb is the
+// workgroup's (sequence, head, tile) index.
 template <int GATE, int DK>
-__global__ __launch_bounds__(256) void bwd_states_kernel(BwdParams p, int n_tiles) {
+__device__ __forceinline__ void states_pass(const BwdParams& p, int n_tiles, int lb, char* smem) {
   typedef SeqLayout<DK, false> L;
   constexpr int DKT = DK / 16, LDK = L::LDK, LDV = L::LDV, LCT = L::LCT;
-  __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
   const ChunkParams& f = p.f;
-  const int lb = logical_block();
   const int64_t bh = lb / n_tiles;
   const int tile = lb % n_tiles;
   const int64_t bb = bh / f.H, hh = bh % f.H;
@@ -291,13 +283,13 @@ __global__ __launch_bounds__(256) void bwd_states_kernel(BwdParams p, int n_tile
 }
 
 // Pass 2: the gradient of the state leaving every chunk, last chunk first, and dS0.
+// One LDS copy of the chunk's tiles: the next chunk waits in registers and goes
+// in after the step's last read.
 template <int GATE, int DK>
-__global__ __launch_bounds__(256) void bwd_reverse_kernel(BwdParams p, int n_tiles) {
+__device__ __forceinline__ void reverse_pass(const BwdParams& p, int n_tiles, int lb, char* smem) {
   typedef SeqLayout<DK, true> L;
   constexpr int DKT = DK / 16, LDK = L::LDK, LDV = L::LDV, LCT = L::LCT, LCP = L::LCP;
-  __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
   const ChunkParams& f = p.f;
-  const int lb = logical_block();
   const int64_t bh = lb / n_tiles;
   const int tile = lb % n_tiles;
   const int64_t bb = bh / f.H, hh = bh % f.H;
@@ -323,21 +315,17 @@ __global__ __launch_bounds__(256) void bwd_reverse_kernel(BwdParams p, int n_til
   SeqStage<DK, 256, true> st;
   if (nch > 0) {
     st.load(rk, rq, rdo, rw, nch - 1, tid, H, dv, col0);
-    st.store(smem + ((nch - 1) & 1) * L::BUF, tid);
-    if (nch > 1) st.load(rk, rq, rdo, rw, nch - 2, tid, H, dv, col0);
+    st.store(smem, tid);
   }
   __syncthreads();
+  if (nch > 1) st.load(rk, rq, rdo, rw, nch - 2, tid, H, dv, col0);
   for (int64_t n = nch - 1; n >= 0; --n) {
-    const char* cur = smem + (n & 1) * L::BUF;
+    const char* cur = smem;
     const T* sK = reinterpret_cast<const T*>(cur + L::O_K);
     const T* sQ = reinterpret_cast<const T*>(cur + L::O_Q);
     const T* sO = reinterpret_cast<const T*>(cur + L::O_V);
     const T* sT = reinterpret_cast<const T*>(cur + L::O_T);
     const float* sF = reinterpret_cast<const float*>(cur + L::O_F);
-    if (n >= 1) {        // the other copy (chunk n + 1) was last read before the previous barrier
-      st.store(smem + ((n - 1) & 1) * L::BUF, tid);
-      if (n >= 2) st.load(rk, rq, rdo, rw, n - 2, tid, H, dv, col0);
-    }
     // P of this chunk, blocks u = wave, wave + 4, .. (row form: row 16R + lr)
     for (int u = wave; u < 10; u += 4) {
       int R, J;
@@ -426,7 +414,12 @@ __global__ __launch_bounds__(256) void bwd_reverse_kernel(BwdParams p, int n_til
       acc = O::mma2(acc, colf(sK, LDK, 32, 16 * t, lr, lg), colf(sK, LDK, 48, 16 * t, lr, lg), Zb[2], Zb[3]);
       dS[t] = acc;
     }
-    __syncthreads();
+    __syncthreads();                    // this chunk's tiles and P are read
+    if (n >= 1) {
+      st.store(smem, tid);              // chunk n - 1, loaded during this step
+      if (n >= 2) st.load(rk, rq, rdo, rw, n - 2, tid, H, dv, col0);
+      __syncthreads();
+    }
   }
   if (p.dS0) {
 #pragma unroll
@@ -434,6 +427,17 @@ __global__ __launch_bounds__(256) void bwd_reverse_kernel(BwdParams p, int n_til
 #pragma unroll
       for (int s = 0; s < 4; ++s) p.dS0[(bh * DK + 16 * t + 4 * lg + s) * dv + scol] = dS[t][s];
   }
+}
+
+// Passes 1 and 2 in one launch of 2 nseq workgroups: the first nseq take pass 1.
+template <int GATE, int DK>
+__global__ __launch_bounds__(256) void bwd_seq_kernel(BwdParams p, int n_tiles, int nseq) {
+  __shared__ __attribute__((aligned(16))) char smem[cmax(SeqLayout<DK, false>::TOTAL, SeqLayout<DK, true>::TOTAL)];
+  const int b = blockIdx.x;
+  const int role = b >= nseq;
+  const int idx = b - role * nseq;
+  if (role == 0) states_pass<GATE, DK>(p, n_tiles, idx, smem);
+  else reverse_pass<GATE, DK>(p, n_tiles, idx, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -875,11 +879,10 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
   const int64_t nch = (f.T + CH - 1) / CH;
   const int n_tiles = f.d_v / 64;
   const int64_t nseq = f.B * f.H * n_tiles;
-  hipLaunchKernelGGL((bwd_states_kernel<GATE, DK>), dim3(static_cast<unsigned>(nseq)), dim3(256), 0, stream, p, n_tiles);
+  hipLaunchKernelGGL((bwd_seq_kernel<GATE, DK>), dim3(static_cast<unsigned>(2 * nseq)), dim3(256), 0, stream, p, n_tiles,
+                     static_cast<int>(nseq));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_reverse_kernel<GATE, DK>), dim3(static_cast<unsigned>(nseq)), dim3(256), 0, stream, p, n_tiles);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   const unsigned grid = static_cast<unsigned>(f.B * f.H * nch);
   if (f.d_v == 128)
     hipLaunchKernelGGL((bwd_chunk_kernel<GATE, DK, 128>), dim3(grid), dim3(512), 0, stream, p);
