@@ -92,8 +92,9 @@ def pick(vals, sub: str):
 
 def counters(fetch_csv: str, write_csv: str, kernels: str, algorithmic: float, command: str,
              digest: str) -> str:
-    """`kernels`: comma-separated name substrings; the traffic of one call of the
-    operation is the sum over them (each kernel runs once per call)."""
+    """`kernels`: name substrings separated by ';' (or by ',' when there is no ';'); the
+    traffic of one call of the operation is the sum over them (each kernel runs once
+    per call)."""
     f = per_dispatch(fetch_csv, "FETCH_SIZE")
     w = per_dispatch(write_csv, "WRITE_SIZE")
     cf, cw = pick(f, CAL_KERNEL), pick(w, CAL_KERNEL)
@@ -110,7 +111,7 @@ def counters(fetch_csv: str, write_csv: str, kernels: str, algorithmic: float, c
            f"| read scale (bytes per counted byte) | {sf:.4f} |",
            f"| write scale (bytes per counted byte) | {sw:.4f} |"]
     tot = 0.0
-    for k in kernels.split(","):
+    for k in kernels.split(";" if ";" in kernels else ","):
         kf, kw = pick(f, k), pick(w, k)
         if not (kf and kw):
             raise SystemExit(f"missing dispatches of {k}")
@@ -137,7 +138,7 @@ def main(argv=None):
     b = sub.add_parser("counters")
     b.add_argument("fetch_csv")
     b.add_argument("write_csv")
-    b.add_argument("--kernel", required=True, help="name substring, or several separated by commas")
+    b.add_argument("--kernel", required=True, help="name substring, or several separated by ';' (or ',')")
     b.add_argument("--algorithmic-bytes", type=float, required=True)
     b.add_argument("--command", required=True)
     args = ap.parse_args(argv)
