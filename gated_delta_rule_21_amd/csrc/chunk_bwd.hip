@@ -466,11 +466,17 @@ struct ChunkLayout {
   static constexpr size_t O_DY = O_DL + size_t(CH) * LDR * 2;   // dY
   static constexpr size_t O_S = O_DY + size_t(CH) * LDR * 2;    // S^T half [64][DK]
   static constexpr size_t O_DS = O_S + KB;           // dS'^T half
-  static constexpr size_t O_RED = O_DS + KB;         // dbeta[64], dg[64], <dS', S>
-  static constexpr size_t TOTAL = O_RED + (2 * CH + 4) * 4;
+  // Partial row sums, each written by one wave and added in a fixed order (no
+  // atomics, so the result does not depend on the order the waves run in):
+  // dbeta over d_v tiles [4][64] and over column blocks [4][64]; dg row sums [4][64],
+  // column sums [4][64] and d_k tiles [DK / 16][64]; two per-wave scalars [8] x 2.
+  static constexpr size_t O_RED = O_DS + KB;
+  static constexpr size_t NRED = (4 + 4 + 4 + 4 + DK / 16) * CH + 16;
+  static constexpr size_t TOTAL = O_RED + NRED * 4;
 };
 
-// Sum over the 16 lanes of a row (lanes with one lg), returned to all of them.
+// Sum over the 16 lanes of a row (lanes with one lg), returned to all of them;
+// the pairing is fixed, so the result is the same on every run.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
@@ -480,6 +486,12 @@ __device__ __forceinline__ float row16_sum(float v) {
   v += dpp<0x124>(v);   // row_ror:4
   v += dpp<0x122>(v);   // row_ror:2
   v += dpp<0x121>(v);   // row_ror:1
+  return v;
+}
+// Sum over the four lanes with one lr (lanes lr, lr + 16, lr + 32, lr + 48).
+__device__ __forceinline__ float lg_sum(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
   return v;
 }
 
@@ -508,9 +520,13 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdParams p) {
   T* sdY = reinterpret_cast<T*>(smem + L::O_DY);
   T* sS = reinterpret_cast<T*>(smem + L::O_S);
   T* sdS = reinterpret_cast<T*>(smem + L::O_DS);
-  float* sdb = reinterpret_cast<float*>(smem + L::O_RED);
-  float* sdg = sdb + CH;
-  float* sred = sdg + CH;
+  float* rbX = reinterpret_cast<float*>(smem + L::O_RED);   // dbeta: [c][r], sum_v dY X of d_v tile c
+  float* rbA = rbX + 4 * CH;            // dbeta: [J][r], the dA term of column block J
+  float* rgA = rbA + 4 * CH;            // dg: [J][r], row sums of dA*A + dP*P over column block J
+  float* rgC = rgA + 4 * CH;            // dg: [R][j], column sums of the same over row block R
+  float* rgK = rgC + 4 * CH;            // dg: [ic][r], the row dots over d_k tile ic
+  float* rcs = rgK + (DK / 16) * CH;    // [wave]: sum_r c_r
+  float* rsd = rcs + 8;                 // [wave]: <dS', S>
 
   const ChunkParams& f = p.f;
   const int64_t nch = (f.T + CH - 1) / CH;
@@ -599,7 +615,6 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdParams p) {
       put16(sT + (16 * J + a) * LCP + 16 * R + b0, ht);
     }
     if (tid < 96) *reinterpret_cast<u32x4*>(smem + L::O_F + tid * 16) = hf;
-    if (tid < 2 * CH + 4) sdb[tid] = 0.f;
     load_half(0);
     __syncthreads();
 
@@ -784,22 +799,27 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdParams p) {
         }
         st_row(sAk, LCP, r, 16 * J + 4 * lg, ak);
         st_row(sP, LCP, r, 16 * J + 4 * lg, pk);
-        atomicAdd(&sdb[r], db);
+        db = lg_sum(db);
+        if (lg == 0) rbA[J * CH + r] = db;
         if constexpr (G) {
-          atomicAdd(&sdg[r], rsum);
+          rsum = lg_sum(rsum);
+          if (lg == 0) rgA[J * CH + r] = rsum;
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
             const float x = row16_sum(csum[s]);
-            if (lr == 0) atomicAdd(&sdg[16 * J + 4 * lg + s], -x);
+            if (lr == 0) rgC[R * CH + 16 * J + 4 * lg + s] = x;
           }
         }
       }
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) atomicAdd(&sdb[16 * ((wave >> 2) + 2 * i) + lr], dbx[i]);
+    for (int i = 0; i < 2; ++i) {       // tile (M, c) = ((wave + 8 i) / 4, wave % 4)
+      const float x = lg_sum(dbx[i]);
+      if (lg == 0) rbX[(wave & 3) * CH + 16 * ((wave >> 2) + 2 * i) + lr] = x;
+    }
     if constexpr (G) {
-      const float x = row16_sum(sdot);
-      if (lr == 0) atomicAdd(sred, x);
+      const float x = lg_sum(row16_sum(sdot));
+      if (lane == 0) rsd[wave] = x;
     }
     __syncthreads();
 
@@ -839,23 +859,41 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdParams p) {
           a += eg * qq[s] * dOS[i][s] - br * er * kk[s] * dYS[i][s];
           c += ed * kk[s] * DdS[i][s];
         }
-        atomicAdd(&sdg[r], a - c);
+        a = lg_sum(a - c);
+        if (lg == 0) rgK[ic * CH + r] = a;
         csum += c;
       }
     }
     if constexpr (G) {
-      const float x = row16_sum(csum);
-      if (lr == 0) atomicAdd(&sdg[CH - 1], x);
+      const float x = lg_sum(row16_sum(csum));
+      if (lane == 0) rcs[wave] = x;
     }
     __syncthreads();
 
     // ---- dbeta, d log a (suffix sums of dg over the chunk) ----------------------------
     if (wave == 0) {
+      const int r = lane, Rr = r >> 4;
       const uint32_t off = static_cast<uint32_t>(lane * H * 2);
-      buf_store2(f32_to_bf16_bits(sdb[lane]), rdb, off, sb);
+      float db = 0.f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) db += rbX[c * CH + r];
+      for (int J = 0; J <= Rr; ++J) db += rbA[J * CH + r];
+      buf_store2(f32_to_bf16_bits(db), rdb, off, sb);
       if constexpr (G) {
-        float x = sdg[lane];
-        if (lane == CH - 1) x += sF[4 * CH] * sred[0];
+        float x = 0.f;
+        for (int J = 0; J <= Rr; ++J) x += rgA[J * CH + r];
+        for (int R = Rr; R < 4; ++R) x -= rgC[R * CH + r];
+#pragma unroll
+        for (int ic = 0; ic < DK / 16; ++ic) x += rgK[ic * CH + r];
+        if (lane == CH - 1) {
+          float cs = 0.f, sd = 0.f;
+#pragma unroll
+          for (int w = 0; w < NW; ++w) {
+            cs += rcs[w];
+            sd += rsd[w];
+          }
+          x += cs + sF[4 * CH] * sd;
+        }
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
           const float y = __shfl_down(x, d);

@@ -172,3 +172,13 @@ def test_bwd_full_size_sampled():
         for n in ("dq", "dk", "dv", "dbeta", "dlog_a"):
             check(f"{n}[b={b},h={h}]", host(g[n][b, :, h]), ref[n][0, :, 0], TOL["bf16"])
         check(f"dS0[b={b},h={h}]", host(g["dS0"][b, h]), ref["dS0"][0, 0], TOL["bf16"])
+
+
+def test_bwd_deterministic():
+    """Two calls on the same inputs give the same bits (no atomics; every sum is
+    taken in a fixed order)."""
+    need_gpu()
+    x = _inputs(2, 300, 3, 128, 128, "scalar", seed=29)
+    a, b = _gpu(x), _gpu(x)
+    for n in NAMES:
+        assert np.array_equal(a[n], b[n]), n
