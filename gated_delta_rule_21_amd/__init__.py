@@ -6,7 +6,7 @@ Public calls (thin wrappers over the C ABI in include/gdr.h):
     recurrent_step(q, k, v, beta, log_a, S, form="page")               -> (o, S_new)
     precond_scan(k, beta, eta, r=None, d0=None)                        -> (kw, d_T), the write keys
                                                                           of the preconditioned rule
-    chunk_bwd(q, k, v, beta, log_a, S0, dO, dS_T=None)                 -> dict of dq, dk, dv, dbeta,
+    chunk_bwd(q, k, v, beta, log_a, S0, dO, dS_T=None, cu_seqlens=None) -> dict of dq, dk, dv, dbeta,
                                                                           dlog_a, dS0 (the gradients)
     chunk_workspace_size(B, T, H, d_k, d_v, dtype, gate)               -> bytes of scratch
     chunk_varlen_workspace_size(T, n_seq, H, d_k, d_v, dtype, gate)    -> bytes of scratch

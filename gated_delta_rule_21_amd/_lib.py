@@ -25,7 +25,8 @@ FORMS = {"page": 0, "literal": 1}
 EXPORTED = ("gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_chunk_fwd_varlen_workspace_size",
             "gdr_chunk_fwd_varlen", "gdr_recurrent_step", "gdr_chunk_fwd_wkey", "gdr_recurrent_step_wkey",
             "gdr_precond_scan", "gdr_status_string", "gdr_last_error", "gdr_version",
-            "gdr_chunk_bwd_workspace_size", "gdr_chunk_bwd")
+            "gdr_chunk_bwd_workspace_size", "gdr_chunk_bwd", "gdr_chunk_bwd_varlen_workspace_size",
+            "gdr_chunk_bwd_varlen")
 
 
 class GdrDesc(ctypes.Structure):
@@ -79,6 +80,12 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         lib.gdr_chunk_bwd_workspace_size.argtypes = [ctypes.POINTER(GdrDesc), ctypes.POINTER(ctypes.c_size_t)]
         lib.gdr_chunk_bwd.restype = ctypes.c_int
         lib.gdr_chunk_bwd.argtypes = [ctypes.POINTER(GdrDesc)] + [vp] * 15 + [ctypes.c_size_t, vp]
+        lib.gdr_chunk_bwd_varlen_workspace_size.restype = ctypes.c_int
+        lib.gdr_chunk_bwd_varlen_workspace_size.argtypes = [ctypes.POINTER(GdrDesc), ctypes.c_int64,
+                                                            ctypes.POINTER(ctypes.c_size_t)]
+        lib.gdr_chunk_bwd_varlen.restype = ctypes.c_int
+        lib.gdr_chunk_bwd_varlen.argtypes = ([ctypes.POINTER(GdrDesc), vp, ctypes.c_int64] + [vp] * 15 +
+                                             [ctypes.c_size_t, vp])
         lib.gdr_status_string.argtypes = [ctypes.c_int]
         lib.gdr_last_error.restype = ctypes.c_char_p
         lib.gdr_last_error.argtypes = []
@@ -207,16 +214,28 @@ def chunk_bwd_workspace_size(B: int, T: int, H: int, d_k: int, d_v: int, dtype=t
     return int(n.value)
 
 
-def chunk_bwd(q, k, v, beta, log_a, S0, dO, dS_T=None, *, want_dS0: bool = True, workspace=None, stream=None):
+def chunk_bwd(q, k, v, beta, log_a, S0, dO, dS_T=None, *, cu_seqlens=None, want_dS0: bool = True, workspace=None,
+              stream=None):
     """gdr_chunk_bwd on torch tensors: the gradients of L = <dO, o> + <dS_T, S_T> for
     the forward chunk_fwd(q, k, v, beta, log_a, S0) (bf16 I/O, no gate or a scalar
     gate, decay before the erase).  dO [B, T, H, d_v] bf16; dS_T None or
-    [B, H, d_k, d_v] float32.  Returns dict(dq, dk, dv, dbeta, dlog_a, dS0) (dlog_a
-    None without a gate, dS0 None when want_dS0 is False).  Asynchronous on the
-    current (or given) stream."""
+    [B, H, d_k, d_v] float32.  With `cu_seqlens` (int32 device tensor [n_seq + 1])
+    the sequences are packed along T of [1, T, H, .] tensors (gdr_chunk_bwd_varlen)
+    and S0, dS_T, dS0 are [n_seq, H, d_k, d_v].  Returns dict(dq, dk, dv, dbeta,
+    dlog_a, dS0) (dlog_a None without a gate, dS0 None when want_dS0 is False).
+    Asynchronous on the current (or given) stream."""
     lib = load()
     B, T, H, dk = k.shape
     dv = v.shape[-1]
+    packed = cu_seqlens is not None
+    if packed:
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.device != q.device:
+            raise ValueError("cu_seqlens must be an int32 vector on the inputs' device")
+        if B != 1:
+            raise ValueError("packed sequences take [1, T, H, d] tensors")
+        nstate = cu_seqlens.numel() - 1
+    else:
+        nstate = B
     dt = q.dtype
     _require(q, "q", dt, (B, T, H, dk))
     _require(k, "k", dt, (B, T, H, dk))
@@ -227,23 +246,29 @@ def chunk_bwd(q, k, v, beta, log_a, S0, dO, dS_T=None, *, want_dS0: bool = True,
     if log_a is not None:
         _require(log_a, "log_a", dt, tuple(log_a.shape))
     if S0 is not None:
-        _require(S0, "S0", torch.float32, (B, H, dk, dv))
+        _require(S0, "S0", torch.float32, (nstate, H, dk, dv))
     if dS_T is not None:
-        _require(dS_T, "dS_T", torch.float32, (B, H, dk, dv))
+        _require(dS_T, "dS_T", torch.float32, (nstate, H, dk, dv))
     out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v), dbeta=torch.empty_like(beta),
                dlog_a=torch.empty_like(log_a) if log_a is not None else None,
-               dS0=torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device) if want_dS0 else None)
+               dS0=torch.empty((nstate, H, dk, dv), dtype=torch.float32, device=q.device) if want_dS0 else None)
     desc = GdrDesc(B, T, H, dk, dv, 64, _io_of(q), gate, 0)
     need = ctypes.c_size_t(0)
-    _check(lib, lib.gdr_chunk_bwd_workspace_size(ctypes.byref(desc), ctypes.byref(need)))
+    if packed:
+        _check(lib, lib.gdr_chunk_bwd_varlen_workspace_size(ctypes.byref(desc), nstate, ctypes.byref(need)))
+    else:
+        _check(lib, lib.gdr_chunk_bwd_workspace_size(ctypes.byref(desc), ctypes.byref(need)))
     if workspace is None:
         workspace = torch.empty(max(int(need.value), 1), dtype=torch.uint8, device=q.device)
     if workspace.dtype != torch.uint8 or not workspace.is_contiguous() or workspace.device != q.device:
         raise ValueError("workspace must be a contiguous uint8 tensor on the inputs' device")
-    st = lib.gdr_chunk_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_a), _ptr(S0), _ptr(dO),
-                           _ptr(dS_T), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dbeta"]),
-                           _ptr(out["dlog_a"]), _ptr(out["dS0"]), _ptr(workspace), workspace.numel(),
-                           _stream_handle(stream))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_a), _ptr(S0), _ptr(dO), _ptr(dS_T), _ptr(out["dq"]),
+            _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dbeta"]), _ptr(out["dlog_a"]), _ptr(out["dS0"]),
+            _ptr(workspace), workspace.numel(), _stream_handle(stream))
+    if packed:
+        st = lib.gdr_chunk_bwd_varlen(ctypes.byref(desc), _ptr(cu_seqlens), nstate, *args)
+    else:
+        st = lib.gdr_chunk_bwd(ctypes.byref(desc), *args)
     _check(lib, st)
     return out
 

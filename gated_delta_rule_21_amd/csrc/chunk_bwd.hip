@@ -181,8 +181,18 @@ struct Slice {
     return make_rsrc(static_cast<const uint16_t*>(base) + row0 * width, span * width * 2);
   }
 };
-__device__ __forceinline__ Slice slice_of(const ChunkParams& f, int64_t bb, int64_t hh) {
-  return Slice{bb * f.T * f.H + hh, static_cast<uint32_t>(f.T > 0 ? (f.T - 1) * f.H + 1 : 0)};
+// One (sequence, head): its token rows, chunks, and first record slot (the per-chunk
+// records and both sets of chunk states are addressed by the same slots).
+// Fixed-length batches: [B, T, H, .] tensors; packed sequences (f.cu set): tokens
+// cu[b] .. cu[b+1] - 1 of [1, T, H, .] tensors (see seq_span).
+struct BwdSeq {
+  Slice sl;
+  int64_t nch, rec0;
+};
+__device__ __forceinline__ BwdSeq bwd_seq_of(const ChunkParams& f, int64_t bb, int64_t hh) {
+  const SeqSpan sp = seq_span(f, bb, hh);
+  return BwdSeq{Slice{sp.t0 * f.H + hh, static_cast<uint32_t>(sp.len > 0 ? (sp.len - 1) * f.H + 1 : 0)},
+                (sp.len + CH - 1) / CH, sp.rec0};
 }
 
 // Pass 1: the state entering every chunk, stored in bf16 value-major.  lb is the
@@ -200,12 +210,13 @@ __device__ __forceinline__ void states_pass(const BwdParams& p, int n_tiles, int
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   const int scol = col0 + 16 * wave + lr;
-  const int64_t nch = (f.T + CH - 1) / CH;
-  const Slice sl = slice_of(f, bb, hh);
+  const BwdSeq sq = bwd_seq_of(f, bb, hh);
+  const int64_t nch = sq.nch;
+  const Slice sl = sq.sl;
   const rsrc_t rk = sl.rs(f.k, DK), rv = sl.rs(f.v, dv);
-  const rsrc_t rw = make_rsrc(static_cast<const char*>(f.ws) + bh * nch * W::BYTES, static_cast<uint32_t>(nch * W::BYTES));
+  const rsrc_t rw = make_rsrc(static_cast<const char*>(f.ws) + sq.rec0 * W::BYTES, static_cast<uint32_t>(nch * W::BYTES));
   const uint32_t sbytes = static_cast<uint32_t>(dv * DK * 2);   // one chunk's state
-  const rsrc_t rst = make_rsrc(static_cast<char*>(p.states) + bh * nch * sbytes, static_cast<uint32_t>(nch * sbytes));
+  const rsrc_t rst = make_rsrc(static_cast<char*>(p.states) + sq.rec0 * sbytes, static_cast<uint32_t>(nch * sbytes));
 
   f32x4 S[DKT];   // S[t][s] = S[16t + 4lg + s][scol]
 #pragma unroll
@@ -298,12 +309,13 @@ __device__ __forceinline__ void reverse_pass(const BwdParams& p, int n_tiles, in
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   const int scol = col0 + 16 * wave + lr;
-  const int64_t nch = (f.T + CH - 1) / CH;
-  const Slice sl = slice_of(f, bb, hh);
+  const BwdSeq sq = bwd_seq_of(f, bb, hh);
+  const int64_t nch = sq.nch;
+  const Slice sl = sq.sl;
   const rsrc_t rk = sl.rs(f.k, DK), rq = sl.rs(f.q, DK), rdo = sl.rs(p.dO, dv);
-  const rsrc_t rw = make_rsrc(static_cast<const char*>(f.ws) + bh * nch * W::BYTES, static_cast<uint32_t>(nch * W::BYTES));
+  const rsrc_t rw = make_rsrc(static_cast<const char*>(f.ws) + sq.rec0 * W::BYTES, static_cast<uint32_t>(nch * W::BYTES));
   const uint32_t sbytes = static_cast<uint32_t>(dv * DK * 2);
-  const rsrc_t rds = make_rsrc(static_cast<char*>(p.dstates) + bh * nch * sbytes, static_cast<uint32_t>(nch * sbytes));
+  const rsrc_t rds = make_rsrc(static_cast<char*>(p.dstates) + sq.rec0 * sbytes, static_cast<uint32_t>(nch * sbytes));
   T* sP = reinterpret_cast<T*>(smem + L::O_P);
 
   f32x4 dS[DKT];   // dS[t][s] = dS[16t + 4lg + s][scol]
@@ -529,41 +541,41 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdParams p) {
   float* rsd = rcs + 8;                 // [wave]: <dS', S>
 
   const ChunkParams& f = p.f;
-  const int64_t nch = (f.T + CH - 1) / CH;
   const int H = static_cast<int>(f.H);
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   constexpr uint32_t SBYTES = DV * DK * 2;          // one chunk's state
 
-  // q, k, the T blocks and the factor rows of one chunk, in registers
-  u32x4 hq[KP], hk[KP], ht, hf;
-  auto load_qk = [&](int64_t task) __attribute__((always_inline)) {
-    const int64_t n = task % nch, bh = task / nch;
-    const Slice sl = slice_of(f, bh / f.H, bh % f.H);
-    const rsrc_t rq = sl.rs(f.q, DK), rk = sl.rs(f.k, DK);
-    const rsrc_t rw = make_rsrc(static_cast<const char*>(f.ws) + bh * nch * W::BYTES, static_cast<uint32_t>(nch * W::BYTES));
-    const uint32_t sk = static_cast<uint32_t>(n * CH * H * DK * 2), sw = static_cast<uint32_t>(n * W::BYTES);
-#pragma unroll
-    for (int i = 0; i < KP; ++i) {
-      const int pc = tid + i * NT;
-      const uint32_t off = static_cast<uint32_t>(((pc / KR) * H * DK + (pc % KR) * 8) * 2);
-      hq[i] = buf_load16(rq, off, sk);
-      hk[i] = buf_load16(rk, off, sk);
-    }
-    if (tid < 320) ht = buf_load16(rw, W::T_OFF + static_cast<uint32_t>(tid * 16), sw);
-    if (tid < 96) hf = buf_load16(rw, W::F_OFF + static_cast<uint32_t>(tid * 16), sw);
-  };
+  // The workgroup's chunk: tasks as for the per-chunk transform (head fastest);
+  // with packed sequences a slot past its sequence's end has no chunk.
+  int64_t bb, n, hh;
+  if (!prep_task(f, blockIdx.x, bb, n, hh)) return;
+  const BwdSeq sq = bwd_seq_of(f, bb, hh);
+  const int64_t nch = sq.nch;
+  const Slice sl = sq.sl;
   {
-    const int64_t task = blockIdx.x;
-    load_qk(task);
-    const int64_t n = task % nch, bh = task / nch;
-    const Slice sl = slice_of(f, bh / f.H, bh % f.H);
+    // q, k, the T blocks and the factor rows of the chunk
+    u32x4 hq[KP], hk[KP], ht, hf;
+    {
+      const rsrc_t rq = sl.rs(f.q, DK), rk = sl.rs(f.k, DK);
+      const rsrc_t rw = make_rsrc(static_cast<const char*>(f.ws) + sq.rec0 * W::BYTES, static_cast<uint32_t>(nch * W::BYTES));
+      const uint32_t sk = static_cast<uint32_t>(n * CH * H * DK * 2), sw = static_cast<uint32_t>(n * W::BYTES);
+#pragma unroll
+      for (int i = 0; i < KP; ++i) {
+        const int pc = tid + i * NT;
+        const uint32_t off = static_cast<uint32_t>(((pc / KR) * H * DK + (pc % KR) * 8) * 2);
+        hq[i] = buf_load16(rq, off, sk);
+        hk[i] = buf_load16(rk, off, sk);
+      }
+      if (tid < 320) ht = buf_load16(rw, W::T_OFF + static_cast<uint32_t>(tid * 16), sw);
+      if (tid < 96) hf = buf_load16(rw, W::F_OFF + static_cast<uint32_t>(tid * 16), sw);
+    }
     const rsrc_t rv = sl.rs(f.v, DV), rdo = sl.rs(p.dO, DV);
     const rsrc_t rdq = sl.rs(p.dq, DK), rdk = sl.rs(p.dk, DK), rdv = sl.rs(p.dv, DV);
     const rsrc_t rdb = sl.rs(p.dbeta, 1), rdl = sl.rs(p.dlog_a, G ? 1 : 0);
-    const rsrc_t rst = make_rsrc(static_cast<const char*>(p.states) + bh * nch * SBYTES, static_cast<uint32_t>(nch * SBYTES));
-    const rsrc_t rds = make_rsrc(static_cast<const char*>(p.dstates) + bh * nch * SBYTES, static_cast<uint32_t>(nch * SBYTES));
+    const rsrc_t rst = make_rsrc(static_cast<const char*>(p.states) + sq.rec0 * SBYTES, static_cast<uint32_t>(nch * SBYTES));
+    const rsrc_t rds = make_rsrc(static_cast<const char*>(p.dstates) + sq.rec0 * SBYTES, static_cast<uint32_t>(nch * SBYTES));
     const uint32_t sk = static_cast<uint32_t>(n * CH * H * DK * 2);   // chunk start in q, k (bytes)
     const uint32_t sv = static_cast<uint32_t>(n * CH * H * DV * 2);   // ... in v, dO
     const uint32_t ss = static_cast<uint32_t>(n) * SBYTES;
@@ -921,7 +933,7 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
                      static_cast<int>(nseq));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const unsigned grid = static_cast<unsigned>(f.B * f.H * nch);
+  const unsigned grid = static_cast<unsigned>(f.cu ? f.H * f.nslots : f.B * f.H * nch);
   if (f.d_v == 128)
     hipLaunchKernelGGL((bwd_chunk_kernel<GATE, DK, 128>), dim3(grid), dim3(512), 0, stream, p);
   else
@@ -946,11 +958,19 @@ size_t chunk_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int d_k, int d
   return chunk_workspace_bytes(B, T, H, IO_BF16, GATE_SCALAR, d_k) + 2 * chunk_bwd_state_bytes(B, T, H, d_k, d_v);
 }
 
+size_t chunk_bwd_varlen_state_bytes(int64_t T, int64_t n_seq, int64_t H, int d_k, int d_v) {
+  return static_cast<size_t>(H * chunk_varlen_slots(T, n_seq)) * static_cast<size_t>(d_k) * static_cast<size_t>(d_v) * 2u;
+}
+
+size_t chunk_bwd_varlen_workspace_bytes(int64_t T, int64_t n_seq, int64_t H, int d_k, int d_v) {
+  return chunk_varlen_records_bytes(T, n_seq, H, IO_BF16, GATE_SCALAR, d_k) +
+         2 * chunk_bwd_varlen_state_bytes(T, n_seq, H, d_k, d_v);
+}
+
 hipError_t launch_chunk_bwd(const BwdParams& p, hipStream_t stream) {
   const ChunkParams& f = p.f;
   if (f.B * f.H == 0) return hipSuccess;
-  if (f.io != IO_BF16 || f.literal || f.cu || f.kw || (f.gate != GATE_NONE && f.gate != GATE_SCALAR))
-    return hipErrorInvalidValue;
+  if (f.io != IO_BF16 || f.literal || f.kw || (f.gate != GATE_NONE && f.gate != GATE_SCALAR)) return hipErrorInvalidValue;
   if (f.T == 0) {
     if (!p.dS0) return hipSuccess;
     const int64_t n = f.B * f.H * f.d_k * f.d_v;

@@ -97,6 +97,16 @@ gdr_status check_bwd_desc(const gdr_desc* d) {
   return GDR_OK;
 }
 
+// Packed sequences: the descriptor's B is 1 and T counts all tokens.
+gdr_status check_packed(const gdr_desc* d, int64_t n_seq) {
+  if (n_seq < 1) return fail(GDR_ERR_INVALID_ARG, "n_seq = %lld must be >= 1", (long long)n_seq);
+  if (d->B != 1) return fail(GDR_ERR_INVALID_ARG, "B = %lld: packed sequences take B = 1 (all tokens in T)", (long long)d->B);
+  int64_t x;
+  if (!mul_ok(n_seq, d->H, &x) || x * 8 > INT32_MAX || d->H * gdr::chunk_varlen_slots(d->T, n_seq) > INT32_MAX)
+    return fail(GDR_ERR_UNSUPPORTED, "n_seq = %lld: exceeds the grid limit", (long long)n_seq);
+  return GDR_OK;
+}
+
 gdr_status check_align(const char* name, const void* p, uintptr_t a) {
   if (p && (reinterpret_cast<uintptr_t>(p) % a) != 0)
     return fail(GDR_ERR_ALIGNMENT, "%s = %p is not %u-byte aligned", name, p, (unsigned)a);
@@ -313,6 +323,82 @@ gdr_status recurrent_step_impl(const gdr_desc* d, const void* q, const void* k, 
 
 }  // namespace
 
+namespace {
+
+// The backward over fixed-length batches (cu == nullptr) or packed sequences.
+gdr_status chunk_bwd_impl(const gdr_desc* d, const int32_t* cu, int64_t n_seq, const void* q, const void* k,
+                          const void* v, const void* beta, const void* log_a, const float* S0, const void* dO,
+                          const float* dS_T, void* dq, void* dk, void* dv, void* dbeta, void* dlog_a, float* dS0,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  gdr_status st = check_bwd_desc(d);
+  if (st != GDR_OK) return st;
+  const bool packed = cu != nullptr;
+  if (packed && (st = check_packed(d, n_seq)) != GDR_OK) return st;
+  const int64_t nseq = packed ? n_seq : d->B;       // sequences, and states in S0 / dS_T / dS0
+  const bool gated = d->gate == GDR_GATE_SCALAR;
+  const int dk_ = static_cast<int>(d->d_k), dv_ = static_cast<int>(d->d_v);
+  const size_t ws_need = d->T == 0 ? 0
+                         : packed  ? gdr::chunk_bwd_varlen_workspace_bytes(d->T, n_seq, d->H, dk_, dv_)
+                                   : gdr::chunk_bwd_workspace_bytes(d->B, d->T, d->H, dk_, dv_);
+  if (d->T > 0) {
+    const void* req[] = {q, k, v, beta, dO, dq, dk, dv, dbeta};
+    const char* names[] = {"q", "k", "v", "beta", "dO", "dq", "dk", "dv", "dbeta"};
+    for (int i = 0; i < 9; ++i)
+      if (!req[i]) return fail(GDR_ERR_INVALID_ARG, "%s is NULL", names[i]);
+    if (gated && !log_a) return fail(GDR_ERR_INVALID_ARG, "log_a is NULL but a gate is requested");
+    if (gated && !dlog_a) return fail(GDR_ERR_INVALID_ARG, "dlog_a is NULL but a gate is requested");
+    if (!workspace) return fail(GDR_ERR_INVALID_ARG, "workspace is NULL (%zu bytes needed)", ws_need);
+    if (workspace_bytes < ws_need)
+      return fail(GDR_ERR_INVALID_ARG, "workspace_bytes = %zu, %zu needed", workspace_bytes, ws_need);
+  }
+  if (!gated && log_a) return fail(GDR_ERR_INVALID_ARG, "log_a must be NULL for GDR_GATE_NONE");
+  if (!gated && dlog_a) return fail(GDR_ERR_INVALID_ARG, "dlog_a must be NULL for GDR_GATE_NONE");
+  if ((st = check_align("q", q, 16)) || (st = check_align("k", k, 16)) || (st = check_align("v", v, 16)) ||
+      (st = check_align("dO", dO, 16)) || (st = check_align("dq", dq, 16)) || (st = check_align("dk", dk, 16)) ||
+      (st = check_align("dv", dv, 16)) || (st = check_align("S0", S0, 16)) || (st = check_align("dS_T", dS_T, 16)) ||
+      (st = check_align("dS0", dS0, 16)) || (st = check_align("beta", beta, 2)) ||
+      (st = check_align("dbeta", dbeta, 2)) || (st = check_align("log_a", log_a, 2)) ||
+      (st = check_align("dlog_a", dlog_a, 2)) || (st = check_align("workspace", workspace, 16)) ||
+      (st = check_align("cu_seqlens", cu, 4)))
+    return st;
+  const int64_t ntok = d->B * d->T * d->H;
+  const int64_t state_bytes = nseq * d->H * d->d_k * d->d_v * 4;
+  Span all[] = {span("q", q, ntok * d->d_k * 2), span("k", k, ntok * d->d_k * 2),
+                span("v", v, ntok * d->d_v * 2), span("beta", beta, ntok * 2),
+                span("log_a", log_a, gated ? ntok * 2 : 0), span("S0", S0, state_bytes),
+                span("dO", dO, ntok * d->d_v * 2), span("dS_T", dS_T, state_bytes),
+                span("cu_seqlens", cu, packed ? (n_seq + 1) * 4 : 0),
+                span("dq", dq, ntok * d->d_k * 2), span("dk", dk, ntok * d->d_k * 2),
+                span("dv", dv, ntok * d->d_v * 2), span("dbeta", dbeta, ntok * 2),
+                span("dlog_a", dlog_a, gated ? ntok * 2 : 0), span("dS0", dS0, state_bytes),
+                span("workspace", d->T > 0 ? workspace : nullptr, static_cast<int64_t>(ws_need))};
+  Span outs[] = {all[9], all[10], all[11], all[12], all[13], all[14], all[15]};
+  if (dS0 && dS0 == dS_T) all[7].hi = all[7].lo;   // the final-state gradient may be overwritten by dS0
+  if ((st = check_no_overlap(outs, 7, all, 16))) return st;
+
+  gdr::BwdParams p;
+  gdr::ChunkParams& f = p.f;
+  f.q = q; f.k = k; f.v = v; f.beta = beta; f.log_a = log_a; f.S0 = S0; f.o = nullptr; f.S_T = nullptr;
+  f.ws = workspace;
+  f.B = nseq; f.T = d->T; f.H = d->H;
+  f.d_k = dk_; f.d_v = dv_;
+  f.io = d->io; f.gate = d->gate; f.literal = 0;
+  f.cu = cu; f.nslots = packed ? gdr::chunk_varlen_slots(d->T, n_seq) : 0; f.order = nullptr; f.kw = nullptr;
+  p.dO = dO; p.dS_T = dS_T; p.dq = dq; p.dk = dk; p.dv = dv; p.dbeta = dbeta; p.dlog_a = dlog_a; p.dS0 = dS0;
+  const size_t rec = packed ? gdr::chunk_varlen_records_bytes(d->T, n_seq, d->H, d->io, d->gate, dk_)
+                            : gdr::chunk_workspace_bytes(d->B, d->T, d->H, d->io, d->gate, dk_);
+  const size_t sb = packed ? gdr::chunk_bwd_varlen_state_bytes(d->T, n_seq, d->H, dk_, dv_)
+                           : gdr::chunk_bwd_state_bytes(d->B, d->T, d->H, dk_, dv_);
+  p.states = d->T > 0 ? static_cast<char*>(workspace) + rec : nullptr;
+  p.dstates = d->T > 0 ? static_cast<char*>(workspace) + rec + sb : nullptr;
+  if (d->T == 0 && !dS0) return GDR_OK;
+  hipError_t e = gdr::launch_chunk_bwd(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(GDR_ERR_HIP, "chunk backward launch failed: %s", hipGetErrorString(e));
+  return GDR_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 gdr_status gdr_recurrent_step(const gdr_desc* d, const void* q, const void* k, const void* v, const void* beta,
@@ -403,7 +489,6 @@ gdr_status gdr_chunk_fwd_wkey(const gdr_desc* d, const void* q, const void* k, c
   }
 }
 
-
 gdr_status gdr_chunk_bwd_workspace_size(const gdr_desc* d, size_t* bytes) {
   try {
     g_last_error.clear();
@@ -418,68 +503,45 @@ gdr_status gdr_chunk_bwd_workspace_size(const gdr_desc* d, size_t* bytes) {
   }
 }
 
+gdr_status gdr_chunk_bwd_varlen_workspace_size(const gdr_desc* d, int64_t n_seq, size_t* bytes) {
+  try {
+    g_last_error.clear();
+    if (!bytes) return fail(GDR_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = 0;
+    gdr_status st = check_bwd_desc(d);
+    if (st != GDR_OK) return st;
+    if ((st = check_packed(d, n_seq)) != GDR_OK) return st;
+    *bytes = d->T > 0 ? gdr::chunk_bwd_varlen_workspace_bytes(d->T, n_seq, d->H, static_cast<int>(d->d_k),
+                                                              static_cast<int>(d->d_v))
+                      : 0;
+    return GDR_OK;
+  } catch (...) {
+    return fail(GDR_ERR_INVALID_ARG, "internal error");
+  }
+}
+
 gdr_status gdr_chunk_bwd(const gdr_desc* d, const void* q, const void* k, const void* v, const void* beta,
                          const void* log_a, const float* S0, const void* dO, const float* dS_T, void* dq, void* dk,
                          void* dv, void* dbeta, void* dlog_a, float* dS0, void* workspace, size_t workspace_bytes,
                          void* stream) {
   try {
     g_last_error.clear();
-    gdr_status st = check_bwd_desc(d);
-    if (st != GDR_OK) return st;
-    const bool gated = d->gate == GDR_GATE_SCALAR;
-    const size_t ws_need =
-        d->T > 0 ? gdr::chunk_bwd_workspace_bytes(d->B, d->T, d->H, static_cast<int>(d->d_k), static_cast<int>(d->d_v)) : 0;
-    if (d->T > 0) {
-      const void* req[] = {q, k, v, beta, dO, dq, dk, dv, dbeta};
-      const char* names[] = {"q", "k", "v", "beta", "dO", "dq", "dk", "dv", "dbeta"};
-      for (int i = 0; i < 9; ++i)
-        if (!req[i]) return fail(GDR_ERR_INVALID_ARG, "%s is NULL", names[i]);
-      if (gated && !log_a) return fail(GDR_ERR_INVALID_ARG, "log_a is NULL but a gate is requested");
-      if (gated && !dlog_a) return fail(GDR_ERR_INVALID_ARG, "dlog_a is NULL but a gate is requested");
-      if (!workspace) return fail(GDR_ERR_INVALID_ARG, "workspace is NULL (%zu bytes needed)", ws_need);
-      if (workspace_bytes < ws_need)
-        return fail(GDR_ERR_INVALID_ARG, "workspace_bytes = %zu, %zu needed", workspace_bytes, ws_need);
-    }
-    if (!gated && log_a) return fail(GDR_ERR_INVALID_ARG, "log_a must be NULL for GDR_GATE_NONE");
-    if (!gated && dlog_a) return fail(GDR_ERR_INVALID_ARG, "dlog_a must be NULL for GDR_GATE_NONE");
-    if ((st = check_align("q", q, 16)) || (st = check_align("k", k, 16)) || (st = check_align("v", v, 16)) ||
-        (st = check_align("dO", dO, 16)) || (st = check_align("dq", dq, 16)) || (st = check_align("dk", dk, 16)) ||
-        (st = check_align("dv", dv, 16)) || (st = check_align("S0", S0, 16)) || (st = check_align("dS_T", dS_T, 16)) ||
-        (st = check_align("dS0", dS0, 16)) || (st = check_align("beta", beta, 2)) ||
-        (st = check_align("dbeta", dbeta, 2)) || (st = check_align("log_a", log_a, 2)) ||
-        (st = check_align("dlog_a", dlog_a, 2)) || (st = check_align("workspace", workspace, 16)))
-      return st;
-    const int64_t ntok = d->B * d->T * d->H;
-    const int64_t state_bytes = d->B * d->H * d->d_k * d->d_v * 4;
-    Span all[] = {span("q", q, ntok * d->d_k * 2), span("k", k, ntok * d->d_k * 2),
-                  span("v", v, ntok * d->d_v * 2), span("beta", beta, ntok * 2),
-                  span("log_a", log_a, gated ? ntok * 2 : 0), span("S0", S0, state_bytes),
-                  span("dO", dO, ntok * d->d_v * 2), span("dS_T", dS_T, state_bytes),
-                  span("dq", dq, ntok * d->d_k * 2), span("dk", dk, ntok * d->d_k * 2),
-                  span("dv", dv, ntok * d->d_v * 2), span("dbeta", dbeta, ntok * 2),
-                  span("dlog_a", dlog_a, gated ? ntok * 2 : 0), span("dS0", dS0, state_bytes),
-                  span("workspace", d->T > 0 ? workspace : nullptr, static_cast<int64_t>(ws_need))};
-    Span outs[] = {all[8], all[9], all[10], all[11], all[12], all[13], all[14]};
-    if (dS0 && dS0 == dS_T) all[7].hi = all[7].lo;   // the final-state gradient may be overwritten by dS0
-    if ((st = check_no_overlap(outs, 7, all, 15))) return st;
+    return chunk_bwd_impl(d, nullptr, 0, q, k, v, beta, log_a, S0, dO, dS_T, dq, dk, dv, dbeta, dlog_a, dS0, workspace,
+                          workspace_bytes, stream);
+  } catch (...) {
+    return fail(GDR_ERR_INVALID_ARG, "internal error");
+  }
+}
 
-    gdr::BwdParams p;
-    gdr::ChunkParams& f = p.f;
-    f.q = q; f.k = k; f.v = v; f.beta = beta; f.log_a = log_a; f.S0 = S0; f.o = nullptr; f.S_T = nullptr;
-    f.ws = workspace;
-    f.B = d->B; f.T = d->T; f.H = d->H;
-    f.d_k = static_cast<int>(d->d_k); f.d_v = static_cast<int>(d->d_v);
-    f.io = d->io; f.gate = d->gate; f.literal = 0;
-    f.cu = nullptr; f.nslots = 0; f.order = nullptr; f.kw = nullptr;
-    p.dO = dO; p.dS_T = dS_T; p.dq = dq; p.dk = dk; p.dv = dv; p.dbeta = dbeta; p.dlog_a = dlog_a; p.dS0 = dS0;
-    const size_t rec = gdr::chunk_workspace_bytes(d->B, d->T, d->H, d->io, d->gate, static_cast<int>(d->d_k));
-    const size_t sb = gdr::chunk_bwd_state_bytes(d->B, d->T, d->H, static_cast<int>(d->d_k), static_cast<int>(d->d_v));
-    p.states = d->T > 0 ? static_cast<char*>(workspace) + rec : nullptr;
-    p.dstates = d->T > 0 ? static_cast<char*>(workspace) + rec + sb : nullptr;
-    if (d->T == 0 && !dS0) return GDR_OK;
-    hipError_t e = gdr::launch_chunk_bwd(p, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return fail(GDR_ERR_HIP, "chunk backward launch failed: %s", hipGetErrorString(e));
-    return GDR_OK;
+gdr_status gdr_chunk_bwd_varlen(const gdr_desc* d, const int32_t* cu_seqlens, int64_t n_seq, const void* q,
+                                const void* k, const void* v, const void* beta, const void* log_a, const float* S0,
+                                const void* dO, const float* dS_T, void* dq, void* dk, void* dv, void* dbeta,
+                                void* dlog_a, float* dS0, void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    g_last_error.clear();
+    if (!cu_seqlens) return fail(GDR_ERR_INVALID_ARG, "cu_seqlens is NULL");
+    return chunk_bwd_impl(d, cu_seqlens, n_seq, q, k, v, beta, log_a, S0, dO, dS_T, dq, dk, dv, dbeta, dlog_a, dS0,
+                          workspace, workspace_bytes, stream);
   } catch (...) {
     return fail(GDR_ERR_INVALID_ARG, "internal error");
   }

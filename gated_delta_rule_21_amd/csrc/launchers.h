@@ -55,8 +55,8 @@ struct PrecondParams {
   float eta;
 };
 // Backward of the chunk forward (bf16 I/O, no gate or a scalar gate, decay before
-// the erase): f carries the forward's inputs and the workspace records (f.ws);
-// o, S_T and the packed-sequence fields of f are unused.
+// the erase): f carries the forward's inputs, the workspace records (f.ws) and,
+// for packed sequences, cu and nslots; o, S_T and order are unused.
 struct BwdParams {
   ChunkParams f;
   const void* dO;       // [B, T, H, d_v] gradient of the output
@@ -92,6 +92,9 @@ hipError_t launch_chunk_bwd(const BwdParams& p, hipStream_t stream);
 // the transform's records, the chunk-start states, the chunk-end state gradients.
 size_t chunk_bwd_state_bytes(int64_t B, int64_t T, int64_t H, int d_k, int d_v);
 size_t chunk_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int d_k, int d_v);
+// Packed sequences: the records and the states by the slots of chunk_varlen_slots.
+size_t chunk_bwd_varlen_state_bytes(int64_t T, int64_t n_seq, int64_t H, int d_k, int d_v);
+size_t chunk_bwd_varlen_workspace_bytes(int64_t T, int64_t n_seq, int64_t H, int d_k, int d_v);
 // Longest-first order of packed sequences into `order` (n_seq int32).
 hipError_t launch_varlen_order(const ChunkParams& p, int32_t* order, hipStream_t stream);
 

@@ -300,7 +300,8 @@ gdr_status gdr_chunk_bwd_workspace_size(const gdr_desc* desc, size_t* bytes);
  *
  * Supported: bf16 I/O; GDR_GATE_NONE or GDR_GATE_SCALAR; GDR_FORM_PAGE (with
  * GDR_GATE_NONE either form, they coincide); d_k, d_v in {64, 128}; fixed-length
- * batches.  Anything else returns GDR_ERR_UNSUPPORTED.
+ * batches here, packed sequences through gdr_chunk_bwd_varlen.  Anything else
+ * returns GDR_ERR_UNSUPPORTED.
  *
  *   q, k, v, beta, log_a, S0   the forward's inputs, as for gdr_chunk_fwd (log_a
  *                              NULL for GDR_GATE_NONE; S0 NULL = zero state)
@@ -325,6 +326,36 @@ gdr_status gdr_chunk_bwd(const gdr_desc* desc, const void* q, const void* k, con
                          const void* log_a, const float* S0, const void* dO, const float* dS_T, void* dq, void* dk,
                          void* dv, void* dbeta, void* dlog_a, float* dS0, void* workspace, size_t workspace_bytes,
                          void* stream /* hipStream_t */);
+
+/*
+ * gdr_chunk_bwd_varlen_workspace_size -- scratch for gdr_chunk_bwd_varlen.
+ *
+ * The records of gdr_chunk_fwd_varlen (H * (ceil(T / 64) + n_seq) slots of 11776
+ * bytes) plus two bf16 d_k x d_v matrices per slot (0 when T == 0).  Returns the
+ * descriptor and n_seq errors of gdr_chunk_bwd_varlen; *bytes is 0 on error.
+ */
+gdr_status gdr_chunk_bwd_varlen_workspace_size(const gdr_desc* desc, int64_t n_seq, size_t* bytes);
+
+/*
+ * gdr_chunk_bwd_varlen -- gdr_chunk_bwd over variable-length sequences packed
+ * along T (training with packed sequences).
+ *
+ * The gradients of L = <dO, o> + <dS_T, S_T> for the forward
+ * gdr_chunk_fwd_varlen(desc, cu_seqlens, n_seq, q, k, v, beta, log_a, S0): sequence
+ * i is tokens cu_seqlens[i] .. cu_seqlens[i+1] - 1 of the packed tensors and
+ * starts from S0[i]; its gradients are those of that sequence alone.  Layouts as
+ * for gdr_chunk_fwd_varlen: desc->B == 1, desc->T the total token count, token
+ * tensors [1, T, H, .] (dO, dq, dk, dv like v, q, k; dbeta, dlog_a like beta);
+ * S0, dS_T, dS0 [n_seq, H, d_k, d_v] fp32.  cu_seqlens is the device int32 table
+ * of gdr_chunk_fwd_varlen, with the same requirements and the same behaviour on
+ * a malformed table (no access outside the tensors; results undefined).
+ * Supported and precision as for gdr_chunk_bwd; errors as for both calls.
+ */
+gdr_status gdr_chunk_bwd_varlen(const gdr_desc* desc, const int32_t* cu_seqlens, int64_t n_seq, const void* q,
+                                const void* k, const void* v, const void* beta, const void* log_a, const float* S0,
+                                const void* dO, const float* dS_T, void* dq, void* dk, void* dv, void* dbeta,
+                                void* dlog_a, float* dS0, void* workspace, size_t workspace_bytes,
+                                void* stream /* hipStream_t */);
 
 #ifdef __cplusplus
 }

@@ -334,3 +334,24 @@ def test_backward_argument_checks(lib):
     bad[9] = bad[1] + 64
     assert _bwd(lib, d, bad) == INVALID
     assert b"dk overlaps k" in lib.gdr_last_error()                        # ... the error is dk's
+
+
+def test_backward_varlen_checks(lib):
+    n = ctypes.c_size_t(7)
+    d = _desc(B=1, T=300, H=2)
+    assert lib.gdr_chunk_bwd_varlen_workspace_size(ctypes.byref(d), 5, ctypes.byref(n)) == OK
+    slots = 2 * (-(-300 // 64) + 5)
+    assert n.value == slots * (11776 + 4 * 128 * 128)
+    assert lib.gdr_chunk_bwd_varlen_workspace_size(ctypes.byref(d), 0, ctypes.byref(n)) == INVALID
+    assert lib.gdr_chunk_bwd_varlen_workspace_size(ctypes.byref(_desc(B=2, T=300)), 3, ctypes.byref(n)) == INVALID
+    assert lib.gdr_chunk_bwd_varlen_workspace_size(ctypes.byref(_desc(B=1, io=0)), 3, ctypes.byref(n)) == UNSUPPORTED
+    p = _ptrs(16)
+    call = lambda d, cu, ns, q=p: lib.gdr_chunk_bwd_varlen(ctypes.byref(d), cu, ns, *q[:14], q[14], 1 << 40, None)
+    assert call(d, None, 5) == INVALID                                     # no offsets table
+    assert b"cu_seqlens" in lib.gdr_last_error()
+    assert call(d, p[15], 0) == INVALID                                    # n_seq < 1
+    assert call(_desc(B=2, T=300), p[15], 5) == INVALID                    # B must be 1
+    assert call(d, p[15] + 2, 5) == ALIGN                                  # int32 table
+    bad = list(p)
+    bad[9] = bad[15]                                                       # dk over the offsets table
+    assert call(d, p[15], 5, bad) == INVALID

@@ -182,3 +182,65 @@ def test_bwd_deterministic():
     a, b = _gpu(x), _gpu(x)
     for n in NAMES:
         assert np.array_equal(a[n], b[n]), n
+
+
+# ---- packed sequences (gdr_chunk_bwd_varlen) ---------------------------------------
+LENS = [0, 1, 63, 64, 65, 130, 200, 7]          # empty, single token, around a chunk, several chunks
+
+
+def _packed(lens, H, dk, dv, gate, seed):
+    """Packed tokens and output gradients ([1, sum(lens), H, .]), one S0 and one dS_T per sequence."""
+    T = int(sum(lens))
+    wl = Workload("bwd_varlen", B=1, T=T, H=H, d_k=dk, d_v=dv, io="bf16", gate=gate, s0_std=0.0, seed=seed)
+    x = chunk_inputs(wl)
+    x["dO"] = grad_inputs(wl)["dO"]
+    per = Workload("bwd_varlen_states", B=len(lens), T=1, H=H, d_k=dk, d_v=dv, io="bf16", gate=gate, s0_std=0.5,
+                   seed=seed + 1)
+    x["S0"] = chunk_inputs(per)["S0"]
+    x["dS_T"] = grad_inputs(per)["dS_T"]
+    return x, np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+
+
+def _seq(a, lo, hi):
+    return None if a is None else np.ascontiguousarray(a[:, lo:hi])
+
+
+@pytest.mark.parametrize("gate", ["scalar", "none"])
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 128)])
+def test_bwd_varlen(gate, dk, dv):
+    """The packed backward against the oracle run on each sequence alone (relative
+    L2 over all packed tokens, and per sequence on dS0), and bit for bit against
+    gdr_chunk_bwd on each sequence alone.  (A per-sequence check of dbeta on a
+    one-token sequence would compare a single sum with heavy cancellation.)"""
+    need_gpu()
+    import torch
+    import gated_delta_rule_21_amd as gdr
+    say(f"case bwd varlen gate={gate} d_k={dk} d_v={dv} lens={LENS}")
+    x, cu = _packed(LENS, 2, dk, dv, gate, seed=71 + dk + len(gate))
+    args = [dev(x[n], "bf16") for n in ("q", "k", "v", "beta", "log_a")]
+    g = gdr.chunk_bwd(*args, torch.from_numpy(x["S0"]).cuda(), dev(x["dO"], "bf16"),
+                      torch.from_numpy(x["dS_T"]).cuda(), cu_seqlens=torch.from_numpy(cu).cuda())
+    torch.cuda.synchronize()
+    got = {n: (host(t) if t is not None else None) for n, t in g.items()}
+    names = ["dq", "dk", "dv", "dbeta"] + (["dlog_a"] if gate == "scalar" else [])
+    ref = {n: np.zeros(got[n].shape) for n in names}
+    for i in range(len(LENS)):
+        lo, hi = int(cu[i]), int(cu[i + 1])
+        seq = {n: _seq(x[n], lo, hi) for n in ("q", "k", "v", "beta", "log_a", "dO")}
+        r = oracle_backward(seq["q"], seq["k"], seq["v"], seq["beta"], seq["log_a"], x["S0"][i:i + 1], seq["dO"],
+                            x["dS_T"][i:i + 1])
+        for n in names:
+            ref[n][:, lo:hi] = r[n]
+        check(f"dS0[seq {i}, T={hi - lo}]", got["dS0"][i:i + 1], r["dS0"], TOL["bf16"])
+        if hi > lo:                      # the same sequence through the fixed-length entry point
+            one = gdr.chunk_bwd(*(dev(seq[n], "bf16") for n in ("q", "k", "v", "beta", "log_a")),
+                                torch.from_numpy(np.ascontiguousarray(x["S0"][i:i + 1])).cuda(), dev(seq["dO"], "bf16"),
+                                torch.from_numpy(np.ascontiguousarray(x["dS_T"][i:i + 1])).cuda())
+            torch.cuda.synchronize()
+            for n in names:
+                assert np.array_equal(host(one[n]), got[n][:, lo:hi]), (n, i)
+            assert np.array_equal(host(one["dS0"]), got["dS0"][i:i + 1]), ("dS0", i)
+        else:
+            assert np.array_equal(got["dS0"][i], x["dS_T"][i].astype(np.float64))
+    for n in names:
+        check(n, got[n], ref[n], TOL["bf16"])
