@@ -14,7 +14,8 @@ preconditioner scan of the preconditioned delta rule (with forgetting) over the
 workload's keys (`precond_scan`, GB/s against HBM peak), and the chunk forward
 with the write keys it produced (`osdn`: phase 2, no gate, and the two phases'
 tokens/s), and the backward of the chunk forward over the same workload
-(`backward`: the gradients of q, k, v, beta, log a and S0 for given dO and dS_T).
+(`backward`: the gradients of q, k, v, beta, log a and S0 for given dO and dS_T;
+`train_step_tokens_per_s` counts the forward and the backward together).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
@@ -295,7 +296,7 @@ def bwd_algorithmic(wl):
     return wl.B * wl.H * ((wl.T + C - 1) // C) * per_chunk
 
 
-def bench_bwd(args, log, wl, q, k, v, beta, log_a, S0):
+def bench_bwd(args, log, wl, q, k, v, beta, log_a, S0, fwd_ms):
     """The backward of the chunk forward over the same workload, with dO ~ N(0, 1)
     and dS_T ~ N(0, 1); the gradients of every input and of S0."""
     import torch
@@ -328,6 +329,8 @@ def bench_bwd(args, log, wl, q, k, v, beta, log_a, S0):
     log(f"chunk backward: {ms:.3f} ms/step, {tf:.1f} TFLOP/s useful")
     return {"workload": wl.name + "_backward", "value": round(wl.B * wl.T / (ms * 1e-3), 1), "unit": "tokens/s",
             "ms_per_launch": round(ms, 4), "useful_flops_per_launch": flops,
+            "train_step_tokens_per_s": round(wl.B * wl.T / ((ms + fwd_ms) * 1e-3), 1),
+            "train_step_ms": round(ms + fwd_ms, 4),
             "algorithmic_bytes_per_launch": bwd_bytes(wl, S0 is not None),
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf / BF16_PEAK_TFLOPS, 4),
@@ -491,7 +494,7 @@ def main():
         kw, precond = bench_precond(args, log, wl, k, beta)
         osdn = bench_wkey(args, log, wl, q, k, v, beta, kw, precond["us_per_launch"])
         del kw
-    bwd = None if args.no_bwd or wl.gate == "channel" else bench_bwd(args, log, wl, q, k, v, beta, log_a, S0)
+    bwd = None if args.no_bwd or wl.gate == "channel" else bench_bwd(args, log, wl, q, k, v, beta, log_a, S0, ms)
     del q, k, v, beta, log_a, S0
     cpu = None
     if not args.no_cpu_baseline:
