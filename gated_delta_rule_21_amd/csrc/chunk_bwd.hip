@@ -29,9 +29,9 @@
 //   2. the gradients of the states leaving each chunk, in reverse order (the same
 //      shape of work, dS in accumulators);
 //   3. every chunk at once: the gradients of q, k, v, beta and log a.
-// Passes 1 and 2 store the states in bf16, the precision the forward's products
-// read them in, value-major ([d_v][d_k] per chunk) so that an accumulator lane
-// writes four adjacent values.
+// Passes 1 and 2 are independent and share one launch.  They store the states in
+// bf16, the precision the forward's products read them in, value-major ([d_v][d_k]
+// per chunk) so that an accumulator lane writes four adjacent values.
 //
 // Operand fragments (16x16 MFMA tiles, lane l: lr = l % 16, lg = l / 16):
 //   rowf(M, ld, x0, k0) = M[x0 + lr][k0 + 4 lg + s]   (8-byte LDS read)
