@@ -394,3 +394,36 @@ def precond_scan(k, beta, eta: float, r=None, d0=None, *, kw=None, d_T=None, wan
                               _ptr(d_T), _stream_handle(stream))
     _check(lib, st)
     return kw, d_T
+
+
+class _ChunkAttn(torch.autograd.Function):
+    """chunk_fwd with chunk_bwd as its backward (marshalling only)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, beta, log_a, S0, cu_seqlens):
+        if cu_seqlens is not None:
+            o, S_T = chunk_fwd_varlen(q, k, v, beta, log_a, cu_seqlens, S0)
+        else:
+            o, S_T = chunk_fwd(q, k, v, beta, log_a, S0)
+        ctx.save_for_backward(q, k, v, beta, log_a, S0, cu_seqlens)
+        ctx.gated = log_a is not None
+        ctx.has_S0 = S0 is not None
+        return o, S_T
+
+    @staticmethod
+    def backward(ctx, dO, dS_T):
+        q, k, v, beta, log_a, S0, cu_seqlens = ctx.saved_tensors
+        dO = torch.zeros_like(v) if dO is None else dO.to(v.dtype).contiguous()
+        dS_T = None if dS_T is None else dS_T.float().contiguous()
+        g = chunk_bwd(q, k, v, beta, log_a, S0, dO, dS_T, cu_seqlens=cu_seqlens, want_dS0=ctx.has_S0)
+        return (g["dq"], g["dk"], g["dv"], g["dbeta"], g["dlog_a"] if ctx.gated else None,
+                g["dS0"] if ctx.has_S0 else None, None)
+
+
+def chunk_attn(q, k, v, beta, log_a=None, S0=None, cu_seqlens=None):
+    """(o, S_T) of chunk_fwd (or chunk_fwd_varlen with cu_seqlens) as a torch autograd
+    function whose backward is chunk_bwd: bf16, no gate or a scalar gate, decay before
+    the erase.  Gradients flow to q, k, v, beta, log_a and S0."""
+    if log_a is not None and log_a.dim() == 4:
+        raise NotImplementedError("the backward takes no gate or a scalar gate")
+    return _ChunkAttn.apply(q, k, v, beta, log_a, S0, cu_seqlens)

@@ -244,3 +244,41 @@ def test_bwd_varlen(gate, dk, dv):
             assert np.array_equal(got["dS0"][i], x["dS_T"][i].astype(np.float64))
     for n in names:
         check(n, got[n], ref[n], TOL["bf16"])
+
+
+@pytest.mark.parametrize("packed", [False, True], ids=["batch", "packed"])
+def test_autograd_function(packed):
+    """chunk_attn (chunk_fwd with chunk_bwd as its torch autograd backward): the .grad
+    of every input against the oracle's gradients of <dO, o> + <dS_T, S_T>."""
+    need_gpu()
+    import torch
+    import gated_delta_rule_21_amd as gdr
+    if packed:
+        x, cu = _packed([70, 1, 130], 2, 128, 128, "scalar", seed=31)
+        cu_t = torch.from_numpy(cu).cuda()
+    else:
+        x, cu_t = _inputs(2, 150, 2, 128, 128, "scalar", seed=31), None
+    leaf = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(dt).cuda().requires_grad_(True)
+    ins = {n: leaf(x[n], torch.bfloat16) for n in ("q", "k", "v", "beta", "log_a")}
+    S0 = leaf(x["S0"], torch.float32)
+    o, S_T = gdr.chunk_attn(ins["q"], ins["k"], ins["v"], ins["beta"], ins["log_a"], S0, cu_seqlens=cu_t)
+    loss = (o.float() * torch.from_numpy(x["dO"]).cuda()).sum() + (S_T * torch.from_numpy(x["dS_T"]).cuda()).sum()
+    loss.backward()
+    torch.cuda.synchronize()
+    if packed:
+        names = ("dq", "dk", "dv", "dbeta", "dlog_a")
+        ref = {n: np.zeros(x[n[1:]].shape) for n in names}
+        ref["dS0"] = np.zeros(x["S0"].shape)
+        for i in range(len(cu) - 1):
+            lo, hi = int(cu[i]), int(cu[i + 1])
+            seq = {n: _seq(x[n], lo, hi) for n in ("q", "k", "v", "beta", "log_a", "dO")}
+            r = oracle_backward(seq["q"], seq["k"], seq["v"], seq["beta"], seq["log_a"], x["S0"][i:i + 1], seq["dO"],
+                                x["dS_T"][i:i + 1])
+            for n in names:
+                ref[n][:, lo:hi] = r[n]
+            ref["dS0"][i] = r["dS0"][0]
+    else:
+        ref = _ref(x)
+    for n, t in (("dq", ins["q"]), ("dk", ins["k"]), ("dv", ins["v"]), ("dbeta", ins["beta"]),
+                 ("dlog_a", ins["log_a"]), ("dS0", S0)):
+        check(n, host(t.grad), ref[n], TOL["bf16"])
