@@ -214,11 +214,11 @@ def chunk_bwd_workspace_size(B: int, T: int, H: int, d_k: int, d_v: int, dtype=t
     return int(n.value)
 
 
-def chunk_bwd(q, k, v, beta, log_a, S0, dO, dS_T=None, *, cu_seqlens=None, want_dS0: bool = True, workspace=None,
-              stream=None):
+def chunk_bwd(q, k, v, beta, log_a, S0, dO, dS_T=None, *, cu_seqlens=None, form: str = "page", want_dS0: bool = True,
+              workspace=None, stream=None):
     """gdr_chunk_bwd on torch tensors: the gradients of L = <dO, o> + <dS_T, S_T> for
-    the forward chunk_fwd(q, k, v, beta, log_a, S0) (bf16 I/O, no gate or a scalar
-    gate, decay before the erase).  dO [B, T, H, d_v] bf16; dS_T None or
+    the forward chunk_fwd(q, k, v, beta, log_a, S0, form=form) (bf16 I/O, no gate or
+    a scalar gate).  dO [B, T, H, d_v] bf16; dS_T None or
     [B, H, d_k, d_v] float32.  With `cu_seqlens` (int32 device tensor [n_seq + 1])
     the sequences are packed along T of [1, T, H, .] tensors (gdr_chunk_bwd_varlen)
     and S0, dS_T, dS0 are [n_seq, H, d_k, d_v].  Returns dict(dq, dk, dv, dbeta,
@@ -252,7 +252,7 @@ def chunk_bwd(q, k, v, beta, log_a, S0, dO, dS_T=None, *, cu_seqlens=None, want_
     out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v), dbeta=torch.empty_like(beta),
                dlog_a=torch.empty_like(log_a) if log_a is not None else None,
                dS0=torch.empty((nstate, H, dk, dv), dtype=torch.float32, device=q.device) if want_dS0 else None)
-    desc = GdrDesc(B, T, H, dk, dv, 64, _io_of(q), gate, 0)
+    desc = GdrDesc(B, T, H, dk, dv, 64, _io_of(q), gate, FORMS[form])
     need = ctypes.c_size_t(0)
     if packed:
         _check(lib, lib.gdr_chunk_bwd_varlen_workspace_size(ctypes.byref(desc), nstate, ctypes.byref(need)))
@@ -400,12 +400,13 @@ class _ChunkAttn(torch.autograd.Function):
     """chunk_fwd with chunk_bwd as its backward (marshalling only)."""
 
     @staticmethod
-    def forward(ctx, q, k, v, beta, log_a, S0, cu_seqlens):
+    def forward(ctx, q, k, v, beta, log_a, S0, cu_seqlens, form):
         if cu_seqlens is not None:
-            o, S_T = chunk_fwd_varlen(q, k, v, beta, log_a, cu_seqlens, S0)
+            o, S_T = chunk_fwd_varlen(q, k, v, beta, log_a, cu_seqlens, S0, form=form)
         else:
-            o, S_T = chunk_fwd(q, k, v, beta, log_a, S0)
+            o, S_T = chunk_fwd(q, k, v, beta, log_a, S0, form=form)
         ctx.save_for_backward(q, k, v, beta, log_a, S0, cu_seqlens)
+        ctx.form = form
         ctx.gated = log_a is not None
         ctx.has_S0 = S0 is not None
         return o, S_T
@@ -415,15 +416,15 @@ class _ChunkAttn(torch.autograd.Function):
         q, k, v, beta, log_a, S0, cu_seqlens = ctx.saved_tensors
         dO = torch.zeros_like(v) if dO is None else dO.to(v.dtype).contiguous()
         dS_T = None if dS_T is None else dS_T.float().contiguous()
-        g = chunk_bwd(q, k, v, beta, log_a, S0, dO, dS_T, cu_seqlens=cu_seqlens, want_dS0=ctx.has_S0)
+        g = chunk_bwd(q, k, v, beta, log_a, S0, dO, dS_T, cu_seqlens=cu_seqlens, form=ctx.form, want_dS0=ctx.has_S0)
         return (g["dq"], g["dk"], g["dv"], g["dbeta"], g["dlog_a"] if ctx.gated else None,
-                g["dS0"] if ctx.has_S0 else None, None)
+                g["dS0"] if ctx.has_S0 else None, None, None)
 
 
-def chunk_attn(q, k, v, beta, log_a=None, S0=None, cu_seqlens=None):
+def chunk_attn(q, k, v, beta, log_a=None, S0=None, cu_seqlens=None, form: str = "page"):
     """(o, S_T) of chunk_fwd (or chunk_fwd_varlen with cu_seqlens) as a torch autograd
-    function whose backward is chunk_bwd: bf16, no gate or a scalar gate, decay before
-    the erase.  Gradients flow to q, k, v, beta, log_a and S0."""
+    function whose backward is chunk_bwd: bf16, no gate or a scalar gate, either form.
+    Gradients flow to q, k, v, beta, log_a and S0."""
     if log_a is not None and log_a.dim() == 4:
         raise NotImplementedError("the backward takes no gate or a scalar gate")
-    return _ChunkAttn.apply(q, k, v, beta, log_a, S0, cu_seqlens)
+    return _ChunkAttn.apply(q, k, v, beta, log_a, S0, cu_seqlens, form)

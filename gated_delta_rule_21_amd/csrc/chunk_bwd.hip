@@ -1,5 +1,6 @@
 // Backward pass of the chunkwise gated delta rule on gfx950: bf16 I/O, no gate or a
-// scalar gate, decay before the erase.
+// scalar gate, decay before the erase (g_read = g below) or erase on the undecayed
+// state (g_read_r = g_{r-1}, the A factor and the residual's decay read g_read).
 //
 // The pages print no gradients; these are the reverse-mode derivatives of the
 // chunk form of "Moonshot AI's New Attention Architecture: Key Innovations
@@ -7,8 +8,8 @@
 // domain).  Per chunk (rows r = 0..63, g_r the running sum of log a inside the
 // chunk, D_rj = e^{g_r - g_j}, S the state entering the chunk, dS' the gradient of
 // the state leaving it, dO the gradient of the output):
-//   forward   X = V - diag(e^g) K S,   Delta = T diag(beta) X,   T = (I + A)^{-1},
-//             A = strict_lower(diag(beta) D * K K^T),   P = lower_incl(D * Q K^T),
+//   forward   X = V - diag(e^{g_read}) K S,   Delta = T diag(beta) X,   T = (I + A)^{-1},
+//             A = strict_lower(diag(beta) D_read * K K^T),   P = lower_incl(D * Q K^T),
 //             O = diag(e^g) Q S + P Delta,   S' = e^{g_63} S + K^T diag(e^{g_63 - g}) Delta
 //   reverse   dDelta = P^T dO + diag(e^{g_63 - g}) K dS',   dY = T^T dDelta,
 //             dS = e^{g_63} dS' + Q^T diag(e^g) dO - K^T diag(beta e^g) dY
@@ -480,10 +481,12 @@ struct ChunkLayout {
   static constexpr size_t O_DS = O_S + KB;           // dS'^T half
   // Partial row sums, each written by one wave and added in a fixed order (no
   // atomics, so the result does not depend on the order the waves run in):
-  // dbeta over d_v tiles [4][64] and over column blocks [4][64]; dg row sums [4][64],
-  // column sums [4][64] and d_k tiles [DK / 16][64]; two per-wave scalars [8] x 2.
+  // dbeta over d_v tiles [4][64] and over column blocks [4][64]; dg row sums of the
+  // A and of the P terms [4][64] each, column sums [4][64], and the row dots over
+  // d_k tiles [DK / 16][64] twice (the terms of g_read and those of g); two per-wave
+  // scalars [8] x 2.
   static constexpr size_t O_RED = O_DS + KB;
-  static constexpr size_t NRED = (4 + 4 + 4 + 4 + DK / 16) * CH + 16;
+  static constexpr size_t NRED = (4 + 4 + 4 + 4 + 4 + 2 * (DK / 16)) * CH + 16;
   static constexpr size_t TOTAL = O_RED + NRED * 4;
 };
 
@@ -534,10 +537,12 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdParams p) {
   T* sdS = reinterpret_cast<T*>(smem + L::O_DS);
   float* rbX = reinterpret_cast<float*>(smem + L::O_RED);   // dbeta: [c][r], sum_v dY X of d_v tile c
   float* rbA = rbX + 4 * CH;            // dbeta: [J][r], the dA term of column block J
-  float* rgA = rbA + 4 * CH;            // dg: [J][r], row sums of dA*A + dP*P over column block J
-  float* rgC = rgA + 4 * CH;            // dg: [R][j], column sums of the same over row block R
-  float* rgK = rgC + 4 * CH;            // dg: [ic][r], the row dots over d_k tile ic
-  float* rcs = rgK + (DK / 16) * CH;    // [wave]: sum_r c_r
+  float* rgA = rbA + 4 * CH;            // dg (g_read): [J][r], row sums of dA*A over column block J
+  float* rgP = rgA + 4 * CH;            // dg: [J][r], row sums of dP*P over column block J
+  float* rgC = rgP + 4 * CH;            // dg: [R][j], column sums of dA*A + dP*P over row block R
+  float* rgK = rgC + 4 * CH;            // dg: [ic][r], the q and Delta dS'^T row dots over d_k tile ic
+  float* rgX = rgK + (DK / 16) * CH;    // dg (g_read): [ic][r], the dY S^T row dot over d_k tile ic
+  float* rcs = rgX + (DK / 16) * CH;    // [wave]: sum_r c_r
   float* rsd = rcs + 8;                 // [wave]: <dS', S>
 
   const ChunkParams& f = p.f;
@@ -793,29 +798,38 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdParams p) {
         tri_block(u, R, J);
         const int r = 16 * R + lr;
         const float br = sF[r];
+        // the A factor e^{g_read_r - g_j}: g_read = g (decay before the erase) or
+        // g_{r-1} (erase on the undecayed state; 0 at the chunk's first row)
+        const float grd = p.f.literal ? (r > 0 ? sF[5 * CH + r - 1] : 0.f) : sF[5 * CH + r];
         f32x4 ak, pk;
-        float db = 0.f, rsum = 0.f;
+        float db = 0.f, rsumA = 0.f, rsumP = 0.f;
         float csum[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           const int j = 16 * J + 4 * lg + s;
-          const float D = G ? __expf(fminf(sF[5 * CH + r] - sF[5 * CH + j], 0.f)) : 1.f;
+          const float DA = G ? __expf(fminf(grd - sF[5 * CH + j], 0.f)) : 1.f;
+          const float DP = G ? __expf(fminf(sF[5 * CH + r] - sF[5 * CH + j], 0.f)) : 1.f;
           const float dA = j < r ? -dAa[i][s] : 0.f;
           const float dP = j <= r ? dPa[i][s] : 0.f;
-          ak[s] = br * D * dA;
-          pk[s] = D * dP;
-          db += dA * D * Gr[i][s];
-          const float e = ak[s] * Gr[i][s] + pk[s] * QKr[i][s];   // dA * A + dP * P
-          rsum += e;
-          csum[s] = e;
+          ak[s] = br * DA * dA;
+          pk[s] = DP * dP;
+          db += dA * DA * Gr[i][s];
+          const float ea = ak[s] * Gr[i][s], ep = pk[s] * QKr[i][s];   // dA * A, dP * P
+          rsumA += ea;
+          rsumP += ep;
+          csum[s] = ea + ep;
         }
         st_row(sAk, LCP, r, 16 * J + 4 * lg, ak);
         st_row(sP, LCP, r, 16 * J + 4 * lg, pk);
         db = lg_sum(db);
         if (lg == 0) rbA[J * CH + r] = db;
         if constexpr (G) {
-          rsum = lg_sum(rsum);
-          if (lg == 0) rgA[J * CH + r] = rsum;
+          rsumA = lg_sum(rsumA);
+          rsumP = lg_sum(rsumP);
+          if (lg == 0) {
+            rgA[J * CH + r] = rsumA;
+            rgP[J * CH + r] = rsumP;
+          }
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
             const float x = row16_sum(csum[s]);
@@ -865,14 +879,19 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdParams p) {
       if constexpr (G) {
         const f32x4 kk = O::f32(O::ld(sK + r * LDK + 16 * ic + 4 * lg));
         const f32x4 qq = O::f32(O::ld(sQ + r * LDK + 16 * ic + 4 * lg));
-        float a = 0.f, c = 0.f;
+        float a = 0.f, x = 0.f, c = 0.f;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          a += eg * qq[s] * dOS[i][s] - br * er * kk[s] * dYS[i][s];
+          a += eg * qq[s] * dOS[i][s];
+          x -= br * er * kk[s] * dYS[i][s];
           c += ed * kk[s] * DdS[i][s];
         }
         a = lg_sum(a - c);
-        if (lg == 0) rgK[ic * CH + r] = a;
+        x = lg_sum(x);
+        if (lg == 0) {
+          rgK[ic * CH + r] = a;
+          rgX[ic * CH + r] = x;
+        }
         csum += c;
       }
     }
@@ -893,10 +912,18 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdParams p) {
       buf_store2(f32_to_bf16_bits(db), rdb, off, sb);
       if constexpr (G) {
         float x = 0.f;
-        for (int J = 0; J <= Rr; ++J) x += rgA[J * CH + r];
+        for (int J = 0; J <= Rr; ++J) x += rgP[J * CH + r];
         for (int R = Rr; R < 4; ++R) x -= rgC[R * CH + r];
 #pragma unroll
         for (int ic = 0; ic < DK / 16; ++ic) x += rgK[ic * CH + r];
+        // terms of g_read_r': row r itself, or row r + 1 whose g_read is g_r
+        const int rr = p.f.literal ? r + 1 : r;
+        if (rr < CH) {
+          const int Rq = rr >> 4;
+          for (int J = 0; J <= Rq; ++J) x += rgA[J * CH + rr];
+#pragma unroll
+          for (int ic = 0; ic < DK / 16; ++ic) x += rgX[ic * CH + rr];
+        }
         if (lane == CH - 1) {
           float cs = 0.f, sd = 0.f;
 #pragma unroll
@@ -970,7 +997,7 @@ size_t chunk_bwd_varlen_workspace_bytes(int64_t T, int64_t n_seq, int64_t H, int
 hipError_t launch_chunk_bwd(const BwdParams& p, hipStream_t stream) {
   const ChunkParams& f = p.f;
   if (f.B * f.H == 0) return hipSuccess;
-  if (f.io != IO_BF16 || f.literal || f.kw || (f.gate != GATE_NONE && f.gate != GATE_SCALAR)) return hipErrorInvalidValue;
+  if (f.io != IO_BF16 || f.kw || (f.gate != GATE_NONE && f.gate != GATE_SCALAR)) return hipErrorInvalidValue;
   if (f.T == 0) {
     if (!p.dS0) return hipSuccess;
     const int64_t n = f.B * f.H * f.d_k * f.d_v;

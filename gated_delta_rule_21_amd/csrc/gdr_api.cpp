@@ -88,8 +88,6 @@ gdr_status check_bwd_desc(const gdr_desc* d) {
   if (st != GDR_OK) return st;
   if (d->io != GDR_BF16) return fail(GDR_ERR_UNSUPPORTED, "chunk backward: bf16 I/O only");
   if (d->gate == GDR_GATE_CHANNEL) return fail(GDR_ERR_UNSUPPORTED, "chunk backward: no per-channel gate");
-  if (d->gate == GDR_GATE_SCALAR && d->form == GDR_FORM_LITERAL)
-    return fail(GDR_ERR_UNSUPPORTED, "chunk backward: decay before the erase (GDR_FORM_PAGE) only");
   // one (sequence, head)'s chunk states are addressed with 32-bit byte offsets
   const int64_t per_seq = ((d->T + 63) / 64) * d->d_k * d->d_v * 2;
   if (per_seq > INT32_MAX)
@@ -382,7 +380,7 @@ gdr_status chunk_bwd_impl(const gdr_desc* d, const int32_t* cu, int64_t n_seq, c
   f.ws = workspace;
   f.B = nseq; f.T = d->T; f.H = d->H;
   f.d_k = dk_; f.d_v = dv_;
-  f.io = d->io; f.gate = d->gate; f.literal = 0;
+  f.io = d->io; f.gate = d->gate; f.literal = d->form == GDR_FORM_LITERAL;
   f.cu = cu; f.nslots = packed ? gdr::chunk_varlen_slots(d->T, n_seq) : 0; f.order = nullptr; f.kw = nullptr;
   p.dO = dO; p.dS_T = dS_T; p.dq = dq; p.dk = dk; p.dv = dv; p.dbeta = dbeta; p.dlog_a = dlog_a; p.dS0 = dS0;
   const size_t rec = packed ? gdr::chunk_varlen_records_bytes(d->T, n_seq, d->H, d->io, d->gate, dk_)

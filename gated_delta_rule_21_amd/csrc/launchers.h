@@ -54,8 +54,8 @@ struct PrecondParams {
   int d_k, io;
   float eta;
 };
-// Backward of the chunk forward (bf16 I/O, no gate or a scalar gate, decay before
-// the erase): f carries the forward's inputs, the workspace records (f.ws) and,
+// Backward of the chunk forward (bf16 I/O, no gate or a scalar gate, either form):
+// f carries the forward's inputs, the workspace records (f.ws) and,
 // for packed sequences, cu and nslots; o, S_T and order are unused.
 struct BwdParams {
   ChunkParams f;

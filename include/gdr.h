@@ -298,10 +298,9 @@ gdr_status gdr_chunk_bwd_workspace_size(const gdr_desc* desc, size_t* bytes);
  * its triangular solve).  The forward's outputs are not needed: the call
  * recomputes what it uses from the inputs.
  *
- * Supported: bf16 I/O; GDR_GATE_NONE or GDR_GATE_SCALAR; GDR_FORM_PAGE (with
- * GDR_GATE_NONE either form, they coincide); d_k, d_v in {64, 128}; fixed-length
- * batches here, packed sequences through gdr_chunk_bwd_varlen.  Anything else
- * returns GDR_ERR_UNSUPPORTED.
+ * Supported: bf16 I/O; GDR_GATE_NONE or GDR_GATE_SCALAR; either gdr_form; d_k,
+ * d_v in {64, 128}; fixed-length batches here, packed sequences through
+ * gdr_chunk_bwd_varlen.  Anything else returns GDR_ERR_UNSUPPORTED.
  *
  *   q, k, v, beta, log_a, S0   the forward's inputs, as for gdr_chunk_fwd (log_a
  *                              NULL for GDR_GATE_NONE; S0 NULL = zero state)

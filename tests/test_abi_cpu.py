@@ -290,12 +290,13 @@ def test_backward_workspace_size(lib):
     assert n.value == 2 * 3 * 3 * (11776 + 4 * 128 * 128)
     assert lib.gdr_chunk_bwd_workspace_size(ctypes.byref(_desc(T=0)), ctypes.byref(n)) == OK and n.value == 0
     for field, value, code in (("io", 0, UNSUPPORTED), ("gate", 2, UNSUPPORTED), ("d_k", 96, UNSUPPORTED),
-                               ("B", 0, INVALID), ("form", 1, UNSUPPORTED)):
+                               ("B", 0, INVALID), ("form", 2, INVALID)):
         n.value = 7
         assert lib.gdr_chunk_bwd_workspace_size(ctypes.byref(_desc(**{field: value})), ctypes.byref(n)) == code, field
         assert n.value == 0
-    # no gate: the two forms coincide, so the literal form is accepted
-    assert lib.gdr_chunk_bwd_workspace_size(ctypes.byref(_desc(gate=0, form=1)), ctypes.byref(n)) == OK
+    # both forms, with and without a gate
+    for gate in (0, 1):
+        assert lib.gdr_chunk_bwd_workspace_size(ctypes.byref(_desc(gate=gate, form=1)), ctypes.byref(n)) == OK
 
 
 def test_backward_argument_checks(lib):

@@ -31,13 +31,14 @@ def _inputs(B, T, H, dk, dv, gate, seed, s0_std=0.5):
     return x
 
 
-def _gpu(x, with_S0=True, with_dST=True, want_dS0=True, in_place=False):
+def _gpu(x, with_S0=True, with_dST=True, want_dS0=True, in_place=False, form="page"):
     import torch
     import gated_delta_rule_21_amd as gdr
     S0 = torch.from_numpy(x["S0"]).cuda() if with_S0 else None
     dS_T = torch.from_numpy(x["dS_T"]).cuda() if with_dST else None
     g = gdr.chunk_bwd(dev(x["q"], "bf16"), dev(x["k"], "bf16"), dev(x["v"], "bf16"), dev(x["beta"], "bf16"),
-                      dev(x["log_a"], "bf16"), S0, dev(x["dO"], "bf16"), dS_T, want_dS0=want_dS0 and not in_place)
+                      dev(x["log_a"], "bf16"), S0, dev(x["dO"], "bf16"), dS_T, want_dS0=want_dS0 and not in_place,
+                      form=form)
     if in_place:
         g = gdr.chunk_bwd(dev(x["q"], "bf16"), dev(x["k"], "bf16"), dev(x["v"], "bf16"), dev(x["beta"], "bf16"),
                           dev(x["log_a"], "bf16"), S0, dev(x["dO"], "bf16"), dS_T, want_dS0=False)
@@ -70,9 +71,9 @@ def _in_place(x, S0, dS_T):
     assert st == 0, lib.gdr_last_error().decode()
 
 
-def _ref(x, with_S0=True, with_dST=True):
+def _ref(x, with_S0=True, with_dST=True, form="page"):
     return oracle_backward(x["q"], x["k"], x["v"], x["beta"], x["log_a"], x["S0"] if with_S0 else None, x["dO"],
-                           x["dS_T"] if with_dST else None)
+                           x["dS_T"] if with_dST else None, form=form)
 
 
 def _compare(got, ref, gate, skip=()):
@@ -282,3 +283,16 @@ def test_autograd_function(packed):
     for n, t in (("dq", ins["q"]), ("dk", ins["k"]), ("dv", ins["v"]), ("dbeta", ins["beta"]),
                  ("dlog_a", ins["log_a"]), ("dS0", S0)):
         check(n, host(t.grad), ref[n], TOL["bf16"])
+
+
+@pytest.mark.parametrize("shape", [(2, 200, 3, 128, 128), (1, 130, 2, 64, 128), (2, 65, 2, 128, 64)],
+                         ids=lambda s: "B%dT%dH%ddk%ddv%d" % s)
+def test_bwd_literal_form(shape):
+    """The erase on the undecayed state (GDR_FORM_LITERAL) with a scalar gate: the A
+    factor and the residual's decay read g_{r-1}, so the gradient of those terms goes
+    to the gate of the token before."""
+    need_gpu()
+    say(f"case bwd literal shape={shape}")
+    x = _inputs(*shape, "scalar", seed=sum(shape) + 5)
+    x["log_a"][:, 40:43] = -6.0            # strong gates: the page and literal forms differ clearly
+    _compare(_gpu(x, form="literal"), _ref(x, form="literal"), "scalar")
