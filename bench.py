@@ -206,7 +206,9 @@ def bench_decode(args, log):
         j = s % n_sets
         gdr.recurrent_step(q[j], k[j], v[j], beta[j], log_a[j], S, o=o)
 
-    for s in range(args.warmup):
+    # A decode step is ~10 us: warm up over as many steps as are timed, so the
+    # clocks are at their steady state however small --warmup is.
+    for s in range(max(args.warmup, args.decode_steps)):
         step(s)
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -444,8 +446,11 @@ def bench_handoff(args, log):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=100)
+    # The GPU's clocks ramp up over its first ~100 steps after an idle spell (the
+    # input generation between legs): a chunk forward step measures 457 us after 3
+    # warmup steps, 393 us after 30 and 365-367 us after 100 or more.
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--chunk-config", type=int, default=3, choices=(2, 3, 4),
                     help="chunk-forward workload (3 = the gated workload of the headline metric)")
