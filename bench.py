@@ -49,7 +49,7 @@ DECODE_SOURCES = [os.path.join(ROOT, "gated_delta_rule_21_amd", "csrc", n)
 PRECOND_SOURCES = [os.path.join(ROOT, "gated_delta_rule_21_amd", "csrc", n)
                    for n in ("precond_scan.hip", "chunk_common.h", "device_common.h")]
 BWD_SOURCES = [os.path.join(ROOT, "gated_delta_rule_21_amd", "csrc", n)
-               for n in ("chunk_bwd.hip", "chunk_prep.hip", "chunk_common.h", "device_common.h")]
+               for n in ("chunk_bwd.hip", "bwd_common.h", "chunk_prep.hip", "chunk_common.h", "device_common.h")]
 
 
 def chunk_algorithmic(wl, with_S0: bool):
@@ -336,7 +336,8 @@ def bench_bwd(args, log, wl, q, k, v, beta, log_a, S0, fwd_ms):
             "algorithmic_bytes_per_launch": bwd_bytes(wl, S0 is not None),
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf / BF16_PEAK_TFLOPS, 4),
-                         "traffic": profiled_traffic("chunk_bwd_gated_b8h16t8192d128_counters.md", BWD_SOURCES)}}
+                         "traffic": (profiled_traffic("chunk_bwd_gated_b8h16t8192d128_counters.md", BWD_SOURCES)
+                                     if wl.name == "gated_deltanet_scalar_b8h16t8192d128_bf16" else None)}}
 
 
 def bench_wkey(args, log, wl, q, k, v, beta, kw, scan_us):
@@ -499,7 +500,7 @@ def main():
         kw, precond = bench_precond(args, log, wl, k, beta)
         osdn = bench_wkey(args, log, wl, q, k, v, beta, kw, precond["us_per_launch"])
         del kw
-    bwd = None if args.no_bwd or wl.gate == "channel" else bench_bwd(args, log, wl, q, k, v, beta, log_a, S0, ms)
+    bwd = None if args.no_bwd else bench_bwd(args, log, wl, q, k, v, beta, log_a, S0, ms)
     del q, k, v, beta, log_a, S0
     cpu = None
     if not args.no_cpu_baseline:

@@ -217,8 +217,8 @@ def chunk_bwd_workspace_size(B: int, T: int, H: int, d_k: int, d_v: int, dtype=t
 def chunk_bwd(q, k, v, beta, log_a, S0, dO, dS_T=None, *, cu_seqlens=None, form: str = "page", want_dS0: bool = True,
               workspace=None, stream=None):
     """gdr_chunk_bwd on torch tensors: the gradients of L = <dO, o> + <dS_T, S_T> for
-    the forward chunk_fwd(q, k, v, beta, log_a, S0, form=form) (bf16 I/O, no gate or
-    a scalar gate).  dO [B, T, H, d_v] bf16; dS_T None or
+    the forward chunk_fwd(q, k, v, beta, log_a, S0, form=form) (bf16 I/O; no gate, a
+    scalar gate, or a per-channel gate with d_k = 128).  dO [B, T, H, d_v] bf16; dS_T None or
     [B, H, d_k, d_v] float32.  With `cu_seqlens` (int32 device tensor [n_seq + 1])
     the sequences are packed along T of [1, T, H, .] tensors (gdr_chunk_bwd_varlen)
     and S0, dS_T, dS0 are [n_seq, H, d_k, d_v].  Returns dict(dq, dk, dv, dbeta,
@@ -423,8 +423,6 @@ class _ChunkAttn(torch.autograd.Function):
 
 def chunk_attn(q, k, v, beta, log_a=None, S0=None, cu_seqlens=None, form: str = "page"):
     """(o, S_T) of chunk_fwd (or chunk_fwd_varlen with cu_seqlens) as a torch autograd
-    function whose backward is chunk_bwd: bf16, no gate or a scalar gate, either form.
-    Gradients flow to q, k, v, beta, log_a and S0."""
-    if log_a is not None and log_a.dim() == 4:
-        raise NotImplementedError("the backward takes no gate or a scalar gate")
+    function whose backward is chunk_bwd: bf16, any gate (per-channel with d_k = 128),
+    either form.  Gradients flow to q, k, v, beta, log_a and S0."""
     return _ChunkAttn.apply(q, k, v, beta, log_a, S0, cu_seqlens, form)

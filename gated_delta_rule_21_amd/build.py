@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libgdr.so")
 SOURCES = ["gdr_api.cpp", "chunk_prep.hip", "chunk_state.hip", "chunk_fwd.hip", "decode_step.hip", "precond_scan.hip",
-           "chunk_bwd.hip"]
+           "chunk_bwd.hip", "chunk_bwd_chan.hip"]
 ARCH = os.environ.get("GDR_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

@@ -34,53 +34,16 @@
 // bf16, the precision the forward's products read them in, value-major ([d_v][d_k]
 // per chunk) so that an accumulator lane writes four adjacent values.
 //
-// Operand fragments (16x16 MFMA tiles, lane l: lr = l % 16, lg = l / 16):
-//   rowf(M, ld, x0, k0) = M[x0 + lr][k0 + 4 lg + s]   (8-byte LDS read)
-//   colf(M, ld, k0, x0) = M[k0 + 4 lg + s][x0 + lr]   (LDS transpose read)
-// For C = A B an A fragment is A[m0 + lr][k0 + 4 lg + s] and a B fragment
-// B[k0 + 4 lg + s][n0 + lr].  mma(a, b) leaves C[m0 + 4 lg + s][n0 + lr] in the lane
-// (the "column" form, whose tiles feed the next product as B fragments); mma(b, a)
-// leaves C[m0 + lr][n0 + 4 lg + s] (the "row" form: one row per lane, four adjacent
-// columns, written with one 8-byte store).
-#include "chunk_common.h"
+// With a per-channel gate the two sequential passes here take the transform's
+// decayed operands (k e^{g_read}, q e^{g}, k e^{g_63 - g}) and its P, and scale the
+// state's rows by e^{g_63} of their channel; the per-chunk gradients of that gate
+// are in chunk_bwd_chan.hip.  Operand fragments as described in bwd_common.h.
+#include "bwd_common.h"
 #include "launchers.h"
 
 namespace gdr {
 
 namespace {
-
-typedef Op<IO_BF16> O;
-typedef __bf16 T;
-typedef bf16x4 frag;
-typedef WsRec<2> W;
-
-__device__ __forceinline__ frag rowf(const T* m, int ld, int x0, int k0, int lr, int lg) {
-  return O::ld(m + (x0 + lr) * ld + k0 + 4 * lg);
-}
-__device__ __forceinline__ frag colf(const T* m, int ld, int k0, int x0, int lr, int lg) {
-  return O::ld_tr(m, ld, k0, x0, lr, lg);
-}
-__device__ __forceinline__ void st_row(T* m, int ld, int r, int c, f32x4 x) {
-  *reinterpret_cast<frag*>(m + r * ld + c) = to_bf16x4(x);
-}
-__device__ __forceinline__ void buf_store2(uint16_t x, rsrc_t r, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_buffer_store_b16(x, r, voff, soff, 0);
-}
-__device__ __forceinline__ u32x2 bits8(f32x4 x) { return __builtin_bit_cast(u32x2, to_bf16x4(x)); }
-// A 16-byte piece into a tile whose rows are 8-byte aligned: two 8-byte stores.
-__device__ __forceinline__ void put16(T* dst, u32x4 x) {
-  u32x2* d = reinterpret_cast<u32x2*>(dst);
-  d[0] = u32x2{x[0], x[1]};
-  d[1] = u32x2{x[2], x[3]};
-}
-
-// LDS row strides (bf16 elements) by how a tile is read, after the rates measured
-// for the forward on gfx950: 8-byte row fragments run fastest when a row is 2 or 6
-// (mod 8) dwords long, transpose reads when it is 8 (mod 32) dwords; a tile read both
-// ways takes 6 (mod 8).
-constexpr int ld_row(int w) { return w + 4; }     // rows only
-constexpr int ld_tr(int w) { return w + 16; }     // transposed only (w = 64, 128)
-constexpr int ld_both(int w) { return w + 12; }   // both
 
 // ---------------------------------------------------------------------------
 // Passes 1 and 2: the sequential passes.  Neither reads what the other writes, so
@@ -91,7 +54,7 @@ constexpr int ld_both(int w) { return w + 12; }   // both
 // the factors) and P of the chunk.  Pass 1 reads k both ways, v and T^T transposed;
 // pass 2 reads k and q both ways, dO and P transposed, T^T by rows.
 // ---------------------------------------------------------------------------
-template <int DK, bool REV>
+template <int DK, bool REV, bool CHAN = false>
 struct SeqLayout {
   static constexpr int LDK = ld_both(DK);
   static constexpr int LDV = ld_tr(64);
@@ -101,34 +64,45 @@ struct SeqLayout {
   static constexpr size_t VB = size_t(CH) * LDV * 2;
   static constexpr size_t TB = size_t(CH) * LCT * 2;
   static constexpr size_t O_K = 0, O_Q = O_K + KB, O_V = O_Q + (REV ? KB : 0), O_T = O_V + VB, O_F = O_T + TB;
-  static constexpr size_t BUF = O_F + 6 * CH * 4;
+  static constexpr size_t O_KD = O_F + 6 * CH * 4;   // per-channel gate: k e^{g_63 - g}
+  static constexpr size_t BUF = O_KD + (CHAN ? KB : 0);
   static constexpr size_t O_P = (REV ? 1 : 2) * BUF;
   static constexpr size_t TOTAL = O_P + (REV ? size_t(CH) * LCP * 2 : 0);
 };
 
 // One chunk's tiles in registers, then into one LDS copy: k (and q), the 64-column
 // tile of v (or dO) from column col0, the T blocks and the factor rows of the record.
-template <int DK, int NT, bool WITH_Q>
+// Per-channel gate: k e^{g_read}, q e^{g} and k e^{g_63 - g} from the record in place
+// of k and q, and (pass 2) the record's P.
+template <int DK, int NT, bool WITH_Q, bool CHAN = false>
 struct SeqStage {
-  typedef SeqLayout<DK, WITH_Q> L;
+  typedef SeqLayout<DK, WITH_Q, CHAN> L;
+  static constexpr uint32_t RB = rec_bytes(IO_BF16, CHAN ? GATE_CHANNEL : GATE_SCALAR, DK);
   static constexpr int KR = DK / 8;                  // 16-byte pieces per k row
   static constexpr int KP = CH * KR / NT;            // per thread
   static constexpr int VP = CH * 8 / NT;
   static constexpr int TP = (10 * 32 + NT - 1) / NT; // T blocks: 32 pieces each
   static_assert(KP * NT == CH * KR && VP * NT == CH * 8, "tile pieces split evenly");
-  u32x4 k[KP], q[WITH_Q ? KP : 1], v[VP], t[TP], f;
+  u32x4 k[KP], q[WITH_Q ? KP : 1], kd[CHAN ? KP : 1], v[VP], t[TP], pp[CHAN && WITH_Q ? TP : 1], f;
 
   __device__ __forceinline__ void load(rsrc_t rk, rsrc_t rq, rsrc_t rv, rsrc_t rw, int64_t n, int tid, int H,
                                        int dv, int col0) {
     const uint32_t sk = static_cast<uint32_t>(n * CH * H * DK * 2);
     const uint32_t sv = static_cast<uint32_t>(n * CH * H * dv * 2);
-    const uint32_t sw = static_cast<uint32_t>(n * W::BYTES);
+    const uint32_t sw = static_cast<uint32_t>(n * RB);
 #pragma unroll
     for (int i = 0; i < KP; ++i) {
       const int pc = tid + i * NT;
-      const uint32_t off = static_cast<uint32_t>(((pc / KR) * H * DK + (pc % KR) * 8) * 2);
-      k[i] = buf_load16(rk, off, sk);
-      if constexpr (WITH_Q) q[i] = buf_load16(rq, off, sk);
+      if constexpr (CHAN) {
+        const uint32_t off = W::X_OFF + static_cast<uint32_t>(((pc / KR) * DK + (pc % KR) * 8) * 2);
+        k[i] = buf_load16(rw, off, sw);
+        if constexpr (WITH_Q) q[i] = buf_load16(rw, off + CH * DK * 2, sw);
+        kd[i] = buf_load16(rw, off + 2 * CH * DK * 2, sw);
+      } else {
+        const uint32_t off = static_cast<uint32_t>(((pc / KR) * H * DK + (pc % KR) * 8) * 2);
+        k[i] = buf_load16(rk, off, sk);
+        if constexpr (WITH_Q) q[i] = buf_load16(rq, off, sk);
+      }
     }
 #pragma unroll
     for (int i = 0; i < VP; ++i) {
@@ -139,6 +113,8 @@ struct SeqStage {
     for (int i = 0; i < TP; ++i) {
       const int pc = tid + i * NT;
       if (pc < 320) t[i] = buf_load16(rw, W::T_OFF + static_cast<uint32_t>(pc * 16), sw);
+      if constexpr (CHAN && WITH_Q)
+        if (pc < 320) pp[i] = buf_load16(rw, W::P_OFF + static_cast<uint32_t>(pc * 16), sw);
     }
     if (tid < 96) f = buf_load16(rw, W::F_OFF + static_cast<uint32_t>(tid * 16), sw);
   }
@@ -153,6 +129,7 @@ struct SeqStage {
       const int pc = tid + i * NT;
       put16(dK + (pc / KR) * L::LDK + (pc % KR) * 8, k[i]);
       if constexpr (WITH_Q) put16(dQ + (pc / KR) * L::LDK + (pc % KR) * 8, q[i]);
+      if constexpr (CHAN) put16(reinterpret_cast<T*>(base + L::O_KD) + (pc / KR) * L::LDK + (pc % KR) * 8, kd[i]);
     }
 #pragma unroll
     for (int i = 0; i < VP; ++i) {
@@ -167,40 +144,21 @@ struct SeqStage {
         tri_block(pc / 32, R, J);
         const int a = (pc % 32) / 2, b0 = (pc % 2) * 8;
         put16(dT + (16 * J + a) * L::LCT + 16 * R + b0, t[i]);
+        if constexpr (CHAN && WITH_Q)   // block u holds P_RJ: rows 16R.., columns 16J.. of P
+          put16(reinterpret_cast<T*>(base + L::O_P) + (16 * R + a) * L::LCP + 16 * J + b0, pp[i]);
       }
     }
     if (tid < 96) *reinterpret_cast<u32x4*>(base + L::O_F + tid * 16) = f;
   }
 };
 
-// Buffers over one (sequence, head) slice of a [B, T, H, width] tensor; the range
-// ends after the last token, so rows past it read as zero and their stores drop.
-struct Slice {
-  int64_t row0;
-  uint32_t span;
-  __device__ __forceinline__ rsrc_t rs(const void* base, int width) const {
-    return make_rsrc(static_cast<const uint16_t*>(base) + row0 * width, span * width * 2);
-  }
-};
-// One (sequence, head): its token rows, chunks, and first record slot (the per-chunk
-// records and both sets of chunk states are addressed by the same slots).
-// Fixed-length batches: [B, T, H, .] tensors; packed sequences (f.cu set): tokens
-// cu[b] .. cu[b+1] - 1 of [1, T, H, .] tensors (see seq_span).
-struct BwdSeq {
-  Slice sl;
-  int64_t nch, rec0;
-};
-__device__ __forceinline__ BwdSeq bwd_seq_of(const ChunkParams& f, int64_t bb, int64_t hh) {
-  const SeqSpan sp = seq_span(f, bb, hh);
-  return BwdSeq{Slice{sp.t0 * f.H + hh, static_cast<uint32_t>(sp.len > 0 ? (sp.len - 1) * f.H + 1 : 0)},
-                (sp.len + CH - 1) / CH, sp.rec0};
-}
-
 // Pass 1: the state entering every chunk, stored in bf16 value-major.  lb is the
 // workgroup's (sequence, head, tile) index.
 template <int GATE, int DK>
 __device__ __forceinline__ void states_pass(const BwdParams& p, int n_tiles, int lb, char* smem) {
-  typedef SeqLayout<DK, false> L;
+  constexpr bool CHAN = GATE == GATE_CHANNEL;
+  constexpr uint32_t RB = rec_bytes(IO_BF16, GATE, DK);
+  typedef SeqLayout<DK, false, CHAN> L;
   constexpr int DKT = DK / 16, LDK = L::LDK, LDV = L::LDV, LCT = L::LCT;
   const ChunkParams& f = p.f;
   const int64_t bh = lb / n_tiles;
@@ -215,7 +173,7 @@ __device__ __forceinline__ void states_pass(const BwdParams& p, int n_tiles, int
   const int64_t nch = sq.nch;
   const Slice sl = sq.sl;
   const rsrc_t rk = sl.rs(f.k, DK), rv = sl.rs(f.v, dv);
-  const rsrc_t rw = make_rsrc(static_cast<const char*>(f.ws) + sq.rec0 * W::BYTES, static_cast<uint32_t>(nch * W::BYTES));
+  const rsrc_t rw = make_rsrc(static_cast<const char*>(f.ws) + sq.rec0 * RB, static_cast<uint32_t>(nch * RB));
   const uint32_t sbytes = static_cast<uint32_t>(dv * DK * 2);   // one chunk's state
   const rsrc_t rst = make_rsrc(static_cast<char*>(p.states) + sq.rec0 * sbytes, static_cast<uint32_t>(nch * sbytes));
 
@@ -225,7 +183,7 @@ __device__ __forceinline__ void states_pass(const BwdParams& p, int n_tiles, int
 #pragma unroll
     for (int s = 0; s < 4; ++s) S[t][s] = f.S0 ? f.S0[(bh * DK + 16 * t + 4 * lg + s) * dv + scol] : 0.f;
 
-  SeqStage<DK, 256, false> st;
+  SeqStage<DK, 256, false, CHAN> st;
   if (nch > 0) {
     st.load(rk, rk, rv, rw, 0, tid, H, dv, col0);
     st.store(smem, tid);
@@ -237,6 +195,7 @@ __device__ __forceinline__ void states_pass(const BwdParams& p, int n_tiles, int
     const T* sK = reinterpret_cast<const T*>(cur + L::O_K);
     const T* sV = reinterpret_cast<const T*>(cur + L::O_V);
     const T* sT = reinterpret_cast<const T*>(cur + L::O_T);
+    const T* sKD = reinterpret_cast<const T*>(cur + (CHAN ? L::O_KD : L::O_K));   // K^T of the update
     const float* sF = reinterpret_cast<const float*>(cur + L::O_F);
     if (n + 1 < nch) {   // the other copy was last read before the previous barrier
       st.store(smem + ((n + 1) & 1) * L::BUF, tid);
@@ -286,8 +245,12 @@ __device__ __forceinline__ void states_pass(const BwdParams& p, int n_tiles, int
     for (int t = 0; t < DKT; ++t) {      // S' = e^{g_63} S + K^T (e^{g_63 - g} Delta)
       f32x4 acc = S[t];
       if constexpr (GATE == GATE_SCALAR) acc = acc * sF[4 * CH];
-      acc = O::mma2(acc, colf(sK, LDK, 0, 16 * t, lr, lg), colf(sK, LDK, 16, 16 * t, lr, lg), Ds[0], Ds[1]);
-      acc = O::mma2(acc, colf(sK, LDK, 32, 16 * t, lr, lg), colf(sK, LDK, 48, 16 * t, lr, lg), Ds[2], Ds[3]);
+      if constexpr (CHAN) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc[s] *= sF[CH + 16 * t + 4 * lg + s];
+      }
+      acc = O::mma2(acc, colf(sKD, LDK, 0, 16 * t, lr, lg), colf(sKD, LDK, 16, 16 * t, lr, lg), Ds[0], Ds[1]);
+      acc = O::mma2(acc, colf(sKD, LDK, 32, 16 * t, lr, lg), colf(sKD, LDK, 48, 16 * t, lr, lg), Ds[2], Ds[3]);
       S[t] = acc;
     }
     __syncthreads();
@@ -299,7 +262,9 @@ __device__ __forceinline__ void states_pass(const BwdParams& p, int n_tiles, int
 // in after the step's last read.
 template <int GATE, int DK>
 __device__ __forceinline__ void reverse_pass(const BwdParams& p, int n_tiles, int lb, char* smem) {
-  typedef SeqLayout<DK, true> L;
+  constexpr bool CHAN = GATE == GATE_CHANNEL;
+  constexpr uint32_t RB = rec_bytes(IO_BF16, GATE, DK);
+  typedef SeqLayout<DK, true, CHAN> L;
   constexpr int DKT = DK / 16, LDK = L::LDK, LDV = L::LDV, LCT = L::LCT, LCP = L::LCP;
   const ChunkParams& f = p.f;
   const int64_t bh = lb / n_tiles;
@@ -314,7 +279,7 @@ __device__ __forceinline__ void reverse_pass(const BwdParams& p, int n_tiles, in
   const int64_t nch = sq.nch;
   const Slice sl = sq.sl;
   const rsrc_t rk = sl.rs(f.k, DK), rq = sl.rs(f.q, DK), rdo = sl.rs(p.dO, dv);
-  const rsrc_t rw = make_rsrc(static_cast<const char*>(f.ws) + sq.rec0 * W::BYTES, static_cast<uint32_t>(nch * W::BYTES));
+  const rsrc_t rw = make_rsrc(static_cast<const char*>(f.ws) + sq.rec0 * RB, static_cast<uint32_t>(nch * RB));
   const uint32_t sbytes = static_cast<uint32_t>(dv * DK * 2);
   const rsrc_t rds = make_rsrc(static_cast<char*>(p.dstates) + sq.rec0 * sbytes, static_cast<uint32_t>(nch * sbytes));
   T* sP = reinterpret_cast<T*>(smem + L::O_P);
@@ -325,7 +290,7 @@ __device__ __forceinline__ void reverse_pass(const BwdParams& p, int n_tiles, in
 #pragma unroll
     for (int s = 0; s < 4; ++s) dS[t][s] = p.dS_T ? p.dS_T[(bh * DK + 16 * t + 4 * lg + s) * dv + scol] : 0.f;
 
-  SeqStage<DK, 256, true> st;
+  SeqStage<DK, 256, true, CHAN> st;
   if (nch > 0) {
     st.load(rk, rq, rdo, rw, nch - 1, tid, H, dv, col0);
     st.store(smem, tid);
@@ -338,9 +303,11 @@ __device__ __forceinline__ void reverse_pass(const BwdParams& p, int n_tiles, in
     const T* sQ = reinterpret_cast<const T*>(cur + L::O_Q);
     const T* sO = reinterpret_cast<const T*>(cur + L::O_V);
     const T* sT = reinterpret_cast<const T*>(cur + L::O_T);
+    const T* sKD = reinterpret_cast<const T*>(cur + (CHAN ? L::O_KD : L::O_K));   // rows of dDelta's K
     const float* sF = reinterpret_cast<const float*>(cur + L::O_F);
-    // P of this chunk, blocks u = wave, wave + 4, .. (row form: row 16R + lr)
-    for (int u = wave; u < 10; u += 4) {
+    // P of this chunk, blocks u = wave, wave + 4, .. (row form: row 16R + lr); the
+    // per-channel gate's P came with the tiles
+    for (int u = wave; u < (CHAN ? 0 : 10); u += 4) {
       int R, J;
       tri_block(u, R, J);
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -386,7 +353,7 @@ __device__ __forceinline__ void reverse_pass(const BwdParams& p, int n_tiles, in
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < DK / 32; ++kb)
-        acc = O::mma2(acc, rowf(sK, LDK, 16 * M, 32 * kb, lr, lg), rowf(sK, LDK, 16 * M, 32 * kb + 16, lr, lg),
+        acc = O::mma2(acc, rowf(sKD, LDK, 16 * M, 32 * kb, lr, lg), rowf(sKD, LDK, 16 * M, 32 * kb + 16, lr, lg),
                       dSb[2 * kb], dSb[2 * kb + 1]);
       if constexpr (GATE == GATE_SCALAR) {
 #pragma unroll
@@ -421,6 +388,10 @@ __device__ __forceinline__ void reverse_pass(const BwdParams& p, int n_tiles, in
     for (int t = 0; t < DKT; ++t) {      // dS = e^{g_63} dS' + Q^T diag(e^g) dO + K^T Z
       f32x4 acc = dS[t];
       if constexpr (GATE == GATE_SCALAR) acc = acc * sF[4 * CH];
+      if constexpr (CHAN) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc[s] *= sF[CH + 16 * t + 4 * lg + s];
+      }
       acc = O::mma2(acc, colf(sQ, LDK, 0, 16 * t, lr, lg), colf(sQ, LDK, 16, 16 * t, lr, lg), dOg[0], dOg[1]);
       acc = O::mma2(acc, colf(sQ, LDK, 32, 16 * t, lr, lg), colf(sQ, LDK, 48, 16 * t, lr, lg), dOg[2], dOg[3]);
       acc = O::mma2(acc, colf(sK, LDK, 0, 16 * t, lr, lg), colf(sK, LDK, 16, 16 * t, lr, lg), Zb[0], Zb[1]);
@@ -445,7 +416,8 @@ __device__ __forceinline__ void reverse_pass(const BwdParams& p, int n_tiles, in
 // Passes 1 and 2 in one launch of 2 nseq workgroups: the first nseq take pass 1.
 template <int GATE, int DK>
 __global__ __launch_bounds__(256) void bwd_seq_kernel(BwdParams p, int n_tiles, int nseq) {
-  __shared__ __attribute__((aligned(16))) char smem[cmax(SeqLayout<DK, false>::TOTAL, SeqLayout<DK, true>::TOTAL)];
+  constexpr bool CHAN = GATE == GATE_CHANNEL;
+  __shared__ __attribute__((aligned(16))) char smem[cmax(SeqLayout<DK, false, CHAN>::TOTAL, SeqLayout<DK, true, CHAN>::TOTAL)];
   const int b = blockIdx.x;
   const int role = b >= nseq;
   const int idx = b - role * nseq;
@@ -489,26 +461,6 @@ struct ChunkLayout {
   static constexpr size_t NRED = (4 + 4 + 4 + 4 + 4 + 2 * (DK / 16)) * CH + 16;
   static constexpr size_t TOTAL = O_RED + NRED * 4;
 };
-
-// Sum over the 16 lanes of a row (lanes with one lg), returned to all of them;
-// the pairing is fixed, so the result is the same on every run.
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float row16_sum(float v) {
-  v += dpp<0x128>(v);   // row_ror:8
-  v += dpp<0x124>(v);   // row_ror:4
-  v += dpp<0x122>(v);   // row_ror:2
-  v += dpp<0x121>(v);   // row_ror:1
-  return v;
-}
-// Sum over the four lanes with one lr (lanes lr, lr + 16, lr + 32, lr + 48).
-__device__ __forceinline__ float lg_sum(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
-}
 
 // One workgroup per chunk (the LDS admits one per compute unit).
 template <int GATE, int DK, int DV>
@@ -953,27 +905,36 @@ __global__ void bwd_copy_state_kernel(const float* src, float* dst, int64_t n) {
 template <int GATE, int DK>
 hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
   const ChunkParams& f = p.f;
-  const int64_t nch = (f.T + CH - 1) / CH;
   const int n_tiles = f.d_v / 64;
   const int64_t nseq = f.B * f.H * n_tiles;
   hipLaunchKernelGGL((bwd_seq_kernel<GATE, DK>), dim3(static_cast<unsigned>(2 * nseq)), dim3(256), 0, stream, p, n_tiles,
                      static_cast<int>(nseq));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const unsigned grid = static_cast<unsigned>(f.cu ? f.H * f.nslots : f.B * f.H * nch);
-  if (f.d_v == 128)
-    hipLaunchKernelGGL((bwd_chunk_kernel<GATE, DK, 128>), dim3(grid), dim3(512), 0, stream, p);
-  else
-    hipLaunchKernelGGL((bwd_chunk_kernel<GATE, DK, 64>), dim3(grid), dim3(512), 0, stream, p);
-  return hipGetLastError();
+  if constexpr (GATE == GATE_CHANNEL) {
+    return launch_chunk_bwd_chan(p, stream);
+  } else {
+    const int64_t nch = (f.T + CH - 1) / CH;
+    const unsigned grid = static_cast<unsigned>(f.cu ? f.H * f.nslots : f.B * f.H * nch);
+    if (f.d_v == 128)
+      hipLaunchKernelGGL((bwd_chunk_kernel<GATE, DK, 128>), dim3(grid), dim3(512), 0, stream, p);
+    else
+      hipLaunchKernelGGL((bwd_chunk_kernel<GATE, DK, 64>), dim3(grid), dim3(512), 0, stream, p);
+    return hipGetLastError();
+  }
 }
 
 template <int GATE>
 hipError_t launch_bwd_g(const BwdParams& p, hipStream_t stream) {
   if (p.f.d_k == 128) return launch_bwd_t<GATE, 128>(p, stream);
-  if (p.f.d_k == 64) return launch_bwd_t<GATE, 64>(p, stream);
+  if constexpr (GATE != GATE_CHANNEL)   // the per-channel gate: d_k = 128 only
+    if (p.f.d_k == 64) return launch_bwd_t<GATE, 64>(p, stream);
   return hipErrorInvalidValue;
 }
+
+// The records follow the gate: with a per-channel gate they also hold the decayed
+// operands the sequential passes read.
+int rec_gate(int gate) { return gate == GATE_CHANNEL ? GATE_CHANNEL : GATE_SCALAR; }
 
 }  // namespace
 
@@ -981,23 +942,23 @@ size_t chunk_bwd_state_bytes(int64_t B, int64_t T, int64_t H, int d_k, int d_v) 
   return static_cast<size_t>(B * H * ((T + CH - 1) / CH)) * static_cast<size_t>(d_k) * static_cast<size_t>(d_v) * 2u;
 }
 
-size_t chunk_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int d_k, int d_v) {
-  return chunk_workspace_bytes(B, T, H, IO_BF16, GATE_SCALAR, d_k) + 2 * chunk_bwd_state_bytes(B, T, H, d_k, d_v);
+size_t chunk_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int d_k, int d_v, int gate) {
+  return chunk_workspace_bytes(B, T, H, IO_BF16, rec_gate(gate), d_k) + 2 * chunk_bwd_state_bytes(B, T, H, d_k, d_v);
 }
 
 size_t chunk_bwd_varlen_state_bytes(int64_t T, int64_t n_seq, int64_t H, int d_k, int d_v) {
   return static_cast<size_t>(H * chunk_varlen_slots(T, n_seq)) * static_cast<size_t>(d_k) * static_cast<size_t>(d_v) * 2u;
 }
 
-size_t chunk_bwd_varlen_workspace_bytes(int64_t T, int64_t n_seq, int64_t H, int d_k, int d_v) {
-  return chunk_varlen_records_bytes(T, n_seq, H, IO_BF16, GATE_SCALAR, d_k) +
+size_t chunk_bwd_varlen_workspace_bytes(int64_t T, int64_t n_seq, int64_t H, int d_k, int d_v, int gate) {
+  return chunk_varlen_records_bytes(T, n_seq, H, IO_BF16, rec_gate(gate), d_k) +
          2 * chunk_bwd_varlen_state_bytes(T, n_seq, H, d_k, d_v);
 }
 
 hipError_t launch_chunk_bwd(const BwdParams& p, hipStream_t stream) {
   const ChunkParams& f = p.f;
   if (f.B * f.H == 0) return hipSuccess;
-  if (f.io != IO_BF16 || f.kw || (f.gate != GATE_NONE && f.gate != GATE_SCALAR)) return hipErrorInvalidValue;
+  if (f.io != IO_BF16 || f.kw || (f.gate == GATE_CHANNEL && f.d_k != 128)) return hipErrorInvalidValue;
   if (f.T == 0) {
     if (!p.dS0) return hipSuccess;
     const int64_t n = f.B * f.H * f.d_k * f.d_v;
@@ -1007,7 +968,12 @@ hipError_t launch_chunk_bwd(const BwdParams& p, hipStream_t stream) {
   }
   hipError_t e = launch_chunk_prep(f, stream);
   if (e != hipSuccess) return e;
-  return f.gate == GATE_SCALAR ? launch_bwd_g<GATE_SCALAR>(p, stream) : launch_bwd_g<GATE_NONE>(p, stream);
+  switch (f.gate) {
+    case GATE_NONE: return launch_bwd_g<GATE_NONE>(p, stream);
+    case GATE_SCALAR: return launch_bwd_g<GATE_SCALAR>(p, stream);
+    case GATE_CHANNEL: return launch_bwd_g<GATE_CHANNEL>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace gdr

@@ -87,7 +87,8 @@ gdr_status check_bwd_desc(const gdr_desc* d) {
   gdr_status st = check_desc(d, false);
   if (st != GDR_OK) return st;
   if (d->io != GDR_BF16) return fail(GDR_ERR_UNSUPPORTED, "chunk backward: bf16 I/O only");
-  if (d->gate == GDR_GATE_CHANNEL) return fail(GDR_ERR_UNSUPPORTED, "chunk backward: no per-channel gate");
+  if (d->gate == GDR_GATE_CHANNEL && d->d_k != 128)
+    return fail(GDR_ERR_UNSUPPORTED, "chunk backward: the per-channel gate needs d_k = 128");
   // one (sequence, head)'s chunk states are addressed with 32-bit byte offsets
   const int64_t per_seq = ((d->T + 63) / 64) * d->d_k * d->d_v * 2;
   if (per_seq > INT32_MAX)
@@ -333,11 +334,12 @@ gdr_status chunk_bwd_impl(const gdr_desc* d, const int32_t* cu, int64_t n_seq, c
   const bool packed = cu != nullptr;
   if (packed && (st = check_packed(d, n_seq)) != GDR_OK) return st;
   const int64_t nseq = packed ? n_seq : d->B;       // sequences, and states in S0 / dS_T / dS0
-  const bool gated = d->gate == GDR_GATE_SCALAR;
+  const bool gated = d->gate != GDR_GATE_NONE;
   const int dk_ = static_cast<int>(d->d_k), dv_ = static_cast<int>(d->d_v);
+  const int64_t gate_width = d->gate == GDR_GATE_CHANNEL ? d->d_k : 1;   // log a values per token and head
   const size_t ws_need = d->T == 0 ? 0
-                         : packed  ? gdr::chunk_bwd_varlen_workspace_bytes(d->T, n_seq, d->H, dk_, dv_)
-                                   : gdr::chunk_bwd_workspace_bytes(d->B, d->T, d->H, dk_, dv_);
+                         : packed  ? gdr::chunk_bwd_varlen_workspace_bytes(d->T, n_seq, d->H, dk_, dv_, d->gate)
+                                   : gdr::chunk_bwd_workspace_bytes(d->B, d->T, d->H, dk_, dv_, d->gate);
   if (d->T > 0) {
     const void* req[] = {q, k, v, beta, dO, dq, dk, dv, dbeta};
     const char* names[] = {"q", "k", "v", "beta", "dO", "dq", "dk", "dv", "dbeta"};
@@ -363,12 +365,12 @@ gdr_status chunk_bwd_impl(const gdr_desc* d, const int32_t* cu, int64_t n_seq, c
   const int64_t state_bytes = nseq * d->H * d->d_k * d->d_v * 4;
   Span all[] = {span("q", q, ntok * d->d_k * 2), span("k", k, ntok * d->d_k * 2),
                 span("v", v, ntok * d->d_v * 2), span("beta", beta, ntok * 2),
-                span("log_a", log_a, gated ? ntok * 2 : 0), span("S0", S0, state_bytes),
+                span("log_a", log_a, gated ? ntok * gate_width * 2 : 0), span("S0", S0, state_bytes),
                 span("dO", dO, ntok * d->d_v * 2), span("dS_T", dS_T, state_bytes),
                 span("cu_seqlens", cu, packed ? (n_seq + 1) * 4 : 0),
                 span("dq", dq, ntok * d->d_k * 2), span("dk", dk, ntok * d->d_k * 2),
                 span("dv", dv, ntok * d->d_v * 2), span("dbeta", dbeta, ntok * 2),
-                span("dlog_a", dlog_a, gated ? ntok * 2 : 0), span("dS0", dS0, state_bytes),
+                span("dlog_a", dlog_a, gated ? ntok * gate_width * 2 : 0), span("dS0", dS0, state_bytes),
                 span("workspace", d->T > 0 ? workspace : nullptr, static_cast<int64_t>(ws_need))};
   Span outs[] = {all[9], all[10], all[11], all[12], all[13], all[14], all[15]};
   if (dS0 && dS0 == dS_T) all[7].hi = all[7].lo;   // the final-state gradient may be overwritten by dS0
@@ -494,7 +496,9 @@ gdr_status gdr_chunk_bwd_workspace_size(const gdr_desc* d, size_t* bytes) {
     *bytes = 0;
     gdr_status st = check_bwd_desc(d);
     if (st != GDR_OK) return st;
-    *bytes = d->T > 0 ? gdr::chunk_bwd_workspace_bytes(d->B, d->T, d->H, static_cast<int>(d->d_k), static_cast<int>(d->d_v)) : 0;
+    *bytes = d->T > 0 ? gdr::chunk_bwd_workspace_bytes(d->B, d->T, d->H, static_cast<int>(d->d_k), static_cast<int>(d->d_v),
+                                                       d->gate)
+                      : 0;
     return GDR_OK;
   } catch (...) {
     return fail(GDR_ERR_INVALID_ARG, "internal error");
@@ -510,7 +514,7 @@ gdr_status gdr_chunk_bwd_varlen_workspace_size(const gdr_desc* d, int64_t n_seq,
     if (st != GDR_OK) return st;
     if ((st = check_packed(d, n_seq)) != GDR_OK) return st;
     *bytes = d->T > 0 ? gdr::chunk_bwd_varlen_workspace_bytes(d->T, n_seq, d->H, static_cast<int>(d->d_k),
-                                                              static_cast<int>(d->d_v))
+                                                              static_cast<int>(d->d_v), d->gate)
                       : 0;
     return GDR_OK;
   } catch (...) {

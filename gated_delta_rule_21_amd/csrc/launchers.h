@@ -91,10 +91,12 @@ hipError_t launch_chunk_bwd(const BwdParams& p, hipStream_t stream);
 // Bytes of one set of per-chunk states (bf16), and of the whole backward workspace:
 // the transform's records, the chunk-start states, the chunk-end state gradients.
 size_t chunk_bwd_state_bytes(int64_t B, int64_t T, int64_t H, int d_k, int d_v);
-size_t chunk_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int d_k, int d_v);
+size_t chunk_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int d_k, int d_v, int gate);
 // Packed sequences: the records and the states by the slots of chunk_varlen_slots.
 size_t chunk_bwd_varlen_state_bytes(int64_t T, int64_t n_seq, int64_t H, int d_k, int d_v);
-size_t chunk_bwd_varlen_workspace_bytes(int64_t T, int64_t n_seq, int64_t H, int d_k, int d_v);
+size_t chunk_bwd_varlen_workspace_bytes(int64_t T, int64_t n_seq, int64_t H, int d_k, int d_v, int gate);
+// The per-chunk gradients with a per-channel gate (d_k = 128), after the sequential passes.
+hipError_t launch_chunk_bwd_chan(const BwdParams& p, hipStream_t stream);
 // Longest-first order of packed sequences into `order` (n_seq int32).
 hipError_t launch_varlen_order(const ChunkParams& p, int32_t* order, hipStream_t stream);
 

@@ -58,7 +58,7 @@ def precond_source_digest() -> str:
 
 def bwd_source_digest() -> str:
     h = hashlib.sha256()
-    for n in ("chunk_bwd.hip", "chunk_prep.hip", "chunk_common.h", "device_common.h"):
+    for n in ("chunk_bwd.hip", "bwd_common.h", "chunk_prep.hip", "chunk_common.h", "device_common.h"):
         with open(os.path.join(ROOT, "gated_delta_rule_21_amd", "csrc", n), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

@@ -298,9 +298,11 @@ gdr_status gdr_chunk_bwd_workspace_size(const gdr_desc* desc, size_t* bytes);
  * its triangular solve).  The forward's outputs are not needed: the call
  * recomputes what it uses from the inputs.
  *
- * Supported: bf16 I/O; GDR_GATE_NONE or GDR_GATE_SCALAR; either gdr_form; d_k,
- * d_v in {64, 128}; fixed-length batches here, packed sequences through
- * gdr_chunk_bwd_varlen.  Anything else returns GDR_ERR_UNSUPPORTED.
+ * Supported: bf16 I/O; GDR_GATE_NONE or GDR_GATE_SCALAR with d_k, d_v in {64, 128},
+ * GDR_GATE_CHANNEL (a gate per key channel, "Moonshot AI's New Attention
+ * Architecture", §2) with d_k = 128 and d_v in {64, 128}; either gdr_form;
+ * fixed-length batches here, packed sequences through gdr_chunk_bwd_varlen.
+ * Anything else returns GDR_ERR_UNSUPPORTED.
  *
  *   q, k, v, beta, log_a, S0   the forward's inputs, as for gdr_chunk_fwd (log_a
  *                              NULL for GDR_GATE_NONE; S0 NULL = zero state)
@@ -309,7 +311,8 @@ gdr_status gdr_chunk_bwd_workspace_size(const gdr_desc* desc, size_t* bytes);
  *   dq, dk [B, T, H, d_k] bf16  written
  *   dv     [B, T, H, d_v] bf16  written
  *   dbeta  [B, T, H]      bf16  written
- *   dlog_a [B, T, H]      bf16  written for GDR_GATE_SCALAR; must be NULL otherwise
+ *   dlog_a [B, T, H] (GDR_GATE_SCALAR) or [B, T, H, d_k] (GDR_GATE_CHANNEL) bf16
+ *          written; must be NULL for GDR_GATE_NONE
  *   dS0    [B, H, d_k, d_v] fp32 written, or NULL (not computed); may equal dS_T
  *          (overwritten in place), no other alias is allowed
  *   workspace / workspace_bytes  scratch of at least gdr_chunk_bwd_workspace_size
@@ -317,7 +320,10 @@ gdr_status gdr_chunk_bwd_workspace_size(const gdr_desc* desc, size_t* bytes);
  *
  * Precision: bf16 products with fp32 accumulation, the carried state and state
  * gradient in fp32 (stored per chunk in bf16, the precision the products read
- * them in); reductions over tokens (dbeta, dlog_a) in fp32.  T == 0 writes dS0 =
+ * them in); reductions over tokens (dbeta, dlog_a) in fp32.  With a per-channel
+ * gate the decay inside a chunk is split at 16-token blocks, so the gate must not
+ * decay by more than e^-80 within 16 tokens of one channel (the forward's bound).
+ * T == 0 writes dS0 =
  * dS_T (or zeros).  Errors as for gdr_chunk_fwd; besides, one sequence's chunk
  * states must stay below 2^31 bytes (ceil(T / 64) * d_k * d_v * 2).
  */

@@ -289,14 +289,18 @@ def test_backward_workspace_size(lib):
     assert lib.gdr_chunk_bwd_workspace_size(ctypes.byref(d), ctypes.byref(n)) == OK
     assert n.value == 2 * 3 * 3 * (11776 + 4 * 128 * 128)
     assert lib.gdr_chunk_bwd_workspace_size(ctypes.byref(_desc(T=0)), ctypes.byref(n)) == OK and n.value == 0
-    for field, value, code in (("io", 0, UNSUPPORTED), ("gate", 2, UNSUPPORTED), ("d_k", 96, UNSUPPORTED),
-                               ("B", 0, INVALID), ("form", 2, INVALID)):
+    for fields, code in (({"io": 0}, UNSUPPORTED), ({"gate": 2, "d_k": 64}, UNSUPPORTED), ({"d_k": 96}, UNSUPPORTED),
+                         ({"B": 0}, INVALID), ({"form": 2}, INVALID)):
         n.value = 7
-        assert lib.gdr_chunk_bwd_workspace_size(ctypes.byref(_desc(**{field: value})), ctypes.byref(n)) == code, field
+        assert lib.gdr_chunk_bwd_workspace_size(ctypes.byref(_desc(**fields)), ctypes.byref(n)) == code, fields
         assert n.value == 0
     # both forms, with and without a gate
-    for gate in (0, 1):
+    for gate in (0, 1, 2):
         assert lib.gdr_chunk_bwd_workspace_size(ctypes.byref(_desc(gate=gate, form=1)), ctypes.byref(n)) == OK
+    # per-channel gate (d_k = 128): the records also hold the three decayed [64][d_k] operands
+    d = _desc(B=2, T=130, H=3, gate=2)
+    assert lib.gdr_chunk_bwd_workspace_size(ctypes.byref(d), ctypes.byref(n)) == OK
+    assert n.value == 2 * 3 * 3 * (11776 + 3 * 64 * 128 * 2 + 4 * 128 * 128)
 
 
 def test_backward_argument_checks(lib):

@@ -206,8 +206,8 @@ def _seq(a, lo, hi):
     return None if a is None else np.ascontiguousarray(a[:, lo:hi])
 
 
-@pytest.mark.parametrize("gate", ["scalar", "none"])
-@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 128)])
+@pytest.mark.parametrize("gate,dk,dv", [("scalar", 128, 128), ("scalar", 64, 128), ("none", 128, 128),
+                                        ("none", 64, 128), ("channel", 128, 128)])
 def test_bwd_varlen(gate, dk, dv):
     """The packed backward against the oracle run on each sequence alone (relative
     L2 over all packed tokens, and per sequence on dS0), and bit for bit against
@@ -223,7 +223,7 @@ def test_bwd_varlen(gate, dk, dv):
                       torch.from_numpy(x["dS_T"]).cuda(), cu_seqlens=torch.from_numpy(cu).cuda())
     torch.cuda.synchronize()
     got = {n: (host(t) if t is not None else None) for n, t in g.items()}
-    names = ["dq", "dk", "dv", "dbeta"] + (["dlog_a"] if gate == "scalar" else [])
+    names = ["dq", "dk", "dv", "dbeta"] + (["dlog_a"] if gate != "none" else [])
     ref = {n: np.zeros(got[n].shape) for n in names}
     for i in range(len(LENS)):
         lo, hi = int(cu[i]), int(cu[i + 1])
@@ -296,3 +296,74 @@ def test_bwd_literal_form(shape):
     x = _inputs(*shape, "scalar", seed=sum(shape) + 5)
     x["log_a"][:, 40:43] = -6.0            # strong gates: the page and literal forms differ clearly
     _compare(_gpu(x, form="literal"), _ref(x, form="literal"), "scalar")
+
+
+# ---- per-channel gate (d_k = 128) --------------------------------------------------
+@pytest.mark.parametrize("form", ["page", "literal"])
+@pytest.mark.parametrize("shape", [(2, 200, 3, 128, 128), (2, 100, 2, 128, 64), (1, 64, 2, 128, 128)],
+                         ids=lambda s: "B%dT%dH%ddk%ddv%d" % s)
+def test_bwd_channel(shape, form):
+    """A gate per key channel: the decayed operands inside the d_k sums, and d log a
+    per (token, head, channel)."""
+    need_gpu()
+    say(f"case bwd channel form={form} shape={shape}")
+    x = _inputs(*shape, "channel", seed=sum(shape) + 11)
+    _compare(_gpu(x, form=form), _ref(x, form=form), "channel")
+
+
+@pytest.mark.parametrize("T", [1, 63, 65, 129])
+def test_bwd_channel_lengths(T):
+    need_gpu()
+    say(f"case bwd channel T={T}")
+    x = _inputs(1, T, 2, 128, 128, "channel", seed=40 + T)
+    _compare(_gpu(x), _ref(x), "channel")
+
+
+def test_bwd_channel_strong_channels():
+    """Some channels forget fast (log a = -3 over 12 tokens, 36 inside one 16-row
+    block) beside slow ones: the block-split decay factors stay in range."""
+    need_gpu()
+    x = _inputs(2, 160, 2, 128, 128, "channel", seed=45)
+    x["log_a"][:, 20:32, :, :16] = -3.0
+    x["log_a"][1, 100:110, 1, 64:] = -3.0
+    _compare(_gpu(x), _ref(x), "channel")
+    _compare(_gpu(x, form="literal"), _ref(x, form="literal"), "channel")
+
+
+def test_bwd_channel_deterministic():
+    need_gpu()
+    x = _inputs(2, 150, 2, 128, 128, "channel", seed=47)
+    a, b = _gpu(x), _gpu(x)
+    for n in NAMES:
+        assert np.array_equal(a[n], b[n]), n
+
+
+def test_bwd_channel_full_size_sampled():
+    """The per-channel B2 H32 T32768 d128 bf16 workload at full size; two (b, h)
+    slices against the oracle run on that slice alone."""
+    need_gpu()
+    import torch
+    import gated_delta_rule_21_amd as gdr
+    wl = CONFIGS[4]
+    say(f"full-size backward {wl.name}: generating inputs")
+    x = chunk_inputs(wl)
+    x.update(grad_inputs(wl))
+    args = [dev(x[n], "bf16") for n in ("q", "k", "v", "beta", "log_a")]
+    S0 = torch.from_numpy(x["S0"]).cuda()
+    dO, dS_T = dev(x["dO"], "bf16"), torch.from_numpy(x["dS_T"]).cuda()
+    del x
+    say("  running GPU")
+    g = gdr.chunk_bwd(*args, S0, dO, dS_T)
+    torch.cuda.synchronize()
+    for n in NAMES:
+        assert bool(torch.isfinite(g[n].float()).all()), n
+    for b, h in [(0, 0), (wl.B - 1, wl.H - 1)]:
+        say(f"  oracle slice b={b} h={h}")
+        s = slice_inputs(wl, b, h)
+        s.update(grad_slice(wl, b, h))
+        e = lambda a: None if a is None else a[None, :, None]
+        ref = oracle_backward(e(s["q"]), e(s["k"]), e(s["v"]), e(s["beta"]), e(s["log_a"]), s["S0"][None, None],
+                              e(s["dO"]), s["dS_T"][None, None])
+        for n in ("dq", "dk", "dv", "dbeta", "dlog_a"):
+            check(f"{n}[b={b},h={h}]", host(g[n][b, :, h]), ref[n][0, :, 0], TOL["bf16"])
+        check(f"dS0[b={b},h={h}]", host(g["dS0"][b, h]), ref["dS0"][0, 0], TOL["bf16"])
