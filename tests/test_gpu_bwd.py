@@ -247,18 +247,20 @@ def test_bwd_varlen(gate, dk, dv):
         check(n, got[n], ref[n], TOL["bf16"])
 
 
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
 @pytest.mark.parametrize("packed", [False, True], ids=["batch", "packed"])
-def test_autograd_function(packed):
+def test_autograd_function(packed, gate):
     """chunk_attn (chunk_fwd with chunk_bwd as its torch autograd backward): the .grad
     of every input against the oracle's gradients of <dO, o> + <dS_T, S_T>."""
     need_gpu()
     import torch
     import gated_delta_rule_21_amd as gdr
+    say(f"case autograd gate={gate} packed={packed}")
     if packed:
-        x, cu = _packed([70, 1, 130], 2, 128, 128, "scalar", seed=31)
+        x, cu = _packed([70, 1, 130], 2, 128, 128, gate, seed=31)
         cu_t = torch.from_numpy(cu).cuda()
     else:
-        x, cu_t = _inputs(2, 150, 2, 128, 128, "scalar", seed=31), None
+        x, cu_t = _inputs(2, 150, 2, 128, 128, gate, seed=31), None
     leaf = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(dt).cuda().requires_grad_(True)
     ins = {n: leaf(x[n], torch.bfloat16) for n in ("q", "k", "v", "beta", "log_a")}
     S0 = leaf(x["S0"], torch.float32)
