@@ -38,7 +38,7 @@
 // rounded once to bf16 they cancel only to its 8 bits, which costs d log a about
 // 2 % relative error on long sequences against 0.1 % with the residual.
 //
-// One workgroup of eight waves per chunk.  Phase 1 takes d_v in slices of 32
+// One workgroup of eight waves per chunk.  Phase 1 takes d_v in slices of QW
 // columns (X, dDelta; Delta, dY; then the products accumulated over d_v); phase 2
 // forms g, the decayed operand tiles and the d_k-side sums, and writes dq, dk,
 // dbeta and d log a.  Every sum is in a fixed order (no atomics).
@@ -52,8 +52,9 @@ namespace gdr {
 namespace {
 
 constexpr int CDK = 128;   // d_k of this kernel
-constexpr int QW = 32;     // d_v columns per phase-1 slice
 
+// QW: d_v columns per phase-1 slice (32 or 64).
+template <int QW>
 struct ChanLayout {
   // phase 1
   static constexpr int LKP = ld_row(CDK);    // k e^{g_read}, k e^{g_63 - g}: rows
@@ -94,18 +95,25 @@ struct ChanLayout {
   static constexpr size_t O_F = cmax(END1, END2);
   static constexpr size_t O_TOT = O_F + 6 * CH * 4;           // [4][d_k]
   static constexpr size_t O_RED = O_TOT + 4 * CDK * 4;
-  // dbeta: [2][64] (sum_v dY X by 16-column tile), [8][64] (k . G by channel tile);
-  // <dS', S> by wave [8][d_k]
-  static constexpr size_t NRED = 2 * CH + 8 * CH + 8 * CDK;
+  // dbeta: [QW / 16][64] (sum_v dY X by 16-column tile), [8][64] (k . G by channel
+  // tile); <dS', S> by wave [8][d_k]
+  static constexpr size_t NRED = (QW / 16) * CH + 8 * CH + 8 * CDK;
   static constexpr size_t TOTAL = O_RED + NRED * 4;
 };
 
-template <int DV>
+template <int DV, int QW>
 __global__ __launch_bounds__(512) void bwd_chunk_chan_kernel(BwdParams p) {
-  typedef ChanLayout L;
+  typedef ChanLayout<QW> L;
   constexpr int DK = CDK;
   constexpr int NT = 512;
   constexpr int NQ = DV / QW;
+  constexpr int VT = QW / 16;                  // 16-column tiles per slice
+  constexpr int NTW = 4 * VT / 8;              // phase-1 tiles (row block, column tile) per wave
+  constexpr int VPR = QW / 8;                  // 16-byte pieces per row of a v or dO slice
+  constexpr int NVP = CH * VPR;                // ... per slice
+  constexpr int NVO = 2 * NVP / NT;            // v and dO pieces per thread
+  constexpr int NSP = QW * DK / 8 / NT;        // pieces of an S^T slice per thread
+  static_assert(NTW >= 1 && NVO >= 1 && NSP >= 1 && NVP % 64 == 0, "slice width");
   constexpr uint32_t RB = rec_bytes(IO_BF16, GATE_CHANNEL, DK);
   constexpr uint32_t SBYTES = DV * DK * 2;
   static_assert(L::TOTAL <= 163840, "LDS budget");
@@ -131,7 +139,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_chan_kernel(BwdParams p) {
   const float* sF = reinterpret_cast<const float*>(smem + L::O_F);   // beta [64], e^{g_63} [d_k]
   float* sTot = reinterpret_cast<float*>(smem + L::O_TOT);
   float* rbX = reinterpret_cast<float*>(smem + L::O_RED);
-  float* rbK = rbX + 2 * CH;
+  float* rbK = rbX + VT * CH;
   float* rsd = rbK + 8 * CH;
 
   const ChunkParams& f = p.f;
@@ -186,28 +194,45 @@ __global__ __launch_bounds__(512) void bwd_chunk_chan_kernel(BwdParams p) {
     if (tid < 96) *reinterpret_cast<u32x4*>(smem + L::O_F + tid * 16) = hf;
   }
 
-  // ---- one 32-column slice of v, dO, S^T, dS'^T ------------------------------------
-  u32x4 hvo, hs, hds;
+  // ---- one slice of v, dO, S^T, dS'^T -----------------------------------------------
+  // Piece pv = tid + i NT of the v and dO slices is dO's when pv >= NVP (the choice is
+  // the same for the whole wave): row (pv % NVP) / VPR, columns 8 (pv % VPR) ..
+  u32x4 hvo[NVO], hs[NSP], hds[NSP];
   float sdot[8];                      // this thread's part of sum_v S dS' for channels 8 (tid % 16) ..
 #pragma unroll
   for (int e = 0; e < 8; ++e) sdot[e] = 0.f;
   auto load_slice = [&](int qi) __attribute__((always_inline)) {
-    const int t = tid & 255;          // v (threads < 256) or dO: row t / 4, columns 8 (t % 4) ..
-    hvo = buf_load16(wave < 4 ? rv : rdo, static_cast<uint32_t>(((t / 4) * H * DV + QW * qi + (t % 4) * 8) * 2), sv);
-    const uint32_t off = static_cast<uint32_t>((QW * qi * DK + tid * 8) * 2);   // value-major: row v = tid / 16
-    hs = buf_load16(rst, off, ss);
-    hds = buf_load16(rds, off, ss);
+#pragma unroll
+    for (int i = 0; i < NVO; ++i) {
+      const int t = (tid + i * NT) % NVP;
+      const bool is_do = (64 * wave + i * NT) >= NVP;
+      hvo[i] = buf_load16(is_do ? rdo : rv, static_cast<uint32_t>(((t / VPR) * H * DV + QW * qi + (t % VPR) * 8) * 2), sv);
+    }
+#pragma unroll
+    for (int i = 0; i < NSP; ++i) {   // value-major: row v = pc / 16
+      const uint32_t off = static_cast<uint32_t>((QW * qi * DK + (tid + i * NT) * 8) * 2);
+      hs[i] = buf_load16(rst, off, ss);
+      hds[i] = buf_load16(rds, off, ss);
+    }
   };
   auto store_slice = [&]() __attribute__((always_inline)) {
-    const int t = tid & 255;
-    put16((tid < 256 ? sV : sdO) + (t / 4) * L::LVQ + (t % 4) * 8, hvo);
-    put16(sS + (tid / 16) * L::LSQ + (tid % 16) * 8, hs);
-    put16(sdS + (tid / 16) * L::LSQ + (tid % 16) * 8, hds);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t a = hs[j], b = hds[j];
-      sdot[2 * j] += bf16_bits_to_f32(a & 0xffffu) * bf16_bits_to_f32(b & 0xffffu);
-      sdot[2 * j + 1] += bf16_bits_to_f32(a >> 16) * bf16_bits_to_f32(b >> 16);
+    for (int i = 0; i < NVO; ++i) {
+      const int t = (tid + i * NT) % NVP;
+      const bool is_do = (64 * wave + i * NT) >= NVP;
+      put16((is_do ? sdO : sV) + (t / VPR) * L::LVQ + (t % VPR) * 8, hvo[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < NSP; ++i) {
+      const int pc = tid + i * NT;
+      put16(sS + (pc / 16) * L::LSQ + (pc % 16) * 8, hs[i]);
+      put16(sdS + (pc / 16) * L::LSQ + (pc % 16) * 8, hds[i]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t a = hs[i][j], b = hds[i][j];
+        sdot[2 * j] += bf16_bits_to_f32(a & 0xffffu) * bf16_bits_to_f32(b & 0xffffu);
+        sdot[2 * j + 1] += bf16_bits_to_f32(a >> 16) * bf16_bits_to_f32(b >> 16);
+      }
     }
   };
   static_assert(L::LVQ == L::LOQ, "v and dO slices share a stride");
@@ -230,51 +255,64 @@ __global__ __launch_bounds__(512) void bwd_chunk_chan_kernel(BwdParams p) {
   store_slice();
   __syncthreads();
 
-  // Phase-1 tiles of this wave: row block R1 and 16-column tile vt of each slice for
-  // X, dDelta, Delta and dY; the 64 x 64 blocks u = wave, wave + 8 (< 10) of dA and
-  // dP; and, for the d_k-side products, channel tile `wave` over all four row blocks.
-  const int R1 = wave >> 1, vt = wave & 1;
+  // Phase-1 tiles of this wave: tiles t = wave + 8 i (row block t / VT, 16-column tile
+  // t % VT of each slice) of X, dDelta, Delta and dY; the 64 x 64 blocks u = wave,
+  // wave + 8 (< 10) of dA and dP; and, for the d_k-side products, channel tile `wave`
+  // over all four row blocks.
   f32x4 dAa[2], dPa[2], dOS[4], dYS[4], DdS[4];
 #pragma unroll
   for (int i = 0; i < 2; ++i) dAa[i] = dPa[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int R = 0; R < 4; ++R) dOS[R] = dYS[R] = DdS[R] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float bxp = 0.f;                     // sum_v dY X of row 16 R1 + lr over this wave's columns
-  const float beta1 = sF[16 * R1 + lr];
+  float bxp[NTW], beta1[NTW];          // sum_v dY X of the tile's row 16 R + lr; beta of that row
+#pragma unroll
+  for (int i = 0; i < NTW; ++i) {
+    bxp[i] = 0.f;
+    beta1[i] = sF[16 * ((wave + 8 * i) / VT) + lr];
+  }
   const rsrc_t rdv = sl.rs(p.dv, DV);
 
   for (int qi = 0; qi < NQ; ++qi) {
     if (qi + 1 < NQ) load_slice(qi + 1);
     else load_phase2();
-    // X and dDelta, row form (lane: row 16 R1 + lr, columns 16 vt + 4 lg ..)
-    f32x4 x = {0.f, 0.f, 0.f, 0.f}, dd = {0.f, 0.f, 0.f, 0.f};
+    // X and dDelta, row form (lane: row 16 R + lr, columns 16 vt + 4 lg ..)
+    f32x4 x[NTW];
 #pragma unroll
-    for (int kb = 0; kb < DK / 32; ++kb) {
-      x = O::mma2(x, rowf(sS, L::LSQ, 16 * vt, 32 * kb, lr, lg), rowf(sS, L::LSQ, 16 * vt, 32 * kb + 16, lr, lg),
-                  rowf(sKp, L::LKP, 16 * R1, 32 * kb, lr, lg), rowf(sKp, L::LKP, 16 * R1, 32 * kb + 16, lr, lg));
-      dd = O::mma2(dd, rowf(sdS, L::LSQ, 16 * vt, 32 * kb, lr, lg), rowf(sdS, L::LSQ, 16 * vt, 32 * kb + 16, lr, lg),
-                   rowf(sKd, L::LKP, 16 * R1, 32 * kb, lr, lg), rowf(sKd, L::LKP, 16 * R1, 32 * kb + 16, lr, lg));
+    for (int i = 0; i < NTW; ++i) {
+      const int R = (wave + 8 * i) / VT, vt = (wave + 8 * i) % VT;
+      f32x4 xa = {0.f, 0.f, 0.f, 0.f}, dd = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < DK / 32; ++kb) {
+        xa = O::mma2(xa, rowf(sS, L::LSQ, 16 * vt, 32 * kb, lr, lg), rowf(sS, L::LSQ, 16 * vt, 32 * kb + 16, lr, lg),
+                     rowf(sKp, L::LKP, 16 * R, 32 * kb, lr, lg), rowf(sKp, L::LKP, 16 * R, 32 * kb + 16, lr, lg));
+        dd = O::mma2(dd, rowf(sdS, L::LSQ, 16 * vt, 32 * kb, lr, lg), rowf(sdS, L::LSQ, 16 * vt, 32 * kb + 16, lr, lg),
+                     rowf(sKd, L::LKP, 16 * R, 32 * kb, lr, lg), rowf(sKd, L::LKP, 16 * R, 32 * kb + 16, lr, lg));
+      }
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)  // + P^T dO (rows of P from block R down)
+        if (kb >= R) dd = O::mma1(dd, colf(sdO, L::LOQ, 16 * kb, 16 * vt, lr, lg), colf(sP, L::LCP, 16 * kb, 16 * R, lr, lg));
+      x[i] = O::f32(rowf(sV, L::LVQ, 16 * R, 16 * vt, lr, lg)) - xa;   // X = V - Kp S
+      st_row(sV, L::LVQ, 16 * R + lr, 16 * vt + 4 * lg, x[i] * beta1[i]);   // only this wave reads this tile of v
+      st_row(sdD, L::LDQ, 16 * R + lr, 16 * vt + 4 * lg, dd);
     }
-#pragma unroll
-    for (int kb = R1; kb < 4; ++kb)   // + P^T dO (rows of P from block R1 down)
-      dd = O::mma1(dd, colf(sdO, L::LOQ, 16 * kb, 16 * vt, lr, lg), colf(sP, L::LCP, 16 * kb, 16 * R1, lr, lg));
-    x = O::f32(rowf(sV, L::LVQ, 16 * R1, 16 * vt, lr, lg)) - x;   // X = V - Kp S
-    st_row(sV, L::LVQ, 16 * R1 + lr, 16 * vt + 4 * lg, x * beta1);   // only this wave reads this tile of v
-    st_row(sdD, L::LDQ, 16 * R1 + lr, 16 * vt + 4 * lg, dd);
     __syncthreads();
 
     // Delta = T diag(beta) X and dY = T^T dDelta, row form
-    f32x4 dl = {0.f, 0.f, 0.f, 0.f}, dy = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int J = 0; J < 4; ++J)
-      if (J <= R1) dl = O::mma1(dl, colf(sV, L::LVQ, 16 * J, 16 * vt, lr, lg), colf(sT, L::LCT, 16 * J, 16 * R1, lr, lg));
+    for (int i = 0; i < NTW; ++i) {
+      const int R = (wave + 8 * i) / VT, vt = (wave + 8 * i) % VT;
+      f32x4 dl = {0.f, 0.f, 0.f, 0.f}, dy = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-      if (kb >= R1) dy = O::mma1(dy, colf(sdD, L::LDQ, 16 * kb, 16 * vt, lr, lg), rowf(sT, L::LCT, 16 * R1, 16 * kb, lr, lg));
-    st_row(sDl, L::LRQ, 16 * R1 + lr, 16 * vt + 4 * lg, dl);
-    st_row(sdY, L::LRQ, 16 * R1 + lr, 16 * vt + 4 * lg, dy);
-    buf_store8(bits8(dy * beta1), rdv, static_cast<uint32_t>(((16 * R1 + lr) * H * DV + QW * qi + 16 * vt + 4 * lg) * 2), sv);
-    bxp += lg_sum(dy[0] * x[0] + dy[1] * x[1] + dy[2] * x[2] + dy[3] * x[3]);
+      for (int J = 0; J < 4; ++J)
+        if (J <= R) dl = O::mma1(dl, colf(sV, L::LVQ, 16 * J, 16 * vt, lr, lg), colf(sT, L::LCT, 16 * J, 16 * R, lr, lg));
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        if (kb >= R) dy = O::mma1(dy, colf(sdD, L::LDQ, 16 * kb, 16 * vt, lr, lg), rowf(sT, L::LCT, 16 * R, 16 * kb, lr, lg));
+      st_row(sDl, L::LRQ, 16 * R + lr, 16 * vt + 4 * lg, dl);
+      st_row(sdY, L::LRQ, 16 * R + lr, 16 * vt + 4 * lg, dy);
+      buf_store8(bits8(dy * beta1[i]), rdv, static_cast<uint32_t>(((16 * R + lr) * H * DV + QW * qi + 16 * vt + 4 * lg) * 2), sv);
+      bxp[i] += lg_sum(dy[0] * x[i][0] + dy[1] * x[i][1] + dy[2] * x[i][2] + dy[3] * x[i][3]);
+    }
     __syncthreads();
 
     // products over this slice's columns
@@ -284,19 +322,28 @@ __global__ __launch_bounds__(512) void bwd_chunk_chan_kernel(BwdParams p) {
       if (u < 10) {                    // row form: lane row 16R + lr of dY Delta^T and dO Delta^T
         int R, J;
         tri_block(u, R, J);
-        const frag d0 = rowf(sDl, L::LRQ, 16 * J, 0, lr, lg), d1 = rowf(sDl, L::LRQ, 16 * J, 16, lr, lg);
-        dAa[i] = O::mma2(dAa[i], d0, d1, rowf(sdY, L::LRQ, 16 * R, 0, lr, lg), rowf(sdY, L::LRQ, 16 * R, 16, lr, lg));
-        dPa[i] = O::mma2(dPa[i], d0, d1, rowf(sdO, L::LOQ, 16 * R, 0, lr, lg), rowf(sdO, L::LOQ, 16 * R, 16, lr, lg));
+#pragma unroll
+        for (int kk = 0; kk < QW / 32; ++kk) {
+          const frag d0 = rowf(sDl, L::LRQ, 16 * J, 32 * kk, lr, lg), d1 = rowf(sDl, L::LRQ, 16 * J, 32 * kk + 16, lr, lg);
+          dAa[i] = O::mma2(dAa[i], d0, d1, rowf(sdY, L::LRQ, 16 * R, 32 * kk, lr, lg),
+                           rowf(sdY, L::LRQ, 16 * R, 32 * kk + 16, lr, lg));
+          dPa[i] = O::mma2(dPa[i], d0, d1, rowf(sdO, L::LOQ, 16 * R, 32 * kk, lr, lg),
+                           rowf(sdO, L::LOQ, 16 * R, 32 * kk + 16, lr, lg));
+        }
       }
     }
-    {
-      const frag s0 = colf(sS, L::LSQ, 0, 16 * wave, lr, lg), s1 = colf(sS, L::LSQ, 16, 16 * wave, lr, lg);
-      const frag e0 = colf(sdS, L::LSQ, 0, 16 * wave, lr, lg), e1 = colf(sdS, L::LSQ, 16, 16 * wave, lr, lg);
+#pragma unroll
+    for (int kk = 0; kk < QW / 32; ++kk) {
+      const frag s0 = colf(sS, L::LSQ, 32 * kk, 16 * wave, lr, lg), s1 = colf(sS, L::LSQ, 32 * kk + 16, 16 * wave, lr, lg);
+      const frag e0 = colf(sdS, L::LSQ, 32 * kk, 16 * wave, lr, lg), e1 = colf(sdS, L::LSQ, 32 * kk + 16, 16 * wave, lr, lg);
 #pragma unroll
       for (int R = 0; R < 4; ++R) {    // column form: rows 16R + 4 lg + s, channel 16 wave + lr
-        dOS[R] = O::mma2(dOS[R], rowf(sdO, L::LOQ, 16 * R, 0, lr, lg), rowf(sdO, L::LOQ, 16 * R, 16, lr, lg), s0, s1);
-        dYS[R] = O::mma2(dYS[R], rowf(sdY, L::LRQ, 16 * R, 0, lr, lg), rowf(sdY, L::LRQ, 16 * R, 16, lr, lg), s0, s1);
-        DdS[R] = O::mma2(DdS[R], rowf(sDl, L::LRQ, 16 * R, 0, lr, lg), rowf(sDl, L::LRQ, 16 * R, 16, lr, lg), e0, e1);
+        dOS[R] = O::mma2(dOS[R], rowf(sdO, L::LOQ, 16 * R, 32 * kk, lr, lg), rowf(sdO, L::LOQ, 16 * R, 32 * kk + 16, lr, lg),
+                         s0, s1);
+        dYS[R] = O::mma2(dYS[R], rowf(sdY, L::LRQ, 16 * R, 32 * kk, lr, lg), rowf(sdY, L::LRQ, 16 * R, 32 * kk + 16, lr, lg),
+                         s0, s1);
+        DdS[R] = O::mma2(DdS[R], rowf(sDl, L::LRQ, 16 * R, 32 * kk, lr, lg), rowf(sDl, L::LRQ, 16 * R, 32 * kk + 16, lr, lg),
+                         e0, e1);
       }
     }
     __syncthreads();
@@ -337,7 +384,9 @@ __global__ __launch_bounds__(512) void bwd_chunk_chan_kernel(BwdParams p) {
     put16(sRk + row * L::LR + c0, hk[i]);
     put16(sRq + row * L::LR + c0, hq[i]);
   }
-  if (lg == 0) rbX[vt * CH + 16 * R1 + lr] = bxp;
+#pragma unroll
+  for (int i = 0; i < NTW; ++i)
+    if (lg == 0) rbX[((wave + 8 * i) % VT) * CH + 16 * ((wave + 8 * i) / VT) + lr] = bxp[i];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {        // <dS', S> over this wave's rows of the slices
     const float v = lg_sum(sdot[e]);
@@ -505,7 +554,8 @@ __global__ __launch_bounds__(512) void bwd_chunk_chan_kernel(BwdParams p) {
 
   // ---- dbeta -----------------------------------------------------------------------------
   if (wave == 0) {
-    float d = rbX[lane] + rbX[CH + lane];
+    float d = 0.f;
+    for (int v = 0; v < VT; ++v) d += rbX[v * CH + lane];
     for (int w = 0; w < 8; ++w) d += rbK[w * CH + lane];
     const rsrc_t rdb = sl.rs(p.dbeta, 1);
     buf_store2(f32_to_bf16_bits(d), rdb, static_cast<uint32_t>(lane * H * 2), sb);
@@ -519,10 +569,12 @@ hipError_t launch_chunk_bwd_chan(const BwdParams& p, hipStream_t stream) {
   if (f.d_k != CDK) return hipErrorInvalidValue;
   const int64_t nch = (f.T + CH - 1) / CH;
   const unsigned grid = static_cast<unsigned>(f.cu ? f.H * f.nslots : f.B * f.H * nch);
+  // 32-column slices: 64-column ones halve phase 1's barriers but spill at d_v = 128
+  // and measured slower (5.92 against 5.74 ms per call on B2 H32 T32768).
   if (f.d_v == 128)
-    hipLaunchKernelGGL((bwd_chunk_chan_kernel<128>), dim3(grid), dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((bwd_chunk_chan_kernel<128, 32>), dim3(grid), dim3(512), 0, stream, p);
   else if (f.d_v == 64)
-    hipLaunchKernelGGL((bwd_chunk_chan_kernel<64>), dim3(grid), dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((bwd_chunk_chan_kernel<64, 32>), dim3(grid), dim3(512), 0, stream, p);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
