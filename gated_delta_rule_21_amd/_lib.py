@@ -17,7 +17,7 @@ import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdr.so")
 
-GDR_OK, GDR_ERR_INVALID_ARG, GDR_ERR_UNSUPPORTED, GDR_ERR_ALIGNMENT, GDR_ERR_HIP = range(5)
+GDR_OK, GDR_ERR_INVALID_ARG, GDR_ERR_UNSUPPORTED, GDR_ERR_ALIGNMENT, GDR_ERR_WORKSPACE, GDR_ERR_HIP = range(6)
 GDR_F32, GDR_BF16 = 0, 1
 GATES = {"none": 0, "scalar": 1, "channel": 2}
 FORMS = {"page": 0, "literal": 1}
@@ -229,8 +229,9 @@ def chunk_bwd(q, k, v, beta, log_a, S0, dO, dS_T=None, *, cu_seqlens=None, form:
     dv = v.shape[-1]
     packed = cu_seqlens is not None
     if packed:
-        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.device != q.device:
-            raise ValueError("cu_seqlens must be an int32 vector on the inputs' device")
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous() \
+                or cu_seqlens.device != q.device:
+            raise ValueError("cu_seqlens must be a contiguous 1-D int32 tensor on the inputs' device")
         if B != 1:
             raise ValueError("packed sequences take [1, T, H, d] tensors")
         nstate = cu_seqlens.numel() - 1

@@ -90,6 +90,21 @@ struct WsRec {
   }
 };
 
+// Per-channel gate: the transform splits each decay e^{g_r - g_j} at the first row
+// of a 16-row block into a factor <= 1 on one operand and a factor >= 1 on the
+// other, and the literal form's first row reads e^{g_{r-1} - g_16R} >= 1.  fp32
+// (and bf16) hold e^x up to x ~ 88.7, and a factor below e^-SPLIT_MAX meeting one
+// above e^+SPLIT_MAX loses at most e^-87.3 * e^SPLIT_MAX of a product to
+// denormals.  A chunk in which some channel decays by more than e^-SPLIT_MAX
+// inside one block (or within the row before a block) is marked in its record and
+// its T and P blocks are formed again by chunk_prep_generic_kernel, which takes
+// every decay as one exponential of a non-positive exponent.
+constexpr float SPLIT_MAX = 64.f;
+// Byte offset in a record of that mark (fp32; 1 = formed by the generic kernel).
+// Row 5 of the factor rows is unused with a per-channel gate (d_k <= 128).
+template <int ESZ>
+__host__ __device__ constexpr uint32_t rec_flag_off() { return WsRec<ESZ>::F_OFF + 5 * CH * 4; }
+
 // Bytes of one record for the I/O type, gate and d_k.
 __host__ __device__ constexpr uint32_t rec_bytes(int io, int gate, int dk) {
   return io == IO_BF16 ? WsRec<2>::BYTES + (gate == GATE_CHANNEL ? 3u * CH * dk * 2u : 0u) : WsRec<4>::BYTES;
@@ -147,6 +162,32 @@ __device__ __forceinline__ bool prep_task(const ChunkParams& p, int64_t task, in
   const SeqSpan s = seq_span(p, b, h);
   n = uni64(slot - (s.t0 / CH + b));
   return n >= 0 && n * CH < s.len;
+}
+
+// The record index of transform task `task` when every lane has a task of its own
+// (prep_task keeps its results wave-uniform).  Same mapping: fixed-length
+// (b H + h) ceil(T / 64) + n; packed sequences h nslots + slot.  False for a task
+// with no chunk.
+__device__ __forceinline__ bool task_record(const ChunkParams& p, int64_t task, int64_t& rec) {
+  const int64_t h = task % p.H;
+  if (!p.cu) {
+    const int64_t nch = (p.T + CH - 1) / CH;
+    const int64_t n = (task / p.H) % nch, b = task / (p.H * nch);
+    rec = (b * p.H + h) * nch + n;
+    return true;
+  }
+  const int64_t slot = task / p.H;
+  int64_t lo = 0, hi = p.B - 1;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi + 1) / 2;
+    if (seq_start(p, mid) / CH + mid <= slot) lo = mid; else hi = mid - 1;
+  }
+  const int64_t a = seq_start(p, lo);
+  int64_t e = p.cu[lo + 1];
+  e = e < a ? a : (e > p.T ? p.T : e);
+  const int64_t n = slot - (a / CH + lo);
+  rec = h * p.nslots + slot;
+  return n >= 0 && n * CH < e - a;
 }
 
 // Block (R, J), J <= R, of the ten-block order above.

@@ -221,6 +221,17 @@ __global__ __launch_bounds__(256) void chunk_prep_lds_kernel(ChunkParams p) {
         for (int r = seg * SEGL; r < (seg + 1) * SEGL; ++r) sG[r * DK + i] += pre;
     }
     __syncthreads();
+    // decays past the split's range go to the generic kernel (see SPLIT_MAX)
+    bool wide = false;
+    for (int task = tid; task < CH * DK; task += NT) {
+      const int r = task / DK, i = task % DK;
+      wide |= sG[16 * (r >> 4) * DK + i] - sG[r * DK + i] > SPLIT_MAX;
+      if (p.literal && (r & 15) == 0)
+        wide |= (r > 0 ? sG[(r - 1) * DK + i] : 0.f) - sG[r * DK + i] > SPLIT_MAX;
+    }
+    wide = __syncthreads_or(wide);
+    if (tid == 0) *reinterpret_cast<float*>(rec + rec_flag_off<ESZ>()) = wide ? 1.f : 0.f;
+    if (wide) return;                           // uniform over the workgroup
     for (int i = tid; i < DK; i += NT) {
 #pragma unroll
       for (int R = 1; R < 4; ++R)
@@ -524,7 +535,21 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_chan_kernel(ChunkParams p) 
     *reinterpret_cast<u32x2*>(x + CH * DK * ESZ) = __builtin_bit_cast(u32x2, to_bf16x4(sq));
     *reinterpret_cast<u32x2*>(x + 2 * CH * DK * ESZ) = __builtin_bit_cast(u32x2, to_bf16x4(sd));
   }
-  __syncthreads();
+  // A decay beyond e^-SPLIT_MAX inside this thread's rows of the block (the column
+  // factor e^{g_16R - g}), or, literal form, on the row before the block (the first
+  // row's read factor e^{g_{16R-1} - g_16R}), leaves the chunk to the generic kernel.
+  // The state pass's operands above carry factors <= 1 and stand as written.
+  bool wide = false;
+#pragma unroll
+  for (int j = 0; j < SL; ++j)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) wide |= gR[c] - g[j][c] > SPLIT_MAX;
+  if (p.literal && r0 % 16 == 0)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) wide |= pre[c] - gR[c] > SPLIT_MAX;
+  wide = __syncthreads_or(wide);
+  if (tid == 0) *reinterpret_cast<float*>(rec + rec_flag_off<2>()) = wide ? 1.f : 0.f;
+  if (wide) return;                             // uniform over the workgroup
 
   // ---- 16x16 blocks: rows (R) of sK or sQ against rows (J) of sY, the column operand
   // carrying e^{g_16R - g_16J} below the diagonal.  With `tr` the product is formed
@@ -615,6 +640,158 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_chan_kernel(ChunkParams p) 
     const int a = (pc % PPB) / PPR, b0 = (pc % PPR) * EPV;
     *reinterpret_cast<u32x4*>(rec + W::T_OFF + pc * 16) =
         *reinterpret_cast<const u32x4*>(sT + (16 * J + a) * LCH + 16 * Rb + b0);
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// Per-channel gate, chunks whose decay inside a 16-row block exceeds the split's
+// range (marked by the transform, see SPLIT_MAX): their T and P blocks are formed
+// again in fp32 with every decay taken as one exponential of a non-positive
+// exponent,
+//     A_rj = beta_r sum_c k_rc k_jc e^{g_read,rc - g_jc}   (j < r),
+//     P_rj = sum_c q_rc k_jc e^{g_rc - g_jc}                (j <= r),
+//     T    = (I + A)^{-1}, by forward substitution, one column per thread.
+// One workgroup covers 256 transform tasks: each thread reads one task's mark, the
+// marked ones are listed in LDS and the workgroup forms them one after another.
+// The rest of the record (the state pass's operands and factors, all carrying
+// factors <= 1) stands as the transform wrote it.
+// ---------------------------------------------------------------------------------
+template <int DK>
+struct GenLayout {
+  static constexpr int LK = DK + 1;                  // odd strides: rows r and j of one column sit in different banks
+  static constexpr int LT = CH + 1;
+  static constexpr size_t OFF_K = 0;                                // k [64][LK] fp32
+  static constexpr size_t OFF_Q = OFF_K + size_t(CH) * LK * 4;      // q
+  static constexpr size_t OFF_G = OFF_Q + size_t(CH) * LK * 4;      // [65][LK]: row 0 zero, row r + 1 = g_r
+  static constexpr size_t OFF_A = OFF_G + size_t(CH + 1) * LK * 4;  // A [64][LT]
+  static constexpr size_t OFF_T = OFF_A + size_t(CH) * LT * 4;      // T [64][LT]
+  static constexpr size_t OFF_B = OFF_T + size_t(CH) * LT * 4;      // beta [64]
+  static constexpr size_t TOTAL = OFF_B + CH * 4;
+};
+
+template <int IO, int DK>
+__global__ __launch_bounds__(256) void chunk_prep_generic_kernel(ChunkParams p, int64_t ntasks) {
+  typedef typename Io<IO>::elem elem;
+  constexpr int ESZ = int(sizeof(elem));
+  typedef WsRec<ESZ> W;
+  typedef GenLayout<DK> L;
+  constexpr int NT = 256, LK = L::LK, LT = L::LT;
+  constexpr uint32_t RB = rec_bytes(IO, GATE_CHANNEL, DK);
+  static_assert(L::TOTAL <= 163840, "LDS budget");
+
+  __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
+  __shared__ int s_list[NT];
+  __shared__ int s_n;
+  float* sK = reinterpret_cast<float*>(smem + L::OFF_K);
+  float* sQ = reinterpret_cast<float*>(smem + L::OFF_Q);
+  float* sG = reinterpret_cast<float*>(smem + L::OFF_G);
+  float* sA = reinterpret_cast<float*>(smem + L::OFF_A);
+  float* sT = reinterpret_cast<float*>(smem + L::OFF_T);
+  float* sB = reinterpret_cast<float*>(smem + L::OFF_B);
+  const int tid = threadIdx.x;
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * NT;
+
+  if (tid == 0) s_n = 0;
+  __syncthreads();
+  {
+    const int64_t task = base + tid;
+    int64_t rec;
+    if (task < ntasks && task_record(p, task, rec)) {
+      const float mark = *reinterpret_cast<const float*>(static_cast<const char*>(p.ws) + rec * RB + rec_flag_off<ESZ>());
+      if (mark != 0.f) s_list[atomicAdd(&s_n, 1)] = tid;
+    }
+  }
+  __syncthreads();
+  const int nmarked = s_n;
+
+  auto load1 = [&](rsrc_t r, uint32_t off) -> float {
+    if constexpr (IO == IO_BF16) return bf16_bits_to_f32(buf_load2(r, off, 0));
+    else return __uint_as_float(buf_load4(r, off, 0));
+  };
+  for (int m = 0; m < nmarked; ++m) {
+    const int64_t task = uni64(base + s_list[m]);
+    int64_t bb, n, hh;
+    prep_task(p, task, bb, n, hh);              // a listed task has a chunk
+    const SeqSpan sq = seq_span(p, bb, hh);
+    const int H = static_cast<int>(p.H);
+    char* rec = static_cast<char*>(p.ws) + (sq.rec0 + n) * RB;
+    // the chunk's rows; rows past the end of the sequence read as zero
+    const int64_t t0 = n * CH;
+    const int64_t row0 = (sq.t0 + t0) * p.H + hh;
+    const int64_t left = sq.len - t0;
+    const uint32_t span = static_cast<uint32_t>(((left < CH ? left : CH) - 1) * p.H + 1);
+    const rsrc_t rk = make_rsrc(static_cast<const elem*>(p.k) + row0 * DK, span * DK * ESZ);
+    const rsrc_t rq = make_rsrc(static_cast<const elem*>(p.q) + row0 * DK, span * DK * ESZ);
+    const rsrc_t rl = make_rsrc(static_cast<const elem*>(p.log_a) + row0 * DK, span * DK * ESZ);
+    const rsrc_t rb = make_rsrc(static_cast<const elem*>(p.beta) + row0, span * ESZ);
+
+    __syncthreads();                            // the previous chunk's tiles are no longer read
+    for (int e = tid; e < CH * DK; e += NT) {
+      const int r = e / DK, c = e % DK;
+      const uint32_t off = static_cast<uint32_t>((r * H * DK + c) * ESZ);
+      sK[r * LK + c] = load1(rk, off);
+      sQ[r * LK + c] = load1(rq, off);
+      sG[(r + 1) * LK + c] = load1(rl, off);
+    }
+    for (int c = tid; c < DK; c += NT) sG[c] = 0.f;
+    if (tid < CH) sB[tid] = load1(rb, static_cast<uint32_t>(tid * H * ESZ));
+    __syncthreads();
+    for (int c = tid; c < DK; c += NT) {        // inclusive running sum down each channel
+      float acc = 0.f;
+      for (int r = 0; r < CH; ++r) {
+        acc += sG[(r + 1) * LK + c];
+        sG[(r + 1) * LK + c] = acc;
+      }
+    }
+    __syncthreads();
+
+    // one (r, j) pair, j <= r, per thread at a time
+    for (int pr = tid; pr < CH * (CH + 1) / 2; pr += NT) {
+      int r = static_cast<int>((sqrtf(8.f * pr + 1.f) - 1.f) * 0.5f);
+      while (r * (r + 1) / 2 > pr) --r;
+      while ((r + 1) * (r + 2) / 2 <= pr) ++r;
+      const int j = pr - r * (r + 1) / 2;
+      const float* kr = sK + r * LK;
+      const float* kj = sK + j * LK;
+      const float* qr = sQ + r * LK;
+      const float* gr = sG + (r + 1) * LK;
+      const float* grd = sG + (p.literal ? r : r + 1) * LK;   // g_read: g_r, or g_{r-1} (g_{-1} = 0)
+      const float* gj = sG + (j + 1) * LK;
+      float a = 0.f, pv = 0.f;
+      if (j < r) {
+        for (int c = 0; c < DK; ++c) {
+          a += kr[c] * kj[c] * __expf(grd[c] - gj[c]);
+          pv += qr[c] * kj[c] * __expf(gr[c] - gj[c]);
+        }
+      } else {
+        for (int c = 0; c < DK; ++c) pv += qr[c] * kr[c];
+      }
+      sA[r * LT + j] = j < r ? sB[r] * a : 0.f;
+      const int R = r >> 4, J = j >> 4;
+      Io<IO>::store(reinterpret_cast<elem*>(rec + W::P_OFF), W::at(R, J, r & 15, j & 15) / ESZ, pv);
+      if (R == J && j < r)                      // the zero above the diagonal of a diagonal block
+        Io<IO>::store(reinterpret_cast<elem*>(rec + W::P_OFF), W::at(R, J, j & 15, r & 15) / ESZ, 0.f);
+    }
+    __syncthreads();
+    if (tid < CH) {                             // column j of T = (I + A)^{-1}
+      const int j = tid;
+      for (int i = 0; i < j; ++i) sT[i * LT + j] = 0.f;
+      sT[j * LT + j] = 1.f;
+      for (int i = j + 1; i < CH; ++i) {
+        float s = 0.f;
+        for (int m2 = j; m2 < i; ++m2) s += sA[i * LT + m2] * sT[m2 * LT + j];
+        sT[i * LT + j] = -s;
+      }
+    }
+    __syncthreads();
+    // block (R, J) of the T region holds (T_RJ)^T: element (a, b) = T[16R + b][16J + a]
+    for (int e = tid; e < 10 * 256; e += NT) {
+      const int u = e >> 8, a = (e >> 4) & 15, b = e & 15;
+      int R, J;
+      tri_block(u, R, J);
+      Io<IO>::store(reinterpret_cast<elem*>(rec + W::T_OFF), W::at(R, J, a, b) / ESZ,
+                    sT[(16 * R + b) * LT + 16 * J + a]);
+    }
   }
 }
 
@@ -831,6 +1008,13 @@ static hipError_t launch_prep_t(const ChunkParams& p, int64_t nchunks, hipStream
                        stream, p);
   } else {
     hipLaunchKernelGGL((chunk_prep_reg_kernel<IO, GATE, DK>), dim3(static_cast<unsigned>((ntasks + 3) / 4)),
+                       dim3(256), 0, stream, p, ntasks);
+  }
+  if constexpr (GATE == GATE_CHANNEL) {
+    // chunks whose decay leaves the split's range: T and P formed again
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((chunk_prep_generic_kernel<IO, DK>), dim3(static_cast<unsigned>((ntasks + 255) / 256)),
                        dim3(256), 0, stream, p, ntasks);
   }
   return hipGetLastError();

@@ -132,6 +132,7 @@ const char* gdr_status_string(gdr_status s) {
     case GDR_ERR_INVALID_ARG: return "GDR_ERR_INVALID_ARG: invalid argument";
     case GDR_ERR_UNSUPPORTED: return "GDR_ERR_UNSUPPORTED: configuration not implemented";
     case GDR_ERR_ALIGNMENT: return "GDR_ERR_ALIGNMENT: pointer misaligned";
+    case GDR_ERR_WORKSPACE: return "GDR_ERR_WORKSPACE: workspace missing or too small";
     case GDR_ERR_HIP: return "GDR_ERR_HIP: HIP runtime error";
   }
   return "unknown gdr_status";
@@ -189,9 +190,9 @@ gdr_status chunk_fwd_impl(const gdr_desc* d, const int32_t* cu, int64_t n_seq, c
     if (!beta) return fail(GDR_ERR_INVALID_ARG, "beta is NULL");
     if (!o) return fail(GDR_ERR_INVALID_ARG, "o is NULL");
     if (d->gate != GDR_GATE_NONE && !log_a) return fail(GDR_ERR_INVALID_ARG, "log_a is NULL but a gate is requested");
-    if (!workspace) return fail(GDR_ERR_INVALID_ARG, "workspace is NULL (%zu bytes needed)", ws_need);
+    if (!workspace) return fail(GDR_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", ws_need);
     if (workspace_bytes < ws_need)
-      return fail(GDR_ERR_INVALID_ARG, "workspace_bytes = %zu, %zu needed", workspace_bytes, ws_need);
+      return fail(GDR_ERR_WORKSPACE, "workspace_bytes = %zu, %zu needed", workspace_bytes, ws_need);
   }
   if (d->gate == GDR_GATE_NONE && log_a) return fail(GDR_ERR_INVALID_ARG, "log_a must be NULL for GDR_GATE_NONE");
   if ((st = check_align("q", q, 16)) || (st = check_align("k", k, 16)) || (st = check_align("v", v, 16)) ||
@@ -347,9 +348,9 @@ gdr_status chunk_bwd_impl(const gdr_desc* d, const int32_t* cu, int64_t n_seq, c
       if (!req[i]) return fail(GDR_ERR_INVALID_ARG, "%s is NULL", names[i]);
     if (gated && !log_a) return fail(GDR_ERR_INVALID_ARG, "log_a is NULL but a gate is requested");
     if (gated && !dlog_a) return fail(GDR_ERR_INVALID_ARG, "dlog_a is NULL but a gate is requested");
-    if (!workspace) return fail(GDR_ERR_INVALID_ARG, "workspace is NULL (%zu bytes needed)", ws_need);
+    if (!workspace) return fail(GDR_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", ws_need);
     if (workspace_bytes < ws_need)
-      return fail(GDR_ERR_INVALID_ARG, "workspace_bytes = %zu, %zu needed", workspace_bytes, ws_need);
+      return fail(GDR_ERR_WORKSPACE, "workspace_bytes = %zu, %zu needed", workspace_bytes, ws_need);
   }
   if (!gated && log_a) return fail(GDR_ERR_INVALID_ARG, "log_a must be NULL for GDR_GATE_NONE");
   if (!gated && dlog_a) return fail(GDR_ERR_INVALID_ARG, "dlog_a must be NULL for GDR_GATE_NONE");

@@ -54,9 +54,9 @@ struct PrecondParams {
   int d_k, io;
   float eta;
 };
-// Backward of the chunk forward (bf16 I/O, no gate or a scalar gate, either form):
-// f carries the forward's inputs, the workspace records (f.ws) and,
-// for packed sequences, cu and nslots; o, S_T and order are unused.
+// Backward of the chunk forward (bf16 I/O, every gate -- a per-channel gate with
+// d_k = 128 --, either form): f carries the forward's inputs, the workspace records
+// (f.ws) and, for packed sequences, cu and nslots; o, S_T and order are unused.
 struct BwdParams {
   ChunkParams f;
   const void* dO;       // [B, T, H, d_v] gradient of the output
@@ -65,7 +65,7 @@ struct BwdParams {
   void* dk;             // [B, T, H, d_k]
   void* dv;             // [B, T, H, d_v]
   void* dbeta;          // [B, T, H]
-  void* dlog_a;         // [B, T, H] (scalar gate), else unused
+  void* dlog_a;         // [B, T, H] (scalar gate), [B, T, H, d_k] (per-channel gate), else unused
   float* dS0;           // [B, H, d_k, d_v], or null (not written)
   void* states;         // B H ceil(T/64) chunk-start states, bf16 [d_v][d_k] each
   void* dstates;        // the gradients of the chunk-end states, same layout

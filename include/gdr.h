@@ -52,7 +52,8 @@ typedef enum {
   GDR_ERR_INVALID_ARG = 1,   /* null pointer, bad size, bad enum, forbidden alias */
   GDR_ERR_UNSUPPORTED = 2,   /* valid but not implemented (d_k, d_v, chunk) */
   GDR_ERR_ALIGNMENT = 3,     /* pointer not aligned as required */
-  GDR_ERR_HIP = 4            /* the HIP runtime reported an error at launch */
+  GDR_ERR_WORKSPACE = 4,     /* workspace missing (NULL) or smaller than its size query returns */
+  GDR_ERR_HIP = 5            /* the HIP runtime reported an error at launch */
 } gdr_status;
 
 typedef enum { GDR_F32 = 0, GDR_BF16 = 1 } gdr_dtype;
@@ -117,7 +118,11 @@ gdr_status gdr_chunk_fwd_workspace_size(const gdr_desc* desc, size_t* bytes);
  *   v      [B, T, H, d_v]  io dtype
  *   beta   [B, T, H]       io dtype (any finite value; workloads use (0, 1))
  *   log_a  NULL for GDR_GATE_NONE; [B, T, H] (scalar) or [B, T, H, d_k]
- *          (channel), io dtype, finite (log of a decay in (0, 1] for workloads)
+ *          (channel), io dtype, finite (log of a decay in (0, 1] for workloads).
+ *          Any finite decay is handled: with a per-channel gate, a chunk in which
+ *          some channel decays by more than e^-64 within one 16-token block has its
+ *          triangular solve and score matrix formed by a slower generic kernel
+ *          (every decay one exponential), the rest by the split-factor transform.
  *   S0     [B, H, d_k, d_v] fp32, or NULL for a zero initial state
  *   o      [B, T, H, d_v]  io dtype, written (may be NULL only when T == 0)
  *   S_T    [B, H, d_k, d_v] fp32 final state, or NULL to skip it.  S_T may be
@@ -134,7 +139,9 @@ gdr_status gdr_chunk_fwd_workspace_size(const gdr_desc* desc, size_t* bytes);
  *
  * Two kernels run in order on `stream`: the per-chunk transform (cumulative
  * log-gate, the gated Gram blocks of the keys, (I + A)^{-1}, the masked score
- * matrix) for all chunks at once, then the sequential state pass with the output.
+ * matrix) for all chunks at once, then the sequential state pass with the output
+ * (with a per-channel gate a third one between them re-forms the chunks whose
+ * decay leaves the transform's range; it exits at once when there are none).
  *
  * T == 0 writes S_T = S0 (or zeros).  T need not be a multiple of the chunk.
  */
@@ -279,8 +286,10 @@ gdr_status gdr_precond_scan(const gdr_desc* desc, const void* k, const void* bet
  *
  * Writes to *bytes: the per-chunk records of the forward's workspace (see
  * gdr_chunk_fwd_workspace_size) plus two bf16 d_k x d_v matrices per (sequence,
- * head, chunk), that is B * H * ceil(T / 64) * (11776 + 4 * d_k * d_v) bytes (0 when
- * T == 0).  Returns gdr_chunk_bwd's descriptor errors; *bytes is 0 on error.
+ * head, chunk), that is B * H * ceil(T / 64) * (R + 4 * d_k * d_v) bytes with the
+ * bf16 record size R = 11776 (no gate, scalar gate) or 11776 + 384 * d_k
+ * (per-channel gate: the three decayed operands), 0 when T == 0.  Returns
+ * gdr_chunk_bwd's descriptor errors; *bytes is 0 on error.
  */
 gdr_status gdr_chunk_bwd_workspace_size(const gdr_desc* desc, size_t* bytes);
 
@@ -321,8 +330,10 @@ gdr_status gdr_chunk_bwd_workspace_size(const gdr_desc* desc, size_t* bytes);
  * Precision: bf16 products with fp32 accumulation, the carried state and state
  * gradient in fp32 (stored per chunk in bf16, the precision the products read
  * them in); reductions over tokens (dbeta, dlog_a) in fp32.  With a per-channel
- * gate the decay inside a chunk is split at 16-token blocks, so the gate must not
- * decay by more than e^-80 within 16 tokens of one channel (the forward's bound).
+ * gate the per-chunk gradient sums split each decay at 16-token blocks with one
+ * factor of up to 16 tokens' decay inverted, so the gate must not decay by more
+ * than e^-80 within 16 tokens of one channel (the forward has no such bound);
+ * past it that chunk's gradients are not finite.
  * T == 0 writes dS0 =
  * dS_T (or zeros).  Errors as for gdr_chunk_fwd; besides, one sequence's chunk
  * states must stay below 2^31 bytes (ceil(T / 64) * d_k * d_v * 2).
@@ -335,8 +346,9 @@ gdr_status gdr_chunk_bwd(const gdr_desc* desc, const void* q, const void* k, con
 /*
  * gdr_chunk_bwd_varlen_workspace_size -- scratch for gdr_chunk_bwd_varlen.
  *
- * The records of gdr_chunk_fwd_varlen (H * (ceil(T / 64) + n_seq) slots of 11776
- * bytes) plus two bf16 d_k x d_v matrices per slot (0 when T == 0).  Returns the
+ * The records of gdr_chunk_fwd_varlen (H * (ceil(T / 64) + n_seq) slots of R
+ * bytes, R as under gdr_chunk_bwd_workspace_size) plus two bf16 d_k x d_v matrices
+ * per slot (0 when T == 0).  Returns the
  * descriptor and n_seq errors of gdr_chunk_bwd_varlen; *bytes is 0 on error.
  */
 gdr_status gdr_chunk_bwd_varlen_workspace_size(const gdr_desc* desc, int64_t n_seq, size_t* bytes);

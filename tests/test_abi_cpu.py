@@ -14,7 +14,7 @@ from gated_delta_rule_21_amd._lib import GdrDesc
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gdr.h")
 
-OK, INVALID, UNSUPPORTED, ALIGN, HIP = range(5)
+OK, INVALID, UNSUPPORTED, ALIGN, WORKSPACE, HIP = range(6)
 FAKE = 0x10000          # a 16-byte aligned address that is never dereferenced
 
 
@@ -41,8 +41,9 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for s in range(5):
+    for s in range(6):
         assert lib.gdr_status_string(s).startswith(b"GDR_")
+    assert b"WORKSPACE" in lib.gdr_status_string(WORKSPACE)
     assert lib.gdr_version() >= 100
 
 
@@ -88,10 +89,11 @@ def test_workspace_size(lib):
 def test_workspace_checks(lib):
     p = _ptrs()
     p[8] = None
-    assert _chunk(lib, _desc(), p) == INVALID                  # missing workspace
+    assert _chunk(lib, _desc(), p) == WORKSPACE                # missing workspace
     assert b"workspace" in lib.gdr_last_error()
     need = _ws_size(lib, _desc())[1]
-    assert _chunk(lib, _desc(), _ptrs(), ws_bytes=need - 1) == INVALID
+    assert _chunk(lib, _desc(), _ptrs(), ws_bytes=need - 1) == WORKSPACE
+    assert b"needed" in lib.gdr_last_error()
     p = _ptrs()
     p[8] += 8
     assert _chunk(lib, _desc(), p) == ALIGN                    # workspace 16-byte alignment
@@ -210,7 +212,7 @@ def test_varlen_argument_checks(lib):
     assert _chunk_varlen(lib, _desc(), p[6] + 16, 2, p) == INVALID        # offsets inside o
     assert b"overlaps" in lib.gdr_last_error()
     need = _ws_varlen(lib, _desc(), 2)[1]
-    assert _chunk_varlen(lib, _desc(), cu, 2, _ptrs(), ws_bytes=need - 1) == INVALID
+    assert _chunk_varlen(lib, _desc(), cu, 2, _ptrs(), ws_bytes=need - 1) == WORKSPACE
 
 
 # ---- write key (the preconditioned delta rule) -------------------------------------------
@@ -313,9 +315,9 @@ def test_backward_argument_checks(lib):
             continue
         bad = list(p)
         bad[i] = None
-        assert _bwd(lib, d, bad) == INVALID, name
+        assert _bwd(lib, d, bad) == (WORKSPACE if name == "workspace" else INVALID), name
         assert name.encode() in lib.gdr_last_error()
-    assert _bwd(lib, d, p, ws_bytes=16) == INVALID                         # workspace too small
+    assert _bwd(lib, d, p, ws_bytes=16) == WORKSPACE                       # workspace too small
     assert _bwd(lib, _desc(gate=0), p) == INVALID                          # log_a given without a gate
     bad = list(p)
     bad[4] = None
@@ -360,3 +362,20 @@ def test_backward_varlen_checks(lib):
     bad = list(p)
     bad[9] = bad[15]                                                       # dk over the offsets table
     assert call(d, p[15], 5, bad) == INVALID
+
+
+def test_binding_rejects_strided_offsets(lib):
+    """The kernels read cu_seqlens as a dense int32 array: a strided view is refused by
+    both packed-sequence wrappers before anything reaches the library."""
+    import torch
+    T, H, d = 40, 2, 64
+    x = torch.zeros((1, T, H, d), dtype=torch.bfloat16)
+    beta = torch.zeros((1, T, H), dtype=torch.bfloat16)
+    cu = torch.tensor([0, 99, 10, 99, 40], dtype=torch.int32)[::2]
+    assert not cu.is_contiguous()
+    with pytest.raises(ValueError, match="contiguous"):
+        gdr.chunk_bwd(x, x, x, beta, None, None, x, cu_seqlens=cu)
+    with pytest.raises(ValueError, match="contiguous"):
+        gdr.chunk_fwd_varlen(x, x, x, beta, None, cu)
+    with pytest.raises(ValueError, match="GPU tensor"):          # a dense table passes this check
+        gdr.chunk_bwd(x, x, x, beta, None, None, x, cu_seqlens=cu.contiguous())

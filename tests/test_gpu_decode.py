@@ -71,6 +71,29 @@ def test_decode_workload_slice_1000_steps():
     _run(DECODE_CONFIG.replace(N=8))
 
 
-def test_decode_workload_all_sequences():
-    """All 256 sequences x 32 heads of the decode workload, first 8 steps."""
-    _run(DECODE_CONFIG.replace(steps=8))
+@pytest.mark.timeout(900)
+def test_decode_workload_all_sequences_100_steps():
+    """All 256 sequences x 32 heads of the decode workload, 100 carried steps; the
+    oracle runs every state (host processes in parallel): rel-L2 of o over all steps
+    and of the final state."""
+    need_gpu()
+    import torch
+    import gated_delta_rule_21_amd as gdr
+    from tests.parallel_oracle import whole_decode
+    wl = DECODE_CONFIG
+    steps = 100
+    say(f"decode workload {wl.name}: {steps} steps, generating inputs")
+    inp = decode_inputs(wl, steps=steps)
+    S = torch.from_numpy(inp["S0"]).cuda()
+    dq, dk, dvv, db, dla = (dev(inp[n], wl.io) for n in ("q", "k", "v", "beta", "log_a"))
+    del inp
+    o_all = torch.empty((steps, wl.N, wl.H, wl.d_v), dtype=torch.bfloat16, device="cuda")
+    for s in range(steps):
+        gdr.recurrent_step(dq[s], dk[s], dvv[s], db[s], dla[s], S, o=o_all[s])
+    torch.cuda.synchronize()
+    o_h, S_h = o_all.float().cpu().numpy(), S.cpu().numpy()
+    del o_all, S, dq, dk, dvv, db, dla
+    say("  oracle on every state")
+    r = whole_decode(wl, steps, o_h, S_h)
+    say(f"  rel_l2 o (all steps) {r['o']:.3e}  S (final) {r['S']:.3e}; {r['procs']} processes, {r['seconds']:.1f} s")
+    assert r["o"] <= TOL[wl.io] and r["S"] <= 1e-4
