@@ -19,10 +19,20 @@ tokens/s), and the backward of the chunk forward over the same workload
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
-Prints one JSON line.  `roofline` is for the chunk-forward kernel: algorithmic
+Every input is generated on the host and moved to the GPU before any leg is
+timed; the legs then run back to back, the headline chunk forward last, so that
+no leg starts on a GPU that has idled while the host generated inputs (its
+clocks take ~100 calls to come back up).  Besides the headline workload, the
+other three chunk-forward workloads are timed (`configs`: the fp32 DeltaNet
+B1 H1 T256 d64, the DeltaNet B4 H16 T4096 d128 with three copies of its inputs
+taken in turn so the repeats do not run from the 256 MB Infinity Cache, and
+the per-channel B2 H32 T32768 d128).
+
+Prints one JSON line.  `roofline` is for the chunk-forward call: algorithmic
 bytes per launch (inputs read once, outputs written once) over the average
 launch time measured with HIP events on the launch stream.  `cpu_baseline` is the
-fp64 oracle timed on one host core over a bounded sample of the same workload.
+fp64 oracle over the whole headline workload, its (b, h) slices split over up to
+16 host processes (one BLAS thread each), with a one-process figure beside it.
 """
 
 from __future__ import annotations
@@ -104,34 +114,61 @@ def profiled_traffic(name: str, sources):
 
 
 # ------------------------------------------------------------------ CPU baseline
-def cpu_baseline_child(T: int, heads: int, batches: int) -> None:
-    """Run the oracle on `batches` sequences x `heads` heads x T tokens of the gated workload."""
+def cpu_baseline_child(T: int, bs, hs) -> None:
+    """Run the oracle on the (b, h) slices zip(bs, hs), T tokens each, of the gated
+    workload (independent slices side by side as the heads of one sequence)."""
     import numpy as np
     from oracle import forward
     from workloads import CONFIGS, slice_inputs
     wl = CONFIGS[3]
-    sl = [[slice_inputs(wl, b, h, T) for h in range(heads)] for b in range(batches)]
-    st = lambda n: np.stack([np.stack([s[n] for s in row], axis=1) for row in sl], axis=0)
-    args = [st(n) for n in ("q", "k", "v", "beta", "log_a")]
+    sl = [slice_inputs(wl, b, h, T) for b, h in zip(bs, hs)]
+    args = [np.stack([s[n] for s in sl], axis=1)[None] for n in ("q", "k", "v", "beta", "log_a")]
     del sl
     t0 = time.perf_counter()
     forward(*args, None)
     dt = time.perf_counter() - t0
-    print(json.dumps({"seconds": dt, "T": T, "heads": heads, "batches": batches}))
+    print(json.dumps({"seconds": dt, "T": T, "slices": len(bs)}))
 
 
-def cpu_baseline(T: int, heads: int, batches: int, H_total: int):
+def host_cores() -> int:
+    """Host cores for the oracle: those this process may run on, at most 16 (a GPU's share)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def cpu_baseline(T: int, log):
+    """The oracle over every (b, h) slice of the headline workload (T tokens each), the
+    slices dealt to P = host_cores() processes run side by side; tokens/s = B T over
+    the slowest process's oracle time.  Then one process alone on one of those groups."""
+    from workloads import CONFIGS
+    wl = CONFIGS[3]
+    P = host_cores()
     env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1")
-    out = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-baseline-child",
-                          "--cpu-T", str(T), "--cpu-heads", str(heads), "--cpu-batches", str(batches)],
-                         capture_output=True, text=True, env=env, check=True)
-    r = json.loads(out.stdout.strip().splitlines()[-1])
-    head_tok_s = r["batches"] * r["heads"] * r["T"] / r["seconds"]
-    return {"value": head_tok_s / H_total, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": (f"fp64 token-by-token oracle (NumPy, one thread) on {batches} sequences x {heads} of "
-                       f"{H_total} heads x {T} tokens of the gated workload, S0 = 0; {r['seconds']:.1f} s; "
-                       "tokens/s = head-tokens/s / H"),
-            "seconds": round(r["seconds"], 2)}
+    slices = [(b, h) for b in range(wl.B) for h in range(wl.H)]
+    groups = [slices[i::P] for i in range(P)]
+    cmd = lambda g: [sys.executable, os.path.abspath(__file__), "--cpu-baseline-child", "--cpu-T", str(T),
+                     "--cpu-b", ",".join(str(b) for b, _ in g), "--cpu-h", ",".join(str(h) for _, h in g)]
+    log(f"CPU oracle: {len(slices)} slices x {T} tokens over {P} processes")
+    t0 = time.perf_counter()
+    procs = [subprocess.Popen(cmd(g), stdout=subprocess.PIPE, text=True, env=env) for g in groups if g]
+    outs = [p.communicate()[0] for p in procs]
+    wall = time.perf_counter() - t0
+    if any(p.returncode != 0 for p in procs):
+        raise RuntimeError("a CPU oracle process failed")
+    secs = [sum(json.loads(l)["seconds"] for l in o.strip().splitlines()) for o in outs]
+    value = wl.B * T / max(secs)
+    log(f"CPU oracle: {max(secs):.1f} s over {len(procs)} processes; one process alone next")
+    one = subprocess.run(cmd(groups[0]), capture_output=True, text=True, env=env, check=True)
+    s1 = sum(json.loads(l)["seconds"] for l in one.stdout.strip().splitlines())
+    per_slice_tok_s = len(groups[0]) * T / s1          # head-tokens per second on one core
+    return {"value": round(value, 1), "unit": "tokens/s", "cores": len(procs), "kind": "oracle",
+            "sample": (f"fp64 token-by-token oracle (NumPy, one BLAS thread per process) on all {len(slices)} "
+                       f"(sequence, head) slices x {T} tokens of the gated workload, S0 = 0, dealt to "
+                       f"{len(procs)} processes side by side; tokens/s = B*T / slowest process's oracle time "
+                       f"({max(secs):.1f} s; wall {wall:.1f} s with input generation)"),
+            "seconds": round(max(secs), 2),
+            "single_core": {"value": round(per_slice_tok_s / wl.H, 1), "unit": "tokens/s", "cores": 1,
+                            "sample": f"one process on {len(groups[0])} slices x {T} tokens ({s1:.1f} s); "
+                                      "tokens/s = head-tokens/s / H"}}
 
 
 def copy_calibration(log, nbytes: int = 1 << 30, reps: int = 3):
@@ -150,79 +187,105 @@ def copy_calibration(log, nbytes: int = 1 << 30, reps: int = 3):
 
 
 # ------------------------------------------------------------------ GPU legs
-def bench_chunk(args, log):
+def time_calls(fn, warmup: int, steps: int) -> float:
+    """ms per call of fn() over `steps` calls after `warmup` untimed ones, from HIP
+    events recorded on the current stream (the stream the library launches on)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(steps):
+        fn(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / steps
+
+
+def chunk_traffic_profile(wl):
+    """Name of the committed HBM counter summary of a chunk-forward workload."""
+    return {"gated_deltanet_scalar_b8h16t8192d128_bf16": "chunk_fwd_gated_b8h16t8192d128_counters.md",
+            "deltanet_b4h16t4096d128_bf16": "chunk_fwd_deltanet_b4h16t4096d128_counters.md",
+            "kda_channel_b2h32t32768d128_bf16": "chunk_fwd_channel_b2h32t32768d128_counters.md"}.get(wl.name)
+
+
+def prepare_chunk(cfg: int, copies: int, log):
+    """Device-resident inputs, outputs and workspace of a chunk-forward workload
+    (`copies` sets of inputs and outputs, taken in turn)."""
     import torch
     import gated_delta_rule_21_amd as gdr
     from workloads import CONFIGS, chunk_inputs
-    wl = CONFIGS[args.chunk_config]
+    wl = CONFIGS[cfg]
     log(f"generating {wl.name}")
     inp = chunk_inputs(wl)
-    dev = lambda x: None if x is None else torch.from_numpy(x).to(torch.bfloat16).cuda()
-    q, k, v, beta, log_a = (dev(inp[n]) for n in ("q", "k", "v", "beta", "log_a"))
+    dt = torch.bfloat16 if wl.io == "bf16" else torch.float32
+    dev = lambda x: None if x is None else torch.from_numpy(x).to(dt).cuda()
     with_S0 = wl.s0_std > 0
-    S0 = torch.from_numpy(inp["S0"]).cuda() if with_S0 else None
+    sets = []
+    for _ in range(copies):
+        sets.append(dict(args=[dev(inp[n]) for n in ("q", "k", "v", "beta", "log_a")],
+                         S0=torch.from_numpy(inp["S0"]).cuda() if with_S0 else None,
+                         o=torch.empty((wl.B, wl.T, wl.H, wl.d_v), dtype=dt, device="cuda"),
+                         S_T=torch.empty((wl.B, wl.H, wl.d_k, wl.d_v), dtype=torch.float32, device="cuda")))
     del inp
-    o = torch.empty((wl.B, wl.T, wl.H, wl.d_v), dtype=torch.bfloat16, device="cuda")
-    S_T = torch.empty((wl.B, wl.H, wl.d_k, wl.d_v), dtype=torch.float32, device="cuda")
-    ws = torch.empty(gdr.chunk_workspace_size(wl.B, wl.T, wl.H, wl.d_k, wl.d_v, torch.bfloat16, wl.gate),
+    ws = torch.empty(gdr.chunk_workspace_size(wl.B, wl.T, wl.H, wl.d_k, wl.d_v, dt, wl.gate),
                      dtype=torch.uint8, device="cuda")
-    stream = torch.cuda.current_stream()
-
-    def step():
-        gdr.chunk_fwd(q, k, v, beta, log_a, S0, o=o, S_T=S_T, workspace=ws)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = ev0.elapsed_time(ev1) / args.steps
-    log(f"chunk forward: {ms:.3f} ms/step (wall {1e3 * wall / args.steps:.3f} ms/step)")
-    nbytes, flops = chunk_algorithmic(wl, with_S0=with_S0)
-    return wl, ms, nbytes, flops, (q, k, v, beta, log_a, S0)
+    return dict(wl=wl, sets=sets, ws=ws, with_S0=with_S0)
 
 
-def bench_decode(args, log):
-    import torch
+def bench_chunk(prep, warmup: int, steps: int, log, label: str):
+    """Time gdr_chunk_fwd on a prepared workload; returns its record."""
     import gated_delta_rule_21_amd as gdr
+    wl, sets, ws = prep["wl"], prep["sets"], prep["ws"]
+
+    def call(i):
+        st = sets[i % len(sets)]
+        gdr.chunk_fwd(*st["args"], st["S0"], o=st["o"], S_T=st["S_T"], workspace=ws)
+
+    ms = time_calls(call, warmup, steps)
+    nbytes, flops = chunk_algorithmic(wl, with_S0=prep["with_S0"])
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    tf = flops / (ms * 1e-3) / 1e12
+    log(f"{label} {wl.name}: {ms:.4f} ms/call, {gbs:.0f} GB/s, {tf:.1f} TFLOP/s useful")
+    prof = chunk_traffic_profile(wl)
+    return {"workload": wl.name, "ms_per_call": round(ms, 4), "tokens_per_s": round(wl.B * wl.T / (ms * 1e-3), 1),
+            "tflops_useful": round(tf, 2), "mfma_frac_useful": round(tf / BF16_PEAK_TFLOPS, 4),
+            "warmup": warmup, "steps": steps, "input_copies": len(sets),
+            "algorithmic_bytes_per_launch": nbytes, "useful_flops_per_launch": flops,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": profiled_traffic(prof, CHUNK_SOURCES) if prof else None}}
+
+
+def prepare_decode(log, n_sets: int = 16):
+    import torch
     from workloads import DECODE_CONFIG, decode_inputs
     wl = DECODE_CONFIG
-    n_sets = 16
     log(f"generating {wl.name} ({n_sets} token sets, reused cyclically)")
     inp = decode_inputs(wl, steps=n_sets)
     dev = lambda x: torch.from_numpy(x).to(torch.bfloat16).cuda()
-    q, k, v, beta, log_a = (dev(inp[n]) for n in ("q", "k", "v", "beta", "log_a"))
-    S = torch.from_numpy(inp["S0"]).cuda()
-    o = torch.empty((wl.N, wl.H, wl.d_v), dtype=torch.bfloat16, device="cuda")
-    stream = torch.cuda.current_stream()
+    return dict(wl=wl, n_sets=n_sets, tok=[dev(inp[n]) for n in ("q", "k", "v", "beta", "log_a")],
+                S=torch.from_numpy(inp["S0"]).cuda(),
+                o=torch.empty((wl.N, wl.H, wl.d_v), dtype=torch.bfloat16, device="cuda"))
+
+
+def bench_decode(prep, args, log):
+    import gated_delta_rule_21_amd as gdr
+    wl, n_sets, (q, k, v, beta, log_a), S, o = prep["wl"], prep["n_sets"], prep["tok"], prep["S"], prep["o"]
 
     def step(s):
         j = s % n_sets
         gdr.recurrent_step(q[j], k[j], v[j], beta[j], log_a[j], S, o=o)
 
-    # A decode step is ~10 us: warm up over as many steps as are timed, so the
-    # clocks are at their steady state however small --warmup is.
-    for s in range(max(args.warmup, args.decode_steps)):
-        step(s)
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for s in range(args.decode_steps):
-        step(s)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / args.decode_steps
+    warmup = max(args.warmup, 100)
+    ms = time_calls(step, warmup, args.decode_steps)
     nbytes = decode_bytes(wl)
     gbs = nbytes / (ms * 1e-3) / 1e9
     log(f"decode: {ms * 1e3:.1f} us/step, {gbs:.0f} GB/s")
     return {"value": round(gbs, 1), "unit": "GB/s", "us_per_step": round(ms * 1e3, 2),
-            "tokens_per_s": round(wl.N / (ms * 1e-3), 1), "steps": args.decode_steps,
+            "tokens_per_s": round(wl.N / (ms * 1e-3), 1), "steps": args.decode_steps, "warmup_steps": warmup,
             "workload": wl.name, "bytes_per_step": nbytes,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4),
@@ -236,32 +299,23 @@ def precond_bytes(B: int, T: int, H: int, d_k: int, esz: int, apf: bool) -> int:
     return ntok * (2 * d_k * esz + esz * (2 if apf else 1)) + 2 * B * H * d_k * 4
 
 
-def bench_precond(args, log, wl, k, beta):
+def prepare_precond(wl, log):
+    import torch
+    from workloads import precond_factors
+    log("generating the scan's retention and starting preconditioner")
+    f = precond_factors(wl)
+    return dict(r=torch.from_numpy(f["r"]).to(torch.bfloat16).cuda(), d0=torch.from_numpy(f["d0"]).cuda())
+
+
+def bench_precond(prep, args, log, wl, k, beta):
     """The preconditioner scan (with forgetting) over the keys of the chunk workload."""
     import torch
     import gated_delta_rule_21_amd as gdr
-    from workloads import PRECOND_ETA, precond_factors
-    log("generating the scan's retention and starting preconditioner")
-    f = precond_factors(wl)
-    r = torch.from_numpy(f["r"]).to(torch.bfloat16).cuda()
-    d0 = torch.from_numpy(f["d0"]).cuda()
+    from workloads import PRECOND_ETA
+    r, d0 = prep["r"], prep["d0"]
     kw = torch.empty_like(k)
     dT = torch.empty_like(d0)
-    stream = torch.cuda.current_stream()
-
-    def step():
-        gdr.precond_scan(k, beta, PRECOND_ETA, r, d0, kw=kw, d_T=dT)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / args.steps
+    ms = time_calls(lambda i: gdr.precond_scan(k, beta, PRECOND_ETA, r, d0, kw=kw, d_T=dT), args.warmup, args.steps)
     nbytes = precond_bytes(wl.B, wl.T, wl.H, wl.d_k, 2, True)
     gbs = nbytes / (ms * 1e-3) / 1e9
     log(f"preconditioner scan: {ms * 1e3:.1f} us, {gbs:.0f} GB/s")
@@ -298,41 +352,29 @@ def bwd_algorithmic(wl):
     return wl.B * wl.H * ((wl.T + C - 1) // C) * per_chunk
 
 
-def bench_bwd(args, log, wl, q, k, v, beta, log_a, S0, fwd_ms):
-    """The backward of the chunk forward over the same workload, with dO ~ N(0, 1)
-    and dS_T ~ N(0, 1); the gradients of every input and of S0."""
+def prepare_bwd(wl, log):
     import torch
     import gated_delta_rule_21_amd as gdr
     from workloads import grad_inputs
     log("generating the output gradients")
     g = grad_inputs(wl)
-    dO = torch.from_numpy(g["dO"]).to(torch.bfloat16).cuda()
-    dS_T = torch.from_numpy(g["dS_T"]).cuda()
-    del g
-    ws = torch.empty(gdr.chunk_bwd_workspace_size(wl.B, wl.T, wl.H, wl.d_k, wl.d_v, torch.bfloat16, wl.gate),
-                     dtype=torch.uint8, device="cuda")
-    stream = torch.cuda.current_stream()
+    return dict(dO=torch.from_numpy(g["dO"]).to(torch.bfloat16).cuda(), dS_T=torch.from_numpy(g["dS_T"]).cuda(),
+                ws=torch.empty(gdr.chunk_bwd_workspace_size(wl.B, wl.T, wl.H, wl.d_k, wl.d_v, torch.bfloat16,
+                                                            wl.gate), dtype=torch.uint8, device="cuda"))
 
-    def step():
-        return gdr.chunk_bwd(q, k, v, beta, log_a, S0, dO, dS_T, workspace=ws)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / args.steps
+def bench_bwd(prep, args, log, wl, q, k, v, beta, log_a, S0):
+    """The backward of the chunk forward over the same workload, with dO ~ N(0, 1)
+    and dS_T ~ N(0, 1); the gradients of every input and of S0."""
+    import gated_delta_rule_21_amd as gdr
+    dO, dS_T, ws = prep["dO"], prep["dS_T"], prep["ws"]
+    ms = time_calls(lambda i: gdr.chunk_bwd(q, k, v, beta, log_a, S0, dO, dS_T, workspace=ws), args.warmup,
+                    args.steps)
     flops = bwd_algorithmic(wl)
     tf = flops / (ms * 1e-3) / 1e12
     log(f"chunk backward: {ms:.3f} ms/step, {tf:.1f} TFLOP/s useful")
     return {"workload": wl.name + "_backward", "value": round(wl.B * wl.T / (ms * 1e-3), 1), "unit": "tokens/s",
             "ms_per_launch": round(ms, 4), "useful_flops_per_launch": flops,
-            "train_step_tokens_per_s": round(wl.B * wl.T / ((ms + fwd_ms) * 1e-3), 1),
-            "train_step_ms": round(ms + fwd_ms, 4),
             "algorithmic_bytes_per_launch": bwd_bytes(wl, S0 is not None),
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf / BF16_PEAK_TFLOPS, 4),
@@ -349,21 +391,8 @@ def bench_wkey(args, log, wl, q, k, v, beta, kw, scan_us):
     S_T = torch.empty((wl.B, wl.H, wl.d_k, wl.d_v), dtype=torch.float32, device="cuda")
     ws = torch.empty(gdr.chunk_workspace_size(wl.B, wl.T, wl.H, wl.d_k, wl.d_v, torch.bfloat16, "none"),
                      dtype=torch.uint8, device="cuda")
-    stream = torch.cuda.current_stream()
-
-    def step():
-        gdr.chunk_fwd(q, k, v, beta, None, None, o=o, S_T=S_T, workspace=ws, kw=kw)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / args.steps
+    ms = time_calls(lambda i: gdr.chunk_fwd(q, k, v, beta, None, None, o=o, S_T=S_T, workspace=ws, kw=kw),
+                    args.warmup, args.steps)
     nbytes, _ = chunk_algorithmic(wl.replace(gate="none"), with_S0=False)
     nbytes += wl.B * wl.T * wl.H * wl.d_k * 2          # the write keys
     gbs = nbytes / (ms * 1e-3) / 1e9
@@ -384,9 +413,7 @@ def handoff_lengths(n_seq: int = 32, lo: int = 128, hi: int = 8192, seed: int = 
     return [int(round(x)) for x in np.exp(rs.uniform(np.log(lo), np.log(hi), size=n_seq))]
 
 
-def bench_handoff(args, log):
-    """Packed prefill of a batch of prompts of mixed lengths, then decode steps on the
-    states it hands over (the serving steps on either side of the chunk forward)."""
+def prepare_handoff(log, n_sets: int = 16):
     import numpy as np
     import torch
     import gated_delta_rule_21_amd as gdr
@@ -396,19 +423,30 @@ def bench_handoff(args, log):
     log(f"generating the handoff mix ({N} prompts, {total} tokens)")
     inp = chunk_inputs(Workload("handoff_prefill", B=1, T=total, H=H, d_k=dk, d_v=dv, io="bf16", gate="scalar",
                                 s0_std=0.0, seed=6))
-    n_sets = 16
     tok = chunk_inputs(Workload("handoff_tokens", B=N, T=n_sets, H=H, d_k=dk, d_v=dv, io="bf16", gate="scalar",
                                 s0_std=0.0, seed=7))
     dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).cuda()
-    q, k, v, beta, log_a = (dev(inp[n]) for n in ("q", "k", "v", "beta", "log_a"))
-    tq, tk, tv, tb, tl = ([dev(tok[n][:, j]) for j in range(n_sets)] for n in ("q", "k", "v", "beta", "log_a"))
-    del inp, tok
-    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device="cuda")
-    o = torch.empty((1, total, H, dv), dtype=torch.bfloat16, device="cuda")
-    S = torch.empty((N, H, dk, dv), dtype=torch.float32, device="cuda")
-    od = torch.empty((N, H, dv), dtype=torch.bfloat16, device="cuda")
-    ws = torch.empty(gdr.chunk_varlen_workspace_size(total, N, H, dk, dv, torch.bfloat16, "scalar"),
-                     dtype=torch.uint8, device="cuda")
+    return dict(lens=lens, N=N, H=H, dk=dk, dv=dv, total=total, n_sets=n_sets,
+                args=[dev(inp[n]) for n in ("q", "k", "v", "beta", "log_a")],
+                tok=[[dev(tok[n][:, j]) for j in range(n_sets)] for n in ("q", "k", "v", "beta", "log_a")],
+                cu=torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device="cuda"),
+                o=torch.empty((1, total, H, dv), dtype=torch.bfloat16, device="cuda"),
+                S=torch.empty((N, H, dk, dv), dtype=torch.float32, device="cuda"),
+                od=torch.empty((N, H, dv), dtype=torch.bfloat16, device="cuda"),
+                ws=torch.empty(gdr.chunk_varlen_workspace_size(total, N, H, dk, dv, torch.bfloat16, "scalar"),
+                               dtype=torch.uint8, device="cuda"))
+
+
+def bench_handoff(prep, log):
+    """Packed prefill of a batch of prompts of mixed lengths, then decode steps on the
+    states it hands over (the serving steps on either side of the chunk forward)."""
+    import torch
+    import gated_delta_rule_21_amd as gdr
+    P = prep
+    N, H, dk, dv, total, n_sets, lens = P["N"], P["H"], P["dk"], P["dv"], P["total"], P["n_sets"], P["lens"]
+    q, k, v, beta, log_a = P["args"]
+    tq, tk, tv, tb, tl = P["tok"]
+    cu, o, S, od, ws = P["cu"], P["o"], P["S"], P["od"], P["ws"]
     stream = torch.cuda.current_stream()
     prefill = lambda: gdr.chunk_fwd_varlen(q, k, v, beta, log_a, cu, None, o=o, S_T=S, workspace=ws)
     decode = lambda j: gdr.recurrent_step(tq[j % n_sets], tk[j % n_sets], tv[j % n_sets], tb[j % n_sets],
@@ -448,13 +486,11 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    # The GPU's clocks ramp up over its first ~100 steps after an idle spell (the
-    # input generation between legs): a chunk forward step measures 457 us after 3
-    # warmup steps, 393 us after 30 and 365-367 us after 100 or more.
-    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--decode-steps", type=int, default=1000)
-    ap.add_argument("--chunk-config", type=int, default=3, choices=(2, 3, 4),
-                    help="chunk-forward workload (3 = the gated workload of the headline metric)")
+    ap.add_argument("--chunk-config", type=int, default=3, choices=(1, 2, 3, 4),
+                    help="headline chunk-forward workload (3 = the gated workload of the headline metric)")
+    ap.add_argument("--no-configs", action="store_true", help="skip the other chunk-forward workloads")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-handoff", action="store_true",
                     help="skip the packed-prefill -> decode handoff leg")
@@ -462,16 +498,17 @@ def main():
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-T", type=int, default=8192)
-    ap.add_argument("--cpu-heads", type=int, default=16)
-    ap.add_argument("--cpu-batches", type=int, default=4)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB streaming copy first (for scaling HBM byte counters)")
     ap.add_argument("--cpu-baseline-child", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--cpu-b", default="", help=argparse.SUPPRESS)
+    ap.add_argument("--cpu-h", default="", help=argparse.SUPPRESS)
     ap.add_argument("--quiet", action="store_true")
     args = ap.parse_args()
 
     if args.cpu_baseline_child:
-        cpu_baseline_child(args.cpu_T, args.cpu_heads, args.cpu_batches)
+        cpu_baseline_child(args.cpu_T, [int(x) for x in args.cpu_b.split(",")],
+                           [int(x) for x in args.cpu_h.split(",")])
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -486,52 +523,69 @@ def main():
         sys.exit(1)
     import gated_delta_rule_21_amd as gdr
     gdr.load()
+
+    # ---- every input to the GPU first ----
+    head = prepare_chunk(args.chunk_config, 1, log)
+    wl = head["wl"]
+    others = {} if args.no_configs else {c: prepare_chunk(c, 1 if c == 4 else 3, log)
+                                         for c in (1, 2, 3, 4) if c != args.chunk_config}
+    dec_prep = None if args.no_decode else prepare_decode(log)
+    hand_prep = None if args.no_handoff else prepare_handoff(log)
+    gated_bf16 = wl.io == "bf16" and wl.gate != "channel"
+    pre_prep = None if args.no_precond or wl.io != "bf16" else prepare_precond(wl, log)
+    bwd_prep = None if args.no_bwd or wl.io != "bf16" else prepare_bwd(wl, log)
+    torch.cuda.synchronize()
     if args.copy_calibration:
         copy_calibration(log)
 
-    wl, ms, nbytes, flops, (q, k, v, beta, log_a, S0) = bench_chunk(args, log)
-    tok_s = wl.B * wl.T / (ms * 1e-3)
-    gbs = nbytes / (ms * 1e-3) / 1e9
-    tflops = flops / (ms * 1e-3) / 1e12
-    decode = None if args.no_decode else bench_decode(args, log)
-    handoff = None if args.no_handoff else bench_handoff(args, log)
+    # ---- legs back to back; the headline forward last ----
+    configs = {str(c): bench_chunk(p, args.warmup, args.steps, log, f"config {c}") for c, p in sorted(others.items())}
+    for p in others.values():
+        p.clear()
+    decode = None if dec_prep is None else bench_decode(dec_prep, args, log)
+    handoff = None if hand_prep is None else bench_handoff(hand_prep, log)
+    q, k, v, beta, log_a = head["sets"][0]["args"]
+    S0 = head["sets"][0]["S0"]
     precond = osdn = None
-    if not args.no_precond:
-        kw, precond = bench_precond(args, log, wl, k, beta)
-        osdn = bench_wkey(args, log, wl, q, k, v, beta, kw, precond["us_per_launch"])
+    if pre_prep is not None:
+        kw, precond = bench_precond(pre_prep, args, log, wl, k, beta)
+        if gated_bf16:
+            osdn = bench_wkey(args, log, wl, q, k, v, beta, kw, precond["us_per_launch"])
         del kw
-    bwd = None if args.no_bwd else bench_bwd(args, log, wl, q, k, v, beta, log_a, S0, ms)
-    del q, k, v, beta, log_a, S0
+    bwd = None if bwd_prep is None else bench_bwd(bwd_prep, args, log, wl, q, k, v, beta, log_a, S0)
+    rec = bench_chunk(head, args.warmup, args.steps, log, "headline")
+    ms = rec["ms_per_call"]
+    if bwd is not None:
+        bwd["train_step_ms"] = round(ms + bwd["ms_per_launch"], 4)
+        bwd["train_step_tokens_per_s"] = round(wl.B * wl.T / ((ms + bwd["ms_per_launch"]) * 1e-3), 1)
+    del q, k, v, beta, log_a, S0, head
     cpu = None
     if not args.no_cpu_baseline:
-        log("timing the CPU oracle sample")
-        cpu = cpu_baseline(args.cpu_T, args.cpu_heads, args.cpu_batches, wl.H)
+        cpu = cpu_baseline(args.cpu_T, log)
 
     line = {
         "metric": "tokens/s + % MFMA peak, gated delta-rule chunk fwd T=8192 d=128; decode GB/s",
-        "value": round(tok_s, 1),
+        "value": rec["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
+        "ms_per_step": ms,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": wl.io,
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "H": wl.H, "d_k": wl.d_k, "d_v": wl.d_v,
                    "chunk": wl.chunk, "gate": wl.gate, "io": wl.io, "state": "fp32",
                    "S0": "N(0, %g^2)" % wl.s0_std if wl.s0_std > 0 else "zero",
                    "global_batch": wl.B, "seq_len": wl.T, "parallelism": "none (1 GPU)"},
-        "tflops_useful": round(tflops, 2),
-        "mfma_frac_useful": round(tflops / BF16_PEAK_TFLOPS, 4),
-        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "traffic": (profiled_traffic("chunk_fwd_gated_b8h16t8192d128_counters.md", CHUNK_SOURCES)
-                                 if args.chunk_config == 3 else None)},
-        "algorithmic_bytes_per_launch": nbytes,
-        "useful_flops_per_launch": flops,
+        "tflops_useful": rec["tflops_useful"],
+        "mfma_frac_useful": rec["mfma_frac_useful"],
+        "roofline": rec["roofline"],
+        "algorithmic_bytes_per_launch": rec["algorithmic_bytes_per_launch"],
+        "useful_flops_per_launch": rec["useful_flops_per_launch"],
+        "configs": configs,
         "decode": decode,
         "handoff": handoff,
         "precond_scan": precond,
