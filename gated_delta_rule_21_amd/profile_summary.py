@@ -128,6 +128,65 @@ def counters(fetch_csv: str, write_csv: str, kernels: str, algorithmic: float, c
     return "\n".join(out)
 
 
+def sq(paths, command: str, digest: str, title: str, useful_flops: float = 0.0) -> str:
+    """Per-kernel means of SQ / GRBM counter passes (counter_collection.csv, one pass
+    per file; the first dispatch of each kernel dropped as warm-up when there are
+    more than two), per dispatch and per wave, with the MFMA-busy fraction of the
+    kernel's time: SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE / 8 (cycles per XCD)
+    times 1024 SIMDs."""
+    rows, meta = {}, {}
+    for path in paths:
+        for r in csv.DictReader(open(path)):
+            k = short_name(r["Kernel_Name"]).replace("gdr::", "")
+            if CAL_KERNEL in k:
+                continue
+            rows.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(
+                (int(r["Dispatch_Id"]), float(r["Counter_Value"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+            meta[k] = (int(r["Grid_Size"]), int(r["Workgroup_Size"]), r["LDS_Block_Size"])
+    out = [f"# {title}", "", "commands (one counter pass per run):", "", "```", command, "```", ""]
+    busy_all = cyc_all = insts_all = 0.0
+    for k, cs in rows.items():
+        grid, wg, lds = meta[k]
+        waves = grid // 64
+        out += [f"## `{k}`", "", f"grid {grid} threads ({waves} waves), workgroup {wg}, LDS {lds} B", "",
+                "| counter | per dispatch | per wave |", "|---|---|---|"]
+        mean = {}
+        dur = []
+        for c, vals in sorted(cs.items()):
+            vals = sorted(vals)[1:] if len(vals) > 2 else vals
+            mean[c] = statistics.mean(v for _, v, _ in vals)
+            dur += [t for _, _, t in vals]
+            out.append(f"| {c} | {mean[c]:.5g} | {mean[c] / waves:.5g} |")
+        out.append("")
+        if "GRBM_GUI_ACTIVE" in mean:
+            cyc = mean["GRBM_GUI_ACTIVE"] / 8
+            out.append(f"- kernel time {statistics.mean(dur) / 1e3:.1f} us (profiled), {cyc:.4g} cycles per XCD, "
+                       f"{cyc / statistics.mean(dur):.3f} GHz")
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
+                f = mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * 1024)
+                busy_all += mean["SQ_VALU_MFMA_BUSY_CYCLES"]
+                cyc_all += cyc
+                out.append(f"- MFMA busy: {f:.4f} of the kernel's SIMD cycles")
+            if "SQ_INSTS_MFMA" in mean:
+                insts_all += mean["SQ_INSTS_MFMA"]
+        if "SQ_LDS_IDX_ACTIVE" in mean and "SQ_LDS_BANK_CONFLICT" in mean:
+            out.append(f"- LDS bank conflicts: {mean['SQ_LDS_BANK_CONFLICT'] / mean['SQ_LDS_IDX_ACTIVE']:.3f} of "
+                       "LDS-active cycles")
+        if "SQ_WAIT_ANY" in mean and "SQ_WAVE_CYCLES" in mean:
+            out.append(f"- waves waiting (SQ_WAIT_ANY / SQ_WAVE_CYCLES): {mean['SQ_WAIT_ANY'] / mean['SQ_WAVE_CYCLES']:.3f}"
+                       f"; on LDS issue (SQ_WAIT_INST_LDS): {mean.get('SQ_WAIT_INST_LDS', 0) / mean['SQ_WAVE_CYCLES']:.3f}")
+        out.append("")
+    if cyc_all:
+        out.append(f"All kernels of one call: MFMA busy {busy_all / (cyc_all * 1024):.4f} of their SIMD cycles.")
+    if useful_flops and insts_all:
+        issued = insts_all * 16384
+        out.append(f"MFMA instructions per call {insts_all:.4g} (16x16x32 bf16, 16384 flop each): {issued:.4g} flop "
+                   f"issued against {useful_flops:.4g} useful ({issued / useful_flops:.3f}x: zero-padded k = 16 steps, "
+                   "full 16x16 tiles of triangular blocks).")
+    out += ["", f"kernel_source_sha256_16: {digest}", ""]
+    return "\n".join(out)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -141,11 +200,22 @@ def main(argv=None):
     b.add_argument("--kernel", required=True, help="name substring, or several separated by ';' (or ',')")
     b.add_argument("--algorithmic-bytes", type=float, required=True)
     b.add_argument("--command", required=True)
+    b.add_argument("--digest", default="", help="source digest to record (default: the current sources')")
+    c = sub.add_parser("sq")
+    c.add_argument("csv", nargs="+")
+    c.add_argument("--command", required=True)
+    c.add_argument("--title", required=True)
+    c.add_argument("--digest", default="")
+    c.add_argument("--useful-flops", type=float, default=0.0)
     args = ap.parse_args(argv)
+    if args.cmd == "sq":
+        sys.stdout.write(sq(args.csv, args.command, args.digest or kernel_source_digest(), args.title,
+                            args.useful_flops))
+        return
     if args.cmd == "stats":
         sys.stdout.write(stats(args.csv, args.command, args.top))
     else:
-        digest = (decode_source_digest() if "decode" in args.kernel else
+        digest = args.digest or (decode_source_digest() if "decode" in args.kernel else
                   precond_source_digest() if "precond" in args.kernel else
                   bwd_source_digest() if "bwd" in args.kernel else kernel_source_digest())
         sys.stdout.write(counters(args.fetch_csv, args.write_csv, args.kernel, args.algorithmic_bytes,
