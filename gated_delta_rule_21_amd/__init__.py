@@ -3,6 +3,8 @@
 Public calls (thin wrappers over the C ABI in include/gdr.h):
     chunk_fwd(q, k, v, beta, log_a=None, S0=None, form="page")        -> (o, S_T)
     chunk_fwd_varlen(q, k, v, beta, log_a, cu_seqlens, S0=None)        -> (o, S_T), sequences packed along T
+    chunk_fwd_noalloc(q, k, v, beta, log_a=None, S0=None)             -> (o, S_T), scratch in a static
+                                                                          device array (no workspace)
     recurrent_step(q, k, v, beta, log_a, S, form="page")               -> (o, S_new)
     precond_scan(k, beta, eta, r=None, d0=None)                        -> (kw, d_T), the write keys
                                                                           of the preconditioned rule
@@ -16,9 +18,9 @@ Public calls (thin wrappers over the C ABI in include/gdr.h):
 """
 
 from ._lib import (EXPORTED, GdrError, LIB_PATH, chunk_attn, chunk_bwd, chunk_bwd_workspace_size, chunk_fwd,
-                   chunk_fwd_varlen, chunk_varlen_workspace_size, chunk_workspace_size, load, precond_scan,
+                   chunk_fwd_noalloc, chunk_fwd_varlen, chunk_varlen_workspace_size, chunk_workspace_size, load, precond_scan,
                    recurrent_step)
 
 __all__ = ["EXPORTED", "GdrError", "LIB_PATH", "chunk_attn", "chunk_bwd", "chunk_bwd_workspace_size", "chunk_fwd",
-           "chunk_fwd_varlen", "chunk_varlen_workspace_size", "chunk_workspace_size", "load", "precond_scan",
+           "chunk_fwd_noalloc", "chunk_fwd_varlen", "chunk_varlen_workspace_size", "chunk_workspace_size", "load", "precond_scan",
            "recurrent_step"]

@@ -26,7 +26,7 @@ EXPORTED = ("gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_chunk_fwd_varl
             "gdr_chunk_fwd_varlen", "gdr_recurrent_step", "gdr_chunk_fwd_wkey", "gdr_recurrent_step_wkey",
             "gdr_precond_scan", "gdr_status_string", "gdr_last_error", "gdr_version",
             "gdr_chunk_bwd_workspace_size", "gdr_chunk_bwd", "gdr_chunk_bwd_varlen_workspace_size",
-            "gdr_chunk_bwd_varlen")
+            "gdr_chunk_bwd_varlen", "gdr_chunk_fwd_noalloc")
 
 
 class GdrDesc(ctypes.Structure):
@@ -60,6 +60,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         lib.gdr_chunk_fwd_workspace_size.argtypes = [ctypes.POINTER(GdrDesc), ctypes.POINTER(ctypes.c_size_t)]
         lib.gdr_chunk_fwd.restype = ctypes.c_int
         lib.gdr_chunk_fwd.argtypes = [ctypes.POINTER(GdrDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        lib.gdr_chunk_fwd_noalloc.restype = ctypes.c_int
+        lib.gdr_chunk_fwd_noalloc.argtypes = [ctypes.POINTER(GdrDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.gdr_chunk_fwd_varlen_workspace_size.restype = ctypes.c_int
         lib.gdr_chunk_fwd_varlen_workspace_size.argtypes = [ctypes.POINTER(GdrDesc), ctypes.c_int64,
                                                             ctypes.POINTER(ctypes.c_size_t)]
@@ -199,6 +201,39 @@ def chunk_fwd(q, k, v, beta, log_a=None, S0=None, *, form: str = "page", o=None,
         return o, S_T
     st = lib.gdr_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_a), _ptr(S0),
                            _ptr(o), _ptr(S_T), _ptr(workspace), workspace.numel(), _stream_handle(stream))
+    _check(lib, st)
+    return o, S_T
+
+
+def chunk_fwd_noalloc(q, k, v, beta, log_a=None, S0=None, *, form: str = "page", o=None, S_T=None,
+                      want_state: bool = True, stream=None):
+    """gdr_chunk_fwd_noalloc on torch tensors: chunk_fwd with its scratch in the
+    library's static device array (no workspace, no device allocation by the call
+    beyond o and S_T when they are not given).  Calls that overlap in time on one
+    GPU share that array and race.  Returns (o, S_T)."""
+    lib = load()
+    B, T, H, dk = k.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    _require(q, "q", dt, (B, T, H, dk))
+    _require(k, "k", dt, (B, T, H, dk))
+    _require(v, "v", dt, (B, T, H, dv))
+    _require(beta, "beta", dt, (B, T, H))
+    gate = _gate_of(log_a, beta.shape, k.shape)
+    if log_a is not None:
+        _require(log_a, "log_a", dt, tuple(log_a.shape))
+    if S0 is not None:
+        _require(S0, "S0", torch.float32, (B, H, dk, dv))
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=dt, device=q.device)
+    _require(o, "o", dt, (B, T, H, dv))
+    if want_state and S_T is None:
+        S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    if S_T is not None:
+        _require(S_T, "S_T", torch.float32, (B, H, dk, dv))
+    desc = GdrDesc(B, T, H, dk, dv, 64, _io_of(q), gate, FORMS[form])
+    st = lib.gdr_chunk_fwd_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_a), _ptr(S0),
+                                   _ptr(o), _ptr(S_T), _stream_handle(stream))
     _check(lib, st)
     return o, S_T
 

@@ -46,6 +46,7 @@
 //
 // Products run on bf16 MFMA with fp32 accumulation for bf16 I/O and on fp32
 // MFMA for fp32 I/O; the state stays fp32.
+#include <mutex>
 #include <type_traits>
 
 #include "chunk_common.h"
@@ -539,6 +540,34 @@ hipError_t launch_varlen_order(const ChunkParams& p, int32_t* order, hipStream_t
   const unsigned nb = static_cast<unsigned>((p.B + 255) / 256);
   hipLaunchKernelGGL(varlen_order_kernel, dim3(nb), dim3(256), 0, stream, p, order);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------
+// The workspace of the forward that allocates nothing (gdr_chunk_fwd_noalloc): the
+// per-chunk records in one file-scope device array, a copy of which every GPU the
+// library runs on holds until the process ends.  In host code `scratch` names a
+// host-side stand-in, never the device memory: the device address of each GPU's
+// copy is looked up once per device (with that device current) and kept here.
+// ---------------------------------------------------------------------------------
+static __device__ __align__(256) char scratch[STATIC_SCRATCH_BYTES];
+
+hipError_t static_scratch(void** ptr) {
+  constexpr int MAX_DEV = 64;
+  static std::mutex mu;
+  static void* addr[MAX_DEV] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEV) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace gdr

@@ -245,6 +245,27 @@ gdr_status gdr_chunk_fwd(const gdr_desc* d, const void* q, const void* k, const 
   }
 }
 
+gdr_status gdr_chunk_fwd_noalloc(const gdr_desc* d, const void* q, const void* k, const void* v, const void* beta,
+                                 const void* log_a, const float* S0, void* o, float* S_T, void* stream) {
+  try {
+    g_last_error.clear();
+    gdr_status st = check_desc(d, false);
+    if (st != GDR_OK) return st;
+    const size_t need = gdr::chunk_workspace_bytes(d->B, d->T, d->H, d->io, d->gate, static_cast<int>(d->d_k));
+    if (need > gdr::STATIC_SCRATCH_BYTES)
+      return fail(GDR_ERR_WORKSPACE, "this forward needs %zu bytes of scratch; the static scratch holds %zu",
+                  need, gdr::STATIC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    if (d->T > 0) {
+      const hipError_t e = gdr::static_scratch(&ws);
+      if (e != hipSuccess) return fail(GDR_ERR_HIP, "static scratch lookup failed: %s", hipGetErrorString(e));
+    }
+    return chunk_fwd_impl(d, nullptr, 0, q, k, v, beta, log_a, S0, o, S_T, ws, gdr::STATIC_SCRATCH_BYTES, stream);
+  } catch (...) {
+    return fail(GDR_ERR_INVALID_ARG, "internal error");
+  }
+}
+
 gdr_status gdr_chunk_fwd_varlen_workspace_size(const gdr_desc* d, int64_t n_seq, size_t* bytes) {
   try {
     g_last_error.clear();

@@ -79,6 +79,11 @@ hipError_t launch_chunk_state_pipe(const ChunkParams& p, hipStream_t stream);   
 hipError_t launch_chunk_fwd(const ChunkParams& p, hipStream_t stream);
 // B*H*ceil(T/64) records of the per-chunk transform (see WsRec in chunk_common.h)
 size_t chunk_workspace_bytes(int64_t B, int64_t T, int64_t H, int io, int gate, int d_k);
+// gdr_chunk_fwd_noalloc: the size of the static device array that holds its
+// workspace, and that array's address on the current device (looked up once per
+// device; the first call on a device loads it).
+constexpr size_t STATIC_SCRATCH_BYTES = size_t(256) << 20;
+hipError_t static_scratch(void** ptr);
 // Packed sequences: record slots per head for n_seq sequences of T tokens in all
 // (sequence b's chunks start at slot floor(cu[b] / 64) + b), and the workspace bytes:
 // the records, then the order of the sequences by length (n_seq int32, 16-byte

@@ -23,7 +23,8 @@
  *    out-parameter of gdr_chunk_fwd_workspace_size), which are host pointers
  *    used during the call only.  The caller owns every buffer, scratch
  *    included; the library allocates no device memory, keeps no mutable global
- *    state and is safe to call from several host threads.
+ *    state and is safe to call from several host threads.  The one exception is
+ *    gdr_chunk_fwd_noalloc, whose scratch is a static device array per GPU.
  *  - Work is enqueued asynchronously on `stream` (0 = the null stream).  The
  *    library never synchronises; the caller synchronises before reading results.
  *  - All tensors are dense, contiguous and row-major in the layouts given
@@ -149,6 +150,28 @@ gdr_status gdr_chunk_fwd(const gdr_desc* desc, const void* q, const void* k, con
                          const void* beta, const void* log_a, const float* S0, void* o,
                          float* S_T, void* workspace, size_t workspace_bytes,
                          void* stream /* hipStream_t */);
+
+/*
+ * gdr_chunk_fwd_noalloc -- gdr_chunk_fwd without a caller workspace and without
+ * any device allocation, for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Same arguments, semantics, kernels and errors as gdr_chunk_fwd minus the
+ * workspace: the per-chunk records live in a static device array of 256 MiB
+ * (268435456 bytes) that every GPU the library runs on holds from its first use
+ * until the process ends.  A forward whose gdr_chunk_fwd_workspace_size exceeds
+ * that returns GDR_ERR_WORKSPACE with nothing enqueued (for example the scalar
+ * gate at d_k = 128 fits B * H * ceil(T / 64) <= 22795 chunk records; the
+ * per-channel gate at d_k = 128, 4405).  The first call on a device looks the
+ * array's address up (GDR_ERR_HIP if that fails).  The array keeps the last call's
+ * contents, which the next call overwrites before reading.  Every call on one GPU
+ * shares that GPU's array: calls whose work overlaps in time on one GPU (on
+ * different streams, or from several host threads at once) race and give
+ * undefined results; calls on one stream are ordered and safe.
+ */
+gdr_status gdr_chunk_fwd_noalloc(const gdr_desc* desc, const void* q, const void* k, const void* v,
+                                 const void* beta, const void* log_a, const float* S0, void* o, float* S_T,
+                                 void* stream /* hipStream_t */);
 
 /*
  * gdr_chunk_fwd_varlen_workspace_size -- workspace of gdr_chunk_fwd_varlen.
