@@ -69,10 +69,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         lib.gdr_chunk_fwd_varlen.argtypes = [ctypes.POINTER(GdrDesc), vp, ctypes.c_int64, vp, vp, vp, vp, vp, vp,
                                              vp, vp, vp, ctypes.c_size_t, vp]
         lib.gdr_chunk_fwd_wkey.restype = ctypes.c_int
-        lib.gdr_chunk_fwd_wkey.argtypes = [ctypes.POINTER(GdrDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp,
+        lib.gdr_chunk_fwd_wkey.argtypes = [ctypes.POINTER(GdrDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                            ctypes.c_size_t, vp]
         lib.gdr_recurrent_step_wkey.restype = ctypes.c_int
-        lib.gdr_recurrent_step_wkey.argtypes = [ctypes.POINTER(GdrDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.gdr_recurrent_step_wkey.argtypes = [ctypes.POINTER(GdrDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.gdr_recurrent_step.restype = ctypes.c_int
         lib.gdr_recurrent_step.argtypes = [ctypes.POINTER(GdrDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.gdr_precond_scan.restype = ctypes.c_int
@@ -161,7 +161,7 @@ def chunk_fwd(q, k, v, beta, log_a=None, S0=None, *, form: str = "page", o=None,
     beta [B, T, H]; log_a None, [B, T, H] or [B, T, H, d_k] (all one I/O dtype);
     S0 None or [B, H, d_k, d_v] float32.  `workspace` is an optional uint8 device
     tensor of at least chunk_workspace_size() bytes (allocated per call when
-    None).  `kw` (optional, [B, T, H, d_k], no gate, bf16) is a separate write key
+    None).  `kw` (optional, [B, T, H, d_k], bf16) is a separate write key
     (gdr_chunk_fwd_wkey).  Returns (o, S_T) (S_T None when want_state is False).
     Asynchronous on the current (or given) stream."""
     lib = load()
@@ -193,10 +193,9 @@ def chunk_fwd(q, k, v, beta, log_a=None, S0=None, *, form: str = "page", o=None,
         raise ValueError("workspace must be a contiguous uint8 tensor on the inputs' device")
     if kw is not None:
         _require(kw, "kw", dt, (B, T, H, dk))
-        if log_a is not None:
-            raise ValueError("a write key goes with no gate (log_a must be None)")
-        st = lib.gdr_chunk_fwd_wkey(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(kw), _ptr(v), _ptr(beta), _ptr(S0),
-                                    _ptr(o), _ptr(S_T), _ptr(workspace), workspace.numel(), _stream_handle(stream))
+        st = lib.gdr_chunk_fwd_wkey(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(kw), _ptr(v), _ptr(beta), _ptr(log_a),
+                                    _ptr(S0), _ptr(o), _ptr(S_T), _ptr(workspace), workspace.numel(),
+                                    _stream_handle(stream))
         _check(lib, st)
         return o, S_T
     st = lib.gdr_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_a), _ptr(S0),
@@ -366,8 +365,8 @@ def chunk_fwd_varlen(q, k, v, beta, log_a, cu_seqlens, S0=None, *, form: str = "
 def recurrent_step(q, k, v, beta, log_a, S, *, S_new=None, o=None, form: str = "page", stream=None, kw=None):
     """gdr_recurrent_step on torch tensors.  q, k [B, H, d_k]; v [B, H, d_v];
     beta [B, H]; log_a None, [B, H] or [B, H, d_k]; S [B, H, d_k, d_v] float32.
-    S_new defaults to S (update in place).  `kw` (optional, [B, H, d_k], no gate)
-    is a separate write key (gdr_recurrent_step_wkey).  Returns (o, S_new)."""
+    S_new defaults to S (update in place).  `kw` (optional, [B, H, d_k]) is a
+    separate write key (gdr_recurrent_step_wkey).  Returns (o, S_new)."""
     lib = load()
     B, H, dk = k.shape
     dv = v.shape[-1]
@@ -389,10 +388,8 @@ def recurrent_step(q, k, v, beta, log_a, S, *, S_new=None, o=None, form: str = "
     desc = GdrDesc(B, 1, H, dk, dv, 0, _io_of(q), gate, FORMS[form])
     if kw is not None:
         _require(kw, "kw", dt, (B, H, dk))
-        if log_a is not None:
-            raise ValueError("a write key goes with no gate (log_a must be None)")
         st = lib.gdr_recurrent_step_wkey(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(kw), _ptr(v), _ptr(beta),
-                                         _ptr(S), _ptr(S_new), _ptr(o), _stream_handle(stream))
+                                         _ptr(log_a), _ptr(S), _ptr(S_new), _ptr(o), _stream_handle(stream))
         _check(lib, st)
         return o, S_new
     st = lib.gdr_recurrent_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_a), _ptr(S),

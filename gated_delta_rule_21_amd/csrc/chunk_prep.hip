@@ -445,7 +445,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_chan_kernel(ChunkParams p) 
   const rsrc_t rb = make_rsrc(static_cast<const elem*>(p.beta) + row0, span * ESZ);
 
   const int cq = tid % NQ, sg = tid / NQ, c0 = 4 * cq, r0 = sg * SL, R = r0 / 16;
-  u32x2 kr[SL], qr[SL], la[SL];
+  u32x2 kr[SL], qr[SL], la[SL], kwr[SL];
   float be[SL];
 #pragma unroll
   for (int j = 0; j < SL; ++j) {
@@ -454,6 +454,18 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_chan_kernel(ChunkParams p) 
     qr[j] = buf_load8(rq, off, 0);
     la[j] = buf_load8(rl, off, 0);
     be[j] = bf16_bits_to_f32(buf_load2(rb, static_cast<uint32_t>((r0 + j) * H * ESZ), 0));
+  }
+  // With a write key ("OSDN: Improving Delta Rule with Provable Online
+  // Preconditioning in Linear Attention", §2.1) the column operand of the Gram and
+  // score blocks and the state pass's update operand take kw; the rows of A and the
+  // residual's operand keep k.
+  if (p.kw) {
+    const rsrc_t rkw = make_rsrc(static_cast<const elem*>(p.kw) + row0 * DK, span * DK * ESZ);
+#pragma unroll
+    for (int j = 0; j < SL; ++j) kwr[j] = buf_load8(rkw, static_cast<uint32_t>(((r0 + j) * H * DK + c0) * ESZ), 0);
+  } else {
+#pragma unroll
+    for (int j = 0; j < SL; ++j) kwr[j] = kr[j];
   }
   auto el = [](u32x2 w, int c) -> float {       // element c of four packed bf16
     const uint32_t x = w[c >> 1];
@@ -516,16 +528,16 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_chan_kernel(ChunkParams p) 
     f32x4 xk, xq, y, sk, sq, sd;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const float kk = el(kr[j], c), qq = el(qr[j], c);
+      const float kk = el(kr[j], c), qq = el(qr[j], c), kwv = el(kwr[j], c);
       const float a = __expf(g[j][c] - gR[c]);
       const float ar = p.literal ? aprev[c] : a;             // e^{g_read - g_16R}
       aprev[c] = a;
       xk[c] = be[j] * kk * ar;
       xq[c] = qq * a;
-      y[c] = kk * __expf(gR[c] - g[j][c]);
+      y[c] = kwv * __expf(gR[c] - g[j][c]);
       sk[c] = kk * ar * eR[c];
       sq[c] = qq * a * eR[c];
-      sd[c] = kk * __expf(g63[c] - g[j][c]);
+      sd[c] = kwv * __expf(g63[c] - g[j][c]);
     }
     *reinterpret_cast<bf16x4*>(sK + r * LDK + c0) = O::cvt(xk);
     *reinterpret_cast<bf16x4*>(sQ + r * LDK + c0) = O::cvt(xq);
@@ -656,15 +668,17 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_chan_kernel(ChunkParams p) 
 // The rest of the record (the state pass's operands and factors, all carrying
 // factors <= 1) stands as the transform wrote it.
 // ---------------------------------------------------------------------------------
-template <int DK>
+template <int DK, int ESZ>
 struct GenLayout {
   static constexpr int LK = DK + 1;                  // odd strides: rows r and j of one column sit in different banks
   static constexpr int LT = CH + 1;
-  static constexpr size_t OFF_K = 0;                                // k [64][LK] fp32
-  static constexpr size_t OFF_Q = OFF_K + size_t(CH) * LK * 4;      // q
-  static constexpr size_t OFF_G = OFF_Q + size_t(CH) * LK * 4;      // [65][LK]: row 0 zero, row r + 1 = g_r
-  static constexpr size_t OFF_A = OFF_G + size_t(CH + 1) * LK * 4;  // A [64][LT]
-  static constexpr size_t OFF_T = OFF_A + size_t(CH) * LT * 4;      // T [64][LT]
+  static constexpr size_t KT = (size_t(CH) * LK * ESZ + 15) / 16 * 16;   // one [64][LK] tile in the I/O dtype
+  static constexpr size_t OFF_K = 0;                                // k
+  static constexpr size_t OFF_Q = OFF_K + KT;                       // q
+  static constexpr size_t OFF_KW = OFF_Q + KT;                      // the write key (or k again)
+  static constexpr size_t OFF_G = OFF_KW + KT;                      // [65][LK] fp32: row 0 zero, row r + 1 = g_r
+  static constexpr size_t OFF_A = OFF_G + size_t(CH + 1) * LK * 4;  // A [64][LT] fp32
+  static constexpr size_t OFF_T = OFF_A + size_t(CH) * LT * 4;      // T [64][LT] fp32
   static constexpr size_t OFF_B = OFF_T + size_t(CH) * LT * 4;      // beta [64]
   static constexpr size_t TOTAL = OFF_B + CH * 4;
 };
@@ -674,7 +688,7 @@ __global__ __launch_bounds__(256) void chunk_prep_generic_kernel(ChunkParams p, 
   typedef typename Io<IO>::elem elem;
   constexpr int ESZ = int(sizeof(elem));
   typedef WsRec<ESZ> W;
-  typedef GenLayout<DK> L;
+  typedef GenLayout<DK, ESZ> L;
   constexpr int NT = 256, LK = L::LK, LT = L::LT;
   constexpr uint32_t RB = rec_bytes(IO, GATE_CHANNEL, DK);
   static_assert(L::TOTAL <= 163840, "LDS budget");
@@ -682,8 +696,9 @@ __global__ __launch_bounds__(256) void chunk_prep_generic_kernel(ChunkParams p, 
   __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
   __shared__ int s_list[NT];
   __shared__ int s_n;
-  float* sK = reinterpret_cast<float*>(smem + L::OFF_K);
-  float* sQ = reinterpret_cast<float*>(smem + L::OFF_Q);
+  elem* sK = reinterpret_cast<elem*>(smem + L::OFF_K);
+  elem* sQ = reinterpret_cast<elem*>(smem + L::OFF_Q);
+  elem* sKW = reinterpret_cast<elem*>(smem + L::OFF_KW);
   float* sG = reinterpret_cast<float*>(smem + L::OFF_G);
   float* sA = reinterpret_cast<float*>(smem + L::OFF_A);
   float* sT = reinterpret_cast<float*>(smem + L::OFF_T);
@@ -708,6 +723,14 @@ __global__ __launch_bounds__(256) void chunk_prep_generic_kernel(ChunkParams p, 
     if constexpr (IO == IO_BF16) return bf16_bits_to_f32(buf_load2(r, off, 0));
     else return __uint_as_float(buf_load4(r, off, 0));
   };
+  auto loade = [&](rsrc_t r, uint32_t off) -> elem {
+    if constexpr (IO == IO_BF16) return buf_load2(r, off, 0);
+    else return __uint_as_float(buf_load4(r, off, 0));
+  };
+  auto f = [&](elem x) -> float {
+    if constexpr (IO == IO_BF16) return bf16_bits_to_f32(x);
+    else return x;
+  };
   for (int m = 0; m < nmarked; ++m) {
     const int64_t task = uni64(base + s_list[m]);
     int64_t bb, n, hh;
@@ -724,13 +747,17 @@ __global__ __launch_bounds__(256) void chunk_prep_generic_kernel(ChunkParams p, 
     const rsrc_t rq = make_rsrc(static_cast<const elem*>(p.q) + row0 * DK, span * DK * ESZ);
     const rsrc_t rl = make_rsrc(static_cast<const elem*>(p.log_a) + row0 * DK, span * DK * ESZ);
     const rsrc_t rb = make_rsrc(static_cast<const elem*>(p.beta) + row0, span * ESZ);
+    // the write key of "OSDN: Improving Delta Rule with Provable Online Preconditioning
+    // in Linear Attention", §2.1 pairs with k in A and with q in P (columns j)
+    const rsrc_t rkw = make_rsrc(static_cast<const elem*>(p.kw ? p.kw : p.k) + row0 * DK, span * DK * ESZ);
 
     __syncthreads();                            // the previous chunk's tiles are no longer read
     for (int e = tid; e < CH * DK; e += NT) {
       const int r = e / DK, c = e % DK;
       const uint32_t off = static_cast<uint32_t>((r * H * DK + c) * ESZ);
-      sK[r * LK + c] = load1(rk, off);
-      sQ[r * LK + c] = load1(rq, off);
+      sK[r * LK + c] = loade(rk, off);
+      sQ[r * LK + c] = loade(rq, off);
+      sKW[r * LK + c] = loade(rkw, off);
       sG[(r + 1) * LK + c] = load1(rl, off);
     }
     for (int c = tid; c < DK; c += NT) sG[c] = 0.f;
@@ -751,20 +778,20 @@ __global__ __launch_bounds__(256) void chunk_prep_generic_kernel(ChunkParams p, 
       while (r * (r + 1) / 2 > pr) --r;
       while ((r + 1) * (r + 2) / 2 <= pr) ++r;
       const int j = pr - r * (r + 1) / 2;
-      const float* kr = sK + r * LK;
-      const float* kj = sK + j * LK;
-      const float* qr = sQ + r * LK;
+      const elem* kr = sK + r * LK;
+      const elem* kj = sKW + j * LK;            // column side: the write key (k without one)
+      const elem* qr = sQ + r * LK;
       const float* gr = sG + (r + 1) * LK;
       const float* grd = sG + (p.literal ? r : r + 1) * LK;   // g_read: g_r, or g_{r-1} (g_{-1} = 0)
       const float* gj = sG + (j + 1) * LK;
       float a = 0.f, pv = 0.f;
       if (j < r) {
         for (int c = 0; c < DK; ++c) {
-          a += kr[c] * kj[c] * __expf(grd[c] - gj[c]);
-          pv += qr[c] * kj[c] * __expf(gr[c] - gj[c]);
+          a += f(kr[c]) * f(kj[c]) * __expf(grd[c] - gj[c]);
+          pv += f(qr[c]) * f(kj[c]) * __expf(gr[c] - gj[c]);
         }
       } else {
-        for (int c = 0; c < DK; ++c) pv += qr[c] * kr[c];
+        for (int c = 0; c < DK; ++c) pv += f(qr[c]) * f(kj[c]);
       }
       sA[r * LT + j] = j < r ? sB[r] * a : 0.f;
       const int R = r >> 4, J = j >> 4;
@@ -808,7 +835,7 @@ __global__ __launch_bounds__(256) void chunk_prep_reg_kernel(ChunkParams p, int6
   constexpr int EPV = 16 / ESZ;                 // elements per 16-byte piece
   constexpr int NSTEP = DK / (4 * EPV);         // products over d_k (four lane groups, one piece each)
   static_assert(GATE != GATE_CHANNEL, "per-channel gate uses chunk_prep_lds_kernel");
-  static_assert(GATE != GATE_WKEY || IO == IO_BF16, "write key: bf16 I/O only");
+  static_assert(!gate_wkey(GATE) || IO == IO_BF16, "write key: bf16 I/O only");
   static_assert(NSTEP * 4 * EPV == DK, "d_k must split into pieces");
 
   __shared__ __attribute__((aligned(16))) float sfac[4][3 * CH];   // per wave: beta, g, g_read
@@ -839,7 +866,7 @@ __global__ __launch_bounds__(256) void chunk_prep_reg_kernel(ChunkParams p, int6
   const rsrc_t rk = make_rsrc(static_cast<const elem*>(p.k) + row0 * DK, span * DK * ESZ);
   const rsrc_t rq = make_rsrc(static_cast<const elem*>(p.q) + row0 * DK, span * DK * ESZ);
   const rsrc_t rb = make_rsrc(static_cast<const elem*>(p.beta) + row0, span * ESZ);
-  const rsrc_t rl = make_rsrc(static_cast<const elem*>(p.log_a) + row0, GATE == GATE_SCALAR ? span * ESZ : 0u);
+  const rsrc_t rl = make_rsrc(static_cast<const elem*>(p.log_a) + row0, gate_scalar(GATE) ? span * ESZ : 0u);
   auto load1 = [&](rsrc_t r, uint32_t off) -> float {
     if constexpr (IO == IO_BF16) return bf16_bits_to_f32(buf_load2(r, off, 0));
     else return __uint_as_float(buf_load4(r, off, 0));
@@ -847,7 +874,7 @@ __global__ __launch_bounds__(256) void chunk_prep_reg_kernel(ChunkParams p, int6
   // Write key (GATE_WKEY): the Gram matrix pairs the key of row r with the write
   // key of row j, A_rj = beta_r (k_r . kw_j), so kw takes the place of k on the
   // column side of every A block.
-  constexpr bool WK = GATE == GATE_WKEY;
+  constexpr bool WK = gate_wkey(GATE);
   const rsrc_t rkw = make_rsrc(static_cast<const elem*>(WK ? p.kw : p.k) + row0 * DK, span * DK * ESZ);
   // piece i of row block R: row 16R + lr, channels [(4i + lg) EPV, (4i + lg + 1) EPV)
   auto piece_off = [&](int R, int i) -> uint32_t {
@@ -874,7 +901,7 @@ __global__ __launch_bounds__(256) void chunk_prep_reg_kernel(ChunkParams p, int6
     const uint32_t off = static_cast<uint32_t>(lane * H * ESZ);
     const float b = load1(rb, off);
     float g = 0.f, gread = 0.f;
-    if constexpr (GATE == GATE_SCALAR) {
+    if constexpr (gate_scalar(GATE)) {
       g = load1(rl, off);
 #pragma unroll
       for (int d = 1; d < 64; d <<= 1) {
@@ -925,7 +952,7 @@ __global__ __launch_bounds__(256) void chunk_prep_reg_kernel(ChunkParams p, int6
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       float v = acc[s] * br;
-      if constexpr (GATE == GATE_SCALAR) v *= __expf(grr - gj[s]);
+      if constexpr (gate_scalar(GATE)) v *= __expf(grr - gj[s]);
       acc[s] = (R == J && lr <= 4 * lg + s) ? 0.f : v;
     }
     return acc;
@@ -959,7 +986,7 @@ __global__ __launch_bounds__(256) void chunk_prep_reg_kernel(ChunkParams p, int6
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         float v = G2[s] * br[s];
-        if constexpr (GATE == GATE_SCALAR) v *= __expf(grr[s] - gj);
+        if constexpr (gate_scalar(GATE)) v *= __expf(grr[s] - gj);
         N[s] = (4 * lg + s > lr) ? v : 0.f;
       }
     }
@@ -990,7 +1017,7 @@ __global__ __launch_bounds__(256) void chunk_prep_reg_kernel(ChunkParams p, int6
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         float v = acc[s];
-        if constexpr (GATE == GATE_SCALAR) v *= __expf(gr - gj[s]);
+        if constexpr (gate_scalar(GATE)) v *= __expf(gr - gj[s]);
         acc[s] = (J == R && lr < 4 * lg + s) ? 0.f : v;
       }
       store4(W::P_OFF + W::at(R, J, lr, 4 * lg), acc);
@@ -1033,8 +1060,12 @@ static hipError_t launch_prep_g(const ChunkParams& p, int64_t nchunks, hipStream
 template <int IO>
 static hipError_t launch_prep_io(const ChunkParams& p, int64_t nchunks, hipStream_t stream) {
   if (p.kw) {
-    if constexpr (IO == IO_BF16) return p.gate == GATE_NONE ? launch_prep_g<IO, GATE_WKEY>(p, nchunks, stream)
-                                                          : hipErrorInvalidValue;
+    if constexpr (IO == IO_BF16) {
+      if (p.gate == GATE_NONE) return launch_prep_g<IO, GATE_WKEY>(p, nchunks, stream);
+      if (p.gate == GATE_SCALAR) return launch_prep_g<IO, GATE_WKEY_SCALAR>(p, nchunks, stream);
+      if (p.gate == GATE_CHANNEL) return launch_prep_g<IO, GATE_CHANNEL>(p, nchunks, stream);   // reads p.kw
+      return hipErrorInvalidValue;
+    }
     else return hipErrorInvalidValue;
   }
   switch (p.gate) {

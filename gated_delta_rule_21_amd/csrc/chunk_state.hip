@@ -86,7 +86,7 @@ __global__ __launch_bounds__((NCH + NHW) * 64) void chunk_state_pipe_kernel(Chun
   typedef uint16_t elem;
   constexpr int DVT = 16 * CG * NCH;            // columns per workgroup
   constexpr bool CHAN = GATE == GATE_CHANNEL;
-  constexpr bool WK = GATE == GATE_WKEY;          // write key: K^T and P take kw instead of k
+  constexpr bool WK = gate_wkey(GATE);            // write key: K^T and P take kw instead of k
   typedef PipeLayout<DK, DVT, CHAN || WK, WK> L;
   typedef WsRec<2> W;
   constexpr uint32_t RB = rec_bytes(IO_BF16, GATE, DK);   // bytes per chunk record
@@ -337,7 +337,7 @@ __global__ __launch_bounds__((NCH + NHW) * 64) void chunk_state_pipe_kernel(Chun
         for (int g = 0; g < CG; ++g) vt[R][g] = O::ld_tr(c.V, LVT, 16 * R, c0 + 16 * g, lr, lg);
         be[R] = *reinterpret_cast<const f32x4*>(c.beta + 16 * R + 4 * lg);
         er[R] = *reinterpret_cast<const f32x4*>(c.er + 16 * R + 4 * lg);
-        eo[R] = GATE == GATE_SCALAR ? c.eo[16 * R + lr] : 1.f;
+        eo[R] = gate_scalar(GATE) ? c.eo[16 * R + lr] : 1.f;
       };
 
       // stage A: P of the previous chunk, rows of block 0; S to bf16
@@ -367,7 +367,7 @@ __global__ __launch_bounds__((NCH + NHW) * 64) void chunk_state_pipe_kernel(Chun
           f32x4 rr;
 #pragma unroll
           for (int s = 0; s < 4; ++s)
-            rr[s] = be[R][s] * (vv[s] - (GATE == GATE_SCALAR ? x[R][g][s] * er[R][s] : x[R][g][s]));
+            rr[s] = be[R][s] * (vv[s] - (gate_scalar(GATE) ? x[R][g][s] * er[R][s] : x[R][g][s]));
           Rb[g][R] = O::cvt(rr);
         }
       };
@@ -383,9 +383,9 @@ __global__ __launch_bounds__((NCH + NHW) * 64) void chunk_state_pipe_kernel(Chun
             for (int m = 0; m <= Rr; ++m) tf[Rr * (Rr + 1) / 2 + m] = O::ld_tr(c.Tt, LCT, 16 * m, 16 * Rr, lr, lg);
 #pragma unroll
           for (int Rr = 0; Rr < 4; ++Rr)
-            ed[Rr] = GATE == GATE_SCALAR ? *reinterpret_cast<const f32x4*>(c.ed + 16 * Rr + 4 * lg)
+            ed[Rr] = gate_scalar(GATE) ? *reinterpret_cast<const f32x4*>(c.ed + 16 * Rr + 4 * lg)
                                          : f32x4{1.f, 1.f, 1.f, 1.f};
-          if constexpr (GATE == GATE_SCALAR) gam = c.gam[0];
+          if constexpr (gate_scalar(GATE)) gam = c.gam[0];
         }
         __builtin_amdgcn_sched_barrier(0);
         f32x4 oq[CG];
@@ -420,7 +420,7 @@ __global__ __launch_bounds__((NCH + NHW) * 64) void chunk_state_pipe_kernel(Chun
               for (int g = 0; g < CG; ++g) op[g] = O::mma1(op[g], db_prev[g][J], pf[Ro * (Ro + 1) / 2 + J]);
 #pragma unroll
             for (int g = 0; g < CG; ++g) {
-              const f32x4 ov = GATE == GATE_SCALAR ? oq_prev[g][Ro] * eo_prev[Ro] + op[g] : oq_prev[g][Ro] + op[g];
+              const f32x4 ov = gate_scalar(GATE) ? oq_prev[g][Ro] * eo_prev[Ro] + op[g] : oq_prev[g][Ro] + op[g];
               buf_store8(__builtin_bit_cast(u32x2, to_bf16x4(ov)), ro, vo[Ro][g] + drop, so);
             }
           }
@@ -466,7 +466,7 @@ __global__ __launch_bounds__((NCH + NHW) * 64) void chunk_state_pipe_kernel(Chun
 #pragma unroll
         for (int g = 0; g < CG; ++g) {
           db_prev[g][R] = O::cvt(d[g]);
-          Ds[g][R] = GATE == GATE_SCALAR ? O::cvt(d[g] * ed[R]) : db_prev[g][R];
+          Ds[g][R] = gate_scalar(GATE) ? O::cvt(d[g] * ed[R]) : db_prev[g][R];
         }
       }
 
@@ -482,7 +482,7 @@ __global__ __launch_bounds__((NCH + NHW) * 64) void chunk_state_pipe_kernel(Chun
 #pragma unroll
           for (int g = 0; g < CG; ++g) {
             f32x4 acc = S[g][t];
-            if constexpr (GATE == GATE_SCALAR) acc = acc * gam;
+            if constexpr (gate_scalar(GATE)) acc = acc * gam;
             if constexpr (CHAN) acc = acc * gc[tp & 1][h];
             acc = O::mma2(acc, ktf[tp & 1][4 * h], ktf[tp & 1][4 * h + 1], Ds[g][0], Ds[g][1]);
             S[g][t] = O::mma2(acc, ktf[tp & 1][4 * h + 2], ktf[tp & 1][4 * h + 3], Ds[g][2], Ds[g][3]);
@@ -510,7 +510,7 @@ __global__ __launch_bounds__((NCH + NHW) * 64) void chunk_state_pipe_kernel(Chun
         }
 #pragma unroll
         for (int g = 0; g < CG; ++g) {
-          const f32x4 ov = GATE == GATE_SCALAR ? oq_prev[g][R] * eo_prev[R] + op[g] : oq_prev[g][R] + op[g];
+          const f32x4 ov = gate_scalar(GATE) ? oq_prev[g][R] * eo_prev[R] + op[g] : oq_prev[g][R] + op[g];
           buf_store8(__builtin_bit_cast(u32x2, to_bf16x4(ov)), ro, vo[R][g], so);
         }
       }
@@ -569,7 +569,7 @@ __global__ __launch_bounds__((NCH + NHW) * 64) void chunk_state_pipe_kernel(Chun
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
             float val = acc[s];
-            if constexpr (GATE == GATE_SCALAR) val *= __expf(gr - gj[s]);
+            if constexpr (gate_scalar(GATE)) val *= __expf(gr - gj[s]);
             acc[s] = (R == J && lr < 4 * lg + s) ? 0.f : val;
           }
           *reinterpret_cast<frag*>(sP + r * LCP + 16 * J + 4 * lg) = O::cvt(acc);
@@ -612,7 +612,7 @@ static hipError_t launch_pipe_dk(const ChunkParams& p, hipStream_t stream) {
   if constexpr (GATE == GATE_CHANNEL) {
     // per-channel gate: the third operand tile leaves LDS room for 32 columns only
     return launch_pipe_t<GATE, DK, 2, 1, 4>(p, stream);
-  } else if constexpr (GATE == GATE_WKEY && DK == 64) {
+  } else if constexpr (gate_wkey(GATE) && DK == 64) {
     return launch_pipe_t<GATE, DK, 2, 1, 4>(p, stream);
   } else {
     // 64 columns per workgroup when that still gives one workgroup per CU, else 32.
@@ -634,7 +634,11 @@ static hipError_t launch_pipe_g(const ChunkParams& p, hipStream_t stream) {
 
 hipError_t launch_chunk_state_pipe(const ChunkParams& p, hipStream_t stream) {
   if (p.io != IO_BF16) return hipErrorInvalidValue;
-  if (p.kw) return p.gate == GATE_NONE ? launch_pipe_g<GATE_WKEY>(p, stream) : hipErrorInvalidValue;
+  if (p.kw) {   // write key: the per-channel gate reads its write-key operands from the records
+    if (p.gate == GATE_NONE) return launch_pipe_g<GATE_WKEY>(p, stream);
+    if (p.gate == GATE_SCALAR) return launch_pipe_g<GATE_WKEY_SCALAR>(p, stream);
+    if (p.gate != GATE_CHANNEL) return hipErrorInvalidValue;
+  }
   if (p.gate == GATE_NONE) return launch_pipe_g<GATE_NONE>(p, stream);
   if (p.gate == GATE_SCALAR) return launch_pipe_g<GATE_SCALAR>(p, stream);
   if (p.gate == GATE_CHANNEL) return launch_pipe_g<GATE_CHANNEL>(p, stream);

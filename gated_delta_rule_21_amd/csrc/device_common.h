@@ -8,9 +8,14 @@ namespace gdr {
 
 enum IoType { IO_F32 = 0, IO_BF16 = 1 };
 enum GateKind { GATE_NONE = 0, GATE_SCALAR = 1, GATE_CHANNEL = 2 };
-// Kernel variant (never a value of the C ABI's gate): no gate, and a separate write
-// key k~ for the state write (the right-preconditioned delta rule).
+// Kernel variants (never values of the C ABI's gate): a separate write key k~ for
+// the state write (the right-preconditioned delta rule), without a gate or with a
+// scalar gate.  (The per-channel gate takes the write key through its transform's
+// operands and keeps GATE_CHANNEL.)
 constexpr int GATE_WKEY = 3;
+constexpr int GATE_WKEY_SCALAR = 4;
+__host__ __device__ constexpr bool gate_scalar(int g) { return g == GATE_SCALAR || g == GATE_WKEY_SCALAR; }
+__host__ __device__ constexpr bool gate_wkey(int g) { return g == GATE_WKEY || g == GATE_WKEY_SCALAR; }
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;

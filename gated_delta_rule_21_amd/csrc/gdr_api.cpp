@@ -434,13 +434,12 @@ gdr_status gdr_recurrent_step(const gdr_desc* d, const void* q, const void* k, c
 }
 
 gdr_status gdr_recurrent_step_wkey(const gdr_desc* d, const void* q, const void* k, const void* kw, const void* v,
-                                   const void* beta, const float* S, float* S_new, void* o, void* stream) {
+                                   const void* beta, const void* log_a, const float* S, float* S_new, void* o,
+                                   void* stream) {
   try {
     g_last_error.clear();
     if (!kw) return fail(GDR_ERR_INVALID_ARG, "kw is NULL");
-    if (d && d->gate != GDR_GATE_NONE)
-      return fail(GDR_ERR_UNSUPPORTED, "write key: no gate only (the preconditioned delta rule)");
-    return recurrent_step_impl(d, q, k, kw, v, beta, nullptr, S, S_new, o, stream);
+    return recurrent_step_impl(d, q, k, kw, v, beta, log_a, S, S_new, o, stream);
   } catch (...) {
     return fail(GDR_ERR_INVALID_ARG, "internal error");
   }
@@ -496,16 +495,15 @@ gdr_status gdr_precond_scan(const gdr_desc* d, const void* k, const void* beta, 
 }
 
 gdr_status gdr_chunk_fwd_wkey(const gdr_desc* d, const void* q, const void* k, const void* kw, const void* v,
-                              const void* beta, const float* S0, void* o, float* S_T, void* workspace,
-                              size_t workspace_bytes, void* stream) {
+                              const void* beta, const void* log_a, const float* S0, void* o, float* S_T,
+                              void* workspace, size_t workspace_bytes, void* stream) {
   try {
     g_last_error.clear();
     if (!kw) return fail(GDR_ERR_INVALID_ARG, "kw is NULL");
-    if (d && d->gate != GDR_GATE_NONE)
-      return fail(GDR_ERR_UNSUPPORTED, "write key: no gate only (the preconditioned delta rule)");
     if (d && d->io != GDR_BF16) return fail(GDR_ERR_UNSUPPORTED, "write key chunk forward: bf16 I/O only");
-    return chunk_fwd_impl(d, nullptr, 0, q, k, v, beta, nullptr, S0, o, S_T, workspace, workspace_bytes, stream,
-                          kw);
+    if (d && d->gate == GDR_GATE_CHANNEL && d->d_k != 128)
+      return fail(GDR_ERR_UNSUPPORTED, "write key with a per-channel gate: d_k = 128 only");
+    return chunk_fwd_impl(d, nullptr, 0, q, k, v, beta, log_a, S0, o, S_T, workspace, workspace_bytes, stream, kw);
   } catch (...) {
     return fail(GDR_ERR_INVALID_ARG, "internal error");
   }

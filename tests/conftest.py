@@ -11,3 +11,11 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: long-running CPU test")
+
+
+def pytest_terminal_summary(terminalreporter):
+    from tests.report import LINES
+    if LINES:
+        terminalreporter.section("parity summary")
+        for line in LINES:
+            terminalreporter.write_line(line)

@@ -221,19 +221,24 @@ def _chunk_wkey(lib, d, kw, ptrs, ws_bytes=None):
     ws = ptrs[8] if len(ptrs) > 8 else None
     if ws_bytes is None:
         ws_bytes = _ws_size(lib, d)[1] if d is not None else 0
-    return lib.gdr_chunk_fwd_wkey(None if d is None else ctypes.byref(d), q, k, kw, v, beta, S0, o, S_T, ws,
+    return lib.gdr_chunk_fwd_wkey(None if d is None else ctypes.byref(d), q, k, kw, v, beta, log_a, S0, o, S_T, ws,
                                   ws_bytes, None)
 
 
 def test_write_key_chunk_checks(lib):
     kw = FAKE + 0x7F000000                     # never dereferenced
-    assert _chunk_wkey(lib, _desc(gate=1), kw, _ptrs()) == UNSUPPORTED      # no gate only
+    p = _ptrs()
+    p[4] = None
+    assert _chunk_wkey(lib, _desc(gate=1), kw, p) == INVALID                # a gate needs log_a
+    assert b"log_a" in lib.gdr_last_error()
+    assert _chunk_wkey(lib, _desc(gate=2, d_k=64), kw, _ptrs()) == UNSUPPORTED   # per-channel: d_k = 128
+    assert _chunk_wkey(lib, _desc(gate=0), kw, _ptrs()) == INVALID          # log_a given without a gate
     assert _chunk_wkey(lib, _desc(gate=0), None, _ptrs()) == INVALID
     assert b"kw" in lib.gdr_last_error()
-    assert _chunk_wkey(lib, _desc(gate=0, io=0, d_k=64), kw, _ptrs()) == UNSUPPORTED   # bf16 only
-    assert _chunk_wkey(lib, _desc(gate=0), kw + 8, _ptrs()) == ALIGN
+    assert _chunk_wkey(lib, _desc(gate=1, io=0, d_k=64), kw, _ptrs()) == UNSUPPORTED   # bf16 only
+    assert _chunk_wkey(lib, _desc(gate=1), kw + 8, _ptrs()) == ALIGN
     p = _ptrs()
-    assert _chunk_wkey(lib, _desc(gate=0), p[6] + 64, p) == INVALID          # kw inside o
+    assert _chunk_wkey(lib, _desc(gate=1), p[6] + 64, p) == INVALID          # kw inside o
     assert b"overlaps" in lib.gdr_last_error()
 
 
@@ -241,9 +246,10 @@ def test_write_key_step_checks(lib):
     kw = FAKE + 0x7F000000
     p = _ptrs()
     d = _desc(T=1, gate=0)
-    call = lambda d, kw: lib.gdr_recurrent_step_wkey(ctypes.byref(d), p[0], p[1], kw, p[2], p[3], p[5], p[7], p[6],
-                                                     None)
-    assert call(_desc(T=1, gate=1), kw) == UNSUPPORTED
+    call = lambda d, kw, la=None: lib.gdr_recurrent_step_wkey(ctypes.byref(d), p[0], p[1], kw, p[2], p[3], la, p[5],
+                                                              p[7], p[6], None)
+    assert call(_desc(T=1, gate=1), kw) == INVALID                         # a gate needs log_a
+    assert call(d, kw, p[4]) == INVALID                                    # log_a given without a gate
     assert call(d, None) == INVALID
     assert call(d, kw + 4) == ALIGN
     assert call(d, p[7] + 64) == INVALID                                   # kw inside S_new

@@ -42,3 +42,18 @@ def test_write_key_chunk_form_equals_oracle(C):
     o, S = chunk_forward(q, k, v, beta, None, S0, C, kw=d * k)
     assert np.max(np.abs(o - o_ref)) <= 1e-12 * max(1, np.max(np.abs(o_ref)))
     assert np.max(np.abs(S - S_ref)) <= 1e-12 * max(1, np.max(np.abs(S_ref)))
+
+
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+@pytest.mark.parametrize("form", ["page", "literal"])
+@pytest.mark.parametrize("C", [1, 8, 64])
+def test_write_key_chunk_form_with_gates(gate, form, C):
+    """The write key under a scalar or per-channel gate (the decay first, the residual
+    along k, the write along kw): the chunk equations with kw in the Gram columns, the
+    scores and the state write reproduce the oracle."""
+    q, k, v, beta, log_a, S0 = _inputs(200 + C, 1, 131, 2, 12, 7, gate)
+    d = np.random.default_rng(C + 7).uniform(0.2, 2.0, k.shape)
+    o_ref, S_ref = forward(q, k, v, beta, log_a, S0, form=form, kw=d * k)
+    o, S = chunk_forward(q, k, v, beta, log_a, S0, C, form=form, kw=d * k)
+    assert np.max(np.abs(o - o_ref)) <= 1e-12 * max(1, np.max(np.abs(o_ref)))
+    assert np.max(np.abs(S - S_ref)) <= 1e-12 * max(1, np.max(np.abs(S_ref)))

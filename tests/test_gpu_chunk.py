@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 
 from tests.gpu_util import TOL, check, gpu_chunk, need_gpu, oracle_chunk, say
+from tests.report import report
 from workloads import CONFIGS, Workload, chunk_inputs
 
 pytestmark = pytest.mark.gpu
@@ -32,7 +33,13 @@ def _run(wl, form="page"):
 
 def test_config1_deltanet_fp32():
     """DeltaNet, B1 H1 T256 d64, fp32 I/O (the small workload, whole tensor)."""
-    _run(CONFIGS[1])
+    need_gpu()
+    wl = CONFIGS[1]
+    inp = chunk_inputs(wl)
+    o, S = gpu_chunk(inp, wl.io)
+    o_ref, S_ref = oracle_chunk(inp)
+    e_o, e_s = check("o", o, o_ref, TOL["f32"]), check("S_T", S, S_ref, TOL["f32"])
+    report(f"{wl.name}: whole-tensor rel_l2 o {e_o:.3e}  S_T {e_s:.3e}")
 
 
 @pytest.mark.parametrize("gate", ["none", "scalar", "channel"])
@@ -163,8 +170,11 @@ def test_full_workload_whole_tensor(cfg):
     assert np.isfinite(o_h).all() and np.isfinite(S_h).all()
     say("  oracle on every slice")
     r = whole_chunk(wl, o_h, S_h, group=2 if cfg == 4 else 4)
-    say(f"  whole-tensor rel_l2 o {r['o']:.3e}  S_T {r['S']:.3e}; worst slice o {r['worst_o']}  "
-        f"S_T {r['worst_S']}; {r['slices']} slices on {r['procs']} processes in {r['seconds']:.1f} s")
+    line = (f"{wl.name}: whole-tensor rel_l2 o {r['o']:.3e}  S_T {r['S']:.3e}; worst (b, h, rel_l2) o "
+            f"({r['worst_o'][0]}, {r['worst_o'][1]}, {r['worst_o'][2]:.3e})  S_T ({r['worst_S'][0]}, {r['worst_S'][1]}, "
+            f"{r['worst_S'][2]:.3e}); {r['slices']} slices on {r['procs']} processes in {r['seconds']:.1f} s")
+    say("  " + line)
+    report(line)
     assert r["o"] <= TOL[wl.io] and r["S"] <= TOL[wl.io]
     assert r["worst_o"][2] <= TOL[wl.io] and r["worst_S"][2] <= TOL[wl.io]
 

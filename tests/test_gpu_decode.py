@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 
 from tests.gpu_util import TOL, check, dev, host, need_gpu, say
+from tests.report import report
 from workloads import DECODE_CONFIG, decode_inputs
 
 pytestmark = pytest.mark.gpu
@@ -95,5 +96,8 @@ def test_decode_workload_all_sequences_100_steps():
     del o_all, S, dq, dk, dvv, db, dla
     say("  oracle on every state")
     r = whole_decode(wl, steps, o_h, S_h)
-    say(f"  rel_l2 o (all steps) {r['o']:.3e}  S (final) {r['S']:.3e}; {r['procs']} processes, {r['seconds']:.1f} s")
+    line = (f"{wl.name}, all {wl.N * wl.H} states x {steps} steps: rel_l2 o (all steps) {r['o']:.3e}  "
+            f"S (final) {r['S']:.3e}; {r['procs']} processes, {r['seconds']:.1f} s")
+    say("  " + line)
+    report(line)
     assert r["o"] <= TOL[wl.io] and r["S"] <= 1e-4

@@ -19,8 +19,8 @@ from workloads.inputs import round_to_io
 pytestmark = pytest.mark.gpu
 
 
-def _wkey_inputs(B, T, H, dk, dv, seed, io="bf16", s0=0.02):
-    inp = chunk_inputs(Workload("wkey", B=B, T=T, H=H, d_k=dk, d_v=dv, io=io, gate="none", s0_std=s0, seed=seed))
+def _wkey_inputs(B, T, H, dk, dv, seed, io="bf16", s0=0.02, gate="none"):
+    inp = chunk_inputs(Workload("wkey", B=B, T=T, H=H, d_k=dk, d_v=dv, io=io, gate=gate, s0_std=s0, seed=seed))
     d = np.random.default_rng([seed, 7]).uniform(0.2, 2.0, inp["k"].shape)
     inp["kw"] = round_to_io(d * inp["k"], io)
     return inp
@@ -94,4 +94,81 @@ def test_write_key_prefill_then_decode():
     torch.cuda.synchronize()
     o_ref, S_ref = oracle_forward(inp["q"], inp["k"], inp["v"], inp["beta"], None, inp["S0"], kw=inp["kw"])
     check("decode o", np.stack(outs, axis=1), o_ref[:, T0:], TOL["bf16"])
+    check("S", host(S), S_ref, TOL["bf16"])
+
+
+# ---- the write key with a gate ("OSDN", §4: the preconditioner on gated backbones) -------
+@pytest.mark.parametrize("form", ["page", "literal"])
+@pytest.mark.parametrize("gate,shape", [("scalar", (2, 200, 3, 128, 128)), ("scalar", (1, 130, 2, 64, 128)),
+                                        ("scalar", (2, 130, 64, 128, 128)), ("channel", (2, 200, 3, 128, 128)),
+                                        ("channel", (1, 65, 2, 128, 64)), ("channel", (1, 1, 2, 128, 128))],
+                         ids=lambda x: x if isinstance(x, str) else "B%dT%dH%d_dk%d_dv%d" % x)
+def test_write_key_chunk_fwd_gated(gate, shape, form):
+    need_gpu()
+    import torch
+    import gated_delta_rule_21_amd as gdr
+    B, T, H, dk, dv = shape
+    say(f"case write key, gate={gate}, {shape}, form={form}")
+    inp = _wkey_inputs(B, T, H, dk, dv, seed=211 + T + H, gate=gate)
+    o, S = gdr.chunk_fwd(*(dev(inp[n], "bf16") for n in ("q", "k", "v", "beta", "log_a")),
+                         torch.from_numpy(inp["S0"]).cuda(), kw=dev(inp["kw"], "bf16"), form=form)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_forward(inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_a"], inp["S0"], kw=inp["kw"],
+                                  form=form)
+    check("o", host(o), o_ref, TOL["bf16"])
+    check("S_T", host(S), S_ref, TOL["bf16"])
+
+
+def test_write_key_channel_gate_fast_forgetting():
+    """A per-channel block past the transform's split range with a write key: the
+    generic kernel pairs k with kw as the split-factor transform does."""
+    need_gpu()
+    import torch
+    import gated_delta_rule_21_amd as gdr
+    inp = _wkey_inputs(1, 200, 2, 128, 128, seed=223, gate="channel")
+    inp["log_a"][0, 70:95, 1, 20:60] = -6.0
+    o, S = gdr.chunk_fwd(*(dev(inp[n], "bf16") for n in ("q", "k", "v", "beta", "log_a")),
+                         torch.from_numpy(inp["S0"]).cuda(), kw=dev(inp["kw"], "bf16"))
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_forward(inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_a"], inp["S0"], kw=inp["kw"])
+    check("o", host(o), o_ref, TOL["bf16"])
+    check("S_T", host(S), S_ref, TOL["bf16"])
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+@pytest.mark.parametrize("form", ["page", "literal"])
+def test_write_key_decode_step_gated(io, gate, form):
+    need_gpu()
+    import torch
+    import gated_delta_rule_21_amd as gdr
+    inp = _wkey_inputs(16, 1, 4, 128, 128, seed=227, io=io, s0=0.05, gate=gate)
+    st = {n: np.ascontiguousarray(inp[n][:, 0]) for n in ("q", "k", "v", "beta", "kw", "log_a")}
+    S = torch.from_numpy(inp["S0"]).cuda()
+    o, S_new = gdr.recurrent_step(*(dev(st[n], io) for n in ("q", "k", "v", "beta", "log_a")), S,
+                                  S_new=torch.empty_like(S), kw=dev(st["kw"], io), form=form)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_step(inp["S0"], st["q"], st["k"], st["v"], st["beta"], st["log_a"], kw=st["kw"], form=form)
+    check("o", host(o), o_ref, TOL[io])
+    check("S_new", host(S_new), S_ref, TOL[io])
+
+
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+def test_write_key_gated_prefill_then_decode(gate):
+    need_gpu()
+    import torch
+    import gated_delta_rule_21_amd as gdr
+    inp = _wkey_inputs(2, 133, 2, 128, 128, seed=229, gate=gate)
+    T0 = 130
+    part = lambda n, sl: np.ascontiguousarray(inp[n][:, sl])
+    o, S = gdr.chunk_fwd(*(dev(part(n, slice(0, T0)), "bf16") for n in ("q", "k", "v", "beta", "log_a")),
+                         torch.from_numpy(inp["S0"]).cuda(), kw=dev(part("kw", slice(0, T0)), "bf16"))
+    outs = [host(o)]
+    for t in range(T0, 133):
+        ot, S = gdr.recurrent_step(*(dev(part(n, t), "bf16") for n in ("q", "k", "v", "beta", "log_a")), S,
+                                   kw=dev(part("kw", t), "bf16"))
+        outs.append(host(ot)[:, None])
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_forward(inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_a"], inp["S0"], kw=inp["kw"])
+    check("o (prefill and decode)", np.concatenate(outs, axis=1), o_ref, TOL["bf16"])
     check("S", host(S), S_ref, TOL["bf16"])
