@@ -402,7 +402,9 @@ def bench_wkey(args, log, wl, q, k, v, beta, kw, scan_us):
             "forward_us": round(ms * 1e3, 2), "scan_us": scan_us,
             "tokens_per_s": round(wl.B * wl.T / (total_ms * 1e-3), 1),
             "forward_roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                 "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+                                 "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                 "traffic": profiled_traffic("chunk_fwd_wkey_b8h16t8192d128_counters.md", CHUNK_SOURCES)
+                                 if (wl.B, wl.T, wl.H, wl.d_k) == (8, 8192, 16, 128) else None},
             "forward_bytes_per_launch": nbytes}
 
 

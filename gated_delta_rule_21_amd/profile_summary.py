@@ -92,7 +92,7 @@ def pick(vals, sub: str):
 
 def counters(fetch_csv: str, write_csv: str, kernels: str, algorithmic: float, command: str,
              digest: str) -> str:
-    """`kernels`: name substrings separated by ';' (or by ',' when there is no ';'); the
+    """`kernels`: name substrings separated by ';' (template names hold commas); the
     traffic of one call of the operation is the sum over them (each kernel runs once
     per call)."""
     f = per_dispatch(fetch_csv, "FETCH_SIZE")
@@ -111,7 +111,7 @@ def counters(fetch_csv: str, write_csv: str, kernels: str, algorithmic: float, c
            f"| read scale (bytes per counted byte) | {sf:.4f} |",
            f"| write scale (bytes per counted byte) | {sw:.4f} |"]
     tot = 0.0
-    for k in kernels.split(";" if ";" in kernels else ","):
+    for k in kernels.split(";"):
         kf, kw = pick(f, k), pick(w, k)
         if not (kf and kw):
             raise SystemExit(f"missing dispatches of {k}")
@@ -197,7 +197,7 @@ def main(argv=None):
     b = sub.add_parser("counters")
     b.add_argument("fetch_csv")
     b.add_argument("write_csv")
-    b.add_argument("--kernel", required=True, help="name substring, or several separated by ';' (or ',')")
+    b.add_argument("--kernel", required=True, help="name substring, or several separated by ';'")
     b.add_argument("--algorithmic-bytes", type=float, required=True)
     b.add_argument("--command", required=True)
     b.add_argument("--digest", default="", help="source digest to record (default: the current sources')")
