@@ -373,8 +373,19 @@ def bench_bwd(prep, args, log, wl, q, k, v, beta, log_a, S0):
     flops = bwd_algorithmic(wl)
     tf = flops / (ms * 1e-3) / 1e12
     log(f"chunk backward: {ms:.3f} ms/step, {tf:.1f} TFLOP/s useful")
+    wk_ms = None
+    if wl.gate in ("none", "scalar"):
+        # the backward with a separate write key (the preconditioned rule's training
+        # step); a copy of k stands for it, since the kernels' work does not depend on
+        # its values
+        kw = k.clone()
+        wk_ms = time_calls(lambda i: gdr.chunk_bwd(q, k, v, beta, log_a, S0, dO, dS_T, workspace=ws, kw=kw),
+                           args.warmup, args.steps)
+        del kw
+        log(f"chunk backward with a write key: {wk_ms:.3f} ms/step")
     return {"workload": wl.name + "_backward", "value": round(wl.B * wl.T / (ms * 1e-3), 1), "unit": "tokens/s",
             "ms_per_launch": round(ms, 4), "useful_flops_per_launch": flops,
+            "write_key_ms_per_launch": None if wk_ms is None else round(wk_ms, 4),
             "algorithmic_bytes_per_launch": bwd_bytes(wl, S0 is not None),
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf / BF16_PEAK_TFLOPS, 4),

@@ -25,7 +25,7 @@ FORMS = {"page": 0, "literal": 1}
 EXPORTED = ("gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_chunk_fwd_varlen_workspace_size",
             "gdr_chunk_fwd_varlen", "gdr_recurrent_step", "gdr_chunk_fwd_wkey", "gdr_recurrent_step_wkey",
             "gdr_precond_scan", "gdr_status_string", "gdr_last_error", "gdr_version",
-            "gdr_chunk_bwd_workspace_size", "gdr_chunk_bwd", "gdr_chunk_bwd_varlen_workspace_size",
+            "gdr_chunk_bwd_workspace_size", "gdr_chunk_bwd", "gdr_chunk_bwd_wkey", "gdr_chunk_bwd_varlen_workspace_size",
             "gdr_chunk_bwd_varlen", "gdr_chunk_fwd_noalloc")
 
 
@@ -82,6 +82,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         lib.gdr_chunk_bwd_workspace_size.argtypes = [ctypes.POINTER(GdrDesc), ctypes.POINTER(ctypes.c_size_t)]
         lib.gdr_chunk_bwd.restype = ctypes.c_int
         lib.gdr_chunk_bwd.argtypes = [ctypes.POINTER(GdrDesc)] + [vp] * 15 + [ctypes.c_size_t, vp]
+        lib.gdr_chunk_bwd_wkey.restype = ctypes.c_int
+        lib.gdr_chunk_bwd_wkey.argtypes = [ctypes.POINTER(GdrDesc)] + [vp] * 17 + [ctypes.c_size_t, vp]
         lib.gdr_chunk_bwd_varlen_workspace_size.restype = ctypes.c_int
         lib.gdr_chunk_bwd_varlen_workspace_size.argtypes = [ctypes.POINTER(GdrDesc), ctypes.c_int64,
                                                             ctypes.POINTER(ctypes.c_size_t)]
@@ -249,7 +251,7 @@ def chunk_bwd_workspace_size(B: int, T: int, H: int, d_k: int, d_v: int, dtype=t
 
 
 def chunk_bwd(q, k, v, beta, log_a, S0, dO, dS_T=None, *, cu_seqlens=None, form: str = "page", want_dS0: bool = True,
-              workspace=None, stream=None):
+              workspace=None, stream=None, kw=None):
     """gdr_chunk_bwd on torch tensors: the gradients of L = <dO, o> + <dS_T, S_T> for
     the forward chunk_fwd(q, k, v, beta, log_a, S0, form=form) (bf16 I/O; no gate, a
     scalar gate, or a per-channel gate with d_k = 128).  dO [B, T, H, d_v] bf16; dS_T None or
@@ -257,7 +259,9 @@ def chunk_bwd(q, k, v, beta, log_a, S0, dO, dS_T=None, *, cu_seqlens=None, form:
     the sequences are packed along T of [1, T, H, .] tensors (gdr_chunk_bwd_varlen)
     and S0, dS_T, dS0 are [n_seq, H, d_k, d_v].  Returns dict(dq, dk, dv, dbeta,
     dlog_a, dS0) (dlog_a None without a gate, dS0 None when want_dS0 is False).
-    Asynchronous on the current (or given) stream."""
+    `kw` ([B, T, H, d_k] bf16, fixed-length batches, no gate or a scalar gate) is the
+    forward's write key (gdr_chunk_bwd_wkey): then dk is the read side's gradient and
+    the dict also holds dkw.  Asynchronous on the current (or given) stream."""
     lib = load()
     B, T, H, dk = k.shape
     dv = v.shape[-1]
@@ -284,6 +288,10 @@ def chunk_bwd(q, k, v, beta, log_a, S0, dO, dS_T=None, *, cu_seqlens=None, form:
         _require(S0, "S0", torch.float32, (nstate, H, dk, dv))
     if dS_T is not None:
         _require(dS_T, "dS_T", torch.float32, (nstate, H, dk, dv))
+    if kw is not None:
+        if packed:
+            raise ValueError("the write-key backward takes fixed-length batches")
+        _require(kw, "kw", dt, (B, T, H, dk))
     out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v), dbeta=torch.empty_like(beta),
                dlog_a=torch.empty_like(log_a) if log_a is not None else None,
                dS0=torch.empty((nstate, H, dk, dv), dtype=torch.float32, device=q.device) if want_dS0 else None)
@@ -300,7 +308,13 @@ def chunk_bwd(q, k, v, beta, log_a, S0, dO, dS_T=None, *, cu_seqlens=None, form:
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_a), _ptr(S0), _ptr(dO), _ptr(dS_T), _ptr(out["dq"]),
             _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dbeta"]), _ptr(out["dlog_a"]), _ptr(out["dS0"]),
             _ptr(workspace), workspace.numel(), _stream_handle(stream))
-    if packed:
+    if kw is not None:
+        out["dkw"] = torch.empty_like(k)
+        st = lib.gdr_chunk_bwd_wkey(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(kw), _ptr(v), _ptr(beta), _ptr(log_a),
+                                    _ptr(S0), _ptr(dO), _ptr(dS_T), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dkw"]),
+                                    _ptr(out["dv"]), _ptr(out["dbeta"]), _ptr(out["dlog_a"]), _ptr(out["dS0"]),
+                                    _ptr(workspace), workspace.numel(), _stream_handle(stream))
+    elif packed:
         st = lib.gdr_chunk_bwd_varlen(ctypes.byref(desc), _ptr(cu_seqlens), nstate, *args)
     else:
         st = lib.gdr_chunk_bwd(ctypes.byref(desc), *args)
@@ -433,12 +447,12 @@ class _ChunkAttn(torch.autograd.Function):
     """chunk_fwd with chunk_bwd as its backward (marshalling only)."""
 
     @staticmethod
-    def forward(ctx, q, k, v, beta, log_a, S0, cu_seqlens, form):
+    def forward(ctx, q, k, v, beta, log_a, S0, cu_seqlens, form, kw):
         if cu_seqlens is not None:
             o, S_T = chunk_fwd_varlen(q, k, v, beta, log_a, cu_seqlens, S0, form=form)
         else:
-            o, S_T = chunk_fwd(q, k, v, beta, log_a, S0, form=form)
-        ctx.save_for_backward(q, k, v, beta, log_a, S0, cu_seqlens)
+            o, S_T = chunk_fwd(q, k, v, beta, log_a, S0, form=form, kw=kw)
+        ctx.save_for_backward(q, k, v, beta, log_a, S0, cu_seqlens, kw)
         ctx.form = form
         ctx.gated = log_a is not None
         ctx.has_S0 = S0 is not None
@@ -446,16 +460,20 @@ class _ChunkAttn(torch.autograd.Function):
 
     @staticmethod
     def backward(ctx, dO, dS_T):
-        q, k, v, beta, log_a, S0, cu_seqlens = ctx.saved_tensors
+        q, k, v, beta, log_a, S0, cu_seqlens, kw = ctx.saved_tensors
         dO = torch.zeros_like(v) if dO is None else dO.to(v.dtype).contiguous()
         dS_T = None if dS_T is None else dS_T.float().contiguous()
-        g = chunk_bwd(q, k, v, beta, log_a, S0, dO, dS_T, cu_seqlens=cu_seqlens, form=ctx.form, want_dS0=ctx.has_S0)
+        g = chunk_bwd(q, k, v, beta, log_a, S0, dO, dS_T, cu_seqlens=cu_seqlens, form=ctx.form, want_dS0=ctx.has_S0,
+                      kw=kw)
         return (g["dq"], g["dk"], g["dv"], g["dbeta"], g["dlog_a"] if ctx.gated else None,
-                g["dS0"] if ctx.has_S0 else None, None, None)
+                g["dS0"] if ctx.has_S0 else None, None, None, g.get("dkw"))
 
 
-def chunk_attn(q, k, v, beta, log_a=None, S0=None, cu_seqlens=None, form: str = "page"):
+def chunk_attn(q, k, v, beta, log_a=None, S0=None, cu_seqlens=None, form: str = "page", kw=None):
     """(o, S_T) of chunk_fwd (or chunk_fwd_varlen with cu_seqlens) as a torch autograd
     function whose backward is chunk_bwd: bf16, any gate (per-channel with d_k = 128),
-    either form.  Gradients flow to q, k, v, beta, log_a and S0."""
-    return _ChunkAttn.apply(q, k, v, beta, log_a, S0, cu_seqlens, form)
+    either form.  Gradients flow to q, k, v, beta, log_a and S0, and to the write key
+    `kw` when one is given (fixed-length batches, no gate or a scalar gate)."""
+    if kw is not None and (cu_seqlens is not None or (log_a is not None and log_a.dim() == 4)):
+        raise ValueError("chunk_attn with a write key: fixed-length batches, no gate or a scalar gate")
+    return _ChunkAttn.apply(q, k, v, beta, log_a, S0, cu_seqlens, form, kw)

@@ -1,6 +1,10 @@
 // Backward pass of the chunkwise gated delta rule on gfx950: bf16 I/O, no gate or a
 // scalar gate, decay before the erase (g_read = g below) or erase on the undecayed
-// state (g_read_r = g_{r-1}, the A factor and the residual's decay read g_read).
+// state (g_read_r = g_{r-1}, the A factor and the residual's decay read g_read),
+// optionally with a separate write key ("OSDN: Improving Delta Rule with Provable
+// Online Preconditioning in Linear Attention", §2.1: the erase reads along k, the
+// write goes along kw; below, the column side of A and P, dDelta's key product and
+// the state write then take KW, see bwd_chunk_kernel).
 //
 // The pages print no gradients; these are the reverse-mode derivatives of the
 // chunk form of "Moonshot AI's New Attention Architecture: Key Innovations
@@ -54,7 +58,9 @@ namespace {
 // the factors) and P of the chunk.  Pass 1 reads k both ways, v and T^T transposed;
 // pass 2 reads k and q both ways, dO and P transposed, T^T by rows.
 // ---------------------------------------------------------------------------
-template <int DK, bool REV, bool CHAN = false>
+// KD: a third key tile, the operand of the state update (pass 1) and of dDelta's key
+// product (pass 2): k e^{g_63 - g} from the record (per-channel gate), or the write key.
+template <int DK, bool REV, bool KD = false>
 struct SeqLayout {
   static constexpr int LDK = ld_both(DK);
   static constexpr int LDV = ld_tr(64);
@@ -65,7 +71,7 @@ struct SeqLayout {
   static constexpr size_t TB = size_t(CH) * LCT * 2;
   static constexpr size_t O_K = 0, O_Q = O_K + KB, O_V = O_Q + (REV ? KB : 0), O_T = O_V + VB, O_F = O_T + TB;
   static constexpr size_t O_KD = O_F + 6 * CH * 4;   // per-channel gate: k e^{g_63 - g}
-  static constexpr size_t BUF = O_KD + (CHAN ? KB : 0);
+  static constexpr size_t BUF = O_KD + (KD ? KB : 0);
   static constexpr size_t O_P = (REV ? 1 : 2) * BUF;
   static constexpr size_t TOTAL = O_P + (REV ? size_t(CH) * LCP * 2 : 0);
 };
@@ -73,20 +79,21 @@ struct SeqLayout {
 // One chunk's tiles in registers, then into one LDS copy: k (and q), the 64-column
 // tile of v (or dO) from column col0, the T blocks and the factor rows of the record.
 // Per-channel gate: k e^{g_read}, q e^{g} and k e^{g_63 - g} from the record in place
-// of k and q, and (pass 2) the record's P.
-template <int DK, int NT, bool WITH_Q, bool CHAN = false>
+// of k and q, and (pass 2) the record's P.  With a write key (WK) its tile is the
+// third key tile.
+template <int DK, int NT, bool WITH_Q, bool CHAN = false, bool WK = false>
 struct SeqStage {
-  typedef SeqLayout<DK, WITH_Q, CHAN> L;
+  typedef SeqLayout<DK, WITH_Q, CHAN || WK> L;
   static constexpr uint32_t RB = rec_bytes(IO_BF16, CHAN ? GATE_CHANNEL : GATE_SCALAR, DK);
   static constexpr int KR = DK / 8;                  // 16-byte pieces per k row
   static constexpr int KP = CH * KR / NT;            // per thread
   static constexpr int VP = CH * 8 / NT;
   static constexpr int TP = (10 * 32 + NT - 1) / NT; // T blocks: 32 pieces each
   static_assert(KP * NT == CH * KR && VP * NT == CH * 8, "tile pieces split evenly");
-  u32x4 k[KP], q[WITH_Q ? KP : 1], kd[CHAN ? KP : 1], v[VP], t[TP], pp[CHAN && WITH_Q ? TP : 1], f;
+  u32x4 k[KP], q[WITH_Q ? KP : 1], kd[CHAN || WK ? KP : 1], v[VP], t[TP], pp[CHAN && WITH_Q ? TP : 1], f;
 
-  __device__ __forceinline__ void load(rsrc_t rk, rsrc_t rq, rsrc_t rv, rsrc_t rw, int64_t n, int tid, int H,
-                                       int dv, int col0) {
+  __device__ __forceinline__ void load(rsrc_t rk, rsrc_t rq, rsrc_t rv, rsrc_t rw, rsrc_t rkw, int64_t n, int tid,
+                                       int H, int dv, int col0) {
     const uint32_t sk = static_cast<uint32_t>(n * CH * H * DK * 2);
     const uint32_t sv = static_cast<uint32_t>(n * CH * H * dv * 2);
     const uint32_t sw = static_cast<uint32_t>(n * RB);
@@ -102,6 +109,7 @@ struct SeqStage {
         const uint32_t off = static_cast<uint32_t>(((pc / KR) * H * DK + (pc % KR) * 8) * 2);
         k[i] = buf_load16(rk, off, sk);
         if constexpr (WITH_Q) q[i] = buf_load16(rq, off, sk);
+        if constexpr (WK) kd[i] = buf_load16(rkw, off, sk);
       }
     }
 #pragma unroll
@@ -129,7 +137,7 @@ struct SeqStage {
       const int pc = tid + i * NT;
       put16(dK + (pc / KR) * L::LDK + (pc % KR) * 8, k[i]);
       if constexpr (WITH_Q) put16(dQ + (pc / KR) * L::LDK + (pc % KR) * 8, q[i]);
-      if constexpr (CHAN) put16(reinterpret_cast<T*>(base + L::O_KD) + (pc / KR) * L::LDK + (pc % KR) * 8, kd[i]);
+      if constexpr (CHAN || WK) put16(reinterpret_cast<T*>(base + L::O_KD) + (pc / KR) * L::LDK + (pc % KR) * 8, kd[i]);
     }
 #pragma unroll
     for (int i = 0; i < VP; ++i) {
@@ -153,12 +161,13 @@ struct SeqStage {
 };
 
 // Pass 1: the state entering every chunk, stored in bf16 value-major.  lb is the
-// workgroup's (sequence, head, tile) index.
-template <int GATE, int DK>
+// workgroup's (sequence, head, tile) index.  With a write key (WK) the update writes
+// along it: S' = e^{g_63} S + KW^T (e^{g_63 - g} Delta).
+template <int GATE, int DK, bool WK>
 __device__ __forceinline__ void states_pass(const BwdParams& p, int n_tiles, int lb, char* smem) {
   constexpr bool CHAN = GATE == GATE_CHANNEL;
   constexpr uint32_t RB = rec_bytes(IO_BF16, GATE, DK);
-  typedef SeqLayout<DK, false, CHAN> L;
+  typedef SeqLayout<DK, false, CHAN || WK> L;
   constexpr int DKT = DK / 16, LDK = L::LDK, LDV = L::LDV, LCT = L::LCT;
   const ChunkParams& f = p.f;
   const int64_t bh = lb / n_tiles;
@@ -172,7 +181,7 @@ __device__ __forceinline__ void states_pass(const BwdParams& p, int n_tiles, int
   const BwdSeq sq = bwd_seq_of(f, bb, hh);
   const int64_t nch = sq.nch;
   const Slice sl = sq.sl;
-  const rsrc_t rk = sl.rs(f.k, DK), rv = sl.rs(f.v, dv);
+  const rsrc_t rk = sl.rs(f.k, DK), rv = sl.rs(f.v, dv), rkw = WK ? sl.rs(f.kw, DK) : rk;
   const rsrc_t rw = make_rsrc(static_cast<const char*>(f.ws) + sq.rec0 * RB, static_cast<uint32_t>(nch * RB));
   const uint32_t sbytes = static_cast<uint32_t>(dv * DK * 2);   // one chunk's state
   const rsrc_t rst = make_rsrc(static_cast<char*>(p.states) + sq.rec0 * sbytes, static_cast<uint32_t>(nch * sbytes));
@@ -183,11 +192,11 @@ __device__ __forceinline__ void states_pass(const BwdParams& p, int n_tiles, int
 #pragma unroll
     for (int s = 0; s < 4; ++s) S[t][s] = f.S0 ? f.S0[(bh * DK + 16 * t + 4 * lg + s) * dv + scol] : 0.f;
 
-  SeqStage<DK, 256, false, CHAN> st;
+  SeqStage<DK, 256, false, CHAN, WK> st;
   if (nch > 0) {
-    st.load(rk, rk, rv, rw, 0, tid, H, dv, col0);
+    st.load(rk, rk, rv, rw, rkw, 0, tid, H, dv, col0);
     st.store(smem, tid);
-    if (nch > 1) st.load(rk, rk, rv, rw, 1, tid, H, dv, col0);
+    if (nch > 1) st.load(rk, rk, rv, rw, rkw, 1, tid, H, dv, col0);
   }
   __syncthreads();
   for (int64_t n = 0; n < nch; ++n) {
@@ -195,11 +204,11 @@ __device__ __forceinline__ void states_pass(const BwdParams& p, int n_tiles, int
     const T* sK = reinterpret_cast<const T*>(cur + L::O_K);
     const T* sV = reinterpret_cast<const T*>(cur + L::O_V);
     const T* sT = reinterpret_cast<const T*>(cur + L::O_T);
-    const T* sKD = reinterpret_cast<const T*>(cur + (CHAN ? L::O_KD : L::O_K));   // K^T of the update
+    const T* sKD = reinterpret_cast<const T*>(cur + (CHAN || WK ? L::O_KD : L::O_K));   // K^T of the update
     const float* sF = reinterpret_cast<const float*>(cur + L::O_F);
     if (n + 1 < nch) {   // the other copy was last read before the previous barrier
       st.store(smem + ((n + 1) & 1) * L::BUF, tid);
-      if (n + 2 < nch) st.load(rk, rk, rv, rw, n + 2, tid, H, dv, col0);
+      if (n + 2 < nch) st.load(rk, rk, rv, rw, rkw, n + 2, tid, H, dv, col0);
     }
     const uint32_t so = static_cast<uint32_t>(n) * sbytes;
 #pragma unroll
@@ -259,12 +268,13 @@ __device__ __forceinline__ void states_pass(const BwdParams& p, int n_tiles, int
 
 // Pass 2: the gradient of the state leaving every chunk, last chunk first, and dS0.
 // One LDS copy of the chunk's tiles: the next chunk waits in registers and goes
-// in after the step's last read.
-template <int GATE, int DK>
+// in after the step's last read.  With a write key (WK) P and dDelta's key product
+// take it: P = lower_incl(D * Q KW^T), dDelta = diag(e^{g_63 - g}) KW dS' + P^T dO.
+template <int GATE, int DK, bool WK>
 __device__ __forceinline__ void reverse_pass(const BwdParams& p, int n_tiles, int lb, char* smem) {
   constexpr bool CHAN = GATE == GATE_CHANNEL;
   constexpr uint32_t RB = rec_bytes(IO_BF16, GATE, DK);
-  typedef SeqLayout<DK, true, CHAN> L;
+  typedef SeqLayout<DK, true, CHAN || WK> L;
   constexpr int DKT = DK / 16, LDK = L::LDK, LDV = L::LDV, LCT = L::LCT, LCP = L::LCP;
   const ChunkParams& f = p.f;
   const int64_t bh = lb / n_tiles;
@@ -278,7 +288,7 @@ __device__ __forceinline__ void reverse_pass(const BwdParams& p, int n_tiles, in
   const BwdSeq sq = bwd_seq_of(f, bb, hh);
   const int64_t nch = sq.nch;
   const Slice sl = sq.sl;
-  const rsrc_t rk = sl.rs(f.k, DK), rq = sl.rs(f.q, DK), rdo = sl.rs(p.dO, dv);
+  const rsrc_t rk = sl.rs(f.k, DK), rq = sl.rs(f.q, DK), rdo = sl.rs(p.dO, dv), rkw = WK ? sl.rs(f.kw, DK) : rk;
   const rsrc_t rw = make_rsrc(static_cast<const char*>(f.ws) + sq.rec0 * RB, static_cast<uint32_t>(nch * RB));
   const uint32_t sbytes = static_cast<uint32_t>(dv * DK * 2);
   const rsrc_t rds = make_rsrc(static_cast<char*>(p.dstates) + sq.rec0 * sbytes, static_cast<uint32_t>(nch * sbytes));
@@ -290,20 +300,20 @@ __device__ __forceinline__ void reverse_pass(const BwdParams& p, int n_tiles, in
 #pragma unroll
     for (int s = 0; s < 4; ++s) dS[t][s] = p.dS_T ? p.dS_T[(bh * DK + 16 * t + 4 * lg + s) * dv + scol] : 0.f;
 
-  SeqStage<DK, 256, true, CHAN> st;
+  SeqStage<DK, 256, true, CHAN, WK> st;
   if (nch > 0) {
-    st.load(rk, rq, rdo, rw, nch - 1, tid, H, dv, col0);
+    st.load(rk, rq, rdo, rw, rkw, nch - 1, tid, H, dv, col0);
     st.store(smem, tid);
   }
   __syncthreads();
-  if (nch > 1) st.load(rk, rq, rdo, rw, nch - 2, tid, H, dv, col0);
+  if (nch > 1) st.load(rk, rq, rdo, rw, rkw, nch - 2, tid, H, dv, col0);
   for (int64_t n = nch - 1; n >= 0; --n) {
     const char* cur = smem;
     const T* sK = reinterpret_cast<const T*>(cur + L::O_K);
     const T* sQ = reinterpret_cast<const T*>(cur + L::O_Q);
     const T* sO = reinterpret_cast<const T*>(cur + L::O_V);
     const T* sT = reinterpret_cast<const T*>(cur + L::O_T);
-    const T* sKD = reinterpret_cast<const T*>(cur + (CHAN ? L::O_KD : L::O_K));   // rows of dDelta's K
+    const T* sKD = reinterpret_cast<const T*>(cur + (CHAN || WK ? L::O_KD : L::O_K));   // rows of dDelta's K
     const float* sF = reinterpret_cast<const float*>(cur + L::O_F);
     // P of this chunk, blocks u = wave, wave + 4, .. (row form: row 16R + lr); the
     // per-channel gate's P came with the tiles
@@ -313,7 +323,7 @@ __device__ __forceinline__ void reverse_pass(const BwdParams& p, int n_tiles, in
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < DK / 32; ++kb)
-        acc = O::mma2(acc, rowf(sK, LDK, 16 * J, 32 * kb, lr, lg), rowf(sK, LDK, 16 * J, 32 * kb + 16, lr, lg),
+        acc = O::mma2(acc, rowf(sKD, LDK, 16 * J, 32 * kb, lr, lg), rowf(sKD, LDK, 16 * J, 32 * kb + 16, lr, lg),
                       rowf(sQ, LDK, 16 * R, 32 * kb, lr, lg), rowf(sQ, LDK, 16 * R, 32 * kb + 16, lr, lg));
       const int r = 16 * R + lr;
 #pragma unroll
@@ -401,7 +411,7 @@ __device__ __forceinline__ void reverse_pass(const BwdParams& p, int n_tiles, in
     __syncthreads();                    // this chunk's tiles and P are read
     if (n >= 1) {
       st.store(smem, tid);              // chunk n - 1, loaded during this step
-      if (n >= 2) st.load(rk, rq, rdo, rw, n - 2, tid, H, dv, col0);
+      if (n >= 2) st.load(rk, rq, rdo, rw, rkw, n - 2, tid, H, dv, col0);
       __syncthreads();
     }
   }
@@ -414,15 +424,15 @@ __device__ __forceinline__ void reverse_pass(const BwdParams& p, int n_tiles, in
 }
 
 // Passes 1 and 2 in one launch of 2 nseq workgroups: the first nseq take pass 1.
-template <int GATE, int DK>
+template <int GATE, int DK, bool WK>
 __global__ __launch_bounds__(256) void bwd_seq_kernel(BwdParams p, int n_tiles, int nseq) {
-  constexpr bool CHAN = GATE == GATE_CHANNEL;
-  __shared__ __attribute__((aligned(16))) char smem[cmax(SeqLayout<DK, false, CHAN>::TOTAL, SeqLayout<DK, true, CHAN>::TOTAL)];
+  constexpr bool KD = GATE == GATE_CHANNEL || WK;
+  __shared__ __attribute__((aligned(16))) char smem[cmax(SeqLayout<DK, false, KD>::TOTAL, SeqLayout<DK, true, KD>::TOTAL)];
   const int b = blockIdx.x;
   const int role = b >= nseq;
   const int idx = b - role * nseq;
-  if (role == 0) states_pass<GATE, DK>(p, n_tiles, idx, smem);
-  else reverse_pass<GATE, DK>(p, n_tiles, idx, smem);
+  if (role == 0) states_pass<GATE, DK, WK>(p, n_tiles, idx, smem);
+  else reverse_pass<GATE, DK, WK>(p, n_tiles, idx, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -430,8 +440,10 @@ __global__ __launch_bounds__(256) void bwd_seq_kernel(BwdParams p, int n_tiles, 
 // halves of 64 (the products over d_v accumulate across them).
 // ---------------------------------------------------------------------------
 // Every tile here is read both ways except dDelta (transposed only), Delta and dY
-// (rows only).
-template <int DK>
+// (rows only).  With a write key (WK) its tile KW sits beside k; to make room,
+// beta D * dA and the partial sums, which are only written after the d_v loop, take
+// the place of dDelta, Delta and dY, which are only read inside it.
+template <int DK, bool WK = false>
 struct ChunkLayout {
   static constexpr int LDK = ld_both(DK);   // q, k, and the value-major states S^T, dS'^T
   static constexpr int LDV = ld_both(64);   // 64-column tiles: v then diag(beta) X, dO
@@ -441,10 +453,10 @@ struct ChunkLayout {
   static constexpr size_t KB = size_t(CH) * LDK * 2;
   static constexpr size_t VB = size_t(CH) * LDV * 2;
   static constexpr size_t CB = size_t(CH) * LCP * 2;
-  static constexpr size_t O_Q = 0, O_K = O_Q + KB, O_T = O_K + KB, O_F = O_T + CB;
+  static constexpr size_t O_Q = 0, O_K = O_Q + KB, O_KW = O_K + KB, O_T = O_KW + (WK ? KB : 0), O_F = O_T + CB;
   static constexpr size_t O_P = O_F + 6 * CH * 4;    // P, then D * dP
-  static constexpr size_t O_AK = O_P + CB;           // beta D * dA
-  static constexpr size_t O_V = O_AK + CB;           // v half, then diag(beta) X
+  static constexpr size_t O_AK0 = O_P + CB;          // beta D * dA (without a write key)
+  static constexpr size_t O_V = O_AK0 + (WK ? 0 : CB);   // v half, then diag(beta) X
   static constexpr size_t O_DO = O_V + VB;
   static constexpr size_t O_DD = O_DO + VB;          // dDelta
   static constexpr size_t O_DL = O_DD + size_t(CH) * LDD * 2;   // Delta
@@ -457,15 +469,24 @@ struct ChunkLayout {
   // A and of the P terms [4][64] each, column sums [4][64], and the row dots over
   // d_k tiles [DK / 16][64] twice (the terms of g_read and those of g); two per-wave
   // scalars [8] x 2.
-  static constexpr size_t O_RED = O_DS + KB;
   static constexpr size_t NRED = (4 + 4 + 4 + 4 + 4 + 2 * (DK / 16)) * CH + 16;
-  static constexpr size_t TOTAL = O_RED + NRED * 4;
+  static constexpr size_t O_AK = WK ? O_DD : O_AK0;
+  static constexpr size_t O_RED = WK ? O_AK + CB : O_DS + KB;
+  static constexpr size_t TOTAL = WK ? O_DS + KB : O_RED + NRED * 4;
+  static_assert(!WK || O_RED + NRED * 4 <= O_S, "the post-loop tiles fit in the loop-only ones");
 };
 
-// One workgroup per chunk (the LDS admits one per compute unit).
-template <int GATE, int DK, int DV>
+// One workgroup per chunk (the LDS admits one per compute unit).  With a write key
+// (WK) the column side of the Gram and score blocks, dDelta's key product and the
+// state write take KW, and the gradient of k splits into its read side (dk) and its
+// write side (dkw):
+//   dk  = (beta D * dA) KW - diag(beta e^{g_read}) dY S^T,
+//   dkw = (beta D * dA)^T K + (D * dP)^T Q + diag(e^{g_63 - g}) Delta dS'^T,
+//   dq  = (D * dP) KW + diag(e^g) dO S^T,
+// and the chunk-end row dot c_r takes kw_r.
+template <int GATE, int DK, int DV, bool WK>
 __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdParams p) {
-  typedef ChunkLayout<DK> L;
+  typedef ChunkLayout<DK, WK> L;
   constexpr int NT = 512, NW = 8;
   constexpr int DKT = DK / 16, LDK = L::LDK, LDV = L::LDV, LDD = L::LDD, LDR = L::LDR, LCP = L::LCP;
   constexpr int KR = DK / 8, KP = CH * KR / NT;     // pieces of a [64][DK] tile per thread
@@ -476,6 +497,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
   T* sQ = reinterpret_cast<T*>(smem + L::O_Q);
   T* sK = reinterpret_cast<T*>(smem + L::O_K);
+  T* sKW = reinterpret_cast<T*>(smem + (WK ? L::O_KW : L::O_K));   // the column-side key
   T* sT = reinterpret_cast<T*>(smem + L::O_T);
   const float* sF = reinterpret_cast<const float*>(smem + L::O_F);
   T* sP = reinterpret_cast<T*>(smem + L::O_P);
@@ -513,9 +535,9 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdParams p) {
   const Slice sl = sq.sl;
   {
     // q, k, the T blocks and the factor rows of the chunk
-    u32x4 hq[KP], hk[KP], ht, hf;
+    u32x4 hq[KP], hk[KP], hkw[WK ? KP : 1], ht, hf;
     {
-      const rsrc_t rq = sl.rs(f.q, DK), rk = sl.rs(f.k, DK);
+      const rsrc_t rq = sl.rs(f.q, DK), rk = sl.rs(f.k, DK), rkw = WK ? sl.rs(f.kw, DK) : rk;
       const rsrc_t rw = make_rsrc(static_cast<const char*>(f.ws) + sq.rec0 * W::BYTES, static_cast<uint32_t>(nch * W::BYTES));
       const uint32_t sk = static_cast<uint32_t>(n * CH * H * DK * 2), sw = static_cast<uint32_t>(n * W::BYTES);
 #pragma unroll
@@ -524,12 +546,14 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdParams p) {
         const uint32_t off = static_cast<uint32_t>(((pc / KR) * H * DK + (pc % KR) * 8) * 2);
         hq[i] = buf_load16(rq, off, sk);
         hk[i] = buf_load16(rk, off, sk);
+        if constexpr (WK) hkw[i] = buf_load16(rkw, off, sk);
       }
       if (tid < 320) ht = buf_load16(rw, W::T_OFF + static_cast<uint32_t>(tid * 16), sw);
       if (tid < 96) hf = buf_load16(rw, W::F_OFF + static_cast<uint32_t>(tid * 16), sw);
     }
     const rsrc_t rv = sl.rs(f.v, DV), rdo = sl.rs(p.dO, DV);
     const rsrc_t rdq = sl.rs(p.dq, DK), rdk = sl.rs(p.dk, DK), rdv = sl.rs(p.dv, DV);
+    const rsrc_t rdkw = WK ? sl.rs(p.dkw, DK) : rdk;
     const rsrc_t rdb = sl.rs(p.dbeta, 1), rdl = sl.rs(p.dlog_a, G ? 1 : 0);
     const rsrc_t rst = make_rsrc(static_cast<const char*>(p.states) + sq.rec0 * SBYTES, static_cast<uint32_t>(nch * SBYTES));
     const rsrc_t rds = make_rsrc(static_cast<const char*>(p.dstates) + sq.rec0 * SBYTES, static_cast<uint32_t>(nch * SBYTES));
@@ -576,6 +600,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdParams p) {
       const int pc = tid + i * NT;
       put16(sQ + (pc / KR) * LDK + (pc % KR) * 8, hq[i]);
       put16(sK + (pc / KR) * LDK + (pc % KR) * 8, hk[i]);
+      if constexpr (WK) put16(sKW + (pc / KR) * LDK + (pc % KR) * 8, hkw[i]);
     }
     if (tid < 320) {
       int R, J;
@@ -599,7 +624,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdParams p) {
         tri_block(u, R, J);
 #pragma unroll
         for (int kb = 0; kb < DK / 32; ++kb) {
-          const frag b0 = rowf(sK, LDK, 16 * J, 32 * kb, lr, lg), b1 = rowf(sK, LDK, 16 * J, 32 * kb + 16, lr, lg);
+          const frag b0 = rowf(sKW, LDK, 16 * J, 32 * kb, lr, lg), b1 = rowf(sKW, LDK, 16 * J, 32 * kb + 16, lr, lg);
           Gr[i] = O::mma2(Gr[i], b0, b1, rowf(sK, LDK, 16 * R, 32 * kb, lr, lg), rowf(sK, LDK, 16 * R, 32 * kb + 16, lr, lg));
           QKr[i] = O::mma2(QKr[i], b0, b1, rowf(sQ, LDK, 16 * R, 32 * kb, lr, lg), rowf(sQ, LDK, 16 * R, 32 * kb + 16, lr, lg));
         }
@@ -651,7 +676,11 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdParams p) {
             const int M = (wave >> 2) + 2 * i;
             const frag a0 = rowf(sK, LDK, 16 * M, 32 * kb, lr, lg), a1 = rowf(sK, LDK, 16 * M, 32 * kb + 16, lr, lg);
             KS2[i] = O::mma2(KS2[i], s0, s1, a0, a1);
-            KD2[i] = O::mma2(KD2[i], d0, d1, a0, a1);
+            if constexpr (WK)
+              KD2[i] = O::mma2(KD2[i], d0, d1, rowf(sKW, LDK, 16 * M, 32 * kb, lr, lg),
+                               rowf(sKW, LDK, 16 * M, 32 * kb + 16, lr, lg));
+            else
+              KD2[i] = O::mma2(KD2[i], d0, d1, a0, a1);
           }
         }
       }
@@ -740,6 +769,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdParams p) {
       }
       if (h + 1 < NHALF) __syncthreads();   // every read of this half's tiles is done
     }
+    if constexpr (WK) __syncthreads();    // beta D * dA and the sums overwrite dDelta, Delta and dY
 
     // ---- beta D * dA and D * dP; dbeta and the row / column sums of dA*A and dP*P ------
 #pragma unroll
@@ -808,35 +838,43 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdParams p) {
       const int mi = i / IC, j = i % IC;
       const int M = Mb + mi, ic = Ib + j;
       const int r = 16 * M + lr;
-      f32x4 gk = {0.f, 0.f, 0.f, 0.f}, gq = {0.f, 0.f, 0.f, 0.f};
+      f32x4 gk = {0.f, 0.f, 0.f, 0.f}, gq = {0.f, 0.f, 0.f, 0.f}, gw = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         const frag bk = colf(sK, LDK, 16 * kb, 16 * ic, lr, lg);
-        if (kb <= M) {                  // (beta D dA) K, (D dP) K: blocks on or left of the diagonal
-          gk = O::mma1(gk, bk, rowf(sAk, LCP, 16 * M, 16 * kb, lr, lg));
-          gq = O::mma1(gq, bk, rowf(sP, LCP, 16 * M, 16 * kb, lr, lg));
+        const frag bw = WK ? colf(sKW, LDK, 16 * kb, 16 * ic, lr, lg) : bk;
+        if (kb <= M) {                  // (beta D dA) KW, (D dP) KW: blocks on or left of the diagonal
+          gk = O::mma1(gk, bw, rowf(sAk, LCP, 16 * M, 16 * kb, lr, lg));
+          gq = O::mma1(gq, bw, rowf(sP, LCP, 16 * M, 16 * kb, lr, lg));
         }
         if (kb >= M) {                  // (beta D dA)^T K + (D dP)^T Q: blocks on or below it
-          gk = O::mma1(gk, bk, colf(sAk, LCP, 16 * kb, 16 * M, lr, lg));
-          gk = O::mma1(gk, colf(sQ, LDK, 16 * kb, 16 * ic, lr, lg), colf(sP, LCP, 16 * kb, 16 * M, lr, lg));
+          gw = O::mma1(gw, bk, colf(sAk, LCP, 16 * kb, 16 * M, lr, lg));
+          gw = O::mma1(gw, colf(sQ, LDK, 16 * kb, 16 * ic, lr, lg), colf(sP, LCP, 16 * kb, 16 * M, lr, lg));
         }
       }
       const float br = sF[r];
       const float er = G ? sF[CH + r] : 1.f, eg = G ? sF[2 * CH + r] : 1.f, ed = G ? sF[3 * CH + r] : 1.f;
-      const f32x4 dk = gk - dYS[i] * (br * er) + DdS[i] * ed;
+      const f32x4 dkr = gk - dYS[i] * (br * er);          // the read side
+      const f32x4 dkw = gw + DdS[i] * ed;                 // the write side
       const f32x4 dq = gq + dOS[i] * eg;
       const uint32_t off = static_cast<uint32_t>((r * H * DK + 16 * ic + 4 * lg) * 2);
-      buf_store8(bits8(dk), rdk, off, sk);
+      if constexpr (WK) {
+        buf_store8(bits8(dkr), rdk, off, sk);
+        buf_store8(bits8(dkw), rdkw, off, sk);
+      } else {
+        buf_store8(bits8(dkr + dkw), rdk, off, sk);
+      }
       buf_store8(bits8(dq), rdq, off, sk);
       if constexpr (G) {
         const f32x4 kk = O::f32(O::ld(sK + r * LDK + 16 * ic + 4 * lg));
+        const f32x4 kwv = WK ? O::f32(O::ld(sKW + r * LDK + 16 * ic + 4 * lg)) : kk;
         const f32x4 qq = O::f32(O::ld(sQ + r * LDK + 16 * ic + 4 * lg));
         float a = 0.f, x = 0.f, c = 0.f;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           a += eg * qq[s] * dOS[i][s];
           x -= br * er * kk[s] * dYS[i][s];
-          c += ed * kk[s] * DdS[i][s];
+          c += ed * kwv[s] * DdS[i][s];
         }
         a = lg_sum(a - c);
         x = lg_sum(x);
@@ -902,33 +940,34 @@ __global__ void bwd_copy_state_kernel(const float* src, float* dst, int64_t n) {
   if (i < n) dst[i] = src ? src[i] : 0.f;
 }
 
-template <int GATE, int DK>
+template <int GATE, int DK, bool WK>
 hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
   const ChunkParams& f = p.f;
   const int n_tiles = f.d_v / 64;
   const int64_t nseq = f.B * f.H * n_tiles;
-  hipLaunchKernelGGL((bwd_seq_kernel<GATE, DK>), dim3(static_cast<unsigned>(2 * nseq)), dim3(256), 0, stream, p, n_tiles,
-                     static_cast<int>(nseq));
+  hipLaunchKernelGGL((bwd_seq_kernel<GATE, DK, WK>), dim3(static_cast<unsigned>(2 * nseq)), dim3(256), 0, stream, p,
+                     n_tiles, static_cast<int>(nseq));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if constexpr (GATE == GATE_CHANNEL) {
+    static_assert(!WK, "per-channel gate: no write key");
     return launch_chunk_bwd_chan(p, stream);
   } else {
     const int64_t nch = (f.T + CH - 1) / CH;
     const unsigned grid = static_cast<unsigned>(f.cu ? f.H * f.nslots : f.B * f.H * nch);
     if (f.d_v == 128)
-      hipLaunchKernelGGL((bwd_chunk_kernel<GATE, DK, 128>), dim3(grid), dim3(512), 0, stream, p);
+      hipLaunchKernelGGL((bwd_chunk_kernel<GATE, DK, 128, WK>), dim3(grid), dim3(512), 0, stream, p);
     else
-      hipLaunchKernelGGL((bwd_chunk_kernel<GATE, DK, 64>), dim3(grid), dim3(512), 0, stream, p);
+      hipLaunchKernelGGL((bwd_chunk_kernel<GATE, DK, 64, WK>), dim3(grid), dim3(512), 0, stream, p);
     return hipGetLastError();
   }
 }
 
-template <int GATE>
+template <int GATE, bool WK = false>
 hipError_t launch_bwd_g(const BwdParams& p, hipStream_t stream) {
-  if (p.f.d_k == 128) return launch_bwd_t<GATE, 128>(p, stream);
+  if (p.f.d_k == 128) return launch_bwd_t<GATE, 128, WK>(p, stream);
   if constexpr (GATE != GATE_CHANNEL)   // the per-channel gate: d_k = 128 only
-    if (p.f.d_k == 64) return launch_bwd_t<GATE, 64>(p, stream);
+    if (p.f.d_k == 64) return launch_bwd_t<GATE, 64, WK>(p, stream);
   return hipErrorInvalidValue;
 }
 
@@ -958,7 +997,8 @@ size_t chunk_bwd_varlen_workspace_bytes(int64_t T, int64_t n_seq, int64_t H, int
 hipError_t launch_chunk_bwd(const BwdParams& p, hipStream_t stream) {
   const ChunkParams& f = p.f;
   if (f.B * f.H == 0) return hipSuccess;
-  if (f.io != IO_BF16 || f.kw || (f.gate == GATE_CHANNEL && f.d_k != 128)) return hipErrorInvalidValue;
+  if (f.io != IO_BF16 || (f.gate == GATE_CHANNEL && (f.d_k != 128 || f.kw))) return hipErrorInvalidValue;
+  if (f.kw && !p.dkw) return hipErrorInvalidValue;
   if (f.T == 0) {
     if (!p.dS0) return hipSuccess;
     const int64_t n = f.B * f.H * f.d_k * f.d_v;
@@ -966,8 +1006,13 @@ hipError_t launch_chunk_bwd(const BwdParams& p, hipStream_t stream) {
                        p.dS0, n);
     return hipGetLastError();
   }
-  hipError_t e = launch_chunk_prep(f, stream);
+  hipError_t e = launch_chunk_prep(f, stream);   // with f.kw: T of the write-key Gram blocks
   if (e != hipSuccess) return e;
+  if (f.kw) {
+    if (f.gate == GATE_NONE) return launch_bwd_g<GATE_NONE, true>(p, stream);
+    if (f.gate == GATE_SCALAR) return launch_bwd_g<GATE_SCALAR, true>(p, stream);
+    return hipErrorInvalidValue;
+  }
   switch (f.gate) {
     case GATE_NONE: return launch_bwd_g<GATE_NONE>(p, stream);
     case GATE_SCALAR: return launch_bwd_g<GATE_SCALAR>(p, stream);

@@ -350,9 +350,13 @@ namespace {
 gdr_status chunk_bwd_impl(const gdr_desc* d, const int32_t* cu, int64_t n_seq, const void* q, const void* k,
                           const void* v, const void* beta, const void* log_a, const float* S0, const void* dO,
                           const float* dS_T, void* dq, void* dk, void* dv, void* dbeta, void* dlog_a, float* dS0,
-                          void* workspace, size_t workspace_bytes, void* stream) {
+                          void* workspace, size_t workspace_bytes, void* stream, const void* kw = nullptr,
+                          void* dkw = nullptr) {
   gdr_status st = check_bwd_desc(d);
   if (st != GDR_OK) return st;
+  const bool wkey = kw != nullptr || dkw != nullptr;
+  if (wkey && d->gate == GDR_GATE_CHANNEL)
+    return fail(GDR_ERR_UNSUPPORTED, "backward with a write key: no gate or a scalar gate");
   const bool packed = cu != nullptr;
   if (packed && (st = check_packed(d, n_seq)) != GDR_OK) return st;
   const int64_t nseq = packed ? n_seq : d->B;       // sequences, and states in S0 / dS_T / dS0
@@ -369,6 +373,8 @@ gdr_status chunk_bwd_impl(const gdr_desc* d, const int32_t* cu, int64_t n_seq, c
       if (!req[i]) return fail(GDR_ERR_INVALID_ARG, "%s is NULL", names[i]);
     if (gated && !log_a) return fail(GDR_ERR_INVALID_ARG, "log_a is NULL but a gate is requested");
     if (gated && !dlog_a) return fail(GDR_ERR_INVALID_ARG, "dlog_a is NULL but a gate is requested");
+    if (wkey && !kw) return fail(GDR_ERR_INVALID_ARG, "kw is NULL");
+    if (wkey && !dkw) return fail(GDR_ERR_INVALID_ARG, "dkw is NULL");
     if (!workspace) return fail(GDR_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", ws_need);
     if (workspace_bytes < ws_need)
       return fail(GDR_ERR_WORKSPACE, "workspace_bytes = %zu, %zu needed", workspace_bytes, ws_need);
@@ -381,7 +387,7 @@ gdr_status chunk_bwd_impl(const gdr_desc* d, const int32_t* cu, int64_t n_seq, c
       (st = check_align("dS0", dS0, 16)) || (st = check_align("beta", beta, 2)) ||
       (st = check_align("dbeta", dbeta, 2)) || (st = check_align("log_a", log_a, 2)) ||
       (st = check_align("dlog_a", dlog_a, 2)) || (st = check_align("workspace", workspace, 16)) ||
-      (st = check_align("cu_seqlens", cu, 4)))
+      (st = check_align("cu_seqlens", cu, 4)) || (st = check_align("kw", kw, 16)) || (st = check_align("dkw", dkw, 16)))
     return st;
   const int64_t ntok = d->B * d->T * d->H;
   const int64_t state_bytes = nseq * d->H * d->d_k * d->d_v * 4;
@@ -393,10 +399,11 @@ gdr_status chunk_bwd_impl(const gdr_desc* d, const int32_t* cu, int64_t n_seq, c
                 span("dq", dq, ntok * d->d_k * 2), span("dk", dk, ntok * d->d_k * 2),
                 span("dv", dv, ntok * d->d_v * 2), span("dbeta", dbeta, ntok * 2),
                 span("dlog_a", dlog_a, gated ? ntok * gate_width * 2 : 0), span("dS0", dS0, state_bytes),
-                span("workspace", d->T > 0 ? workspace : nullptr, static_cast<int64_t>(ws_need))};
-  Span outs[] = {all[9], all[10], all[11], all[12], all[13], all[14], all[15]};
+                span("workspace", d->T > 0 ? workspace : nullptr, static_cast<int64_t>(ws_need)),
+                span("kw", kw, ntok * d->d_k * 2), span("dkw", dkw, ntok * d->d_k * 2)};
+  Span outs[] = {all[9], all[10], all[11], all[12], all[13], all[14], all[15], all[17]};
   if (dS0 && dS0 == dS_T) all[7].hi = all[7].lo;   // the final-state gradient may be overwritten by dS0
-  if ((st = check_no_overlap(outs, 7, all, 16))) return st;
+  if ((st = check_no_overlap(outs, 8, all, 18))) return st;
 
   gdr::BwdParams p;
   gdr::ChunkParams& f = p.f;
@@ -405,8 +412,9 @@ gdr_status chunk_bwd_impl(const gdr_desc* d, const int32_t* cu, int64_t n_seq, c
   f.B = nseq; f.T = d->T; f.H = d->H;
   f.d_k = dk_; f.d_v = dv_;
   f.io = d->io; f.gate = d->gate; f.literal = d->form == GDR_FORM_LITERAL;
-  f.cu = cu; f.nslots = packed ? gdr::chunk_varlen_slots(d->T, n_seq) : 0; f.order = nullptr; f.kw = nullptr;
+  f.cu = cu; f.nslots = packed ? gdr::chunk_varlen_slots(d->T, n_seq) : 0; f.order = nullptr; f.kw = kw;
   p.dO = dO; p.dS_T = dS_T; p.dq = dq; p.dk = dk; p.dv = dv; p.dbeta = dbeta; p.dlog_a = dlog_a; p.dS0 = dS0;
+  p.dkw = dkw;
   const size_t rec = packed ? gdr::chunk_varlen_records_bytes(d->T, n_seq, d->H, d->io, d->gate, dk_)
                             : gdr::chunk_workspace_bytes(d->B, d->T, d->H, d->io, d->gate, dk_);
   const size_t sb = packed ? gdr::chunk_bwd_varlen_state_bytes(d->T, n_seq, d->H, dk_, dv_)
@@ -550,6 +558,21 @@ gdr_status gdr_chunk_bwd(const gdr_desc* d, const void* q, const void* k, const 
     g_last_error.clear();
     return chunk_bwd_impl(d, nullptr, 0, q, k, v, beta, log_a, S0, dO, dS_T, dq, dk, dv, dbeta, dlog_a, dS0, workspace,
                           workspace_bytes, stream);
+  } catch (...) {
+    return fail(GDR_ERR_INVALID_ARG, "internal error");
+  }
+}
+
+gdr_status gdr_chunk_bwd_wkey(const gdr_desc* d, const void* q, const void* k, const void* kw, const void* v,
+                              const void* beta, const void* log_a, const float* S0, const void* dO, const float* dS_T,
+                              void* dq, void* dk, void* dkw, void* dv, void* dbeta, void* dlog_a, float* dS0,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    g_last_error.clear();
+    if (!kw) return fail(GDR_ERR_INVALID_ARG, "kw is NULL");
+    if (!dkw) return fail(GDR_ERR_INVALID_ARG, "dkw is NULL");
+    return chunk_bwd_impl(d, nullptr, 0, q, k, v, beta, log_a, S0, dO, dS_T, dq, dk, dv, dbeta, dlog_a, dS0, workspace,
+                          workspace_bytes, stream, kw, dkw);
   } catch (...) {
     return fail(GDR_ERR_INVALID_ARG, "internal error");
   }

@@ -62,7 +62,8 @@ struct BwdParams {
   const void* dO;       // [B, T, H, d_v] gradient of the output
   const float* dS_T;    // [B, H, d_k, d_v] gradient of the final state, or null (zero)
   void* dq;             // [B, T, H, d_k]
-  void* dk;             // [B, T, H, d_k]
+  void* dk;             // [B, T, H, d_k]; with a write key (f.kw) the read side only
+  void* dkw;            // [B, T, H, d_k] gradient of the write key (f.kw set), else unused
   void* dv;             // [B, T, H, d_v]
   void* dbeta;          // [B, T, H]
   void* dlog_a;         // [B, T, H] (scalar gate), [B, T, H, d_k] (per-channel gate), else unused

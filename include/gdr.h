@@ -371,6 +371,37 @@ gdr_status gdr_chunk_bwd(const gdr_desc* desc, const void* q, const void* k, con
                          void* stream /* hipStream_t */);
 
 /*
+ * gdr_chunk_bwd_wkey -- gradients of gdr_chunk_fwd_wkey (training the
+ * preconditioned delta rule).
+ *
+ * For the forward gdr_chunk_fwd_wkey(desc, q, k, kw, v, beta, log_a, S0) -- the
+ * erase reads the state along k and the write goes along the separate write key
+ * kw ("OSDN: Improving Delta Rule with Provable Online Preconditioning in Linear
+ * Attention", §2.1) -- returns the gradients of L = <dO, o> + <dS_T, S_T> with
+ * respect to q, k, kw, v, beta, log_a and S0, the reverse mode of that recurrence
+ * through its chunk form (the column side of the Gram and score matrices, the
+ * state write and its gradient take kw; the residual and the rows of the Gram
+ * matrix take k).  dk is the gradient through the read side only and dkw the one
+ * through the write side; with kw == k their sum is gdr_chunk_bwd's dk.
+ *
+ * Supported: bf16 I/O; GDR_GATE_NONE or GDR_GATE_SCALAR with d_k, d_v in {64, 128};
+ * either gdr_form; fixed-length batches.  GDR_GATE_CHANNEL returns
+ * GDR_ERR_UNSUPPORTED.
+ *
+ *   kw     [B, T, H, d_k] bf16  the write key (non-NULL when T > 0)
+ *   dkw    [B, T, H, d_k] bf16  written (non-NULL when T > 0)
+ *   every other argument as for gdr_chunk_bwd; the workspace is that of
+ *   gdr_chunk_bwd_workspace_size for the same descriptor.
+ *
+ * Precision and errors as for gdr_chunk_bwd; kw and dkw take part in the alias
+ * checks like the other token tensors.
+ */
+gdr_status gdr_chunk_bwd_wkey(const gdr_desc* desc, const void* q, const void* k, const void* kw, const void* v,
+                              const void* beta, const void* log_a, const float* S0, const void* dO, const float* dS_T,
+                              void* dq, void* dk, void* dkw, void* dv, void* dbeta, void* dlog_a, float* dS0,
+                              void* workspace, size_t workspace_bytes, void* stream /* hipStream_t */);
+
+/*
  * gdr_chunk_bwd_varlen_workspace_size -- scratch for gdr_chunk_bwd_varlen.
  *
  * The records of gdr_chunk_fwd_varlen (H * (ceil(T / 64) + n_seq) slots of R

@@ -349,6 +349,37 @@ def test_backward_argument_checks(lib):
     assert b"dk overlaps k" in lib.gdr_last_error()                        # ... the error is dk's
 
 
+def _bwd_wkey(lib, d, p, ws_bytes=1 << 40):
+    """gdr_chunk_bwd_wkey with p = (q, k, kw, v, beta, log_a, S0, dO, dS_T, dq, dk, dkw, dv, dbeta, dlog_a,
+    dS0, ws)."""
+    return lib.gdr_chunk_bwd_wkey(None if d is None else ctypes.byref(d), *p[:16], p[16], ws_bytes, None)
+
+
+def test_backward_write_key_checks(lib):
+    p = _ptrs(17)
+    d = _desc()
+    assert _bwd_wkey(lib, None, p) == INVALID
+    for i, name in ((2, "kw"), (11, "dkw"), (0, "q"), (9, "dq")):
+        bad = list(p)
+        bad[i] = None
+        assert _bwd_wkey(lib, d, bad) == INVALID, name
+        assert name.encode() in lib.gdr_last_error()
+    assert _bwd_wkey(lib, _desc(gate=2), p) == UNSUPPORTED                 # no per-channel gate with a write key
+    assert _bwd_wkey(lib, _desc(io=0), p) == UNSUPPORTED                   # bf16 only
+    assert _bwd_wkey(lib, d, p, ws_bytes=16) == WORKSPACE
+    for i in (2, 11):                                                      # kw, dkw: 16-byte operands
+        bad = list(p)
+        bad[i] += 8
+        assert _bwd_wkey(lib, d, bad) == ALIGN, i
+    bad = list(p)
+    bad[11] = bad[2] + 64                                                  # dkw inside kw
+    assert _bwd_wkey(lib, d, bad) == INVALID
+    assert b"dkw overlaps kw" in lib.gdr_last_error()
+    bad = list(p)
+    bad[11] = bad[10]                                                      # dkw == dk
+    assert _bwd_wkey(lib, d, bad) == INVALID
+
+
 def test_backward_varlen_checks(lib):
     n = ctypes.c_size_t(7)
     d = _desc(B=1, T=300, H=2)
