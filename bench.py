@@ -319,8 +319,19 @@ def bench_precond(prep, args, log, wl, k, beta):
     nbytes = precond_bytes(wl.B, wl.T, wl.H, wl.d_k, 2, True)
     gbs = nbytes / (ms * 1e-3) / 1e9
     log(f"preconditioner scan: {ms * 1e3:.1f} us, {gbs:.0f} GB/s")
+    # its backward (the gradients of <dkw, kw> + <dd_T, d_T> in k, beta, r and d0),
+    # with seeded N(0, 1) output gradients generated on the GPU before the timing
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    dkw = torch.randn(k.shape, generator=gen, device="cuda").to(k.dtype)
+    dd_T = torch.randn(d0.shape, generator=gen, device="cuda")
+    ws = torch.empty(gdr.precond_scan_bwd_workspace_size(wl.B, wl.T, wl.H, wl.d_k), dtype=torch.uint8, device="cuda")
+    bms = time_calls(lambda i: gdr.precond_scan_bwd(k, beta, PRECOND_ETA, r, d0, dkw, dd_T, workspace=ws),
+                     args.warmup, args.steps)
+    del dkw, dd_T, ws
+    log(f"preconditioner scan backward: {bms * 1e3:.1f} us")
     return kw, {"workload": "osdn_precond_scan_apf_b%dh%dt%dd%d_bf16" % (wl.B, wl.H, wl.T, wl.d_k),
             "value": round(gbs, 1), "unit": "GB/s", "us_per_launch": round(ms * 1e3, 2),
+            "backward_us_per_launch": round(bms * 1e3, 2),
             "tokens_per_s": round(wl.B * wl.T / (ms * 1e-3), 1), "bytes_per_launch": nbytes,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4),

@@ -26,7 +26,8 @@ EXPORTED = ("gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_chunk_fwd_varl
             "gdr_chunk_fwd_varlen", "gdr_recurrent_step", "gdr_chunk_fwd_wkey", "gdr_recurrent_step_wkey",
             "gdr_precond_scan", "gdr_status_string", "gdr_last_error", "gdr_version",
             "gdr_chunk_bwd_workspace_size", "gdr_chunk_bwd", "gdr_chunk_bwd_wkey", "gdr_chunk_bwd_varlen_workspace_size",
-            "gdr_chunk_bwd_varlen", "gdr_chunk_fwd_noalloc")
+            "gdr_chunk_bwd_varlen", "gdr_chunk_fwd_noalloc", "gdr_precond_scan_bwd_workspace_size",
+            "gdr_precond_scan_bwd", "gdr_chunk_fwd_varlen_wkey", "gdr_chunk_bwd_varlen_wkey")
 
 
 class GdrDesc(ctypes.Structure):
@@ -77,6 +78,11 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         lib.gdr_recurrent_step.argtypes = [ctypes.POINTER(GdrDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.gdr_precond_scan.restype = ctypes.c_int
         lib.gdr_precond_scan.argtypes = [ctypes.POINTER(GdrDesc), vp, vp, vp, ctypes.c_float, vp, vp, vp, vp]
+        lib.gdr_precond_scan_bwd_workspace_size.restype = ctypes.c_int
+        lib.gdr_precond_scan_bwd_workspace_size.argtypes = [ctypes.POINTER(GdrDesc), ctypes.POINTER(ctypes.c_size_t)]
+        lib.gdr_precond_scan_bwd.restype = ctypes.c_int
+        lib.gdr_precond_scan_bwd.argtypes = ([ctypes.POINTER(GdrDesc), vp, vp, vp, ctypes.c_float] + [vp] * 7 +
+                                             [vp, ctypes.c_size_t, vp])
         lib.gdr_status_string.restype = ctypes.c_char_p
         lib.gdr_chunk_bwd_workspace_size.restype = ctypes.c_int
         lib.gdr_chunk_bwd_workspace_size.argtypes = [ctypes.POINTER(GdrDesc), ctypes.POINTER(ctypes.c_size_t)]
@@ -84,6 +90,12 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         lib.gdr_chunk_bwd.argtypes = [ctypes.POINTER(GdrDesc)] + [vp] * 15 + [ctypes.c_size_t, vp]
         lib.gdr_chunk_bwd_wkey.restype = ctypes.c_int
         lib.gdr_chunk_bwd_wkey.argtypes = [ctypes.POINTER(GdrDesc)] + [vp] * 17 + [ctypes.c_size_t, vp]
+        lib.gdr_chunk_bwd_varlen_wkey.restype = ctypes.c_int
+        lib.gdr_chunk_bwd_varlen_wkey.argtypes = ([ctypes.POINTER(GdrDesc), vp, ctypes.c_int64] + [vp] * 17 +
+                                                  [ctypes.c_size_t, vp])
+        lib.gdr_chunk_fwd_varlen_wkey.restype = ctypes.c_int
+        lib.gdr_chunk_fwd_varlen_wkey.argtypes = ([ctypes.POINTER(GdrDesc), vp, ctypes.c_int64] + [vp] * 10 +
+                                                  [ctypes.c_size_t, vp])
         lib.gdr_chunk_bwd_varlen_workspace_size.restype = ctypes.c_int
         lib.gdr_chunk_bwd_varlen_workspace_size.argtypes = [ctypes.POINTER(GdrDesc), ctypes.c_int64,
                                                             ctypes.POINTER(ctypes.c_size_t)]
@@ -259,9 +271,9 @@ def chunk_bwd(q, k, v, beta, log_a, S0, dO, dS_T=None, *, cu_seqlens=None, form:
     the sequences are packed along T of [1, T, H, .] tensors (gdr_chunk_bwd_varlen)
     and S0, dS_T, dS0 are [n_seq, H, d_k, d_v].  Returns dict(dq, dk, dv, dbeta,
     dlog_a, dS0) (dlog_a None without a gate, dS0 None when want_dS0 is False).
-    `kw` ([B, T, H, d_k] bf16, fixed-length batches, no gate or a scalar gate) is the
-    forward's write key (gdr_chunk_bwd_wkey): then dk is the read side's gradient and
-    the dict also holds dkw.  Asynchronous on the current (or given) stream."""
+    `kw` ([B, T, H, d_k] bf16, no gate or a scalar gate) is the forward's write key
+    (gdr_chunk_bwd_wkey, gdr_chunk_bwd_varlen_wkey): then dk is the read side's
+    gradient and the dict also holds dkw.  Asynchronous on the current (or given) stream."""
     lib = load()
     B, T, H, dk = k.shape
     dv = v.shape[-1]
@@ -289,8 +301,6 @@ def chunk_bwd(q, k, v, beta, log_a, S0, dO, dS_T=None, *, cu_seqlens=None, form:
     if dS_T is not None:
         _require(dS_T, "dS_T", torch.float32, (nstate, H, dk, dv))
     if kw is not None:
-        if packed:
-            raise ValueError("the write-key backward takes fixed-length batches")
         _require(kw, "kw", dt, (B, T, H, dk))
     out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v), dbeta=torch.empty_like(beta),
                dlog_a=torch.empty_like(log_a) if log_a is not None else None,
@@ -310,10 +320,13 @@ def chunk_bwd(q, k, v, beta, log_a, S0, dO, dS_T=None, *, cu_seqlens=None, form:
             _ptr(workspace), workspace.numel(), _stream_handle(stream))
     if kw is not None:
         out["dkw"] = torch.empty_like(k)
-        st = lib.gdr_chunk_bwd_wkey(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(kw), _ptr(v), _ptr(beta), _ptr(log_a),
-                                    _ptr(S0), _ptr(dO), _ptr(dS_T), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dkw"]),
-                                    _ptr(out["dv"]), _ptr(out["dbeta"]), _ptr(out["dlog_a"]), _ptr(out["dS0"]),
-                                    _ptr(workspace), workspace.numel(), _stream_handle(stream))
+        wargs = (_ptr(q), _ptr(k), _ptr(kw), _ptr(v), _ptr(beta), _ptr(log_a), _ptr(S0), _ptr(dO), _ptr(dS_T),
+                 _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dkw"]), _ptr(out["dv"]), _ptr(out["dbeta"]),
+                 _ptr(out["dlog_a"]), _ptr(out["dS0"]), _ptr(workspace), workspace.numel(), _stream_handle(stream))
+        if packed:
+            st = lib.gdr_chunk_bwd_varlen_wkey(ctypes.byref(desc), _ptr(cu_seqlens), nstate, *wargs)
+        else:
+            st = lib.gdr_chunk_bwd_wkey(ctypes.byref(desc), *wargs)
     elif packed:
         st = lib.gdr_chunk_bwd_varlen(ctypes.byref(desc), _ptr(cu_seqlens), nstate, *args)
     else:
@@ -333,11 +346,12 @@ def chunk_varlen_workspace_size(T: int, n_seq: int, H: int, d_k: int, d_v: int, 
 
 
 def chunk_fwd_varlen(q, k, v, beta, log_a, cu_seqlens, S0=None, *, form: str = "page", o=None, S_T=None,
-                     want_state: bool = True, workspace=None, stream=None):
+                     want_state: bool = True, workspace=None, stream=None, kw=None):
     """gdr_chunk_fwd_varlen on torch tensors: sequences packed along T.
     q, k [1, T, H, d_k]; v [1, T, H, d_v]; beta [1, T, H]; log_a None, [1, T, H] or
     [1, T, H, d_k] (bf16); cu_seqlens int32 device tensor [N + 1] of offsets;
-    S0 None or [N, H, d_k, d_v] float32.  Returns (o [1, T, H, d_v], S_T [N, H, d_k, d_v])."""
+    S0 None or [N, H, d_k, d_v] float32.  `kw` (optional, [1, T, H, d_k]) is a separate
+    write key (gdr_chunk_fwd_varlen_wkey).  Returns (o [1, T, H, d_v], S_T [N, H, d_k, d_v])."""
     lib = load()
     B, T, H, dk = k.shape
     dv = v.shape[-1]
@@ -369,9 +383,15 @@ def chunk_fwd_varlen(q, k, v, beta, log_a, cu_seqlens, S0=None, *, form: str = "
         workspace = torch.empty(max(int(need.value), 1), dtype=torch.uint8, device=q.device)
     if workspace.dtype != torch.uint8 or not workspace.is_contiguous() or workspace.device != q.device:
         raise ValueError("workspace must be a contiguous uint8 tensor on the inputs' device")
-    st = lib.gdr_chunk_fwd_varlen(ctypes.byref(desc), _ptr(cu_seqlens), N, _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
-                                  _ptr(log_a), _ptr(S0), _ptr(o), _ptr(S_T), _ptr(workspace), workspace.numel(),
-                                  _stream_handle(stream))
+    if kw is not None:
+        _require(kw, "kw", dt, (1, T, H, dk))
+        st = lib.gdr_chunk_fwd_varlen_wkey(ctypes.byref(desc), _ptr(cu_seqlens), N, _ptr(q), _ptr(k), _ptr(kw),
+                                           _ptr(v), _ptr(beta), _ptr(log_a), _ptr(S0), _ptr(o), _ptr(S_T),
+                                           _ptr(workspace), workspace.numel(), _stream_handle(stream))
+    else:
+        st = lib.gdr_chunk_fwd_varlen(ctypes.byref(desc), _ptr(cu_seqlens), N, _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                                      _ptr(log_a), _ptr(S0), _ptr(o), _ptr(S_T), _ptr(workspace), workspace.numel(),
+                                      _stream_handle(stream))
     _check(lib, st)
     return o, S_T
 
@@ -443,13 +463,86 @@ def precond_scan(k, beta, eta: float, r=None, d0=None, *, kw=None, d_T=None, wan
     return kw, d_T
 
 
+def precond_scan_bwd_workspace_size(B: int, T: int, H: int, d_k: int) -> int:
+    """Bytes of scratch gdr_precond_scan_bwd needs (gdr_precond_scan_bwd_workspace_size)."""
+    lib = load()
+    desc = GdrDesc(B, T, H, d_k, d_k, 64, 1, 0, 0)
+    n = ctypes.c_size_t(0)
+    _check(lib, lib.gdr_precond_scan_bwd_workspace_size(ctypes.byref(desc), ctypes.byref(n)))
+    return int(n.value)
+
+
+def precond_scan_bwd(k, beta, eta: float, r=None, d0=None, dkw=None, dd_T=None, *, want_dd0: bool = True,
+                     workspace=None, stream=None):
+    """gdr_precond_scan_bwd on torch tensors: the gradients of <dkw, kw> + <dd_T, d_T>
+    for the scan precond_scan(k, beta, eta, r, d0).  dkw None (zero) or
+    [B, T, H, d_k] in the I/O dtype; dd_T None (zero) or [B, H, d_k] float32.
+    Returns dict(dk, dbeta, dr, dd0) (dr None without r, dd0 None when want_dd0 is
+    False).  Asynchronous on the current (or given) stream."""
+    lib = load()
+    B, T, H, dk = k.shape
+    dt = k.dtype
+    _require(k, "k", dt, (B, T, H, dk))
+    _require(beta, "beta", dt, (B, T, H))
+    if r is not None:
+        _require(r, "r", dt, (B, T, H))
+    if d0 is not None:
+        _require(d0, "d0", torch.float32, (B, H, dk))
+    if dkw is not None:
+        _require(dkw, "dkw", dt, (B, T, H, dk))
+    if dd_T is not None:
+        _require(dd_T, "dd_T", torch.float32, (B, H, dk))
+    desc = GdrDesc(B, T, H, dk, dk, 64, _io_of(k), 0, 0)
+    need = ctypes.c_size_t(0)
+    _check(lib, lib.gdr_precond_scan_bwd_workspace_size(ctypes.byref(desc), ctypes.byref(need)))
+    if workspace is None:
+        workspace = torch.empty(max(int(need.value), 1), dtype=torch.uint8, device=k.device)
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous() or workspace.device != k.device:
+        raise ValueError("workspace must be a contiguous uint8 tensor on the inputs' device")
+    out = dict(dk=torch.empty_like(k), dbeta=torch.empty_like(beta),
+               dr=torch.empty_like(r) if r is not None else None,
+               dd0=torch.empty((B, H, dk), dtype=torch.float32, device=k.device) if want_dd0 else None)
+    st = lib.gdr_precond_scan_bwd(ctypes.byref(desc), _ptr(k), _ptr(beta), _ptr(r), float(eta), _ptr(d0), _ptr(dkw),
+                                  _ptr(dd_T), _ptr(out["dk"]), _ptr(out["dbeta"]), _ptr(out["dr"]), _ptr(out["dd0"]),
+                                  _ptr(workspace), workspace.numel(), _stream_handle(stream))
+    _check(lib, st)
+    return out
+
+
+class _PrecondScan(torch.autograd.Function):
+    """precond_scan with precond_scan_bwd as its backward (marshalling only)."""
+
+    @staticmethod
+    def forward(ctx, k, beta, eta, r, d0):
+        kw, d_T = precond_scan(k, beta, eta, r, d0)
+        ctx.save_for_backward(k, beta, r, d0)
+        ctx.eta = eta
+        return kw, d_T
+
+    @staticmethod
+    def backward(ctx, dkw, dd_T):
+        k, beta, r, d0 = ctx.saved_tensors
+        dkw = None if dkw is None else dkw.to(k.dtype).contiguous()
+        dd_T = None if dd_T is None else dd_T.float().contiguous()
+        g = precond_scan_bwd(k, beta, ctx.eta, r, d0, dkw, dd_T, want_dd0=d0 is not None)
+        return g["dk"], g["dbeta"], None, g["dr"], g["dd0"]
+
+
+def precond_attn(k, beta, eta: float, r=None, d0=None):
+    """(kw, d_T) of precond_scan as a torch autograd function whose backward is
+    precond_scan_bwd: gradients flow to k, beta, r and d0.  Composed with
+    chunk_attn(..., kw=kw) it gives the gradients of both phases of the
+    preconditioned delta rule."""
+    return _PrecondScan.apply(k, beta, float(eta), r, d0)
+
+
 class _ChunkAttn(torch.autograd.Function):
     """chunk_fwd with chunk_bwd as its backward (marshalling only)."""
 
     @staticmethod
     def forward(ctx, q, k, v, beta, log_a, S0, cu_seqlens, form, kw):
         if cu_seqlens is not None:
-            o, S_T = chunk_fwd_varlen(q, k, v, beta, log_a, cu_seqlens, S0, form=form)
+            o, S_T = chunk_fwd_varlen(q, k, v, beta, log_a, cu_seqlens, S0, form=form, kw=kw)
         else:
             o, S_T = chunk_fwd(q, k, v, beta, log_a, S0, form=form, kw=kw)
         ctx.save_for_backward(q, k, v, beta, log_a, S0, cu_seqlens, kw)
@@ -473,7 +566,7 @@ def chunk_attn(q, k, v, beta, log_a=None, S0=None, cu_seqlens=None, form: str = 
     """(o, S_T) of chunk_fwd (or chunk_fwd_varlen with cu_seqlens) as a torch autograd
     function whose backward is chunk_bwd: bf16, any gate (per-channel with d_k = 128),
     either form.  Gradients flow to q, k, v, beta, log_a and S0, and to the write key
-    `kw` when one is given (fixed-length batches, no gate or a scalar gate)."""
-    if kw is not None and (cu_seqlens is not None or (log_a is not None and log_a.dim() == 4)):
-        raise ValueError("chunk_attn with a write key: fixed-length batches, no gate or a scalar gate")
+    `kw` when one is given (no gate or a scalar gate)."""
+    if kw is not None and log_a is not None and log_a.dim() == 4:
+        raise ValueError("chunk_attn with a write key: no gate or a scalar gate (the backward's scope)")
     return _ChunkAttn.apply(q, k, v, beta, log_a, S0, cu_seqlens, form, kw)

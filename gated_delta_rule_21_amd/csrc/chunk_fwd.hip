@@ -456,8 +456,12 @@ static hipError_t launch_chunk_t(const ChunkParams& p, hipStream_t stream) {
 
 template <int IO, int GATE>
 static hipError_t launch_chunk_g(const ChunkParams& p, hipStream_t stream) {
-  // fp32 I/O: d_k = 64 only (LDS budget); two waves, 32 columns per workgroup
+  // fp32 I/O: two waves, 32 columns per workgroup; at d_k = 128 one LDS copy of the
+  // tiles (no double buffer), and no per-channel gate (its fp32 running sums of the
+  // gate and third operand tile leave no room)
   if (p.d_k == 64) return launch_chunk_t<IO, GATE, 64, 2>(p, stream);
+  if constexpr (GATE != GATE_CHANNEL)
+    if (p.d_k == 128) return launch_chunk_t<IO, GATE, 128, 2>(p, stream);
   return hipErrorInvalidValue;
 }
 

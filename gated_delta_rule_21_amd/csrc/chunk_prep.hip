@@ -193,6 +193,7 @@ __global__ __launch_bounds__(256) void chunk_prep_lds_kernel(ChunkParams p) {
       f[2 * CH + lane] = __expf(g);
       f[3 * CH + lane] = __expf(gC - g);
       f[4 * CH + lane] = __expf(gC);
+      f[5 * CH + lane] = g;
     }
   } else {
     if (tid < CH) sBc[tid] = load1(rb, static_cast<uint32_t>(tid * H * ESZ));
@@ -1030,7 +1031,9 @@ static hipError_t launch_prep_t(const ChunkParams& p, int64_t nchunks, hipStream
   const int64_t ntasks = p.cu ? p.H * p.nslots : p.B * p.H * nchunks;
   if constexpr (GATE == GATE_CHANNEL && IO == IO_BF16) {
     hipLaunchKernelGGL((chunk_prep_chan_kernel<DK>), dim3(static_cast<unsigned>(ntasks)), dim3(256), 0, stream, p);
-  } else if constexpr (GATE == GATE_CHANNEL) {
+  } else if constexpr (GATE == GATE_CHANNEL || (IO == IO_F32 && DK == 128)) {
+    // fp32 at d_k = 128: the operands of a chunk do not fit a wave's registers, so
+    // the four-wave kernel takes them through LDS
     hipLaunchKernelGGL((chunk_prep_lds_kernel<IO, GATE, DK>), dim3(static_cast<unsigned>(ntasks)), dim3(256), 0,
                        stream, p);
   } else {
@@ -1050,7 +1053,7 @@ static hipError_t launch_prep_t(const ChunkParams& p, int64_t nchunks, hipStream
 template <int IO, int GATE>
 static hipError_t launch_prep_g(const ChunkParams& p, int64_t nchunks, hipStream_t stream) {
   if (p.d_k == 128) {
-    if constexpr (IO == IO_F32) return hipErrorInvalidValue;
+    if constexpr (IO == IO_F32 && GATE == GATE_CHANNEL) return hipErrorInvalidValue;   // LDS budget
     else return launch_prep_t<IO, GATE, 128>(p, nchunks, stream);
   }
   if (p.d_k == 64) return launch_prep_t<IO, GATE, 64>(p, nchunks, stream);

@@ -62,8 +62,8 @@ gdr_status check_desc(const gdr_desc* d, bool decode) {
   }
   if (d->d_k != 64 && d->d_k != 128) return fail(GDR_ERR_UNSUPPORTED, "d_k = %lld: supported 64, 128", (long long)d->d_k);
   if (d->d_v != 64 && d->d_v != 128) return fail(GDR_ERR_UNSUPPORTED, "d_v = %lld: supported 64, 128", (long long)d->d_v);
-  if (!decode && d->io == GDR_F32 && d->d_k != 64)
-    return fail(GDR_ERR_UNSUPPORTED, "fp32 I/O chunk forward supports d_k = 64 only");
+  if (!decode && d->io == GDR_F32 && d->d_k != 64 && d->gate == GDR_GATE_CHANNEL)
+    return fail(GDR_ERR_UNSUPPORTED, "fp32 I/O chunk forward with a per-channel gate supports d_k = 64 only");
   int64_t bh, bth, x;
   if (!mul_ok(d->B, d->H, &bh) || !mul_ok(bh, d->T, &bth) || !mul_ok(bth, 128, &x) || !mul_ok(bh, 128 * 128 * 4, &x))
     return fail(GDR_ERR_INVALID_ARG, "sizes overflow");
@@ -296,6 +296,23 @@ gdr_status gdr_chunk_fwd_varlen(const gdr_desc* d, const int32_t* cu_seqlens, in
   }
 }
 
+gdr_status gdr_chunk_fwd_varlen_wkey(const gdr_desc* d, const int32_t* cu_seqlens, int64_t n_seq, const void* q,
+                                     const void* k, const void* kw, const void* v, const void* beta,
+                                     const void* log_a, const float* S0, void* o, float* S_T, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  try {
+    g_last_error.clear();
+    if (!cu_seqlens) return fail(GDR_ERR_INVALID_ARG, "cu_seqlens is NULL");
+    if (!kw) return fail(GDR_ERR_INVALID_ARG, "kw is NULL");
+    if (d && d->gate == GDR_GATE_CHANNEL && d->d_k != 128)
+      return fail(GDR_ERR_UNSUPPORTED, "write key with a per-channel gate: d_k = 128 only");
+    return chunk_fwd_impl(d, cu_seqlens, n_seq, q, k, v, beta, log_a, S0, o, S_T, workspace, workspace_bytes,
+                          stream, kw);
+  } catch (...) {
+    return fail(GDR_ERR_INVALID_ARG, "internal error");
+  }
+}
+
 }  // extern "C"
 
 namespace {
@@ -502,6 +519,89 @@ gdr_status gdr_precond_scan(const gdr_desc* d, const void* k, const void* beta, 
   }
 }
 
+namespace {
+gdr_status check_precond_desc(const gdr_desc* d) {
+  if (!d) return fail(GDR_ERR_INVALID_ARG, "desc is NULL");
+  if (d->io != GDR_F32 && d->io != GDR_BF16) return fail(GDR_ERR_INVALID_ARG, "io dtype %d is not GDR_F32/GDR_BF16", d->io);
+  if (d->B < 1) return fail(GDR_ERR_INVALID_ARG, "B = %lld must be >= 1", (long long)d->B);
+  if (d->H < 1) return fail(GDR_ERR_INVALID_ARG, "H = %lld must be >= 1", (long long)d->H);
+  if (d->T < 0) return fail(GDR_ERR_INVALID_ARG, "T = %lld must be >= 0", (long long)d->T);
+  if (d->d_k != 64 && d->d_k != 128) return fail(GDR_ERR_UNSUPPORTED, "d_k = %lld: supported 64, 128", (long long)d->d_k);
+  int64_t bh = 0, bth = 0, elems = 0;
+  if (!mul_ok(d->B, d->H, &bh) || !mul_ok(bh, d->T, &bth) || !mul_ok(bth, d->d_k + 2, &elems) ||
+      !mul_ok(elems, 4, &elems))
+    return fail(GDR_ERR_INVALID_ARG, "sizes overflow");
+  if (bh > INT32_MAX) return fail(GDR_ERR_UNSUPPORTED, "B*H = %lld exceeds the grid limit", (long long)bh);
+  return GDR_OK;
+}
+}  // namespace
+
+gdr_status gdr_precond_scan_bwd_workspace_size(const gdr_desc* d, size_t* bytes) {
+  try {
+    g_last_error.clear();
+    if (!bytes) return fail(GDR_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = 0;
+    gdr_status st = check_precond_desc(d);
+    if (st != GDR_OK) return st;
+    *bytes = gdr::precond_scan_bwd_workspace_bytes(d->B, d->T, d->H, static_cast<int>(d->d_k));
+    return GDR_OK;
+  } catch (...) {
+    return fail(GDR_ERR_INVALID_ARG, "internal error");
+  }
+}
+
+gdr_status gdr_precond_scan_bwd(const gdr_desc* d, const void* k, const void* beta, const void* r, float eta,
+                                const float* d0, const void* dkw, const float* dd_T, void* dk, void* dbeta, void* dr,
+                                float* dd0, void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    g_last_error.clear();
+    gdr_status st = check_precond_desc(d);
+    if (st != GDR_OK) return st;
+    if (!(eta == eta) || eta > 3.0e38f || eta < -3.0e38f) return fail(GDR_ERR_INVALID_ARG, "eta is not finite");
+    const int64_t esz = d->io == GDR_BF16 ? 2 : 4;
+    const int64_t bth = d->B * d->T * d->H;
+    const size_t need = gdr::precond_scan_bwd_workspace_bytes(d->B, d->T, d->H, static_cast<int>(d->d_k));
+    if (!r && dr) return fail(GDR_ERR_INVALID_ARG, "dr must be NULL without a retention r");
+    if (d->T > 0) {
+      const void* req[] = {k, beta, dk, dbeta};
+      const char* names[] = {"k", "beta", "dk", "dbeta"};
+      for (int i = 0; i < 4; ++i)
+        if (!req[i]) return fail(GDR_ERR_INVALID_ARG, "%s is NULL", names[i]);
+      if (!workspace) return fail(GDR_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+      if (workspace_bytes < need) return fail(GDR_ERR_WORKSPACE, "workspace_bytes = %zu, %zu needed", workspace_bytes, need);
+    }
+    if ((st = check_align("k", k, 16)) || (st = check_align("dkw", dkw, 16)) || (st = check_align("dk", dk, 16)) ||
+        (st = check_align("beta", beta, esz)) || (st = check_align("r", r, esz)) ||
+        (st = check_align("dbeta", dbeta, esz)) || (st = check_align("dr", dr, esz)) ||
+        (st = check_align("d0", d0, 4)) || (st = check_align("dd_T", dd_T, 4)) || (st = check_align("dd0", dd0, 4)) ||
+        (st = check_align("workspace", workspace, 16)))
+      return st;
+    const int64_t kbytes = bth * d->d_k * esz, dbytes = d->B * d->H * d->d_k * 4;
+    const bool t0 = d->T > 0;
+    Span all[] = {span("k", t0 ? k : nullptr, kbytes), span("beta", t0 ? beta : nullptr, bth * esz),
+                  span("r", t0 ? r : nullptr, bth * esz), span("d0", d0, dbytes),
+                  span("dkw", t0 ? dkw : nullptr, kbytes), span("dd_T", dd_T, dbytes),
+                  span("dk", t0 ? dk : nullptr, kbytes), span("dbeta", t0 ? dbeta : nullptr, bth * esz),
+                  span("dr", t0 ? dr : nullptr, bth * esz), span("dd0", dd0, dbytes),
+                  span("workspace", t0 ? workspace : nullptr, static_cast<int64_t>(need))};
+    Span outs[] = {all[6], all[7], all[8], all[9], all[10]};
+    if (dd0 && dd0 == dd_T) all[5].hi = all[5].lo;   // dd0 may overwrite dd_T
+    if ((st = check_no_overlap(outs, 5, all, 11))) return st;
+
+    gdr::PrecondBwdParams p;
+    p.f.k = k; p.f.beta = beta; p.f.r = r; p.f.d0 = d0; p.f.kw = nullptr; p.f.d_T = nullptr;
+    p.f.B = d->B; p.f.T = d->T; p.f.H = d->H;
+    p.f.d_k = static_cast<int>(d->d_k); p.f.io = d->io; p.f.eta = eta;
+    p.dkw = dkw; p.dd_T = dd_T; p.dk = dk; p.dbeta = dbeta; p.dr = dr; p.dd0 = dd0;
+    p.ws = static_cast<float*>(workspace);
+    hipError_t e = gdr::launch_precond_scan_bwd(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(GDR_ERR_HIP, "preconditioner scan backward launch failed: %s", hipGetErrorString(e));
+    return GDR_OK;
+  } catch (...) {
+    return fail(GDR_ERR_INVALID_ARG, "internal error");
+  }
+}
+
 gdr_status gdr_chunk_fwd_wkey(const gdr_desc* d, const void* q, const void* k, const void* kw, const void* v,
                               const void* beta, const void* log_a, const float* S0, void* o, float* S_T,
                               void* workspace, size_t workspace_bytes, void* stream) {
@@ -573,6 +673,23 @@ gdr_status gdr_chunk_bwd_wkey(const gdr_desc* d, const void* q, const void* k, c
     if (!dkw) return fail(GDR_ERR_INVALID_ARG, "dkw is NULL");
     return chunk_bwd_impl(d, nullptr, 0, q, k, v, beta, log_a, S0, dO, dS_T, dq, dk, dv, dbeta, dlog_a, dS0, workspace,
                           workspace_bytes, stream, kw, dkw);
+  } catch (...) {
+    return fail(GDR_ERR_INVALID_ARG, "internal error");
+  }
+}
+
+gdr_status gdr_chunk_bwd_varlen_wkey(const gdr_desc* d, const int32_t* cu_seqlens, int64_t n_seq, const void* q,
+                                     const void* k, const void* kw, const void* v, const void* beta,
+                                     const void* log_a, const float* S0, const void* dO, const float* dS_T, void* dq,
+                                     void* dk, void* dkw, void* dv, void* dbeta, void* dlog_a, float* dS0,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    g_last_error.clear();
+    if (!cu_seqlens) return fail(GDR_ERR_INVALID_ARG, "cu_seqlens is NULL");
+    if (!kw) return fail(GDR_ERR_INVALID_ARG, "kw is NULL");
+    if (!dkw) return fail(GDR_ERR_INVALID_ARG, "dkw is NULL");
+    return chunk_bwd_impl(d, cu_seqlens, n_seq, q, k, v, beta, log_a, S0, dO, dS_T, dq, dk, dv, dbeta, dlog_a, dS0,
+                          workspace, workspace_bytes, stream, kw, dkw);
   } catch (...) {
     return fail(GDR_ERR_INVALID_ARG, "internal error");
   }

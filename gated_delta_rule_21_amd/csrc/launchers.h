@@ -40,7 +40,7 @@ struct ChunkParams {
   const int32_t* cu;
   int64_t nslots;
   const int32_t* order;   // packed sequences: longest first (in the workspace, after the records)
-  const void* kw;         // write key [B, T, H, d_k] (no gate, bf16), or null: the state is written along k
+  const void* kw;         // write key [B, T, H, d_k] (bf16), or null: the state is written along k
 };
 
 struct PrecondParams {
@@ -71,9 +71,22 @@ struct BwdParams {
   void* states;         // B H ceil(T/64) chunk-start states, bf16 [d_v][d_k] each
   void* dstates;        // the gradients of the chunk-end states, same layout
 };
+// Reverse mode of the preconditioner scan (the gradients of <dkw, kw> + <dd_T, d_T>).
+struct PrecondBwdParams {
+  PrecondParams f;      // the forward's inputs (f.kw, f.d_T unused)
+  const void* dkw;      // [B, T, H, d_k] io dtype gradient of kw, or null (zero)
+  const float* dd_T;    // [B, H, d_k] gradient of d_T, or null (zero)
+  void* dk;             // [B, T, H, d_k] io dtype
+  void* dbeta;          // [B, T, H] io dtype
+  void* dr;             // [B, T, H] io dtype (f.r set), or null (not written)
+  float* dd0;           // [B, H, d_k], or null (not written)
+  float* ws;            // precond_scan_bwd_workspace_bytes: d_t of every token, then (x_t, n_t)
+};
+size_t precond_scan_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int d_k);
 hipError_t launch_decode_step(const DecodeParams& p, hipStream_t stream);
 // Preconditioner scan: one workgroup per (sequence, head).
 hipError_t launch_precond_scan(const PrecondParams& p, hipStream_t stream);
+hipError_t launch_precond_scan_bwd(const PrecondBwdParams& p, hipStream_t stream);
 // Per-chunk transform (T tiles into p.ws), then the state pass; one stream, in order.
 hipError_t launch_chunk_prep(const ChunkParams& p, hipStream_t stream);
 hipError_t launch_chunk_state_pipe(const ChunkParams& p, hipStream_t stream);   // bf16 I/O

@@ -542,6 +542,325 @@ static hipError_t launch_seq_t(const PrecondParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------------
+// Reverse mode of the scan, token by token, one wave per (sequence, head), in fp32
+// for both I/O dtypes.  With w_t = k_t^2, n_t = ||k_t||^2, x_t = <d_t, w_t>,
+// e_t = eta beta_t (1 - beta_t x_t) / n_t and D the gradient of d carried from the
+// end (D_T = dd_T), token t going backwards:
+//     u_t     = <D_{t+1}, w_t>,   dr_t = <D_{t+1}, d_t>,
+//     dbeta_t = u_t eta (1 - 2 beta_t x_t) / n_t,
+//     dk_t    = dkw_t * d_t + 2 k_t * (e_t D_{t+1} - u_t rho_t d_t - u_t e_t / n_t),
+//     D_t     = r_t D_{t+1} - u_t rho_t w_t + dkw_t * k_t,     rho_t = eta beta_t^2 / n_t,
+// and dd0 = D_0 (a zero key adds only dkw_t * d_t).  A first sweep runs the scan
+// forward and keeps every d_t and (x_t, n_t) in the workspace; the second walks the
+// tokens back, U at a time, loading the next U while the current ones run.
+// ---------------------------------------------------------------------------------
+// The CPL channels of one lane as raw words, one vector access (bf16: 2 or 4 bytes,
+// fp32: 4 or 8), unpacked only where they are used: a load whose value is converted
+// at once would make the compiler wait for it there, serialising the prefetch.
+template <int IO, int CPL>
+struct LaneRaw {
+  uint32_t w[IO == IO_BF16 ? 1 : CPL];
+};
+template <int IO, int CPL>
+__device__ __forceinline__ LaneRaw<IO, CPL> ld_raw(const void* base, int64_t i) {
+  LaneRaw<IO, CPL> r;
+  if constexpr (IO == IO_BF16) {
+    if constexpr (CPL == 2) r.w[0] = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(base) + i);
+    else r.w[0] = static_cast<const uint16_t*>(base)[i];
+  } else if constexpr (CPL == 2) {
+    const uint2 v = *reinterpret_cast<const uint2*>(static_cast<const float*>(base) + i);
+    r.w[0] = v.x;
+    r.w[1] = v.y;
+  } else {
+    r.w[0] = *reinterpret_cast<const uint32_t*>(static_cast<const float*>(base) + i);
+  }
+  return r;
+}
+template <int IO, int CPL>
+__device__ __forceinline__ void unpack(const LaneRaw<IO, CPL>& r, float (&x)[CPL]) {
+  if constexpr (IO == IO_BF16) {
+    x[0] = __uint_as_float(r.w[0] << 16);
+    if constexpr (CPL == 2) x[1] = __uint_as_float(r.w[0] & 0xffff0000u);
+  } else {
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) x[i] = __uint_as_float(r.w[i]);
+  }
+}
+template <int IO>
+__device__ __forceinline__ uint32_t ld_raw1(const void* base, int64_t i) {
+  if constexpr (IO == IO_BF16) return static_cast<const uint16_t*>(base)[i];
+  else return *reinterpret_cast<const uint32_t*>(static_cast<const float*>(base) + i);
+}
+template <int IO>
+__device__ __forceinline__ float unpack1(uint32_t w) {
+  return __uint_as_float(IO == IO_BF16 ? w << 16 : w);
+}
+template <int IO, int CPL>
+__device__ __forceinline__ void st_lane(void* base, int64_t i, const float (&x)[CPL]) {
+  if constexpr (IO == IO_BF16) {
+    if constexpr (CPL == 2)
+      *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(base) + i) =
+          static_cast<uint32_t>(f32_to_bf16_bits(x[0])) | (static_cast<uint32_t>(f32_to_bf16_bits(x[1])) << 16);
+    else
+      static_cast<uint16_t*>(base)[i] = f32_to_bf16_bits(x[0]);
+  } else {
+    if constexpr (CPL == 2) *reinterpret_cast<float2*>(static_cast<float*>(base) + i) = float2{x[0], x[1]};
+    else static_cast<float*>(base)[i] = x[0];
+  }
+}
+__device__ __forceinline__ float lane_bcast(uint32_t v, int src) {   // src: a compile-time constant in the loops below
+  return __int_as_float(__builtin_amdgcn_readlane(static_cast<int>(v), src));
+}
+
+// ---------------------------------------------------------------------------------
+// Reverse mode of the scan, token by token, one wave per (sequence, head), in fp32
+// for both I/O dtypes.  With w_t = k_t^2, n_t = ||k_t||^2, x_t = <d_t, w_t>,
+// e_t = eta beta_t (1 - beta_t x_t) / n_t and D the gradient of d carried from the
+// end (D_T = dd_T), token t going backwards:
+//     u_t     = <D_{t+1}, w_t>,   dr_t = <D_{t+1}, d_t>,
+//     dbeta_t = u_t eta (1 - 2 beta_t x_t) / n_t,
+//     dk_t    = dkw_t * d_t + 2 k_t * (e_t D_{t+1} - u_t rho_t d_t - u_t e_t / n_t),
+//     D_t     = r_t D_{t+1} - u_t rho_t w_t + dkw_t * k_t,     rho_t = eta beta_t^2 / n_t,
+// and dd0 = D_0 (a zero key adds only dkw_t * d_t).  A first sweep runs the scan
+// forward and keeps every d_t and (x_t, n_t) in the workspace; the second walks the
+// tokens back.  Both take U tokens at a time and load the next U meanwhile, every
+// load unconditional (clamped indexes; k stands in for a missing dkw, scaled by 0):
+// the lane's channels of k, dkw and d_t one vector access each, and the per-token
+// scalars (beta, r, x, n) once per block, token u on lane u, broadcast as they are
+// used.
+// ---------------------------------------------------------------------------------
+template <int IO, int DK, bool HAS_R>
+__global__ __launch_bounds__(64) void precond_scan_bwd_kernel(PrecondBwdParams q) {
+  const PrecondParams& p = q.f;
+  constexpr int CPL = DK / 64;
+  constexpr int U = 16;
+  typedef LaneRaw<IO, CPL> LR;
+  typedef LaneRaw<IO_F32, CPL> LF;
+  typedef typename Io<IO>::elem elem;
+  const int64_t bh = blockIdx.x;
+  const int64_t b = bh / p.H, h = bh - b * p.H;
+  const int64_t T = p.T, H = p.H;
+  const int lane = threadIdx.x;
+  const int c0 = lane * CPL;
+  float* __restrict__ wd = q.ws + bh * T * DK;                     // d_t, [T][DK]
+  float* __restrict__ wxn = q.ws + p.B * H * T * DK + bh * T * 2;  // (x_t, n_t), [T][2]
+  const void* gsrc = q.dkw ? q.dkw : p.k;                          // dkw, or k times 0
+  const float gscale = q.dkw ? 1.f : 0.f;
+  const void* rsrc = HAS_R ? p.r : p.beta;
+  auto row_of = [&](int64_t t) { return (b * T + t) * H + h; };
+  auto clampt = [&](int64_t t) { return t < 0 ? int64_t(0) : (t >= T ? T - 1 : t); };
+  // Stores and loads share one in-order memory counter, and a store's data registers
+  // may not be rewritten before it has read them; so each block's results are kept
+  // in registers of their own and stored at the start of the next block, before its
+  // prefetch, where waiting for them never waits for the prefetch.
+
+  // ---- forward: d_t of every token ----------------------------------------------------
+  float d[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) d[i] = p.d0 ? p.d0[bh * DK + c0 + i] : 1.f;
+  if (T > 0) {
+    LR kc[U], kn[U];
+    uint32_t bc, rc, bn = 0, rn = 0;              // token `lane` of the block (lanes >= U: unused)
+    float dsave[U][CPL], xs = 0.f, ns = 0.f;      // the block's d_t; (x, n) of token `lane`
+    auto load = [&](int64_t t0, LR (&kx)[U], uint32_t& bx, uint32_t& rx) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) kx[u] = ld_raw<IO, CPL>(p.k, row_of(clampt(t0 + u)) * DK + c0);
+      const int64_t row = row_of(clampt(t0 + lane));
+      bx = ld_raw1<IO>(p.beta, row);
+      rx = ld_raw1<IO>(rsrc, row);
+    };
+    auto store = [&](int64_t t0) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (t0 + u < T) st_lane<IO_F32, CPL>(wd, (t0 + u) * DK + c0, dsave[u]);
+      if (lane < U && t0 + lane < T) *reinterpret_cast<float2*>(wxn + 2 * (t0 + lane)) = float2{xs, ns};
+    };
+    load(0, kc, bc, rc);
+    for (int64_t t0 = 0; t0 < T; t0 += U) {
+      if (t0 > 0) store(t0 - U);
+      __builtin_amdgcn_sched_barrier(0);          // the stores stay ahead of the prefetch
+      load(t0 + U, kn, bn, rn);                   // unconditional (clamped): a conditional prefetch
+                                                  // would make the compiler wait for every load
+      // Off the chain: the 16 key norms n_t (independent sums, side by side) and, on
+      // lane u for token u, e_t = c1 - c2 x_t with c1 = eta beta / n, c2 = eta beta^2 / n
+      // (0 for a zero key or a token past the end) and the retention (1 past the end).
+      float w[U][CPL];
+      {
+        float nu[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          float kk[CPL];
+          unpack<IO, CPL>(kc[u], kk);
+          nu[u] = 0.f;
+#pragma unroll
+          for (int i = 0; i < CPL; ++i) {
+            w[u][i] = kk[i] * kk[i];
+            nu[u] += w[u][i];
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          nu[u] = wave_sum(nu[u]);
+          ns = lane == u ? nu[u] : ns;
+        }
+      }
+      const bool lvalid = t0 + lane < T && ns > 0.f;
+      const float bl = unpack1<IO>(bc), inv_nl = lvalid ? 1.f / ns : 0.f;
+      const float c1l = p.eta * bl * inv_nl, c2l = c1l * bl;
+      const float rl = HAS_R && t0 + lane < T ? unpack1<IO>(rc) : 1.f;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        // tokens past the end run as identity steps (no update, retention 1) and are
+        // not stored: no early exit, so the block's arrays stay in registers
+        float x = 0.f;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+          dsave[u][i] = d[i];
+          x = fmaf(d[i], w[u][i], x);
+        }
+        x = wave_sum(x);
+        xs = lane == u ? x : xs;
+        const float e = fmaf(-lane_bcast(__float_as_uint(c2l), u), x, lane_bcast(__float_as_uint(c1l), u));
+        const float rt = HAS_R ? lane_bcast(__float_as_uint(rl), u) : 1.f;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) d[i] = fmaf(e, w[u][i], rt * d[i]);
+      }
+      bc = bn;
+      rc = rn;
+#pragma unroll
+      for (int u = 0; u < U; ++u) kc[u] = kn[u];
+    }
+    store((T - 1) / U * U);
+  }
+  __threadfence_block();   // the sweep below reads what this wave wrote (x_t, n_t across lanes)
+  __syncthreads();
+
+  // ---- reverse ----------------------------------------------------------------------
+  float D[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) D[i] = q.dd_T ? q.dd_T[bh * DK + c0 + i] : 0.f;
+  if (T > 0) {
+    // the block of U tokens ending at token t1 - 1; lane u holds the scalars of token
+    // t1 - U + u (tokens before 0 read token 0 and are skipped).  Two sets of plain
+    // register arrays (a struct copy here went to scratch memory).
+    LR ck[U], cg[U], nk[U], ng[U];
+    LF cd[U], nd[U];
+    uint32_t cb, cr, nb = 0, nr = 0;
+    float cx, cn, nx = 0.f, nn = 0.f;
+    float gks[U][CPL], gbs = 0.f, grs = 0.f;    // the block's dk_t; dbeta, dr of token t1 - U + lane
+    auto load = [&](int64_t t1, LR (&zk)[U], LR (&zg)[U], LF (&zd)[U], uint32_t& zb, uint32_t& zr, float& zx,
+                    float& zn) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t t = clampt(t1 - U + u);
+        const int64_t row = row_of(t);
+        zk[u] = ld_raw<IO, CPL>(p.k, row * DK + c0);
+        zg[u] = ld_raw<IO, CPL>(gsrc, row * DK + c0);
+        zd[u] = ld_raw<IO_F32, CPL>(wd, t * DK + c0);
+      }
+      const int64_t tl = clampt(t1 - U + lane);
+      const int64_t row = row_of(tl);
+      zb = ld_raw1<IO>(p.beta, row);
+      zr = ld_raw1<IO>(rsrc, row);
+      const float2 xn = *reinterpret_cast<const float2*>(wxn + 2 * tl);
+      zx = xn.x;
+      zn = xn.y;
+    };
+    auto store = [&](int64_t t1) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (t1 - U + u >= 0) st_lane<IO, CPL>(q.dk, row_of(t1 - U + u) * DK + c0, gks[u]);
+      if (lane < U && t1 - U + lane >= 0) {
+        const int64_t row = row_of(t1 - U + lane);
+        Io<IO>::store(static_cast<elem*>(q.dbeta), row, gbs);
+        if (HAS_R && q.dr) Io<IO>::store(static_cast<elem*>(q.dr), row, grs);
+      }
+    };
+    load(T, ck, cg, cd, cb, cr, cx, cn);
+    for (int64_t t1 = T; t1 > 0; t1 -= U) {
+      if (t1 < T) store(t1 + U);
+      __builtin_amdgcn_sched_barrier(0);          // the stores stay ahead of the prefetch
+      load(t1 - U, nk, ng, nd, nb, nr, nx, nn);   // unconditional (clamped), as above
+      // Off the chain, on lane u for token t1 - U + u: e, rho, e / n, the dbeta factor
+      // and the retention (tokens before 0: identity steps, not stored, as above).
+      const bool lvalid = t1 - U + lane >= 0 && cn > 0.f;
+      const float bl = unpack1<IO>(cb), inv_nl = lvalid ? 1.f / cn : 0.f;
+      const float el = p.eta * bl * (1.f - bl * cx) * inv_nl, rhol = p.eta * bl * bl * inv_nl;
+      const float enl = el * inv_nl, dbl = p.eta * (1.f - 2.f * bl * cx) * inv_nl;
+      const float rl = HAS_R && t1 - U + lane >= 0 ? unpack1<IO>(cr) : 1.f;
+      const float gsl = t1 - U + lane >= 0 ? gscale : 0.f;
+#pragma unroll
+      for (int uu = U - 1; uu >= 0; --uu) {
+        float kk[CPL], gg[CPL], dd[CPL], w[CPL], pu = 0.f, pr = 0.f;
+        unpack<IO, CPL>(ck[uu], kk);
+        unpack<IO, CPL>(cg[uu], gg);
+        unpack<IO_F32, CPL>(cd[uu], dd);
+        const float gs = lane_bcast(__float_as_uint(gsl), uu);
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+          gg[i] *= gs;
+          w[i] = kk[i] * kk[i];
+          pu = fmaf(D[i], w[i], pu);
+          pr = fmaf(D[i], dd[i], pr);
+        }
+        const float u = wave_sum(pu);
+        const float g_r = HAS_R ? wave_sum(pr) : 0.f;
+        const float e = lane_bcast(__float_as_uint(el), uu), rho = lane_bcast(__float_as_uint(rhol), uu);
+        const float en = lane_bcast(__float_as_uint(enl), uu);
+        const float rt = HAS_R ? lane_bcast(__float_as_uint(rl), uu) : 1.f;
+        gbs = lane == uu ? u * dbl : gbs;
+        grs = lane == uu ? g_r : grs;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+          const float dw = e * D[i] - u * rho * dd[i] - u * en;
+          gks[uu][i] = fmaf(2.f * kk[i], dw, gg[i] * dd[i]);
+          D[i] = fmaf(gg[i], kk[i], fmaf(-u * rho, w[i], rt * D[i]));
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        ck[u] = nk[u];
+        cg[u] = ng[u];
+        cd[u] = nd[u];
+      }
+      cb = nb;
+      cr = nr;
+      cx = nx;
+      cn = nn;
+    }
+    store(T - (T - 1) / U * U);                 // the last block processed ends at that token count
+  }
+  if (q.dd0) {
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) q.dd0[bh * DK + c0 + i] = D[i];
+  }
+}
+
+template <int IO, int DK, bool HAS_R>
+static hipError_t launch_bwd_t(const PrecondBwdParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL((precond_scan_bwd_kernel<IO, DK, HAS_R>), dim3(static_cast<unsigned>(p.f.B * p.f.H)), dim3(64), 0,
+                     stream, p);
+  return hipGetLastError();
+}
+
+template <int IO>
+static hipError_t launch_bwd_io(const PrecondBwdParams& p, hipStream_t stream) {
+  const bool hr = p.f.r != nullptr;
+  if (p.f.d_k == 128) return hr ? launch_bwd_t<IO, 128, true>(p, stream) : launch_bwd_t<IO, 128, false>(p, stream);
+  if (p.f.d_k == 64) return hr ? launch_bwd_t<IO, 64, true>(p, stream) : launch_bwd_t<IO, 64, false>(p, stream);
+  return hipErrorInvalidValue;
+}
+
+size_t precond_scan_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int d_k) {
+  return static_cast<size_t>(B * H * T) * static_cast<size_t>(d_k + 2) * 4u;
+}
+
+hipError_t launch_precond_scan_bwd(const PrecondBwdParams& p, hipStream_t stream) {
+  if (p.f.B * p.f.H == 0) return hipSuccess;
+  return p.f.io == IO_BF16 ? launch_bwd_io<IO_BF16>(p, stream) : launch_bwd_io<IO_F32>(p, stream);
+}
+
 hipError_t launch_precond_scan(const PrecondParams& p, hipStream_t stream) {
   if (p.B * p.H == 0) return hipSuccess;
   const bool hr = p.r != nullptr;

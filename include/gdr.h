@@ -138,6 +138,10 @@ gdr_status gdr_chunk_fwd_workspace_size(const gdr_desc* desc, size_t* bytes);
  *                    stream).  Calls that overlap in time need separate ones.
  *   workspace_bytes  its size in bytes.
  *
+ * Supported: d_k, d_v in {64, 128} with every gate and form for bf16 I/O; fp32 I/O
+ * with every gate at d_k = 64 and without a gate or with a scalar gate at
+ * d_k = 128 (an fp32 per-channel gate at d_k = 128 returns GDR_ERR_UNSUPPORTED).
+ *
  * Two kernels run in order on `stream`: the per-chunk transform (cumulative
  * log-gate, the gated Gram blocks of the keys, (I + A)^{-1}, the masked score
  * matrix) for all chunks at once, then the sequential state pass with the output
@@ -272,6 +276,19 @@ gdr_status gdr_recurrent_step_wkey(const gdr_desc* desc, const void* q, const vo
                                    float* S_new, void* o, void* stream /* hipStream_t */);
 
 /*
+ * gdr_chunk_fwd_varlen_wkey -- gdr_chunk_fwd_wkey over variable-length sequences
+ * packed along T (phase 2 of the preconditioned rule on packed prompts).
+ *
+ * Every argument as for gdr_chunk_fwd_varlen, plus kw ([1, T, H, d_k] bf16) as for
+ * gdr_chunk_fwd_wkey; the workspace is gdr_chunk_fwd_varlen_workspace_size's.
+ * Supported and errors as for both calls.
+ */
+gdr_status gdr_chunk_fwd_varlen_wkey(const gdr_desc* desc, const int32_t* cu_seqlens, int64_t n_seq, const void* q,
+                                     const void* k, const void* kw, const void* v, const void* beta,
+                                     const void* log_a, const float* S0, void* o, float* S_T, void* workspace,
+                                     size_t workspace_bytes, void* stream /* hipStream_t */);
+
+/*
  * gdr_precond_scan -- the preconditioner scan that produces the write keys of the
  * preconditioned delta rule ("OSDN: Improving Delta Rule with Provable Online
  * Preconditioning in Linear Attention", §2.2: a first phase over the keys alone;
@@ -307,6 +324,46 @@ gdr_status gdr_recurrent_step_wkey(const gdr_desc* desc, const void* q, const vo
  */
 gdr_status gdr_precond_scan(const gdr_desc* desc, const void* k, const void* beta, const void* r, float eta,
                             const float* d0, void* kw, float* d_T, void* stream /* hipStream_t */);
+
+/*
+ * gdr_precond_scan_bwd_workspace_size -- device scratch for gdr_precond_scan_bwd:
+ * B * H * T * (d_k + 2) * 4 bytes (the preconditioner before every token and two
+ * fp32 sums per token).  Returns gdr_precond_scan_bwd's descriptor errors; *bytes is
+ * 0 on error.
+ */
+gdr_status gdr_precond_scan_bwd_workspace_size(const gdr_desc* desc, size_t* bytes);
+
+/*
+ * gdr_precond_scan_bwd -- gradients of the preconditioner scan (training the
+ * preconditioned delta rule, "OSDN: Improving Delta Rule with Provable Online
+ * Preconditioning in Linear Attention", §2.2 and §4: the write keys of phase 1
+ * feed phase 2, so the gradient of phase 2's write key flows back through the scan).
+ *
+ * For the scan gdr_precond_scan(desc, k, beta, r, eta, d0) with outputs kw and d_T,
+ * returns the gradients of L = <dkw, kw> + <dd_T, d_T> with respect to k, beta, r
+ * and d0 -- the reverse-mode derivatives of the scan's update, taken token by token
+ * (the pages print no gradients; a zero key, which leaves d unchanged, passes only
+ * dkw_t * d_t to k_t).
+ *
+ *   desc, k, beta, r, eta, d0   as for gdr_precond_scan (desc->d_v is not read)
+ *   dkw    [B, T, H, d_k] io dtype gradient of kw, or NULL (zero)
+ *   dd_T   [B, H, d_k] fp32 gradient of d_T, or NULL (zero)
+ *   dk     [B, T, H, d_k] io dtype, written (non-NULL when T > 0)
+ *   dbeta  [B, T, H] io dtype, written (non-NULL when T > 0)
+ *   dr     [B, T, H] io dtype, written; NULL to skip it; must be NULL when r is NULL
+ *   dd0    [B, H, d_k] fp32, written, or NULL to skip it; may equal dd_T
+ *   workspace / workspace_bytes  at least gdr_precond_scan_bwd_workspace_size bytes,
+ *          16-byte aligned, overwritten
+ *
+ * One wave per (sequence, head) runs the scan forward in fp32, keeping each token's
+ * preconditioner in the workspace, then walks the tokens back in fp32 (both dtypes).
+ * T == 0 writes dd0 = dd_T (or zeros).  Errors as for gdr_precond_scan, plus
+ * GDR_ERR_WORKSPACE for a missing or short workspace and the alias checks of the
+ * outputs against every other buffer.
+ */
+gdr_status gdr_precond_scan_bwd(const gdr_desc* desc, const void* k, const void* beta, const void* r, float eta,
+                                const float* d0, const void* dkw, const float* dd_T, void* dk, void* dbeta, void* dr,
+                                float* dd0, void* workspace, size_t workspace_bytes, void* stream /* hipStream_t */);
 
 /*
  * gdr_chunk_bwd_workspace_size -- device scratch that gdr_chunk_bwd needs.
@@ -400,6 +457,20 @@ gdr_status gdr_chunk_bwd_wkey(const gdr_desc* desc, const void* q, const void* k
                               const void* beta, const void* log_a, const float* S0, const void* dO, const float* dS_T,
                               void* dq, void* dk, void* dkw, void* dv, void* dbeta, void* dlog_a, float* dS0,
                               void* workspace, size_t workspace_bytes, void* stream /* hipStream_t */);
+
+/*
+ * gdr_chunk_bwd_varlen_wkey -- gdr_chunk_bwd_wkey over variable-length sequences
+ * packed along T (training the preconditioned rule on packed sequences).
+ *
+ * The gradients of gdr_chunk_fwd_varlen_wkey's forward; every argument as for
+ * gdr_chunk_bwd_varlen, plus kw and dkw ([1, T, H, d_k] bf16) as for
+ * gdr_chunk_bwd_wkey.  Supported, precision and errors as for both calls.
+ */
+gdr_status gdr_chunk_bwd_varlen_wkey(const gdr_desc* desc, const int32_t* cu_seqlens, int64_t n_seq, const void* q,
+                                     const void* k, const void* kw, const void* v, const void* beta,
+                                     const void* log_a, const float* S0, const void* dO, const float* dS_T, void* dq,
+                                     void* dk, void* dkw, void* dv, void* dbeta, void* dlog_a, float* dS0,
+                                     void* workspace, size_t workspace_bytes, void* stream /* hipStream_t */);
 
 /*
  * gdr_chunk_bwd_varlen_workspace_size -- scratch for gdr_chunk_bwd_varlen.

@@ -117,8 +117,12 @@ def test_bad_descriptor_fields(lib, field, value, code):
     assert _chunk(lib, _desc(**{field: value}), _ptrs()) == code
 
 
-def test_fp32_io_with_dk128_is_unsupported(lib):
-    assert _chunk(lib, _desc(io=0), _ptrs()) == UNSUPPORTED
+def test_fp32_io_with_dk128_per_channel_gate_is_unsupported(lib):
+    # fp32 I/O at d_k = 128 is offered without a gate or with a scalar gate only
+    assert _chunk(lib, _desc(io=0, gate=2), _ptrs()) == UNSUPPORTED
+    n = ctypes.c_size_t(7)
+    for gate, code in ((0, OK), (1, OK), (2, UNSUPPORTED)):
+        assert lib.gdr_chunk_fwd_workspace_size(ctypes.byref(_desc(io=0, gate=gate)), ctypes.byref(n)) == code, gate
 
 
 @pytest.mark.parametrize("which", range(5))
@@ -416,3 +420,66 @@ def test_binding_rejects_strided_offsets(lib):
         gdr.chunk_fwd_varlen(x, x, x, beta, None, cu)
     with pytest.raises(ValueError, match="GPU tensor"):          # a dense table passes this check
         gdr.chunk_bwd(x, x, x, beta, None, None, x, cu_seqlens=cu.contiguous())
+
+
+def _scan_bwd(lib, d, p, eta=1.0, ws_bytes=1 << 40):
+    """gdr_precond_scan_bwd with p = (k, beta, r, d0, dkw, dd_T, dk, dbeta, dr, dd0, ws)."""
+    return lib.gdr_precond_scan_bwd(None if d is None else ctypes.byref(d), p[0], p[1], p[2], ctypes.c_float(eta),
+                                    *p[3:10], p[10], ws_bytes, None)
+
+
+def test_precond_scan_backward_checks(lib):
+    n = ctypes.c_size_t(7)
+    d = _desc(B=2, T=100, H=3, d_k=64)
+    assert lib.gdr_precond_scan_bwd_workspace_size(ctypes.byref(d), ctypes.byref(n)) == OK
+    assert n.value == 2 * 3 * 100 * (64 + 2) * 4
+    assert lib.gdr_precond_scan_bwd_workspace_size(ctypes.byref(_desc(d_k=96)), ctypes.byref(n)) == UNSUPPORTED
+    assert n.value == 0
+    p = _ptrs(11)
+    d = _desc()
+    assert _scan_bwd(lib, None, p) == INVALID
+    for i, name in ((0, "k"), (1, "beta"), (6, "dk"), (7, "dbeta")):
+        bad = list(p)
+        bad[i] = None
+        assert _scan_bwd(lib, d, bad) == INVALID, name
+        assert name.encode() in lib.gdr_last_error()
+    bad = list(p)
+    bad[10] = None
+    assert _scan_bwd(lib, d, bad) == WORKSPACE
+    assert _scan_bwd(lib, d, p, ws_bytes=16) == WORKSPACE
+    bad = list(p)
+    bad[2] = None                                                          # dr given without r
+    assert _scan_bwd(lib, d, bad) == INVALID
+    assert _scan_bwd(lib, d, p, eta=float("nan")) == INVALID
+    assert _scan_bwd(lib, _desc(d_k=96), p) == UNSUPPORTED
+    for i in (0, 4, 6):                                                    # k, dkw, dk: 16-byte operands
+        bad = list(p)
+        bad[i] += 8
+        assert _scan_bwd(lib, d, bad) == ALIGN, i
+    bad = list(p)
+    bad[6] = bad[0] + 64                                                   # dk inside k
+    assert _scan_bwd(lib, d, bad) == INVALID
+    assert b"dk overlaps k" in lib.gdr_last_error()
+    bad = list(p)
+    bad[9] = bad[5] + 4                                                    # dd0 inside dd_T, not equal
+    assert _scan_bwd(lib, d, bad) == INVALID
+
+
+def test_packed_write_key_checks(lib):
+    d = _desc(B=1, T=300, H=2)
+    p = _ptrs(12)
+    fwd = lambda d, cu, ns, q: lib.gdr_chunk_fwd_varlen_wkey(ctypes.byref(d), cu, ns, *q[:9], q[9], 1 << 40, None)
+    assert fwd(d, None, 3, p) == INVALID                                   # no offset table
+    bad = list(p)
+    bad[2] = None
+    assert fwd(d, FAKE, 3, bad) == INVALID                                 # no write key
+    assert b"kw" in lib.gdr_last_error()
+    assert fwd(_desc(B=1, T=300, H=2, io=0), FAKE, 3, p) == UNSUPPORTED    # packed: bf16 only
+    q = _ptrs(18)
+    bwd = lambda d, cu, ns, q: lib.gdr_chunk_bwd_varlen_wkey(ctypes.byref(d), cu, ns, *q[:16], q[16], 1 << 40, None)
+    assert bwd(d, None, 3, q) == INVALID
+    for i, name in ((2, "kw"), (11, "dkw")):
+        bad = list(q)
+        bad[i] = None
+        assert bwd(d, FAKE, 3, bad) == INVALID, name
+    assert bwd(_desc(B=1, T=300, H=2, gate=2), FAKE, 3, q) == UNSUPPORTED  # no per-channel gate with a write key

@@ -193,3 +193,52 @@ def test_autograd_function_write_key(gate):
         if t is None:
             continue
         check(n, host(t.grad), ref[n], TOL["bf16"])
+
+
+@pytest.mark.parametrize("gate", ["scalar", "none"])
+def test_bwd_wkey_varlen(gate):
+    """gdr_chunk_bwd_varlen_wkey: packed sequences of lengths 0, 1, 63, 64, 65, 130,
+    200, 7 against the oracle per sequence, and bit for bit against the fixed-length
+    write-key backward on each sequence alone."""
+    need_gpu()
+    import torch
+    import gated_delta_rule_21_amd as gdr
+    say(f"case bwd write key, packed sequences, gate={gate}")
+    lens = [0, 1, 63, 64, 65, 130, 200, 7]
+    T = int(sum(lens))
+    wl = Workload("bwd_wkey_varlen", B=1, T=T, H=2, d_k=128, d_v=128, io="bf16", gate=gate, s0_std=0.0, seed=97)
+    x = chunk_inputs(wl)
+    x["dO"] = grad_inputs(wl)["dO"]
+    per = Workload("bwd_wkey_varlen_states", B=len(lens), T=1, H=2, d_k=128, d_v=128, io="bf16", gate=gate,
+                   s0_std=0.5, seed=98)
+    x["S0"] = chunk_inputs(per)["S0"]
+    x["dS_T"] = grad_inputs(per)["dS_T"]
+    _with_kw(x, 99)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    t = lambda n: dev(x[n], "bf16")
+    g = gdr.chunk_bwd(t("q"), t("k"), t("v"), t("beta"), t("log_a"), torch.from_numpy(x["S0"]).cuda(), t("dO"),
+                      torch.from_numpy(x["dS_T"]).cuda(), cu_seqlens=torch.from_numpy(cu).cuda(), kw=t("kw"))
+    torch.cuda.synchronize()
+    gh = {n: host(v) if v is not None else None for n, v in g.items()}
+    seq = lambda a, lo, hi: None if a is None else np.ascontiguousarray(a[:, lo:hi])
+    names = ("dq", "dk", "dkw", "dv", "dbeta") + (("dlog_a",) if gate == "scalar" else ())
+    ref = {n: np.zeros(gh[n].shape) for n in names}
+    ref["dS0"] = np.zeros(x["S0"].shape)
+    for i in range(len(lens)):
+        lo, hi = int(cu[i]), int(cu[i + 1])
+        s = {n: seq(x[n], lo, hi) for n in ("q", "k", "kw", "v", "beta", "log_a", "dO")}
+        r = oracle_backward(s["q"], s["k"], s["v"], s["beta"], s["log_a"], x["S0"][i:i + 1], s["dO"],
+                            x["dS_T"][i:i + 1], kw=s["kw"])
+        for n in names:
+            ref[n][:, lo:hi] = r[n]
+        ref["dS0"][i] = r["dS0"][0]
+        if hi > lo:
+            a = gdr.chunk_bwd(*(dev(s[n], "bf16") for n in ("q", "k", "v", "beta", "log_a")),
+                              torch.from_numpy(x["S0"][i:i + 1]).cuda(), dev(s["dO"], "bf16"),
+                              torch.from_numpy(x["dS_T"][i:i + 1]).cuda(), kw=dev(s["kw"], "bf16"))
+            torch.cuda.synchronize()
+            for n in names:
+                assert np.array_equal(host(a[n]), gh[n][:, lo:hi]), f"sequence {i}: {n} differs from the call on it alone"
+            assert np.array_equal(host(a["dS0"])[0], gh["dS0"][i]), f"sequence {i}: dS0"
+    for n in names + ("dS0",):
+        check(n, gh[n], ref[n], TOL["bf16"])

@@ -65,6 +65,16 @@ def test_four_wave_tiles():
     _run(_wl("wide", 1, 130, 128, 128, 128, gate="scalar", seed=23))
 
 
+@pytest.mark.parametrize("gate,form", [("none", "page"), ("scalar", "page"), ("scalar", "literal")])
+@pytest.mark.parametrize("shape", [(2, 200, 3, 128, 128), (1, 130, 2, 128, 64), (1, 1, 2, 128, 128)],
+                         ids=lambda s: "B%dT%dH%d_dk%d_dv%d" % s)
+def test_fp32_dk128(gate, form, shape):
+    """fp32 I/O at d_k = 128 (no gate or a scalar gate): the transform through LDS and
+    the single-buffered fp32 state pass."""
+    B, T, H, dk, dv = shape
+    _run(_wl("f32d128", B, T, H, dk, dv, io="f32", gate=gate, seed=37 + T + dv), form=form)
+
+
 def test_fp32_channel_gate():
     _run(_wl("f32ch", 2, 150, 2, 64, 128, io="f32", gate="channel", seed=29))
 

@@ -20,13 +20,15 @@ def _wl(name, B, T, H, dk, dv, io="bf16", gate="scalar", seed=11):
     return Workload(name, B=B, T=T, H=H, d_k=dk, d_v=dv, io=io, gate=gate, s0_std=0.05, seed=seed)
 
 
-@pytest.mark.parametrize("io,dk", [("bf16", 128), ("f32", 64)])
+@pytest.mark.parametrize("io,dk", [("bf16", 128), ("f32", 64), ("f32", 128)])
 @pytest.mark.parametrize("gate", ["none", "scalar", "channel"])
 @pytest.mark.parametrize("form", ["page", "literal"])
 def test_chunk_forward_equals_token_steps(io, dk, gate, form):
     """chunk_fwd over 150 tokens against 150 gdr_recurrent_step calls (state carried
     in place): o of every token and the final state, relative L2 within the I/O
     dtype's tolerance."""
+    if io == "f32" and dk == 128 and gate == "channel":
+        pytest.skip("the per-channel fp32 chunk forward takes d_k = 64")
     need_gpu()
     import torch
     import gated_delta_rule_21_amd as gdr

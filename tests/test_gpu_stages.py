@@ -150,11 +150,13 @@ def _wl(B, T, H, dk, dv, io, gate, seed):
     return Workload("stages", B=B, T=T, H=H, d_k=dk, d_v=dv, io=io, gate=gate, s0_std=0.02, seed=seed)
 
 
-@pytest.mark.parametrize("io,dk", [("bf16", 128), ("bf16", 64), ("f32", 64)])
+@pytest.mark.parametrize("io,dk", [("bf16", 128), ("bf16", 64), ("f32", 64), ("f32", 128)])
 @pytest.mark.parametrize("gate", ["none", "scalar", "channel"])
 def test_transform_records(io, dk, gate):
     if gate == "channel" and io == "bf16" and dk != 128:
         pytest.skip("the per-channel bf16 forward takes d_k = 128")
+    if gate == "channel" and io == "f32" and dk != 64:
+        pytest.skip("the per-channel fp32 forward takes d_k = 64")
     say(f"case transform records io={io} d_k={dk} gate={gate}")
     _run(chunk_inputs(_wl(2, 200, 3, dk, 128, io, gate, seed=101 + dk + len(gate))), io, gate)
 

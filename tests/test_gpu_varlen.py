@@ -159,3 +159,37 @@ def test_varlen_order_longest_first():
     assert list(order) == want, (list(order), want)
     o_ref, S_ref = _oracle(inp, S0, cu)
     _check_each(o, S, o_ref, S_ref, cu)
+
+
+@pytest.mark.parametrize("gate", ["none", "scalar", "channel"])
+def test_varlen_write_key(gate):
+    """gdr_chunk_fwd_varlen_wkey: each packed sequence against the write-key oracle of
+    that sequence alone, and bit for bit against gdr_chunk_fwd_wkey on it."""
+    need_gpu()
+    import torch
+    import gated_delta_rule_21_amd as gdr
+    say(f"case varlen write key gate={gate} lens={LENS}")
+    inp, S0, cu = _inputs(LENS, 2, 128, 128, gate, seed=91 + len(gate))
+    rng = np.random.default_rng(92)
+    from workloads import round_to_io
+    kw = round_to_io(inp["k"].astype(np.float64) * rng.uniform(0.2, 2.0, inp["k"].shape), "bf16")
+    args = [dev(inp[n], "bf16") for n in ("q", "k", "v", "beta", "log_a")]
+    o, S = gdr.chunk_fwd_varlen(*args, torch.from_numpy(cu).cuda(), torch.from_numpy(S0).cuda(), kw=dev(kw, "bf16"))
+    torch.cuda.synchronize()
+    o_h, S_h = host(o), host(S)
+    o_ref = np.zeros(inp["v"].shape)
+    S_ref = np.zeros(S0.shape)
+    for i in range(len(cu) - 1):
+        lo, hi = int(cu[i]), int(cu[i + 1])
+        oi, Si = oracle_forward(*(_seq(inp[n], lo, hi) for n in ("q", "k", "v", "beta", "log_a")), S0[i:i + 1],
+                                kw=_seq(kw, lo, hi))
+        o_ref[:, lo:hi] = oi
+        S_ref[i] = Si[0]
+        if hi > lo:
+            a = [dev(_seq(inp[n], lo, hi), "bf16") for n in ("q", "k", "v", "beta", "log_a")]
+            oa, Sa = gdr.chunk_fwd(*a, torch.from_numpy(S0[i:i + 1]).cuda(), kw=dev(_seq(kw, lo, hi), "bf16"))
+            torch.cuda.synchronize()
+            assert np.array_equal(host(oa), o_h[:, lo:hi]), f"sequence {i}: o differs from the call on it alone"
+            assert np.array_equal(host(Sa)[0], S_h[i]), f"sequence {i}: S_T differs from the call on it alone"
+    check("o", o_h, o_ref, TOL["bf16"])
+    check("S_T", S_h, S_ref, TOL["bf16"])
