@@ -143,10 +143,12 @@ __global__ __launch_bounds__(NW * 64) void chunk_fwd_kernel(ChunkParams p, int n
   const int lg = lane >> 4;
   const int scol = col0 + 16 * wave + lr;   // this lane's state column
 
-  const int64_t nchunks = (p.T + CH - 1) / CH;
+  // This sequence's tokens (a packed sequence's from the offset table) and records.
+  const SeqSpan sq = seq_span(p, bb, hh);
+  const int64_t nchunks = (sq.len + CH - 1) / CH;
   // Buffers over this sequence's (b, h) slice; each range ends after the last token.
-  const int64_t row0 = bb * p.T * p.H + hh;            // token-row index of (b, t = 0, h)
-  const uint32_t span = static_cast<uint32_t>(p.T > 0 ? (p.T - 1) * p.H + 1 : 0);   // rows in range
+  const int64_t row0 = sq.t0 * p.H + hh;               // token-row index of (b, t = 0, h)
+  const uint32_t span = static_cast<uint32_t>(sq.len > 0 ? (sq.len - 1) * p.H + 1 : 0);   // rows in range
   const rsrc_t rk = make_rsrc(static_cast<const elem*>(p.k) + row0 * DK, span * DK * ESZ);
   const rsrc_t rq = make_rsrc(static_cast<const elem*>(p.q) + row0 * DK, span * DK * ESZ);
   const rsrc_t rv = make_rsrc(static_cast<const elem*>(p.v) + row0 * dv, span * dv * ESZ);
@@ -154,9 +156,9 @@ __global__ __launch_bounds__(NW * 64) void chunk_fwd_kernel(ChunkParams p, int n
   const rsrc_t rb = make_rsrc(static_cast<const elem*>(p.beta) + row0, span * ESZ);
   const rsrc_t rl = make_rsrc(static_cast<const elem*>(p.log_a) + row0 * (GATE == GATE_CHANNEL ? DK : 1),
                               GATE == GATE_NONE ? 0u : span * (GATE == GATE_CHANNEL ? DK : 1) * ESZ);
-  const rsrc_t rw = make_rsrc(static_cast<const char*>(p.ws) + bh * nchunks * W::BYTES,
+  const rsrc_t rw = make_rsrc(static_cast<const char*>(p.ws) + sq.rec0 * W::BYTES,
                               static_cast<uint32_t>(nchunks * W::BYTES));
-  static_assert(IO == IO_F32, "bf16 I/O runs the chain/helper kernel (chunk_state.hip)");   // fixed-length only
+  static_assert(IO == IO_F32, "bf16 I/O runs the chain/helper kernel (chunk_state.hip)");
   // per-thread byte offsets within a chunk (the chunk start goes in the scalar offset)
   uint32_t offk[KV], offv[VV];
 #pragma unroll

@@ -1082,7 +1082,6 @@ static hipError_t launch_prep_io(const ChunkParams& p, int64_t nchunks, hipStrea
 hipError_t launch_chunk_prep(const ChunkParams& p, hipStream_t stream) {
   const int64_t nchunks = (p.T + CH - 1) / CH;
   if (p.B * p.H * nchunks == 0) return hipSuccess;
-  if (p.cu && p.io != IO_BF16) return hipErrorInvalidValue;   // packed sequences: bf16 kernels only
   return p.io == IO_BF16 ? launch_prep_io<IO_BF16>(p, nchunks, stream) : launch_prep_io<IO_F32>(p, nchunks, stream);
 }
 

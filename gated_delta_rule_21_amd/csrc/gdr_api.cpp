@@ -171,7 +171,6 @@ gdr_status chunk_fwd_impl(const gdr_desc* d, const int32_t* cu, int64_t n_seq, c
     if (!cu) return fail(GDR_ERR_INVALID_ARG, "cu_seqlens is NULL");
     if (n_seq < 1) return fail(GDR_ERR_INVALID_ARG, "n_seq = %lld must be >= 1", (long long)n_seq);
     if (d->B != 1) return fail(GDR_ERR_INVALID_ARG, "B = %lld: packed sequences take B = 1 (all tokens in T)", (long long)d->B);
-    if (d->io != GDR_BF16) return fail(GDR_ERR_UNSUPPORTED, "packed sequences: bf16 I/O only");
     int64_t x;
     if (!mul_ok(n_seq, d->H, &x) || x * 8 > INT32_MAX || d->H * gdr::chunk_varlen_slots(d->T, n_seq) > INT32_MAX)
       return fail(GDR_ERR_UNSUPPORTED, "n_seq = %lld: exceeds the grid limit", (long long)n_seq);
@@ -275,7 +274,6 @@ gdr_status gdr_chunk_fwd_varlen_workspace_size(const gdr_desc* d, int64_t n_seq,
     if (st != GDR_OK) return st;
     if (n_seq < 1) return fail(GDR_ERR_INVALID_ARG, "n_seq = %lld must be >= 1", (long long)n_seq);
     if (d->B != 1) return fail(GDR_ERR_INVALID_ARG, "B = %lld: packed sequences take B = 1 (all tokens in T)", (long long)d->B);
-    if (d->io != GDR_BF16) return fail(GDR_ERR_UNSUPPORTED, "packed sequences: bf16 I/O only");
     *bytes = gdr::chunk_varlen_workspace_bytes(d->T, n_seq, d->H, d->io, d->gate, static_cast<int>(d->d_k));
     return GDR_OK;
   } catch (...) {
@@ -304,6 +302,7 @@ gdr_status gdr_chunk_fwd_varlen_wkey(const gdr_desc* d, const int32_t* cu_seqlen
     g_last_error.clear();
     if (!cu_seqlens) return fail(GDR_ERR_INVALID_ARG, "cu_seqlens is NULL");
     if (!kw) return fail(GDR_ERR_INVALID_ARG, "kw is NULL");
+    if (d && d->io != GDR_BF16) return fail(GDR_ERR_UNSUPPORTED, "write key chunk forward: bf16 I/O only");
     if (d && d->gate == GDR_GATE_CHANNEL && d->d_k != 128)
       return fail(GDR_ERR_UNSUPPORTED, "write key with a per-channel gate: d_k = 128 only");
     return chunk_fwd_impl(d, cu_seqlens, n_seq, q, k, v, beta, log_a, S0, o, S_T, workspace, workspace_bytes,

@@ -185,8 +185,9 @@ gdr_status gdr_chunk_fwd_noalloc(const gdr_desc* desc, const void* q, const void
  * record slots from floor(cu_seqlens[i] / 64) + i on, so H * (ceil(T / 64) +
  * n_seq) records of the size given under gdr_chunk_fwd_workspace_size cover
  * any split of the T tokens; then 4 * n_seq bytes (rounded up to 16) hold the
- * order, longest sequence first, in which the state pass takes the sequences.
- * bf16 I/O only (GDR_ERR_UNSUPPORTED otherwise).
+ * order, longest sequence first, in which the bf16 state pass takes the sequences
+ * (the fp32 one, which serves parity, takes them in order).  Both dtypes, with the
+ * configurations of gdr_chunk_fwd.
  */
 gdr_status gdr_chunk_fwd_varlen_workspace_size(const gdr_desc* desc, int64_t n_seq, size_t* bytes);
 

@@ -200,7 +200,9 @@ def test_varlen_workspace_size(lib):
     assert _ws_varlen(lib, _desc(T=130, H=3, gate=2), 2) == (OK, 3 * (3 + 2) * (rec + 3 * 64 * 128 * 2) + 16)
     assert _ws_varlen(lib, _desc(T=130, H=3), 0) == (INVALID, 0)
     assert _ws_varlen(lib, _desc(B=2), 2) == (INVALID, 0)                  # packed tensors take B = 1
-    assert _ws_varlen(lib, _desc(io=0, d_k=64), 2) == (UNSUPPORTED, 0)     # bf16 only
+    rec32 = 2 * 10 * 256 * 4 + 6 * 64 * 4                                  # fp32 records
+    assert _ws_varlen(lib, _desc(io=0, d_k=64), 2) == (OK, 2 * (1 + 2) * rec32 + 16)
+    assert _ws_varlen(lib, _desc(io=0, d_k=128, gate=2), 2) == (UNSUPPORTED, 0)   # fp32 per-channel: d_k = 64
     assert _ws_varlen(lib, None, 2) == (INVALID, 0)
 
 
@@ -210,7 +212,7 @@ def test_varlen_argument_checks(lib):
     assert _chunk_varlen(lib, _desc(), None, 2, _ptrs()) == INVALID
     assert b"cu_seqlens" in lib.gdr_last_error()
     assert _chunk_varlen(lib, _desc(), cu, 0, _ptrs()) == INVALID
-    assert _chunk_varlen(lib, _desc(io=0, d_k=64), cu, 2, _ptrs()) == UNSUPPORTED
+    assert _chunk_varlen(lib, _desc(io=0, d_k=128, gate=2), cu, 2, _ptrs()) == UNSUPPORTED
     assert _chunk_varlen(lib, _desc(), cu + 2, 2, _ptrs()) == ALIGN
     p = _ptrs()
     assert _chunk_varlen(lib, _desc(), p[6] + 16, 2, p) == INVALID        # offsets inside o
@@ -474,7 +476,7 @@ def test_packed_write_key_checks(lib):
     bad[2] = None
     assert fwd(d, FAKE, 3, bad) == INVALID                                 # no write key
     assert b"kw" in lib.gdr_last_error()
-    assert fwd(_desc(B=1, T=300, H=2, io=0), FAKE, 3, p) == UNSUPPORTED    # packed: bf16 only
+    assert fwd(_desc(B=1, T=300, H=2, io=0), FAKE, 3, p) == UNSUPPORTED    # write key: bf16 only
     q = _ptrs(18)
     bwd = lambda d, cu, ns, q: lib.gdr_chunk_bwd_varlen_wkey(ctypes.byref(d), cu, ns, *q[:16], q[16], 1 << 40, None)
     assert bwd(d, None, 3, q) == INVALID

@@ -193,3 +193,36 @@ def test_varlen_write_key(gate):
             assert np.array_equal(host(Sa)[0], S_h[i]), f"sequence {i}: S_T differs from the call on it alone"
     check("o", o_h, o_ref, TOL["bf16"])
     check("S_T", S_h, S_ref, TOL["bf16"])
+
+
+@pytest.mark.parametrize("gate,dk", [("none", 64), ("scalar", 64), ("channel", 64), ("none", 128), ("scalar", 128)])
+def test_varlen_fp32(gate, dk):
+    """fp32 I/O over packed sequences: each sequence against the oracle of that sequence
+    alone (1e-4) and bit for bit against gdr_chunk_fwd on it."""
+    need_gpu()
+    import torch
+    import gated_delta_rule_21_amd as gdr
+    say(f"case varlen fp32 gate={gate} d_k={dk} lens={LENS}")
+    T = int(sum(LENS))
+    inp = chunk_inputs(Workload("varlen32", B=1, T=T, H=2, d_k=dk, d_v=64, io="f32", gate=gate, s0_std=0.0,
+                                seed=111 + dk + len(gate)))
+    S0 = chunk_inputs(Workload("varlen32_s0", B=len(LENS), T=1, H=2, d_k=dk, d_v=64, io="f32", gate=gate,
+                               s0_std=0.02, seed=112))["S0"]
+    cu = np.concatenate([[0], np.cumsum(LENS)]).astype(np.int32)
+    args = [dev(inp[n], "f32") for n in ("q", "k", "v", "beta", "log_a")]
+    o, S = gdr.chunk_fwd_varlen(*args, torch.from_numpy(cu).cuda(), torch.from_numpy(S0).cuda())
+    torch.cuda.synchronize()
+    o_h, S_h = host(o), host(S)
+    o_ref, S_ref = _oracle(inp, S0, cu)
+    check("o", o_h, o_ref, TOL["f32"])
+    check("S_T", S_h, S_ref, TOL["f32"])
+    for i in range(len(cu) - 1):
+        lo, hi = int(cu[i]), int(cu[i + 1])
+        if hi == lo:
+            assert np.array_equal(S_h[i], S0[i].astype(np.float64)), f"empty sequence {i}: S_T != S0"
+            continue
+        a = [dev(_seq(inp[n], lo, hi), "f32") for n in ("q", "k", "v", "beta", "log_a")]
+        oa, Sa = gdr.chunk_fwd(*a, torch.from_numpy(S0[i:i + 1]).cuda())
+        torch.cuda.synchronize()
+        assert np.array_equal(host(oa), o_h[:, lo:hi]), f"sequence {i}: o differs from the call on it alone"
+        assert np.array_equal(host(Sa)[0], S_h[i]), f"sequence {i}: S_T differs from the call on it alone"
