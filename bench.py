@@ -15,7 +15,9 @@ workload's keys (`precond_scan`, GB/s against HBM peak), and the chunk forward
 with the write keys it produced (`osdn`: phase 2, no gate, and the two phases'
 tokens/s), and the backward of the chunk forward over the same workload
 (`backward`: the gradients of q, k, v, beta, log a and S0 for given dO and dS_T;
-`train_step_tokens_per_s` counts the forward and the backward together).
+`train_step_tokens_per_s` counts the forward and the backward together; its
+`training_path` times the forward that keeps the chunk-start states,
+gdr_chunk_fwd_save, and the backward that takes them, gdr_chunk_bwd_saved).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
@@ -352,14 +354,17 @@ def bwd_bytes(wl, with_S0: bool):
     return rd + wr
 
 
-def bwd_algorithmic(wl):
+def bwd_algorithmic(wl, saved: bool = False):
     """Useful flops of the backward per launch: per chunk (C = 64, d = d_k = d_v),
     the chunk-start states 4 C d^2 + C^2 d (K S, T X, K^T Delta), the reverse pass
     6 C d^2 + 3 C^2 d (P, K dS', P^T dO, T^T dDelta, Q^T dO, K^T Z) and the
     per-chunk gradients 10 C d^2 + 11 C^2 d (five state products, eleven 64-row
-    products, the masked ones counted at half)."""
+    products, the masked ones counted at half).  `saved`: the chunk-start states
+    come from the training forward and are not counted."""
     C, d = 64, wl.d_k
     per_chunk = 20 * C * d * d + 15 * C * C * d
+    if saved:
+        per_chunk -= 4 * C * d * d + C * C * d
     return wl.B * wl.H * ((wl.T + C - 1) // C) * per_chunk
 
 
@@ -394,9 +399,29 @@ def bench_bwd(prep, args, log, wl, q, k, v, beta, log_a, S0):
                            args.warmup, args.steps)
         del kw
         log(f"chunk backward with a write key: {wk_ms:.3f} ms/step")
+    # the training path: the forward keeps the transform's records and the
+    # chunk-start states in the backward's workspace (gdr_chunk_fwd_save) and the
+    # backward takes them from there (gdr_chunk_bwd_saved)
+    import torch
+    o_s, S_s = torch.empty_like(v), torch.empty((wl.B, wl.H, wl.d_k, wl.d_v), dtype=torch.float32, device="cuda")
+    fs_ms = time_calls(lambda i: gdr.chunk_fwd_save(q, k, v, beta, log_a, S0, o=o_s, S_T=S_s, workspace=ws),
+                       args.warmup, args.steps)
+    bs_ms = time_calls(lambda i: gdr.chunk_bwd(q, k, v, beta, log_a, S0, dO, dS_T, saved=ws), args.warmup, args.steps)
+    del o_s, S_s
+    sflops = bwd_algorithmic(wl, saved=True)
+    stf = sflops / (bs_ms * 1e-3) / 1e12
+    log(f"training path: forward keeping its states {fs_ms:.3f} ms, backward taking them {bs_ms:.3f} ms "
+        f"({stf:.1f} TFLOP/s useful)")
+    saved = {"forward_ms_per_launch": round(fs_ms, 4), "backward_ms_per_launch": round(bs_ms, 4),
+             "backward_useful_flops_per_launch": sflops,
+             "train_step_ms": round(fs_ms + bs_ms, 4),
+             "train_step_tokens_per_s": round(wl.B * wl.T / ((fs_ms + bs_ms) * 1e-3), 1),
+             "backward_roofline": {"bound": "mfma", "achieved": round(stf, 2), "peak": BF16_PEAK_TFLOPS,
+                                   "unit": "TFLOP/s", "frac": round(stf / BF16_PEAK_TFLOPS, 4), "traffic": None}}
     return {"workload": wl.name + "_backward", "value": round(wl.B * wl.T / (ms * 1e-3), 1), "unit": "tokens/s",
             "ms_per_launch": round(ms, 4), "useful_flops_per_launch": flops,
             "write_key_ms_per_launch": None if wk_ms is None else round(wk_ms, 4),
+            "training_path": saved,
             "algorithmic_bytes_per_launch": bwd_bytes(wl, S0 is not None),
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf / BF16_PEAK_TFLOPS, 4),
@@ -580,6 +605,8 @@ def main():
     rec = bench_chunk(head, args.warmup, args.steps, log, "headline")
     ms = rec["ms_per_call"]
     if bwd is not None:
+        # forward then the recomputing backward; the training path's own figure is in
+        # bwd["training_path"]
         bwd["train_step_ms"] = round(ms + bwd["ms_per_launch"], 4)
         bwd["train_step_tokens_per_s"] = round(wl.B * wl.T / ((ms + bwd["ms_per_launch"]) * 1e-3), 1)
     del q, k, v, beta, log_a, S0, head

@@ -27,7 +27,8 @@ EXPORTED = ("gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_chunk_fwd_varl
             "gdr_precond_scan", "gdr_status_string", "gdr_last_error", "gdr_version",
             "gdr_chunk_bwd_workspace_size", "gdr_chunk_bwd", "gdr_chunk_bwd_wkey", "gdr_chunk_bwd_varlen_workspace_size",
             "gdr_chunk_bwd_varlen", "gdr_chunk_fwd_noalloc", "gdr_precond_scan_bwd_workspace_size",
-            "gdr_precond_scan_bwd", "gdr_chunk_fwd_varlen_wkey", "gdr_chunk_bwd_varlen_wkey")
+            "gdr_precond_scan_bwd", "gdr_chunk_fwd_varlen_wkey", "gdr_chunk_bwd_varlen_wkey", "gdr_chunk_fwd_save",
+            "gdr_chunk_bwd_saved")
 
 
 class GdrDesc(ctypes.Structure):
@@ -102,6 +103,12 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         lib.gdr_chunk_bwd_varlen.restype = ctypes.c_int
         lib.gdr_chunk_bwd_varlen.argtypes = ([ctypes.POINTER(GdrDesc), vp, ctypes.c_int64] + [vp] * 15 +
                                              [ctypes.c_size_t, vp])
+        lib.gdr_chunk_fwd_save.restype = ctypes.c_int
+        lib.gdr_chunk_fwd_save.argtypes = ([ctypes.POINTER(GdrDesc), vp, ctypes.c_int64] + [vp] * 10 +
+                                           [ctypes.c_size_t, vp])
+        lib.gdr_chunk_bwd_saved.restype = ctypes.c_int
+        lib.gdr_chunk_bwd_saved.argtypes = ([ctypes.POINTER(GdrDesc), vp, ctypes.c_int64] + [vp] * 17 +
+                                            [ctypes.c_size_t, vp])
         lib.gdr_status_string.argtypes = [ctypes.c_int]
         lib.gdr_last_error.restype = ctypes.c_char_p
         lib.gdr_last_error.argtypes = []
@@ -262,8 +269,65 @@ def chunk_bwd_workspace_size(B: int, T: int, H: int, d_k: int, d_v: int, dtype=t
     return int(n.value)
 
 
+def chunk_fwd_save(q, k, v, beta, log_a=None, S0=None, *, cu_seqlens=None, form: str = "page", kw=None, o=None,
+                   S_T=None, want_state: bool = True, workspace=None, stream=None):
+    """gdr_chunk_fwd_save on torch tensors: the forward of a training step.  The
+    arguments are those of chunk_fwd (with `cu_seqlens`: of chunk_fwd_varlen); bf16
+    and the backward's configurations.  Returns (o, S_T, workspace): o and S_T as
+    chunk_fwd's, and the workspace (uint8, the backward's size; given or allocated)
+    holding the transform's records and the chunk-start states, for
+    chunk_bwd(..., saved=workspace) over the same inputs."""
+    lib = load()
+    B, T, H, dk = k.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    packed = cu_seqlens is not None
+    if packed:
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous() \
+                or cu_seqlens.device != q.device:
+            raise ValueError("cu_seqlens must be a contiguous 1-D int32 tensor on the inputs' device")
+        if B != 1:
+            raise ValueError("packed sequences take [1, T, H, d] tensors")
+        nstate = cu_seqlens.numel() - 1
+    else:
+        nstate = B
+    _require(q, "q", dt, (B, T, H, dk))
+    _require(k, "k", dt, (B, T, H, dk))
+    _require(v, "v", dt, (B, T, H, dv))
+    _require(beta, "beta", dt, (B, T, H))
+    gate = _gate_of(log_a, beta.shape, k.shape)
+    if log_a is not None:
+        _require(log_a, "log_a", dt, tuple(log_a.shape))
+    if S0 is not None:
+        _require(S0, "S0", torch.float32, (nstate, H, dk, dv))
+    if kw is not None:
+        _require(kw, "kw", dt, (B, T, H, dk))
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=dt, device=q.device)
+    _require(o, "o", dt, (B, T, H, dv))
+    if want_state and S_T is None:
+        S_T = torch.empty((nstate, H, dk, dv), dtype=torch.float32, device=q.device)
+    if S_T is not None:
+        _require(S_T, "S_T", torch.float32, (nstate, H, dk, dv))
+    desc = GdrDesc(B, T, H, dk, dv, 64, _io_of(q), gate, FORMS[form])
+    need = ctypes.c_size_t(0)
+    if packed:
+        _check(lib, lib.gdr_chunk_bwd_varlen_workspace_size(ctypes.byref(desc), nstate, ctypes.byref(need)))
+    else:
+        _check(lib, lib.gdr_chunk_bwd_workspace_size(ctypes.byref(desc), ctypes.byref(need)))
+    if workspace is None:
+        workspace = torch.empty(max(int(need.value), 1), dtype=torch.uint8, device=q.device)
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous() or workspace.device != q.device:
+        raise ValueError("workspace must be a contiguous uint8 tensor on the inputs' device")
+    st = lib.gdr_chunk_fwd_save(ctypes.byref(desc), _ptr(cu_seqlens), nstate if packed else 0, _ptr(q), _ptr(k),
+                                _ptr(kw), _ptr(v), _ptr(beta), _ptr(log_a), _ptr(S0), _ptr(o), _ptr(S_T),
+                                _ptr(workspace), workspace.numel(), _stream_handle(stream))
+    _check(lib, st)
+    return o, S_T, workspace
+
+
 def chunk_bwd(q, k, v, beta, log_a, S0, dO, dS_T=None, *, cu_seqlens=None, form: str = "page", want_dS0: bool = True,
-              workspace=None, stream=None, kw=None):
+              workspace=None, stream=None, kw=None, saved=None):
     """gdr_chunk_bwd on torch tensors: the gradients of L = <dO, o> + <dS_T, S_T> for
     the forward chunk_fwd(q, k, v, beta, log_a, S0, form=form) (bf16 I/O; no gate, a
     scalar gate, or a per-channel gate with d_k = 128).  dO [B, T, H, d_v] bf16; dS_T None or
@@ -273,7 +337,10 @@ def chunk_bwd(q, k, v, beta, log_a, S0, dO, dS_T=None, *, cu_seqlens=None, form:
     dlog_a, dS0) (dlog_a None without a gate, dS0 None when want_dS0 is False).
     `kw` ([B, T, H, d_k] bf16, no gate or a scalar gate) is the forward's write key
     (gdr_chunk_bwd_wkey, gdr_chunk_bwd_varlen_wkey): then dk is the read side's
-    gradient and the dict also holds dkw.  Asynchronous on the current (or given) stream."""
+    gradient and the dict also holds dkw.  `saved` is the workspace returned by
+    chunk_fwd_save over the same inputs (gdr_chunk_bwd_saved: the transform and the
+    chunk-start states are taken from it, and S0 is not read); it is overwritten.
+    Asynchronous on the current (or given) stream."""
     lib = load()
     B, T, H, dk = k.shape
     dv = v.shape[-1]
@@ -311,10 +378,22 @@ def chunk_bwd(q, k, v, beta, log_a, S0, dO, dS_T=None, *, cu_seqlens=None, form:
         _check(lib, lib.gdr_chunk_bwd_varlen_workspace_size(ctypes.byref(desc), nstate, ctypes.byref(need)))
     else:
         _check(lib, lib.gdr_chunk_bwd_workspace_size(ctypes.byref(desc), ctypes.byref(need)))
+    if saved is not None:
+        workspace = saved
     if workspace is None:
         workspace = torch.empty(max(int(need.value), 1), dtype=torch.uint8, device=q.device)
     if workspace.dtype != torch.uint8 or not workspace.is_contiguous() or workspace.device != q.device:
         raise ValueError("workspace must be a contiguous uint8 tensor on the inputs' device")
+    if saved is not None:
+        if kw is not None:
+            out["dkw"] = torch.empty_like(k)
+        st = lib.gdr_chunk_bwd_saved(ctypes.byref(desc), _ptr(cu_seqlens), nstate if packed else 0, _ptr(q), _ptr(k),
+                                     _ptr(kw), _ptr(v), _ptr(beta), _ptr(log_a), _ptr(S0), _ptr(dO), _ptr(dS_T),
+                                     _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out.get("dkw")), _ptr(out["dv"]),
+                                     _ptr(out["dbeta"]), _ptr(out["dlog_a"]), _ptr(out["dS0"]), _ptr(workspace),
+                                     workspace.numel(), _stream_handle(stream))
+        _check(lib, st)
+        return out
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_a), _ptr(S0), _ptr(dO), _ptr(dS_T), _ptr(out["dq"]),
             _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dbeta"]), _ptr(out["dlog_a"]), _ptr(out["dS0"]),
             _ptr(workspace), workspace.numel(), _stream_handle(stream))
@@ -541,7 +620,12 @@ class _ChunkAttn(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, q, k, v, beta, log_a, S0, cu_seqlens, form, kw):
-        if cu_seqlens is not None:
+        # the training forward: its workspace keeps the transform and the chunk-start
+        # states for the backward, which then only runs the reverse pass and the
+        # per-chunk gradients
+        if any(ctx.needs_input_grad):
+            o, S_T, ctx.ws = chunk_fwd_save(q, k, v, beta, log_a, S0, cu_seqlens=cu_seqlens, form=form, kw=kw)
+        elif cu_seqlens is not None:
             o, S_T = chunk_fwd_varlen(q, k, v, beta, log_a, cu_seqlens, S0, form=form, kw=kw)
         else:
             o, S_T = chunk_fwd(q, k, v, beta, log_a, S0, form=form, kw=kw)
@@ -556,8 +640,10 @@ class _ChunkAttn(torch.autograd.Function):
         q, k, v, beta, log_a, S0, cu_seqlens, kw = ctx.saved_tensors
         dO = torch.zeros_like(v) if dO is None else dO.to(v.dtype).contiguous()
         dS_T = None if dS_T is None else dS_T.float().contiguous()
+        # the backward leaves the records and the states in place, so the graph may be
+        # walked more than once (retain_graph)
         g = chunk_bwd(q, k, v, beta, log_a, S0, dO, dS_T, cu_seqlens=cu_seqlens, form=ctx.form, want_dS0=ctx.has_S0,
-                      kw=kw)
+                      kw=kw, saved=ctx.ws)
         return (g["dq"], g["dk"], g["dv"], g["dbeta"], g["dlog_a"] if ctx.gated else None,
                 g["dS0"] if ctx.has_S0 else None, None, None, g.get("dkw"))
 
@@ -565,7 +651,8 @@ class _ChunkAttn(torch.autograd.Function):
 def chunk_attn(q, k, v, beta, log_a=None, S0=None, cu_seqlens=None, form: str = "page", kw=None):
     """(o, S_T) of chunk_fwd (or chunk_fwd_varlen with cu_seqlens) as a torch autograd
     function whose backward is chunk_bwd: bf16, any gate (per-channel with d_k = 128),
-    either form.  Gradients flow to q, k, v, beta, log_a and S0, and to the write key
+    either form.  The forward is chunk_fwd_save and the backward takes what it kept
+    (the backward's workspace stays allocated between the two).  Gradients flow to q, k, v, beta, log_a and S0, and to the write key
     `kw` when one is given (no gate or a scalar gate)."""
     if kw is not None and log_a is not None and log_a.dim() == 4:
         raise ValueError("chunk_attn with a write key: no gate or a scalar gate (the backward's scope)")

@@ -35,8 +35,9 @@
 //      shape of work, dS in accumulators);
 //   3. every chunk at once: the gradients of q, k, v, beta and log a.
 // Passes 1 and 2 are independent and share one launch.  They store the states in
-// bf16, the precision the forward's products read them in, value-major ([d_v][d_k]
-// per chunk) so that an accumulator lane writes four adjacent values.
+// bf16, the precision the forward's products read them in, in d_k tiles of 16 that
+// are value-major (chunk_state_off) so that an accumulator lane writes four adjacent
+// values and a store instruction 512 contiguous bytes.
 //
 // With a per-channel gate the two sequential passes here take the transform's
 // decayed operands (k e^{g_read}, q e^{g}, k e^{g_63 - g}) and its P, and scale the
@@ -160,7 +161,7 @@ struct SeqStage {
   }
 };
 
-// Pass 1: the state entering every chunk, stored in bf16 value-major.  lb is the
+// Pass 1: the state entering every chunk, stored in bf16 (chunk_state_off).  lb is the
 // workgroup's (sequence, head, tile) index.  With a write key (WK) the update writes
 // along it: S' = e^{g_63} S + KW^T (e^{g_63 - g} Delta).
 template <int GATE, int DK, bool WK>
@@ -212,7 +213,7 @@ __device__ __forceinline__ void states_pass(const BwdParams& p, int n_tiles, int
     }
     const uint32_t so = static_cast<uint32_t>(n) * sbytes;
 #pragma unroll
-    for (int t = 0; t < DKT; ++t) buf_store8(bits8(S[t]), rst, static_cast<uint32_t>((scol * DK + 16 * t + 4 * lg) * 2), so);
+    for (int t = 0; t < DKT; ++t) buf_store8(bits8(S[t]), rst, chunk_state_off(16 * t + 4 * lg, scol, dv), so);
 
     frag Sb[DKT];
 #pragma unroll
@@ -339,7 +340,7 @@ __device__ __forceinline__ void reverse_pass(const BwdParams& p, int n_tiles, in
 
     const uint32_t so = static_cast<uint32_t>(n) * sbytes;
 #pragma unroll
-    for (int t = 0; t < DKT; ++t) buf_store8(bits8(dS[t]), rds, static_cast<uint32_t>((scol * DK + 16 * t + 4 * lg) * 2), so);
+    for (int t = 0; t < DKT; ++t) buf_store8(bits8(dS[t]), rds, chunk_state_off(16 * t + 4 * lg, scol, dv), so);
 
     frag dSb[DKT];
 #pragma unroll
@@ -424,13 +425,14 @@ __device__ __forceinline__ void reverse_pass(const BwdParams& p, int n_tiles, in
 }
 
 // Passes 1 and 2 in one launch of 2 nseq workgroups: the first nseq take pass 1.
+// With the chunk-start states saved by the forward (p.saved), nseq workgroups of pass 2.
 template <int GATE, int DK, bool WK>
 __global__ __launch_bounds__(256) void bwd_seq_kernel(BwdParams p, int n_tiles, int nseq) {
   constexpr bool KD = GATE == GATE_CHANNEL || WK;
   __shared__ __attribute__((aligned(16))) char smem[cmax(SeqLayout<DK, false, KD>::TOTAL, SeqLayout<DK, true, KD>::TOTAL)];
   const int b = blockIdx.x;
-  const int role = b >= nseq;
-  const int idx = b - role * nseq;
+  const int role = p.saved ? 1 : b >= nseq;
+  const int idx = p.saved ? b : b - role * nseq;
   if (role == 0) states_pass<GATE, DK, WK>(p, n_tiles, idx, smem);
   else reverse_pass<GATE, DK, WK>(p, n_tiles, idx, smem);
 }
@@ -569,8 +571,9 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdParams p) {
       hv = buf_load16(rv, static_cast<uint32_t>(((tid / 8) * H * DV + 64 * h + (tid % 8) * 8) * 2), sv);
       hdo = buf_load16(rdo, static_cast<uint32_t>(((tid / 8) * H * DV + 64 * h + (tid % 8) * 8) * 2), sv);
 #pragma unroll
-      for (int i = 0; i < KP; ++i) {
-        const uint32_t off = static_cast<uint32_t>((64 * h * DK + (tid + i * NT) * 8) * 2);
+      for (int i = 0; i < KP; ++i) {   // piece pc: column 64 h + pc / KR of S, d_k values 8 (pc % KR) ..
+        const int pc = tid + i * NT;
+        const uint32_t off = chunk_state_off(8 * (pc % KR), 64 * h + pc / KR, DV);
         hs[i] = buf_load16(rst, off, ss);
         hds[i] = buf_load16(rds, off, ss);
       }
@@ -945,8 +948,8 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
   const ChunkParams& f = p.f;
   const int n_tiles = f.d_v / 64;
   const int64_t nseq = f.B * f.H * n_tiles;
-  hipLaunchKernelGGL((bwd_seq_kernel<GATE, DK, WK>), dim3(static_cast<unsigned>(2 * nseq)), dim3(256), 0, stream, p,
-                     n_tiles, static_cast<int>(nseq));
+  hipLaunchKernelGGL((bwd_seq_kernel<GATE, DK, WK>), dim3(static_cast<unsigned>((p.saved ? 1 : 2) * nseq)), dim3(256),
+                     0, stream, p, n_tiles, static_cast<int>(nseq));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if constexpr (GATE == GATE_CHANNEL) {
@@ -1006,8 +1009,10 @@ hipError_t launch_chunk_bwd(const BwdParams& p, hipStream_t stream) {
                        p.dS0, n);
     return hipGetLastError();
   }
-  hipError_t e = launch_chunk_prep(f, stream);   // with f.kw: T of the write-key Gram blocks
-  if (e != hipSuccess) return e;
+  if (!p.saved) {   // else the records are the training forward's
+    const hipError_t e = launch_chunk_prep(f, stream);   // with f.kw: T of the write-key Gram blocks
+    if (e != hipSuccess) return e;
+  }
   if (f.kw) {
     if (f.gate == GATE_NONE) return launch_bwd_g<GATE_NONE, true>(p, stream);
     if (f.gate == GATE_SCALAR) return launch_bwd_g<GATE_SCALAR, true>(p, stream);

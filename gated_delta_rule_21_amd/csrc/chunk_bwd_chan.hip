@@ -209,8 +209,9 @@ __global__ __launch_bounds__(512) void bwd_chunk_chan_kernel(BwdParams p) {
       hvo[i] = buf_load16(is_do ? rdo : rv, static_cast<uint32_t>(((t / VPR) * H * DV + QW * qi + (t % VPR) * 8) * 2), sv);
     }
 #pragma unroll
-    for (int i = 0; i < NSP; ++i) {   // value-major: row v = pc / 16
-      const uint32_t off = static_cast<uint32_t>((QW * qi * DK + (tid + i * NT) * 8) * 2);
+    for (int i = 0; i < NSP; ++i) {   // piece pc: column QW qi + pc / 16 of S, d_k values 8 (pc % 16) ..
+      const int pc = tid + i * NT;
+      const uint32_t off = chunk_state_off(8 * (pc % 16), QW * qi + pc / 16, DV);
       hs[i] = buf_load16(rst, off, ss);
       hds[i] = buf_load16(rds, off, ss);
     }

@@ -485,8 +485,9 @@ hipError_t launch_chunk_fwd(const ChunkParams& p, hipStream_t stream) {
     if (!p.cu) return launch_chunk_state_pipe(p, stream);
     // packed sequences: the state pass takes them longest first
     ChunkParams q = p;
-    int32_t* order = reinterpret_cast<int32_t*>(
-        static_cast<char*>(p.ws) + chunk_varlen_records_bytes(p.T, p.B, p.H, p.io, p.gate, p.d_k));
+    int32_t* order = p.order_out ? p.order_out
+                                 : reinterpret_cast<int32_t*>(static_cast<char*>(p.ws) +
+                                                              chunk_varlen_records_bytes(p.T, p.B, p.H, p.io, p.gate, p.d_k));
     q.order = order;
     if ((e = launch_varlen_order(q, order, stream)) != hipSuccess) return e;
     return launch_chunk_state_pipe(q, stream);

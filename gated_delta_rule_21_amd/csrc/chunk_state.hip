@@ -314,6 +314,14 @@ __global__ __launch_bounds__((NCH + NHW) * 64) void chunk_state_pipe_kernel(Chun
         vo[R][g] = static_cast<uint32_t>(((16 * R + lr) * H * dv + col0 + c0 + 16 * g + 4 * lg) * ESZ);
     constexpr uint32_t DROP = 0x80000000u;     // beyond any sequence (at most 2^31 - 1 bytes)
     constexpr int NKB = DK / 32;
+    // Training forward: the state entering each chunk, in bf16 and in the layout the
+    // backward reads (four adjacent d_k values per lane, streaming stores).
+    const uint32_t sbytes = static_cast<uint32_t>(dv * DK * 2);
+    const rsrc_t rst = make_rsrc(p.states ? static_cast<char*>(p.states) + sq.rec0 * sbytes : nullptr,
+                                 p.states ? static_cast<uint32_t>(nchunks * sbytes) : 0u);
+    uint32_t sto[CG];
+#pragma unroll
+    for (int g = 0; g < CG; ++g) sto[g] = chunk_state_off(4 * lg, col0 + c0 + 16 * g + lr, dv);
     __syncthreads();                            // chunk 0 in LDS
 
     for (int64_t n = 0; n < nchunks; ++n) {
@@ -352,6 +360,14 @@ __global__ __launch_bounds__((NCH + NHW) * 64) void chunk_state_pipe_kernel(Chun
       for (int g = 0; g < CG; ++g)
 #pragma unroll
         for (int t = 0; t < DKT; ++t) Sb[g][t] = O::cvt(S[g][t]);
+      if (p.states) {
+        const uint32_t so = static_cast<uint32_t>(n) * sbytes;
+#pragma unroll
+        for (int g = 0; g < CG; ++g)
+#pragma unroll
+          for (int t = 0; t < DKT; ++t)
+            buf_store8_nt(__builtin_bit_cast(u32x2, Sb[g][t]), rst, sto[g] + chunk_state_off(16 * t, 0, dv), so);
+      }
 
       // stages KS(R): K S and Q S of row block R; the residual of block R-1 (its K S has
       // had a stage to drain); the previous chunk's output after block 0

@@ -120,6 +120,10 @@ __device__ __forceinline__ uint16_t buf_load2(rsrc_t r, uint32_t voff, uint32_t 
 __device__ __forceinline__ void buf_store8(u32x2 x, rsrc_t r, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_buffer_store_b64(x, r, voff, soff, 0);
 }
+// A streaming store (non-temporal): data read back only by a later kernel.
+__device__ __forceinline__ void buf_store8_nt(u32x2 x, rsrc_t r, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b64(x, r, voff, soff, 2);
+}
 __device__ __forceinline__ void buf_store16(u32x4 x, rsrc_t r, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_buffer_store_b128(x, r, voff, soff, 0);
 }

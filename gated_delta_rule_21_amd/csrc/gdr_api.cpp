@@ -106,6 +106,16 @@ gdr_status check_packed(const gdr_desc* d, int64_t n_seq) {
   return GDR_OK;
 }
 
+// The backward's workspace: the transform's records (rec bytes), the chunk-start
+// states (sb bytes), then the chunk-end state gradients (sb bytes).
+void bwd_ws_layout(const gdr_desc* d, bool packed, int64_t n_seq, size_t* rec, size_t* sb) {
+  const int dk = static_cast<int>(d->d_k), dv = static_cast<int>(d->d_v);
+  *rec = packed ? gdr::chunk_varlen_records_bytes(d->T, n_seq, d->H, d->io, d->gate, dk)
+                : gdr::chunk_workspace_bytes(d->B, d->T, d->H, d->io, d->gate, dk);
+  *sb = packed ? gdr::chunk_bwd_varlen_state_bytes(d->T, n_seq, d->H, dk, dv)
+               : gdr::chunk_bwd_state_bytes(d->B, d->T, d->H, dk, dv);
+}
+
 gdr_status check_align(const char* name, const void* p, uintptr_t a) {
   if (p && (reinterpret_cast<uintptr_t>(p) % a) != 0)
     return fail(GDR_ERR_ALIGNMENT, "%s = %p is not %u-byte aligned", name, p, (unsigned)a);
@@ -160,12 +170,17 @@ gdr_status gdr_chunk_fwd_workspace_size(const gdr_desc* d, size_t* bytes) {
 
 namespace {
 
-// The forward over fixed-length batches (cu == nullptr) or packed sequences.
+// The forward over fixed-length batches (cu == nullptr) or packed sequences.  With
+// `save` (the training forward) the workspace is the backward's, and the call also
+// leaves there the chunk-start states the backward reads.
 gdr_status chunk_fwd_impl(const gdr_desc* d, const int32_t* cu, int64_t n_seq, const void* q, const void* k,
                           const void* v, const void* beta, const void* log_a, const float* S0, void* o, float* S_T,
-                          void* workspace, size_t workspace_bytes, void* stream, const void* kw = nullptr) {
-  gdr_status st = check_desc(d, false);
+                          void* workspace, size_t workspace_bytes, void* stream, const void* kw = nullptr,
+                          bool save = false) {
+  gdr_status st = save ? check_bwd_desc(d) : check_desc(d, false);
   if (st != GDR_OK) return st;
+  if (save && kw && d->gate == GDR_GATE_CHANNEL)
+    return fail(GDR_ERR_UNSUPPORTED, "training forward with a write key: no gate or a scalar gate");
   const bool packed = cu != nullptr || n_seq != 0;
   if (packed) {
     if (!cu) return fail(GDR_ERR_INVALID_ARG, "cu_seqlens is NULL");
@@ -176,9 +191,12 @@ gdr_status chunk_fwd_impl(const gdr_desc* d, const int32_t* cu, int64_t n_seq, c
       return fail(GDR_ERR_UNSUPPORTED, "n_seq = %lld: exceeds the grid limit", (long long)n_seq);
   }
   const int64_t nseq = packed ? n_seq : d->B;        // sequences, and states in S0 / S_T
+  const int dk_ = static_cast<int>(d->d_k), dv_ = static_cast<int>(d->d_v);
   const size_t ws_need =
-      packed ? gdr::chunk_varlen_workspace_bytes(d->T, n_seq, d->H, d->io, d->gate, static_cast<int>(d->d_k))
-             : gdr::chunk_workspace_bytes(d->B, d->T, d->H, d->io, d->gate, static_cast<int>(d->d_k));
+      save ? (packed ? gdr::chunk_bwd_varlen_workspace_bytes(d->T, n_seq, d->H, dk_, dv_, d->gate)
+                     : gdr::chunk_bwd_workspace_bytes(d->B, d->T, d->H, dk_, dv_, d->gate))
+      : packed ? gdr::chunk_varlen_workspace_bytes(d->T, n_seq, d->H, d->io, d->gate, dk_)
+               : gdr::chunk_workspace_bytes(d->B, d->T, d->H, d->io, d->gate, dk_);
   const int64_t esz = d->io == GDR_BF16 ? 2 : 4;
   const int64_t ntok = d->B * d->T * d->H;
   const bool any = d->T > 0;
@@ -223,6 +241,13 @@ gdr_status chunk_fwd_impl(const gdr_desc* d, const int32_t* cu, int64_t n_seq, c
   p.nslots = packed ? gdr::chunk_varlen_slots(d->T, n_seq) : 0;
   p.order = nullptr;
   p.kw = kw;
+  if (save && d->T > 0) {
+    size_t rec, sb;
+    bwd_ws_layout(d, packed, n_seq, &rec, &sb);
+    p.states = static_cast<char*>(workspace) + rec;
+    // the packed order goes where the backward later writes its state gradients
+    if (packed) p.order_out = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + rec + sb);
+  }
   if (d->T == 0 && !S_T) return GDR_OK;
   hipError_t e = gdr::launch_chunk_fwd(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(GDR_ERR_HIP, "chunk forward launch failed: %s", hipGetErrorString(e));
@@ -367,7 +392,7 @@ gdr_status chunk_bwd_impl(const gdr_desc* d, const int32_t* cu, int64_t n_seq, c
                           const void* v, const void* beta, const void* log_a, const float* S0, const void* dO,
                           const float* dS_T, void* dq, void* dk, void* dv, void* dbeta, void* dlog_a, float* dS0,
                           void* workspace, size_t workspace_bytes, void* stream, const void* kw = nullptr,
-                          void* dkw = nullptr) {
+                          void* dkw = nullptr, bool saved = false) {
   gdr_status st = check_bwd_desc(d);
   if (st != GDR_OK) return st;
   const bool wkey = kw != nullptr || dkw != nullptr;
@@ -431,10 +456,9 @@ gdr_status chunk_bwd_impl(const gdr_desc* d, const int32_t* cu, int64_t n_seq, c
   f.cu = cu; f.nslots = packed ? gdr::chunk_varlen_slots(d->T, n_seq) : 0; f.order = nullptr; f.kw = kw;
   p.dO = dO; p.dS_T = dS_T; p.dq = dq; p.dk = dk; p.dv = dv; p.dbeta = dbeta; p.dlog_a = dlog_a; p.dS0 = dS0;
   p.dkw = dkw;
-  const size_t rec = packed ? gdr::chunk_varlen_records_bytes(d->T, n_seq, d->H, d->io, d->gate, dk_)
-                            : gdr::chunk_workspace_bytes(d->B, d->T, d->H, d->io, d->gate, dk_);
-  const size_t sb = packed ? gdr::chunk_bwd_varlen_state_bytes(d->T, n_seq, d->H, dk_, dv_)
-                           : gdr::chunk_bwd_state_bytes(d->B, d->T, d->H, dk_, dv_);
+  p.saved = saved ? 1 : 0;
+  size_t rec, sb;
+  bwd_ws_layout(d, packed, n_seq, &rec, &sb);
   p.states = d->T > 0 ? static_cast<char*>(workspace) + rec : nullptr;
   p.dstates = d->T > 0 ? static_cast<char*>(workspace) + rec + sb : nullptr;
   if (d->T == 0 && !dS0) return GDR_OK;
@@ -689,6 +713,36 @@ gdr_status gdr_chunk_bwd_varlen_wkey(const gdr_desc* d, const int32_t* cu_seqlen
     if (!dkw) return fail(GDR_ERR_INVALID_ARG, "dkw is NULL");
     return chunk_bwd_impl(d, cu_seqlens, n_seq, q, k, v, beta, log_a, S0, dO, dS_T, dq, dk, dv, dbeta, dlog_a, dS0,
                           workspace, workspace_bytes, stream, kw, dkw);
+  } catch (...) {
+    return fail(GDR_ERR_INVALID_ARG, "internal error");
+  }
+}
+
+gdr_status gdr_chunk_fwd_save(const gdr_desc* d, const int32_t* cu_seqlens, int64_t n_seq, const void* q,
+                              const void* k, const void* kw, const void* v, const void* beta, const void* log_a,
+                              const float* S0, void* o, float* S_T, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  try {
+    g_last_error.clear();
+    if (!cu_seqlens && n_seq != 0) return fail(GDR_ERR_INVALID_ARG, "n_seq = %lld without cu_seqlens", (long long)n_seq);
+    return chunk_fwd_impl(d, cu_seqlens, n_seq, q, k, v, beta, log_a, S0, o, S_T, workspace, workspace_bytes, stream,
+                          kw, true);
+  } catch (...) {
+    return fail(GDR_ERR_INVALID_ARG, "internal error");
+  }
+}
+
+gdr_status gdr_chunk_bwd_saved(const gdr_desc* d, const int32_t* cu_seqlens, int64_t n_seq, const void* q,
+                               const void* k, const void* kw, const void* v, const void* beta, const void* log_a,
+                               const float* S0, const void* dO, const float* dS_T, void* dq, void* dk, void* dkw,
+                               void* dv, void* dbeta, void* dlog_a, float* dS0, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  try {
+    g_last_error.clear();
+    if (!cu_seqlens && n_seq != 0) return fail(GDR_ERR_INVALID_ARG, "n_seq = %lld without cu_seqlens", (long long)n_seq);
+    if ((kw == nullptr) != (dkw == nullptr)) return fail(GDR_ERR_INVALID_ARG, "kw and dkw: both or neither");
+    return chunk_bwd_impl(d, cu_seqlens, n_seq, q, k, v, beta, log_a, S0, dO, dS_T, dq, dk, dv, dbeta, dlog_a, dS0,
+                          workspace, workspace_bytes, stream, kw, dkw, true);
   } catch (...) {
     return fail(GDR_ERR_INVALID_ARG, "internal error");
   }

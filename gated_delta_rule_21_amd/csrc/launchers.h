@@ -41,7 +41,21 @@ struct ChunkParams {
   int64_t nslots;
   const int32_t* order;   // packed sequences: longest first (in the workspace, after the records)
   const void* kw;         // write key [B, T, H, d_k] (bf16), or null: the state is written along k
+  // Training forward (bf16 state pass): the state entering every chunk, bf16 in
+  // the backward's chunk-state layout (chunk_state_off), or null.
+  void* states = nullptr;
+  // Packed sequences: where the order is written (null: after the records in ws).
+  int32_t* order_out = nullptr;
 };
+
+// Byte offset of element (d, v) of one chunk's bf16 state (d_k x d_v) in the
+// per-chunk state records of the backward: d_k in tiles of 16, each tile value-major,
+// [d_k / 16][d_v][16].  A lane holding four adjacent d of one column of an MFMA
+// accumulator tile writes 8 bytes, and the 16 columns of a tile row are contiguous,
+// so one store instruction covers 512 contiguous bytes.
+__host__ __device__ constexpr uint32_t chunk_state_off(int d, int v, int d_v) {
+  return static_cast<uint32_t>((((d >> 4) * d_v + v) * 16 + (d & 15)) * 2);
+}
 
 struct PrecondParams {
   const void* k;        // [B, T, H, d_k] io dtype
@@ -68,8 +82,11 @@ struct BwdParams {
   void* dbeta;          // [B, T, H]
   void* dlog_a;         // [B, T, H] (scalar gate), [B, T, H, d_k] (per-channel gate), else unused
   float* dS0;           // [B, H, d_k, d_v], or null (not written)
-  void* states;         // B H ceil(T/64) chunk-start states, bf16 [d_v][d_k] each
+  void* states;         // B H ceil(T/64) chunk-start states, bf16, laid out by chunk_state_off
   void* dstates;        // the gradients of the chunk-end states, same layout
+  // The records (f.ws) and the chunk-start states were left by a training forward
+  // over the same inputs: no transform and no pass 1.
+  int saved = 0;
 };
 // Reverse mode of the preconditioner scan (the gradients of <dkw, kw> + <dd_T, d_T>).
 struct PrecondBwdParams {
@@ -105,7 +122,8 @@ hipError_t static_scratch(void** ptr);
 inline int64_t chunk_varlen_slots(int64_t T, int64_t n_seq) { return (T + 63) / 64 + n_seq; }
 size_t chunk_varlen_records_bytes(int64_t T, int64_t n_seq, int64_t H, int io, int gate, int d_k);
 size_t chunk_varlen_workspace_bytes(int64_t T, int64_t n_seq, int64_t H, int io, int gate, int d_k);
-// Backward: the per-chunk transform into p.f.ws, then the three passes.
+// Backward: the per-chunk transform into p.f.ws, then the three passes (p.saved:
+// pass 2 and pass 3 only).
 hipError_t launch_chunk_bwd(const BwdParams& p, hipStream_t stream);
 // Bytes of one set of per-chunk states (bf16), and of the whole backward workspace:
 // the transform's records, the chunk-start states, the chunk-end state gradients.

@@ -504,6 +504,61 @@ gdr_status gdr_chunk_bwd_varlen(const gdr_desc* desc, const int32_t* cu_seqlens,
                                 void* dlog_a, float* dS0, void* workspace, size_t workspace_bytes,
                                 void* stream /* hipStream_t */);
 
+/*
+ * gdr_chunk_fwd_save -- the chunk forward of a training step: gdr_chunk_fwd (with
+ * cu_seqlens: gdr_chunk_fwd_varlen; with kw: the _wkey forms) that also leaves in
+ * its workspace what gdr_chunk_bwd would otherwise recompute, for a later
+ * gdr_chunk_bwd_saved.
+ *
+ * The backward of the chunk form ("Moonshot AI's New Attention Architecture", §3)
+ * needs the state entering every chunk and the per-chunk transform (T and the
+ * gate factors); the forward forms both on its way.  This call writes them into
+ * a workspace laid out as gdr_chunk_bwd's: the transform's records, then the
+ * chunk-start states in bf16 (the precision the backward's products read them
+ * in), then room the backward uses.  o and S_T are those of gdr_chunk_fwd, bit
+ * for bit.
+ *
+ *   cu_seqlens, n_seq   NULL and 0 for fixed-length batches; else packed
+ *                       sequences as for gdr_chunk_fwd_varlen (desc->B == 1)
+ *   kw                  NULL, or the write key as for gdr_chunk_fwd_wkey (no
+ *                       gate or a scalar gate)
+ *   workspace / workspace_bytes  at least gdr_chunk_bwd_workspace_size (packed:
+ *                       gdr_chunk_bwd_varlen_workspace_size) bytes, 16-byte
+ *                       aligned; written, and to be passed unchanged to
+ *                       gdr_chunk_bwd_saved
+ *   every other argument as for gdr_chunk_fwd
+ *
+ * Supported: the configurations of gdr_chunk_bwd (bf16 I/O), with a write key
+ * those of gdr_chunk_bwd_wkey; else GDR_ERR_UNSUPPORTED.  Errors as for
+ * gdr_chunk_fwd (GDR_ERR_WORKSPACE for a missing or short workspace), and
+ * GDR_ERR_INVALID_ARG for n_seq != 0 without cu_seqlens.
+ */
+gdr_status gdr_chunk_fwd_save(const gdr_desc* desc, const int32_t* cu_seqlens, int64_t n_seq, const void* q,
+                              const void* k, const void* kw, const void* v, const void* beta, const void* log_a,
+                              const float* S0, void* o, float* S_T, void* workspace, size_t workspace_bytes,
+                              void* stream /* hipStream_t */);
+
+/*
+ * gdr_chunk_bwd_saved -- gdr_chunk_bwd (with cu_seqlens: _varlen; with kw and dkw:
+ * _wkey) that takes the transform's records and the chunk-start states from the
+ * workspace of an earlier gdr_chunk_fwd_save instead of recomputing them, so
+ * only the reverse pass over the chunks and the per-chunk gradients run.
+ *
+ * The descriptor, cu_seqlens, n_seq, q, k, kw, v, beta and log_a must be those of
+ * that gdr_chunk_fwd_save call, unchanged since, and the workspace must hold what
+ * it wrote (no check is possible: otherwise the gradients are undefined, and no
+ * access leaves the buffers).  S0 is not read (its chunk-start state is in the
+ * workspace) and may be NULL.  The workspace is overwritten past the records and
+ * the states only, so one saved forward can serve several backward calls.  kw and dkw: both NULL, or both given (dk is then the read side's
+ * gradient, as for gdr_chunk_bwd_wkey).  Outputs, precision, supported
+ * configurations and errors as for gdr_chunk_bwd and its _varlen and _wkey forms.
+ */
+gdr_status gdr_chunk_bwd_saved(const gdr_desc* desc, const int32_t* cu_seqlens, int64_t n_seq, const void* q,
+                               const void* k, const void* kw, const void* v, const void* beta, const void* log_a,
+                               const float* S0, const void* dO, const float* dS_T, void* dq, void* dk, void* dkw,
+                               void* dv, void* dbeta, void* dlog_a, float* dS0, void* workspace,
+                               size_t workspace_bytes, void* stream /* hipStream_t */);
+
 #ifdef __cplusplus
 }
 #endif

@@ -485,3 +485,84 @@ def test_packed_write_key_checks(lib):
         bad[i] = None
         assert bwd(d, FAKE, 3, bad) == INVALID, name
     assert bwd(_desc(B=1, T=300, H=2, gate=2), FAKE, 3, q) == UNSUPPORTED  # no per-channel gate with a write key
+
+
+def _fwd_save(lib, d, cu, n_seq, p, ws_bytes=1 << 40):
+    """gdr_chunk_fwd_save with p = (q, k, kw, v, beta, log_a, S0, o, S_T, ws)."""
+    return lib.gdr_chunk_fwd_save(None if d is None else ctypes.byref(d), cu, n_seq, *p[:9], p[9], ws_bytes, None)
+
+
+def test_training_forward_checks(lib):
+    """The training forward takes the backward's configurations and the backward's
+    workspace size (its records plus the chunk-start states)."""
+    p = _ptrs(11)
+    p[2] = None                                                            # no write key
+    d = _desc(B=2, T=130, H=3)
+    assert _fwd_save(lib, None, None, 0, p) == INVALID
+    n_fwd, n_bwd = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert lib.gdr_chunk_fwd_workspace_size(ctypes.byref(d), ctypes.byref(n_fwd)) == OK
+    assert lib.gdr_chunk_bwd_workspace_size(ctypes.byref(d), ctypes.byref(n_bwd)) == OK
+    assert n_bwd.value > n_fwd.value
+    assert _fwd_save(lib, d, None, 0, p, ws_bytes=n_fwd.value) == WORKSPACE    # the forward's size is not enough
+    assert _fwd_save(lib, d, None, 0, p, ws_bytes=n_bwd.value - 1) == WORKSPACE
+    bad = list(p)
+    bad[9] = None
+    assert _fwd_save(lib, d, None, 0, bad) == WORKSPACE                    # no workspace
+    assert _fwd_save(lib, _desc(io=0, d_k=64, d_v=64), None, 0, p) == UNSUPPORTED   # bf16 only
+    assert _fwd_save(lib, _desc(gate=2, d_k=64), None, 0, p) == UNSUPPORTED        # per-channel: d_k = 128
+    kw = list(p)
+    kw[2] = p[10]
+    assert _fwd_save(lib, _desc(gate=2), None, 0, kw) == UNSUPPORTED       # per-channel gate with a write key
+    assert _fwd_save(lib, d, None, 3, p) == INVALID                        # n_seq without an offset table
+    assert b"cu_seqlens" in lib.gdr_last_error()
+    for i, name in ((0, "q"), (1, "k"), (3, "v"), (4, "beta"), (7, "o")):
+        bad = list(p)
+        bad[i] = None
+        assert _fwd_save(lib, d, None, 0, bad) == INVALID, name
+    bad = list(p)
+    bad[7] = bad[9] + 256                                                  # o inside the workspace
+    assert _fwd_save(lib, d, None, 0, bad) == INVALID
+    # packed sequences
+    dp = _desc(B=1, T=300, H=2)
+    assert _fwd_save(lib, _desc(B=2, T=300, H=2), FAKE, 3, p) == INVALID  # B must be 1
+    assert _fwd_save(lib, dp, FAKE, 0, p) == INVALID                       # n_seq < 1
+    assert _fwd_save(lib, dp, FAKE + 2, 3, p) == ALIGN                     # int32 table
+    n = ctypes.c_size_t(0)
+    assert lib.gdr_chunk_bwd_varlen_workspace_size(ctypes.byref(dp), 3, ctypes.byref(n)) == OK
+    assert _fwd_save(lib, dp, FAKE, 3, p, ws_bytes=n.value - 16) == WORKSPACE
+
+
+def _bwd_saved(lib, d, cu, n_seq, p, ws_bytes=1 << 40):
+    """gdr_chunk_bwd_saved with p = (q, k, kw, v, beta, log_a, S0, dO, dS_T, dq, dk, dkw, dv, dbeta, dlog_a,
+    dS0, ws)."""
+    return lib.gdr_chunk_bwd_saved(None if d is None else ctypes.byref(d), cu, n_seq, *p[:16], p[16], ws_bytes, None)
+
+
+def test_saved_backward_checks(lib):
+    p = _ptrs(18)
+    p[2] = p[11] = None                                                    # no write key
+    d = _desc(B=2, T=130, H=3)
+    assert _bwd_saved(lib, None, None, 0, p) == INVALID
+    n = ctypes.c_size_t(0)
+    assert lib.gdr_chunk_bwd_workspace_size(ctypes.byref(d), ctypes.byref(n)) == OK
+    assert _bwd_saved(lib, d, None, 0, p, ws_bytes=n.value - 1) == WORKSPACE
+    bad = list(p)
+    bad[16] = None
+    assert _bwd_saved(lib, d, None, 0, bad) == WORKSPACE
+    assert _bwd_saved(lib, _desc(io=0), None, 0, p) == UNSUPPORTED
+    assert _bwd_saved(lib, d, None, 2, p) == INVALID                       # n_seq without an offset table
+    half = list(p)
+    half[2] = p[17]                                                        # kw without dkw
+    assert _bwd_saved(lib, d, None, 0, half) == INVALID
+    assert b"kw and dkw" in lib.gdr_last_error()
+    both = list(half)
+    both[11] = p[17] + (1 << 22)
+    assert _bwd_saved(lib, _desc(gate=2), None, 0, both) == UNSUPPORTED    # per-channel gate with a write key
+    for i, name in ((0, "q"), (7, "dO"), (9, "dq"), (13, "dbeta")):
+        bad = list(p)
+        bad[i] = None
+        assert _bwd_saved(lib, d, None, 0, bad) == INVALID, name
+    bad = list(p)
+    bad[10] = bad[1] + 64                                                  # dk inside k
+    assert _bwd_saved(lib, d, None, 0, bad) == INVALID
+    assert _bwd_saved(lib, _desc(B=2, T=300, H=2), FAKE, 3, p) == INVALID  # packed: B must be 1

@@ -1,0 +1,253 @@
+"""GPU checks of the training path: gdr_chunk_fwd_save leaves the per-chunk
+transform and the state entering every chunk in the backward's workspace, and
+gdr_chunk_bwd_saved takes them from there instead of recomputing them.
+
+"Moonshot AI's New Attention Architecture", §3 (chunk form): the backward needs
+the state entering each chunk and T of each chunk, which the forward forms on its
+way.  What is checked:
+- the training forward's o and S_T equal gdr_chunk_fwd's bit for bit, and its
+  records equal the backward's own transform bit for bit;
+- the chunk-start states it keeps against the fp64 chunk form's (sequence 0, head
+  0) and against the states the backward's first pass forms (gdr_chunk_bwd's
+  workspace after a call);
+- the saved backward's gradients against the fp64 oracle (relative L2 of 2e-2, the
+  bf16 bar of the backward) and against gdr_chunk_bwd's, for every gate, both
+  forms, the write key and packed sequences;
+- a second saved backward from the same workspace gives the same bits;
+- the gated B8 H16 T8192 d128 workload at full size: both backward paths agree
+  over whole tensors.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import backward as oracle_backward, rel_l2
+from tests.chunk_form import chunk_forward
+from tests.gpu_util import TOL, check, dev, host, need_gpu, say
+from tests.report import report
+from workloads import CONFIGS, Workload, chunk_inputs, grad_inputs, round_to_io
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("dq", "dk", "dv", "dbeta", "dlog_a", "dS0")
+# Two GPU paths that read the same bf16 chunk states: their gradients differ at most
+# by the rounding of those states to bf16, far below the oracle bar.
+AGREE = 5e-3
+
+
+def _inputs(B, T, H, dk, dv, gate, seed, wkey=False):
+    wl = Workload("saved", B=B, T=T, H=H, d_k=dk, d_v=dv, io="bf16", gate=gate, s0_std=0.5, seed=seed)
+    x = chunk_inputs(wl)
+    x.update(grad_inputs(wl))
+    if wkey:
+        d = np.random.default_rng(seed + 1000).uniform(0.2, 2.0, x["k"].shape)
+        x["kw"] = round_to_io(x["k"].astype(np.float64) * d, "bf16")
+    return x
+
+
+def _dev(x):
+    import torch
+    t = {n: dev(x.get(n), "bf16") for n in ("q", "k", "v", "beta", "log_a", "dO", "kw")}
+    t["S0"] = torch.from_numpy(x["S0"]).cuda()
+    t["dS_T"] = torch.from_numpy(x["dS_T"]).cuda()
+    return t
+
+
+def _layout(B, T, H, dk, dv, gate):
+    """Byte offsets in the backward's workspace: records, chunk-start states."""
+    import gated_delta_rule_21_amd as gdr
+    rec = gdr.chunk_workspace_size(B, T, H, dk, dv, gate=gate)
+    sb = B * H * (-(-T // 64)) * dk * dv * 2
+    return rec, sb
+
+
+def _states(ws, rec, sb, B, H, nch, dk, dv):
+    """The bf16 chunk-start states of a workspace as [B, H, nch, d_k, d_v] float64 (each
+    chunk's state is stored in d_k tiles of 16, value-major: [d_k / 16][d_v][16])."""
+    import torch
+    s = ws[rec:rec + sb].view(torch.bfloat16).float().cpu().numpy().astype(np.float64)
+    s = s.reshape(B, H, nch, dk // 16, dv, 16).transpose(0, 1, 2, 3, 5, 4)
+    return s.reshape(B, H, nch, dk, dv)
+
+
+def _run_both(t, form="page", packed_cu=None):
+    """Training forward + saved backward, and the plain forward and backward, on the
+    same device inputs.  Returns (fwd_save, fwd, bwd_saved, bwd, ws_save, ws_plain)."""
+    import torch
+    import gated_delta_rule_21_amd as gdr
+    B, T, H, dk = t["k"].shape
+    dv = t["v"].shape[-1]
+    gate = "none" if t["log_a"] is None else ("scalar" if t["log_a"].dim() == 3 else "channel")
+    if packed_cu is None:
+        need = gdr.chunk_bwd_workspace_size(B, T, H, dk, dv, gate=gate)
+    else:
+        need = None
+    ws_s = torch.zeros(max(need, 1), dtype=torch.uint8, device="cuda") if need is not None else None
+    base = (t["q"], t["k"], t["v"], t["beta"], t["log_a"], t["S0"])
+    o_s, S_s, ws_s = gdr.chunk_fwd_save(*base, cu_seqlens=packed_cu, form=form, kw=t["kw"], workspace=ws_s)
+    if packed_cu is None:
+        o_p, S_p = gdr.chunk_fwd(*base, form=form, kw=t["kw"])
+    else:
+        o_p, S_p = gdr.chunk_fwd_varlen(t["q"], t["k"], t["v"], t["beta"], t["log_a"], packed_cu, t["S0"], form=form,
+                                        kw=t["kw"])
+    # the backward's own workspace, zeroed so that bytes neither path writes compare equal
+    ws_p = torch.zeros_like(ws_s)
+    g_s = gdr.chunk_bwd(*base, t["dO"], t["dS_T"], cu_seqlens=packed_cu, form=form, kw=t["kw"], saved=ws_s)
+    g_p = gdr.chunk_bwd(*base, t["dO"], t["dS_T"], cu_seqlens=packed_cu, form=form, kw=t["kw"], workspace=ws_p)
+    torch.cuda.synchronize()
+    return (o_s, S_s), (o_p, S_p), g_s, g_p, ws_s, ws_p
+
+
+def _agree(g_s, g_p, gate, wkey):
+    worst = 0.0
+    for n in NAMES + (("dkw",) if wkey else ()):
+        if n == "dlog_a" and gate == "none":
+            continue
+        a, b = host(g_s[n]), host(g_p[n])
+        assert np.all(np.isfinite(a)), n
+        e = rel_l2(a, b)
+        worst = max(worst, e)
+        assert e <= AGREE, f"{n}: saved and recomputed backward differ by rel_l2 {e:.3e}"
+    return worst
+
+
+CASES = [  # B, T, H, d_k, d_v, gate, form, write key
+    (2, 200, 3, 128, 128, "scalar", "page", False),
+    (2, 200, 3, 128, 128, "none", "page", False),
+    (1, 130, 2, 64, 64, "scalar", "page", False),
+    (2, 100, 2, 128, 64, "scalar", "literal", False),
+    (1, 70, 2, 64, 128, "none", "literal", False),
+    (2, 150, 2, 128, 128, "channel", "page", False),
+    (1, 129, 2, 128, 64, "channel", "literal", False),
+    (2, 200, 2, 128, 128, "scalar", "page", True),
+    (1, 100, 3, 64, 128, "none", "page", True),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B%dT%dH%ddk%ddv%d-%s-%s%s" % (c[:7] + ("-wkey" if c[7] else "",)))
+def test_saved_training_step(case):
+    need_gpu()
+    B, T, H, dk, dv, gate, form, wkey = case
+    say(f"case training step {case}")
+    x = _inputs(B, T, H, dk, dv, gate, seed=B + T + dk + dv + len(gate) + wkey, wkey=wkey)
+    t = _dev(x)
+    (o_s, S_s), (o_p, S_p), g_s, g_p, ws_s, ws_p = _run_both(t, form=form)
+    # the forward's outputs are unchanged by saving
+    assert bool((o_s == o_p).all()) and bool((S_s == S_p).all())
+    rec, sb = _layout(B, T, H, dk, dv, gate)
+    # the same transform as the backward's own
+    assert bool((ws_s[:rec] == ws_p[:rec]).all()), "records differ from the backward's transform"
+    nch = -(-T // 64)
+    st_s = _states(ws_s, rec, sb, B, H, nch, dk, dv)
+    st_p = _states(ws_p, rec, sb, B, H, nch, dk, dv)
+    same = float(np.mean(st_s == st_p))
+    e_states = rel_l2(st_s, st_p)
+    say(f"  chunk-start states: {same:.4f} of the values equal to the backward's first pass, rel_l2 {e_states:.2e}")
+    assert e_states <= AGREE
+    # against the fp64 chunk form (sequence 0, head 0)
+    _, _, inter = chunk_forward(x["q"], x["k"], x["v"], x["beta"], x["log_a"], x["S0"], 64, form=form, keep=True,
+                                kw=x.get("kw"))
+    ref_states = np.stack([c["S_in"] for c in inter])
+    check("states[b=0,h=0]", st_s[0, 0], ref_states, TOL["bf16"])
+    # gradients
+    ref = oracle_backward(x["q"], x["k"], x["v"], x["beta"], x["log_a"], x["S0"], x["dO"], x["dS_T"], form=form,
+                          kw=x.get("kw"))
+    for n in NAMES + (("dkw",) if wkey else ()):
+        if n == "dlog_a" and gate == "none":
+            continue
+        check(n, host(g_s[n]), ref[n], TOL["bf16"])
+    worst = _agree(g_s, g_p, gate, wkey)
+    say(f"  saved vs recomputed backward: worst rel_l2 {worst:.2e}")
+
+
+LENS = [0, 1, 63, 64, 65, 130, 200, 7]
+
+
+@pytest.mark.parametrize("gate,wkey", [("scalar", False), ("none", False), ("channel", False), ("scalar", True)])
+def test_saved_training_step_packed(gate, wkey):
+    """Packed sequences: the training forward's order table sits where the backward
+    later writes its state gradients; per-sequence gradients against the oracle."""
+    need_gpu()
+    import torch
+    say(f"case packed training step gate={gate} wkey={wkey} lens={LENS}")
+    Ttot, H, dk, dv = int(sum(LENS)), 2, 128, 128
+    x = _inputs(1, Ttot, H, dk, dv, gate, seed=91 + len(gate) + wkey, wkey=wkey)
+    per = Workload("saved_states", B=len(LENS), T=1, H=H, d_k=dk, d_v=dv, io="bf16", gate=gate, s0_std=0.5, seed=93)
+    x["S0"] = chunk_inputs(per)["S0"]
+    x["dS_T"] = grad_inputs(per)["dS_T"]
+    cu = np.concatenate([[0], np.cumsum(LENS)]).astype(np.int32)
+    t = _dev(x)
+    (o_s, S_s), (o_p, S_p), g_s, g_p, _, _ = _run_both(t, packed_cu=torch.from_numpy(cu).cuda())
+    assert bool((o_s == o_p).all()) and bool((S_s == S_p).all())
+    names = ["dq", "dk", "dv", "dbeta"] + (["dlog_a"] if gate != "none" else []) + (["dkw"] if wkey else [])
+    got = {n: host(g_s[n]) for n in names + ["dS0"]}
+    ref = {n: np.zeros(got[n].shape) for n in names}
+    for i in range(len(LENS)):
+        lo, hi = int(cu[i]), int(cu[i + 1])
+        sl = lambda a: None if a is None else np.ascontiguousarray(a[:, lo:hi])
+        r = oracle_backward(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["beta"]), sl(x["log_a"]), x["S0"][i:i + 1],
+                            sl(x["dO"]), x["dS_T"][i:i + 1], kw=sl(x.get("kw")))
+        for n in names:
+            ref[n][:, lo:hi] = r[n]
+        check(f"dS0[seq {i}, T={hi - lo}]", got["dS0"][i:i + 1], r["dS0"], TOL["bf16"])
+    for n in names:
+        check(n, got[n], ref[n], TOL["bf16"])
+    _agree(g_s, g_p, gate, wkey)
+
+
+def test_saved_workspace_serves_repeated_backward():
+    """The saved backward leaves the records and the states in place: a second call
+    from the same workspace gives the same bits."""
+    need_gpu()
+    import torch
+    import gated_delta_rule_21_amd as gdr
+    x = _inputs(2, 300, 3, 128, 128, "scalar", seed=31)
+    t = _dev(x)
+    base = (t["q"], t["k"], t["v"], t["beta"], t["log_a"], t["S0"])
+    _, _, ws = gdr.chunk_fwd_save(*base)
+    a = gdr.chunk_bwd(*base, t["dO"], t["dS_T"], saved=ws)
+    b = gdr.chunk_bwd(*base, t["dO"], t["dS_T"], saved=ws)
+    torch.cuda.synchronize()
+    for n in NAMES:
+        assert bool((a[n] == b[n]).all()), n
+
+
+def test_saved_backward_ignores_S0():
+    """S0 is not read by the saved backward (its chunk-start state is in the
+    workspace): NULL, or the final state written over it in place by the forward."""
+    need_gpu()
+    import torch
+    import gated_delta_rule_21_amd as gdr
+    x = _inputs(2, 150, 2, 128, 128, "scalar", seed=37)
+    t = _dev(x)
+    base = (t["q"], t["k"], t["v"], t["beta"], t["log_a"])
+    S = t["S0"].clone()
+    _, _, ws = gdr.chunk_fwd_save(*base, S, S_T=S)        # S now holds S_T
+    a = gdr.chunk_bwd(*base, None, t["dO"], t["dS_T"], saved=ws, want_dS0=True)
+    ref = gdr.chunk_bwd(*base, t["S0"], t["dO"], t["dS_T"])
+    torch.cuda.synchronize()
+    for n in NAMES:
+        assert np.all(np.isfinite(host(a[n]))), n
+        assert rel_l2(host(a[n]), host(ref[n])) <= AGREE, n
+
+
+def test_saved_full_size():
+    """The gated B8 H16 T8192 d128 bf16 workload: training forward and saved backward
+    against the plain forward and backward, over whole tensors."""
+    need_gpu()
+    import torch
+    wl = CONFIGS[3]
+    say(f"full-size training step {wl.name}: generating inputs")
+    x = chunk_inputs(wl)
+    x.update(grad_inputs(wl))
+    x["kw"] = None
+    t = _dev(x)
+    del x
+    say("  running GPU")
+    (o_s, S_s), (o_p, S_p), g_s, g_p, _, _ = _run_both(t)
+    assert bool((o_s == o_p).all()) and bool((S_s == S_p).all())
+    worst = _agree(g_s, g_p, "scalar", False)
+    report(f"training step {wl.name}: forward outputs equal bit for bit with the states kept; "
+           f"saved vs recomputed backward, whole tensors: worst rel_l2 {worst:.2e}")
+    del g_s, g_p
+    torch.cuda.empty_cache()
