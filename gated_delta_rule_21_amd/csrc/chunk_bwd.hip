@@ -424,17 +424,241 @@ __device__ __forceinline__ void reverse_pass(const BwdParams& p, int n_tiles, in
   }
 }
 
-// Passes 1 and 2 in one launch of 2 nseq workgroups: the first nseq take pass 1.
-// With the chunk-start states saved by the forward (p.saved), nseq workgroups of pass 2.
+// Passes 1 and 2 in one launch of 2 nseq workgroups: the first nseq take pass 1
+// (mode 0); nseq workgroups of pass 1 alone (mode 1) or of pass 2 alone (mode 2).
 template <int GATE, int DK, bool WK>
-__global__ __launch_bounds__(256) void bwd_seq_kernel(BwdParams p, int n_tiles, int nseq) {
+__global__ __launch_bounds__(256) void bwd_seq_kernel(BwdParams p, int n_tiles, int nseq, int mode) {
   constexpr bool KD = GATE == GATE_CHANNEL || WK;
   __shared__ __attribute__((aligned(16))) char smem[cmax(SeqLayout<DK, false, KD>::TOTAL, SeqLayout<DK, true, KD>::TOTAL)];
   const int b = blockIdx.x;
-  const int role = p.saved ? 1 : b >= nseq;
-  const int idx = p.saved ? b : b - role * nseq;
+  const int role = mode == 0 ? b >= nseq : mode == 2;
+  const int idx = mode == 0 ? b - role * nseq : b;
   if (role == 0) states_pass<GATE, DK, WK>(p, n_tiles, idx, smem);
   else reverse_pass<GATE, DK, WK>(p, n_tiles, idx, smem);
+}
+
+// Pass 2 with chain and helper waves (no gate or a scalar gate, no write key): four
+// chain waves keep 16 columns of dS each in MFMA accumulators, four helper waves
+// stage the tiles and form P one chunk ahead, with two copies of the tiles and of P
+// in LDS and two barriers per chunk.  In the step of chunk n (copy b):
+//   chain   | dS' out; dDelta = diag(e^{g_63 - g}) K dS' + P^T dO; dY = T^T dDelta;
+//           |   Z = -diag(beta e^g) dY
+//   helpers | chunk n - 1 from registers into copy 1 - b; loads of chunk n - 2
+//   ------------------------------------------------------------------- barrier
+//   chain   | dS = e^{g_63} dS' + Q^T diag(e^g) dO + K^T Z
+//   helpers | P of chunk n - 1 from copy 1 - b into P copy 1 - b
+//   ------------------------------------------------------------------- barrier
+// Copy 1 - b and P copy 1 - b were last read by the chain in the step before,
+// ahead of its closing barrier.  Only dDelta -> dY -> Z -> K^T Z lies on the chain
+// from chunk to chunk; P, the staging and Q^T dO are off it or beside it.
+template <int GATE, int DK>
+struct RevPipeLayout {
+  typedef SeqLayout<DK, true, false> S;   // one copy of the tiles (k, q, dO, T^T, factors) and P
+  static constexpr size_t BUF = S::BUF;
+  static constexpr size_t PB = size_t(CH) * S::LCP * 2;
+  static constexpr size_t O_P = 2 * BUF;
+  static constexpr size_t TOTAL = O_P + 2 * PB;
+};
+
+template <int GATE, int DK>
+__global__ __launch_bounds__(512) void bwd_rev_pipe_kernel(BwdParams p, int n_tiles) {
+  static_assert(GATE == GATE_NONE || GATE == GATE_SCALAR, "chain/helper reverse pass: no gate or a scalar gate");
+  typedef SeqLayout<DK, true, false> S;
+  typedef RevPipeLayout<GATE, DK> L;
+  static_assert(L::TOTAL <= 163840, "LDS budget");
+  constexpr uint32_t RB = rec_bytes(IO_BF16, GATE, DK);
+  constexpr int DKT = DK / 16, LDK = S::LDK, LDV = S::LDV, LCT = S::LCT, LCP = S::LCP;
+  __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
+  const ChunkParams& f = p.f;
+  const int lb = blockIdx.x;
+  const int64_t bh = lb / n_tiles;
+  const int tile = lb % n_tiles;
+  const int64_t bb = bh / f.H, hh = bh % f.H;
+  const int dv = f.d_v, H = static_cast<int>(f.H), col0 = tile * 64;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool chain = wave < 4;
+  const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const BwdSeq sq = bwd_seq_of(f, bb, hh);
+  const int64_t nch = sq.nch;
+  const Slice sl = sq.sl;
+  const rsrc_t rk = sl.rs(f.k, DK), rq = sl.rs(f.q, DK), rdo = sl.rs(p.dO, dv);
+  const rsrc_t rw = make_rsrc(static_cast<const char*>(f.ws) + sq.rec0 * RB, static_cast<uint32_t>(nch * RB));
+  auto buf = [&](int64_t i) -> char* { return smem + (i & 1) * L::BUF; };
+  auto pbuf = [&](int64_t i) -> T* { return reinterpret_cast<T*>(smem + L::O_P + (i & 1) * L::PB); };
+
+  if (chain) {
+    const int scol = col0 + 16 * wave + lr;
+    const uint32_t sbytes = static_cast<uint32_t>(dv * DK * 2);
+    const rsrc_t rds = make_rsrc(static_cast<char*>(p.dstates) + sq.rec0 * sbytes, static_cast<uint32_t>(nch * sbytes));
+    f32x4 dS[DKT];   // dS[t][s] = dS[16t + 4lg + s][scol]
+#pragma unroll
+    for (int t = 0; t < DKT; ++t)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) dS[t][s] = p.dS_T ? p.dS_T[(bh * DK + 16 * t + 4 * lg + s) * dv + scol] : 0.f;
+    __syncthreads();                    // the last chunk's tiles in copy 0
+    __syncthreads();                    // its P
+    for (int64_t n = nch - 1; n >= 0; --n) {
+      const int64_t i = nch - 1 - n;    // step index: the copy in use
+      const char* cur = buf(i);
+      const T* sK = reinterpret_cast<const T*>(cur + S::O_K);
+      const T* sQ = reinterpret_cast<const T*>(cur + S::O_Q);
+      const T* sO = reinterpret_cast<const T*>(cur + S::O_V);
+      const T* sT = reinterpret_cast<const T*>(cur + S::O_T);
+      const float* sF = reinterpret_cast<const float*>(cur + S::O_F);
+      const T* sP = pbuf(i);
+
+      const uint32_t so = static_cast<uint32_t>(n) * sbytes;
+#pragma unroll
+      for (int t = 0; t < DKT; ++t) buf_store8(bits8(dS[t]), rds, chunk_state_off(16 * t + 4 * lg, scol, dv), so);
+      frag dSb[DKT];
+#pragma unroll
+      for (int t = 0; t < DKT; ++t) dSb[t] = O::cvt(dS[t]);
+      frag dOf[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) dOf[kb] = colf(sO, LDV, 16 * kb, 16 * wave, lr, lg);
+      // The products below read their LDS fragments one row block (or state tile) ahead,
+      // and scheduling fences keep the compiler from sinking those reads to their use.
+      frag kf[2][DK / 16], pf[2][4];    // rows of K of block M, columns of P^T of block M
+      auto load_d = [&](int b, int M) __attribute__((always_inline)) {
+#pragma unroll
+        for (int kb = 0; kb < DK / 32; ++kb) {
+          kf[b][2 * kb] = rowf(sK, LDK, 16 * M, 32 * kb, lr, lg);
+          kf[b][2 * kb + 1] = rowf(sK, LDK, 16 * M, 32 * kb + 16, lr, lg);
+        }
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+          if (kb >= M) pf[b][kb] = colf(sP, LCP, 16 * kb, 16 * M, lr, lg);
+      };
+      load_d(0, 0);
+      frag dDb[4];
+#pragma unroll
+      for (int M = 0; M < 4; ++M) {     // dDelta = diag(e^{g_63 - g}) K dS' + P^T dO
+        __builtin_amdgcn_sched_barrier(0);
+        if (M < 3) load_d((M + 1) & 1, M + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < DK / 32; ++kb)
+          acc = O::mma2(acc, kf[M & 1][2 * kb], kf[M & 1][2 * kb + 1], dSb[2 * kb], dSb[2 * kb + 1]);
+        if constexpr (GATE == GATE_SCALAR) {
+#pragma unroll
+          for (int s = 0; s < 4; ++s) acc[s] *= sF[3 * CH + 16 * M + 4 * lg + s];
+        }
+        int kb = M;
+#pragma unroll
+        for (; kb + 1 <= 3; kb += 2) acc = O::mma2(acc, pf[M & 1][kb], pf[M & 1][kb + 1], dOf[kb], dOf[kb + 1]);
+        if (kb <= 3) acc = O::mma1(acc, pf[M & 1][kb], dOf[kb]);
+        dDb[M] = O::cvt(acc);
+      }
+      frag Zb[4];
+#pragma unroll
+      for (int M = 0; M < 4; ++M) {     // dY = T^T dDelta; Z = -diag(beta e^g) dY
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        int kb = M;
+#pragma unroll
+        for (; kb + 1 <= 3; kb += 2)
+          acc = O::mma2(acc, rowf(sT, LCT, 16 * M, 16 * kb, lr, lg), rowf(sT, LCT, 16 * M, 16 * (kb + 1), lr, lg),
+                        dDb[kb], dDb[kb + 1]);
+        if (kb <= 3) acc = O::mma1(acc, rowf(sT, LCT, 16 * M, 16 * kb, lr, lg), dDb[kb]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int r = 16 * M + 4 * lg + s;
+          acc[s] *= -(GATE == GATE_SCALAR ? sF[r] * sF[CH + r] : sF[r]);
+        }
+        Zb[M] = O::cvt(acc);
+      }
+      __syncthreads();                  // the helpers' copy of chunk n - 1 in place
+      frag dOg[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        if constexpr (GATE == GATE_SCALAR) {
+          f32x4 x = O::f32(dOf[kb]);
+#pragma unroll
+          for (int s = 0; s < 4; ++s) x[s] *= sF[2 * CH + 16 * kb + 4 * lg + s];
+          dOg[kb] = O::cvt(x);
+        } else {
+          dOg[kb] = dOf[kb];
+        }
+      }
+      frag uf[2][8];                    // columns of Q^T and K^T of state tile t
+      auto load_u = [&](int b, int t) __attribute__((always_inline)) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          uf[b][m] = colf(sQ, LDK, 16 * m, 16 * t, lr, lg);
+          uf[b][4 + m] = colf(sK, LDK, 16 * m, 16 * t, lr, lg);
+        }
+      };
+      const float gam = GATE == GATE_SCALAR ? sF[4 * CH] : 1.f;
+      load_u(0, 0);
+#pragma unroll
+      for (int t = 0; t < DKT; ++t) {   // dS = e^{g_63} dS' + Q^T diag(e^g) dO + K^T Z
+        __builtin_amdgcn_sched_barrier(0);
+        if (t + 1 < DKT) load_u((t + 1) & 1, t + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4 acc = dS[t];
+        if constexpr (GATE == GATE_SCALAR) acc = acc * gam;
+        acc = O::mma2(acc, uf[t & 1][0], uf[t & 1][1], dOg[0], dOg[1]);
+        acc = O::mma2(acc, uf[t & 1][2], uf[t & 1][3], dOg[2], dOg[3]);
+        acc = O::mma2(acc, uf[t & 1][4], uf[t & 1][5], Zb[0], Zb[1]);
+        acc = O::mma2(acc, uf[t & 1][6], uf[t & 1][7], Zb[2], Zb[3]);
+        dS[t] = acc;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();                  // P of chunk n - 1 in place; this chunk's copies read
+    }
+    if (p.dS0) {
+#pragma unroll
+      for (int t = 0; t < DKT; ++t)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) p.dS0[(bh * DK + 16 * t + 4 * lg + s) * dv + scol] = dS[t][s];
+    }
+  } else {
+    const int ht = tid - 256, hw = wave - 4;
+    SeqStage<DK, 256, true, false, false> st;
+    // P of one chunk from its copy: blocks u = hw, hw + 4, .. (row form: row 16R + lr)
+    auto form_p = [&](const char* c, T* sP) __attribute__((always_inline)) {
+      const T* sK = reinterpret_cast<const T*>(c + S::O_K);
+      const T* sQ = reinterpret_cast<const T*>(c + S::O_Q);
+      const float* sF = reinterpret_cast<const float*>(c + S::O_F);
+      for (int u = hw; u < 10; u += 4) {
+        int R, J;
+        tri_block(u, R, J);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < DK / 32; ++kb)
+          acc = O::mma2(acc, rowf(sK, LDK, 16 * J, 32 * kb, lr, lg), rowf(sK, LDK, 16 * J, 32 * kb + 16, lr, lg),
+                        rowf(sQ, LDK, 16 * R, 32 * kb, lr, lg), rowf(sQ, LDK, 16 * R, 32 * kb + 16, lr, lg));
+        const int r = 16 * R + lr;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int j = 16 * J + 4 * lg + s;
+          float x = j <= r ? acc[s] : 0.f;
+          if constexpr (GATE == GATE_SCALAR) x *= __expf(fminf(sF[5 * CH + r] - sF[5 * CH + j], 0.f));
+          acc[s] = x;
+        }
+        st_row(sP, LCP, r, 16 * J + 4 * lg, acc);
+      }
+    };
+    if (nch > 0) {
+      st.load(rk, rq, rdo, rw, rk, nch - 1, ht, H, dv, col0);
+      st.store(buf(0), ht);
+      if (nch > 1) st.load(rk, rq, rdo, rw, rk, nch - 2, ht, H, dv, col0);
+    }
+    __syncthreads();                    // the last chunk's tiles in copy 0
+    if (nch > 0) form_p(buf(0), pbuf(0));
+    __syncthreads();                    // its P
+    for (int64_t n = nch - 1; n >= 0; --n) {
+      const int64_t i = nch - 1 - n;
+      if (n >= 1) {
+        st.store(buf(i + 1), ht);       // chunk n - 1 into the other copy
+        if (n >= 2) st.load(rk, rq, rdo, rw, rk, n - 2, ht, H, dv, col0);
+      }
+      __syncthreads();                  // chunk n - 1 in place
+      if (n >= 1) form_p(buf(i + 1), pbuf(i + 1));
+      __syncthreads();                  // its P in place
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -948,9 +1172,21 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
   const ChunkParams& f = p.f;
   const int n_tiles = f.d_v / 64;
   const int64_t nseq = f.B * f.H * n_tiles;
-  hipLaunchKernelGGL((bwd_seq_kernel<GATE, DK, WK>), dim3(static_cast<unsigned>((p.saved ? 1 : 2) * nseq)), dim3(256),
-                     0, stream, p, n_tiles, static_cast<int>(nseq));
-  hipError_t e = hipGetLastError();
+  hipError_t e;
+  bool rev_pipe = false;
+  if constexpr (GATE != GATE_CHANNEL && !WK) rev_pipe = p.saved != 0;
+  if (rev_pipe) {
+    // the states came from the training forward: pass 2 alone, with chain and helper
+    // waves.  (Both passes run side by side otherwise, a workgroup of each per compute
+    // unit, which the chain/helper pass's LDS would not leave room for.)
+    if constexpr (GATE != GATE_CHANNEL && !WK)
+      hipLaunchKernelGGL((bwd_rev_pipe_kernel<GATE, DK>), dim3(static_cast<unsigned>(nseq)), dim3(512), 0, stream, p,
+                         n_tiles);
+  } else {
+    hipLaunchKernelGGL((bwd_seq_kernel<GATE, DK, WK>), dim3(static_cast<unsigned>((p.saved ? 1 : 2) * nseq)),
+                       dim3(256), 0, stream, p, n_tiles, static_cast<int>(nseq), p.saved ? 2 : 0);
+  }
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   if constexpr (GATE == GATE_CHANNEL) {
     static_assert(!WK, "per-channel gate: no write key");
