@@ -389,7 +389,8 @@ def bench_bwd(prep, args, log, wl, q, k, v, beta, log_a, S0):
     flops = bwd_algorithmic(wl)
     tf = flops / (ms * 1e-3) / 1e12
     log(f"chunk backward: {ms:.3f} ms/step, {tf:.1f} TFLOP/s useful")
-    wk_ms = None
+    wk_ms = wk_train = None
+    import torch
     if wl.gate in ("none", "scalar"):
         # the backward with a separate write key (the preconditioned rule's training
         # step); a copy of k stands for it, since the kernels' work does not depend on
@@ -397,12 +398,22 @@ def bench_bwd(prep, args, log, wl, q, k, v, beta, log_a, S0):
         kw = k.clone()
         wk_ms = time_calls(lambda i: gdr.chunk_bwd(q, k, v, beta, log_a, S0, dO, dS_T, workspace=ws, kw=kw),
                            args.warmup, args.steps)
-        del kw
         log(f"chunk backward with a write key: {wk_ms:.3f} ms/step")
+        # ... and its training path (the forward keeping the chunk-start states)
+        o_w = torch.empty_like(v)
+        S_w = torch.empty((wl.B, wl.H, wl.d_k, wl.d_v), dtype=torch.float32, device="cuda")
+        wf = time_calls(lambda i: gdr.chunk_fwd_save(q, k, v, beta, log_a, S0, kw=kw, o=o_w, S_T=S_w, workspace=ws),
+                        args.warmup, args.steps)
+        wb = time_calls(lambda i: gdr.chunk_bwd(q, k, v, beta, log_a, S0, dO, dS_T, kw=kw, saved=ws), args.warmup,
+                        args.steps)
+        wk_train = {"forward_ms_per_launch": round(wf, 4), "backward_ms_per_launch": round(wb, 4),
+                    "train_step_ms": round(wf + wb, 4),
+                    "train_step_tokens_per_s": round(wl.B * wl.T / ((wf + wb) * 1e-3), 1)}
+        log(f"write-key training path: forward {wf:.3f} ms, backward {wb:.3f} ms")
+        del kw, o_w, S_w
     # the training path: the forward keeps the transform's records and the
     # chunk-start states in the backward's workspace (gdr_chunk_fwd_save) and the
     # backward takes them from there (gdr_chunk_bwd_saved)
-    import torch
     o_s, S_s = torch.empty_like(v), torch.empty((wl.B, wl.H, wl.d_k, wl.d_v), dtype=torch.float32, device="cuda")
     fs_ms = time_calls(lambda i: gdr.chunk_fwd_save(q, k, v, beta, log_a, S0, o=o_s, S_T=S_s, workspace=ws),
                        args.warmup, args.steps)
@@ -421,7 +432,7 @@ def bench_bwd(prep, args, log, wl, q, k, v, beta, log_a, S0):
     return {"workload": wl.name + "_backward", "value": round(wl.B * wl.T / (ms * 1e-3), 1), "unit": "tokens/s",
             "ms_per_launch": round(ms, 4), "useful_flops_per_launch": flops,
             "write_key_ms_per_launch": None if wk_ms is None else round(wk_ms, 4),
-            "training_path": saved,
+            "training_path": saved, "write_key_training_path": wk_train,
             "algorithmic_bytes_per_launch": bwd_bytes(wl, S0 is not None),
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf / BF16_PEAK_TFLOPS, 4),

@@ -251,3 +251,43 @@ def test_saved_full_size():
            f"saved vs recomputed backward, whole tensors: worst rel_l2 {worst:.2e}")
     del g_s, g_p
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("T", [0, 1, 63, 64, 65])
+def test_saved_lengths(T):
+    """Empty, single-token and chunk-boundary lengths; with T = 0 the saved backward
+    passes dS_T through to dS0 and the forward's workspace may be empty."""
+    need_gpu()
+    import torch
+    import gated_delta_rule_21_amd as gdr
+    say(f"case training step T={T}")
+    x = _inputs(2, T, 2, 128, 128, "scalar", seed=300 + T)
+    t = _dev(x)
+    base = (t["q"], t["k"], t["v"], t["beta"], t["log_a"], t["S0"])
+    o, S_T, ws = gdr.chunk_fwd_save(*base)
+    g = gdr.chunk_bwd(*base, t["dO"], t["dS_T"], saved=ws)
+    torch.cuda.synchronize()
+    if T == 0:
+        assert np.array_equal(host(S_T), x["S0"].astype(np.float64))
+        assert np.array_equal(host(g["dS0"]), x["dS_T"].astype(np.float64))
+        return
+    ref = oracle_backward(x["q"], x["k"], x["v"], x["beta"], x["log_a"], x["S0"], x["dO"], x["dS_T"])
+    for n in NAMES:
+        check(n, host(g[n]), ref[n], TOL["bf16"])
+
+
+def test_saved_without_state_terms():
+    """No initial state (zero) and no final-state gradient; dS0 not requested."""
+    need_gpu()
+    import torch
+    import gated_delta_rule_21_amd as gdr
+    x = _inputs(2, 150, 2, 128, 128, "none", seed=41)
+    t = _dev(x)
+    base = (t["q"], t["k"], t["v"], t["beta"], None)
+    _, _, ws = gdr.chunk_fwd_save(*base, None)
+    g = gdr.chunk_bwd(*base, None, t["dO"], None, saved=ws, want_dS0=False)
+    torch.cuda.synchronize()
+    assert g["dS0"] is None
+    ref = oracle_backward(x["q"], x["k"], x["v"], x["beta"], None, None, x["dO"], None)
+    for n in ("dq", "dk", "dv", "dbeta"):
+        check(n, host(g[n]), ref[n], TOL["bf16"])
