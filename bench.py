@@ -425,10 +425,14 @@ def bench_bwd(prep, args, log, wl, q, k, v, beta, log_a, S0):
         f"({stf:.1f} TFLOP/s useful)")
     saved = {"forward_ms_per_launch": round(fs_ms, 4), "backward_ms_per_launch": round(bs_ms, 4),
              "backward_useful_flops_per_launch": sflops,
+             "backward_algorithmic_bytes_per_launch": bwd_bytes(wl, False),
              "train_step_ms": round(fs_ms + bs_ms, 4),
              "train_step_tokens_per_s": round(wl.B * wl.T / ((fs_ms + bs_ms) * 1e-3), 1),
              "backward_roofline": {"bound": "mfma", "achieved": round(stf, 2), "peak": BF16_PEAK_TFLOPS,
-                                   "unit": "TFLOP/s", "frac": round(stf / BF16_PEAK_TFLOPS, 4), "traffic": None}}
+                                   "unit": "TFLOP/s", "frac": round(stf / BF16_PEAK_TFLOPS, 4),
+                                   "traffic": (profiled_traffic("chunk_bwd_saved_gated_b8h16t8192d128_counters.md",
+                                                                BWD_SOURCES)
+                                               if wl.name == "gated_deltanet_scalar_b8h16t8192d128_bf16" else None)}}
     return {"workload": wl.name + "_backward", "value": round(wl.B * wl.T / (ms * 1e-3), 1), "unit": "tokens/s",
             "ms_per_launch": round(ms, 4), "useful_flops_per_launch": flops,
             "write_key_ms_per_launch": None if wk_ms is None else round(wk_ms, 4),

@@ -169,10 +169,10 @@ def sq(paths, command: str, digest: str, title: str, useful_flops: float = 0.0) 
                 out.append(f"- MFMA busy: {f:.4f} of the kernel's SIMD cycles")
             if "SQ_INSTS_MFMA" in mean:
                 insts_all += mean["SQ_INSTS_MFMA"]
-        if "SQ_LDS_IDX_ACTIVE" in mean and "SQ_LDS_BANK_CONFLICT" in mean:
+        if mean.get("SQ_LDS_IDX_ACTIVE", 0) > 0 and "SQ_LDS_BANK_CONFLICT" in mean:
             out.append(f"- LDS bank conflicts: {mean['SQ_LDS_BANK_CONFLICT'] / mean['SQ_LDS_IDX_ACTIVE']:.3f} of "
                        "LDS-active cycles")
-        if "SQ_WAIT_ANY" in mean and "SQ_WAVE_CYCLES" in mean:
+        if "SQ_WAIT_ANY" in mean and mean.get("SQ_WAVE_CYCLES", 0) > 0:
             out.append(f"- waves waiting (SQ_WAIT_ANY / SQ_WAVE_CYCLES): {mean['SQ_WAIT_ANY'] / mean['SQ_WAVE_CYCLES']:.3f}"
                        f"; on LDS issue (SQ_WAIT_INST_LDS): {mean.get('SQ_WAIT_INST_LDS', 0) / mean['SQ_WAVE_CYCLES']:.3f}")
         out.append("")
