@@ -121,6 +121,7 @@ CASES = [  # B, T, H, d_k, d_v, gate, form, write key
     (1, 129, 2, 128, 64, "channel", "literal", False),
     (2, 200, 2, 128, 128, "scalar", "page", True),
     (1, 100, 3, 64, 128, "none", "page", True),
+    (2, 130, 2, 128, 64, "scalar", "literal", True),
 ]
 
 
