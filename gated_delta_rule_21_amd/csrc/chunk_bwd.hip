@@ -39,6 +39,11 @@
 // are value-major (chunk_state_off) so that an accumulator lane writes four adjacent
 // values and a store instruction 512 contiguous bytes.
 //
+// After a training forward (gdr_chunk_fwd_save), which leaves the transform's
+// records and the chunk-start states in this workspace, neither the transform nor
+// pass 1 runs; pass 2 then has the compute unit to itself and, without a per-channel
+// gate or a write key, runs as bwd_rev_pipe_kernel (chain and helper waves).
+//
 // With a per-channel gate the two sequential passes here take the transform's
 // decayed operands (k e^{g_read}, q e^{g}, k e^{g_63 - g}) and its P, and scale the
 // state's rows by e^{g_63} of their channel; the per-chunk gradients of that gate
