@@ -78,7 +78,9 @@ struct PipeLayout {
   static constexpr size_t TOTAL = OFF_P + 2 * PB;
 };
 
-template <int GATE, int DK, int NCH, int CG, int NHW>
+// SAVE: the training forward, which also stores the state entering every chunk
+// (p.states); a kernel of its own, so the inference forward carries none of it.
+template <int GATE, int DK, int NCH, int CG, int NHW, bool SAVE>
 __global__ __launch_bounds__((NCH + NHW) * 64) void chunk_state_pipe_kernel(ChunkParams p, int n_tiles) {
   typedef Op<IO_BF16> O;
   typedef __bf16 T;
@@ -317,8 +319,8 @@ __global__ __launch_bounds__((NCH + NHW) * 64) void chunk_state_pipe_kernel(Chun
     // Training forward: the state entering each chunk, in bf16 and in the layout the
     // backward reads (four adjacent d_k values per lane, streaming stores).
     const uint32_t sbytes = static_cast<uint32_t>(dv * DK * 2);
-    const rsrc_t rst = make_rsrc(p.states ? static_cast<char*>(p.states) + sq.rec0 * sbytes : nullptr,
-                                 p.states ? static_cast<uint32_t>(nchunks * sbytes) : 0u);
+    const rsrc_t rst = make_rsrc(SAVE ? static_cast<char*>(p.states) + sq.rec0 * sbytes : nullptr,
+                                 SAVE ? static_cast<uint32_t>(nchunks * sbytes) : 0u);
     uint32_t sto[CG];
 #pragma unroll
     for (int g = 0; g < CG; ++g) sto[g] = chunk_state_off(4 * lg, col0 + c0 + 16 * g + lr, dv);
@@ -360,7 +362,7 @@ __global__ __launch_bounds__((NCH + NHW) * 64) void chunk_state_pipe_kernel(Chun
       for (int g = 0; g < CG; ++g)
 #pragma unroll
         for (int t = 0; t < DKT; ++t) Sb[g][t] = O::cvt(S[g][t]);
-      if (p.states) {
+      if constexpr (SAVE) {
         const uint32_t so = static_cast<uint32_t>(n) * sbytes;
 #pragma unroll
         for (int g = 0; g < CG; ++g)
@@ -616,8 +618,12 @@ template <int GATE, int DK, int NCH, int CG, int NHW>
 static hipError_t launch_pipe_t(const ChunkParams& p, hipStream_t stream) {
   const int n_tiles = p.d_v / (16 * CG * NCH);
   const int64_t nblk = p.B * p.H * n_tiles;
-  hipLaunchKernelGGL((chunk_state_pipe_kernel<GATE, DK, NCH, CG, NHW>), dim3(static_cast<unsigned>(nblk)),
-                     dim3((NCH + NHW) * 64), 0, stream, p, n_tiles);
+  if (p.states)
+    hipLaunchKernelGGL((chunk_state_pipe_kernel<GATE, DK, NCH, CG, NHW, true>), dim3(static_cast<unsigned>(nblk)),
+                       dim3((NCH + NHW) * 64), 0, stream, p, n_tiles);
+  else
+    hipLaunchKernelGGL((chunk_state_pipe_kernel<GATE, DK, NCH, CG, NHW, false>), dim3(static_cast<unsigned>(nblk)),
+                       dim3((NCH + NHW) * 64), 0, stream, p, n_tiles);
   return hipGetLastError();
 }
 
