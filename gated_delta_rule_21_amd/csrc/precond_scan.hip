@@ -837,6 +837,409 @@ __global__ __launch_bounds__(64) void precond_scan_bwd_kernel(PrecondBwdParams q
   }
 }
 
+// ---------------------------------------------------------------------------------
+// bf16 I/O: the same reverse mode in blocks of U = 16 tokens, so that no sum over
+// the channels lies on the token-to-token chain.  NW = d_k / 64 waves per
+// (sequence, head); wave w owns channels 64 w .. 64 w + 63 (lane c: channel 64 w + c)
+// for the elementwise work, and the block's key products run on fp32 MFMA
+// (16x16x4, exact fp32 products).  Within a block starting from d_0, with the
+// retention products rat(j, i) = r_{i+1} ... r_{j-1} and P_j = r_0 ... r_{j-1}:
+//
+//   forward:  x_j = P_j <d_0, w_j> + sum_{i<j} rat(j, i) e_i <w_j, w_i>,
+//             e_j = gam_j - alf_j x_j       (one scalar per token, lane j, in order),
+//             d_{j+1} = r_j d_j + e_j w_j   (per channel, every d_j kept);
+//   reverse:  with D_U the gradient at the block's end and f_i = dkw_i * k_i,
+//             u_j = Q(j, U) <D_U, w_j> + sum_{i>j} Q(j, i) (<f_i, w_j> - rho_i u_i <w_i, w_j>),
+//             Q(j, i) = r_{j+1} ... r_{i-1}  (scalars, lane j, from the last token down),
+//             then per channel, token by token downwards, dk_j, the dr_j partial sums and
+//             D_j = r_j D_{j+1} - u_j rho_j w_j + f_j.
+//
+// The Gram matrix <w_i, w_j> (and its column of ones, the key norms n_i), the
+// cross products <f_i, w_j>, and the sums <d_0, w_j>, <D_U, w_j>, <D_{j+1}, d_j>
+// are the only sums over channels: MFMA for the first two, a halving exchange
+// across lanes for the others, each wave's part added through LDS (one barrier per
+// block).  Every wave runs the scalar chain of the block itself.
+// ---------------------------------------------------------------------------------
+namespace {
+// Sums over the 64 lanes of the sixteen values v[0..15] held by each lane: lane l
+// returns the total of v[l >> 2].  Each exchange halves the values a lane keeps and
+// pairs lanes that differ in one bit of the kept index: lanes 32 apart
+// (v_permlane32_swap), 16 apart (v_permlane16_swap), 8 apart (rotation by 8 in a
+// row of 16), then the mirror lane in each half row (l ^ 7: bit 2 flipped, bits 0
+// and 1 summed over by the quad that follows).
+__device__ __forceinline__ float lanes_sum16(float (&v)[16]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[i + 8]), false, false);
+    v[i] = __uint_as_float(s[0]) + __uint_as_float(s[1]);   // lanes 0-31: index i, lanes 32-63: i + 8
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i + 4]), false, false);
+    v[i] = __uint_as_float(s[0]) + __uint_as_float(s[1]);   // odd rows of 16: + 4
+  }
+  const int lane = threadIdx.x & 63;
+  const bool b3 = (lane & 8) != 0, b2 = (lane & 4) != 0;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const float keep = b3 ? v[i + 2] : v[i], send = b3 ? v[i] : v[i + 2];
+    v[i] = keep + dpp<0x128>(0.f, send);   // row_ror:8
+  }
+  const float keep = b2 ? v[1] : v[0], send = b2 ? v[0] : v[1];
+  return quad_sum(keep + dpp<0x141>(0.f, send));   // row_half_mirror, then the quad
+}
+// A 16-byte view of a tile of 16-bit elements: exempt from type-based alias
+// analysis, so that these accesses stay ordered with the element accesses.
+typedef u32x4 __attribute__((may_alias)) u32x4_alias;
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+// The 16 bf16 values of two 16-byte words, as fp32.
+__device__ __forceinline__ void unpack16(const uint4 (&x)[2], float (&o)[16]) {
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const uint32_t w[4] = {x[q].x, x[q].y, x[q].z, x[q].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[8 * q + 2 * i] = bf16_lo(w[i]);
+      o[8 * q + 2 * i + 1] = bf16_hi(w[i]);
+    }
+  }
+}
+}  // namespace
+
+template <int DK, bool HAS_R>
+__global__ __launch_bounds__(DK) void precond_scan_bwd_blk_kernel(PrecondBwdParams q) {
+  constexpr int NW = DK / 64, U = 16, GS = 20, TR = 72;   // GS, TR: row strides of the LDS matrices and tiles
+  const PrecondParams& p = q.f;
+  const int64_t bh = blockIdx.x;
+  const int64_t b = bh / p.H, h = bh - b * p.H;
+  const int64_t T = p.T, H = p.H;
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int c = 64 * wv + lane;                       // elementwise role: channel c
+  const int ta = lane & 15, ga = lane >> 4;           // MFMA role: token ta, channels 64 wv + 16 ga .. + 15
+  const int j = lane & 15;                            // scalar role: token j (lanes 16-63 repeat 0-15)
+  const uint32_t tokb = static_cast<uint32_t>(H * DK * 2);   // bytes from one token to the next: k, dkw, dk
+  const int64_t row0 = b * T * H + h;                        // element (token 0, head h) of [B, T, H] tensors
+  const uint32_t voffA = ta * tokb + (64 * wv + 16 * ga) * 2;
+  float* __restrict__ wd = q.ws + bh * T * DK;                     // d_t, [T][DK]
+  float* __restrict__ wxn = q.ws + p.B * H * T * DK + bh * T * 2;  // (x_t, n_t), [T][2]
+  // Buffer resources over this sequence's tokens 0 .. T - 1: loads of tokens past
+  // the end or before the start (offsets wrap to 2^32 - x) read zero, stores there
+  // are dropped.  Offsets within a sequence stay below 2^31.
+  auto rs_key = [&](const void* base) {   // [B, T, H, d_k] bf16
+    return make_rsrc(static_cast<const uint16_t*>(base) + row0 * DK,
+                     T > 0 ? static_cast<uint32_t>((T - 1) * tokb + DK * 2) : 0u);
+  };
+  const uint16_t* __restrict__ bp = static_cast<const uint16_t*>(p.beta);
+  const uint16_t* __restrict__ rp = static_cast<const uint16_t*>(HAS_R ? p.r : p.beta);
+  auto row_of = [&](int64_t t) { return (b * T + t) * H + h; };
+  auto clampt = [&](int64_t t) { return t < 0 ? int64_t(0) : (t >= T ? T - 1 : t); };
+  __shared__ __attribute__((aligned(16))) uint16_t sT[3][NW][U][TR];   // per-wave tiles of 16 tokens: k, dkw, dk
+  __shared__ __attribute__((aligned(16))) float sM[2][2][NW][U][GS];   // [block parity][G, F][wave][row][col]
+  __shared__ float sV[2][2][NW][U];                                    // [parity][sum][wave][token]
+  __shared__ __attribute__((aligned(16))) float sC[NW][U][4];          // per-wave, per-token coefficients
+  __shared__ __attribute__((aligned(16))) float sR[NW][2][U];          // per-wave: r_j and a second vector
+  const float eta = p.eta;
+  if (T <= 0) {                                       // no tokens: dd0 = dd_T
+    if (q.dd0) q.dd0[bh * DK + c] = q.dd_T ? q.dd_T[bh * DK + c] : 0.f;
+    return;
+  }
+  const int64_t nblk = (T + U - 1) / U;
+  // A wave's 16 tokens x 64 channels, loaded 16 channels per lane (MFMA layout), into
+  // its tile, from which each lane reads its channel of every token.
+  auto tile_put = [&](int t, const u32x4 (&x)[2]) {
+    *reinterpret_cast<u32x4_alias*>(&sT[t][wv][ta][16 * ga]) = x[0];
+    *reinterpret_cast<u32x4_alias*>(&sT[t][wv][ta][16 * ga + 8]) = x[1];
+  };
+  auto tile_get = [&](int t, int u) { return __uint_as_float(static_cast<uint32_t>(sT[t][wv][u][lane]) << 16); };
+  // the sixteen values a wave's lanes 0-15 wrote to sR[wv][i], on every lane
+  auto bcast16 = [&](int i, float (&o)[U]) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const float4 v = *reinterpret_cast<const float4*>(&sR[wv][i][4 * q4]);
+      o[4 * q4] = v.x;
+      o[4 * q4 + 1] = v.y;
+      o[4 * q4 + 2] = v.z;
+      o[4 * q4 + 3] = v.w;
+    }
+  };
+
+  // ---- forward: d_t, x_t and n_t of every token ------------------------------------
+  float d = p.d0 ? p.d0[bh * DK + c] : 1.f;
+  {
+    u32x4 kAc[2], kAn[2];
+    uint32_t bc, rc, bn = 0, rn = 0;
+    float dsave[U], xs = 0.f, ns = 0.f;
+    const rsrc_t rk = rs_key(p.k), rd = make_rsrc(wd, static_cast<uint32_t>(T * DK * 4));
+    auto load = [&](int64_t t0, u32x4 (&kA)[2], uint32_t& bx, uint32_t& rx) {
+      const uint32_t vo = voffA + static_cast<uint32_t>(t0) * tokb;
+      kA[0] = buf_load16(rk, vo, 0);
+      kA[1] = buf_load16(rk, vo + 16, 0);
+      const int64_t row = row_of(clampt(t0 + j));
+      bx = bp[row];
+      rx = HAS_R ? rp[row] : 0u;
+    };
+    auto store = [&](int64_t t0) {
+      const uint32_t vo = static_cast<uint32_t>(t0 * DK + c) * 4;
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dsave[u]), rd, vo + u * DK * 4, 0, 0);
+      if (wv == 0 && lane < U && t0 + lane < T) *reinterpret_cast<float2*>(wxn + 2 * (t0 + lane)) = float2{xs, ns};
+    };
+    load(0, kAc, bc, rc);
+    for (int64_t blk = 0; blk < nblk; ++blk) {
+      const int64_t t0 = blk * U;
+      const int par = static_cast<int>(blk & 1);
+      if (blk > 0) store(t0 - U);
+      __builtin_amdgcn_sched_barrier(0);          // the stores stay ahead of the prefetch
+      load(t0 + U, kAn, bn, rn);
+      tile_put(0, kAc);
+      // Gram matrix of this wave's channels, the last column against ones (the norms)
+      {
+        float wa[16];
+        unpack16(reinterpret_cast<const uint4(&)[2]>(kAc), wa);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+          wa[m] *= wa[m];
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(wa[m], ta == 15 ? 1.f : wa[m], acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sM[par][0][wv][4 * ga + r][ta] = acc[r];   // row 4 ga + r, column ta
+      }
+      float wc[U];
+      {
+        float pb[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const float kk = tile_get(0, u);
+          wc[u] = kk * kk;
+          pb[u] = d * wc[u];
+        }
+        const float sb = lanes_sum16(pb);
+        if ((lane & 3) == 0) sV[par][0][wv][lane >> 2] = sb;
+      }
+      __syncthreads();
+      // lane j: row j of the Gram matrix (column 15: n_j) and <d_0, w_j>
+      float grow[U], bsum = 0.f;
+#pragma unroll
+      for (int i = 0; i < U; ++i) grow[i] = 0.f;
+#pragma unroll
+      for (int w2 = 0; w2 < NW; ++w2) {
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const float4 g4 = *reinterpret_cast<const float4*>(&sM[par][0][w2][j][4 * i4]);
+          grow[4 * i4] += g4.x;
+          grow[4 * i4 + 1] += g4.y;
+          grow[4 * i4 + 2] += g4.z;
+          grow[4 * i4 + 3] += g4.w;
+        }
+        bsum += sV[par][0][w2][j];
+      }
+      const float nj = grow[15];
+      const bool lvalid = t0 + j < T && nj > 0.f;
+      const float bt = __uint_as_float(bc << 16);
+      const float gam = lvalid ? eta * bt / nj : 0.f, alf = gam * bt;
+      float rr[U];
+      if (HAS_R) {
+        if (lane < U) sR[wv][0][lane] = t0 + lane < T ? __uint_as_float(rc << 16) : 1.f;
+        bcast16(0, rr);
+      }
+      // rat(j, i) for i < j, built from i = j - 1 downwards; afterwards pr = P_j
+      float mrow[U], pr = 1.f;
+#pragma unroll
+      for (int i = U - 1; i >= 0; --i) {
+        mrow[i] = i < j ? pr * grow[i] : 0.f;
+        if (HAS_R) pr = i < j ? pr * rr[i] : 1.f;
+      }
+      float x = pr * bsum;
+#pragma unroll
+      for (int i = 0; i < U; ++i)             // lane i's x is complete at step i
+        x = fmaf(mrow[i], lane_bcast(__float_as_uint(fmaf(-alf, x, gam)), i), x);
+      xs = x;
+      ns = nj;
+      float ee[U];
+      if (lane < U) sR[wv][1][lane] = fmaf(-alf, x, gam);
+      bcast16(1, ee);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        dsave[u] = d;
+        d = fmaf(ee[u], wc[u], HAS_R ? rr[u] * d : d);
+      }
+      kAc[0] = kAn[0];
+      kAc[1] = kAn[1];
+      bc = bn;
+      rc = rn;
+    }
+    store((nblk - 1) * U);
+  }
+  __threadfence_block();   // the reverse reads what this workgroup wrote
+  __syncthreads();
+
+  // ---- reverse ------------------------------------------------------------------------
+  float D = q.dd_T ? q.dd_T[bh * DK + c] : 0.f;
+  {
+    const void* gsrc = q.dkw ? q.dkw : p.k;          // no dkw: an empty range, which reads zero
+    u32x4 kAc[2], gAc[2], kAn[2], gAn[2];
+    uint32_t bc, rc, bn = 0, rn = 0;
+    float dcc[U], dcn[U];
+    float2 xnc, xnn = float2{0.f, 0.f};
+    float dbs = 0.f;
+    const rsrc_t rk = rs_key(p.k), rg = q.dkw ? rs_key(gsrc) : make_rsrc(gsrc, 0u), ro = rs_key(q.dk);
+    const rsrc_t rd = make_rsrc(wd, static_cast<uint32_t>(T * DK * 4));
+    auto load = [&](int64_t t0, u32x4 (&kA)[2], u32x4 (&gA)[2], float (&dc)[U], uint32_t& bx, uint32_t& rx,
+                    float2& xn) {
+      const uint32_t vo = voffA + static_cast<uint32_t>(t0) * tokb;
+      kA[0] = buf_load16(rk, vo, 0);
+      kA[1] = buf_load16(rk, vo + 16, 0);
+      gA[0] = buf_load16(rg, vo, 0);
+      gA[1] = buf_load16(rg, vo + 16, 0);
+      const uint32_t vd = static_cast<uint32_t>(t0 * DK + c) * 4;
+#pragma unroll
+      for (int u = 0; u < U; ++u) dc[u] = __uint_as_float(buf_load4(rd, vd + u * DK * 4, 0));
+      const int64_t tl = clampt(t0 + j);
+      bx = bp[row_of(tl)];
+      rx = HAS_R ? rp[row_of(tl)] : 0u;
+      xn = *reinterpret_cast<const float2*>(wxn + 2 * tl);
+    };
+    // the dk of block t0 (in the wave's dk tile) and its dbeta (wave 0, lanes 0-15)
+    auto store = [&](int64_t t0) {
+      const uint32_t vo = voffA + static_cast<uint32_t>(t0) * tokb;
+      buf_store16(*reinterpret_cast<const u32x4_alias*>(&sT[2][wv][ta][16 * ga]), ro, vo, 0);
+      buf_store16(*reinterpret_cast<const u32x4_alias*>(&sT[2][wv][ta][16 * ga + 8]), ro, vo + 16, 0);
+      if (wv == 0 && lane < U && t0 + lane < T)
+        static_cast<uint16_t*>(q.dbeta)[row_of(t0 + lane)] = f32_to_bf16_bits(dbs);
+    };
+    // dr of block t0 from the sums in slot par (after a barrier)
+    auto store_dr = [&](int64_t t0, int par) {
+      if (HAS_R && q.dr && wv == 0 && lane < U && t0 + lane < T) {
+        float sum = 0.f;
+#pragma unroll
+        for (int w2 = 0; w2 < NW; ++w2) sum += sV[par][1][w2][lane];
+        static_cast<uint16_t*>(q.dr)[row_of(t0 + lane)] = f32_to_bf16_bits(sum);
+      }
+    };
+    load((nblk - 1) * U, kAc, gAc, dcc, bc, rc, xnc);
+    for (int64_t blk = nblk - 1; blk >= 0; --blk) {
+      const int64_t t0 = blk * U;
+      const int par = static_cast<int>(blk & 1);
+      if (blk < nblk - 1) store(t0 + U);
+      __builtin_amdgcn_sched_barrier(0);          // the stores stay ahead of the prefetch
+      load(t0 - U, kAn, gAn, dcn, bn, rn, xnn);
+      tile_put(0, kAc);
+      tile_put(1, gAc);
+      // <w_i, w_j> and <f_i, w_j> over this wave's channels (zero keys past the end)
+      {
+        float wa[16], fa[16];
+        unpack16(reinterpret_cast<const uint4(&)[2]>(kAc), wa);
+        unpack16(reinterpret_cast<const uint4(&)[2]>(gAc), fa);
+        f32x4 ag = {0.f, 0.f, 0.f, 0.f}, af = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+          fa[m] *= wa[m];
+          wa[m] *= wa[m];
+          ag = __builtin_amdgcn_mfma_f32_16x16x4f32(wa[m], wa[m], ag, 0, 0, 0);
+          af = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[m], wa[m], af, 0, 0, 0);
+        }
+        // row ta of each transposed: [ta][4 ga + r] = D[4 ga + r][ta]
+        *reinterpret_cast<float4*>(&sM[par][0][wv][ta][4 * ga]) = float4{ag[0], ag[1], ag[2], ag[3]};
+        *reinterpret_cast<float4*>(&sM[par][1][wv][ta][4 * ga]) = float4{af[0], af[1], af[2], af[3]};
+      }
+      float kc[U], wc[U];
+      {
+        float pc[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          kc[u] = tile_get(0, u);
+          wc[u] = kc[u] * kc[u];
+          pc[u] = D * wc[u];
+        }
+        const float sc = lanes_sum16(pc);
+        if ((lane & 3) == 0) sV[par][0][wv][lane >> 2] = sc;
+      }
+      __syncthreads();
+      if (blk < nblk - 1) store_dr(t0 + U, par ^ 1);
+      // lane j: <w_i, w_j>, <f_i, w_j> over i and <D_U, w_j>
+      float grow[U], frow[U], csum = 0.f;
+#pragma unroll
+      for (int i = 0; i < U; ++i) grow[i] = frow[i] = 0.f;
+#pragma unroll
+      for (int w2 = 0; w2 < NW; ++w2) {
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const float4 g4 = *reinterpret_cast<const float4*>(&sM[par][0][w2][j][4 * i4]);
+          const float4 f4 = *reinterpret_cast<const float4*>(&sM[par][1][w2][j][4 * i4]);
+          grow[4 * i4] += g4.x;
+          grow[4 * i4 + 1] += g4.y;
+          grow[4 * i4 + 2] += g4.z;
+          grow[4 * i4 + 3] += g4.w;
+          frow[4 * i4] += f4.x;
+          frow[4 * i4 + 1] += f4.y;
+          frow[4 * i4 + 2] += f4.z;
+          frow[4 * i4 + 3] += f4.w;
+        }
+        csum += sV[par][0][w2][j];
+      }
+      // token j's coefficients (zero past the end and for a zero key)
+      const float xj = xnc.x, nj = xnc.y;
+      const bool lvalid = t0 + j < T && nj > 0.f;
+      const float bt = __uint_as_float(bc << 16), inv_n = lvalid ? 1.f / nj : 0.f;
+      const float el = eta * bt * (1.f - bt * xj) * inv_n, rhol = eta * bt * bt * inv_n;
+      const float enl = el * inv_n, dbl = eta * (1.f - 2.f * bt * xj) * inv_n;
+      const float rl = HAS_R && t0 + j < T ? __uint_as_float(rc << 16) : 1.f;
+      float rr[U], rho[U];
+      if (lane < U) {
+        sR[wv][0][lane] = rl;
+        sR[wv][1][lane] = rhol;
+      }
+      if (HAS_R) bcast16(0, rr);
+      bcast16(1, rho);
+      // Q(j, i) for i > j, built from i = j + 1 upwards; afterwards qa = Q(j, U)
+      float mrow[U], qa = 1.f, a = 0.f;
+#pragma unroll
+      for (int i = 0; i < U; ++i) {
+        const float qv = i > j ? qa : 0.f;
+        a = fmaf(qv, frow[i], a);
+        mrow[i] = qv * rho[i] * grow[i];
+        if (HAS_R) qa = i > j ? qa * rr[i] : 1.f;
+      }
+      float u = fmaf(qa, csum, a);
+#pragma unroll
+      for (int i = U - 1; i >= 0; --i)        // lane i's u is complete at step i
+        u = fmaf(-mrow[i], lane_bcast(__float_as_uint(u), i), u);
+      dbs = u * dbl;
+      if (lane < U) *reinterpret_cast<float4*>(&sC[wv][lane][0]) = float4{el, u * rhol, u * enl, rl};
+      float pd[U];
+#pragma unroll
+      for (int uu = U - 1; uu >= 0; --uu) {
+        const float4 cf = *reinterpret_cast<const float4*>(&sC[wv][uu][0]);   // e, u rho, u e / n, r
+        const float gg = tile_get(1, uu), dd = dcc[uu];
+        pd[uu] = D * dd;
+        const float tt = fmaf(-cf.y, dd, fmaf(cf.x, D, -cf.z));
+        sT[2][wv][uu][lane] = f32_to_bf16_bits(fmaf(2.f * kc[uu], tt, gg * dd));
+        D = fmaf(-cf.y, wc[uu], fmaf(cf.w, D, gg * kc[uu]));
+      }
+      if (HAS_R) {
+        const float sd = lanes_sum16(pd);
+        if ((lane & 3) == 0) sV[par][1][wv][lane >> 2] = sd;
+      }
+      kAc[0] = kAn[0];
+      kAc[1] = kAn[1];
+      gAc[0] = gAn[0];
+      gAc[1] = gAn[1];
+#pragma unroll
+      for (int uu = 0; uu < U; ++uu) dcc[uu] = dcn[uu];
+      bc = bn;
+      rc = rn;
+      xnc = xnn;
+    }
+    store(0);
+    __syncthreads();
+    store_dr(0, 0);
+  }
+  if (q.dd0) q.dd0[bh * DK + c] = D;
+}
+
 template <int IO, int DK, bool HAS_R>
 static hipError_t launch_bwd_t(const PrecondBwdParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((precond_scan_bwd_kernel<IO, DK, HAS_R>), dim3(static_cast<unsigned>(p.f.B * p.f.H)), dim3(64), 0,
@@ -844,9 +1247,21 @@ static hipError_t launch_bwd_t(const PrecondBwdParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int DK, bool HAS_R>
+static hipError_t launch_bwd_blk_t(const PrecondBwdParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL((precond_scan_bwd_blk_kernel<DK, HAS_R>), dim3(static_cast<unsigned>(p.f.B * p.f.H)), dim3(DK),
+                     0, stream, p);
+  return hipGetLastError();
+}
+
 template <int IO>
 static hipError_t launch_bwd_io(const PrecondBwdParams& p, hipStream_t stream) {
   const bool hr = p.f.r != nullptr;
+  if constexpr (IO == IO_BF16) {
+    if (p.f.d_k == 128) return hr ? launch_bwd_blk_t<128, true>(p, stream) : launch_bwd_blk_t<128, false>(p, stream);
+    if (p.f.d_k == 64) return hr ? launch_bwd_blk_t<64, true>(p, stream) : launch_bwd_blk_t<64, false>(p, stream);
+    return hipErrorInvalidValue;
+  }
   if (p.f.d_k == 128) return hr ? launch_bwd_t<IO, 128, true>(p, stream) : launch_bwd_t<IO, 128, false>(p, stream);
   if (p.f.d_k == 64) return hr ? launch_bwd_t<IO, 64, true>(p, stream) : launch_bwd_t<IO, 64, false>(p, stream);
   return hipErrorInvalidValue;

@@ -78,7 +78,7 @@ def test_scan_bwd(io, dk, forget, shape):
     _compare(_gpu(x, io), _ref(x), io)
 
 
-@pytest.mark.parametrize("T", [0, 1, 15, 16, 17, 64])
+@pytest.mark.parametrize("T", [0, 1, 15, 16, 17, 33, 64, 200])
 def test_scan_bwd_lengths(T):
     need_gpu()
     say(f"case scan backward T={T}")
@@ -90,26 +90,32 @@ def test_scan_bwd_lengths(T):
     _compare(got, _ref(x), "bf16")
 
 
-def test_scan_bwd_optional_inputs():
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_scan_bwd_optional_inputs(io):
     """No d0 (ones), no dkw (zero), no dd_T (zero), each in turn."""
     need_gpu()
-    x = _inputs(2, 100, 2, 128, "f32", seed=51)
+    x = _inputs(2, 100, 2, 128, io, seed=51)
     for opt in ({"with_d0": False}, {"with_dkw": False}, {"with_ddT": False}):
-        say(f"case scan backward {opt}")
-        _compare(_gpu(x, "f32", **opt), _ref(x, **opt), "f32")
+        say(f"case scan backward io={io} {opt}")
+        _compare(_gpu(x, io, **opt), _ref(x, **opt), io)
 
 
-def test_scan_bwd_edge_values():
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_scan_bwd_edge_values(io):
     """Zero keys (d passes unchanged), eta in {0.25, 8}, a retention of 1e-3 over a
-    run of tokens."""
+    run of tokens, a retention of exactly 0 (d restarts from e_t w_t) inside a
+    block of 16 tokens and on a block's first token."""
     need_gpu()
-    x = _inputs(2, 120, 2, 128, "f32", seed=53)
+    x = _inputs(2, 120, 2, 128, io, seed=53)
     x["k"][0, 10:13, 1] = 0.0
     x["k"][1, 0, 0] = 0.0
     x["r"][:, 60:80] = 1e-3
+    x["r"][0, 37, 0] = 0.0
+    x["r"][1, 96, 1] = 0.0
+    x["r"] = round_to_io(x["r"], io)
     for eta in (0.25, 8.0):
-        say(f"case scan backward edge values eta={eta}")
-        _compare(_gpu(x, "f32", eta=eta), _ref(x, eta=eta), "f32")
+        say(f"case scan backward edge values io={io} eta={eta}")
+        _compare(_gpu(x, io, eta=eta), _ref(x, eta=eta), io)
 
 
 def test_scan_bwd_deterministic():
