@@ -839,11 +839,8 @@ __global__ __launch_bounds__(64) void precond_scan_bwd_kernel(PrecondBwdParams q
 
 // ---------------------------------------------------------------------------------
 // bf16 I/O: the same reverse mode in blocks of U = 16 tokens, so that no sum over
-// the channels lies on the token-to-token chain.  NW = d_k / 64 waves per
-// (sequence, head); wave w owns channels 64 w .. 64 w + 63 (lane c: channel 64 w + c)
-// for the elementwise work, and the block's key products run on fp32 MFMA
-// (16x16x4, exact fp32 products).  Within a block starting from d_0, with the
-// retention products rat(j, i) = r_{i+1} ... r_{j-1} and P_j = r_0 ... r_{j-1}:
+// the channels lies on the token-to-token chain.  Within a block starting from d_0,
+// with the retention products rat(j, i) = r_{i+1} ... r_{j-1} and P_j = r_0 ... r_{j-1}:
 //
 //   forward:  x_j = P_j <d_0, w_j> + sum_{i<j} rat(j, i) e_i <w_j, w_i>,
 //             e_j = gam_j - alf_j x_j       (one scalar per token, lane j, in order),
@@ -856,9 +853,21 @@ __global__ __launch_bounds__(64) void precond_scan_bwd_kernel(PrecondBwdParams q
 //
 // The Gram matrix <w_i, w_j> (and its column of ones, the key norms n_i), the
 // cross products <f_i, w_j>, and the sums <d_0, w_j>, <D_U, w_j>, <D_{j+1}, d_j>
-// are the only sums over channels: MFMA for the first two, a halving exchange
-// across lanes for the others, each wave's part added through LDS (one barrier per
-// block).  Every wave runs the scalar chain of the block itself.
+// are the only sums over channels.
+//
+// One workgroup of 2 NW waves (NW = d_k / 64) per (sequence, head), in two roles,
+// each wave owning the 64 channels of one half (NW halves):
+//   * prep waves, two blocks ahead: load the block's keys (and dkw) sixteen
+//     channels per lane, stage them in LDS tiles, form the key products on fp32
+//     MFMA (16x16x4: exact fp32 products) and, one block ahead, the chain's
+//     coefficients (rat or Q times the products, P_j, Q(j, U), the per-token
+//     factors) from both halves' partial products;
+//   * elementwise waves (lane c: channel 64 half + c): the scalar chain of the
+//     block in hand (every such wave runs it), the per-channel sweep over its
+//     tokens, and the next block's sums against d_0 or D_U by a halving exchange
+//     across lanes, each half's part added through LDS.
+// One barrier per block; LDS slots alternate between neighbouring blocks (three
+// for the tiles, which are read two blocks after they are written).
 // ---------------------------------------------------------------------------------
 namespace {
 // Sums over the 64 lanes of the sixteen values v[0..15] held by each lane: lane l
@@ -908,336 +917,396 @@ __device__ __forceinline__ void unpack16(const uint4 (&x)[2], float (&o)[16]) {
 }  // namespace
 
 template <int DK, bool HAS_R>
-__global__ __launch_bounds__(DK) void precond_scan_bwd_blk_kernel(PrecondBwdParams q) {
+__global__ __launch_bounds__(2 * DK) void precond_scan_bwd_blk_kernel(PrecondBwdParams q) {
   constexpr int NW = DK / 64, U = 16, GS = 20, TR = 72;   // GS, TR: row strides of the LDS matrices and tiles
   const PrecondParams& p = q.f;
   const int64_t bh = blockIdx.x;
   const int64_t b = bh / p.H, h = bh - b * p.H;
   const int64_t T = p.T, H = p.H;
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int c = 64 * wv + lane;                       // elementwise role: channel c
-  const int ta = lane & 15, ga = lane >> 4;           // MFMA role: token ta, channels 64 wv + 16 ga .. + 15
+  const bool prep = wv >= NW;                         // the waves that work ahead
+  const int half = prep ? wv - NW : wv;               // channels 64 half .. 64 half + 63
+  const int c = 64 * half + lane;                     // elementwise role: channel c
+  const int ta = lane & 15, ga = lane >> 4;           // MFMA role: token ta, channels 64 half + 16 ga .. + 15
   const int j = lane & 15;                            // scalar role: token j (lanes 16-63 repeat 0-15)
   const uint32_t tokb = static_cast<uint32_t>(H * DK * 2);   // bytes from one token to the next: k, dkw, dk
+  const uint32_t scb = static_cast<uint32_t>(H * 2);         // ... beta, r, dbeta, dr
   const int64_t row0 = b * T * H + h;                        // element (token 0, head h) of [B, T, H] tensors
-  const uint32_t voffA = ta * tokb + (64 * wv + 16 * ga) * 2;
+  const uint32_t voffA = ta * tokb + (64 * half + 16 * ga) * 2;
   float* __restrict__ wd = q.ws + bh * T * DK;                     // d_t, [T][DK]
   float* __restrict__ wxn = q.ws + p.B * H * T * DK + bh * T * 2;  // (x_t, n_t), [T][2]
-  // Buffer resources over this sequence's tokens 0 .. T - 1: loads of tokens past
-  // the end or before the start (offsets wrap to 2^32 - x) read zero, stores there
-  // are dropped.  Offsets within a sequence stay below 2^31.
-  auto rs_key = [&](const void* base) {   // [B, T, H, d_k] bf16
-    return make_rsrc(static_cast<const uint16_t*>(base) + row0 * DK,
-                     T > 0 ? static_cast<uint32_t>((T - 1) * tokb + DK * 2) : 0u);
+  // Every access goes through a buffer resource that covers one block of 16 tokens
+  // (its tokens before T; none for a block outside 0 .. nblk - 1), at offsets that
+  // do not change from block to block: loads outside read zero, stores there are
+  // dropped, and no address register of a load in flight is ever rewritten (which
+  // would make the wave wait for it).
+  const int T32 = static_cast<int>(T);   // 32-bit block arithmetic stays on the scalar unit
+  auto ntok = [&](int blk) -> uint32_t {
+    const int n = T32 - blk * U;
+    return blk < 0 || n <= 0 ? 0u : (n > U ? uint32_t(U) : static_cast<uint32_t>(n));
   };
-  const uint16_t* __restrict__ bp = static_cast<const uint16_t*>(p.beta);
-  const uint16_t* __restrict__ rp = static_cast<const uint16_t*>(HAS_R ? p.r : p.beta);
-  auto row_of = [&](int64_t t) { return (b * T + t) * H + h; };
-  auto clampt = [&](int64_t t) { return t < 0 ? int64_t(0) : (t >= T ? T - 1 : t); };
-  __shared__ __attribute__((aligned(16))) uint16_t sT[3][NW][U][TR];   // per-wave tiles of 16 tokens: k, dkw, dk
-  __shared__ __attribute__((aligned(16))) float sM[2][2][NW][U][GS];   // [block parity][G, F][wave][row][col]
-  __shared__ float sV[2][2][NW][U];                                    // [parity][sum][wave][token]
-  __shared__ __attribute__((aligned(16))) float sC[NW][U][4];          // per-wave, per-token coefficients
-  __shared__ __attribute__((aligned(16))) float sR[NW][2][U];          // per-wave: r_j and a second vector
+  auto tok0 = [&](int blk) -> int64_t {   // first token of a block, clamped to 0 .. T
+    const int t = blk * U;
+    return t < 0 ? 0 : (t > T32 ? T32 : t);
+  };
+  // (base and size taken through the scalar unit: the compiler cannot tell that a
+  // 64-bit product formed on the vector unit is the same on every lane, and would
+  // otherwise loop over the lanes for each access)
+  auto rs_uni = [](const void* base, uint32_t bytes) {
+    const int64_t a = uni64(reinterpret_cast<int64_t>(base));
+    return make_rsrc(reinterpret_cast<const void*>(a), __builtin_amdgcn_readfirstlane(bytes));
+  };
+  auto rs_key = [&](const void* base, int blk) {   // [B, T, H, d_k] bf16
+    const uint32_t n = ntok(blk);
+    return rs_uni(static_cast<const uint16_t*>(base) + (row0 + tok0(blk) * H) * DK, n ? (n - 1) * tokb + DK * 2 : 0u);
+  };
+  auto rs_scal = [&](const void* base, int blk) {   // [B, T, H] bf16
+    const uint32_t n = ntok(blk);
+    return rs_uni(static_cast<const uint16_t*>(base) + row0 + tok0(blk) * H, n ? (n - 1) * scb + 2 : 0u);
+  };
+  auto rs_d = [&](int blk) { return rs_uni(wd + tok0(blk) * DK, ntok(blk) * DK * 4); };
+  auto rs_xn = [&](int blk) { return rs_uni(wxn + 2 * tok0(blk), ntok(blk) * 8); };
+  const uint32_t voffS = j * scb, voffX = j * 8, voffD = c * 4;
+  __shared__ __attribute__((aligned(16))) uint16_t sT[3][2][NW][U][TR];   // [step % 3][k, dkw][half][token][ch]
+  __shared__ __attribute__((aligned(16))) uint16_t sO[NW][U][TR];         // the block's dk (elementwise waves)
+  __shared__ __attribute__((aligned(16))) float sM[2][2][NW][U][GS];      // [step % 2][G, F][half]: partial products
+  __shared__ __attribute__((aligned(16))) float sQ[2][U][GS];             // [step % 2]: row j of the chain matrix
+  __shared__ __attribute__((aligned(16))) float sS[2][U][8];              // [step % 2]: token j's coefficients
+  __shared__ float sV[2][2][NW][U];                                       // [step % 2][<., w_j>, dr][half]: partials
+  __shared__ __attribute__((aligned(16))) float sC[NW][U][4];             // elementwise waves: per-token factors
+  __shared__ __attribute__((aligned(16))) float sP[2][U];                 // prep: per-token vectors, every lane
   const float eta = p.eta;
   if (T <= 0) {                                       // no tokens: dd0 = dd_T
-    if (q.dd0) q.dd0[bh * DK + c] = q.dd_T ? q.dd_T[bh * DK + c] : 0.f;
+    if (!prep && q.dd0) q.dd0[bh * DK + c] = q.dd_T ? q.dd_T[bh * DK + c] : 0.f;
     return;
   }
-  const int64_t nblk = (T + U - 1) / U;
-  // A wave's 16 tokens x 64 channels, loaded 16 channels per lane (MFMA layout), into
-  // its tile, from which each lane reads its channel of every token.
-  auto tile_put = [&](int t, const u32x4 (&x)[2]) {
-    *reinterpret_cast<u32x4_alias*>(&sT[t][wv][ta][16 * ga]) = x[0];
-    *reinterpret_cast<u32x4_alias*>(&sT[t][wv][ta][16 * ga + 8]) = x[1];
+  const int nblk = static_cast<int>((T + U - 1) / U);
+  auto tile_put = [&](int slot, int kind, const u32x4 (&x)[2]) {
+    *reinterpret_cast<u32x4_alias*>(&sT[slot][kind][half][ta][16 * ga]) = x[0];
+    *reinterpret_cast<u32x4_alias*>(&sT[slot][kind][half][ta][16 * ga + 8]) = x[1];
   };
-  auto tile_get = [&](int t, int u) { return __uint_as_float(static_cast<uint32_t>(sT[t][wv][u][lane]) << 16); };
-  // the sixteen values a wave's lanes 0-15 wrote to sR[wv][i], on every lane
-  auto bcast16 = [&](int i, float (&o)[U]) {
+  auto tile_get = [&](int slot, int kind, int u) {
+    return __uint_as_float(static_cast<uint32_t>(sT[slot][kind][half][u][lane]) << 16);
+  };
+  auto read16 = [&](const float* src, float (&o)[U]) {   // 16 floats at a 16-byte aligned LDS address
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
-      const float4 v = *reinterpret_cast<const float4*>(&sR[wv][i][4 * q4]);
+      const float4 v = *reinterpret_cast<const float4*>(src + 4 * q4);
       o[4 * q4] = v.x;
       o[4 * q4 + 1] = v.y;
       o[4 * q4 + 2] = v.z;
       o[4 * q4 + 3] = v.w;
     }
   };
+  auto write16 = [&](float* dst, const float (&v)[U]) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4)
+      *reinterpret_cast<float4*>(dst + 4 * q4) = float4{v[4 * q4], v[4 * q4 + 1], v[4 * q4 + 2], v[4 * q4 + 3]};
+  };
+  auto slot3 = [](int s) { return (s + 3) % 3; };   // s >= -2
+  auto slot2 = [](int s) { return s & 1; };
 
   // ---- forward: d_t, x_t and n_t of every token ------------------------------------
+  // Step s (s = -2 .. nblk - 1, one barrier each): the elementwise waves finish block
+  // s (the chain, every d_t) and form <d, w_j> of block s + 1; the prep waves form the
+  // Gram matrix of block s + 2 and the chain's coefficients of block s + 1.
   float d = p.d0 ? p.d0[bh * DK + c] : 1.f;
   {
     u32x4 kAc[2], kAn[2];
-    uint32_t bc, rc, bn = 0, rn = 0;
-    float dsave[U], xs = 0.f, ns = 0.f;
-    const rsrc_t rk = rs_key(p.k), rd = make_rsrc(wd, static_cast<uint32_t>(T * DK * 4));
-    auto load = [&](int64_t t0, u32x4 (&kA)[2], uint32_t& bx, uint32_t& rx) {
-      const uint32_t vo = voffA + static_cast<uint32_t>(t0) * tokb;
-      kA[0] = buf_load16(rk, vo, 0);
-      kA[1] = buf_load16(rk, vo + 16, 0);
-      const int64_t row = row_of(clampt(t0 + j));
-      bx = bp[row];
-      rx = HAS_R ? rp[row] : 0u;
+    uint32_t bc = 0, rc = 0, bn = 0, rn = 0;
+    float wc[U];
+    auto ldA = [&](int blk, u32x4 (&x)[2]) {
+      const rsrc_t rk = rs_key(p.k, blk);
+      x[0] = buf_load16(rk, voffA, 0);
+      x[1] = buf_load16(rk, voffA + 16, 0);
     };
-    auto store = [&](int64_t t0) {
-      const uint32_t vo = static_cast<uint32_t>(t0 * DK + c) * 4;
+    if (prep) {
+      ldA(0, kAc);
+      for (int s = -2; s < nblk; ++s) {
+        const int bm = s + 2, bq = s + 1;
+        ldA(bm + 1, kAn);
+        bn = buf_load2(rs_scal(p.beta, bm), voffS, 0);
+        rn = HAS_R ? buf_load2(rs_scal(p.r, bm), voffS, 0) : 0u;
+        if (bm < nblk) {   // Gram matrix of this half's channels, the last column against ones (the norms)
+          tile_put(slot3(bm), 0, kAc);
+          float wa[16];
+          unpack16(reinterpret_cast<const uint4(&)[2]>(kAc), wa);
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int u = 0; u < U; ++u)
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dsave[u]), rd, vo + u * DK * 4, 0, 0);
-      if (wv == 0 && lane < U && t0 + lane < T) *reinterpret_cast<float2*>(wxn + 2 * (t0 + lane)) = float2{xs, ns};
-    };
-    load(0, kAc, bc, rc);
-    for (int64_t blk = 0; blk < nblk; ++blk) {
-      const int64_t t0 = blk * U;
-      const int par = static_cast<int>(blk & 1);
-      if (blk > 0) store(t0 - U);
-      __builtin_amdgcn_sched_barrier(0);          // the stores stay ahead of the prefetch
-      load(t0 + U, kAn, bn, rn);
-      tile_put(0, kAc);
-      // Gram matrix of this wave's channels, the last column against ones (the norms)
-      {
-        float wa[16];
-        unpack16(reinterpret_cast<const uint4(&)[2]>(kAc), wa);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          for (int m = 0; m < 16; ++m) {
+            wa[m] *= wa[m];
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(wa[m], ta == 15 ? 1.f : wa[m], acc, 0, 0, 0);
+          }
 #pragma unroll
-        for (int m = 0; m < 16; ++m) {
-          wa[m] *= wa[m];
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(wa[m], ta == 15 ? 1.f : wa[m], acc, 0, 0, 0);
+          for (int r = 0; r < 4; ++r) sM[slot2(bm)][0][half][4 * ga + r][ta] = acc[r];   // row 4 ga + r, column ta
         }
+        if (bq >= 0 && bq < nblk && half == 0) {   // coefficients of block bq, lane j
+          const int64_t t0 = bq * U;
+          float grow[U];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sM[par][0][wv][4 * ga + r][ta] = acc[r];   // row 4 ga + r, column ta
-      }
-      float wc[U];
-      {
-        float pb[U];
+          for (int i = 0; i < U; ++i) grow[i] = 0.f;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const float kk = tile_get(0, u);
-          wc[u] = kk * kk;
-          pb[u] = d * wc[u];
+          for (int w2 = 0; w2 < NW; ++w2) {
+            float g[U];
+            read16(&sM[slot2(bq)][0][w2][j][0], g);
+#pragma unroll
+            for (int i = 0; i < U; ++i) grow[i] += g[i];
+          }
+          const float nj = grow[15];
+          const bool lvalid = t0 + j < T && nj > 0.f;
+          const float bt = __uint_as_float(bc << 16);
+          const float gam = lvalid ? eta * bt / nj : 0.f, alf = gam * bt;
+          const float rl = HAS_R && t0 + j < T ? __uint_as_float(rc << 16) : 1.f;
+          float rr[U];
+          if (HAS_R) {
+            if (lane < U) sP[0][lane] = rl;
+            read16(&sP[0][0], rr);
+          }
+          // rat(j, i) for i < j, built from i = j - 1 downwards; afterwards pr = P_j
+          float mrow[U], pr = 1.f;
+#pragma unroll
+          for (int i = U - 1; i >= 0; --i) {
+            mrow[i] = i < j ? pr * grow[i] : 0.f;
+            if (HAS_R) pr = i < j ? pr * rr[i] : 1.f;
+          }
+          if (lane < U) {
+            write16(&sQ[slot2(bq)][lane][0], mrow);
+            *reinterpret_cast<float4*>(&sS[slot2(bq)][lane][0]) = float4{pr, gam, alf, nj};
+            sS[slot2(bq)][lane][4] = rl;
+          }
         }
-        const float sb = lanes_sum16(pb);
-        if ((lane & 3) == 0) sV[par][0][wv][lane >> 2] = sb;
+        kAc[0] = kAn[0];
+        kAc[1] = kAn[1];
+        bc = bn;
+        rc = rn;
+        __syncthreads();
       }
-      __syncthreads();
-      // lane j: row j of the Gram matrix (column 15: n_j) and <d_0, w_j>
-      float grow[U], bsum = 0.f;
+    } else {
+      for (int s = -2; s < nblk; ++s) {
+        if (s >= 0) {   // block s: the chain, then d_t of its tokens
+          const int64_t t0 = s * U;
+          float bsum = 0.f, mrow[U];
 #pragma unroll
-      for (int i = 0; i < U; ++i) grow[i] = 0.f;
+          for (int w2 = 0; w2 < NW; ++w2) bsum += sV[slot2(s)][0][w2][j];
+          read16(&sQ[slot2(s)][j][0], mrow);
+          const float4 cf = *reinterpret_cast<const float4*>(&sS[slot2(s)][j][0]);   // P_j, gam, alf, n_j
+          const float rl = sS[slot2(s)][j][4];
+          float x = cf.x * bsum;
 #pragma unroll
-      for (int w2 = 0; w2 < NW; ++w2) {
+          for (int i = 0; i < U; ++i)             // lane i's x is complete at step i
+            x = fmaf(mrow[i], lane_bcast(__float_as_uint(fmaf(-cf.z, x, cf.y)), i), x);
+          if (half == 0 && lane < U)
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(x), __float_as_uint(cf.w)}, rs_xn(s), voffX, 0, 0);
+          if (lane < U) *reinterpret_cast<float2*>(&sC[half][lane][0]) = float2{fmaf(-cf.z, x, cf.y), rl};
+          float2 er[U];                         // every token's (e, r), read before the sequential update
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const float4 g4 = *reinterpret_cast<const float4*>(&sM[par][0][w2][j][4 * i4]);
-          grow[4 * i4] += g4.x;
-          grow[4 * i4 + 1] += g4.y;
-          grow[4 * i4 + 2] += g4.z;
-          grow[4 * i4 + 3] += g4.w;
+          for (int u = 0; u < U; ++u) er[u] = *reinterpret_cast<const float2*>(&sC[half][u][0]);
+          const rsrc_t rd = rs_d(s);
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(d), rd, voffD + u * DK * 4, 0, 0);
+            d = fmaf(er[u].x, wc[u], HAS_R ? er[u].y * d : d);
+          }
         }
-        bsum += sV[par][0][w2][j];
-      }
-      const float nj = grow[15];
-      const bool lvalid = t0 + j < T && nj > 0.f;
-      const float bt = __uint_as_float(bc << 16);
-      const float gam = lvalid ? eta * bt / nj : 0.f, alf = gam * bt;
-      float rr[U];
-      if (HAS_R) {
-        if (lane < U) sR[wv][0][lane] = t0 + lane < T ? __uint_as_float(rc << 16) : 1.f;
-        bcast16(0, rr);
-      }
-      // rat(j, i) for i < j, built from i = j - 1 downwards; afterwards pr = P_j
-      float mrow[U], pr = 1.f;
+        if (s >= -1 && s + 1 < nblk) {   // <d, w_j> of block s + 1 over this half's channels
+          float pb[U];
 #pragma unroll
-      for (int i = U - 1; i >= 0; --i) {
-        mrow[i] = i < j ? pr * grow[i] : 0.f;
-        if (HAS_R) pr = i < j ? pr * rr[i] : 1.f;
+          for (int u = 0; u < U; ++u) {
+            const float kk = tile_get(slot3(s + 1), 0, u);
+            wc[u] = kk * kk;
+            pb[u] = d * wc[u];
+          }
+          const float sb = lanes_sum16(pb);
+          if ((lane & 3) == 0) sV[slot2(s + 1)][0][half][lane >> 2] = sb;
+        }
+        __syncthreads();
       }
-      float x = pr * bsum;
-#pragma unroll
-      for (int i = 0; i < U; ++i)             // lane i's x is complete at step i
-        x = fmaf(mrow[i], lane_bcast(__float_as_uint(fmaf(-alf, x, gam)), i), x);
-      xs = x;
-      ns = nj;
-      float ee[U];
-      if (lane < U) sR[wv][1][lane] = fmaf(-alf, x, gam);
-      bcast16(1, ee);
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        dsave[u] = d;
-        d = fmaf(ee[u], wc[u], HAS_R ? rr[u] * d : d);
-      }
-      kAc[0] = kAn[0];
-      kAc[1] = kAn[1];
-      bc = bn;
-      rc = rn;
     }
-    store((nblk - 1) * U);
   }
   __threadfence_block();   // the reverse reads what this workgroup wrote
   __syncthreads();
 
   // ---- reverse ------------------------------------------------------------------------
+  // Step s handles block B(s) = nblk - 1 - s: the elementwise waves finish block B(s)
+  // (u, then dk, D, the dr partials) and form <D, w_j> of block B(s + 1); the prep
+  // waves form <w_i, w_j>, <f_i, w_j> of block B(s + 2) and the chain's coefficients
+  // of block B(s + 1).
   float D = q.dd_T ? q.dd_T[bh * DK + c] : 0.f;
   {
+    auto B_ = [&](int s) { return nblk - 1 - s; };
     const void* gsrc = q.dkw ? q.dkw : p.k;          // no dkw: an empty range, which reads zero
     u32x4 kAc[2], gAc[2], kAn[2], gAn[2];
-    uint32_t bc, rc, bn = 0, rn = 0;
-    float dcc[U], dcn[U];
-    float2 xnc, xnn = float2{0.f, 0.f};
-    float dbs = 0.f;
-    const rsrc_t rk = rs_key(p.k), rg = q.dkw ? rs_key(gsrc) : make_rsrc(gsrc, 0u), ro = rs_key(q.dk);
-    const rsrc_t rd = make_rsrc(wd, static_cast<uint32_t>(T * DK * 4));
-    auto load = [&](int64_t t0, u32x4 (&kA)[2], u32x4 (&gA)[2], float (&dc)[U], uint32_t& bx, uint32_t& rx,
-                    float2& xn) {
-      const uint32_t vo = voffA + static_cast<uint32_t>(t0) * tokb;
-      kA[0] = buf_load16(rk, vo, 0);
-      kA[1] = buf_load16(rk, vo + 16, 0);
-      gA[0] = buf_load16(rg, vo, 0);
-      gA[1] = buf_load16(rg, vo + 16, 0);
-      const uint32_t vd = static_cast<uint32_t>(t0 * DK + c) * 4;
+    uint32_t bc = 0, rc = 0, bn = 0, rn = 0;
+    float2 xnc = float2{0.f, 0.f}, xnn = float2{0.f, 0.f};
+    float kc[U], wc[U], dcc[U], dcn[U];
+    auto ldA = [&](int blk, u32x4 (&kx)[2], u32x4 (&gx)[2]) {
+      const rsrc_t rk = rs_key(p.k, blk), rg = q.dkw ? rs_key(gsrc, blk) : rs_uni(gsrc, 0u);
+      kx[0] = buf_load16(rk, voffA, 0);
+      kx[1] = buf_load16(rk, voffA + 16, 0);
+      gx[0] = buf_load16(rg, voffA, 0);
+      gx[1] = buf_load16(rg, voffA + 16, 0);
+    };
+    auto ldD = [&](int blk, float (&dc)[U]) {
+      const rsrc_t rd = rs_d(blk);
 #pragma unroll
-      for (int u = 0; u < U; ++u) dc[u] = __uint_as_float(buf_load4(rd, vd + u * DK * 4, 0));
-      const int64_t tl = clampt(t0 + j);
-      bx = bp[row_of(tl)];
-      rx = HAS_R ? rp[row_of(tl)] : 0u;
-      xn = *reinterpret_cast<const float2*>(wxn + 2 * tl);
+      for (int u = 0; u < U; ++u) dc[u] = __uint_as_float(buf_load4(rd, voffD + u * DK * 4, 0));
     };
-    // the dk of block t0 (in the wave's dk tile) and its dbeta (wave 0, lanes 0-15)
-    auto store = [&](int64_t t0) {
-      const uint32_t vo = voffA + static_cast<uint32_t>(t0) * tokb;
-      buf_store16(*reinterpret_cast<const u32x4_alias*>(&sT[2][wv][ta][16 * ga]), ro, vo, 0);
-      buf_store16(*reinterpret_cast<const u32x4_alias*>(&sT[2][wv][ta][16 * ga + 8]), ro, vo + 16, 0);
-      if (wv == 0 && lane < U && t0 + lane < T)
-        static_cast<uint16_t*>(q.dbeta)[row_of(t0 + lane)] = f32_to_bf16_bits(dbs);
-    };
-    // dr of block t0 from the sums in slot par (after a barrier)
-    auto store_dr = [&](int64_t t0, int par) {
-      if (HAS_R && q.dr && wv == 0 && lane < U && t0 + lane < T) {
+    auto store_dr = [&](int blk, int slot) {   // dr of block blk from the partials in a slot
+      if (HAS_R && q.dr && half == 0 && lane < U) {
         float sum = 0.f;
 #pragma unroll
-        for (int w2 = 0; w2 < NW; ++w2) sum += sV[par][1][w2][lane];
-        static_cast<uint16_t*>(q.dr)[row_of(t0 + lane)] = f32_to_bf16_bits(sum);
+        for (int w2 = 0; w2 < NW; ++w2) sum += sV[slot][1][w2][lane];
+        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(sum), rs_scal(q.dr, blk), voffS, 0, 0);
       }
     };
-    load((nblk - 1) * U, kAc, gAc, dcc, bc, rc, xnc);
-    for (int64_t blk = nblk - 1; blk >= 0; --blk) {
-      const int64_t t0 = blk * U;
-      const int par = static_cast<int>(blk & 1);
-      if (blk < nblk - 1) store(t0 + U);
-      __builtin_amdgcn_sched_barrier(0);          // the stores stay ahead of the prefetch
-      load(t0 - U, kAn, gAn, dcn, bn, rn, xnn);
-      tile_put(0, kAc);
-      tile_put(1, gAc);
-      // <w_i, w_j> and <f_i, w_j> over this wave's channels (zero keys past the end)
-      {
-        float wa[16], fa[16];
-        unpack16(reinterpret_cast<const uint4(&)[2]>(kAc), wa);
-        unpack16(reinterpret_cast<const uint4(&)[2]>(gAc), fa);
-        f32x4 ag = {0.f, 0.f, 0.f, 0.f}, af = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int m = 0; m < 16; ++m) {
-          fa[m] *= wa[m];
-          wa[m] *= wa[m];
-          ag = __builtin_amdgcn_mfma_f32_16x16x4f32(wa[m], wa[m], ag, 0, 0, 0);
-          af = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[m], wa[m], af, 0, 0, 0);
+    if (prep) {
+      ldA(B_(0), kAc, gAc);
+      for (int s = -2; s < nblk; ++s) {
+        const int bm = s + 2, bq = s + 1;
+        ldA(B_(bm + 1), kAn, gAn);
+        bn = buf_load2(rs_scal(p.beta, B_(bm)), voffS, 0);
+        rn = HAS_R ? buf_load2(rs_scal(p.r, B_(bm)), voffS, 0) : 0u;
+        {
+          const u32x2 xn = buf_load8(rs_xn(B_(bm)), voffX, 0);
+          xnn = float2{__uint_as_float(xn[0]), __uint_as_float(xn[1])};
         }
-        // row ta of each transposed: [ta][4 ga + r] = D[4 ga + r][ta]
-        *reinterpret_cast<float4*>(&sM[par][0][wv][ta][4 * ga]) = float4{ag[0], ag[1], ag[2], ag[3]};
-        *reinterpret_cast<float4*>(&sM[par][1][wv][ta][4 * ga]) = float4{af[0], af[1], af[2], af[3]};
-      }
-      float kc[U], wc[U];
-      {
-        float pc[U];
+        if (bm < nblk) {   // <w_i, w_j> and <f_i, w_j> of block B(bm) over this half's channels
+          tile_put(slot3(bm), 0, kAc);
+          tile_put(slot3(bm), 1, gAc);
+          float wa[16], fa[16];
+          unpack16(reinterpret_cast<const uint4(&)[2]>(kAc), wa);
+          unpack16(reinterpret_cast<const uint4(&)[2]>(gAc), fa);
+          f32x4 ag = {0.f, 0.f, 0.f, 0.f}, af = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          kc[u] = tile_get(0, u);
-          wc[u] = kc[u] * kc[u];
-          pc[u] = D * wc[u];
+          for (int m = 0; m < 16; ++m) {
+            fa[m] *= wa[m];
+            wa[m] *= wa[m];
+            ag = __builtin_amdgcn_mfma_f32_16x16x4f32(wa[m], wa[m], ag, 0, 0, 0);
+            af = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[m], wa[m], af, 0, 0, 0);
+          }
+          // row ta of each transposed: [ta][4 ga + r] = D[4 ga + r][ta]
+          *reinterpret_cast<float4*>(&sM[slot2(bm)][0][half][ta][4 * ga]) = float4{ag[0], ag[1], ag[2], ag[3]};
+          *reinterpret_cast<float4*>(&sM[slot2(bm)][1][half][ta][4 * ga]) = float4{af[0], af[1], af[2], af[3]};
         }
-        const float sc = lanes_sum16(pc);
-        if ((lane & 3) == 0) sV[par][0][wv][lane >> 2] = sc;
-      }
-      __syncthreads();
-      if (blk < nblk - 1) store_dr(t0 + U, par ^ 1);
-      // lane j: <w_i, w_j>, <f_i, w_j> over i and <D_U, w_j>
-      float grow[U], frow[U], csum = 0.f;
+        if (bq >= 0 && bq < nblk && half == 0) {   // coefficients of block B(bq), lane j
+          const int64_t t0 = B_(bq) * U;
+          float grow[U], frow[U];
 #pragma unroll
-      for (int i = 0; i < U; ++i) grow[i] = frow[i] = 0.f;
+          for (int i = 0; i < U; ++i) grow[i] = frow[i] = 0.f;
 #pragma unroll
-      for (int w2 = 0; w2 < NW; ++w2) {
+          for (int w2 = 0; w2 < NW; ++w2) {
+            float g[U], f[U];
+            read16(&sM[slot2(bq)][0][w2][j][0], g);
+            read16(&sM[slot2(bq)][1][w2][j][0], f);
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const float4 g4 = *reinterpret_cast<const float4*>(&sM[par][0][w2][j][4 * i4]);
-          const float4 f4 = *reinterpret_cast<const float4*>(&sM[par][1][w2][j][4 * i4]);
-          grow[4 * i4] += g4.x;
-          grow[4 * i4 + 1] += g4.y;
-          grow[4 * i4 + 2] += g4.z;
-          grow[4 * i4 + 3] += g4.w;
-          frow[4 * i4] += f4.x;
-          frow[4 * i4 + 1] += f4.y;
-          frow[4 * i4 + 2] += f4.z;
-          frow[4 * i4 + 3] += f4.w;
+            for (int i = 0; i < U; ++i) {
+              grow[i] += g[i];
+              frow[i] += f[i];
+            }
+          }
+          // token j's coefficients (zero past the end and for a zero key)
+          const float xj = xnc.x, nj = xnc.y;
+          const bool lvalid = t0 + j < T && nj > 0.f;
+          const float bt = __uint_as_float(bc << 16), inv_n = lvalid ? 1.f / nj : 0.f;
+          const float el = eta * bt * (1.f - bt * xj) * inv_n, rhol = eta * bt * bt * inv_n;
+          const float enl = el * inv_n, dbl = eta * (1.f - 2.f * bt * xj) * inv_n;
+          const float rl = HAS_R && t0 + j < T ? __uint_as_float(rc << 16) : 1.f;
+          float rr[U], rho[U];
+          if (lane < U) {
+            sP[0][lane] = rl;
+            sP[1][lane] = rhol;
+          }
+          if (HAS_R) read16(&sP[0][0], rr);
+          read16(&sP[1][0], rho);
+          // Q(j, i) for i > j, built from i = j + 1 upwards; afterwards qa = Q(j, U)
+          float mrow[U], qa = 1.f, a = 0.f;
+#pragma unroll
+          for (int i = 0; i < U; ++i) {
+            const float qv = i > j ? qa : 0.f;
+            a = fmaf(qv, frow[i], a);
+            mrow[i] = qv * rho[i] * grow[i];
+            if (HAS_R) qa = i > j ? qa * rr[i] : 1.f;
+          }
+          if (lane < U) {
+            write16(&sQ[slot2(bq)][lane][0], mrow);
+            *reinterpret_cast<float4*>(&sS[slot2(bq)][lane][0]) = float4{qa, a, el, rhol};
+            *reinterpret_cast<float4*>(&sS[slot2(bq)][lane][4]) = float4{enl, dbl, rl, 0.f};
+          }
         }
-        csum += sV[par][0][w2][j];
+        kAc[0] = kAn[0];
+        kAc[1] = kAn[1];
+        gAc[0] = gAn[0];
+        gAc[1] = gAn[1];
+        bc = bn;
+        rc = rn;
+        xnc = xnn;
+        __syncthreads();
       }
-      // token j's coefficients (zero past the end and for a zero key)
-      const float xj = xnc.x, nj = xnc.y;
-      const bool lvalid = t0 + j < T && nj > 0.f;
-      const float bt = __uint_as_float(bc << 16), inv_n = lvalid ? 1.f / nj : 0.f;
-      const float el = eta * bt * (1.f - bt * xj) * inv_n, rhol = eta * bt * bt * inv_n;
-      const float enl = el * inv_n, dbl = eta * (1.f - 2.f * bt * xj) * inv_n;
-      const float rl = HAS_R && t0 + j < T ? __uint_as_float(rc << 16) : 1.f;
-      float rr[U], rho[U];
-      if (lane < U) {
-        sR[wv][0][lane] = rl;
-        sR[wv][1][lane] = rhol;
-      }
-      if (HAS_R) bcast16(0, rr);
-      bcast16(1, rho);
-      // Q(j, i) for i > j, built from i = j + 1 upwards; afterwards qa = Q(j, U)
-      float mrow[U], qa = 1.f, a = 0.f;
+    } else {
+      for (int s = -2; s < nblk; ++s) {
+        if (s >= -1 && s + 1 < nblk) ldD(B_(s + 1), dcn);
+        if (s >= 0) {   // block B(s): u, then dk, D and the dr partials
+          const int64_t t0 = B_(s) * U;
+          if (s >= 1) store_dr(B_(s - 1), slot2(s - 1));
+          float csum = 0.f, mrow[U];
 #pragma unroll
-      for (int i = 0; i < U; ++i) {
-        const float qv = i > j ? qa : 0.f;
-        a = fmaf(qv, frow[i], a);
-        mrow[i] = qv * rho[i] * grow[i];
-        if (HAS_R) qa = i > j ? qa * rr[i] : 1.f;
-      }
-      float u = fmaf(qa, csum, a);
+          for (int w2 = 0; w2 < NW; ++w2) csum += sV[slot2(s)][0][w2][j];
+          read16(&sQ[slot2(s)][j][0], mrow);
+          const float4 c0 = *reinterpret_cast<const float4*>(&sS[slot2(s)][j][0]);   // Q(j, U), a, e, rho
+          const float4 c1 = *reinterpret_cast<const float4*>(&sS[slot2(s)][j][4]);   // e / n, dbeta factor, r
+          float u = fmaf(c0.x, csum, c0.y);
 #pragma unroll
-      for (int i = U - 1; i >= 0; --i)        // lane i's u is complete at step i
-        u = fmaf(-mrow[i], lane_bcast(__float_as_uint(u), i), u);
-      dbs = u * dbl;
-      if (lane < U) *reinterpret_cast<float4*>(&sC[wv][lane][0]) = float4{el, u * rhol, u * enl, rl};
-      float pd[U];
+          for (int i = U - 1; i >= 0; --i)      // lane i's u is complete at step i
+            u = fmaf(-mrow[i], lane_bcast(__float_as_uint(u), i), u);
+          if (half == 0 && lane < U)
+            __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(u * c1.y), rs_scal(q.dbeta, B_(s)), voffS, 0, 0);
+          if (lane < U) *reinterpret_cast<float4*>(&sC[half][lane][0]) = float4{c0.z, u * c0.w, u * c1.x, c1.z};
+          float pd[U], gg[U], dkv[U];
+          float4 cf[U];                         // every token's (e, u rho, u e / n, r) and dkw, read first
 #pragma unroll
-      for (int uu = U - 1; uu >= 0; --uu) {
-        const float4 cf = *reinterpret_cast<const float4*>(&sC[wv][uu][0]);   // e, u rho, u e / n, r
-        const float gg = tile_get(1, uu), dd = dcc[uu];
-        pd[uu] = D * dd;
-        const float tt = fmaf(-cf.y, dd, fmaf(cf.x, D, -cf.z));
-        sT[2][wv][uu][lane] = f32_to_bf16_bits(fmaf(2.f * kc[uu], tt, gg * dd));
-        D = fmaf(-cf.y, wc[uu], fmaf(cf.w, D, gg * kc[uu]));
-      }
-      if (HAS_R) {
-        const float sd = lanes_sum16(pd);
-        if ((lane & 3) == 0) sV[par][1][wv][lane >> 2] = sd;
-      }
-      kAc[0] = kAn[0];
-      kAc[1] = kAn[1];
-      gAc[0] = gAn[0];
-      gAc[1] = gAn[1];
+          for (int uu = 0; uu < U; ++uu) {
+            cf[uu] = *reinterpret_cast<const float4*>(&sC[half][uu][0]);
+            gg[uu] = tile_get(slot3(s), 1, uu);
+          }
 #pragma unroll
-      for (int uu = 0; uu < U; ++uu) dcc[uu] = dcn[uu];
-      bc = bn;
-      rc = rn;
-      xnc = xnn;
+          for (int uu = U - 1; uu >= 0; --uu) {
+            const float dd = dcc[uu];
+            pd[uu] = D * dd;
+            const float tt = fmaf(-cf[uu].y, dd, fmaf(cf[uu].x, D, -cf[uu].z));
+            dkv[uu] = fmaf(2.f * kc[uu], tt, gg[uu] * dd);
+            D = fmaf(-cf[uu].y, wc[uu], fmaf(cf[uu].w, D, gg[uu] * kc[uu]));
+          }
+#pragma unroll
+          for (int uu = 0; uu < U; ++uu) sO[half][uu][lane] = f32_to_bf16_bits(dkv[uu]);
+          {
+            const rsrc_t ro = rs_key(q.dk, B_(s));
+            buf_store16(*reinterpret_cast<const u32x4_alias*>(&sO[half][ta][16 * ga]), ro, voffA, 0);
+            buf_store16(*reinterpret_cast<const u32x4_alias*>(&sO[half][ta][16 * ga + 8]), ro, voffA + 16, 0);
+          }
+          if (HAS_R) {
+            const float sd = lanes_sum16(pd);
+            if ((lane & 3) == 0) sV[slot2(s)][1][half][lane >> 2] = sd;
+          }
+        }
+        if (s >= -1 && s + 1 < nblk) {   // <D, w_j> of block B(s + 1) over this half's channels
+          float pc[U];
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            kc[u] = tile_get(slot3(s + 1), 0, u);
+            wc[u] = kc[u] * kc[u];
+            pc[u] = D * wc[u];
+          }
+          const float sc = lanes_sum16(pc);
+          if ((lane & 3) == 0) sV[slot2(s + 1)][0][half][lane >> 2] = sc;
+#pragma unroll
+          for (int u = 0; u < U; ++u) dcc[u] = dcn[u];
+        }
+        __syncthreads();
+      }
     }
-    store(0);
-    __syncthreads();
-    store_dr(0, 0);
+    if (!prep) store_dr(B_(nblk - 1), slot2(nblk - 1));
   }
-  if (q.dd0) q.dd0[bh * DK + c] = D;
+  if (!prep && q.dd0) q.dd0[bh * DK + c] = D;
 }
 
 template <int IO, int DK, bool HAS_R>
@@ -1249,8 +1318,8 @@ static hipError_t launch_bwd_t(const PrecondBwdParams& p, hipStream_t stream) {
 
 template <int DK, bool HAS_R>
 static hipError_t launch_bwd_blk_t(const PrecondBwdParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((precond_scan_bwd_blk_kernel<DK, HAS_R>), dim3(static_cast<unsigned>(p.f.B * p.f.H)), dim3(DK),
-                     0, stream, p);
+  hipLaunchKernelGGL((precond_scan_bwd_blk_kernel<DK, HAS_R>), dim3(static_cast<unsigned>(p.f.B * p.f.H)),
+                     dim3(2 * DK), 0, stream, p);
   return hipGetLastError();
 }
 
