@@ -967,8 +967,10 @@ __global__ __launch_bounds__(2 * DK) void precond_scan_bwd_blk_kernel(PrecondBwd
   auto rs_d = [&](int blk) { return rs_uni(wd + tok0(blk) * DK, ntok(blk) * DK * 4); };
   auto rs_xn = [&](int blk) { return rs_uni(wxn + 2 * tok0(blk), ntok(blk) * 8); };
   const uint32_t voffS = j * scb, voffX = j * 8, voffD = c * 4;
+  uint32_t voffK[U];                        // channel c of each token of a block: k, dk
+#pragma unroll
+  for (int u = 0; u < U; ++u) voffK[u] = u * tokb + c * 2;
   __shared__ __attribute__((aligned(16))) uint16_t sT[3][2][NW][U][TR];   // [step % 3][k, dkw][half][token][ch]
-  __shared__ __attribute__((aligned(16))) uint16_t sO[NW][U][TR];         // the block's dk (elementwise waves)
   __shared__ __attribute__((aligned(16))) float sM[2][2][NW][U][GS];      // [step % 2][G, F][half]: partial products
   __shared__ __attribute__((aligned(16))) float sQ[2][U][GS];             // [step % 2]: row j of the chain matrix
   __shared__ __attribute__((aligned(16))) float sS[2][U][8];              // [step % 2]: token j's coefficients
@@ -1276,12 +1278,11 @@ __global__ __launch_bounds__(2 * DK) void precond_scan_bwd_blk_kernel(PrecondBwd
             dkv[uu] = fmaf(2.f * kc[uu], tt, gg[uu] * dd);
             D = fmaf(-cf[uu].y, wc[uu], fmaf(cf[uu].w, D, gg[uu] * kc[uu]));
           }
-#pragma unroll
-          for (int uu = 0; uu < U; ++uu) sO[half][uu][lane] = f32_to_bf16_bits(dkv[uu]);
           {
             const rsrc_t ro = rs_key(q.dk, B_(s));
-            buf_store16(*reinterpret_cast<const u32x4_alias*>(&sO[half][ta][16 * ga]), ro, voffA, 0);
-            buf_store16(*reinterpret_cast<const u32x4_alias*>(&sO[half][ta][16 * ga + 8]), ro, voffA + 16, 0);
+#pragma unroll
+            for (int uu = 0; uu < U; ++uu)
+              __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(dkv[uu]), ro, voffK[uu], 0, 0);
           }
           if (HAS_R) {
             const float sd = lanes_sum16(pd);
