@@ -356,8 +356,10 @@ gdr_status gdr_precond_scan_bwd_workspace_size(const gdr_desc* desc, size_t* byt
  *   workspace / workspace_bytes  at least gdr_precond_scan_bwd_workspace_size bytes,
  *          16-byte aligned, overwritten
  *
- * One wave per (sequence, head) runs the scan forward in fp32, keeping each token's
- * preconditioner in the workspace, then walks the tokens back in fp32 (both dtypes).
+ * Each (sequence, head) runs the scan forward in fp32, keeping each token's
+ * preconditioner in the workspace, then walks the tokens back in fp32: bf16 I/O in
+ * blocks of 16 tokens (the key products on fp32 MFMA, one scalar chain per block),
+ * fp32 I/O token by token.
  * T == 0 writes dd0 = dd_T (or zeros).  Errors as for gdr_precond_scan, plus
  * GDR_ERR_WORKSPACE for a missing or short workspace and the alias checks of the
  * outputs against every other buffer.
