@@ -301,6 +301,15 @@ def precond_bytes(B: int, T: int, H: int, d_k: int, esz: int, apf: bool) -> int:
     return ntok * (2 * d_k * esz + esz * (2 if apf else 1)) + 2 * B * H * d_k * 4
 
 
+def precond_bwd_bytes(B: int, T: int, H: int, d_k: int, esz: int, apf: bool) -> int:
+    """Bytes of one scan backward if every input were read once and every output
+    written once: k, dkw, beta (and r) read, d0 and dd_T read; dk, dbeta (and dr)
+    written, dd0 written.  The workspace (each token's preconditioner, written by
+    the forward sweep and read back by the reverse) is not counted."""
+    ntok = B * T * H
+    return ntok * (3 * d_k * esz + esz * (4 if apf else 2)) + 3 * B * H * d_k * 4
+
+
 def prepare_precond(wl, log):
     import torch
     from workloads import precond_factors
@@ -330,10 +339,16 @@ def bench_precond(prep, args, log, wl, k, beta):
     bms = time_calls(lambda i: gdr.precond_scan_bwd(k, beta, PRECOND_ETA, r, d0, dkw, dd_T, workspace=ws),
                      args.warmup, args.steps)
     del dkw, dd_T, ws
+    bbytes = precond_bwd_bytes(wl.B, wl.T, wl.H, wl.d_k, 2, True)
+    bgbs = bbytes / (bms * 1e-3) / 1e9
     log(f"preconditioner scan backward: {bms * 1e3:.1f} us")
     return kw, {"workload": "osdn_precond_scan_apf_b%dh%dt%dd%d_bf16" % (wl.B, wl.H, wl.T, wl.d_k),
             "value": round(gbs, 1), "unit": "GB/s", "us_per_launch": round(ms * 1e3, 2),
             "backward_us_per_launch": round(bms * 1e3, 2),
+            "backward_roofline": {"bound": "hbm", "achieved": round(bgbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                  "frac": round(bgbs / HBM_PEAK_GBS, 4), "bytes_per_launch": bbytes,
+                                  "traffic": profiled_traffic("precond_scan_bwd_b8h16t8192d128_counters.md",
+                                                              PRECOND_SOURCES)},
             "tokens_per_s": round(wl.B * wl.T / (ms * 1e-3), 1), "bytes_per_launch": nbytes,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4),
