@@ -542,19 +542,6 @@ static hipError_t launch_seq_t(const PrecondParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------------
-// Reverse mode of the scan, token by token, one wave per (sequence, head), in fp32
-// for both I/O dtypes.  With w_t = k_t^2, n_t = ||k_t||^2, x_t = <d_t, w_t>,
-// e_t = eta beta_t (1 - beta_t x_t) / n_t and D the gradient of d carried from the
-// end (D_T = dd_T), token t going backwards:
-//     u_t     = <D_{t+1}, w_t>,   dr_t = <D_{t+1}, d_t>,
-//     dbeta_t = u_t eta (1 - 2 beta_t x_t) / n_t,
-//     dk_t    = dkw_t * d_t + 2 k_t * (e_t D_{t+1} - u_t rho_t d_t - u_t e_t / n_t),
-//     D_t     = r_t D_{t+1} - u_t rho_t w_t + dkw_t * k_t,     rho_t = eta beta_t^2 / n_t,
-// and dd0 = D_0 (a zero key adds only dkw_t * d_t).  A first sweep runs the scan
-// forward and keeps every d_t and (x_t, n_t) in the workspace; the second walks the
-// tokens back, U at a time, loading the next U while the current ones run.
-// ---------------------------------------------------------------------------------
 // The CPL channels of one lane as raw words, one vector access (bf16: 2 or 4 bytes,
 // fp32: 4 or 8), unpacked only where they are used: a load whose value is converted
 // at once would make the compiler wait for it there, serialising the prefetch.
@@ -614,10 +601,10 @@ __device__ __forceinline__ float lane_bcast(uint32_t v, int src) {   // src: a c
 }
 
 // ---------------------------------------------------------------------------------
-// Reverse mode of the scan, token by token, one wave per (sequence, head), in fp32
-// for both I/O dtypes.  With w_t = k_t^2, n_t = ||k_t||^2, x_t = <d_t, w_t>,
-// e_t = eta beta_t (1 - beta_t x_t) / n_t and D the gradient of d carried from the
-// end (D_T = dd_T), token t going backwards:
+// Reverse mode of the scan for fp32 I/O, token by token, one wave per (sequence,
+// head), in fp32 (bf16 I/O takes the blocked kernel below).  With w_t = k_t^2,
+// n_t = ||k_t||^2, x_t = <d_t, w_t>, e_t = eta beta_t (1 - beta_t x_t) / n_t and D
+// the gradient of d carried from the end (D_T = dd_T), token t going backwards:
 //     u_t     = <D_{t+1}, w_t>,   dr_t = <D_{t+1}, d_t>,
 //     dbeta_t = u_t eta (1 - 2 beta_t x_t) / n_t,
 //     dk_t    = dkw_t * d_t + 2 k_t * (e_t D_{t+1} - u_t rho_t d_t - u_t e_t / n_t),
