@@ -13,7 +13,7 @@ import pytest
 
 from oracle import forward as oracle_forward, recurrent_step as oracle_step, rel_l2
 from tests.gpu_util import TOL, check, dev, host, need_gpu, say
-from workloads import Workload, chunk_inputs
+from workloads import CONFIGS, Workload, chunk_inputs
 from workloads.inputs import round_to_io
 
 pytestmark = pytest.mark.gpu
@@ -172,3 +172,41 @@ def test_write_key_gated_prefill_then_decode(gate):
     o_ref, S_ref = oracle_forward(inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_a"], inp["S0"], kw=inp["kw"])
     check("o (prefill and decode)", np.concatenate(outs, axis=1), o_ref, TOL["bf16"])
     check("S", host(S), S_ref, TOL["bf16"])
+
+
+def test_write_key_full_size_whole_tensor():
+    """The write-key forward over the gated B8 H16 T8192 d128 bf16 workload (scalar
+    gate) at full size, in the launch the benchmark's write-key training path times;
+    every (b, h) slice against the oracle with the same write keys (host processes in
+    parallel): whole-tensor relative L2 of o and S_T, and that of the worst slice,
+    within the bf16 tolerance."""
+    need_gpu()
+    import torch
+    import gated_delta_rule_21_amd as gdr
+    from tests.parallel_oracle import whole_chunk
+    from tests.report import report
+    wl = CONFIGS[3]
+    say(f"full-size write-key forward {wl.name}: generating inputs")
+    inp = chunk_inputs(wl)
+    d = np.random.default_rng([wl.seed, 7]).uniform(0.2, 2.0, inp["k"].shape)
+    kw_h = round_to_io(d * inp["k"], "bf16")
+    del d
+    args = [dev(inp[n], "bf16") for n in ("q", "k", "v", "beta", "log_a")]
+    S0 = torch.from_numpy(inp["S0"]).cuda()
+    del inp
+    say("  running GPU")
+    o, S = gdr.chunk_fwd(*args, S0, kw=dev(kw_h, "bf16"))
+    torch.cuda.synchronize()
+    o_h, S_h = o.float().cpu().numpy(), S.cpu().numpy()
+    del o, S, args, S0
+    assert np.isfinite(o_h).all() and np.isfinite(S_h).all()
+    say("  oracle on every slice")
+    r = whole_chunk(wl, o_h, S_h, group=4, kw=kw_h)
+    line = (f"write-key forward {wl.name}: whole-tensor rel_l2 o {r['o']:.3e}  S_T {r['S']:.3e}; worst (b, h, rel_l2) "
+            f"o ({r['worst_o'][0]}, {r['worst_o'][1]}, {r['worst_o'][2]:.3e})  S_T ({r['worst_S'][0]}, "
+            f"{r['worst_S'][1]}, {r['worst_S'][2]:.3e}); {r['slices']} slices on {r['procs']} processes in "
+            f"{r['seconds']:.1f} s")
+    say("  " + line)
+    report(line)
+    assert r["o"] <= TOL["bf16"] and r["S"] <= TOL["bf16"]
+    assert r["worst_o"][2] <= TOL["bf16"] and r["worst_S"][2] <= TOL["bf16"]

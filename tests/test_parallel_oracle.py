@@ -4,9 +4,10 @@ relative L2 of a known perturbation."""
 
 import numpy as np
 
-from oracle import forward, recurrent_step, rel_l2
-from tests.parallel_oracle import whole_chunk, whole_decode
-from workloads import DECODE_CONFIG, Workload, chunk_inputs, decode_inputs
+from oracle import backward, forward, precond_scan, recurrent_step, rel_l2
+from oracle.preconditioner import precond_scan_backward
+from tests.parallel_oracle import whole_backward, whole_chunk, whole_decode, whole_scan, whole_scan_backward
+from workloads import DECODE_CONFIG, Workload, chunk_inputs, decode_inputs, grad_inputs, precond_inputs
 
 
 def test_whole_chunk_matches_single_process():
@@ -33,3 +34,62 @@ def test_whole_decode_matches_single_process():
     assert r["o"] < 1e-13 and r["S"] < 1e-13
     r = whole_decode(wl, 7, o_all * 1.02, S, group=3)
     assert abs(r["o"] - 0.02) < 1e-9
+
+
+def test_whole_chunk_with_write_key():
+    wl = Workload("par_kw", B=2, T=40, H=2, d_k=16, d_v=8, io="bf16", gate="scalar", s0_std=0.1, seed=5)
+    inp = chunk_inputs(wl)
+    kw = inp["k"] * np.random.default_rng(1).uniform(0.5, 1.5, inp["k"].shape)
+    o, S = forward(inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_a"], inp["S0"], kw=kw)
+    r = whole_chunk(wl, o, S, group=1, kw=kw)
+    assert r["o"] < 1e-13 and r["S"] < 1e-13
+    r = whole_chunk(wl, o, S, group=1)          # the plain forward differs from the write-key one
+    assert r["o"] > 1e-3
+
+
+def _grads(wl, kw=None):
+    x = chunk_inputs(wl)
+    x.update(grad_inputs(wl))
+    return backward(x["q"], x["k"], x["v"], x["beta"], x["log_a"], x["S0"], x["dO"], x["dS_T"], kw=kw)
+
+
+def test_whole_backward_matches_single_process():
+    wl = Workload("par_bwd", B=2, T=70, H=3, d_k=16, d_v=8, io="bf16", gate="channel", s0_std=0.1, seed=7)
+    g = _grads(wl)
+    r = whole_backward(wl, g)
+    assert r["slices"] == 6 and max(r["rel"].values()) < 1e-13, r["rel"]
+    g2 = {n: (None if a is None else a.copy()) for n, a in g.items()}
+    g2["dk"][0, :, 1] *= 1.03                   # one slice of dk off by 3 %
+    g2["dS0"] *= 1.002
+    r = whole_backward(wl, g2)
+    assert abs(r["rel"]["dk"] - rel_l2(g2["dk"], g["dk"])) < 1e-12
+    assert r["worst"]["dk"][:2] == (0, 1) and abs(r["worst"]["dk"][2] - 0.03) < 1e-9
+    assert abs(r["rel"]["dS0"] - 2e-3) < 1e-9 and r["rel"]["dq"] < 1e-13
+
+
+def test_whole_backward_with_write_key():
+    wl = Workload("par_bwd_kw", B=1, T=50, H=2, d_k=16, d_v=8, io="bf16", gate="scalar", s0_std=0.1, seed=9)
+    x = chunk_inputs(wl)
+    kw = x["k"] * np.random.default_rng(2).uniform(0.5, 1.5, x["k"].shape)
+    g = _grads(wl, kw=kw)
+    assert "dkw" in g
+    r = whole_backward(wl, g, kw=kw)
+    assert max(r["rel"].values()) < 1e-13, r["rel"]
+
+
+def test_whole_scan_and_its_backward():
+    wl = Workload("par_scan", B=2, T=90, H=2, d_k=16, d_v=16, io="bf16", gate="scalar", s0_std=0.0, seed=11)
+    x = precond_inputs(wl)
+    kw, d_T = precond_scan(x["k"], x["beta"], 0.5, x["r"], x["d0"])
+    r = whole_scan(wl, 0.5, kw, d_T)
+    assert r["slices"] == 4 and max(r["rel"].values()) < 1e-13, r["rel"]
+    r = whole_scan(wl, 0.5, kw * 1.01, d_T)
+    assert abs(r["rel"]["kw"] - 0.01) < 1e-9
+    rng = np.random.default_rng(3)
+    dkw, dd_T = rng.standard_normal(kw.shape), rng.standard_normal(d_T.shape)
+    g = precond_scan_backward(x["k"], x["beta"], 0.5, x["r"], x["d0"], dkw, dd_T)
+    r = whole_scan_backward(wl, 0.5, dkw, dd_T, g)
+    assert max(r["rel"].values()) < 1e-13, r["rel"]
+    g["dr"] = g["dr"] * 1.05
+    r = whole_scan_backward(wl, 0.5, dkw, dd_T, g)
+    assert abs(r["rel"]["dr"] - 0.05) < 1e-9
