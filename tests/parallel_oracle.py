@@ -206,6 +206,37 @@ def whole_scan_backward(wl, eta: float, dkw: np.ndarray, dd_T: np.ndarray, grads
     return _whole(_scan_bwd_slice, items, grads, {"dkw_in": dkw, "ddT_in": dd_T})
 
 
+def _packed_seq(i):
+    inp, cu = _GPU["inp"], _GPU["cu"]
+    lo, hi = int(cu[i]), int(cu[i + 1])
+    sl = lambda a: None if a is None else np.ascontiguousarray(a[:, lo:hi])
+    o_ref, S_ref = forward(*(sl(inp[n]) for n in ("q", "k", "v", "beta", "log_a")), _GPU["S0"][i:i + 1])
+    o_sums = _sums(_GPU["out"]["o"][:, lo:hi], o_ref)
+    S_sums = _sums(_GPU["out"]["S"][i], S_ref[0])
+    return i, o_sums, S_sums, S_ref[0]
+
+
+def whole_packed(inp: dict, cu: np.ndarray, S0: np.ndarray, o_gpu: np.ndarray, S_gpu: np.ndarray):
+    """Packed sequences ([1, T, H, .] inputs, offsets cu) against the oracle run on each
+    sequence alone, sequences dealt to host processes.  Returns the rel-L2 of the whole
+    o and of the whole S_T, the worst sequence's S_T rel-L2, and the oracle's final
+    states [n_seq, H, d_k, d_v] (fp64)."""
+    n_seq = len(cu) - 1
+    _GPU.update(inp=inp, cu=cu, S0=S0, out={"o": o_gpu, "S": S_gpu})
+    procs = host_procs()
+    t0 = time.perf_counter()
+    try:
+        with mp.get_context("fork").Pool(procs, initializer=_init) as pool:
+            rows = sorted(pool.imap_unordered(_packed_seq, range(n_seq)), key=lambda r: r[0])
+    finally:
+        _GPU.clear()
+    num_o, den_o = sum(r[1][0] for r in rows), sum(r[1][1] for r in rows)
+    num_S, den_S = sum(r[2][0] for r in rows), sum(r[2][1] for r in rows)
+    worst = max(float(np.sqrt(r[2][0] / max(r[2][1], 1e-300))) for r in rows)
+    return dict(o=float(np.sqrt(num_o / den_o)), S=float(np.sqrt(num_S / den_S)), worst_S=worst,
+                S_ref=np.stack([r[3] for r in rows]), procs=procs, seconds=time.perf_counter() - t0)
+
+
 def assert_whole(label: str, r: dict, tol: float) -> str:
     """Print and report the whole-tensor numbers of r (from whole_backward, whole_scan
     or whole_scan_backward); every name's whole-tensor rel-L2 and its worst (b, h)

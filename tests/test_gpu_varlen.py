@@ -226,3 +226,53 @@ def test_varlen_fp32(gate, dk):
         torch.cuda.synchronize()
         assert np.array_equal(host(oa), o_h[:, lo:hi]), f"sequence {i}: o differs from the call on it alone"
         assert np.array_equal(host(Sa)[0], S_h[i]), f"sequence {i}: S_T differs from the call on it alone"
+
+
+@pytest.mark.timeout(600)
+def test_serving_mix_full_size_whole():
+    """The benchmark's serving mix at full size, in the launch it times: 32 prompts of
+    log-uniform lengths in [128, 8192] (H16 d128, scalar gate, no initial state)
+    through the packed forward, then 16 decode steps on the states it hands over.
+    o over every packed token, S_T of every sequence, every decode output and the
+    final states against the oracle, whole tensors."""
+    need_gpu()
+    import torch
+    import gated_delta_rule_21_amd as gdr
+    from bench import handoff_lengths
+    from tests.report import report
+    lens = handoff_lengths()
+    N, H, dk, dv, T, steps = len(lens), 16, 128, 128, int(sum(lens)), 16
+    say(f"serving mix: {N} prompts, {T} tokens")
+    inp = chunk_inputs(Workload("handoff_prefill", B=1, T=T, H=H, d_k=dk, d_v=dv, io="bf16", gate="scalar",
+                                s0_std=0.0, seed=6))
+    tok = chunk_inputs(Workload("handoff_tokens", B=N, T=steps, H=H, d_k=dk, d_v=dv, io="bf16", gate="scalar",
+                                s0_std=0.0, seed=7))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    o, S = gdr.chunk_fwd_varlen(*(dev(inp[n], "bf16") for n in ("q", "k", "v", "beta", "log_a")),
+                                torch.from_numpy(cu).cuda(), None)
+    o_pre = host(o)
+    S_pre_gpu = host(S)
+    dec = []
+    for s in range(steps):
+        od, S = gdr.recurrent_step(*(dev(np.ascontiguousarray(tok[n][:, s]), "bf16")
+                                     for n in ("q", "k", "v", "beta", "log_a")), S)
+        dec.append(host(od))
+    torch.cuda.synchronize()
+    S_dec = host(S)
+    say("  oracle on every sequence")
+    from tests.parallel_oracle import whole_packed
+    r = whole_packed(inp, cu, np.zeros((N, H, dk, dv)), o_pre, S_pre_gpu)
+    e_o, e_s, worst = r["o"], r["S"], r["worst_S"]
+    say(f"  prefill o {e_o:.3e}  S_T {e_s:.3e}  worst sequence S_T {worst:.3e} ({r['procs']} processes, "
+        f"{r['seconds']:.1f} s)")
+    assert e_o <= TOL["bf16"] and e_s <= TOL["bf16"] and worst <= TOL["bf16"], (e_o, e_s, worst)
+    Sr = r["S_ref"]
+    e_d = 0.0
+    for s in range(steps):
+        od_ref, Sr = oracle_step(Sr, *(tok[n][:, s] for n in ("q", "k", "v", "beta", "log_a")))
+        e_d = max(e_d, check(f"decode o step {s}", dec[s], od_ref, TOL["bf16"]))
+    e_f = check("decode S", S_dec, Sr, TOL["bf16"])
+    line = (f"serving mix ({N} prompts, {T} tokens, H{H} d{dk}): prefill o {e_o:.3e}  S_T {e_s:.3e} (worst sequence "
+            f"{worst:.3e}); {steps} decode steps: worst o {e_d:.3e}, final S {e_f:.3e}")
+    say("  " + line)
+    report(line)

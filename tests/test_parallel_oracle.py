@@ -93,3 +93,26 @@ def test_whole_scan_and_its_backward():
     g["dr"] = g["dr"] * 1.05
     r = whole_scan_backward(wl, 0.5, dkw, dd_T, g)
     assert abs(r["rel"]["dr"] - 0.05) < 1e-9
+
+
+def test_whole_packed_matches_single_process():
+    from tests.parallel_oracle import whole_packed
+    lens = [0, 5, 70, 1, 130]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    wl = Workload("par_packed", B=1, T=int(cu[-1]), H=2, d_k=16, d_v=8, io="bf16", gate="scalar", s0_std=0.0, seed=13)
+    inp = chunk_inputs(wl)
+    S0 = np.random.default_rng(4).standard_normal((len(lens), 2, 16, 8)) * 0.1
+    o = np.zeros(inp["v"].shape)
+    S = np.zeros(S0.shape)
+    for i in range(len(lens)):
+        lo, hi = int(cu[i]), int(cu[i + 1])
+        sl = lambda a: None if a is None else a[:, lo:hi]
+        oi, Si = forward(*(sl(inp[n]) for n in ("q", "k", "v", "beta", "log_a")), S0[i:i + 1])
+        o[:, lo:hi], S[i] = oi, Si[0]
+    r = whole_packed(inp, cu, S0, o, S)
+    assert r["o"] < 1e-13 and r["S"] < 1e-13 and r["worst_S"] < 1e-13
+    assert np.array_equal(r["S_ref"], S)
+    S2 = S.copy()
+    S2[3] *= 1.05                               # the one-token sequence's state off by 5 %
+    r = whole_packed(inp, cu, S0, o, S2)
+    assert abs(r["worst_S"] - 0.05) < 1e-9 and abs(r["S"] - rel_l2(S2, S)) < 1e-12
