@@ -38,13 +38,14 @@ def _init():
 
 
 def _chunk_group(args):
-    wl, b, hs = args
+    wl, b, hs, form = args
     sl = [slice_inputs(wl, b, h) for h in hs]
     st = lambda n: np.stack([s[n] for s in sl], axis=1)[None]          # [1, T, nh, .]
     la = None if wl.gate == "none" else st("log_a")
     kw = _GPU.get("kw_in")
     kw = None if kw is None else kw[b:b + 1, :, hs[0]:hs[-1] + 1]
-    o_ref, S_ref = forward(st("q"), st("k"), st("v"), st("beta"), la, np.stack([s["S0"] for s in sl])[None], kw=kw)
+    o_ref, S_ref = forward(st("q"), st("k"), st("v"), st("beta"), la, np.stack([s["S0"] for s in sl])[None], kw=kw,
+                           form=form)
     out = []
     for i, h in enumerate(hs):
         do = _GPU["o"][b, :, h].astype(np.float64) - o_ref[0, :, i]
@@ -54,14 +55,17 @@ def _chunk_group(args):
     return out
 
 
-def whole_chunk(wl, o_gpu: np.ndarray, S_gpu: np.ndarray, group: int = 4, kw: np.ndarray = None):
+def whole_chunk(wl, o_gpu: np.ndarray, S_gpu: np.ndarray, group: int = 4, kw: np.ndarray = None,
+                form: str = "page"):
     """Whole-tensor rel-L2 of o and S_T against the oracle, and the worst (b, h) slice
     of each.  o_gpu [B, T, H, d_v], S_gpu [B, H, d_k, d_v] (host arrays); kw the
-    write key [B, T, H, d_k] the GPU was given (host), or None."""
+    write key [B, T, H, d_k] the GPU was given (host), or None; form the gate's
+    placement the GPU ran ("page" or "literal")."""
     _GPU["o"], _GPU["S"] = o_gpu, S_gpu
     if kw is not None:
         _GPU["kw_in"] = kw
-    items = [(wl, b, list(range(h0, min(h0 + group, wl.H)))) for b in range(wl.B) for h0 in range(0, wl.H, group)]
+    items = [(wl, b, list(range(h0, min(h0 + group, wl.H))), form) for b in range(wl.B)
+             for h0 in range(0, wl.H, group)]
     procs = host_procs()
     t0 = time.perf_counter()
     with mp.get_context("fork").Pool(procs, initializer=_init) as pool:

@@ -156,11 +156,12 @@ def test_caller_workspace_reused_and_dirty():
 
 # ---- full-size workloads in the benchmarked launch, every (b, h) slice against the oracle ----
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("cfg", [2, 3, 4])
-def test_full_workload_whole_tensor(cfg):
+@pytest.mark.parametrize("cfg,form", [(2, "page"), (3, "page"), (4, "page"), (3, "literal"), (4, "literal")])
+def test_full_workload_whole_tensor(cfg, form):
     """The whole o and S_T of the full-size workload against the fp64 oracle run on
     every (b, h) slice (host processes in parallel): whole-tensor relative L2 within
-    the bf16 tolerance, and the worst slice reported."""
+    the bf16 tolerance, and the worst slice reported.  The gated workloads also run
+    in the literal form (the gate read after the erase)."""
     need_gpu()
     import torch
     from tests.gpu_util import dev
@@ -173,14 +174,15 @@ def test_full_workload_whole_tensor(cfg):
     args = [dev(inp[n], wl.io) for n in ("q", "k", "v", "beta", "log_a")]
     del inp
     say("  running GPU")
-    o, S = gdr.chunk_fwd(*args, S0)
+    o, S = gdr.chunk_fwd(*args, S0, form=form)
     torch.cuda.synchronize()
     o_h, S_h = o.float().cpu().numpy(), S.cpu().numpy()
     del o, S, args, S0
     assert np.isfinite(o_h).all() and np.isfinite(S_h).all()
     say("  oracle on every slice")
-    r = whole_chunk(wl, o_h, S_h, group=2 if cfg == 4 else 4)
-    line = (f"{wl.name}: whole-tensor rel_l2 o {r['o']:.3e}  S_T {r['S']:.3e}; worst (b, h, rel_l2) o "
+    r = whole_chunk(wl, o_h, S_h, group=2 if cfg == 4 else 4, form=form)
+    name = wl.name + ("" if form == "page" else " (literal form)")
+    line = (f"{name}: whole-tensor rel_l2 o {r['o']:.3e}  S_T {r['S']:.3e}; worst (b, h, rel_l2) o "
             f"({r['worst_o'][0]}, {r['worst_o'][1]}, {r['worst_o'][2]:.3e})  S_T ({r['worst_S'][0]}, {r['worst_S'][1]}, "
             f"{r['worst_S'][2]:.3e}); {r['slices']} slices on {r['procs']} processes in {r['seconds']:.1f} s")
     say("  " + line)

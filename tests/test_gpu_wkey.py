@@ -174,18 +174,20 @@ def test_write_key_gated_prefill_then_decode(gate):
     check("S", host(S), S_ref, TOL["bf16"])
 
 
-def test_write_key_full_size_whole_tensor():
-    """The write-key forward over the gated B8 H16 T8192 d128 bf16 workload (scalar
-    gate) at full size, in the launch the benchmark's write-key training path times;
-    every (b, h) slice against the oracle with the same write keys (host processes in
-    parallel): whole-tensor relative L2 of o and S_T, and that of the worst slice,
-    within the bf16 tolerance."""
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("cfg", [3, 4])
+def test_write_key_full_size_whole_tensor(cfg):
+    """The write-key forward over a gated workload at full size: B8 H16 T8192 d128
+    with the scalar gate (the launch the benchmark's write-key training path times)
+    and B2 H32 T32768 d128 with the per-channel gate; every (b, h) slice against the
+    oracle with the same write keys (host processes in parallel): whole-tensor
+    relative L2 of o and S_T, and that of the worst slice, within the bf16 tolerance."""
     need_gpu()
     import torch
     import gated_delta_rule_21_amd as gdr
     from tests.parallel_oracle import whole_chunk
     from tests.report import report
-    wl = CONFIGS[3]
+    wl = CONFIGS[cfg]
     say(f"full-size write-key forward {wl.name}: generating inputs")
     inp = chunk_inputs(wl)
     d = np.random.default_rng([wl.seed, 7]).uniform(0.2, 2.0, inp["k"].shape)
@@ -201,7 +203,7 @@ def test_write_key_full_size_whole_tensor():
     del o, S, args, S0
     assert np.isfinite(o_h).all() and np.isfinite(S_h).all()
     say("  oracle on every slice")
-    r = whole_chunk(wl, o_h, S_h, group=4, kw=kw_h)
+    r = whole_chunk(wl, o_h, S_h, group=2 if cfg == 4 else 4, kw=kw_h)
     line = (f"write-key forward {wl.name}: whole-tensor rel_l2 o {r['o']:.3e}  S_T {r['S']:.3e}; worst (b, h, rel_l2) "
             f"o ({r['worst_o'][0]}, {r['worst_o'][1]}, {r['worst_o'][2]:.3e})  S_T ({r['worst_S'][0]}, "
             f"{r['worst_S'][1]}, {r['worst_S'][2]:.3e}); {r['slices']} slices on {r['procs']} processes in "
