@@ -103,6 +103,20 @@ def test_workspace_checks(lib):
     assert b"overlaps" in lib.gdr_last_error()
 
 
+def test_per_sequence_offset_limit(lib):
+    """The kernels address one (sequence, head) slice with 32-bit byte offsets: the
+    longest sequence at H16 d128 bf16 is T = 524,287 (T*H*d*2 = 2^31 - 4096); one
+    token more is refused before anything is enqueued, by the size query and the call."""
+    assert _ws_size(lib, _desc(B=1, T=524287, H=16))[0] == OK
+    assert _ws_size(lib, _desc(B=1, T=524288, H=16))[0] == UNSUPPORTED
+    assert b"2^31 - 1 per sequence" in lib.gdr_last_error()
+    assert _chunk(lib, _desc(B=1, T=524288, H=16), _ptrs(), ws_bytes=1 << 40) == UNSUPPORTED
+    assert _ws_size(lib, _desc(B=1, T=524287, H=16, io=0, d_k=64, d_v=64))[0] == OK     # fp32 d64: as many bytes
+    assert _ws_size(lib, _desc(B=1, T=524288, H=16, io=0, d_k=64, d_v=64))[0] == UNSUPPORTED
+    assert _ws_size(lib, _desc(B=1, T=1048575, H=8))[0] == OK                            # half the heads: twice T
+    assert _ws_size(lib, _desc(B=1, T=1048576, H=8))[0] == UNSUPPORTED
+
+
 def test_null_desc(lib):
     assert _chunk(lib, None, _ptrs()) == INVALID
     assert b"desc" in lib.gdr_last_error()

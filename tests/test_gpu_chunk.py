@@ -162,12 +162,26 @@ def test_full_workload_whole_tensor(cfg, form):
     every (b, h) slice (host processes in parallel): whole-tensor relative L2 within
     the bf16 tolerance, and the worst slice reported.  The gated workloads also run
     in the literal form (the gate read after the erase)."""
+    _whole_forward(CONFIGS[cfg], form, group=2 if cfg == 4 else 4)
+
+
+@pytest.mark.timeout(900)
+def test_longest_sequence_the_offsets_allow():
+    """The longest sequence the kernels' 32-bit per-sequence byte offsets allow at H16
+    d128 bf16: T = 524,287 tokens, so that T*H*d*2 = 2^31 - 4096 bytes (one token more
+    is refused, see the ABI tests), with a ragged last chunk, a scalar gate and an
+    initial state; the whole o and S_T against the oracle run on every head."""
+    wl = Workload("max_span_b1h16t524287d128_bf16", B=1, T=524287, H=16, d_k=128, d_v=128, io="bf16",
+                  gate="scalar", s0_std=0.02, seed=31)
+    _whole_forward(wl, "page", group=1)
+
+
+def _whole_forward(wl, form, group):
     need_gpu()
     import torch
     from tests.gpu_util import dev
     from tests.parallel_oracle import whole_chunk
     import gated_delta_rule_21_amd as gdr
-    wl = CONFIGS[cfg]
     say(f"full workload {wl.name}: generating inputs")
     inp = chunk_inputs(wl)
     S0 = torch.from_numpy(inp["S0"]).cuda()
@@ -180,7 +194,7 @@ def test_full_workload_whole_tensor(cfg, form):
     del o, S, args, S0
     assert np.isfinite(o_h).all() and np.isfinite(S_h).all()
     say("  oracle on every slice")
-    r = whole_chunk(wl, o_h, S_h, group=2 if cfg == 4 else 4, form=form)
+    r = whole_chunk(wl, o_h, S_h, group=group, form=form)
     name = wl.name + ("" if form == "page" else " (literal form)")
     line = (f"{name}: whole-tensor rel_l2 o {r['o']:.3e}  S_T {r['S']:.3e}; worst (b, h, rel_l2) o "
             f"({r['worst_o'][0]}, {r['worst_o'][1]}, {r['worst_o'][2]:.3e})  S_T ({r['worst_S'][0]}, {r['worst_S'][1]}, "
