@@ -161,6 +161,32 @@ def test_varlen_order_longest_first():
     _check_each(o, S, o_ref, S_ref, cu)
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("n_seq", [16384, 16385])
+def test_varlen_order_at_its_limit(n_seq):
+    """The rank kernel orders up to 16,384 packed sequences longest first and leaves
+    the identity order above that; either way every sequence (lengths 0 to 3 tokens)
+    matches the oracle run on it alone."""
+    need_gpu()
+    import torch
+    import gated_delta_rule_21_amd as gdr
+    lens = [int(x) for x in np.random.RandomState(n_seq).randint(0, 4, size=n_seq)]
+    N, H, T = n_seq, 2, int(sum(lens))
+    say(f"case {N} packed sequences, {T} tokens")
+    inp, S0, cu = _inputs(lens, H, 64, 64, "scalar", seed=131)
+    size = gdr.chunk_varlen_workspace_size(T, N, H, 64, 64, torch.bfloat16, "scalar")
+    ws = torch.zeros(size, dtype=torch.uint8, device="cuda")
+    o, S = gdr.chunk_fwd_varlen(*(dev(inp[n], "bf16") for n in ("q", "k", "v", "beta", "log_a")),
+                                torch.from_numpy(cu).cuda(), torch.from_numpy(S0).cuda(), workspace=ws)
+    torch.cuda.synchronize()
+    tail = (N * 4 + 15) // 16 * 16
+    order = ws[size - tail:size - tail + 4 * N].cpu().view(torch.int32).numpy()
+    want = sorted(range(N), key=lambda i: (-lens[i], i)) if N <= 16384 else list(range(N))
+    assert list(order) == want
+    o_ref, S_ref = _oracle(inp, S0, cu)
+    _check_each(o, S, o_ref, S_ref, cu)
+
+
 @pytest.mark.parametrize("gate", ["none", "scalar", "channel"])
 def test_varlen_write_key(gate):
     """gdr_chunk_fwd_varlen_wkey: each packed sequence against the write-key oracle of
