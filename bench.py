@@ -592,7 +592,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
-              "the hot path has no multi-GPU leg in this build.", file=sys.stderr)
+              "the library has no multi-GPU path (a sharding design is described with the kernels).", file=sys.stderr)
         sys.exit(2)
 
     log = (lambda *a: None) if args.quiet else (lambda *a: print("[bench]", *a, file=sys.stderr, flush=True))
