@@ -28,7 +28,8 @@ clocks take ~100 calls to come back up).  Besides the headline workload, the
 other three chunk-forward workloads are timed (`configs`: the fp32 DeltaNet
 B1 H1 T256 d64, the DeltaNet B4 H16 T4096 d128 with three copies of its inputs
 taken in turn so the repeats do not run from the 256 MB Infinity Cache, and
-the per-channel B2 H32 T32768 d128).
+the per-channel B2 H32 T32768 d128), and so is the backward on the per-channel
+workload (`backward_channel`: the recomputing backward and the training path).
 
 Prints one JSON line.  `roofline` is for the chunk-forward call: algorithmic
 bytes per launch (inputs read once, outputs written once) over the average
@@ -362,7 +363,7 @@ def bwd_bytes(wl, with_S0: bool):
     the call keeps in its workspace are not counted."""
     esz = 2
     ntok = wl.B * wl.T * wl.H
-    gate_w = 1 if wl.gate == "scalar" else 0
+    gate_w = {"none": 0, "scalar": 1, "channel": wl.d_k}[wl.gate]
     state = wl.B * wl.H * wl.d_k * wl.d_v * 4
     rd = ntok * (2 * wl.d_k + 2 * wl.d_v + 1 + gate_w) * esz + state * (2 if with_S0 else 1)
     wr = ntok * (2 * wl.d_k + wl.d_v + 1 + gate_w) * esz + state
@@ -457,6 +458,39 @@ def bench_bwd(prep, args, log, wl, q, k, v, beta, log_a, S0):
                          "frac": round(tf / BF16_PEAK_TFLOPS, 4),
                          "traffic": (profiled_traffic("chunk_bwd_gated_b8h16t8192d128_counters.md", BWD_SOURCES)
                                      if wl.name == "gated_deltanet_scalar_b8h16t8192d128_bf16" else None)}}
+
+
+def bench_bwd_channel(prep, bprep, args, log):
+    """The backward on the per-channel workload (B2 H32 T32768 d128, S0 ~ N(0, 0.02^2)):
+    the recomputing backward, then the training path (the forward keeping its records
+    and chunk-start states, and the backward taking them).  Useful flops as for the
+    scalar gate (the per-channel decays inside the products are not counted)."""
+    import torch
+    import gated_delta_rule_21_amd as gdr
+    wl = prep["wl"]
+    q, k, v, beta, log_a = prep["sets"][0]["args"]
+    S0 = prep["sets"][0]["S0"]
+    dO, dS_T, ws = bprep["dO"], bprep["dS_T"], bprep["ws"]
+    steps, warmup = max(10, args.steps // 5), max(3, args.warmup // 5)
+    ms = time_calls(lambda i: gdr.chunk_bwd(q, k, v, beta, log_a, S0, dO, dS_T, workspace=ws), warmup, steps)
+    o_s, S_s = torch.empty_like(v), torch.empty((wl.B, wl.H, wl.d_k, wl.d_v), dtype=torch.float32, device="cuda")
+    fs = time_calls(lambda i: gdr.chunk_fwd_save(q, k, v, beta, log_a, S0, o=o_s, S_T=S_s, workspace=ws), warmup,
+                    steps)
+    bs = time_calls(lambda i: gdr.chunk_bwd(q, k, v, beta, log_a, S0, dO, dS_T, saved=ws), warmup, steps)
+    del o_s, S_s
+    flops, sflops = bwd_algorithmic(wl), bwd_algorithmic(wl, saved=True)
+    tf, stf = flops / (ms * 1e-3) / 1e12, sflops / (bs * 1e-3) / 1e12
+    log(f"per-channel backward: {ms:.3f} ms/step ({tf:.1f} TFLOP/s useful); training path: forward {fs:.3f} ms, "
+        f"backward {bs:.3f} ms")
+    roof = lambda t: {"bound": "mfma", "achieved": round(t, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                      "frac": round(t / BF16_PEAK_TFLOPS, 4), "traffic": None}
+    return {"workload": wl.name + "_backward", "value": round(wl.B * wl.T / (ms * 1e-3), 1), "unit": "tokens/s",
+            "ms_per_launch": round(ms, 4), "warmup": warmup, "steps": steps, "useful_flops_per_launch": flops,
+            "algorithmic_bytes_per_launch": bwd_bytes(wl, True), "roofline": roof(tf),
+            "training_path": {"forward_ms_per_launch": round(fs, 4), "backward_ms_per_launch": round(bs, 4),
+                              "train_step_ms": round(fs + bs, 4),
+                              "train_step_tokens_per_s": round(wl.B * wl.T / ((fs + bs) * 1e-3), 1),
+                              "backward_useful_flops_per_launch": sflops, "backward_roofline": roof(stf)}}
 
 
 def bench_wkey(args, log, wl, q, k, v, beta, kw, scan_us):
@@ -613,12 +647,16 @@ def main():
     gated_bf16 = wl.io == "bf16" and wl.gate != "channel"
     pre_prep = None if args.no_precond or wl.io != "bf16" else prepare_precond(wl, log)
     bwd_prep = None if args.no_bwd or wl.io != "bf16" else prepare_bwd(wl, log)
+    chan_bwd_prep = None if args.no_bwd or 4 not in others else prepare_bwd(others[4]["wl"], log)
     torch.cuda.synchronize()
     if args.copy_calibration:
         copy_calibration(log)
 
     # ---- legs back to back; the headline forward last ----
     configs = {str(c): bench_chunk(p, args.warmup, args.steps, log, f"config {c}") for c, p in sorted(others.items())}
+    bwd_chan = None if chan_bwd_prep is None else bench_bwd_channel(others[4], chan_bwd_prep, args, log)
+    if chan_bwd_prep is not None:
+        chan_bwd_prep.clear()
     for p in others.values():
         p.clear()
     decode = None if dec_prep is None else bench_decode(dec_prep, args, log)
@@ -672,6 +710,7 @@ def main():
         "precond_scan": precond,
         "osdn": osdn,
         "backward": bwd,
+        "backward_channel": bwd_chan,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
